@@ -1,0 +1,459 @@
+"""CPU oracle for one GPU's mixture-of-experts layer -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+this module.  The product path (the HIP library and its Python binding) never
+calls it and shares no code with it; both sides only share the seeded input
+generators of moe_inputs.py.
+
+What it computes is the plain definition of the layer, evaluated in float64
+with numpy (a matmul is the only library primitive used), following the pages
+"Scalable Training of Mixture-of-Experts Models with Megatron Core":
+
+* the layer output y = sum over the top-k experts of g(x)_i * E_i(x)
+  (papers.lunadong.com summary, "Problem Definition");
+* the stage order Router -> Dispatcher -> Experts -> Combiner
+  (same page, "Pipeline Flow"; thelatestinai.com page, Figure 1);
+* the router as a learned linear projection, a score function, top-k selection
+  and load balancing (summary page, "System Modules: Router"; Figure 2);
+* the combiner putting rows back in their original token position and forming
+  the gate-weighted sum (summary page, "System Modules: Combiner");
+* SwiGLU experts (Table 4 names "Activation Function (SwiGLU)"; the GLU-variants
+  paper is in the citation list);
+* a shared expert that sees every token (Table 1 "Shared Experts", Figure 40).
+
+The pages give no formula for scores, groups, gates, the aux loss or the
+backward pass.  Those follow the workload descriptions (sigmoid + selection-only
+bias, 8 groups / top-4 by top-2 sum, renormalise then x2.5, aux coefficient
+1e-3) and the readings listed in the design doc (R1..R20):
+
+  R3  softmax selection key = fp32 logit (softmax is monotone), ties -> lower id
+  R4  sigmoid score s = fp32(1 / (1 + exp(-(double) l))); key = fp32(s + b)
+  R5  contiguous groups of E/n_group experts; group score = fp32 sum of the two
+      largest keys; group ties -> lower group id
+  R7  gates divide by the sum of the unbiased selected scores, then x scale
+  R8  aux = coeff * E * sum_e f_e * Pbar_e, f_e = c_e / (T k), Pbar_e = mean
+      full-softmax probability; only Pbar carries gradient
+  R9  dropless: every (token, choice) gets a row, T*k rows in all
+  R10 rows are expert-major, ascending token id inside an expert
+  R12 storage rounding (bf16 round-to-nearest-even) where a tensor is
+      materialised; everything in between is float64 here
+  R13 combine sums j = 0..k-1 in selection order, then the shared output
+
+Pins that tie this oracle to facts outside itself live in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------
+# storage rounding
+# ----------------------------------------------------------------------------
+def round_bf16(a) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even), via fp32; returned as fp64.
+
+    bfloat16 keeps the top 16 bits of an IEEE binary32; rounding to nearest even
+    adds 0x7FFF plus the lowest kept bit before truncating the low 16 bits.
+    """
+    a32 = np.ascontiguousarray(np.asarray(a, dtype=F64).astype(F32))
+    u = a32.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep_lsb) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    return r.view(F32).astype(F64)
+
+
+def store(a, storage: str) -> np.ndarray:
+    """Value of `a` after it is materialised in the layer's storage dtype."""
+    if storage == "bf16":
+        return round_bf16(a)
+    if storage == "f32":
+        return np.asarray(a, dtype=F64).astype(F32).astype(F64)
+    if storage == "f64":          # exact mode used by the finite-difference pins
+        return np.asarray(a, dtype=F64)
+    raise ValueError(storage)
+
+
+def storage_of(cfg) -> str:
+    return "f32" if cfg.dtype == "f32" else "bf16"
+
+
+# ----------------------------------------------------------------------------
+# Router: projection, score, (group-limited) top-k, gates, statistics
+# ----------------------------------------------------------------------------
+def router_logits(x, w_router, storage: str = "f32") -> np.ndarray:
+    """logits[t,e] = sum_i x[t,i] * W_r[e,i]  (learned linear projection).
+    Stored as fp32 (or kept exact in "f64" mode)."""
+    l = np.asarray(x, F64) @ np.asarray(w_router, F64).T
+    return l if storage == "f64" else l.astype(F32)
+
+
+def sigmoid_scores(logits, exact: bool = False) -> np.ndarray:
+    """s = 1/(1+exp(-l)) evaluated in float64 and rounded once to fp32 (R4)."""
+    s = 1.0 / (1.0 + np.exp(-np.asarray(logits, F64)))
+    return s if exact else s.astype(F32)
+
+
+def softmax_probs(logits) -> np.ndarray:
+    """Full softmax over all E experts, float64."""
+    l = np.asarray(logits, F64)
+    z = np.exp(l - l.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def selection_keys(logits, cfg, bias=None, exact: bool = False) -> np.ndarray:
+    """Key each expert is ranked by.  Softmax: the logit itself (R3).
+    Sigmoid: fp32(s + b), the bias steering selection only (R4)."""
+    if cfg.score == "softmax":
+        return np.asarray(logits, F64 if exact else F32)
+    s = sigmoid_scores(logits, exact)
+    if bias is None:
+        return s
+    b = np.asarray(bias, F32)
+    return (s + b) if not exact else (np.asarray(s, F64) + b.astype(F64))
+
+
+def _desc_order(values, ids) -> np.ndarray:
+    """ids sorted by value descending, equal values by id ascending."""
+    values = np.asarray(values)
+    ids = np.asarray(ids)
+    o = np.argsort(ids, kind="stable")               # ids ascending first
+    o2 = np.argsort(-values[o], kind="stable")       # then a stable sort by value desc
+    return ids[o][o2]
+
+
+def eligible_groups(keys_row, n_group: int, topk_group: int) -> np.ndarray:
+    """Group-limited routing for one token (R5): split the E experts into
+    n_group contiguous groups, score each group by the sum of its two largest
+    keys (one fp32 add; a single-expert group scores its only key), keep the
+    topk_group best groups.  Returns the kept group ids in rank order."""
+    E = keys_row.shape[0]
+    per = E // n_group
+    gscore = np.empty(n_group, dtype=keys_row.dtype)
+    for g in range(n_group):
+        member = np.sort(keys_row[g * per:(g + 1) * per])[::-1]
+        gscore[g] = member[0] + member[1] if per >= 2 else member[0]
+    return _desc_order(gscore, np.arange(n_group))[:topk_group]
+
+
+def select_topk(keys, cfg) -> np.ndarray:
+    """idx[t, :] = the k eligible experts with the largest keys, in descending
+    key order, equal keys by lower expert id (R6)."""
+    T, E = keys.shape
+    idx = np.empty((T, cfg.k), dtype=np.int32)
+    per = E // cfg.n_group
+    for t in range(T):
+        if cfg.n_group > 1:
+            groups = eligible_groups(keys[t], cfg.n_group, cfg.topk_group)
+            cand = np.concatenate([np.arange(g * per, (g + 1) * per) for g in groups])
+        else:
+            cand = np.arange(E)
+        idx[t] = _desc_order(keys[t][cand], cand)[:cfg.k]
+    return idx
+
+
+def gates_from_selection(logits, idx, cfg, exact: bool = False) -> np.ndarray:
+    """Gate weights g[t, j] of the selected experts (R7).
+    softmax + renorm: softmax restricted to the selection;
+    softmax without renorm: the full-softmax probability;
+    sigmoid: s / sum of selected s (if renorm), times cfg.scale."""
+    l = np.asarray(logits, F64)
+    sel_l = np.take_along_axis(l, idx.astype(np.int64), axis=1)
+    if cfg.score == "softmax":
+        if cfg.renorm:
+            z = np.exp(sel_l - sel_l.max(axis=1, keepdims=True))
+            g = z / z.sum(axis=1, keepdims=True)
+        else:
+            g = np.take_along_axis(softmax_probs(l), idx.astype(np.int64), axis=1)
+    else:
+        s = np.asarray(sigmoid_scores(l, exact), F64)
+        sel_s = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+        g = sel_s / sel_s.sum(axis=1, keepdims=True) if cfg.renorm else sel_s
+    g = g * cfg.scale
+    return g if exact else g.astype(F32)
+
+
+def route(x, w_router, bias, cfg, storage: str = None) -> dict:
+    """Router stage on the tokens in x: logits, idx, gates (and full softmax
+    probabilities when the score is softmax)."""
+    exact = storage == "f64"
+    logits = router_logits(x, w_router, "f64" if exact else "f32")
+    keys = selection_keys(logits, cfg, bias, exact)
+    idx = select_topk(keys, cfg)
+    gates = gates_from_selection(logits, idx, cfg, exact)
+    out = {"logits": logits, "keys": keys, "idx": idx, "gates": gates}
+    if cfg.score == "softmax":
+        out["probs"] = softmax_probs(logits)
+    else:
+        out["scores"] = sigmoid_scores(logits, exact)
+    return out
+
+
+def expert_counts(idx, E: int) -> np.ndarray:
+    c = np.zeros(E, dtype=np.int64)
+    for e in np.asarray(idx).ravel():
+        c[e] += 1
+    return c.astype(np.int32)
+
+
+def aux_loss(probs, counts, T: int, k: int, coeff: float) -> float:
+    """Load-balancing loss (R8): coeff * E * sum_e f_e * Pbar_e with
+    f_e = c_e/(T k) the fraction of assignments and Pbar_e the mean probability."""
+    E = probs.shape[1]
+    if T == 0:
+        return 0.0
+    f = np.asarray(counts, F64) / (T * k)
+    pbar = np.asarray(probs, F64).sum(axis=0) / T
+    return float(coeff * E * np.sum(f * pbar))
+
+
+# ----------------------------------------------------------------------------
+# Dispatch on one GPU: permutation into expert-contiguous rows
+# ----------------------------------------------------------------------------
+def permutation(idx, E: int) -> dict:
+    """Stable counting sort of (token, choice) pairs by expert (R9, R10).
+
+    offsets[e] = number of assignments to experts < e; the rows of expert e are
+    offsets[e] .. offsets[e+1]-1, filled by ascending token id;
+    row_id_map[t, j] = row of (t, j); src_token[row] = t.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counts = expert_counts(idx, E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    next_row = offsets[:E].copy()
+    row_id_map = np.empty((T, k), dtype=np.int32)
+    src_token = np.empty(T * k, dtype=np.int32)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            row_id_map[t, j] = next_row[e]
+            src_token[next_row[e]] = t
+            next_row[e] += 1
+    return {"counts": counts, "offsets": offsets.astype(np.int32),
+            "row_id_map": row_id_map, "src_token": src_token}
+
+
+def permute_rows(x, src_token) -> np.ndarray:
+    """Xp[row] = x[src_token[row]]: the one permuted copy of the activations."""
+    return np.asarray(x)[np.asarray(src_token, dtype=np.int64)]
+
+
+# ----------------------------------------------------------------------------
+# Experts: SwiGLU FFNs
+# ----------------------------------------------------------------------------
+def silu(h):
+    return h / (1.0 + np.exp(-h))
+
+
+def swiglu_ffn_fwd(xe, w13_e, w2_e, storage: str) -> dict:
+    """One SwiGLU FFN on rows xe [n, d] with W13 [2f, d] (gate rows then up
+    rows) and W2 [d, f]:  H = xe Wg^T, U = xe Wu^T, A = silu(H) * U, Y = A W2^T.
+    H and U are kept as stored (for backward); A is formed from the unrounded
+    H, U and then stored; Y is stored."""
+    f = w2_e.shape[1]
+    xe = np.asarray(xe, F64)
+    w13_e = np.asarray(w13_e, F64)
+    h = xe @ w13_e[:f].T
+    u = xe @ w13_e[f:].T
+    a = store(silu(h) * u, storage)
+    y = store(a @ np.asarray(w2_e, F64).T, storage)
+    return {"H": store(h, storage), "U": store(u, storage), "A": a, "Y": y}
+
+
+def swiglu_ffn_bwd(xe, H, U, A, dY, w13_e, w2_e, storage: str) -> dict:
+    """Backward of swiglu_ffn_fwd given the stored H, U, A and the incoming dY:
+      dA  = dY W2                       dW2 = dY^T A
+      dH  = dA * U * sig(H) * (1 + H (1 - sig(H)))      (d silu)
+      dU  = dA * silu(H)
+      dX  = dH Wg + dU Wu               dWg = dH^T X,  dWu = dU^T X
+    dA stays unrounded (it lives only inside the producing kernel); dH, dU, dX
+    and the weight gradients are stored."""
+    f = w2_e.shape[1]
+    dY = np.asarray(dY, F64)
+    H = np.asarray(H, F64)
+    U = np.asarray(U, F64)
+    w13_e = np.asarray(w13_e, F64)
+    dA = dY @ np.asarray(w2_e, F64)
+    dW2 = store(dY.T @ np.asarray(A, F64), storage)
+    sig = 1.0 / (1.0 + np.exp(-H))
+    dH = store(dA * U * sig * (1.0 + H * (1.0 - sig)), storage)
+    dU = store(dA * H * sig, storage)
+    dHU = np.concatenate([dH, dU], axis=1)
+    xe = np.asarray(xe, F64)
+    dX_unrounded = dHU @ w13_e
+    dW13 = store(dHU.T @ xe, storage)
+    return {"dA": dA, "dH": dH, "dU": dU, "dX32": dX_unrounded,
+            "dX": store(dX_unrounded, storage), "dW13": dW13, "dW2": dW2}
+
+
+# ----------------------------------------------------------------------------
+# Combine and the whole layer
+# ----------------------------------------------------------------------------
+def combine(Yp, gates, row_id_map, Ys, storage: str) -> np.ndarray:
+    """y[t] = sum_{j<k} g[t,j] * Yp[row(t,j)]  (+ Ys[t]), summed in j order and
+    stored once (R13)."""
+    T, k = row_id_map.shape
+    y = np.zeros((T, Yp.shape[1]), F64)
+    for j in range(k):
+        y += np.asarray(gates, F64)[:, j:j + 1] * Yp[row_id_map[:, j].astype(np.int64)]
+    if Ys is not None:
+        y += Ys
+    return store(y, storage)
+
+
+def layer_forward(inp: dict, cfg, storage: str = None) -> dict:
+    """The whole layer: Route -> permute -> grouped SwiGLU experts (+ shared
+    expert) -> unpermute/combine.  `inp` holds numpy/torch CPU arrays as made
+    by moe_inputs.make_inputs."""
+    storage = storage or storage_of(cfg)
+    x = _np(inp["x"])
+    T = x.shape[0]
+    r = route(x, _np(inp["w_router"]), _np(inp.get("bias")), cfg, storage)
+    p = permutation(r["idx"], cfg.E)
+    Xp = permute_rows(x, p["src_token"])
+    rows, f = T * cfg.k, cfg.f
+    H = np.zeros((rows, f)); U = np.zeros((rows, f)); A = np.zeros((rows, f))
+    Yp = np.zeros((rows, cfg.d))
+    w13, w2 = inp["w13"], inp["w2"]
+    off = p["offsets"]
+    for e in range(cfg.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        o = swiglu_ffn_fwd(Xp[lo:hi], _np(w13[e]), _np(w2[e]), storage)
+        H[lo:hi], U[lo:hi], A[lo:hi], Yp[lo:hi] = o["H"], o["U"], o["A"], o["Y"]
+    out = dict(r)
+    out.update(p)
+    out.update({"Xp": Xp, "H": H, "U": U, "A": A, "Yp": Yp})
+    Ys = None
+    if cfg.f_shared > 0:
+        s = swiglu_ffn_fwd(x, _np(inp["ws13"]), _np(inp["ws2"]), storage)
+        out.update({"Hs": s["H"], "Us": s["U"], "As": s["A"], "Ys": s["Y"]})
+        Ys = s["Y"]
+    out["y"] = combine(Yp, r["gates"], p["row_id_map"], Ys, storage)
+    if cfg.aux_coeff != 0.0:
+        out["aux"] = aux_loss(r["probs"], p["counts"], T, cfg.k, cfg.aux_coeff)
+    return out
+
+
+def router_backward(logits, idx, gates, d_gates, counts, cfg, d_aux: float = 1.0,
+                    exact: bool = False) -> np.ndarray:
+    """d loss / d logits, routing held fixed (top-k is piecewise constant and the
+    selection bias receives no gradient).
+
+    softmax + renorm:  dl_m = g_m (dg_m - sum_j g_j dg_j) on the selection
+    softmax, no renorm: dl = p * (dg_full - sum_e p_e dg_full_e)
+    aux (softmax):     dl[t,e] += d_aux * p[t,e] * (a_e - sum_e' p[t,e'] a_e'),
+                       a_e = coeff * E * f_e / T
+    sigmoid:           S = sum s_sel, ds_m = (scale/S) (dg_m - sum_j dg_j s_j / S)
+                       (renorm), ds_m = scale * dg_m (no renorm); dl = ds s (1-s)
+    """
+    l = np.asarray(logits, F64)
+    T, E = l.shape
+    ii = idx.astype(np.int64)
+    dg = np.asarray(d_gates, F64)
+    g = np.asarray(gates, F64) / cfg.scale          # unscaled gate values
+    dgs = dg * cfg.scale                            # gradient w.r.t. unscaled gates
+    dl = np.zeros((T, E), F64)
+    if cfg.score == "softmax":
+        if cfg.renorm:
+            inner = np.sum(g * dgs, axis=1, keepdims=True)
+            np.put_along_axis(dl, ii, g * (dgs - inner), axis=1)
+        else:
+            p = softmax_probs(l)
+            full = np.zeros((T, E), F64)
+            np.put_along_axis(full, ii, dgs, axis=1)
+            dl = p * (full - np.sum(p * full, axis=1, keepdims=True))
+        if cfg.aux_coeff != 0.0 and T > 0:
+            p = softmax_probs(l)
+            a = cfg.aux_coeff * E * (np.asarray(counts, F64) / (T * cfg.k)) / T
+            dl += d_aux * p * (a[None, :] - np.sum(p * a[None, :], axis=1, keepdims=True))
+    else:
+        s = np.asarray(sigmoid_scores(l, exact), F64)
+        sel = np.take_along_axis(s, ii, axis=1)
+        if cfg.renorm:
+            S = sel.sum(axis=1, keepdims=True)
+            ds_sel = (dgs - np.sum(dgs * sel, axis=1, keepdims=True) / S) / S
+        else:
+            ds_sel = dgs
+        ds = np.zeros((T, E), F64)
+        np.put_along_axis(ds, ii, ds_sel, axis=1)
+        dl = ds * s * (1.0 - s)
+    return dl
+
+
+def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
+                   storage: str = None) -> dict:
+    """Gradients of <y, dy> (+ d_aux * aux) w.r.t. x, the router weight and all
+    expert weights, for the forward pass `fwd` of layer_forward."""
+    storage = storage or storage_of(cfg)
+    exact = storage == "f64"
+    x = _np(inp["x"])
+    dy = _np(inp["dy"])
+    T, d = x.shape
+    rmap = fwd["row_id_map"].astype(np.int64)
+    gates = np.asarray(fwd["gates"], F64)
+    Yp = fwd["Yp"]
+    # combine backward: dYp[row(t,j)] = g[t,j] dy[t]; dg[t,j] = <dy[t], Yp[row]>
+    dYp = np.zeros_like(Yp)
+    d_gates = np.zeros((T, cfg.k), F64)
+    for j in range(cfg.k):
+        dYp[rmap[:, j]] = gates[:, j:j + 1] * dy
+        d_gates[:, j] = np.sum(dy * Yp[rmap[:, j]], axis=1)
+    dYp = store(dYp, storage)
+    if not exact:
+        d_gates = d_gates.astype(F32)
+    rows = T * cfg.k
+    dHU = np.zeros((rows, 2 * cfg.f))
+    dXp32 = np.zeros((rows, d))
+    dXp = np.zeros((rows, d))
+    dw13 = np.zeros(inp["w13"].shape)
+    dw2 = np.zeros(inp["w2"].shape)
+    off = fwd["offsets"]
+    Xp = fwd["Xp"]
+    for e in range(cfg.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue            # empty expert: exact zero weight gradients
+        b = swiglu_ffn_bwd(Xp[lo:hi], fwd["H"][lo:hi], fwd["U"][lo:hi], fwd["A"][lo:hi],
+                           dYp[lo:hi], _np(inp["w13"][e]), _np(inp["w2"][e]), storage)
+        dHU[lo:hi] = np.concatenate([b["dH"], b["dU"]], axis=1)
+        dXp32[lo:hi], dXp[lo:hi] = b["dX32"], b["dX"]
+        dw13[e], dw2[e] = b["dW13"], b["dW2"]
+    out = {"dYp": dYp, "d_gates": d_gates, "dHU": dHU, "dXp": dXp,
+           "dw13": dw13, "dw2": dw2}
+    dx_partial = np.zeros((T, d))
+    if cfg.f_shared > 0:
+        s = swiglu_ffn_bwd(x, fwd["Hs"], fwd["Us"], fwd["As"], dy,
+                           _np(inp["ws13"]), _np(inp["ws2"]), storage)
+        out.update({"dHUs": np.concatenate([s["dH"], s["dU"]], axis=1),
+                    "dws13": s["dW13"], "dws2": s["dW2"]})
+        dx_partial += s["dX32"]
+    dl = router_backward(fwd["logits"], fwd["idx"], fwd["gates"], d_gates,
+                         fwd["counts"], cfg, d_aux, exact)
+    out["d_logits"] = dl if exact else dl.astype(F32)
+    out["dw_router"] = store(dl.T @ x, storage)
+    dx_partial += dl @ _np(inp["w_router"])
+    # permute backward: dx[t] = partial[t] + sum_j dXp[row(t,j)], stored once
+    dx = dx_partial.copy()
+    for j in range(cfg.k):
+        dx += dXp[rmap[:, j]]
+    out["dx"] = store(dx, storage)
+    return out
+
+
+def _np(a):
+    """torch tensor / numpy array -> float64 numpy array (None passes through)."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        a = a.detach().to("cpu")
+        if str(a.dtype) == "torch.bfloat16":
+            a = a.float()
+        a = a.double().numpy()
+    return np.asarray(a, F64)
