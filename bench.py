@@ -1,0 +1,223 @@
+"""Benchmark: one MoE layer, forward + backward, at the DeepSeek-V3 shape on one
+MI355X, through the C ABI of libmoe_gfx950.
+
+    python bench.py [--steps K] [--warmup W] [--workload deepseek_v3] [--no-cpu-baseline]
+
+A step is one full pass of the layer over one batch: route -> permute ->
+grouped SwiGLU experts (+ shared expert) -> combine, then the backward in
+reverse (combine, experts, router, permute).  Inputs are seeded synthetic
+tensors already resident in HBM when the timed region starts.  Prints ONE JSON
+line.  Per-kernel durations come from HIP events that the library records
+around each kernel on its own stream during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_inputs as mi  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def step_flops(cfg: mi.MoEConfig, backward: bool = True) -> float:
+    """Algorithmic FLOPs of one layer pass: router 2TdE, routed experts 6Tk d f,
+    shared expert 6 T d f_s; the backward costs twice the forward.  Elementwise
+    work is not counted, nor padded tile rows."""
+    fwd = 2.0 * cfg.T * cfg.d * cfg.E + 6.0 * cfg.T * cfg.k * cfg.d * cfg.f + 6.0 * cfg.T * cfg.d * cfg.f_shared
+    return fwd * (3.0 if backward else 1.0)
+
+
+def kernel_work(cfg: mi.MoEConfig, counts) -> dict:
+    """Algorithmic (flops, HBM bytes) per launch of each expert GEMM kernel:
+    every non-empty expert's weights read once, activations read and written
+    once, weight gradients written for every expert (bf16 = 2 bytes)."""
+    B = 2
+    rows, d, f, fs, T, E = cfg.T * cfg.k, cfg.d, cfg.f, cfg.f_shared, cfg.T, cfg.E
+    ne = int((counts > 0).sum())
+    w13, w2 = ne * 2 * f * d * B, ne * d * f * B
+    out = {
+        "gemm_swiglu_fwd": (2.0 * rows * d * 2 * f, w13 + rows * d * B + rows * f * B + rows * 2 * f * B),
+        "gemm_down_fwd": (2.0 * rows * f * d, w2 + rows * f * B + rows * d * B),
+        "gemm_down_dgrad_swiglu_bwd": (2.0 * rows * d * f, w2 + rows * d * B + 2 * rows * 2 * f * B),
+        "gemm_wgrad_down": (2.0 * rows * d * f, rows * d * B + rows * f * B + E * d * f * B),
+        "gemm_gateup_dgrad": (2.0 * rows * 2 * f * d, w13 + rows * 2 * f * B + rows * d * B),
+        "gemm_wgrad_gateup": (2.0 * rows * 2 * f * d, rows * 2 * f * B + rows * d * B + E * 2 * f * d * B),
+    }
+    if fs:
+        out.update({
+            "gemm_swiglu_fwd_shared": (2.0 * T * d * 2 * fs, 2 * fs * d * B + T * d * B + T * fs * B + T * 2 * fs * B),
+            "gemm_down_fwd_shared": (2.0 * T * fs * d, d * fs * B + T * fs * B + T * d * B),
+            "gemm_down_dgrad_swiglu_bwd_shared": (2.0 * T * d * fs, d * fs * B + T * d * B + 2 * T * 2 * fs * B),
+            "gemm_wgrad_down_shared": (2.0 * T * d * fs, T * d * B + T * fs * B + d * fs * B),
+            "gemm_gateup_dgrad_shared": (2.0 * T * 2 * fs * d, 2 * fs * d * B + T * 2 * fs * B + T * d * 4),
+            "gemm_wgrad_gateup_shared": (2.0 * T * 2 * fs * d, T * 2 * fs * B + T * d * B + 2 * fs * d * B),
+        })
+    return out
+
+
+def cpu_baseline(cfg, dev_inp, sample_tokens: int) -> dict:
+    """Time the CPU oracle (as it stands) on the first `sample_tokens` tokens of
+    the same workload: full router over all experts, the sampled tokens' experts
+    and the shared expert, forward and backward."""
+    from oracle import moe_oracle as O
+    import numpy as np
+
+    Ts = sample_tokens
+    scfg = cfg.with_(T=Ts)
+    x = dev_inp["x"][:Ts].float().cpu()
+    wr = dev_inp["w_router"].float().cpu()
+    bias = None if dev_inp["bias"] is None else dev_inp["bias"].cpu()
+    # which experts the sample reaches (routing input only; the timed run routes again)
+    r = O.route(O._np(x), O._np(wr), O._np(bias), scfg)
+    used = sorted(set(np.asarray(r["idx"]).ravel().tolist()))
+
+    class Experts:
+        """Host copies of the experts the sample uses (bf16 values, copied
+        before timing); indexing any other expert is an error."""
+        def __init__(self, t):
+            self.shape = tuple(t.shape)
+            self.h = {e: t[e].cpu() for e in used}
+
+        def __getitem__(self, e):
+            return self.h[e]
+
+    inp = {"x": x, "w_router": wr, "bias": bias, "w13": Experts(dev_inp["w13"]),
+           "w2": Experts(dev_inp["w2"]), "dy": dev_inp["dy"][:Ts].float().cpu(),
+           "ws13": None if dev_inp["ws13"] is None else dev_inp["ws13"].cpu(),
+           "ws2": None if dev_inp["ws2"] is None else dev_inp["ws2"].cpu()}
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    fwd = O.layer_forward(inp, scfg)
+    O.layer_backward(inp, fwd, scfg, dense=False)
+    dt = time.perf_counter() - t0
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "tflops": step_flops(scfg) / dt / 1e12,
+            "sample": f"first {Ts} of {cfg.T} tokens of the {cfg.name} workload, fwd+bwd "
+                      f"({len(used)} experts reached + shared), numpy float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="deepseek_v3", choices=sorted(mi.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16)
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this layer runs on one GPU; multi-GPU sharding is not built "
+                                   "(see DESIGN.md: how the path would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    from mixture_experts_layer_limited_amd import LayerShape, MoELayer, _abi as abi
+
+    cfg = mi.CONFIGS[args.workload]
+    if cfg.dtype == "mxfp8":
+        raise SystemExit("the MXFP8 expert path is not built yet")
+    torch.cuda.set_device(0)
+    print(f"# generating {cfg.name} inputs on the GPU", file=sys.stderr, flush=True)
+    inp = mi.make_inputs(cfg, seed=args.seed, device="cuda", with_grad_inputs=True)
+    shape = LayerShape(T=cfg.T, d=cfg.d, E=cfg.E, k=cfg.k, f=cfg.f, f_shared=cfg.f_shared, score=cfg.score,
+                       n_group=cfg.n_group, topk_group=cfg.topk_group, renorm=cfg.renorm, scale=cfg.scale,
+                       aux_coeff=cfg.aux_coeff, dtype="f32" if cfg.dtype == "f32" else "bf16")
+    layer = MoELayer(shape, "cuda", backward=True)
+    a = inp
+
+    def step():
+        layer.forward(a["x"], a["w_router"], a["bias"], a["w13"], a["w2"], a["ws13"], a["ws2"])
+        layer.backward(a["dy"], a["x"], a["w_router"], a["w13"], a["w2"], a["ws13"], a["ws2"], d_aux=1.0)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    cap = 64 * max(args.steps, 1)
+    stream = torch.cuda.current_stream()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    abi.moe_trace_begin(cap)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    trace = abi.moe_trace_end(cap)
+    ms = t_start.elapsed_time(t_end) / max(args.steps, 1)
+    print("# timed steps done", file=sys.stderr, flush=True)
+
+    flops = step_flops(cfg)
+    tflops = flops / (ms * 1e-3) / 1e12
+    per_kernel = {}
+    for name, t in trace:
+        s = per_kernel.setdefault(name, [0.0, 0])
+        s[0] += t
+        s[1] += 1
+    kern = {n: {"avg_ms": round(v[0] / v[1], 4), "launches_per_step": round(v[1] / max(args.steps, 1), 2)}
+            for n, v in per_kernel.items()}
+    counts = layer.buf["counts"].cpu()
+    work = kernel_work(cfg, counts)
+    # dominant kernel: largest total time among the traced kernels
+    dom = max(per_kernel.items(), key=lambda kv: kv[1][0])[0]
+    roof = None
+    if dom in work:
+        fl, by = work[dom]
+        t = per_kernel[dom][0] / per_kernel[dom][1] * 1e-3
+        ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+        if fl / by < ridge:
+            ach = by / t / 1e9
+            roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "algorithmic_bytes": by, "algorithmic_flops": fl,
+                    "achieved_tflops": round(fl / t / 1e12, 1)}
+        else:
+            ach = fl / t / 1e12
+            roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "algorithmic_bytes": by, "algorithmic_flops": fl}
+        for n, (fl2, by2) in work.items():
+            if n in kern:
+                tt = kern[n]["avg_ms"] * 1e-3
+                if tt > 0:
+                    kern[n]["tflops"] = round(fl2 / tt / 1e12, 1)
+                    kern[n]["gbs"] = round(by2 / tt / 1e9, 1)
+
+    out = {
+        "metric": "MoE layer fwd+bwd TFLOPS & tokens/s at DSv3 shape, 1 MI355X; % MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} MoE layer fwd+bwd", "T": cfg.T, "d": cfg.d, "E": cfg.E,
+                   "k": cfg.k, "f": cfg.f, "f_shared": cfg.f_shared, "score": cfg.score,
+                   "n_group": cfg.n_group, "topk_group": cfg.topk_group, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "kernels": kern,
+        "expert_rows": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle on a token sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,270 @@
+/*
+ * libmoe_gfx950 -- one GPU's mixture-of-experts layer on AMD Instinct MI355X
+ * (gfx950), forward and backward, as a C ABI.
+ *
+ * The layer is y = sum over the top-k experts of g(x)_i * E_i(x) ("Scalable
+ * Training of Mixture-of-Experts Models with Megatron Core", summary page,
+ * "Problem Definition"), run in the stage order Router -> Dispatcher ->
+ * Experts -> Combiner (same page, "Pipeline Flow"; thelatestinai.com page,
+ * Figure 1).  On one GPU, dispatch and combine become a permutation of token
+ * rows into expert-contiguous order and its inverse.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is DEVICE memory unless stated otherwise; the
+ *   caller owns and allocates all of it (inputs, outputs, workspace).  The
+ *   library never allocates, frees or synchronises, never copies anything to
+ *   the host and only enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *   default stream).  Calls are asynchronous: device-side faults surface at the
+ *   caller's next synchronisation.
+ * - Matrices are row-major and contiguous.  "storage" means the element type
+ *   named by moe_cfg.dtype: float (MOE_F32) or bfloat16 (MOE_BF16, stored as
+ *   uint16_t bit patterns).  fp32 tensors (logits, gates, d_gates, d_logits,
+ *   dx_partial) are float in every mode.  Indices are int32.
+ * - Weights use the nn.Linear orientation [out, in]: w_router [E, d];
+ *   w13 [E, 2f, d] with rows 0..f-1 the gate projection and f..2f-1 the up
+ *   projection; w2 [E, d, f]; the shared expert ws13 [2 f_shared, d] and
+ *   ws2 [d, f_shared].
+ * - Rows of the permuted buffers ([T*k, .]) are expert-major: expert e owns rows
+ *   expert_offsets[e] .. expert_offsets[e+1]-1, tokens in ascending order inside
+ *   an expert.  Routing is dropless: exactly T*k rows, no capacity, no padding.
+ * - Every argument is validated on the host before anything is launched
+ *   (null pointers, shape limits, 16-byte alignment of storage matrices).  On
+ *   failure nothing is enqueued and a status is returned; moe_last_error() then
+ *   names the offending argument.  Indices produced by these calls are trusted:
+ *   out-of-range expert ids or row ids passed in by a caller are undefined.
+ * - Results are deterministic: no floating-point atomics, fixed reduction order.
+ *   topk_idx, expert_counts, expert_offsets, row_id_map and src_token are
+ *   bit-identical to any correct implementation of the rules below given the
+ *   same fp32 router logits.
+ * - Limits: 1 <= k <= E <= 256, d and f multiples of 8 (f_shared too), T*k and
+ *   every matrix dimension below 2^31 elements per row index.
+ */
+#ifndef MOE_GFX950_H
+#define MOE_GFX950_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad shape, misalignment    */
+  MOE_ERR_UNSUPPORTED = 2,        /* not a gfx950 device, dtype not built     */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_DEVICE = 4              /* a HIP call or kernel launch failed       */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+/* Shape and routing rule of one MoE layer (host memory). */
+typedef struct moe_cfg {
+  int64_t T;          /* tokens (batch x sequence, flattened)                */
+  int64_t d;          /* hidden size                                          */
+  int64_t E;          /* routed experts                                       */
+  int64_t k;          /* experts per token                                    */
+  int64_t f;          /* routed expert FFN width                              */
+  int64_t f_shared;   /* shared-expert FFN width, 0 = no shared expert        */
+  int32_t score;      /* moe_score                                            */
+  int32_t n_group;    /* expert groups for group-limited routing (1 = off)    */
+  int32_t topk_group; /* groups kept per token                                */
+  int32_t renorm;     /* 1: gates renormalised over the selected experts      */
+  float scale;        /* gate multiplier applied after renormalisation        */
+  float aux_coeff;    /* load-balancing loss coefficient (0 = off; softmax)   */
+  int32_t dtype;      /* moe_dtype of activations and weights                 */
+  int32_t reserved;   /* must be 0                                            */
+} moe_cfg;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/* Message describing the last failure of a call made on this host thread
+ * ("" if the last call succeeded).  Valid until the next call on the thread. */
+const char* moe_last_error(void);
+
+/* Checks that `device` is a gfx950 GPU and caches its properties.  Optional:
+ * every call performs the same check lazily on the current device. */
+moe_status moe_init(int device);
+
+/* Bytes of device workspace every call below needs for `cfg` (the same size
+ * serves all of them).  0 on an invalid cfg (see moe_last_error). */
+size_t moe_workspace_size(const moe_cfg* cfg);
+
+/* ---------------------------------------------------------------------------
+ * Router ("System Modules: Router": a learned linear layer producing a
+ * probability distribution and a top-k choice per token; Figure 2: linear
+ * projection, score function, top-k selection, load balancing).
+ *
+ *   logits[t,e] = sum_i x[t,i] w_router[e,i]     fp32 accumulation, stored fp32
+ *   softmax: selection key = the logit; p = softmax over all E (fp32)
+ *   sigmoid: s = fp32(1/(1+exp(-(double)l))); key = fp32(s + bias[e]); the
+ *            bias only steers selection
+ *   n_group > 1: experts split into n_group contiguous groups of E/n_group;
+ *            group score = fp32 sum of its two largest keys (its only key for
+ *            one-expert groups); the topk_group best groups (ties -> lower
+ *            group id) are eligible, the rest are not
+ *   topk_idx[t,:] = the k eligible experts by key descending, equal keys ->
+ *            lower expert id, in that order
+ *   gates:   softmax+renorm: softmax over the selected logits; softmax without
+ *            renorm: p of the selected experts; sigmoid: s_j / sum of selected s
+ *            (if renorm) -- all multiplied by cfg.scale
+ *   expert_counts[e] = number of (t, j) with topk_idx[t,j] == e
+ *   aux_loss (only if cfg.aux_coeff != 0; softmax only):
+ *            aux_coeff * E * sum_e (counts[e] / (T k)) * (sum_t p[t,e] / T)
+ *
+ * x [T,d] storage, w_router [E,d] storage, bias [E] fp32 or NULL;
+ * logits [T,E] fp32 written -- or, if x and w_router are both NULL, READ as
+ * precomputed router logits; topk_idx [T,k] int32, topk_gates [T,k] fp32,
+ * expert_counts [E] int32 written; aux_loss [1] fp32 written when aux is on,
+ * may be NULL otherwise.  T = 0 writes zero counts (and aux 0).
+ * ------------------------------------------------------------------------- */
+moe_status moe_router_topk(const moe_cfg* cfg, const void* x, const void* w_router,
+                           const float* bias, float* logits, int32_t* topk_idx,
+                           float* topk_gates, int32_t* expert_counts, float* aux_loss,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Permute ("System Modules: Dispatcher" on one GPU; memory-efficient
+ * permutation, Figure 7): a stable counting sort of the (token, choice) pairs
+ * by expert and one gather of the token rows.
+ *
+ *   expert_offsets[e] = number of assignments to experts < e  ([E+1] int32,
+ *                       expert_offsets[E] = T*k)
+ *   row_id_map[t,j]   = expert_offsets[e] + #{t' < t : e in topk_idx[t',:]},
+ *                       e = topk_idx[t,j]                          ([T,k] int32)
+ *   src_token[row]    = the token of that row                     ([T*k] int32)
+ *   x_perm[row,:]     = x[src_token[row],:]                       ([T*k,d] storage)
+ *
+ * x [T,d] storage, topk_idx [T,k] int32 (each row k distinct ids in [0,E)).
+ * x_perm is the only permuted copy of the activations kept by the layer.
+ * ------------------------------------------------------------------------- */
+moe_status moe_permute(const moe_cfg* cfg, const void* x, const int32_t* topk_idx,
+                       int32_t* expert_offsets, int32_t* row_id_map, int32_t* src_token,
+                       void* x_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Experts ("System Modules: Experts": FFNs run as a grouped GEMM over uneven
+ * expert sizes, "Key Terms: Grouped GEMM"; SwiGLU activation, Table 4; shared
+ * expert processing every token, Table 1 and Figure 40).
+ *
+ * For each expert e over its rows r in [off[e], off[e+1]) (empty experts
+ * skipped):
+ *   H = x_perm[r] w13[e][0:f]^T, U = x_perm[r] w13[e][f:2f]^T   (fp32 accumulate)
+ *   act[r]    = storage(silu(H) * U), silu(h) = h / (1 + exp(-h))
+ *   y_perm[r] = storage(act[r] w2[e]^T)
+ *   hu_save[r] = (storage(H) | storage(U))       [T*k, 2f], if non-NULL
+ * Shared expert (cfg.f_shared > 0): the same FFN with ws13/ws2 on every token
+ * of x, writing act_shared [T,fs], y_shared [T,d], hu_shared_save [T,2fs].
+ *
+ * x_perm [T*k,d], expert_offsets [E+1] (from moe_permute), w13, w2 storage;
+ * act [T*k,f] and y_perm [T*k,d] required; hu_save optional (needed by the
+ * backward call).  x, ws13, ws2, act_shared, y_shared required iff
+ * f_shared > 0; hu_shared_save optional.
+ * ------------------------------------------------------------------------- */
+moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm,
+                                   const int32_t* expert_offsets, const void* w13,
+                                   const void* w2, void* hu_save, void* act, void* y_perm,
+                                   const void* x, const void* ws13, const void* ws2,
+                                   void* hu_shared_save, void* act_shared, void* y_shared,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Unpermute-combine ("System Modules: Combiner": tokens go back to their
+ * original position and the gate-weighted sum is formed).
+ *   y[t] = storage( sum_{j=0}^{k-1} gates[t,j] * y_perm[row_id_map[t,j]]
+ *                   + y_shared[t] )        fp32 sum in j order, one rounding
+ * y_perm [T*k,d], row_id_map [T,k], topk_gates [T,k] fp32, y_shared [T,d] or
+ * NULL, y [T,d].
+ * ------------------------------------------------------------------------- */
+moe_status moe_unpermute_combine(const moe_cfg* cfg, const void* y_perm,
+                                 const int32_t* row_id_map, const float* topk_gates,
+                                 const void* y_shared, void* y, void* stream);
+
+/* ===========================================================================
+ * Backward.  Gradients of <y, dy> (+ d_aux * aux_loss).  Routing is held
+ * fixed (top-k is piecewise constant; the selection bias gets no gradient).
+ * Call order: combine_bwd -> grouped_gemm_swiglu_bwd -> router_topk_bwd ->
+ * permute_bwd.
+ * ========================================================================= */
+
+/* dy_perm[row_id_map[t,j]] = storage(gates[t,j] * dy[t])          [T*k,d]
+ * d_gates[t,j] = sum_i dy[t,i] * y_perm[row_id_map[t,j], i]      [T,k] fp32 */
+moe_status moe_unpermute_combine_bwd(const moe_cfg* cfg, const void* dy,
+                                     const void* y_perm, const int32_t* row_id_map,
+                                     const float* topk_gates, void* dy_perm,
+                                     float* d_gates, void* stream);
+
+/* Per expert e over its rows (weights of empty experts get exact zeros):
+ *   dA  = dy_perm w2[e]                      (fp32, never stored)
+ *   dH  = dA * U * sig(H) * (1 + H (1 - sig(H))),  dU = dA * silu(H)
+ *         (H, U read from hu_save) -> dhu [T*k, 2f] = (dH | dU), storage
+ *   dw2[e]  = dy_perm[rows]^T act[rows]                  [d, f]   storage
+ *   dx_perm = dhu w13[e]                                 [T*k, d] storage
+ *   dw13[e] = dhu[rows]^T x_perm[rows]                   [2f, d]  storage
+ * Shared expert (f_shared > 0), on all tokens with upstream gradient dy:
+ *   the same with ws13/ws2, hu_shared_save, act_shared, x -> dhu_shared,
+ *   dws13, dws2, and its input gradient dhu_shared ws13 written in fp32 to
+ *   dx_partial [T,d].  Without a shared expert dx_partial is zero-filled.
+ * dx_partial is consumed by moe_router_topk_bwd (accumulates) and
+ * moe_permute_bwd (reads). */
+moe_status moe_grouped_gemm_swiglu_bwd(const moe_cfg* cfg, const void* dy_perm,
+                                       const void* x_perm, const int32_t* expert_offsets,
+                                       const void* hu_save, const void* act,
+                                       const void* w13, const void* w2, void* dhu,
+                                       void* dx_perm, void* dw13, void* dw2,
+                                       const void* dy, const void* x,
+                                       const void* hu_shared_save, const void* act_shared,
+                                       const void* ws13, const void* ws2, void* dhu_shared,
+                                       float* dx_partial, void* dws13, void* dws2,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Router backward, from d_gates [T,k] fp32 (moe_unpermute_combine_bwd) and the
+ * scalar d_aux (host value; ignored when aux is off):
+ *   softmax+renorm: dl_m = scale q_m (dg_m - sum_j q_j dg_j) on the selection,
+ *                   q = gates / scale (the renormalised probabilities)
+ *   softmax, no renorm: dl = scale p (dg_full - sum_e p_e dg_full_e), dg_full
+ *                   the d_gates scattered to their experts (0 elsewhere)
+ *   aux:            dl[t,e] += d_aux p[t,e] (a_e - sum_e' p[t,e'] a_e'),
+ *                   a_e = aux_coeff E counts[e] / (T k T)
+ *   sigmoid:        ds_m = (scale/S)(dg_m - sum_j dg_j s_j / S), S = sum s_sel
+ *                   (renorm) or scale dg_m; dl = ds s (1 - s)
+ *   d_logits [T,E] fp32 written; dw_router [E,d] = d_logits^T x (storage);
+ *   dx_partial [T,d] fp32 += d_logits w_router.
+ * In bf16 mode the two router GEMMs consume d_logits rounded to bf16.
+ * logits/topk_idx/topk_gates/expert_counts are the forward call's outputs. */
+moe_status moe_router_topk_bwd(const moe_cfg* cfg, const void* x, const void* w_router,
+                               const float* logits, const int32_t* topk_idx,
+                               const float* topk_gates, const int32_t* expert_counts,
+                               const float* d_gates, float d_aux, float* d_logits,
+                               void* dw_router, float* dx_partial, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* dx[t] = storage( dx_partial[t] + sum_{j=0}^{k-1} dx_perm[row_id_map[t,j]] )
+ * (fp32 sum, j in order, one rounding).  dx_partial may be NULL (zeros). */
+moe_status moe_permute_bwd(const moe_cfg* cfg, const void* dx_perm,
+                           const int32_t* row_id_map, const float* dx_partial, void* dx,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing trace (a profiling aid; no computation depends on it).
+ * moe_trace_begin(capacity) starts a trace on the calling host thread: every
+ * kernel the library enqueues afterwards is bracketed by two HIP events
+ * recorded on that kernel's stream, for up to `capacity` kernels (later ones
+ * are not traced).  It creates 2*capacity events (no device memory).
+ * moe_trace_end(names, ms, capacity) stops the trace, waits for the recorded
+ * events, writes up to `capacity` kernel names (static strings) and durations
+ * in milliseconds, destroys the events and returns the number of kernels
+ * traced (or -1 on a HIP error).  Do not trace inside a hipGraph capture.
+ * ------------------------------------------------------------------------- */
+moe_status moe_trace_begin(int capacity);
+int moe_trace_end(const char** names, float* ms, int capacity);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_GFX950_H */

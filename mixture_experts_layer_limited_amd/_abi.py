@@ -1,0 +1,209 @@
+"""ctypes binding of libmoe_gfx950 (include/moe.h).
+
+Argument marshalling only: each function takes torch tensors (device memory)
+or None, passes their data pointers and the current HIP stream to the C call
+of the same name, and raises MoEError on a non-zero status.  No computation of
+the layer happens here, and there is no fallback: if the shared library is not
+built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_gfx950.so")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+
+
+class moe_cfg(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("f", ctypes.c_int64), ("f_shared", ctypes.c_int64),
+                ("score", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("renorm", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("aux_coeff", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {_status_name(status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_SIGS = {
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_init": (ctypes.c_int, [ctypes.c_int]),
+    "moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(moe_cfg)]),
+    "moe_router_topk": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]),
+    "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 6 + [_P, ctypes.c_size_t, _P]),
+    "moe_grouped_gemm_swiglu": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 13 + [_P, ctypes.c_size_t, _P]),
+    "moe_unpermute_combine": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 5 + [_P]),
+    "moe_unpermute_combine_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 6 + [_P]),
+    "moe_grouped_gemm_swiglu_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 21 + [_P, ctypes.c_size_t, _P]),
+    "moe_router_topk_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 8 + [ctypes.c_float] + [_P] * 3
+                            + [_P, ctypes.c_size_t, _P]),
+    "moe_permute_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 4 + [_P]),
+    "moe_trace_begin": (ctypes.c_int, [ctypes.c_int]),
+    "moe_trace_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
+                                     ctypes.c_int]),
+}
+
+
+def lib():
+    """Load libmoe_gfx950.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_layer_limited_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().moe_status_string(s).decode()
+    except Exception:
+        return str(s)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoEError(status, where, lib().moe_last_error().decode())
+
+
+def make_cfg(T, d, E, k, f, f_shared=0, score="softmax", n_group=1, topk_group=1, renorm=True,
+             scale=1.0, aux_coeff=0.0, dtype="bf16") -> moe_cfg:
+    return moe_cfg(T=T, d=d, E=E, k=k, f=f, f_shared=f_shared,
+                   score=MOE_SCORE_SIGMOID if score == "sigmoid" else MOE_SCORE_SOFTMAX,
+                   n_group=n_group, topk_group=topk_group, renorm=int(bool(renorm)),
+                   scale=scale, aux_coeff=aux_coeff,
+                   dtype=MOE_F32 if dtype == "f32" else MOE_BF16, reserved=0)
+
+
+def moe_status_string(s: int) -> str:
+    return lib().moe_status_string(s).decode()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_init(device: int = 0):
+    _check(lib().moe_init(device), "moe_init")
+
+
+def moe_workspace_size(cfg: moe_cfg) -> int:
+    n = lib().moe_workspace_size(ctypes.byref(cfg))
+    if n == 0:
+        raise MoEError(MOE_ERR_INVALID_ARGUMENT, "moe_workspace_size", moe_last_error())
+    return n
+
+
+def _ws(ws):
+    return (_ptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
+
+
+def moe_router_topk(cfg, x, w_router, bias, logits, topk_idx, topk_gates, expert_counts, aux_loss,
+                    workspace, stream=None):
+    w, n = _ws(workspace)
+    _check(lib().moe_router_topk(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits),
+                                 _ptr(topk_idx), _ptr(topk_gates), _ptr(expert_counts), _ptr(aux_loss),
+                                 w, n, _stream(stream)), "moe_router_topk")
+
+
+def moe_permute(cfg, x, topk_idx, expert_offsets, row_id_map, src_token, x_perm, workspace, stream=None):
+    w, n = _ws(workspace)
+    _check(lib().moe_permute(ctypes.byref(cfg), _ptr(x), _ptr(topk_idx), _ptr(expert_offsets),
+                             _ptr(row_id_map), _ptr(src_token), _ptr(x_perm), w, n, _stream(stream)),
+           "moe_permute")
+
+
+def moe_grouped_gemm_swiglu(cfg, x_perm, expert_offsets, w13, w2, hu_save, act, y_perm, x, ws13, ws2,
+                            hu_shared_save, act_shared, y_shared, workspace, stream=None):
+    w, n = _ws(workspace)
+    _check(lib().moe_grouped_gemm_swiglu(
+        ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_offsets), _ptr(w13), _ptr(w2), _ptr(hu_save),
+        _ptr(act), _ptr(y_perm), _ptr(x), _ptr(ws13), _ptr(ws2), _ptr(hu_shared_save),
+        _ptr(act_shared), _ptr(y_shared), w, n, _stream(stream)), "moe_grouped_gemm_swiglu")
+
+
+def moe_unpermute_combine(cfg, y_perm, row_id_map, topk_gates, y_shared, y, stream=None):
+    _check(lib().moe_unpermute_combine(ctypes.byref(cfg), _ptr(y_perm), _ptr(row_id_map),
+                                       _ptr(topk_gates), _ptr(y_shared), _ptr(y), _stream(stream)),
+           "moe_unpermute_combine")
+
+
+def moe_unpermute_combine_bwd(cfg, dy, y_perm, row_id_map, topk_gates, dy_perm, d_gates, stream=None):
+    _check(lib().moe_unpermute_combine_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(y_perm), _ptr(row_id_map),
+                                           _ptr(topk_gates), _ptr(dy_perm), _ptr(d_gates),
+                                           _stream(stream)), "moe_unpermute_combine_bwd")
+
+
+def moe_grouped_gemm_swiglu_bwd(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, w13, w2, dhu,
+                                dx_perm, dw13, dw2, dy, x, hu_shared_save, act_shared, ws13, ws2,
+                                dhu_shared, dx_partial, dws13, dws2, workspace, stream=None):
+    w, n = _ws(workspace)
+    _check(lib().moe_grouped_gemm_swiglu_bwd(
+        ctypes.byref(cfg), _ptr(dy_perm), _ptr(x_perm), _ptr(expert_offsets), _ptr(hu_save), _ptr(act),
+        _ptr(w13), _ptr(w2), _ptr(dhu), _ptr(dx_perm), _ptr(dw13), _ptr(dw2), _ptr(dy), _ptr(x),
+        _ptr(hu_shared_save), _ptr(act_shared), _ptr(ws13), _ptr(ws2), _ptr(dhu_shared),
+        _ptr(dx_partial), _ptr(dws13), _ptr(dws2), w, n, _stream(stream)), "moe_grouped_gemm_swiglu_bwd")
+
+
+def moe_router_topk_bwd(cfg, x, w_router, logits, topk_idx, topk_gates, expert_counts, d_gates, d_aux,
+                        d_logits, dw_router, dx_partial, workspace, stream=None):
+    w, n = _ws(workspace)
+    _check(lib().moe_router_topk_bwd(
+        ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(topk_idx), _ptr(topk_gates),
+        _ptr(expert_counts), _ptr(d_gates), float(d_aux), _ptr(d_logits), _ptr(dw_router),
+        _ptr(dx_partial), w, n, _stream(stream)), "moe_router_topk_bwd")
+
+
+def moe_permute_bwd(cfg, dx_perm, row_id_map, dx_partial, dx, stream=None):
+    _check(lib().moe_permute_bwd(ctypes.byref(cfg), _ptr(dx_perm), _ptr(row_id_map), _ptr(dx_partial),
+                                 _ptr(dx), _stream(stream)), "moe_permute_bwd")
+
+
+def moe_trace_begin(capacity: int):
+    _check(lib().moe_trace_begin(capacity), "moe_trace_begin")
+
+
+def moe_trace_end(capacity: int):
+    """Stop the kernel trace; returns [(kernel name, milliseconds), ...] in launch order."""
+    names = (ctypes.c_char_p * capacity)()
+    ms = (ctypes.c_float * capacity)()
+    n = lib().moe_trace_end(names, ms, capacity)
+    if n < 0:
+        raise MoEError(MOE_ERR_DEVICE, "moe_trace_end", "reading the trace events failed")
+    n = min(n, capacity)
+    return [(names[i].decode(), float(ms[i])) for i in range(n)]

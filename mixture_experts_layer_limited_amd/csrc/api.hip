@@ -1,0 +1,498 @@
+// C ABI of libmoe_gfx950: host-side validation and orchestration of the
+// kernels.  Nothing here allocates device memory or synchronises; every call
+// checks its arguments before the first launch and reports failures through
+// moe_status and moe_last_error().
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+// ---- device check (cached per device) --------------------------------------
+constexpr int kMaxDevices = 64;
+struct DevInfo {
+  bool checked = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+DevInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+moe_status check_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_INVALID_ARGUMENT, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo& di = g_dev[dev];
+  if (!di.checked) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties(%d): %s", dev, hipGetErrorString(e));
+    di.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    di.cus = prop.multiProcessorCount;
+    di.checked = true;
+    if (!di.gfx950) {
+      return fail(MOE_ERR_UNSUPPORTED, "device %d is %s, this library is built for gfx950", dev,
+                  prop.gcnArchName);
+    }
+  }
+  if (!di.gfx950) return fail(MOE_ERR_UNSUPPORTED, "device %d is not a gfx950 GPU", dev);
+  return MOE_OK;
+}
+
+moe_status check_current_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  return check_device(dev);
+}
+
+// ---- argument validation ---------------------------------------------------
+moe_status check_cfg(const moe_cfg* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg is NULL");
+  if (c->reserved != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.reserved must be 0");
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "cfg.dtype %d not supported", c->dtype);
+  if (c->T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.T = %lld < 0", (long long)c->T);
+  if (c->E < 1 || c->E > kMaxExperts)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.E = %lld outside [1, %d]", (long long)c->E, kMaxExperts);
+  if (c->k < 1 || c->k > c->E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.k = %lld outside [1, E=%lld]", (long long)c->k,
+                (long long)c->E);
+  if (c->d < 8 || c->d % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.d = %lld must be a positive multiple of 8", (long long)c->d);
+  if (c->f < 8 || c->f % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.f = %lld must be a positive multiple of 8", (long long)c->f);
+  if (c->f_shared < 0 || c->f_shared % 8)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.f_shared = %lld must be 0 or a multiple of 8", (long long)c->f_shared);
+  if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.score = %d unknown", c->score);
+  if (c->n_group < 1 || c->E % c->n_group)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.n_group = %d must divide E = %lld", c->n_group, (long long)c->E);
+  if (c->topk_group < 1 || c->topk_group > c->n_group)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.topk_group = %d outside [1, n_group=%d]", c->topk_group, c->n_group);
+  if ((int64_t)c->topk_group * (c->E / c->n_group) < c->k)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "topk_group * E / n_group = %lld < k = %lld",
+                (long long)c->topk_group * (c->E / c->n_group), (long long)c->k);
+  if (c->renorm != 0 && c->renorm != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.renorm must be 0 or 1");
+  if (c->aux_coeff != 0.0f && c->score != MOE_SCORE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "the aux loss is defined for the softmax score only");
+  const int64_t lim = (int64_t)1 << 31;
+  if (c->T * c->k >= lim || c->d >= lim / 8 || c->f >= lim / 8 || c->f_shared >= lim / 8)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shape too large (T*k, d, f must stay below 2^31 / 8)");
+  return MOE_OK;
+}
+
+#define REQ(p)                                                                          \
+  do {                                                                                  \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARGUMENT, "argument '%s' must not be NULL", #p); \
+  } while (0)
+#define ALIGNED(p)                                                                            \
+  do {                                                                                        \
+    if ((p) && ((uintptr_t)(p) & 15))                                                         \
+      return fail(MOE_ERR_INVALID_ARGUMENT, "argument '%s' must be 16-byte aligned", #p);      \
+  } while (0)
+#define CHECK(call)                                                                     \
+  do {                                                                                  \
+    moe_status s_ = (call);                                                             \
+    if (s_ != MOE_OK) return s_;                                                        \
+  } while (0)
+// ---- kernel timing trace -----------------------------------------------------
+struct Trace {
+  bool on = false;
+  int cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;          // 2 per kernel: before, after
+  std::vector<const char*> names;
+};
+thread_local Trace g_trace;
+
+inline void trace_pre(hipStream_t st) {
+  if (g_trace.on && g_trace.n < g_trace.cap) hipEventRecord(g_trace.ev[2 * g_trace.n], st);
+}
+inline void trace_post(const char* name, hipStream_t st) {
+  if (g_trace.on && g_trace.n < g_trace.cap) {
+    hipEventRecord(g_trace.ev[2 * g_trace.n + 1], st);
+    g_trace.names[g_trace.n++] = name;
+  }
+}
+
+// every launcher enqueues exactly one kernel (or none for empty work)
+#define LAUNCH_NAMED(name, call)                                                                      \
+  do {                                                                                                \
+    trace_pre(st);                                                                                    \
+    hipError_t e_ = (call);                                                                           \
+    trace_post(name, st);                                                                             \
+    if (e_ != hipSuccess) return fail(MOE_ERR_DEVICE, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+#define LAUNCH(call) LAUNCH_NAMED(#call, call)
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int64_t ranges(int64_t T) { return (T + kPermTokensPerRange - 1) / kPermTokensPerRange; }
+inline int64_t router_blocks(int64_t T) { return (T + kRouterTokensPerBlock - 1) / kRouterTokensPerBlock; }
+inline int64_t pad8(int64_t e) { return (e + 7) & ~int64_t(7); }
+inline size_t elt(const moe_cfg* c) { return c->dtype == MOE_F32 ? 4 : 2; }
+
+size_t ws_bytes_for(const moe_cfg* c) {
+  size_t router = 2 * align256((size_t)router_blocks(c->T) * c->E * 4);
+  size_t perm = align256((size_t)ranges(c->T) * c->E * 4);
+  size_t gemm = align256((size_t)(c->E + 2) * 4);
+  size_t rbwd = align256((size_t)c->T * pad8(c->E) * elt(c));
+  size_t m = router;
+  if (perm > m) m = perm;
+  if (gemm > m) m = gemm;
+  if (rbwd > m) m = rbwd;
+  return m < 256 ? 256 : m;
+}
+
+moe_status check_ws(const moe_cfg* c, void* ws, size_t bytes) {
+  size_t need = ws_bytes_for(c);
+  if (!ws) return fail(MOE_ERR_INVALID_ARGUMENT, "argument 'workspace' must not be NULL");
+  ALIGNED(ws);
+  if (bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", bytes, need);
+  return MOE_OK;
+}
+
+RouterParams router_params(const moe_cfg* c) {
+  RouterParams p;
+  p.T = (int)c->T; p.E = (int)c->E; p.k = (int)c->k; p.score = c->score;
+  p.n_group = c->n_group; p.topk_group = c->topk_group; p.renorm = c->renorm;
+  p.scale = c->scale; p.aux_coeff = c->aux_coeff;
+  return p;
+}
+
+template <class T>
+moe_status router_topk_impl(const moe_cfg* c, const void* x, const void* w_router, const float* bias,
+                            float* logits, int32_t* idx, float* gates, int32_t* counts, float* aux,
+                            void* ws, hipStream_t st) {
+  RouterParams p = router_params(c);
+  const int nblk = (int)router_blocks(c->T);
+  char* w = (char*)ws;
+  int* cnt_part = (int*)w;
+  float* colsum_part = (float*)(w + align256((size_t)nblk * c->E * 4));
+  if (x) LAUNCH_NAMED("gemm_router_logits", gemm_router_logits<T>(x, w_router, logits, (int)c->T, (int)c->E, (int)c->d, st));
+  const bool want_colsum = c->aux_coeff != 0.0f;
+  LAUNCH_NAMED("router_topk", launch_router_topk(logits, bias, p, idx, gates, cnt_part, want_colsum ? colsum_part : nullptr, st));
+  LAUNCH_NAMED("router_finalize", launch_router_finalize(cnt_part, want_colsum ? colsum_part : nullptr, nblk, p, counts,
+                                want_colsum ? aux : nullptr, st));
+  return ok();
+}
+
+template <class T>
+moe_status gemm_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off, const void* w13,
+                         const void* w2, void* hu, void* act, void* y_perm, const void* x,
+                         const void* ws13, const void* ws2, void* hu_s, void* act_s, void* y_s,
+                         void* ws, hipStream_t st) {
+  const bool bf = sizeof(T) == 2;
+  const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f;
+  int* prefix = (int*)ws;
+  if (rows > 0) {
+    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf), prefix, st));
+    LAUNCH_NAMED("gemm_swiglu_fwd", gemm_swiglu_fwd<T>(x_perm, off, prefix, E, w13, hu, act, rows, d, f, st));
+    LAUNCH_NAMED("gemm_down_fwd", gemm_down_fwd<T>(act, off, prefix, E, w2, y_perm, rows, d, f, st));
+  }
+  if (c->f_shared > 0 && c->T > 0) {
+    const int fs = (int)c->f_shared, T_ = (int)c->T;
+    LAUNCH_NAMED("gemm_swiglu_fwd_shared", gemm_swiglu_fwd<T>(x, nullptr, nullptr, 1, ws13, hu_s, act_s, T_, d, fs, st));
+    LAUNCH_NAMED("gemm_down_fwd_shared", gemm_down_fwd<T>(act_s, nullptr, nullptr, 1, ws2, y_s, T_, d, fs, st));
+  }
+  return ok();
+}
+
+template <class T>
+moe_status gemm_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm, const int32_t* off,
+                         const void* hu, const void* act, const void* w13, const void* w2, void* dhu,
+                         void* dx_perm, void* dw13, void* dw2, const void* dy, const void* x,
+                         const void* hu_s, const void* act_s, const void* ws13, const void* ws2,
+                         void* dhu_s, float* dx_partial, void* dws13, void* dws2, void* ws,
+                         hipStream_t st) {
+  const bool bf = sizeof(T) == 2;
+  const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
+  int* prefix = (int*)ws;
+  if (rows > 0) LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf), prefix, st));
+  if (rows > 0)
+    LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd", gemm_down_dgrad_swiglu_bwd<T>(dy_perm, off, prefix, E, w2, hu, dhu, rows, d, f, st));
+  // weight gradients cover every expert (empty experts get zeros)
+  LAUNCH_NAMED("gemm_wgrad_down", gemm_wgrad<T>(dy_perm, d, act, f, off, E, 0, dw2, st));
+  if (rows > 0) LAUNCH_NAMED("gemm_gateup_dgrad", gemm_gateup_dgrad<T>(dhu, off, prefix, E, w13, dx_perm, false, rows, d, f, st));
+  LAUNCH_NAMED("gemm_wgrad_gateup", gemm_wgrad<T>(dhu, 2 * f, x_perm, d, off, E, 0, dw13, st));
+  if (c->f_shared > 0) {
+    const int fs = (int)c->f_shared;
+    if (T_ > 0) LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd_shared", gemm_down_dgrad_swiglu_bwd<T>(dy, nullptr, nullptr, 1, ws2, hu_s, dhu_s, T_, d, fs, st));
+    LAUNCH_NAMED("gemm_wgrad_down_shared", gemm_wgrad<T>(dy, d, act_s, fs, nullptr, 1, T_, dws2, st));
+    if (T_ > 0) LAUNCH_NAMED("gemm_gateup_dgrad_shared", gemm_gateup_dgrad<T>(dhu_s, nullptr, nullptr, 1, ws13, dx_partial, true, T_, d, fs, st));
+    LAUNCH_NAMED("gemm_wgrad_gateup_shared", gemm_wgrad<T>(dhu_s, 2 * fs, x, d, nullptr, 1, T_, dws13, st));
+  } else {
+    LAUNCH_NAMED("fill_f32", launch_fill_f32(dx_partial, (int64_t)T_ * d, 0.0f, st));
+  }
+  return ok();
+}
+
+template <class T>
+moe_status router_bwd_impl(const moe_cfg* c, const void* x, const void* w_router, const float* logits,
+                           const int32_t* idx, const float* gates, const int32_t* counts,
+                           const float* d_gates, float d_aux, float* d_logits, void* dw_router,
+                           float* dx_partial, void* ws, hipStream_t st) {
+  RouterParams p = router_params(c);
+  const int T_ = (int)c->T, E = (int)c->E, d = (int)c->d;
+  const bool bf = sizeof(T) == 2;
+  const int Ep = bf ? (int)pad8(E) : E;
+  T* dl_store = bf ? (T*)ws : nullptr;
+  LAUNCH_NAMED("router_bwd", launch_router_bwd<T>(logits, idx, gates, d_gates, counts, p, d_aux, d_logits, dl_store, Ep, st));
+  const void* dl = bf ? (const void*)dl_store : (const void*)d_logits;
+  LAUNCH_NAMED("gemm_router_wgrad", gemm_router_wgrad<T>(dl, Ep, E, x, T_, d, dw_router, st));
+  if (T_ > 0) LAUNCH_NAMED("gemm_router_dgrad", gemm_router_dgrad<T>(dl, Ep, E, w_router, T_, d, dx_partial, st));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_trace_begin(int capacity) {
+  if (capacity < 1 || capacity > (1 << 20))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "trace capacity %d outside [1, 2^20]", capacity);
+  if (g_trace.on) return fail(MOE_ERR_INVALID_ARGUMENT, "a trace is already active on this thread");
+  g_trace.ev.assign(2 * (size_t)capacity, nullptr);
+  g_trace.names.assign(capacity, nullptr);
+  for (auto& e : g_trace.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      for (auto& q : g_trace.ev)
+        if (q) hipEventDestroy(q);
+      g_trace.ev.clear();
+      return fail(MOE_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorString(r));
+    }
+  }
+  g_trace.cap = capacity;
+  g_trace.n = 0;
+  g_trace.on = true;
+  return ok();
+}
+
+int moe_trace_end(const char** names, float* ms, int capacity) {
+  if (!g_trace.on) return 0;
+  g_trace.on = false;
+  int n = g_trace.n, rc = n;
+  for (int i = 0; i < n && i < capacity; ++i) {
+    float t = 0.0f;
+    if (hipEventSynchronize(g_trace.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&t, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]) != hipSuccess)
+      rc = -1;
+    if (names) names[i] = g_trace.names[i];
+    if (ms) ms[i] = t;
+  }
+  for (auto& e : g_trace.ev) hipEventDestroy(e);
+  g_trace.ev.clear();
+  g_trace.names.clear();
+  return rc;
+}
+
+moe_status moe_init(int device) {
+  CHECK(check_device(device));
+  return ok();
+}
+
+size_t moe_workspace_size(const moe_cfg* cfg) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  g_err.clear();
+  return ws_bytes_for(cfg);
+}
+
+moe_status moe_router_topk(const moe_cfg* cfg, const void* x, const void* w_router, const float* bias,
+                           float* logits, int32_t* topk_idx, float* topk_gates, int32_t* expert_counts,
+                           float* aux_loss, void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  if ((x == nullptr) != (w_router == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x and w_router must both be given or both be NULL");
+  REQ(logits); REQ(topk_idx); REQ(topk_gates); REQ(expert_counts);
+  if (cfg->aux_coeff != 0.0f) REQ(aux_loss);
+  ALIGNED(x); ALIGNED(w_router); ALIGNED(logits);
+  CHECK(check_ws(cfg, workspace, workspace_bytes));
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (cfg->dtype == MOE_BF16)
+    return router_topk_impl<bf16>(cfg, x, w_router, bias, logits, topk_idx, topk_gates, expert_counts,
+                                  aux_loss, workspace, st);
+  return router_topk_impl<float>(cfg, x, w_router, bias, logits, topk_idx, topk_gates, expert_counts,
+                                 aux_loss, workspace, st);
+}
+
+moe_status moe_permute(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, int32_t* expert_offsets,
+                       int32_t* row_id_map, int32_t* src_token, void* x_perm, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  REQ(x); REQ(topk_idx); REQ(expert_offsets); REQ(row_id_map); REQ(src_token); REQ(x_perm);
+  ALIGNED(x); ALIGNED(x_perm);
+  CHECK(check_ws(cfg, workspace, workspace_bytes));
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  const int T_ = (int)cfg->T, k = (int)cfg->k, E = (int)cfg->E, rows = T_ * k;
+  int* hist = (int*)workspace;
+  LAUNCH_NAMED("perm_hist", launch_perm_hist(topk_idx, T_, k, E, hist, st));
+  LAUNCH_NAMED("perm_scan", launch_perm_scan(hist, (int)ranges(T_), E, rows, expert_offsets, st));
+  LAUNCH_NAMED("perm_rank", launch_perm_rank(topk_idx, T_, k, E, hist, row_id_map, src_token, st));
+  LAUNCH_NAMED("gather_rows", launch_gather_rows(x, src_token, rows, (int)(cfg->d * elt(cfg)), x_perm, st));
+  return ok();
+}
+
+moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm, const int32_t* expert_offsets,
+                                   const void* w13, const void* w2, void* hu_save, void* act, void* y_perm,
+                                   const void* x, const void* ws13, const void* ws2, void* hu_shared_save,
+                                   void* act_shared, void* y_shared, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  REQ(x_perm); REQ(expert_offsets); REQ(w13); REQ(w2); REQ(act); REQ(y_perm);
+  ALIGNED(x_perm); ALIGNED(w13); ALIGNED(w2); ALIGNED(hu_save); ALIGNED(act); ALIGNED(y_perm);
+  if (cfg->f_shared > 0) {
+    REQ(x); REQ(ws13); REQ(ws2); REQ(act_shared); REQ(y_shared);
+    ALIGNED(x); ALIGNED(ws13); ALIGNED(ws2); ALIGNED(hu_shared_save); ALIGNED(act_shared); ALIGNED(y_shared);
+  }
+  CHECK(check_ws(cfg, workspace, workspace_bytes));
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (cfg->dtype == MOE_BF16)
+    return gemm_fwd_impl<bf16>(cfg, x_perm, expert_offsets, w13, w2, hu_save, act, y_perm, x, ws13, ws2,
+                               hu_shared_save, act_shared, y_shared, workspace, st);
+  return gemm_fwd_impl<float>(cfg, x_perm, expert_offsets, w13, w2, hu_save, act, y_perm, x, ws13, ws2,
+                              hu_shared_save, act_shared, y_shared, workspace, st);
+}
+
+moe_status moe_unpermute_combine(const moe_cfg* cfg, const void* y_perm, const int32_t* row_id_map,
+                                 const float* topk_gates, const void* y_shared, void* y, void* stream) {
+  CHECK(check_cfg(cfg));
+  REQ(y_perm); REQ(row_id_map); REQ(topk_gates); REQ(y);
+  ALIGNED(y_perm); ALIGNED(y_shared); ALIGNED(y);
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  const int T_ = (int)cfg->T, k = (int)cfg->k, d = (int)cfg->d;
+  if (cfg->dtype == MOE_BF16)
+    LAUNCH_NAMED("combine", launch_combine<bf16>((const bf16*)y_perm, row_id_map, topk_gates, (const bf16*)y_shared, (bf16*)y,
+                                T_, k, d, st));
+  else
+    LAUNCH_NAMED("combine", launch_combine<float>((const float*)y_perm, row_id_map, topk_gates, (const float*)y_shared,
+                                 (float*)y, T_, k, d, st));
+  return ok();
+}
+
+moe_status moe_unpermute_combine_bwd(const moe_cfg* cfg, const void* dy, const void* y_perm,
+                                     const int32_t* row_id_map, const float* topk_gates, void* dy_perm,
+                                     float* d_gates, void* stream) {
+  CHECK(check_cfg(cfg));
+  REQ(dy); REQ(y_perm); REQ(row_id_map); REQ(topk_gates); REQ(dy_perm); REQ(d_gates);
+  ALIGNED(dy); ALIGNED(y_perm); ALIGNED(dy_perm);
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  const int T_ = (int)cfg->T, k = (int)cfg->k, d = (int)cfg->d;
+  if (cfg->dtype == MOE_BF16)
+    LAUNCH_NAMED("combine_bwd", launch_combine_bwd<bf16>((const bf16*)dy, (const bf16*)y_perm, row_id_map, topk_gates,
+                                    (bf16*)dy_perm, d_gates, T_, k, d, st));
+  else
+    LAUNCH_NAMED("combine_bwd", launch_combine_bwd<float>((const float*)dy, (const float*)y_perm, row_id_map, topk_gates,
+                                     (float*)dy_perm, d_gates, T_, k, d, st));
+  return ok();
+}
+
+moe_status moe_grouped_gemm_swiglu_bwd(const moe_cfg* cfg, const void* dy_perm, const void* x_perm,
+                                       const int32_t* expert_offsets, const void* hu_save, const void* act,
+                                       const void* w13, const void* w2, void* dhu, void* dx_perm, void* dw13,
+                                       void* dw2, const void* dy, const void* x, const void* hu_shared_save,
+                                       const void* act_shared, const void* ws13, const void* ws2,
+                                       void* dhu_shared, float* dx_partial, void* dws13, void* dws2,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  REQ(dy_perm); REQ(x_perm); REQ(expert_offsets); REQ(hu_save); REQ(act); REQ(w13); REQ(w2);
+  REQ(dhu); REQ(dx_perm); REQ(dw13); REQ(dw2); REQ(dx_partial);
+  ALIGNED(dy_perm); ALIGNED(x_perm); ALIGNED(hu_save); ALIGNED(act); ALIGNED(w13); ALIGNED(w2);
+  ALIGNED(dhu); ALIGNED(dx_perm); ALIGNED(dw13); ALIGNED(dw2); ALIGNED(dx_partial);
+  if (cfg->f_shared > 0) {
+    REQ(dy); REQ(x); REQ(hu_shared_save); REQ(act_shared); REQ(ws13); REQ(ws2); REQ(dhu_shared);
+    REQ(dws13); REQ(dws2);
+    ALIGNED(dy); ALIGNED(x); ALIGNED(hu_shared_save); ALIGNED(act_shared); ALIGNED(ws13); ALIGNED(ws2);
+    ALIGNED(dhu_shared); ALIGNED(dws13); ALIGNED(dws2);
+  }
+  CHECK(check_ws(cfg, workspace, workspace_bytes));
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (cfg->dtype == MOE_BF16)
+    return gemm_bwd_impl<bf16>(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, w13, w2, dhu, dx_perm, dw13,
+                               dw2, dy, x, hu_shared_save, act_shared, ws13, ws2, dhu_shared, dx_partial,
+                               dws13, dws2, workspace, st);
+  return gemm_bwd_impl<float>(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, w13, w2, dhu, dx_perm, dw13,
+                              dw2, dy, x, hu_shared_save, act_shared, ws13, ws2, dhu_shared, dx_partial,
+                              dws13, dws2, workspace, st);
+}
+
+moe_status moe_router_topk_bwd(const moe_cfg* cfg, const void* x, const void* w_router, const float* logits,
+                               const int32_t* topk_idx, const float* topk_gates, const int32_t* expert_counts,
+                               const float* d_gates, float d_aux, float* d_logits, void* dw_router,
+                               float* dx_partial, void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  REQ(x); REQ(w_router); REQ(logits); REQ(topk_idx); REQ(topk_gates); REQ(d_gates); REQ(d_logits);
+  REQ(dw_router); REQ(dx_partial);
+  if (cfg->aux_coeff != 0.0f) REQ(expert_counts);
+  ALIGNED(x); ALIGNED(w_router); ALIGNED(logits); ALIGNED(d_logits); ALIGNED(dw_router); ALIGNED(dx_partial);
+  CHECK(check_ws(cfg, workspace, workspace_bytes));
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (cfg->dtype == MOE_BF16)
+    return router_bwd_impl<bf16>(cfg, x, w_router, logits, topk_idx, topk_gates, expert_counts, d_gates, d_aux,
+                                 d_logits, dw_router, dx_partial, workspace, st);
+  return router_bwd_impl<float>(cfg, x, w_router, logits, topk_idx, topk_gates, expert_counts, d_gates, d_aux,
+                                d_logits, dw_router, dx_partial, workspace, st);
+}
+
+moe_status moe_permute_bwd(const moe_cfg* cfg, const void* dx_perm, const int32_t* row_id_map,
+                           const float* dx_partial, void* dx, void* stream) {
+  CHECK(check_cfg(cfg));
+  REQ(dx_perm); REQ(row_id_map); REQ(dx);
+  ALIGNED(dx_perm); ALIGNED(dx_partial); ALIGNED(dx);
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  const int T_ = (int)cfg->T, k = (int)cfg->k, d = (int)cfg->d;
+  if (cfg->dtype == MOE_BF16)
+    LAUNCH_NAMED("unpermute_sum", launch_unpermute_sum<bf16>((const bf16*)dx_perm, row_id_map, dx_partial, (bf16*)dx, T_, k, d, st));
+  else
+    LAUNCH_NAMED("unpermute_sum", launch_unpermute_sum<float>((const float*)dx_perm, row_id_map, dx_partial, (float*)dx, T_, k, d, st));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal launchers of libmoe_gfx950 (host side).  Every launcher only
+// enqueues work on `st` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouterParams {
+  int T, E, k;
+  int score;        // 0 softmax, 1 sigmoid
+  int n_group, topk_group;
+  int renorm;
+  float scale;
+  float aux_coeff;
+};
+
+constexpr int kRouterTokensPerBlock = 64;
+constexpr int kPermTokensPerRange = 64;
+
+// router.hip
+hipError_t launch_router_topk(const float* logits, const float* bias, const RouterParams& p,
+                              int32_t* idx, float* gates, int* cnt_part, float* colsum_part,
+                              hipStream_t st);
+hipError_t launch_router_finalize(const int* cnt_part, const float* colsum_part, int nblk,
+                                  const RouterParams& p, int32_t* counts, float* aux, hipStream_t st);
+template <class T>
+hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gates,
+                             const float* d_gates, const int32_t* counts, const RouterParams& p,
+                             float d_aux, float* d_logits, T* dl_store, int Ep, hipStream_t st);
+
+// permute.hip
+hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int E, int* hist, hipStream_t st);
+hipError_t launch_perm_scan(int* hist, int R, int E, int rows, int32_t* offsets, hipStream_t st);
+hipError_t launch_perm_rank(const int32_t* idx, int T, int k, int E, int* base, int32_t* row_id_map,
+                            int32_t* src_token, hipStream_t st);
+hipError_t launch_gather_rows(const void* x, const int32_t* src_token, int rows, int row_bytes,
+                              void* out, hipStream_t st);
+template <class T>
+hipError_t launch_combine(const T* y_perm, const int32_t* rmap, const float* gates, const T* y_shared,
+                          T* y, int T_, int k, int d, hipStream_t st);
+template <class T>
+hipError_t launch_combine_bwd(const T* dy, const T* y_perm, const int32_t* rmap, const float* gates,
+                              T* dy_perm, float* d_gates, int T_, int k, int d, hipStream_t st);
+template <class T>
+hipError_t launch_unpermute_sum(const T* dx_perm, const int32_t* rmap, const float* partial, T* dx,
+                                int T_, int k, int d, hipStream_t st);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
+
+// gemm.hip
+hipError_t launch_tile_prefix(const int* offsets, int G, int BM, int* prefix, hipStream_t st);
+int gemm_tile_rows(bool bf16);
+template <class T>
+hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int T_, int E, int d,
+                              hipStream_t st);
+template <class T>
+hipError_t gemm_swiglu_fwd(const void* xin, const int* offsets, const int* tile_prefix, int G,
+                           const void* w13, void* hu, void* act, int rows, int d, int f,
+                           hipStream_t st);
+template <class T>
+hipError_t gemm_down_fwd(const void* act, const int* offsets, const int* tile_prefix, int G,
+                         const void* w2, void* y, int rows, int d, int f, hipStream_t st);
+template <class T>
+hipError_t gemm_down_dgrad_swiglu_bwd(const void* dy, const int* offsets, const int* tile_prefix,
+                                      int G, const void* w2, const void* hu, void* dhu, int rows,
+                                      int d, int f, hipStream_t st);
+template <class T>
+hipError_t gemm_gateup_dgrad(const void* dhu, const int* offsets, const int* tile_prefix, int G,
+                             const void* w13, void* dx, bool f32_out, int rows, int d, int f,
+                             hipStream_t st);
+template <class T>
+hipError_t gemm_wgrad(const void* P_, int M, const void* Q_, int N, const int* offsets, int G,
+                      int K_dense, void* dw, hipStream_t st);
+template <class T>
+hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T_, int d, void* dw_r,
+                             hipStream_t st);
+template <class T>
+hipError_t gemm_router_dgrad(const void* dl, int Ep, int E, const void* w_r, int T_, int d,
+                             float* dx_partial, hipStream_t st);
+
+}  // namespace moe

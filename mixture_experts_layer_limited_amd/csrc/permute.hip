@@ -1,0 +1,316 @@
+// Dispatch and combine on one GPU ("System Modules: Dispatcher" and
+// "Combiner"; memory-efficient permutation, Figure 7): a stable counting sort
+// of (token, choice) pairs by expert, the row gather into expert-contiguous
+// order, and the gate-weighted unpermute-combine with its backward.
+//
+// Counting sort: tokens are cut into ranges of 64.  perm_hist counts each
+// range's assignments per expert, perm_scan turns the [range, expert] table
+// into the first row of every (range, expert) pair, and perm_rank walks each
+// range in (token, choice) order one wave at a time, ranking equal expert ids
+// inside a 64-entry chunk with ballots over the id's bits.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                        int E, int* __restrict__ hist) {
+  __shared__ int h[kMaxExperts];
+  for (int e = threadIdx.x; e < kMaxExperts; e += blockDim.x) h[e] = 0;
+  __syncthreads();
+  const int64_t n0 = (int64_t)blockIdx.x * kPermTokensPerRange * k;
+  const int64_t n1 = min((int64_t)(blockIdx.x + 1) * kPermTokensPerRange, (int64_t)T) * k;
+  for (int64_t n = n0 + threadIdx.x; n < n1; n += blockDim.x) atomicAdd(&h[idx[n]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int E, int* hist, hipStream_t st) {
+  int R = (T + kPermTokensPerRange - 1) / kPermTokensPerRange;
+  if (R == 0) return hipSuccess;
+  perm_hist_kernel<<<R, 256, 0, st>>>(idx, T, k, E, hist);
+  return hipGetLastError();
+}
+
+// hist[r][e] (counts) -> base[r][e] = offsets[e] + sum_{r' < r} hist[r'][e]; offsets[E] = rows
+__global__ __launch_bounds__(256) void perm_scan_kernel(int* __restrict__ hist, int R, int E, int rows,
+                                                        int32_t* __restrict__ offsets) {
+  __shared__ int tot[kMaxExperts];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int r = 0; r < R; ++r) {
+      int c = hist[(int64_t)r * E + e];
+      hist[(int64_t)r * E + e] = run;
+      run += c;
+    }
+  }
+  tot[e] = (e < E) ? run : 0;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {      // inclusive scan of the totals
+    int add = (e >= o) ? tot[e - o] : 0;
+    __syncthreads();
+    tot[e] += add;
+    __syncthreads();
+  }
+  if (e < E) {
+    int off = tot[e] - run;                  // exclusive
+    offsets[e] = off;
+    for (int r = 0; r < R; ++r) hist[(int64_t)r * E + e] += off;
+  }
+  if (e == 0) offsets[E] = rows;
+}
+
+hipError_t launch_perm_scan(int* hist, int R, int E, int rows, int32_t* offsets, hipStream_t st) {
+  perm_scan_kernel<<<1, 256, 0, st>>>(hist, R, E, rows, offsets);
+  return hipGetLastError();
+}
+
+// one wave per token range; entries n = t*k + j in increasing order
+__global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                       int E, const int* __restrict__ base,
+                                                       int32_t* __restrict__ row_id_map,
+                                                       int32_t* __restrict__ src_token) {
+  __shared__ int run[kMaxExperts];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) run[e] = base[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  const int64_t n0 = (int64_t)blockIdx.x * kPermTokensPerRange * k;
+  const int64_t n1 = min((int64_t)(blockIdx.x + 1) * kPermTokensPerRange, (int64_t)T) * k;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t c0 = n0; c0 < n1; c0 += 64) {
+    const int64_t n = c0 + lane;
+    const bool valid = n < n1;
+    const int e = valid ? idx[n] : 0;
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {            // E <= 256: 8 id bits
+      uint64_t ones = __ballot(valid && ((e >> b) & 1));
+      m &= ((e >> b) & 1) ? ones : ~ones;
+    }
+    int row = 0;
+    if (valid) {
+      row = run[e] + __popcll(m & below);
+      row_id_map[n] = row;
+      src_token[row] = (int32_t)(n / k);
+    }
+    __syncthreads();
+    // the highest lane of each id group advances that expert's running row
+    if (valid && (m >> lane) == 1ull) run[e] += __popcll(m);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_perm_rank(const int32_t* idx, int T, int k, int E, int* base, int32_t* row_id_map,
+                            int32_t* src_token, hipStream_t st) {
+  int R = (T + kPermTokensPerRange - 1) / kPermTokensPerRange;
+  if (R == 0) return hipSuccess;
+  perm_rank_kernel<<<R, 64, 0, st>>>(idx, T, k, E, base, row_id_map, src_token);
+  return hipGetLastError();
+}
+
+// out[row] = x[src_token[row]], 16-byte vectors; one row per 64-thread group
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ x,
+                                                          const int32_t* __restrict__ src, int rows,
+                                                          int vec_per_row, u32x4* __restrict__ out) {
+  const int sub = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + sub;
+  if (row >= rows) return;
+  const int64_t s = src[row];
+  const u32x4* in = x + s * vec_per_row;
+  u32x4* o = out + (int64_t)row * vec_per_row;
+  for (int c = lane; c < vec_per_row; c += 64) o[c] = in[c];
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* src_token, int rows, int row_bytes,
+                              void* out, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  gather_rows_kernel<<<(rows + 3) / 4, 256, 0, st>>>((const u32x4*)x, src_token, rows, row_bytes / 16,
+                                                      (u32x4*)out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Combine: y[t] = sum_j g[t,j] y_perm[row(t,j)] (+ y_shared[t]), fp32, j order.
+// One workgroup per token; each thread owns 8 consecutive elements.
+// ---------------------------------------------------------------------------
+template <class T>
+struct Vec8 {
+  float v[8];
+  __device__ void load(const T* p) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = to_f32(p[i]);
+  }
+  __device__ void store(T* p) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = from_f32<T>(v[i]);
+  }
+};
+template <>
+__device__ void Vec8<bf16>::load(const bf16* p) {
+  u32x4 w = *(const u32x4*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_bits_lo(w[i]); v[2 * i + 1] = bf16_bits_hi(w[i]); }
+}
+template <>
+__device__ void Vec8<bf16>::store(bf16* p) const {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  *(u32x4*)p = w;
+}
+template <>
+__device__ void Vec8<float>::load(const float* p) {
+  floatx4 a = *(const floatx4*)p, b = *(const floatx4*)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+template <>
+__device__ void Vec8<float>::store(float* p) const {
+  floatx4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[4 + i]; }
+  *(floatx4*)p = a;
+  *(floatx4*)(p + 4) = b;
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ rmap,
+                                                      const float* __restrict__ gates,
+                                                      const T* __restrict__ y_shared, T* __restrict__ y,
+                                                      int k, int d) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    Vec8<T> acc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc.v[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t row = rmap[(int64_t)t * k + j];
+      const float g = gates[(int64_t)t * k + j];
+      Vec8<T> r;
+      r.load(y_perm + row * d + c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc.v[i] += g * r.v[i];
+    }
+    if (y_shared) {
+      Vec8<T> s;
+      s.load(y_shared + (int64_t)t * d + c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc.v[i] += s.v[i];
+    }
+    acc.store(y + (int64_t)t * d + c);
+  }
+}
+
+template <class T>
+hipError_t launch_combine(const T* y_perm, const int32_t* rmap, const float* gates, const T* y_shared,
+                          T* y, int T_, int k, int d, hipStream_t st) {
+  if (T_ == 0) return hipSuccess;
+  combine_kernel<T><<<T_, 256, 0, st>>>(y_perm, rmap, gates, y_shared, y, k, d);
+  return hipGetLastError();
+}
+
+// dy_perm[row(t,j)] = storage(g dy[t]); d_gates[t,j] = <dy[t], y_perm[row(t,j)]>
+template <class T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy,
+                                                          const T* __restrict__ y_perm,
+                                                          const int32_t* __restrict__ rmap,
+                                                          const float* __restrict__ gates,
+                                                          T* __restrict__ dy_perm,
+                                                          float* __restrict__ d_gates, int k, int d) {
+  __shared__ float part[4];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int j = 0; j < k; ++j) {
+    const int64_t row = rmap[(int64_t)t * k + j];
+    const float g = gates[(int64_t)t * k + j];
+    float dot = 0.0f;
+    for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+      Vec8<T> a, r, o;
+      a.load(dy + (int64_t)t * d + c);
+      r.load(y_perm + row * d + c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dot += a.v[i] * r.v[i];
+        o.v[i] = g * a.v[i];
+      }
+      o.store(dy_perm + row * d + c);
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) part[wave] = dot;
+    __syncthreads();
+    if (threadIdx.x == 0) d_gates[(int64_t)t * k + j] = ((part[0] + part[1]) + part[2]) + part[3];
+    __syncthreads();
+  }
+}
+
+template <class T>
+hipError_t launch_combine_bwd(const T* dy, const T* y_perm, const int32_t* rmap, const float* gates,
+                              T* dy_perm, float* d_gates, int T_, int k, int d, hipStream_t st) {
+  if (T_ == 0) return hipSuccess;
+  combine_bwd_kernel<T><<<T_, 256, 0, st>>>(dy, y_perm, rmap, gates, dy_perm, d_gates, k, d);
+  return hipGetLastError();
+}
+
+// dx[t] = storage(partial[t] + sum_j dx_perm[row(t,j)])
+template <class T>
+__global__ __launch_bounds__(256) void unpermute_sum_kernel(const T* __restrict__ dx_perm,
+                                                            const int32_t* __restrict__ rmap,
+                                                            const float* __restrict__ partial,
+                                                            T* __restrict__ dx, int k, int d) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    Vec8<T> acc;
+    if (partial) {
+      Vec8<float> p;
+      p.load(partial + (int64_t)t * d + c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc.v[i] = p.v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc.v[i] = 0.0f;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int64_t row = rmap[(int64_t)t * k + j];
+      Vec8<T> r;
+      r.load(dx_perm + row * d + c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc.v[i] += r.v[i];
+    }
+    acc.store(dx + (int64_t)t * d + c);
+  }
+}
+
+template <class T>
+hipError_t launch_unpermute_sum(const T* dx_perm, const int32_t* rmap, const float* partial, T* dx,
+                                int T_, int k, int d, hipStream_t st) {
+  if (T_ == 0) return hipSuccess;
+  unpermute_sum_kernel<T><<<T_, 256, 0, st>>>(dx_perm, rmap, partial, dx, k, d);
+  return hipGetLastError();
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  fill_f32_kernel<<<(unsigned)blocks, 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+#define MOE_INST(T)                                                                               \
+  template hipError_t launch_combine<T>(const T*, const int32_t*, const float*, const T*, T*, int, \
+                                        int, int, hipStream_t);                                    \
+  template hipError_t launch_combine_bwd<T>(const T*, const T*, const int32_t*, const float*, T*,  \
+                                            float*, int, int, int, hipStream_t);                   \
+  template hipError_t launch_unpermute_sum<T>(const T*, const int32_t*, const float*, T*, int, int, \
+                                              int, hipStream_t);
+MOE_INST(float)
+MOE_INST(bf16)
+
+}  // namespace moe

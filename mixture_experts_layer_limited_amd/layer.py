@@ -1,0 +1,145 @@
+"""One MoE layer's forward and backward driven through libmoe_gfx950.
+
+This module only allocates device buffers (torch) and sequences the C calls:
+Route (moe_router_topk) -> Dispatch (moe_permute) -> Compute
+(moe_grouped_gemm_swiglu) -> Combine (moe_unpermute_combine), and the
+backward counterparts in reverse.  Every number is produced by the HIP kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import _abi as abi
+
+
+@dataclass
+class LayerShape:
+    T: int
+    d: int
+    E: int
+    k: int
+    f: int
+    f_shared: int = 0
+    score: str = "softmax"
+    n_group: int = 1
+    topk_group: int = 1
+    renorm: bool = True
+    scale: float = 1.0
+    aux_coeff: float = 0.0
+    dtype: str = "bf16"
+
+    def cfg(self) -> abi.moe_cfg:
+        return abi.make_cfg(self.T, self.d, self.E, self.k, self.f, self.f_shared, self.score,
+                            self.n_group, self.topk_group, self.renorm, self.scale,
+                            self.aux_coeff, self.dtype)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+
+@dataclass
+class Buffers:
+    """Every tensor the layer reads or writes, allocated once and reused."""
+    t: dict = field(default_factory=dict)
+
+    def __getitem__(self, k):
+        return self.t[k]
+
+    def get(self, k):
+        return self.t.get(k)
+
+
+class MoELayer:
+    def __init__(self, shape: LayerShape, device="cuda", backward: bool = True):
+        self.s = shape
+        self.cfg = shape.cfg()
+        self.device = torch.device(device)
+        self.backward_enabled = backward
+        abi.moe_init(self.device.index or 0)
+        self.ws = torch.empty(abi.moe_workspace_size(self.cfg), dtype=torch.uint8, device=self.device)
+        self.buf = self._alloc()
+
+    def _alloc(self) -> Buffers:
+        s, dev, dt = self.s, self.device, self.s.torch_dtype
+        rows = s.T * s.k
+        e = lambda *shape, dtype=dt: torch.empty(shape, dtype=dtype, device=dev)
+        b = {
+            "logits": e(s.T, s.E, dtype=torch.float32),
+            "idx": e(s.T, s.k, dtype=torch.int32),
+            "gates": e(s.T, s.k, dtype=torch.float32),
+            "counts": e(s.E, dtype=torch.int32),
+            "aux": e(1, dtype=torch.float32),
+            "offsets": e(s.E + 1, dtype=torch.int32),
+            "row_id_map": e(s.T, s.k, dtype=torch.int32),
+            "src_token": e(rows, dtype=torch.int32),
+            "x_perm": e(rows, s.d),
+            "hu": e(rows, 2 * s.f) if self.backward_enabled else None,
+            "act": e(rows, s.f),
+            "y_perm": e(rows, s.d),
+            "y": e(s.T, s.d),
+        }
+        if s.f_shared:
+            b.update({"hu_s": e(s.T, 2 * s.f_shared) if self.backward_enabled else None,
+                      "act_s": e(s.T, s.f_shared), "y_s": e(s.T, s.d)})
+        if self.backward_enabled:
+            b.update({
+                "dy_perm": e(rows, s.d), "d_gates": e(s.T, s.k, dtype=torch.float32),
+                "dhu": e(rows, 2 * s.f), "dx_perm": e(rows, s.d),
+                "dw13": e(s.E, 2 * s.f, s.d), "dw2": e(s.E, s.d, s.f),
+                "dx_partial": e(s.T, s.d, dtype=torch.float32),
+                "d_logits": e(s.T, s.E, dtype=torch.float32),
+                "dw_router": e(s.E, s.d), "dx": e(s.T, s.d),
+            })
+            if s.f_shared:
+                b.update({"dhu_s": e(s.T, 2 * s.f_shared), "dws13": e(2 * s.f_shared, s.d),
+                          "dws2": e(s.d, s.f_shared)})
+        return Buffers(b)
+
+    # -- forward ------------------------------------------------------------
+    def route(self, x, w_router, bias, stream=None):
+        b = self.buf
+        abi.moe_router_topk(self.cfg, x, w_router, bias, b["logits"], b["idx"], b["gates"], b["counts"],
+                            b["aux"] if self.s.aux_coeff else None, self.ws, stream)
+
+    def permute(self, x, stream=None):
+        b = self.buf
+        abi.moe_permute(self.cfg, x, b["idx"], b["offsets"], b["row_id_map"], b["src_token"], b["x_perm"],
+                        self.ws, stream)
+
+    def experts(self, x, w13, w2, ws13=None, ws2=None, stream=None):
+        b = self.buf
+        abi.moe_grouped_gemm_swiglu(self.cfg, b["x_perm"], b["offsets"], w13, w2, b.get("hu"), b["act"],
+                                    b["y_perm"], x if self.s.f_shared else None, ws13, ws2, b.get("hu_s"),
+                                    b.get("act_s"), b.get("y_s"), self.ws, stream)
+
+    def combine(self, stream=None):
+        b = self.buf
+        abi.moe_unpermute_combine(self.cfg, b["y_perm"], b["row_id_map"], b["gates"], b.get("y_s"), b["y"],
+                                  stream)
+
+    def forward(self, x, w_router, bias, w13, w2, ws13=None, ws2=None, stream=None):
+        self.route(x, w_router, bias, stream)
+        self.permute(x, stream)
+        self.experts(x, w13, w2, ws13, ws2, stream)
+        self.combine(stream)
+        return self.buf["y"]
+
+    # -- backward -----------------------------------------------------------
+    def backward(self, dy, x, w_router, w13, w2, ws13=None, ws2=None, d_aux: float = 1.0, stream=None):
+        b, s = self.buf, self.s
+        abi.moe_unpermute_combine_bwd(self.cfg, dy, b["y_perm"], b["row_id_map"], b["gates"], b["dy_perm"],
+                                      b["d_gates"], stream)
+        sh = bool(s.f_shared)
+        abi.moe_grouped_gemm_swiglu_bwd(
+            self.cfg, b["dy_perm"], b["x_perm"], b["offsets"], b["hu"], b["act"], w13, w2, b["dhu"],
+            b["dx_perm"], b["dw13"], b["dw2"], dy if sh else None, x if sh else None, b.get("hu_s"),
+            b.get("act_s"), ws13, ws2, b.get("dhu_s"), b["dx_partial"], b.get("dws13"), b.get("dws2"),
+            self.ws, stream)
+        abi.moe_router_topk_bwd(self.cfg, x, w_router, b["logits"], b["idx"], b["gates"], b["counts"],
+                                b["d_gates"], d_aux, b["d_logits"], b["dw_router"], b["dx_partial"],
+                                self.ws, stream)
+        abi.moe_permute_bwd(self.cfg, b["dx_perm"], b["row_id_map"], b["dx_partial"], b["dx"], stream)
+        return b["dx"]

@@ -388,9 +388,11 @@ def router_backward(logits, idx, gates, d_gates, counts, cfg, d_aux: float = 1.0
 
 
 def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
-                   storage: str = None) -> dict:
+                   storage: str = None, dense: bool = True) -> dict:
     """Gradients of <y, dy> (+ d_aux * aux) w.r.t. x, the router weight and all
-    expert weights, for the forward pass `fwd` of layer_forward."""
+    expert weights, for the forward pass `fwd` of layer_forward.  With
+    dense=False the expert weight gradients come back as {expert: array} for
+    the experts that received rows only (all others are exactly zero)."""
     storage = storage or storage_of(cfg)
     exact = storage == "f64"
     x = _np(inp["x"])
@@ -412,8 +414,8 @@ def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
     dHU = np.zeros((rows, 2 * cfg.f))
     dXp32 = np.zeros((rows, d))
     dXp = np.zeros((rows, d))
-    dw13 = np.zeros(inp["w13"].shape)
-    dw2 = np.zeros(inp["w2"].shape)
+    dw13 = np.zeros(inp["w13"].shape) if dense else {}
+    dw2 = np.zeros(inp["w2"].shape) if dense else {}
     off = fwd["offsets"]
     Xp = fwd["Xp"]
     for e in range(cfg.E):

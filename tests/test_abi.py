@@ -1,0 +1,113 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+symbol include/moe.h declares, and rejects bad arguments on the host before
+touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import mixture_experts_layer_limited_amd as m
+from mixture_experts_layer_limited_amd import _abi as abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = abi.lib()
+    names = _declared_symbols()
+    assert {"moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine",
+            "moe_unpermute_combine_bwd", "moe_grouped_gemm_swiglu_bwd", "moe_router_topk_bwd",
+            "moe_permute_bwd"} <= names
+    for n in sorted(names):
+        assert hasattr(L, n), f"{n} declared in include/ but not exported"
+    # the binding wraps every declared call under the same name
+    for n in names:
+        assert hasattr(m, n), f"binding lacks {n}"
+
+
+def test_status_strings():
+    assert abi.moe_status_string(0) == "MOE_OK"
+    assert abi.moe_status_string(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
+    assert abi.moe_status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def test_workspace_size_and_invalid_cfg():
+    c = abi.make_cfg(4096, 7168, 256, 8, 2048, 2048, "sigmoid", 8, 4, True, 2.5)
+    assert abi.moe_workspace_size(c) >= 4096 * 256 * 2
+    bad = abi.make_cfg(16, 64, 8, 9, 128)                  # k > E
+    with pytest.raises(abi.MoEError) as ei:
+        abi.moe_workspace_size(bad)
+    assert "cfg.k" in str(ei.value)
+
+
+# The calls below pass dummy non-NULL device addresses.  They must fail in
+# host-side validation, before any launch; to stay safe even if a validation
+# bug let one through, they only run where no GPU is visible.
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="dummy pointers: CPU-only test")
+FAKE = 0x100000
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(k=9), abi.MOE_ERR_INVALID_ARGUMENT, "cfg.k"),
+    (dict(E=300, k=2), abi.MOE_ERR_INVALID_ARGUMENT, "cfg.E"),
+    (dict(d=60), abi.MOE_ERR_INVALID_ARGUMENT, "cfg.d"),
+    (dict(f=100), abi.MOE_ERR_INVALID_ARGUMENT, "cfg.f"),
+    (dict(n_group=3), abi.MOE_ERR_INVALID_ARGUMENT, "n_group"),
+    (dict(n_group=4, topk_group=1, k=3), abi.MOE_ERR_INVALID_ARGUMENT, "topk_group"),
+    (dict(score="sigmoid", aux_coeff=1e-3), abi.MOE_ERR_UNSUPPORTED, "aux"),
+])
+def test_router_rejects_bad_cfg(kw, status, needle):
+    base = dict(T=16, d=64, E=8, k=2, f=128)
+    base.update(kw)
+    cfg = abi.make_cfg(**base)
+    st = abi.lib().moe_router_topk(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, 1 << 20, None)
+    assert st == status
+    assert needle in abi.moe_last_error()
+
+
+@no_gpu
+def test_rejects_null_misaligned_and_small_workspace():
+    cfg = abi.make_cfg(16, 64, 8, 2, 128)
+    L = abi.lib()
+    ws = abi.moe_workspace_size(cfg)
+    st = L.moe_router_topk(ctypes.byref(cfg), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "logits" in abi.moe_last_error()
+    st = L.moe_router_topk(ctypes.byref(cfg), FAKE + 2, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "aligned" in abi.moe_last_error()
+    st = L.moe_router_topk(ctypes.byref(cfg), FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "both" in abi.moe_last_error()
+    st = L.moe_router_topk(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws - 1, None)
+    assert st == abi.MOE_ERR_WORKSPACE_TOO_SMALL
+    st = L.moe_permute(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "src_token" in abi.moe_last_error()
+    shared = abi.make_cfg(16, 64, 8, 2, 128, f_shared=64)
+    st = L.moe_grouped_gemm_swiglu(ctypes.byref(shared), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                                   FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "'x'" in abi.moe_last_error()
+    cfg.dtype = 7
+    st = L.moe_permute(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED
+
+
+@no_gpu
+def test_valid_call_without_gpu_reports_device_error():
+    cfg = abi.make_cfg(16, 64, 8, 2, 128)
+    ws = abi.moe_workspace_size(cfg)
+    st = abi.lib().moe_unpermute_combine(ctypes.byref(cfg), FAKE, FAKE, FAKE, None, FAKE, None)
+    assert st == abi.MOE_ERR_DEVICE
+    assert abi.lib().moe_init(0) == abi.MOE_ERR_DEVICE
+    del ws

@@ -1,0 +1,145 @@
+"""HIP path vs the CPU oracle, through the C ABI, on seeded inputs.
+
+Integer results (top-k ids, counts, offsets, row maps) are compared bit for
+bit; floating outputs and gradients by relative L2 error (1e-5 fp32, 1e-2
+bf16).  Layer-level cases use inputs on an exact grid (moe_inputs.
+exact_grid_inputs) so that the fp32 router logits -- and therefore every routing
+decision -- are the same on both sides whatever the summation order.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from mixture_experts_layer_limited_amd import _abi as abi
+from oracle import moe_oracle as O
+
+from harness import compare_layer, host, rel_l2, run_gpu, run_oracle, shape_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(name, **kw):
+    base = dict(T=256, d=128, E=8, k=2, f=128, dtype="bf16", expert_std=0.05)
+    base.update(kw)
+    return mi.MoEConfig(name, **base)
+
+
+# ---------------------------------------------------------------------------
+# router: identical fp32 logits -> identical choices, counts; gates and aux
+# ---------------------------------------------------------------------------
+ROUTER_CASES = [
+    _cfg("softmax_e8_k2", T=300),
+    _cfg("softmax_e128_k8_aux", T=300, E=128, k=8, aux_coeff=1e-3),
+    _cfg("sigmoid_e256_groups", T=300, E=256, k=8, score="sigmoid", n_group=8, topk_group=4,
+         scale=2.5, bias="normal", bias_std=0.01),
+    _cfg("softmax_k_eq_E_norenorm", T=70, E=6, k=6, renorm=False),
+    _cfg("sigmoid_one_expert_groups", T=130, E=16, k=3, score="sigmoid", n_group=16, topk_group=4),
+    _cfg("softmax_e200_k17", T=65, E=200, k=17),
+]
+
+
+@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("cfg", ROUTER_CASES, ids=lambda c: c.name)
+def test_router_topk_from_logits_bitexact(cfg, ties):
+    print(f"case router {cfg.name} ties={ties}", flush=True)
+    logits = mi.fixed_logits(cfg.T, cfg.E, seed=5, std=2.0, ties=ties)
+    bias = mi.make_inputs(cfg, seed=5, experts=False)["bias"]
+    o_keys = O.selection_keys(logits.numpy(), cfg, None if bias is None else bias.numpy())
+    o_idx = O.select_topk(o_keys, cfg)
+    o_g = O.gates_from_selection(logits.numpy(), o_idx, cfg)
+    o_cnt = O.expert_counts(o_idx, cfg.E)
+    c = shape_of(cfg).cfg()
+    dev = "cuda"
+    L = logits.to(dev)
+    idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
+    gates = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev)
+    cnt = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(abi.moe_workspace_size(c), dtype=torch.uint8, device=dev)
+    abi.moe_router_topk(c, None, None, None if bias is None else bias.to(dev), L, idx, gates, cnt,
+                        aux if cfg.aux_coeff else None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), o_idx)
+    assert np.array_equal(host(cnt), o_cnt)
+    assert np.max(np.abs(host(gates) - o_g)) <= 2e-6 * cfg.scale
+    if cfg.aux_coeff:
+        want = O.aux_loss(O.softmax_probs(logits.numpy()), o_cnt, cfg.T, cfg.k, cfg.aux_coeff)
+        assert abs(float(host(aux)[0]) - want) <= 1e-5 * want
+
+
+# ---------------------------------------------------------------------------
+# permute: stable counting sort and row gather, bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k", [(300, 8, 2), (1000, 256, 8), (64, 64, 2), (5, 16, 16), (0, 8, 2)])
+def test_permute_bitexact(T, E, k):
+    print(f"case permute T={T} E={E} k={k}", flush=True)
+    cfg = _cfg("perm", T=T, E=E, k=k, d=72)
+    logits = mi.fixed_logits(max(T, 1), E, seed=6)[:T]
+    o_idx = O.select_topk(O.selection_keys(logits.numpy(), cfg), cfg)
+    p = O.permutation(o_idx, E)
+    x = mi.make_inputs(cfg.with_(T=max(T, 1)), seed=6, experts=False)["x"][:T]
+    c = shape_of(cfg).cfg()
+    dev = "cuda"
+    n = max(T * k, 1)
+    idx = torch.from_numpy(o_idx.astype(np.int32)).to(dev) if T else torch.zeros(1, dtype=torch.int32, device=dev)
+    xd = x.to(dev) if T else torch.zeros(1, cfg.d, dtype=torch.bfloat16, device=dev)
+    off = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
+    rmap = torch.empty(n, dtype=torch.int32, device=dev)
+    src = torch.empty(n, dtype=torch.int32, device=dev)
+    xp = torch.empty(n, cfg.d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(abi.moe_workspace_size(c), dtype=torch.uint8, device=dev)
+    abi.moe_permute(c, xd, idx, off, rmap, src, xp, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(off), p["offsets"])
+    if T:
+        assert np.array_equal(host(rmap).reshape(T, k), p["row_id_map"])
+        assert np.array_equal(host(src), p["src_token"])
+        assert torch.equal(xp.cpu(), x[torch.from_numpy(p["src_token"].astype(np.int64))])
+
+
+# ---------------------------------------------------------------------------
+# the whole layer, forward (+ backward), every output against the oracle
+# ---------------------------------------------------------------------------
+LAYER_CASES = [
+    # the tiny fp32 workload exactly as specified (normal inputs)
+    (mi.TINY, False, False),
+    _cfg("f32_sigmoid_groups_shared_bwd", T=160, d=64, E=16, k=4, f=48, f_shared=32, dtype="f32",
+         score="sigmoid", n_group=4, topk_group=2, scale=2.5, bias="normal", bias_std=0.05,
+         backward=True),
+    _cfg("f32_softmax_aux_bwd", T=130, d=32, E=8, k=2, f=40, dtype="f32", aux_coeff=1e-2, backward=True),
+    _cfg("f32_softmax_norenorm_bwd", T=96, d=40, E=6, k=3, f=24, dtype="f32", renorm=False, backward=True),
+    _cfg("bf16_qwen3_like_bwd", T=300, d=256, E=16, k=4, f=192, aux_coeff=1e-3, backward=True),
+    _cfg("bf16_dsv3_like_bwd", T=256, d=384, E=32, k=8, f=256, f_shared=256, score="sigmoid", n_group=8,
+         topk_group=4, scale=2.5, bias="normal", bias_std=0.01, backward=True, expert_std=0.02,
+         router_std=0.02),
+    _cfg("bf16_mostly_empty_experts_bwd", T=40, d=128, E=64, k=2, f=64, backward=True),
+    _cfg("bf16_mixtral_like_fwd", T=512, d=512, E=8, k=2, f=512),
+]
+
+
+def _case(c):
+    if isinstance(c, tuple):
+        return c[0], c[1], c[2]
+    return c, c.backward, True
+
+
+@pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: _case(c)[0].name)
+def test_layer_parity(case):
+    cfg, backward, grid = _case(case)
+    print(f"case layer {cfg.name} backward={backward}", flush=True)
+    inp = mi.exact_grid_inputs(cfg, seed=0) if grid else mi.make_inputs(cfg, seed=0)
+    g = run_gpu(cfg, inp, backward, d_aux=0.5)
+    o = run_oracle(cfg, inp, backward, d_aux=0.5)
+    compare_layer(cfg, g, o, backward)
+
+
+def test_layer_deterministic():
+    cfg = _cfg("det", T=300, d=256, E=16, k=4, f=192, f_shared=64, score="sigmoid", n_group=4,
+               topk_group=2, bias="normal", bias_std=0.01, backward=True)
+    print("case determinism", flush=True)
+    inp = mi.make_inputs(cfg, seed=3)
+    a = run_gpu(cfg, inp, True)
+    b = run_gpu(cfg, inp, True)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
