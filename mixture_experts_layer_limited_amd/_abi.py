@@ -48,7 +48,7 @@ _SIGS = {
     "moe_unpermute_combine": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 5 + [_P]),
     "moe_unpermute_combine_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 6 + [_P]),
     "moe_grouped_gemm_swiglu_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 21 + [_P, ctypes.c_size_t, _P]),
-    "moe_router_topk_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 8 + [ctypes.c_float] + [_P] * 3
+    "moe_router_topk_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 7 + [ctypes.c_float] + [_P] * 3
                             + [_P, ctypes.c_size_t, _P]),
     "moe_permute_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 4 + [_P]),
     "moe_trace_begin": (ctypes.c_int, [ctypes.c_int]),

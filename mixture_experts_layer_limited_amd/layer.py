@@ -71,7 +71,7 @@ class MoELayer:
             "idx": e(s.T, s.k, dtype=torch.int32),
             "gates": e(s.T, s.k, dtype=torch.float32),
             "counts": e(s.E, dtype=torch.int32),
-            "aux": e(1, dtype=torch.float32),
+            "aux": e(1, dtype=torch.float32) if s.aux_coeff else None,
             "offsets": e(s.E + 1, dtype=torch.int32),
             "row_id_map": e(s.T, s.k, dtype=torch.int32),
             "src_token": e(rows, dtype=torch.int32),

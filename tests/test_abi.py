@@ -37,6 +37,22 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(m, n), f"binding lacks {n}"
 
 
+def test_binding_signatures_match_header():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    decls = dict(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", src))
+    abi.lib()
+    for name, params in decls.items():
+        params = [p.strip() for p in params.split(",") if p.strip() and p.strip() != "void"]
+        res, args = abi._SIGS[name]
+        assert len(args) == len(params), f"{name}: header has {len(params)} parameters, binding {len(args)}"
+        for p, a in zip(params, args):
+            if re.match(r"(const\s+)?float\s+\w+$", p):
+                assert a is ctypes.c_float, f"{name}: {p}"
+            elif "*" in p:
+                assert a in (ctypes.c_void_p,) or hasattr(a, "_type_"), f"{name}: {p}"
+
+
 def test_status_strings():
     assert abi.moe_status_string(0) == "MOE_OK"
     assert abi.moe_status_string(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
