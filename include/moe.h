@@ -37,7 +37,8 @@
  *   topk_idx, expert_counts, expert_offsets, row_id_map and src_token are
  *   bit-identical to any correct implementation of the rules below given the
  *   same fp32 router logits.
- * - Limits: 1 <= k <= E <= 256, d and f multiples of 8 (f_shared too), T*k and
+ * - Limits: 1 <= k <= E <= 256, d and f multiples of 8 (f_shared too; multiples
+ *   of 64 for calls that run bf16 GEMMs: router with x, experts, backward), T*k and
  *   every matrix dimension below 2^31 elements per row index.
  */
 #ifndef MOE_GFX950_H

@@ -108,6 +108,13 @@ moe_status check_cfg(const moe_cfg* c) {
   return MOE_OK;
 }
 
+// the bf16 GEMM path streams K-contiguous operands in 64-wide slices
+moe_status check_gemm_shapes(const moe_cfg* c) {
+  if (c->dtype == MOE_BF16 && (c->d % 64 || c->f % 64 || c->f_shared % 64))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "bf16 GEMMs need d, f and f_shared to be multiples of 64");
+  return MOE_OK;
+}
+
 #define REQ(p)                                                                          \
   do {                                                                                  \
     if (!(p)) return fail(MOE_ERR_INVALID_ARGUMENT, "argument '%s' must not be NULL", #p); \
@@ -154,14 +161,14 @@ inline void trace_post(const char* name, hipStream_t st) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline int64_t ranges(int64_t T) { return (T + kPermTokensPerRange - 1) / kPermTokensPerRange; }
 inline int64_t router_blocks(int64_t T) { return (T + kRouterTokensPerBlock - 1) / kRouterTokensPerBlock; }
-inline int64_t pad8(int64_t e) { return (e + 7) & ~int64_t(7); }
+inline int64_t pad64(int64_t e) { return (e + 63) & ~int64_t(63); }
 inline size_t elt(const moe_cfg* c) { return c->dtype == MOE_F32 ? 4 : 2; }
 
 size_t ws_bytes_for(const moe_cfg* c) {
   size_t router = 2 * align256((size_t)router_blocks(c->T) * c->E * 4);
   size_t perm = align256((size_t)ranges(c->T) * c->E * 4);
   size_t gemm = align256((size_t)(c->E + 2) * 4);
-  size_t rbwd = align256((size_t)c->T * pad8(c->E) * elt(c));
+  size_t rbwd = align256((size_t)c->T * pad64(c->E) * elt(c));
   size_t m = router;
   if (perm > m) m = perm;
   if (gemm > m) m = gemm;
@@ -212,7 +219,7 @@ moe_status gemm_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* of
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f;
   int* prefix = (int*)ws;
   if (rows > 0) {
-    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf), prefix, st));
+    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E), prefix, st));
     LAUNCH_NAMED("gemm_swiglu_fwd", gemm_swiglu_fwd<T>(x_perm, off, prefix, E, w13, hu, act, rows, d, f, st));
     LAUNCH_NAMED("gemm_down_fwd", gemm_down_fwd<T>(act, off, prefix, E, w2, y_perm, rows, d, f, st));
   }
@@ -234,7 +241,7 @@ moe_status gemm_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_pe
   const bool bf = sizeof(T) == 2;
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
   int* prefix = (int*)ws;
-  if (rows > 0) LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf), prefix, st));
+  if (rows > 0) LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E), prefix, st));
   if (rows > 0)
     LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd", gemm_down_dgrad_swiglu_bwd<T>(dy_perm, off, prefix, E, w2, hu, dhu, rows, d, f, st));
   // weight gradients cover every expert (empty experts get zeros)
@@ -261,7 +268,7 @@ moe_status router_bwd_impl(const moe_cfg* c, const void* x, const void* w_router
   RouterParams p = router_params(c);
   const int T_ = (int)c->T, E = (int)c->E, d = (int)c->d;
   const bool bf = sizeof(T) == 2;
-  const int Ep = bf ? (int)pad8(E) : E;
+  const int Ep = bf ? (int)pad64(E) : E;   // K of the router dgrad: a multiple of 64
   T* dl_store = bf ? (T*)ws : nullptr;
   LAUNCH_NAMED("router_bwd", launch_router_bwd<T>(logits, idx, gates, d_gates, counts, p, d_aux, d_logits, dl_store, Ep, st));
   const void* dl = bf ? (const void*)dl_store : (const void*)d_logits;
@@ -343,6 +350,7 @@ moe_status moe_router_topk(const moe_cfg* cfg, const void* x, const void* w_rout
   CHECK(check_cfg(cfg));
   if ((x == nullptr) != (w_router == nullptr))
     return fail(MOE_ERR_INVALID_ARGUMENT, "x and w_router must both be given or both be NULL");
+  if (x) CHECK(check_gemm_shapes(cfg));
   REQ(logits); REQ(topk_idx); REQ(topk_gates); REQ(expert_counts);
   if (cfg->aux_coeff != 0.0f) REQ(aux_loss);
   ALIGNED(x); ALIGNED(w_router); ALIGNED(logits);
@@ -380,6 +388,7 @@ moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm, const
                                    void* act_shared, void* y_shared, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
+  CHECK(check_gemm_shapes(cfg));
   REQ(x_perm); REQ(expert_offsets); REQ(w13); REQ(w2); REQ(act); REQ(y_perm);
   ALIGNED(x_perm); ALIGNED(w13); ALIGNED(w2); ALIGNED(hu_save); ALIGNED(act); ALIGNED(y_perm);
   if (cfg->f_shared > 0) {
@@ -439,6 +448,7 @@ moe_status moe_grouped_gemm_swiglu_bwd(const moe_cfg* cfg, const void* dy_perm, 
                                        void* dhu_shared, float* dx_partial, void* dws13, void* dws2,
                                        void* workspace, size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
+  CHECK(check_gemm_shapes(cfg));
   REQ(dy_perm); REQ(x_perm); REQ(expert_offsets); REQ(hu_save); REQ(act); REQ(w13); REQ(w2);
   REQ(dhu); REQ(dx_perm); REQ(dw13); REQ(dw2); REQ(dx_partial);
   ALIGNED(dy_perm); ALIGNED(x_perm); ALIGNED(hu_save); ALIGNED(act); ALIGNED(w13); ALIGNED(w2);
@@ -466,6 +476,7 @@ moe_status moe_router_topk_bwd(const moe_cfg* cfg, const void* x, const void* w_
                                const float* d_gates, float d_aux, float* d_logits, void* dw_router,
                                float* dx_partial, void* workspace, size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
+  CHECK(check_gemm_shapes(cfg));
   REQ(x); REQ(w_router); REQ(logits); REQ(topk_idx); REQ(topk_gates); REQ(d_gates); REQ(d_logits);
   REQ(dw_router); REQ(dx_partial);
   if (cfg->aux_coeff != 0.0f) REQ(expert_counts);

@@ -1,6 +1,10 @@
 // Grouped GEMM kernels: the bf16 MFMA path (gfx950 v_mfma_f32_32x32x16_bf16)
 // and a plain fp32 path, over the tile schedules of gemm.hpp.
+#include <stdlib.h>
+
 #include "gemm.hpp"
+#include "gemm_mfma.hpp"
+#include "gemm_regs.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -29,214 +33,6 @@ __global__ __launch_bounds__(256) void tile_prefix_kernel(const int* __restrict_
 hipError_t launch_tile_prefix(const int* offsets, int G, int BM, int* prefix, hipStream_t st) {
   tile_prefix_kernel<<<1, 256, 0, st>>>(offsets, G, BM, prefix);
   return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// bf16 MFMA kernel: 256 threads = 4 waves in a 2x2 arrangement, each wave
-// owning a 64x64 sub-tile as 2x2 blocks of 32x32 MFMA accumulators.
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, typename Epi::P ep, int NT, int MT) {
-  static_assert(BM == 128 && BN == 128, "wave layout assumes 128x128 tiles");
-  constexpr int PITCH = BK + 8;                 // bf16 elements per LDS row
-  constexpr int KCH = BK / 8;                   // 16-byte chunks per row
-  constexpr int A_KC_LOADS = BM * KCH / 256;
-  constexpr int B_KC_LOADS = BN * KCH / 256;
-  constexpr int A_MC_BLKS = (BK / 4) * (BM / 8) / 256;
-  constexpr int B_MC_BLKS = (BK / 4) * (BN / 8) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[BN * PITCH];
-
-  const int total = total_tiles<MODE>(a, NT, MT);
-  if ((int)blockIdx.x >= total) return;
-  const int L = xcd_remap(blockIdx.x, total);
-  TileCoord c;
-  resolve_tile<MODE, BM>(a, L, NT, MT, c);
-  const int nt = c.n0;
-
-  const uint16_t* __restrict__ A = (const uint16_t*)a.A;
-  const uint16_t* __restrict__ B = (const uint16_t*)a.B + (MODE == RAGGED_M ? (int64_t)c.g * a.b_gstride : 0);
-  const int tid = threadIdx.x;
-  const int b_kend = (MODE == RAGGED_K) ? c.k_end : min(c.k_end, a.b_kend);
-
-  // B tile rows resolved once (KC layout): absolute B row or "invalid"
-  int brow[B_KC_LOADS > 0 ? B_KC_LOADS : 1];
-  if (LB == KC) {
-#pragma unroll
-    for (int i = 0; i < B_KC_LOADS; ++i) {
-      int q = tid + i * 256;
-      int r = q / KCH;
-      brow[i] = Epi::b_row(ep, nt, r, BN);
-    }
-  }
-
-  u32x4 ra[LA == KC ? A_KC_LOADS : 4 * A_MC_BLKS];
-  u32x4 rb[LB == KC ? B_KC_LOADS : 4 * B_MC_BLKS];
-
-  auto load_tiles = [&](int k0) {
-    if (LA == KC) {
-#pragma unroll
-      for (int i = 0; i < A_KC_LOADS; ++i) {
-        int q = tid + i * 256;
-        int r = q / KCH, kc = q % KCH;
-        int grow = c.m0 + r, kk = k0 + kc * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (grow < c.m_end && kk < c.k_end) v = *(const u32x4*)(A + (int64_t)grow * a.lda + kk);
-        ra[i] = v;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < A_MC_BLKS; ++i) {
-        int q = tid + i * 256;
-        int kb = q / (BM / 8), mb = q % (BM / 8);
-        int m = c.m0 + mb * 8;
-        bool mok = m + 8 <= a.a_mext;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int kk = k0 + kb * 4 + r;
-          u32x4 v = {0, 0, 0, 0};
-          if (mok && kk < c.k_end) v = *(const u32x4*)(A + (int64_t)kk * a.lda + m);
-          ra[i * 4 + r] = v;
-        }
-      }
-    }
-    if (LB == KC) {
-#pragma unroll
-      for (int i = 0; i < B_KC_LOADS; ++i) {
-        int q = tid + i * 256;
-        int kc = q % KCH;
-        int kk = k0 + kc * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (brow[i] < a.b_next && kk < c.k_end) v = *(const u32x4*)(B + (int64_t)brow[i] * a.ldb + kk);
-        rb[i] = v;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < B_MC_BLKS; ++i) {
-        int q = tid + i * 256;
-        int kb = q / (BN / 8), nb = q % (BN / 8);
-        int n = nt * BN + nb * 8;
-        bool nok = n + 8 <= a.b_next;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int kk = k0 + kb * 4 + r;
-          u32x4 v = {0, 0, 0, 0};
-          if (nok && kk < b_kend) v = *(const u32x4*)(B + (int64_t)kk * a.ldb + n);
-          rb[i * 4 + r] = v;
-        }
-      }
-    }
-  };
-
-  // 4 rows (k..k+3) x 8 columns -> 8 columns x 4 k, written K-contiguous
-  auto store_transposed = [&](uint16_t* s, const u32x4* r4, int row0, int kcol) {
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      int w = m >> 1;
-      uint32_t e0 = (m & 1) ? (r4[0][w] >> 16) : (r4[0][w] & 0xFFFFu);
-      uint32_t e1 = (m & 1) ? (r4[1][w] >> 16) : (r4[1][w] & 0xFFFFu);
-      uint32_t e2 = (m & 1) ? (r4[2][w] >> 16) : (r4[2][w] & 0xFFFFu);
-      uint32_t e3 = (m & 1) ? (r4[3][w] >> 16) : (r4[3][w] & 0xFFFFu);
-      u32x2 o = {e0 | (e1 << 16), e2 | (e3 << 16)};
-      *(u32x2*)(s + (row0 + m) * PITCH + kcol) = o;
-    }
-  };
-
-  auto store_tiles = [&]() {
-    if (LA == KC) {
-#pragma unroll
-      for (int i = 0; i < A_KC_LOADS; ++i) {
-        int q = tid + i * 256;
-        int r = q / KCH, kc = q % KCH;
-        *(u32x4*)(sA + r * PITCH + kc * 8) = ra[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < A_MC_BLKS; ++i) {
-        int q = tid + i * 256;
-        int kb = q / (BM / 8), mb = q % (BM / 8);
-        store_transposed(sA, &ra[i * 4], mb * 8, kb * 4);
-      }
-    }
-    if (LB == KC) {
-#pragma unroll
-      for (int i = 0; i < B_KC_LOADS; ++i) {
-        int q = tid + i * 256;
-        int r = q / KCH, kc = q % KCH;
-        *(u32x4*)(sB + r * PITCH + kc * 8) = rb[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < B_MC_BLKS; ++i) {
-        int q = tid + i * 256;
-        int kb = q / (BN / 8), nb = q % (BN / 8);
-        store_transposed(sB, &rb[i * 4], nb * 8, kb * 4);
-      }
-    }
-  };
-
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  floatx16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  const int klen = c.k_end - c.k_begin;
-  const int nk = (klen + BK - 1) / BK;
-  if (nk > 0) {
-    load_tiles(c.k_begin);
-    store_tiles();
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_tiles(c.k_begin + (kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        af[mb] = *(const bf16x8*)(sA + (wm * 64 + mb * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        bfr[nb] = *(const bf16x8*)(sB + (wn * 64 + nb * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-    }
-    __syncthreads();
-    if (kt + 1 < nk) {
-      store_tiles();
-      __syncthreads();
-    }
-  }
-
-  // epilogue: accumulator element e of block (mb, nb) sits at
-  // row 8*(e/4) + 4*(lane/32) + e%4, column lane%32 of that 32x32 block
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      int lr = wm * 64 + mb * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-      int row = c.m0 + lr;
-      if (row >= c.m_end) continue;
-      if constexpr (Epi::kPaired) {
-        int col = nt * (BN / 2) + wn * 32 + (lane & 31);
-        Epi::at_pair(ep, row, col, acc[mb][0][e], acc[mb][1][e]);
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          int col = nt * BN + wn * 64 + nb * 32 + (lane & 31);
-          Epi::at(ep, c.g, row, col, acc[mb][nb][e]);
-        }
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -281,24 +77,110 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(GemmArgs a, typename E
 }
 
 // ---------------------------------------------------------------------------
-// Launchers.  `mtiles_bound` = upper bound of m-tiles (RAGGED_M), n = logical
-// N (gate columns for the paired SwiGLU epilogue).
+// Launchers.  The bf16 path runs a persistent grid of 128x128 tiles with 2x2
+// waves; the fp32 path one 16x16 tile per workgroup.  For RAGGED_M the tile
+// count is only bounded on the host (sum over experts of ceil(n_e/BM) <=
+// rows/BM + G); the kernels read the exact count on the device.
 // ---------------------------------------------------------------------------
+
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
+static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int n_logical, int rows_total,
+                              hipStream_t st, bool persistent) {
+  using C = TileCfg<BM, BN, WM, WN, STAGES>;
+  constexpr bool paired = Epi::kPaired;
+  const int bn_cols = paired ? BN / 2 : BN;
+  const int NT = (n_logical + bn_cols - 1) / bn_cols;
+  const int MT = (MODE == RAGGED_M) ? 0 : (a.M + BM - 1) / BM;
+  int64_t tiles;                          // upper bound of the logical tiles
+  if (MODE == RAGGED_M) tiles = (int64_t)((rows_total + BM - 1) / BM + a.G) * NT;
+  else if (MODE == RAGGED_K) tiles = (int64_t)a.G * MT * NT;
+  else tiles = (int64_t)MT * NT;
+  if (tiles <= 0) return hipSuccess;
+  constexpr int kLdsPerCU = 160 * 1024;
+  const int per_cu = kLdsPerCU / C::LDS_BYTES > 0 ? kLdsPerCU / C::LDS_BYTES : 1;
+  int64_t grid = persistent ? (int64_t)device_cus() * per_cu : tiles;
+  if (tiles < grid) grid = tiles;
+  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, STAGES, LA, LB, MODE, Epi>;
+  static bool attr_set = false;           // one attribute per instantiation
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, ep, NT, MT);
+  return hipGetLastError();
+}
+
+// Kernel of the bf16 path: 3 = register-staged 128x128 (gemm_regs.hpp, the
+// default); DMA-fed LDS ring (gemm_mfma.hpp) with 0 = 128x128 x 4 stages,
+// 1 = 128x256 x 3 stages, 2 = 256x128 x 3 stages.  MOE_TILE overrides the
+// choice for tuning runs.
+static int tile_choice() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MOE_TILE");
+    v = e ? atoi(e) : 3;
+    if (v < 0 || v > 3) v = 3;
+  }
+  return v;
+}
+
+template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
+static hipError_t launch_regs(const GemmArgs& a, const typename Epi::P& ep, int n_logical, int rows_total,
+                              hipStream_t st) {
+  using C = RegTile;
+  const int bn_cols = Epi::kPaired ? C::BN / 2 : C::BN;
+  const int NT = (n_logical + bn_cols - 1) / bn_cols;
+  const int MT = (MODE == RAGGED_M) ? 0 : (a.M + C::BM - 1) / C::BM;
+  int64_t grid;
+  if (MODE == RAGGED_M) grid = (int64_t)((rows_total + C::BM - 1) / C::BM + a.G) * NT;
+  else if (MODE == RAGGED_K) grid = (int64_t)a.G * MT * NT;
+  else grid = (int64_t)MT * NT;
+  if (grid <= 0) return hipSuccess;
+  auto kern = gemm_regs_kernel<LA, LB, MODE, Epi>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, ep, NT, MT);
+  return hipGetLastError();
+}
+
+// Tile rows of the ragged-row schedule.  The device tile prefix is built with
+// this value and the kernel resolves its tiles with its own BM: they must agree.
+int gemm_tile_rows(bool bf16, int64_t, int) { return bf16 ? (tile_choice() == 2 ? 256 : 128) : 16; }
+
 template <class T, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
 static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int rows_total, hipStream_t st) {
-  constexpr bool paired = Epi::kPaired;
   int n_logical;
-  if constexpr (paired) n_logical = (int)ep.f; else n_logical = a.N;
+  if constexpr (Epi::kPaired) n_logical = (int)ep.f; else n_logical = a.N;
   if constexpr (sizeof(T) == 2) {
-    constexpr int BM = 128, BN = 128, BK = 64;
-    const int NT = (n_logical + (paired ? BN / 2 : BN) - 1) / (paired ? BN / 2 : BN);
-    const int MT = (MODE == RAGGED_M) ? 0 : (a.M + BM - 1) / BM;
-    int64_t grid;
-    if (MODE == RAGGED_M) grid = (int64_t)((rows_total + BM - 1) / BM + a.G) * NT;
-    else if (MODE == RAGGED_K) grid = (int64_t)a.G * MT * NT;
-    else grid = (int64_t)MT * NT;
-    if (grid <= 0) return hipSuccess;
-    gemm_mfma_kernel<BM, BN, BK, LA, LB, MODE, Epi><<<(unsigned)grid, 256, 0, st>>>(a, ep, NT, MT);
+    // weight gradients (short contractions) run persistent so that a tile's
+    // stores overlap the next tile's loads; the rest one tile per workgroup
+    const bool persistent = MODE == RAGGED_K;
+    const int t = tile_choice();
+    if (t == 3) return launch_regs<LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st);
+    if (t == 1)
+      return launch_mfma<128, 256, 2, 2, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+    if (t == 2)
+      return launch_mfma<256, 128, 2, 2, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+    return launch_mfma<128, 128, 2, 2, 4, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
   } else {
     const int NT = (n_logical + 15) / 16;
     const int MT = (MODE == RAGGED_M) ? 0 : (a.M + 15) / 16;
@@ -308,11 +190,21 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
     else grid = (int64_t)MT * NT;
     if (grid <= 0) return hipSuccess;
     gemm_simple_kernel<T, LA, LB, MODE, Epi><<<(unsigned)grid, 256, 0, st>>>(a, ep, NT, MT);
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
-int gemm_tile_rows(bool bf16) { return bf16 ? 128 : 16; }
+// Weight gradients of experts without rows are exactly zero; the MFMA kernel
+// skips their (empty) contractions, so they are filled here.
+__global__ __launch_bounds__(256) void zero_empty_groups_kernel(const int* __restrict__ offsets,
+                                                                u32x4* __restrict__ out, int64_t vec_per_group) {
+  const int g = blockIdx.y;
+  if (offsets[g + 1] != offsets[g]) return;
+  u32x4* o = out + g * vec_per_group;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vec_per_group; i += (int64_t)gridDim.x * blockDim.x)
+    o[i] = z;
+}
 
 template <class T>
 hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int T_, int E, int d,
@@ -408,6 +300,12 @@ hipError_t gemm_wgrad(const void* P_, int M, const void* Q_, int N, const int* o
   a.M = M; a.N = N; a.K = K_dense; a.a_mext = M; a.b_next = N; a.b_kend = K_dense;
   a.offsets = offsets; a.G = offsets ? G : 1;
   typename EpiStore<T>::P ep{(T*)dw, N, (int64_t)M * N, M, N};
+  if (sizeof(T) == 2 && offsets) {
+    const int64_t vec = (int64_t)M * N * sizeof(T) / 16;   // M*N is a multiple of 64
+    zero_empty_groups_kernel<<<dim3(64, G), 256, 0, st>>>(offsets, (u32x4*)dw, vec);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T>>(a, ep, 0, st);
 }
 

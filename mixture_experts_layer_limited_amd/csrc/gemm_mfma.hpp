@@ -1,0 +1,407 @@
+// bf16 MFMA grouped-GEMM kernel for gfx950 (v_mfma_f32_32x32x16_bf16).
+//
+// Data path.  Operand tiles go from global memory straight into LDS with
+// buffer_load_dwordx4 ... lds (16 bytes per lane, written to LDS in lane
+// order from the M0 base), so no registers are spent on staging and STAGES
+// K-slices of 64 can be in flight in an LDS ring.  Each operand of a tile gets
+// a buffer resource whose range ends where its valid rows end, and each lane a
+// 32-bit offset computed once per tile; a slice advances only the scalar
+// offset.  Loads outside the range return zeros, which masks rows past an
+// expert's end, the ragged contraction of weight gradients, and rows past N
+// (those lanes get an offset beyond any range).  K-contiguous operands need K
+// to be a multiple of 64.
+//
+// LDS layouts (16-byte chunks; LDS serves 64 banks, 16 lanes of a 16-byte read
+// or 32 lanes of an 8-byte read per cycle):
+//   K-contiguous operand ("KC"): row r holds its 64 K values as 8 chunks,
+//     logical chunk c at position c ^ ((r >> 1) & 7).  Fragments are read with
+//     ds_read_b128; the 16 lanes of a cycle read 16 consecutive rows (8 even
+//     rows in one half of the banks, 8 odd rows in the other) at 8 distinct
+//     positions each.
+//   Row-contiguous operand ("MC", the weight in dgrad, both operands in wgrad):
+//     the slice is kept as it lies in memory, 64 K-rows of ROWS values (ROWS/8
+//     chunks), logical chunk c of K-row k at position c ^ (2 (k & 3) | 8 c1),
+//     c1 = bit 1 of c.  Fragments are read with ds_read_b64_tr_b16: in each
+//     group of 16 lanes, lane i receives element i%4 of the 8-byte piece
+//     addressed by lane i/4 + 4j (j = 0..3).  Pointing lane q at K-row
+//     k0 + q/4, columns n0 + 4(q%4) .. +3 hands lane i the four K values
+//     k0..k0+3 of column n0 + i -- an MFMA fragment straight from the
+//     row-contiguous layout.  A cycle's 32 lanes touch 4 K-rows x 4 chunks,
+//     which the XOR spreads over all 16 chunk positions of the 64 banks.
+//   Per-lane read offsets are computed once; the K step enters as an
+//   immediate offset and the ring stage as one add per slice.
+//
+// Schedule.  A workgroup walks rounds r = 0, 1, ...: round r covers logical
+// tiles [r G, (r+1) G) (G = grid size), spread so each XCD gets a contiguous run
+// (tiles running together on one XCD are neighbours in the expert-major order
+// and share weight / activation panels in its L2).  With G >= tiles this is one
+// tile per workgroup; with a smaller grid the kernel is persistent.  The main
+// loop walks (tile, slice) pairs: the DMA for the pair STAGES-1 ahead is issued
+// before the current pair is multiplied, so loads of the next tile overlap the
+// current tile's last slices and its epilogue.  Tiles with an empty
+// contraction are skipped (the caller zero-fills them).
+//
+// The MFMA takes the B fragment first, so a lane's accumulator holds four
+// consecutive output columns (element e of a block: column 8*(e/4) +
+// 4*(lane/32) + e%4, row lane%32) and the epilogue stores 4-column vectors.
+//
+// Synchronisation: s_barrier without a memory fence (a fenced barrier would
+// drain every in-flight DMA) and explicit s_waitcnt vmcnt(N): a lane's DMA for
+// slice s is complete once at most N of its later vector-memory operations are
+// outstanding; after an epilogue (global stores and loads) the wait is vmcnt(0).
+#pragma once
+
+#include "gemm.hpp"
+
+namespace moe {
+
+#define MOE_LDS __attribute__((address_space(3)))
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4i16;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short v8i16;
+
+constexpr int kRawBufferFlags = 0x00020000;   // raw (unformatted) buffer, gfx9 family
+constexpr uint32_t kOffRange = 0x80000000u;   // lane offset that is outside every range
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct TileCfg {
+  static constexpr int BK = 64;
+  static constexpr int NW = WM * WN;
+  static constexpr int NTHR = 64 * NW;
+  static constexpr int FM = BM / (32 * WM);
+  static constexpr int FN = BN / (32 * WN);
+  static constexpr int A_BYTES = BM * 128;                 // one operand slice in LDS
+  static constexpr int B_BYTES = BN * 128;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int A_DMA = BM * 8 / 64 / NW;           // DMA instructions per wave per slice
+  static constexpr int B_DMA = BN * 8 / 64 / NW;
+  static_assert(FM >= 1 && FN >= 1 && BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile");
+  static_assert(A_DMA * 64 * NW == BM * 8 && B_DMA * 64 * NW == BN * 8, "DMA split");
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "row-contiguous layout needs >= 16 chunks per K-row");
+  static_assert(STAGES >= 2, "stages");
+  static_assert(STAGE_BYTES <= 65536, "read immediates");
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferFlags);
+}
+
+// logical chunk -> position helpers
+__device__ __forceinline__ int kc_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int mc_mask(int k, int c) { return ((k & 3) << 1) | (((c >> 1) & 1) << 3); }
+
+// Per-lane byte offsets of one operand slice's DMA (relative to the operand's
+// resource base); KC: element (i, k) at i*ld + k (i relative to the base row);
+// MC: element (i, k) at k*ld + i (k relative to the base K-row).
+template <OpLayout L, int ROWS, int NDMA, int NW>
+struct DmaPlan {
+  uint32_t off[NDMA];
+
+  // KC: rowv(r) = row of tile row r relative to the resource base, or -1
+  template <class RowFn>
+  __device__ __forceinline__ void plan_kc(int64_t ld, RowFn rowv) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int p = (wave + j * NW) * 64 + lane;
+      const int r = p >> 3, c = (p & 7) ^ kc_swz(r);
+      const int gi = rowv(r);
+      off[j] = gi >= 0 ? (uint32_t)((int64_t)gi * ld * 2 + c * 16) : kOffRange;
+    }
+  }
+  // MC: columns i0 + 8c (relative to the base); every K-row 0..63 of the slice
+  __device__ __forceinline__ void plan_mc(int64_t ld, int i0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int CPR = ROWS / 8;
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int p = (wave + j * NW) * 64 + lane;
+      const int k = p / CPR, cp = p % CPR;
+      const int c1 = ((cp >> 1) & 1) ^ (k & 1);             // bit 1 of the logical chunk
+      const int c = cp ^ (((k & 3) << 1) | (c1 << 3));
+      off[j] = (uint32_t)((int64_t)k * ld * 2 + (int64_t)(i0 + c * 8) * 2);
+    }
+  }
+  // one slice: instruction j fills chunk positions (wave + j*NW)*64 .. +63
+  // (device pass only: in the host pass this builtin inside a helper makes the
+  // compiler drop the launch stubs of later kernel instantiations)
+  __device__ __forceinline__ void issue(const void* rbase, uint32_t rbytes, uint32_t soff, uint32_t lds_byte) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int wave = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(rbase, rbytes);
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const uint32_t dst = lds_byte + (uint32_t)((wave + j * NW) * 64 * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MOE_LDS void*)(uintptr_t)dst, 16, off[j], soff, 0, 0);
+    }
+#endif
+  }
+};
+
+// Per-lane LDS read offsets (bytes within an operand slice) of the fragments
+// a wave reads: NF fragments of 32 tile rows starting at row0 + 32 f.
+template <OpLayout L, int ROWS, int NF>
+struct FragPlan {
+  uint32_t off[L == KC ? 4 : NF];   // KC: per K-step (same for every fragment); MC: per fragment
+
+  __device__ __forceinline__ void init(int row0) {
+    const int lane = threadIdx.x & 63;
+    if (L == KC) {
+      const int r = lane & 31, h = lane >> 5;               // row0 is a multiple of 32
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        off[kk] = (uint32_t)((row0 + r) * 128 + (((2 * kk + h) ^ kc_swz(r)) * 16));
+    } else {
+      constexpr int CPR = ROWS / 8;
+      const int g = lane >> 4, q = lane & 15;
+      const int klane = 8 * (g >> 1) + (q >> 2);           // K-row within a 16-step, t = 0
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int n = row0 + 32 * f + 16 * (g & 1) + 4 * (q & 3);
+        const int c = n >> 3, half = q & 1;
+        off[f] = (uint32_t)(klane * CPR * 16 + ((c ^ mc_mask(klane, c)) * 16) + half * 8);
+      }
+    }
+  }
+  // fragment f, K-step kk; `base` = byte address of the operand slice
+  __device__ __forceinline__ bf16x8 read(uint32_t base, int f, int kk) const {
+    if (L == KC) {
+      const MOE_LDS bf16x8* p = (const MOE_LDS bf16x8*)(uintptr_t)(base + off[kk] + f * 32 * 128);
+      return *p;
+    } else {
+      constexpr int CPR = ROWS / 8;
+      // K-rows kk*16 + {0..3} and kk*16 + {4..7}: k & 3 is unchanged, so the XOR is too
+      const uint32_t a = base + off[f] + (uint32_t)(kk * 16 * CPR * 16);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS v4i16*)(uintptr_t)a);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS v4i16*)(uintptr_t)(a + 4 * CPR * 16));
+      v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, v);
+    }
+  }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// position in the (tile, slice) sequence of one workgroup
+struct SliceIter {
+  int r;          // round of the current tile (-1: finished)
+  int ks, nk;     // slice within the tile, slices of the tile
+  TileCoord c;
+};
+
+template <int BM, int BN, int WM, int WN, int STAGES, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typename Epi::P ep, int NT, int MT) {
+  using C = TileCfg<BM, BN, WM, WN, STAGES>;
+  constexpr int BK = C::BK, FM = C::FM, FN = C::FN;
+  constexpr int DMA_PER_SLICE = C::A_DMA + C::B_DMA;
+  extern __shared__ u32x4 smem[];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(MOE_LDS void*)smem;
+
+  const int total = total_tiles<MODE>(a, NT, MT);
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // next round >= r holding a tile of this workgroup with a non-empty contraction
+  auto settle = [&](int r, SliceIter& it) {
+    for (;; ++r) {
+      const int base = r * G;
+      if (base >= total) break;
+      const int cnt = min(G, total - base);
+      if (b >= cnt) break;
+      resolve_tile<MODE, BM>(a, base + xcd_remap(b, cnt), NT, MT, it.c);
+      it.nk = (it.c.k_end - it.c.k_begin + BK - 1) / BK;
+      // a tile starting past its group's rows has nothing to do (only a tile
+      // prefix built for another tile height could produce one)
+      if (it.c.m0 >= it.c.m_end) it.nk = 0;
+      if (it.nk > 0) {
+        it.r = r;
+        it.ks = 0;
+        return;
+      }
+    }
+    it.r = -1;
+  };
+
+  // DMA state of the load iterator: resources, per-lane offsets, slice strides
+  DmaPlan<LA, BM, C::A_DMA, C::NW> pa;
+  DmaPlan<LB, BN, C::B_DMA, C::NW> pb;
+  const void* ra_base = nullptr;   // operand resources: base address and byte range
+  const void* rb_base = nullptr;
+  uint32_t ra_bytes = 0, rb_bytes = 0;
+  uint32_t soa = 0, sob = 0;
+  const uint32_t stride_a = LA == KC ? BK * 2 : (uint32_t)(BK * a.lda * 2);
+  const uint32_t stride_b = LB == KC ? BK * 2 : (uint32_t)(BK * a.ldb * 2);
+
+  auto plan_tile = [&](const TileCoord& c) {
+    const uint16_t* A = (const uint16_t*)a.A;
+    const uint16_t* B = (const uint16_t*)a.B + (MODE == RAGGED_M ? (int64_t)c.g * a.b_gstride : 0);
+    if (LA == KC) {
+      // rows m0 .. m_end-1, K = lda
+      const int nrows = min(c.m_end - c.m0, BM);
+      ra_base = A + (int64_t)c.m0 * a.lda;
+      ra_bytes = (uint32_t)(nrows * a.lda * 2);
+      pa.plan_kc(a.lda, [&](int r) { return r < nrows ? r : -1; });
+    } else {
+      // K-rows k_begin .. k_end-1, columns m0 ..
+      ra_base = A + (int64_t)c.k_begin * a.lda;
+      ra_bytes = (uint32_t)((int64_t)(c.k_end - c.k_begin) * a.lda * 2);
+      pa.plan_mc(a.lda, c.m0);
+    }
+    const int nt = c.n0;
+    if (LB == KC) {
+      rb_base = B;
+      rb_bytes = (uint32_t)((int64_t)a.b_next * a.ldb * 2);
+      pb.plan_kc(a.ldb, [&](int r) {
+        int g;
+        if constexpr (Epi::kPaired) g = Epi::template b_row_paired<BN, WN>(ep, nt, r);
+        else g = nt * BN + r;
+        return g < a.b_next ? g : -1;
+      });
+    } else {
+      const int b_kend = (MODE == RAGGED_K) ? c.k_end : min(c.k_end, a.b_kend);
+      rb_base = B + (int64_t)c.k_begin * a.ldb;
+      rb_bytes = (uint32_t)((int64_t)max(b_kend - c.k_begin, 0) * a.ldb * 2);
+      pb.plan_mc(a.ldb, nt * BN);
+    }
+    soa = 0;
+    sob = 0;
+  };
+  auto issue = [&](int stage) {
+    const uint32_t s = lds0 + stage * C::STAGE_BYTES;
+    pa.issue(ra_base, ra_bytes, soa, s);
+    pb.issue(rb_base, rb_bytes, sob, s + C::A_BYTES);
+    soa += stride_a;
+    sob += stride_b;
+  };
+
+  FragPlan<LA, BM, FM> fa;
+  FragPlan<LB, BN, FN> fb;
+  fa.init(wm * (BM / WM));
+  fb.init(wn * (BN / WN));
+
+  floatx16 acc[FM][FN];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  };
+
+  // epilogue: row = lane%32 of the block, columns 8*(e/4) + 4*(lane/32) + 0..3
+  auto epilogue = [&](const TileCoord& c) {
+    const int nt = c.n0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = c.m0 + wm * (BM / WM) + i * 32 + (lane & 31);
+      if (row >= c.m_end) continue;
+      if constexpr (Epi::kPaired) {
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = nt * (BN / 2) + wn * (BN / WN / 2) + j * 32 + q * 8 + (lane >> 5) * 4;
+            float h[4], u[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              h[e] = acc[i][j][4 * q + e];
+              u[e] = acc[i][j + FN / 2][4 * q + e];
+            }
+            Epi::at_pair4(ep, row, col, h, u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = nt * BN + wn * (BN / WN) + j * 32 + q * 8 + (lane >> 5) * 4;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+            Epi::at4(ep, c.g, row, col, v);
+          }
+        }
+      }
+    }
+  };
+
+  SliceIter comp, ld;
+  settle(0, comp);
+  if (comp.r < 0) return;
+  ld = comp;
+  plan_tile(ld.c);
+
+  auto advance_ld = [&]() {
+    if (++ld.ks >= ld.nk) {
+      settle(ld.r + 1, ld);
+      if (ld.r >= 0) plan_tile(ld.c);
+    }
+  };
+
+  // prologue: the first STAGES-1 slices
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    if (ld.r >= 0) {
+      issue(s);
+      advance_ld();
+      ++issued;
+    }
+  }
+  zero_acc();
+
+  int n = 0;                      // index of the slice being multiplied
+  bool stores_pending = false;
+  for (;;) {
+    // wait for slice n: later slices already issued may stay in flight
+    if (!stores_pending && issued - n - 1 == STAGES - 2) wait_vmcnt<(STAGES - 2) * DMA_PER_SLICE>();
+    else wait_vmcnt<0>();
+    stores_pending = false;
+    bar();
+    if (ld.r >= 0) {
+      issue(issued % STAGES);     // the stage multiplied in the previous iteration
+      advance_ld();
+      ++issued;
+    }
+    const uint32_t sa = lds0 + (n % STAGES) * C::STAGE_BYTES;
+    const uint32_t sb = sa + C::A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = fa.read(sa, i, kk);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = fb.read(sb, j, kk);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    if (comp.ks == comp.nk - 1) {
+      epilogue(comp.c);
+      zero_acc();
+      stores_pending = true;
+    }
+    ++n;
+    if (++comp.ks >= comp.nk) settle(comp.r + 1, comp);
+    if (comp.r < 0) break;
+  }
+}
+
+}  // namespace moe

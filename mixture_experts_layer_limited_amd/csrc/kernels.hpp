@@ -50,7 +50,7 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
 
 // gemm.hip
 hipError_t launch_tile_prefix(const int* offsets, int G, int BM, int* prefix, hipStream_t st);
-int gemm_tile_rows(bool bf16);
+int gemm_tile_rows(bool bf16, int64_t rows, int G);
 template <class T>
 hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int T_, int E, int d,
                               hipStream_t st);
