@@ -28,6 +28,36 @@ import moe_inputs as mi  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
+# HBM bytes per launch of a kernel as read from rocprofv3 counters: FETCH_SIZE
+# and WRITE_SIZE (KiB per dispatch) of one layer pass at the bench workload,
+# each times the factor that makes the same counter match a plain 1 GiB copy
+# (FETCH_SIZE reads 512 MiB for it: x2; WRITE_SIZE reads 1 GiB: x1).  A figure
+# only holds for the kernel sources it was taken with: `src_sha` is the sha256
+# of the GEMM sources at that time, and a mismatch reports traffic as null.
+GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm.hip")
+TRAFFIC_MEASURED = {
+    # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
+    "gemm_wgrad_gateup": {"src_sha": "9d0430006e382630d192be9819c36b3bc40492b2ad22bac921983ffc58138097",
+                          "fetch_bytes": 10584568012, "write_bytes": 15032385536},
+}
+
+
+def gemm_src_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_limited_amd", "csrc")
+    for name in GEMM_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    t = TRAFFIC_MEASURED.get(kernel)
+    if not t or t["src_sha"] != gemm_src_sha():
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
 
 def step_flops(cfg: mi.MoEConfig, backward: bool = True) -> float:
     """Algorithmic FLOPs of one layer pass: router 2TdE, routed experts 6Tk d f,
@@ -117,9 +147,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="deepseek_v3", choices=sorted(mi.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB buffer 3 times (scale reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
+                          "launches": 3}))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this layer runs on one GPU; multi-GPU sharding is not built "
                                    "(see DESIGN.md: how the path would shard)", "n_gpus": args.gpus}))
@@ -184,13 +226,13 @@ def main():
         if fl / by < ridge:
             ach = by / t / 1e9
             roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom),
                     "algorithmic_bytes": by, "algorithmic_flops": fl,
                     "achieved_tflops": round(fl / t / 1e12, 1)}
         else:
             ach = fl / t / 1e12
             roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom),
                     "algorithmic_bytes": by, "algorithmic_flops": fl}
         for n, (fl2, by2) in work.items():
             if n in kern:

@@ -245,15 +245,15 @@ moe_status gemm_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_pe
   if (rows > 0)
     LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd", gemm_down_dgrad_swiglu_bwd<T>(dy_perm, off, prefix, E, w2, hu, dhu, rows, d, f, st));
   // weight gradients cover every expert (empty experts get zeros)
-  LAUNCH_NAMED("gemm_wgrad_down", gemm_wgrad<T>(dy_perm, d, act, f, off, E, 0, dw2, st));
+  LAUNCH_NAMED("gemm_wgrad_down", gemm_wgrad<T>(dy_perm, d, act, f, off, E, 0, dw2, 1, st));
   if (rows > 0) LAUNCH_NAMED("gemm_gateup_dgrad", gemm_gateup_dgrad<T>(dhu, off, prefix, E, w13, dx_perm, false, rows, d, f, st));
-  LAUNCH_NAMED("gemm_wgrad_gateup", gemm_wgrad<T>(dhu, 2 * f, x_perm, d, off, E, 0, dw13, st));
+  LAUNCH_NAMED("gemm_wgrad_gateup", gemm_wgrad<T>(dhu, 2 * f, x_perm, d, off, E, 0, dw13, 0, st));
   if (c->f_shared > 0) {
     const int fs = (int)c->f_shared;
     if (T_ > 0) LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd_shared", gemm_down_dgrad_swiglu_bwd<T>(dy, nullptr, nullptr, 1, ws2, hu_s, dhu_s, T_, d, fs, st));
-    LAUNCH_NAMED("gemm_wgrad_down_shared", gemm_wgrad<T>(dy, d, act_s, fs, nullptr, 1, T_, dws2, st));
+    LAUNCH_NAMED("gemm_wgrad_down_shared", gemm_wgrad<T>(dy, d, act_s, fs, nullptr, 1, T_, dws2, 3, st));
     if (T_ > 0) LAUNCH_NAMED("gemm_gateup_dgrad_shared", gemm_gateup_dgrad<T>(dhu_s, nullptr, nullptr, 1, ws13, dx_partial, true, T_, d, fs, st));
-    LAUNCH_NAMED("gemm_wgrad_gateup_shared", gemm_wgrad<T>(dhu_s, 2 * fs, x, d, nullptr, 1, T_, dws13, st));
+    LAUNCH_NAMED("gemm_wgrad_gateup_shared", gemm_wgrad<T>(dhu_s, 2 * fs, x, d, nullptr, 1, T_, dws13, 2, st));
   } else {
     LAUNCH_NAMED("fill_f32", launch_fill_f32(dx_partial, (int64_t)T_ * d, 0.0f, st));
   }

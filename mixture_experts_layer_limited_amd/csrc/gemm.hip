@@ -124,18 +124,24 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
   return hipGetLastError();
 }
 
-// Kernel of the bf16 path: 3 = register-staged 128x128 (gemm_regs.hpp, the
-// default); DMA-fed LDS ring (gemm_mfma.hpp) with 0 = 128x128 x 4 stages,
-// 1 = 128x256 x 3 stages, 2 = 256x128 x 3 stages.  MOE_TILE overrides the
-// choice for tuning runs.
-static int tile_choice() {
-  static int v = -1;
+// Kernel of the bf16 path: 3 = register-staged 128x128, one tile per
+// workgroup (gemm_regs.hpp); 4 / 5 = its persistent pipelined form with
+// K-slices of 64 (two LDS stages) / 128 (one stage); DMA-fed LDS ring (gemm_mfma.hpp)
+// with 0 = 128x128 x 4 stages, 1 = 128x256 x 3 stages, 2 = 256x128 x 3 stages.
+// MOE_TILE / MOE_TILE_WGRAD override the choice for tuning runs.
+static int env_choice(const char* name, int dflt) {
+  const char* e = getenv(name);
+  int v = e ? atoi(e) : dflt;
+  return (v < 0 || v > 5) ? dflt : v;
+}
+// ragged-row and dense contractions (MOE_TILE) / weight gradients (MOE_TILE_WGRAD)
+static int tile_choice(bool wgrad = false) {
+  static int v = -1, w = -1;
   if (v < 0) {
-    const char* e = getenv("MOE_TILE");
-    v = e ? atoi(e) : 3;
-    if (v < 0 || v > 3) v = 3;
+    v = env_choice("MOE_TILE", 3);
+    w = env_choice("MOE_TILE_WGRAD", getenv("MOE_TILE") ? v : 4);
   }
-  return v;
+  return wgrad ? w : v;
 }
 
 template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
@@ -162,6 +168,33 @@ static hipError_t launch_regs(const GemmArgs& a, const typename Epi::P& ep, int 
   return hipGetLastError();
 }
 
+template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi, int BK>
+static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int n_logical, int rows_total,
+                              hipStream_t st) {
+  using C = PipeCfg<BK>;
+  const int bn_cols = Epi::kPaired ? C::BN / 2 : C::BN;
+  const int NT = (n_logical + bn_cols - 1) / bn_cols;
+  const int MT = (MODE == RAGGED_M) ? 0 : (a.M + C::BM - 1) / C::BM;
+  int64_t tiles;                          // upper bound of the logical tiles
+  if (MODE == RAGGED_M) tiles = (int64_t)((rows_total + C::BM - 1) / C::BM + a.G) * NT;
+  else if (MODE == RAGGED_K) tiles = (int64_t)a.G * MT * NT;
+  else tiles = (int64_t)MT * NT;
+  if (tiles <= 0) return hipSuccess;
+  if (a.G > kMaxExperts) return hipErrorInvalidValue;
+  int64_t grid = (int64_t)device_cus() * 2;   // two workgroups fit a CU's LDS
+  if (tiles < grid) grid = tiles;
+  auto kern = gemm_pipe_kernel<LA, LB, MODE, Epi, BK>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, ep, NT, MT);
+  return hipGetLastError();
+}
+
 // Tile rows of the ragged-row schedule.  The device tile prefix is built with
 // this value and the kernel resolves its tiles with its own BM: they must agree.
 int gemm_tile_rows(bool bf16, int64_t, int) { return bf16 ? (tile_choice() == 2 ? 256 : 128) : 16; }
@@ -174,8 +207,16 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
     // weight gradients (short contractions) run persistent so that a tile's
     // stores overlap the next tile's loads; the rest one tile per workgroup
     const bool persistent = MODE == RAGGED_K;
-    const int t = tile_choice();
+    const int t = tile_choice(MODE == RAGGED_K);
     if (t == 3) return launch_regs<LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st);
+    if (t >= 4) {
+      bool aligned = true;      // the staged epilogue stores 16-byte row pieces
+      if constexpr (Epi::kStaged)
+        aligned = ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0;
+      if (!aligned) return launch_regs<LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st);
+      if (t == 5) return launch_pipe<LA, LB, MODE, Epi, 128>(a, ep, n_logical, rows_total, st);
+      return launch_pipe<LA, LB, MODE, Epi, 64>(a, ep, n_logical, rows_total, st);
+    }
     if (t == 1)
       return launch_mfma<128, 256, 2, 2, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
     if (t == 2)
@@ -194,12 +235,13 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
   }
 }
 
-// Weight gradients of experts without rows are exactly zero; the MFMA kernel
-// skips their (empty) contractions, so they are filled here.
+// Weight gradients of experts without rows (or of a dense contraction over
+// no rows) are exactly zero; the MFMA kernels skip empty contractions, so
+// those outputs are filled here.
 __global__ __launch_bounds__(256) void zero_empty_groups_kernel(const int* __restrict__ offsets,
                                                                 u32x4* __restrict__ out, int64_t vec_per_group) {
   const int g = blockIdx.y;
-  if (offsets[g + 1] != offsets[g]) return;
+  if (offsets && offsets[g + 1] != offsets[g]) return;    // NULL offsets: one empty group
   u32x4* o = out + g * vec_per_group;
   const u32x4 z = {0u, 0u, 0u, 0u};
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vec_per_group; i += (int64_t)gridDim.x * blockDim.x)
@@ -291,22 +333,34 @@ hipError_t gemm_gateup_dgrad(const void* dhu, const int* offsets, const int* til
 }
 
 // dW[g] (M x N) = sum over rows r of group g: P[r, m] Q[r, n]
-// (P [rows, M], Q [rows, N] both read with the row as the contraction index)
+// (P [rows, M], Q [rows, N] both read with the row as the contraction index).
+// `site` (0..3) selects a distinct kernel symbol per call site.
+template <class T, int kSite>
+static hipError_t wgrad_site(const GemmArgs& a, void* dw, int M, int N, hipStream_t st) {
+  typename EpiStore<T, kSite>::P ep{(T*)dw, N, (int64_t)M * N, M, N};
+  return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T, kSite>>(a, ep, 0, st);
+}
+
 template <class T>
 hipError_t gemm_wgrad(const void* P_, int M, const void* Q_, int N, const int* offsets, int G,
-                      int K_dense, void* dw, hipStream_t st) {
+                      int K_dense, void* dw, int site, hipStream_t st) {
   GemmArgs a{};
   a.A = P_; a.lda = M; a.B = Q_; a.ldb = N;
   a.M = M; a.N = N; a.K = K_dense; a.a_mext = M; a.b_next = N; a.b_kend = K_dense;
   a.offsets = offsets; a.G = offsets ? G : 1;
-  typename EpiStore<T>::P ep{(T*)dw, N, (int64_t)M * N, M, N};
-  if (sizeof(T) == 2 && offsets) {
+  if (sizeof(T) == 2 && (offsets || K_dense == 0)) {
+    // the bf16 kernels skip tiles without a contraction: zero those outputs
     const int64_t vec = (int64_t)M * N * sizeof(T) / 16;   // M*N is a multiple of 64
-    zero_empty_groups_kernel<<<dim3(64, G), 256, 0, st>>>(offsets, (u32x4*)dw, vec);
+    zero_empty_groups_kernel<<<dim3(64, offsets ? G : 1), 256, 0, st>>>(offsets, (u32x4*)dw, vec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T>>(a, ep, 0, st);
+  switch (site) {
+    case 1: return wgrad_site<T, 1>(a, dw, M, N, st);
+    case 2: return wgrad_site<T, 2>(a, dw, M, N, st);
+    case 3: return wgrad_site<T, 3>(a, dw, M, N, st);
+    default: return wgrad_site<T, 0>(a, dw, M, N, st);
+  }
 }
 
 // router backward: dW_r = dl^T x   (dl [T, Ep] with Ep = E rounded up to 8, zero padded)
@@ -316,8 +370,8 @@ hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T
   GemmArgs a{};
   a.A = dl; a.lda = Ep; a.B = x; a.ldb = d;
   a.M = E; a.N = d; a.K = T_; a.a_mext = Ep; a.b_next = d; a.b_kend = T_; a.G = 1;
-  typename EpiStore<T>::P ep{(T*)dw_r, d, 0, E, d};
-  return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T>>(a, ep, 0, st);
+  typename EpiStore<T, 4>::P ep{(T*)dw_r, d, 0, E, d};
+  return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T, 4>>(a, ep, 0, st);
 }
 
 // router backward: dx_partial += dl W_r  (K = Ep, rows k >= E of W_r read as 0)
@@ -345,7 +399,7 @@ hipError_t gemm_router_dgrad(const void* dl, int Ep, int E, const void* w_r, int
                                            const void*, void*, bool, int, int, int,              \
                                            hipStream_t);                                         \
   template hipError_t gemm_wgrad<T>(const void*, int, const void*, int, const int*, int, int,    \
-                                    void*, hipStream_t);                                         \
+                                    void*, int, hipStream_t);                                         \
   template hipError_t gemm_router_wgrad<T>(const void*, int, int, const void*, int, int, void*,  \
                                            hipStream_t);                                         \
   template hipError_t gemm_router_dgrad<T>(const void*, int, int, const void*, int, int, float*, \

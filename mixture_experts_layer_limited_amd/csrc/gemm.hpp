@@ -18,6 +18,14 @@
 namespace moe {
 
 enum OpLayout { KC = 0, MC = 1 };
+
+constexpr int kRawBufferFlags = 0x00020000;   // raw (unformatted) buffer, gfx9 family
+
+// buffer resource over `bytes` bytes from `base`: accesses past the range are
+// dropped (stores) or read as zero (loads)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferFlags);
+}
 enum GemmMode { DENSE = 0, RAGGED_M = 1, RAGGED_K = 2 };
 
 struct GemmArgs {
@@ -44,38 +52,101 @@ struct TileCoord {
   int k_end;
 };
 
-// Resolve a logical tile index.  Returns false when the tile is empty.
+// Resolve a logical tile index.  `off` / `pre` are the ragged offsets and the
+// tile prefix (a copy in LDS or the global arrays of `a`).
 template <GemmMode MODE, int BM>
-__device__ __forceinline__ bool resolve_tile(const GemmArgs& a, int L, int NT, int MT, TileCoord& c) {
+__device__ __forceinline__ void resolve_tile(const GemmArgs& a, const int* off, const int* pre, int L, int NT,
+                                             int MT, TileCoord& c) {
   if (MODE == DENSE) {
     int mt = L % MT, nt = L / MT;
     c.g = 0; c.m0 = mt * BM; c.m_end = a.M; c.n0 = nt; c.k_begin = 0; c.k_end = a.K;
-    return true;
   } else if (MODE == RAGGED_M) {
     // expert-major order: all tiles of group g, n-tile major, m-tile fastest
-    int lo = 0, hi = a.G;  // find g with tile_prefix[g]*NT <= L < tile_prefix[g+1]*NT
+    int lo = 0, hi = a.G;  // find g with pre[g]*NT <= L < pre[g+1]*NT
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
-      if (a.tile_prefix[mid] * NT <= L) lo = mid; else hi = mid;
+      if (pre[mid] * NT <= L) lo = mid; else hi = mid;
     }
     int g = lo;
-    int first = a.tile_prefix[g], mt_g = a.tile_prefix[g + 1] - first;
+    int first = pre[g], mt_g = pre[g + 1] - first;
     int local = L - first * NT;
     int nt = local / mt_g, mi = local % mt_g;
-    int row0 = a.offsets[g];
-    c.g = g; c.m0 = row0 + mi * BM; c.m_end = a.offsets[g + 1]; c.n0 = nt;
+    int row0 = off[g];
+    c.g = g; c.m0 = row0 + mi * BM; c.m_end = off[g + 1]; c.n0 = nt;
     c.k_begin = 0; c.k_end = a.K;
-    return true;
   } else {
+    // group-major; inside a group, bands of kBandM m-tiles walked n-tile by
+    // n-tile (m fastest inside the band).  A run of 64 consecutive tiles (what
+    // one XCD takes of a round) is then about 8 x 8 tiles: it reads 8 row
+    // blocks of each operand once and reuses each 8 times from L2, instead of
+    // re-reading one operand's whole panel for every row of tiles.
+    constexpr int kBandM = 8;
     int per = MT * NT;
     int g = L / per, r = L % per;
-    int mt = r % MT, nt = r / MT;
+    int band = r / (kBandM * NT), in = r % (kBandM * NT);
+    int bm = min(kBandM, MT - band * kBandM);
+    int mt = band * kBandM + in % bm, nt = in / bm;
     c.g = g; c.m0 = mt * BM; c.m_end = a.M; c.n0 = nt;
-    c.k_begin = a.offsets ? a.offsets[g] : 0;
-    c.k_end = a.offsets ? a.offsets[g + 1] : a.K;
-    return true;
+    c.k_begin = a.offsets ? off[g] : 0;
+    c.k_end = a.offsets ? off[g + 1] : a.K;
   }
 }
+
+template <GemmMode MODE, int BM>
+__device__ __forceinline__ void resolve_tile(const GemmArgs& a, int L, int NT, int MT, TileCoord& c) {
+  resolve_tile<MODE, BM>(a, a.offsets, a.tile_prefix, L, NT, MT, c);
+}
+
+// ---------------------------------------------------------------------------
+// LDS slices of row-contiguous ("MC") operands.  A slice is kept as it lies in
+// memory: K-rows of ROWS values (ROWS/8 16-byte chunks each), logical chunk c
+// of K-row k at position c ^ mc_mask(k, c).  MFMA fragments are read with
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i%4
+// of the 8-byte piece addressed by lane i/4 + 4j (j = 0..3).  Pointing lane q
+// at K-row k0 + q/4, columns n0 + 4(q%4) .. +3 hands lane i the four K values
+// k0..k0+3 of column n0 + i.  A cycle's 32 lanes touch 4 K-rows x 4 chunks,
+// which the XOR spreads over all 16 chunk positions of the 64 banks; 16 lanes
+// writing one K-row's 16 chunks also land on distinct positions.
+// ---------------------------------------------------------------------------
+#define MOE_LDS __attribute__((address_space(3)))
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4i16;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short v8i16;
+
+__device__ __forceinline__ int mc_mask(int k, int c) { return ((k & 3) << 1) | (((c >> 1) & 1) << 3); }
+
+// Fragment reads of NF fragments of 32 tile rows (row0 + 32 f) from an MC
+// slice of ROWS columns; per-lane byte offsets are computed once.
+template <int ROWS, int NF>
+struct McFrag {
+  static constexpr int CPR = ROWS / 8;
+  uint32_t off[NF];
+
+  __device__ __forceinline__ void init(int row0) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, q = lane & 15;
+    const int klane = 8 * (g >> 1) + (q >> 2);             // K-row within a 16-step
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int n = row0 + 32 * f + 16 * (g & 1) + 4 * (q & 3);
+      const int c = n >> 3, half = q & 1;
+      off[f] = (uint32_t)(klane * CPR * 16 + ((c ^ mc_mask(klane, c)) * 16) + half * 8);
+    }
+  }
+  // fragment f, K-step kk; `base` = LDS byte address of the slice
+  __device__ __forceinline__ bf16x8 read(uint32_t base, int f, int kk) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // K-rows kk*16 + {0..3} and kk*16 + {4..7}: k & 3 is unchanged, so the XOR is too
+    const uint32_t a = base + off[f] + (uint32_t)(kk * 16 * CPR * 16);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS v4i16*)(uintptr_t)a);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS v4i16*)(uintptr_t)(a + 4 * CPR * 16));
+    v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+#else
+    return bf16x8{};
+#endif
+  }
+};
 
 // Total logical tiles (device side; RAGGED_M depends on the expert sizes).
 template <GemmMode MODE>
@@ -130,10 +201,21 @@ __device__ __forceinline__ void load4(const T* p, float v[4]) {
   }
 }
 
-template <class T>
+// kSite only tells launch sites apart (distinct kernel symbols for profiles)
+template <class T, int kSite = 0>
 struct EpiStore {                       // C[row, col] = storage(v)
   struct P { T* C; int64_t ldc; int64_t c_gstride; int M; int N; };
   static constexpr bool kPaired = false;
+  // 2-byte outputs may be staged through LDS and stored 8 columns at a time
+  static constexpr bool kStaged = sizeof(T) == 2;
+  __device__ static void store8(const P& p, int g, int row, int col, u32x4 v) {
+    uint16_t* c = (uint16_t*)(p.C + g * p.c_gstride + (int64_t)row * p.ldc + col);
+    if (col + 8 <= p.N && (p.ldc & 7) == 0) {
+      *(u32x4*)c = v;
+    } else {
+      for (int i = 0; i < 8 && col + i < p.N; ++i) c[i] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+    }
+  }
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void at(const P& p, int g, int row, int col, float v) {
     if (col < p.N) p.C[g * p.c_gstride + (int64_t)row * p.ldc + col] = from_f32<T>(v);
@@ -152,6 +234,7 @@ template <int kUnused>
 struct EpiStoreF32T {                   // C[row, col] = v   (fp32 output)
   struct P { float* C; int64_t ldc; int64_t c_gstride; int M; int N; };
   static constexpr bool kPaired = false;
+  static constexpr bool kStaged = false;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void at(const P& p, int g, int row, int col, float v) {
     if (col < p.N) p.C[g * p.c_gstride + (int64_t)row * p.ldc + col] = v;
@@ -170,6 +253,7 @@ template <int kUnused>
 struct EpiAccumF32T {                   // C[row, col] += v  (fp32, one writer per element)
   struct P { float* C; int64_t ldc; int64_t c_gstride; int M; int N; };
   static constexpr bool kPaired = false;
+  static constexpr bool kStaged = false;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void at(const P& p, int g, int row, int col, float v) {
     if (col < p.N) {
@@ -202,6 +286,7 @@ template <class T>
 struct EpiSwiGLU {
   struct P { T* act; T* hu; int64_t f; };  // act [rows, f], hu [rows, 2f] or NULL
   static constexpr bool kPaired = true;
+  static constexpr bool kStaged = false;
   // tile-row r of a BN-row tile split over WN waves: wave part w = r / (BN/WN);
   // its first half are gate rows, its second half the matching up rows
   template <int BN, int WN>
@@ -245,6 +330,7 @@ template <class T>
 struct EpiSwiGLUBwd {
   struct P { const T* hu; T* dhu; int64_t f; };
   static constexpr bool kPaired = false;
+  static constexpr bool kStaged = false;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void grad(float dA, float h, float u, float& dh, float& du) {
     float sg = 1.0f / (1.0f + expf(-h));

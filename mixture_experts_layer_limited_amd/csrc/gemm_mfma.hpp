@@ -35,10 +35,12 @@
 // tiles [r G, (r+1) G) (G = grid size), spread so each XCD gets a contiguous run
 // (tiles running together on one XCD are neighbours in the expert-major order
 // and share weight / activation panels in its L2).  With G >= tiles this is one
-// tile per workgroup; with a smaller grid the kernel is persistent.  The main
-// loop walks (tile, slice) pairs: the DMA for the pair STAGES-1 ahead is issued
+// tile per workgroup; with a smaller grid the kernel is persistent.  The
+// loads walk (tile, slice) pairs: the DMA for the pair STAGES-1 ahead is issued
 // before the current pair is multiplied, so loads of the next tile overlap the
-// current tile's last slices and its epilogue.  Tiles with an empty
+// current tile's last slices and its epilogue.  The multiply side is a tile
+// loop around a slice loop with the epilogue between slice loops, so the
+// accumulators never move between register files inside the slice loop.  Tiles with an empty
 // contraction are skipped (the caller zero-fills them).
 //
 // The MFMA takes the B fragment first, so a lane's accumulator holds four
@@ -48,19 +50,16 @@
 // Synchronisation: s_barrier without a memory fence (a fenced barrier would
 // drain every in-flight DMA) and explicit s_waitcnt vmcnt(N): a lane's DMA for
 // slice s is complete once at most N of its later vector-memory operations are
-// outstanding; after an epilogue (global stores and loads) the wait is vmcnt(0).
+// outstanding (they complete in issue order, so the epilogue's global stores
+// and loads, always issued after the DMA they could be confused with, only
+// lengthen a wait).
 #pragma once
 
 #include "gemm.hpp"
 
 namespace moe {
 
-#define MOE_LDS __attribute__((address_space(3)))
 
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4i16;
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short v8i16;
-
-constexpr int kRawBufferFlags = 0x00020000;   // raw (unformatted) buffer, gfx9 family
 constexpr uint32_t kOffRange = 0x80000000u;   // lane offset that is outside every range
 
 template <int BM, int BN, int WM, int WN, int STAGES>
@@ -83,13 +82,8 @@ struct TileCfg {
   static_assert(STAGE_BYTES <= 65536, "read immediates");
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferFlags);
-}
-
 // logical chunk -> position helpers
 __device__ __forceinline__ int kc_swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int mc_mask(int k, int c) { return ((k & 3) << 1) | (((c >> 1) & 1) << 3); }
 
 // Per-lane byte offsets of one operand slice's DMA (relative to the operand's
 // resource base); KC: element (i, k) at i*ld + k (i relative to the base row);
@@ -143,7 +137,8 @@ struct DmaPlan {
 // a wave reads: NF fragments of 32 tile rows starting at row0 + 32 f.
 template <OpLayout L, int ROWS, int NF>
 struct FragPlan {
-  uint32_t off[L == KC ? 4 : NF];   // KC: per K-step (same for every fragment); MC: per fragment
+  uint32_t off[4];          // KC: per K-step (same for every fragment)
+  McFrag<ROWS, NF> mc;      // MC
 
   __device__ __forceinline__ void init(int row0) {
     const int lane = threadIdx.x & 63;
@@ -153,15 +148,7 @@ struct FragPlan {
       for (int kk = 0; kk < 4; ++kk)
         off[kk] = (uint32_t)((row0 + r) * 128 + (((2 * kk + h) ^ kc_swz(r)) * 16));
     } else {
-      constexpr int CPR = ROWS / 8;
-      const int g = lane >> 4, q = lane & 15;
-      const int klane = 8 * (g >> 1) + (q >> 2);           // K-row within a 16-step, t = 0
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int n = row0 + 32 * f + 16 * (g & 1) + 4 * (q & 3);
-        const int c = n >> 3, half = q & 1;
-        off[f] = (uint32_t)(klane * CPR * 16 + ((c ^ mc_mask(klane, c)) * 16) + half * 8);
-      }
+      mc.init(row0);
     }
   }
   // fragment f, K-step kk; `base` = byte address of the operand slice
@@ -170,13 +157,7 @@ struct FragPlan {
       const MOE_LDS bf16x8* p = (const MOE_LDS bf16x8*)(uintptr_t)(base + off[kk] + f * 32 * 128);
       return *p;
     } else {
-      constexpr int CPR = ROWS / 8;
-      // K-rows kk*16 + {0..3} and kk*16 + {4..7}: k & 3 is unchanged, so the XOR is too
-      const uint32_t a = base + off[f] + (uint32_t)(kk * 16 * CPR * 16);
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS v4i16*)(uintptr_t)a);
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS v4i16*)(uintptr_t)(a + 4 * CPR * 16));
-      v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      return __builtin_bit_cast(bf16x8, v);
+      return mc.read(base, f, kk);
     }
   }
 };
@@ -185,6 +166,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most `later` slices of DMA (D operations each) are outstanding
+template <int MAXL, int D>
+__device__ __forceinline__ void wait_slices_after(int later) {
+  if constexpr (MAXL <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= MAXL) wait_vmcnt<MAXL * D>();
+    else wait_slices_after<MAXL - 1, D>(later);
+  }
 }
 
 __device__ __forceinline__ void bar() {
@@ -363,45 +355,42 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typ
       ++issued;
     }
   }
-  zero_acc();
-
   int n = 0;                      // index of the slice being multiplied
-  bool stores_pending = false;
-  for (;;) {
-    // wait for slice n: later slices already issued may stay in flight
-    if (!stores_pending && issued - n - 1 == STAGES - 2) wait_vmcnt<(STAGES - 2) * DMA_PER_SLICE>();
-    else wait_vmcnt<0>();
-    stores_pending = false;
-    bar();
-    if (ld.r >= 0) {
-      issue(issued % STAGES);     // the stage multiplied in the previous iteration
-      advance_ld();
-      ++issued;
+  // tile loop around a slice loop: the accumulators are only touched by MFMAs
+  // inside the slice loop, so they stay in place across it
+  do {
+    zero_acc();
+    for (int ks = 0; ks < comp.nk; ++ks, ++n) {
+      // wait for slice n: the DMA of the slices issued after it may stay in
+      // flight.  Vector memory operations complete in issue order, so the
+      // epilogue's stores and loads (issued after every DMA in flight) only
+      // make this wait more conservative, never too short.
+      wait_slices_after<STAGES - 2, DMA_PER_SLICE>(issued - n - 1);
+      bar();
+      if (ld.r >= 0) {
+        issue(issued % STAGES);   // the stage multiplied in the previous iteration
+        advance_ld();
+        ++issued;
+      }
+      const uint32_t sa = lds0 + (n % STAGES) * C::STAGE_BYTES;
+      const uint32_t sb = sa + C::A_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[FM], bfr[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = fa.read(sa, i, kk);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[j] = fb.read(sb, j, kk);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      }
     }
-    const uint32_t sa = lds0 + (n % STAGES) * C::STAGE_BYTES;
-    const uint32_t sb = sa + C::A_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = fa.read(sa, i, kk);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = fb.read(sb, j, kk);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    if (comp.ks == comp.nk - 1) {
-      epilogue(comp.c);
-      zero_acc();
-      stores_pending = true;
-    }
-    ++n;
-    if (++comp.ks >= comp.nk) settle(comp.r + 1, comp);
-    if (comp.r < 0) break;
-  }
+    epilogue(comp.c);
+    settle(comp.r + 1, comp);
+  } while (comp.r >= 0);
 }
 
 }  // namespace moe

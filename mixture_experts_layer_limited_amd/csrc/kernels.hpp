@@ -71,7 +71,7 @@ hipError_t gemm_gateup_dgrad(const void* dhu, const int* offsets, const int* til
                              hipStream_t st);
 template <class T>
 hipError_t gemm_wgrad(const void* P_, int M, const void* Q_, int N, const int* offsets, int G,
-                      int K_dense, void* dw, hipStream_t st);
+                      int K_dense, void* dw, int site, hipStream_t st);
 template <class T>
 hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T_, int d, void* dw_r,
                              hipStream_t st);
