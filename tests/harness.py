@@ -43,6 +43,17 @@ def run_gpu(cfg: mi.MoEConfig, inp: dict, backward: bool, d_aux: float = 1.0) ->
     return {k: host(v) for k, v in layer.buf.t.items() if v is not None}
 
 
+def run_gpu_tensors(cfg: mi.MoEConfig, dev: dict, backward: bool, d_aux: float = 1.0) -> dict:
+    """Run the layer on device inputs; return its device buffers (no copies)."""
+    layer = MoELayer(shape_of(cfg), "cuda", backward=backward)
+    layer.forward(dev["x"], dev["w_router"], dev["bias"], dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    if backward:
+        layer.backward(dev["dy"], dev["x"], dev["w_router"], dev["w13"], dev["w2"], dev["ws13"], dev["ws2"],
+                       d_aux=d_aux)
+    torch.cuda.synchronize()
+    return {k: v for k, v in layer.buf.t.items() if v is not None}
+
+
 def run_oracle(cfg: mi.MoEConfig, inp: dict, backward: bool, d_aux: float = 1.0) -> dict:
     fwd = O.layer_forward(inp, cfg)
     out = dict(fwd)
