@@ -38,6 +38,14 @@ bias, 8 groups / top-4 by top-2 sum, renormalise then x2.5, aux coefficient
   R12 storage rounding (bf16 round-to-nearest-even) where a tensor is
       materialised; everything in between is float64 here
   R13 combine sums j = 0..k-1 in selection order, then the shared output
+  R15 MXFP8: fp8 e4m3fn codes, one e8m0 power-of-two scale 2^e per 32
+      consecutive values along the contraction dimension, e the smallest
+      integer with 448 * 2^e >= block amax (clamped to [-127, 127]; amax 0
+      gives e = -127 and zero codes); element = RNE(v / 2^e), saturating
+  R16 MXFP8 along a ragged row range: blocks of 32 rows start at the range's
+      first row, rows past its end count as zeros
+  R17 expert weights enter the MXFP8 GEMMs quantised along whichever of their
+      dimensions the GEMM contracts
 
 Pins that tie this oracle to facts outside itself live in tests/test_oracle_*.py.
 """
@@ -292,6 +300,124 @@ def swiglu_ffn_bwd(xe, H, U, A, dY, w13_e, w2_e, storage: str) -> dict:
 
 
 # ----------------------------------------------------------------------------
+# MXFP8 (DeepSeek-V3 workload with skewed load: expert GEMM operands in fp8
+# e4m3 with 1x32 e8m0 block scales along the contraction, fp32+ accumulation,
+# bf16 outputs)
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0
+MX_BLOCK = 32
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each e4m3fn byte: sign, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN (the format
+    has no infinities)."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sgn = np.where(c >> 7, -1.0, 1.0)
+    ex = (c >> 3) & 15
+    man = c & 7
+    mag = np.where(ex == 0, man / 8.0 * 2.0 ** -6, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
+    mag = np.where((ex == 15) & (man == 7), np.nan, mag)
+    return sgn * mag
+
+
+def _e4m3_table():
+    """The 127 non-negative finite magnitudes of e4m3fn, ascending, and their
+    codes (codes 0x00 .. 0x7E)."""
+    codes = np.arange(0x7F, dtype=np.uint8)
+    return e4m3_decode(codes), codes
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Round each finite value to the nearest e4m3fn value (ties to the code
+    with an even mantissa, i.e. an even code), saturating at +-448; the sign
+    of zero is kept.  Found by searching the table of representable values."""
+    v = np.asarray(v, F64)
+    mags, codes = _e4m3_table()
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, len(mags) - 1)
+    lo = np.clip(hi - 1, 0, len(mags) - 1)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
+    c = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    return np.where(np.signbit(v), c | np.uint8(0x80), c).astype(np.uint8)
+
+
+def mx_scale_exp(amax) -> np.ndarray:
+    """Smallest integer e with 448 * 2^e >= amax, clamped to [-127, 127]
+    (amax = 0 gives -127).  Stored as the e8m0 byte e + 127."""
+    amax = np.asarray(amax, F64)
+    with np.errstate(divide="ignore"):
+        e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / E4M3_MAX))
+    # the float log2 may sit one off near powers of two: settle on the exact rule
+    e = np.where(E4M3_MAX * np.exp2(e) < amax, e + 1, e)
+    e = np.where(E4M3_MAX * np.exp2(e - 1) >= amax, e - 1, e)
+    e = np.where(amax > 0, e, -127.0)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def mx_quantize(a, axis: int):
+    """Codes and e8m0 scale bytes of `a` with blocks of 32 consecutive values
+    along `axis`, the first block starting at index 0 of that axis and a short
+    last block padded with zeros.  Returns (codes shaped like a, scale bytes
+    with the blocked axis of length ceil(n/32))."""
+    a = np.moveaxis(np.asarray(a, F64), axis, -1)
+    n = a.shape[-1]
+    nb = -(-n // MX_BLOCK)
+    pad = np.zeros(a.shape[:-1] + (nb * MX_BLOCK,))
+    pad[..., :n] = a
+    blk = pad.reshape(a.shape[:-1] + (nb, MX_BLOCK))
+    e = mx_scale_exp(np.max(np.abs(blk), axis=-1))
+    codes = e4m3_encode(blk / np.exp2(e)[..., None]).reshape(pad.shape)[..., :n]
+    return np.moveaxis(codes, -1, axis), np.moveaxis((e + 127).astype(np.uint8), -1, axis)
+
+
+def mx_dequantize(codes, scale_bytes, axis: int) -> np.ndarray:
+    c = np.moveaxis(np.asarray(codes, np.uint8), axis, -1)
+    sb = np.moveaxis(np.asarray(scale_bytes, np.uint8), axis, -1).astype(np.int64)
+    n = c.shape[-1]
+    scale = np.repeat(np.exp2(sb - 127.0), MX_BLOCK, axis=-1)[..., :n]
+    return np.moveaxis(e4m3_decode(c) * scale, -1, axis)
+
+
+def mx_qdq(a, axis: int) -> np.ndarray:
+    """What an MXFP8 GEMM sees of `a` when it contracts along `axis`."""
+    return mx_dequantize(*mx_quantize(a, axis), axis)
+
+
+def swiglu_ffn_fwd_mx(xe, w13_e, w2_e, storage: str) -> dict:
+    """swiglu_ffn_fwd with MXFP8 GEMM operands: X and W13 quantised along d,
+    A (after its bf16 store) and W2 along f."""
+    f = w2_e.shape[1]
+    xq = mx_qdq(xe, 1)
+    wq = mx_qdq(w13_e, 1)
+    h = xq @ wq[:f].T
+    u = xq @ wq[f:].T
+    a = store(silu(h) * u, storage)
+    y = store(mx_qdq(a, 1) @ mx_qdq(w2_e, 1).T, storage)
+    return {"H": store(h, storage), "U": store(u, storage), "A": a, "Y": y}
+
+
+def swiglu_ffn_bwd_mx(xe, H, U, A, dY, w13_e, w2_e, storage: str) -> dict:
+    """swiglu_ffn_bwd with MXFP8 GEMM operands, each quantised along the
+    dimension its GEMM contracts: dA = dY W2 (d), dW2 = dY^T A (rows),
+    dX = dHU W13 (2f), dW13 = dHU^T X (rows; blocks start at the first row)."""
+    H = np.asarray(H, F64)
+    U = np.asarray(U, F64)
+    dY = np.asarray(dY, F64)
+    dA = mx_qdq(dY, 1) @ mx_qdq(w2_e, 0)
+    dW2 = store(mx_qdq(dY, 0).T @ mx_qdq(A, 0), storage)
+    sig = 1.0 / (1.0 + np.exp(-H))
+    dH = store(dA * U * sig * (1.0 + H * (1.0 - sig)), storage)
+    dU = store(dA * H * sig, storage)
+    dHU = np.concatenate([dH, dU], axis=1)
+    dX_unrounded = mx_qdq(dHU, 1) @ mx_qdq(w13_e, 0)
+    dW13 = store(mx_qdq(dHU, 0).T @ mx_qdq(xe, 0), storage)
+    return {"dA": dA, "dH": dH, "dU": dU, "dX32": dX_unrounded,
+            "dX": store(dX_unrounded, storage), "dW13": dW13, "dW2": dW2}
+
+
+# ----------------------------------------------------------------------------
 # Combine and the whole layer
 # ----------------------------------------------------------------------------
 def combine(Yp, gates, row_id_map, Ys, storage: str) -> np.ndarray:
@@ -311,6 +437,7 @@ def layer_forward(inp: dict, cfg, storage: str = None) -> dict:
     expert) -> unpermute/combine.  `inp` holds numpy/torch CPU arrays as made
     by moe_inputs.make_inputs."""
     storage = storage or storage_of(cfg)
+    ffn_fwd = swiglu_ffn_fwd_mx if cfg.dtype == "mxfp8" else swiglu_ffn_fwd
     x = _np(inp["x"])
     T = x.shape[0]
     r = route(x, _np(inp["w_router"]), _np(inp.get("bias")), cfg, storage)
@@ -325,14 +452,14 @@ def layer_forward(inp: dict, cfg, storage: str = None) -> dict:
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
             continue
-        o = swiglu_ffn_fwd(Xp[lo:hi], _np(w13[e]), _np(w2[e]), storage)
+        o = ffn_fwd(Xp[lo:hi], _np(w13[e]), _np(w2[e]), storage)
         H[lo:hi], U[lo:hi], A[lo:hi], Yp[lo:hi] = o["H"], o["U"], o["A"], o["Y"]
     out = dict(r)
     out.update(p)
     out.update({"Xp": Xp, "H": H, "U": U, "A": A, "Yp": Yp})
     Ys = None
     if cfg.f_shared > 0:
-        s = swiglu_ffn_fwd(x, _np(inp["ws13"]), _np(inp["ws2"]), storage)
+        s = ffn_fwd(x, _np(inp["ws13"]), _np(inp["ws2"]), storage)
         out.update({"Hs": s["H"], "Us": s["U"], "As": s["A"], "Ys": s["Y"]})
         Ys = s["Y"]
     out["y"] = combine(Yp, r["gates"], p["row_id_map"], Ys, storage)
@@ -394,6 +521,7 @@ def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
     dense=False the expert weight gradients come back as {expert: array} for
     the experts that received rows only (all others are exactly zero)."""
     storage = storage or storage_of(cfg)
+    ffn_bwd = swiglu_ffn_bwd_mx if cfg.dtype == "mxfp8" else swiglu_ffn_bwd
     exact = storage == "f64"
     x = _np(inp["x"])
     dy = _np(inp["dy"])
@@ -422,7 +550,7 @@ def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
             continue            # empty expert: exact zero weight gradients
-        b = swiglu_ffn_bwd(Xp[lo:hi], fwd["H"][lo:hi], fwd["U"][lo:hi], fwd["A"][lo:hi],
+        b = ffn_bwd(Xp[lo:hi], fwd["H"][lo:hi], fwd["U"][lo:hi], fwd["A"][lo:hi],
                            dYp[lo:hi], _np(inp["w13"][e]), _np(inp["w2"][e]), storage)
         dHU[lo:hi] = np.concatenate([b["dH"], b["dU"]], axis=1)
         dXp32[lo:hi], dXp[lo:hi] = b["dX32"], b["dX"]
@@ -431,7 +559,7 @@ def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
            "dw13": dw13, "dw2": dw2}
     dx_partial = np.zeros((T, d))
     if cfg.f_shared > 0:
-        s = swiglu_ffn_bwd(x, fwd["Hs"], fwd["Us"], fwd["As"], dy,
+        s = ffn_bwd(x, fwd["Hs"], fwd["Us"], fwd["As"], dy,
                            _np(inp["ws13"]), _np(inp["ws2"]), storage)
         out.update({"dHUs": np.concatenate([s["dH"], s["dU"]], axis=1),
                     "dws13": s["dW13"], "dws2": s["dW2"]})
