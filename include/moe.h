@@ -18,8 +18,8 @@
  *   default stream).  Calls are asynchronous: device-side faults surface at the
  *   caller's next synchronisation.
  * - Matrices are row-major and contiguous.  "storage" means the element type
- *   named by moe_cfg.dtype: float (MOE_F32) or bfloat16 (MOE_BF16, stored as
- *   uint16_t bit patterns).  fp32 tensors (logits, gates, d_gates, d_logits,
+ *   named by moe_cfg.dtype: float (MOE_F32) or bfloat16 (MOE_BF16 and
+ *   MOE_MXFP8, stored as uint16_t bit patterns).  fp32 tensors (logits, gates, d_gates, d_logits,
  *   dx_partial) are float in every mode.  Indices are int32.
  * - Weights use the nn.Linear orientation [out, in]: w_router [E, d];
  *   w13 [E, 2f, d] with rows 0..f-1 the gate projection and f..2f-1 the up
@@ -59,7 +59,9 @@ typedef enum moe_status {
   MOE_ERR_DEVICE = 4              /* a HIP call or kernel launch failed       */
 } moe_status;
 
-typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* MOE_MXFP8: bf16 storage everywhere, expert GEMMs (routed and shared) on fp8
+ * e4m3 operands with e8m0 block scales -- see moe_quantize_mxfp8. */
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
 
 typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 
@@ -264,6 +266,86 @@ moe_status moe_permute_bwd(const moe_cfg* cfg, const void* dx_perm,
  * ------------------------------------------------------------------------- */
 moe_status moe_trace_begin(int capacity);
 int moe_trace_end(const char** names, float* ms, int capacity);
+
+/* ---------------------------------------------------------------------------
+ * MXFP8 ("microscaling FP8": thelatestinai.com page, Figure 30, FP8 training
+ * recipes, and Table 11, Dtype column; Figure 31 on quantisation granularity
+ * and the tensor layouts each GEMM needs; Table 8, quantisation kernel
+ * overhead).  A tensor becomes fp8 e4m3fn codes (one byte per value) plus one
+ * e8m0 scale byte per 32 consecutive values along a chosen dimension:
+ *
+ *   scale byte = e + 127, e the smallest integer with 448 * 2^e >= the block's
+ *                largest magnitude, clamped to [-127, 127] (an all-zero block
+ *                gives byte 0 and zero codes)
+ *   code       = the e4m3fn value nearest to v / 2^e, ties to the even code,
+ *                saturating at +-448;   value = decode(code) * 2^(byte - 127)
+ *
+ * A GEMM contracts each operand along its blocked dimension, so the expert
+ * weights are needed in both orientations (quantised once per weight update,
+ * outside the layer calls); activations are quantised inside the layer calls.
+ * ------------------------------------------------------------------------- */
+typedef enum moe_mx_orientation {
+  MOE_MX_ROWS = 0,  /* blocks along the contiguous dimension: codes [B][R][C],
+                       scales [B][R][C/32]; C % 32 == 0                        */
+  MOE_MX_COLS = 1   /* transposed copy, blocks along R: codes [B][C][R],
+                       scales [B][C][R/32]; R % 32 == 0                        */
+} moe_mx_orientation;
+
+/* Quantises `batch` row-major bf16 matrices src [batch][rows][cols] in the
+ * given orientation.  codes 16-byte aligned; rows * cols < 2^31; batch <=
+ * 65535.  Deterministic and bit-exact to the rule above. */
+moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                              int32_t orientation, uint8_t* codes, uint8_t* scales, void* stream);
+
+/* One quantised operand (device memory): codes 16-byte, scales 4-byte aligned. */
+typedef struct moe_mx_tensor {
+  const uint8_t* codes;
+  const uint8_t* scales;
+} moe_mx_tensor;
+
+/* Expert weights for the MXFP8 calls, each in the orientation its GEMM
+ * contracts (MOE_MX_ROWS of the tensor named, or of its per-expert transpose):
+ *   w13   codes [E][2f][d]  scales [E][2f][d/32]   forward gate/up (along d)
+ *   w2    codes [E][d][f]   scales [E][d][f/32]    forward down (along f)
+ *   w13_t codes [E][d][2f]  scales [E][d][2f/32]   dX = dHU W13 (along 2f)
+ *   w2_t  codes [E][f][d]   scales [E][f][d/32]    dA = dY W2 (along d)
+ *   ws13, ws2, ws13_t, ws2_t: the shared expert's, same layouts without [E]
+ *                                        (ignored when f_shared = 0)
+ * w13_t and w2_t are moe_quantize_mxfp8(w, E, rows, cols, MOE_MX_COLS). */
+typedef struct moe_mx_weights {
+  moe_mx_tensor w13, w2, w13_t, w2_t;
+  moe_mx_tensor ws13, ws2, ws13_t, ws2_t;
+} moe_mx_weights;
+
+/* moe_grouped_gemm_swiglu with MXFP8 expert GEMMs (cfg.dtype = MOE_MXFP8;
+ * d, f, f_shared multiples of 128).  Same tensors and semantics, except that
+ * x_perm (and x for the shared expert) is quantised along d before GEMM1 and
+ * the bf16 act along f before GEMM2; weights come quantised in `weights`
+ * (host pointer to the struct; its members are device pointers).  fp32
+ * accumulation, bf16 outputs. */
+moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm,
+                                         const int32_t* expert_offsets,
+                                         const moe_mx_weights* weights, void* hu_save, void* act,
+                                         void* y_perm, const void* x, void* hu_shared_save,
+                                         void* act_shared, void* y_shared, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/* moe_grouped_gemm_swiglu_bwd with MXFP8 GEMMs.  Every GEMM quantises its two
+ * operands along the dimension it contracts: dY_perm along d (dA = dY W2,
+ * with weights->w2_t), dHU along 2f (dX = dHU W13, with weights->w13_t), and
+ * for the weight gradients dY_perm, act, dHU and x_perm along their rows, in
+ * blocks of 32 rows that restart at each expert's first row (rows past the
+ * expert's end count as zeros); the shared expert likewise over all T rows.
+ * Same outputs as the bf16 call (dx_partial written, not accumulated). */
+moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_perm,
+                                             const void* x_perm, const int32_t* expert_offsets,
+                                             const void* hu_save, const void* act,
+                                             const moe_mx_weights* weights, void* dhu, void* dx_perm,
+                                             void* dw13, void* dw2, const void* dy, const void* x,
+                                             const void* hu_shared_save, const void* act_shared,
+                                             void* dhu_shared, float* dx_partial, void* dws13,
+                                             void* dws2, void* workspace, size_t workspace_bytes,
+                                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_gfx950.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+MOE_MX_ROWS, MOE_MX_COLS = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 
 
@@ -27,6 +28,14 @@ class moe_cfg(ctypes.Structure):
                 ("topk_group", ctypes.c_int32), ("renorm", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("aux_coeff", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class moe_mx_tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class moe_mx_weights(ctypes.Structure):
+    _fields_ = [(n, moe_mx_tensor) for n in ("w13", "w2", "w13_t", "w2_t", "ws13", "ws2", "ws13_t", "ws2_t")]
 
 
 class MoEError(RuntimeError):
@@ -51,6 +60,14 @@ _SIGS = {
     "moe_router_topk_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 7 + [ctypes.c_float] + [_P] * 3
                             + [_P, ctypes.c_size_t, _P]),
     "moe_permute_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 4 + [_P]),
+    "moe_quantize_mxfp8": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                          _P, _P, _P]),
+    "moe_grouped_gemm_swiglu_mxfp8": (ctypes.c_int, [ctypes.POINTER(moe_cfg), _P, _P,
+                                                     ctypes.POINTER(moe_mx_weights)] + [_P] * 7
+                                      + [_P, ctypes.c_size_t, _P]),
+    "moe_grouped_gemm_swiglu_bwd_mxfp8": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 5
+                                          + [ctypes.POINTER(moe_mx_weights)] + [_P] * 12
+                                          + [_P, ctypes.c_size_t, _P]),
     "moe_trace_begin": (ctypes.c_int, [ctypes.c_int]),
     "moe_trace_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
                                      ctypes.c_int]),
@@ -107,7 +124,7 @@ def make_cfg(T, d, E, k, f, f_shared=0, score="softmax", n_group=1, topk_group=1
                    score=MOE_SCORE_SIGMOID if score == "sigmoid" else MOE_SCORE_SOFTMAX,
                    n_group=n_group, topk_group=topk_group, renorm=int(bool(renorm)),
                    scale=scale, aux_coeff=aux_coeff,
-                   dtype=MOE_F32 if dtype == "f32" else MOE_BF16, reserved=0)
+                   dtype={"f32": MOE_F32, "mxfp8": MOE_MXFP8}.get(dtype, MOE_BF16), reserved=0)
 
 
 def moe_status_string(s: int) -> str:
@@ -192,6 +209,41 @@ def moe_router_topk_bwd(cfg, x, w_router, logits, topk_idx, topk_gates, expert_c
 def moe_permute_bwd(cfg, dx_perm, row_id_map, dx_partial, dx, stream=None):
     _check(lib().moe_permute_bwd(ctypes.byref(cfg), _ptr(dx_perm), _ptr(row_id_map), _ptr(dx_partial),
                                  _ptr(dx), _stream(stream)), "moe_permute_bwd")
+
+
+def moe_quantize_mxfp8(src, batch, rows, cols, orientation, codes, scales, stream=None):
+    _check(lib().moe_quantize_mxfp8(_ptr(src), batch, rows, cols, orientation, _ptr(codes), _ptr(scales),
+                                    _stream(stream)), "moe_quantize_mxfp8")
+
+
+def mx_weights(**tensors) -> moe_mx_weights:
+    """moe_mx_weights from (codes, scales) tensor pairs keyed by member name;
+    missing members stay NULL."""
+    w = moe_mx_weights()
+    for name, pair in tensors.items():
+        if pair is not None:
+            setattr(w, name, moe_mx_tensor(_ptr(pair[0]), _ptr(pair[1])))
+    return w
+
+
+def moe_grouped_gemm_swiglu_mxfp8(cfg, x_perm, expert_offsets, weights, hu_save, act, y_perm, x,
+                                  hu_shared_save, act_shared, y_shared, workspace, stream=None):
+    w, n = _ws(workspace)
+    _check(lib().moe_grouped_gemm_swiglu_mxfp8(
+        ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_offsets), ctypes.byref(weights), _ptr(hu_save),
+        _ptr(act), _ptr(y_perm), _ptr(x), _ptr(hu_shared_save), _ptr(act_shared), _ptr(y_shared),
+        w, n, _stream(stream)), "moe_grouped_gemm_swiglu_mxfp8")
+
+
+def moe_grouped_gemm_swiglu_bwd_mxfp8(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, weights, dhu,
+                                      dx_perm, dw13, dw2, dy, x, hu_shared_save, act_shared, dhu_shared,
+                                      dx_partial, dws13, dws2, workspace, stream=None):
+    w, n = _ws(workspace)
+    _check(lib().moe_grouped_gemm_swiglu_bwd_mxfp8(
+        ctypes.byref(cfg), _ptr(dy_perm), _ptr(x_perm), _ptr(expert_offsets), _ptr(hu_save), _ptr(act),
+        ctypes.byref(weights), _ptr(dhu), _ptr(dx_perm), _ptr(dw13), _ptr(dw2), _ptr(dy), _ptr(x),
+        _ptr(hu_shared_save), _ptr(act_shared), _ptr(dhu_shared), _ptr(dx_partial), _ptr(dws13),
+        _ptr(dws2), w, n, _stream(stream)), "moe_grouped_gemm_swiglu_bwd_mxfp8")
 
 
 def moe_trace_begin(capacity: int):

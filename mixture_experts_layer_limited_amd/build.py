@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_gfx950.so")
-SOURCES = ["api.hip", "router.hip", "permute.hip", "gemm.hip"]
+SOURCES = ["api.hip", "router.hip", "permute.hip", "gemm.hip", "mxfp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

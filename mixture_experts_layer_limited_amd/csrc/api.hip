@@ -78,7 +78,7 @@ moe_status check_current_device() {
 moe_status check_cfg(const moe_cfg* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg is NULL");
   if (c->reserved != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.reserved must be 0");
-  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16)
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_MXFP8)
     return fail(MOE_ERR_UNSUPPORTED, "cfg.dtype %d not supported", c->dtype);
   if (c->T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.T = %lld < 0", (long long)c->T);
   if (c->E < 1 || c->E > kMaxExperts)
@@ -110,8 +110,23 @@ moe_status check_cfg(const moe_cfg* c) {
 
 // the bf16 GEMM path streams K-contiguous operands in 64-wide slices
 moe_status check_gemm_shapes(const moe_cfg* c) {
-  if (c->dtype == MOE_BF16 && (c->d % 64 || c->f % 64 || c->f_shared % 64))
+  if (c->dtype != MOE_F32 && (c->d % 64 || c->f % 64 || c->f_shared % 64))
     return fail(MOE_ERR_INVALID_ARGUMENT, "bf16 GEMMs need d, f and f_shared to be multiples of 64");
+  return MOE_OK;
+}
+
+// expert GEMM calls of the bf16 / fp32 path
+moe_status check_not_mx(const moe_cfg* c) {
+  if (c->dtype == MOE_MXFP8)
+    return fail(MOE_ERR_UNSUPPORTED, "cfg.dtype is MXFP8: use the *_mxfp8 expert GEMM calls");
+  return MOE_OK;
+}
+
+// the MXFP8 GEMMs contract in 128-deep slices
+moe_status check_mx_shapes(const moe_cfg* c) {
+  if (c->dtype != MOE_MXFP8) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.dtype must be MOE_MXFP8");
+  if (c->d % 128 || c->f % 128 || c->f_shared % 128)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "MXFP8 GEMMs need d, f and f_shared to be multiples of 128");
   return MOE_OK;
 }
 
@@ -164,6 +179,30 @@ inline int64_t router_blocks(int64_t T) { return (T + kRouterTokensPerBlock - 1)
 inline int64_t pad64(int64_t e) { return (e + 63) & ~int64_t(63); }
 inline size_t elt(const moe_cfg* c) { return c->dtype == MOE_F32 ? 4 : 2; }
 
+// MXFP8 workspace: two int arrays (tile prefix, padded offsets), one row-form
+// quantised activation (codes + scales) and two column-form ones
+struct MxWs {
+  int64_t rows_max, cmax_rows, cmax_cols, rp_max;
+  size_t ints, qa, qt;            // region sizes
+  size_t total() const { return ints + qa + 2 * qt; }
+};
+inline int64_t pad128(int64_t v) { return (v + 127) / 128 * 128; }
+MxWs mx_ws(const moe_cfg* c) {
+  MxWs w;
+  const int64_t rows = c->T * c->k;
+  w.rows_max = rows > c->T ? rows : c->T;
+  int64_t cm = c->d;
+  if (2 * c->f > cm) cm = 2 * c->f;
+  if (2 * c->f_shared > cm) cm = 2 * c->f_shared;
+  w.cmax_rows = cm;
+  w.cmax_cols = cm;
+  w.rp_max = pad128(w.rows_max) + (int64_t)kMxRowAlign * c->E;
+  w.ints = 2 * align256((size_t)(c->E + 2) * 4);
+  w.qa = align256((size_t)(w.rows_max * w.cmax_rows)) + align256((size_t)(w.rows_max * w.cmax_rows / 32));
+  w.qt = align256((size_t)(w.cmax_cols * w.rp_max)) + align256((size_t)(w.cmax_cols * w.rp_max / 32));
+  return w;
+}
+
 size_t ws_bytes_for(const moe_cfg* c) {
   size_t router = 2 * align256((size_t)router_blocks(c->T) * c->E * 4);
   size_t perm = align256((size_t)ranges(c->T) * c->E * 4);
@@ -173,6 +212,7 @@ size_t ws_bytes_for(const moe_cfg* c) {
   if (perm > m) m = perm;
   if (gemm > m) m = gemm;
   if (rbwd > m) m = rbwd;
+  if (c->dtype == MOE_MXFP8 && mx_ws(c).total() > m) m = mx_ws(c).total();
   return m < 256 ? 256 : m;
 }
 
@@ -277,6 +317,118 @@ moe_status router_bwd_impl(const moe_cfg* c, const void* x, const void* w_router
   return ok();
 }
 
+
+// ---- MXFP8 expert GEMMs --------------------------------------------------------
+struct MxBufs {
+  int* prefix;
+  int* poff;
+  uint8_t *qa_c, *qa_s, *q1_c, *q1_s, *q2_c, *q2_s;
+  int64_t rp_max;
+};
+MxBufs mx_bufs(const moe_cfg* c, void* ws) {
+  const MxWs w = mx_ws(c);
+  uint8_t* p = (uint8_t*)ws;
+  MxBufs b;
+  b.prefix = (int*)p;
+  b.poff = (int*)(p + w.ints / 2);
+  p += w.ints;
+  b.qa_c = p;
+  b.qa_s = p + align256((size_t)(w.rows_max * w.cmax_rows));
+  p += w.qa;
+  b.q1_c = p;
+  b.q1_s = p + align256((size_t)(w.cmax_cols * w.rp_max));
+  p += w.qt;
+  b.q2_c = p;
+  b.q2_s = p + align256((size_t)(w.cmax_cols * w.rp_max));
+  b.rp_max = w.rp_max;
+  return b;
+}
+inline MxQ mxq(const uint8_t* c, const uint8_t* s) { return MxQ{c, s}; }
+inline MxQ mxq(const moe_mx_tensor& t) { return MxQ{t.codes, t.scales}; }
+
+moe_status mx_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off, const moe_mx_weights* w,
+                       void* hu, void* act, void* y_perm, const void* x, void* hu_s, void* act_s, void* y_s,
+                       void* ws, hipStream_t st) {
+  const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
+  MxBufs b = mx_bufs(c, ws);
+  const MxQ qa = mxq(b.qa_c, b.qa_s);
+  if (rows > 0) {
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
+    LAUNCH_NAMED("gemm_mx_swiglu_fwd", gemm_mx_swiglu_fwd(qa, off, b.prefix, E, mxq(w->w13), hu, act, rows, d, f, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act, f, 0, 1, rows, f, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("gemm_mx_down_fwd", gemm_mx_down_fwd(qa, off, b.prefix, E, mxq(w->w2), y_perm, rows, d, f, st));
+  }
+  if (c->f_shared > 0 && T_ > 0) {
+    const int fs = (int)c->f_shared;
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x, d, 0, 1, T_, d, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("gemm_mx_swiglu_fwd_shared",
+                 gemm_mx_swiglu_fwd(qa, nullptr, nullptr, 1, mxq(w->ws13), hu_s, act_s, T_, d, fs, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act_s, fs, 0, 1, T_, fs, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("gemm_mx_down_fwd_shared",
+                 gemm_mx_down_fwd(qa, nullptr, nullptr, 1, mxq(w->ws2), y_s, T_, d, fs, st));
+  }
+  return ok();
+}
+
+moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm, const int32_t* off,
+                       const void* hu, const void* act, const moe_mx_weights* w, void* dhu, void* dx_perm,
+                       void* dw13, void* dw2, const void* dy, const void* x, const void* hu_s, const void* act_s,
+                       void* dhu_s, float* dx_partial, void* dws13, void* dws2, void* ws, hipStream_t st) {
+  const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
+  MxBufs b = mx_bufs(c, ws);
+  const MxQ qa = mxq(b.qa_c, b.qa_s), q1 = mxq(b.q1_c, b.q1_s), q2 = mxq(b.q2_c, b.q2_s);
+  const int rp = (int)b.rp_max;
+  if (rows > 0) {
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
+    LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd",
+                 gemm_mx_down_dgrad_swiglu_bwd(qa, off, b.prefix, E, mxq(w->w2_t), hu, dhu, rows, d, f, st));
+  }
+  // weight gradients cover every expert: experts without rows get zeros
+  LAUNCH_NAMED("padded_offsets", launch_padded_offsets(off, E, b.poff, st));
+  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dy_perm, d, rows, d, off, b.poff, E, rp, rp, b.q1_c, b.q1_s, st));
+  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(act, f, rows, f, off, b.poff, E, rp, rp, b.q2_c, b.q2_s, st));
+  LAUNCH_NAMED("gemm_mx_wgrad_down", gemm_mx_wgrad(q1, d, q2, f, rp, b.poff, E, 0, dw2, 1, st));
+  if (rows > 0) {
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu, 2 * f, 0, 1, rows, 2 * f, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("gemm_mx_gateup_dgrad",
+                 gemm_mx_gateup_dgrad(qa, off, b.prefix, E, mxq(w->w13_t), dx_perm, false, rows, d, f, st));
+  }
+  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dhu, 2 * f, rows, 2 * f, off, b.poff, E, rp, rp, b.q1_c, b.q1_s, st));
+  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(x_perm, d, rows, d, off, b.poff, E, rp, rp, b.q2_c, b.q2_s, st));
+  LAUNCH_NAMED("gemm_mx_wgrad_gateup", gemm_mx_wgrad(q1, 2 * f, q2, d, rp, b.poff, E, 0, dw13, 0, st));
+  if (c->f_shared > 0) {
+    const int fs = (int)c->f_shared;
+    const int tp = (int)pad128(T_);
+    if (T_ > 0) {
+      LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy, d, 0, 1, T_, d, b.qa_c, b.qa_s, st));
+      LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd_shared",
+                   gemm_mx_down_dgrad_swiglu_bwd(qa, nullptr, nullptr, 1, mxq(w->ws2_t), hu_s, dhu_s, T_, d, fs, st));
+    }
+    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dy, d, T_, d, nullptr, nullptr, 1, tp, tp, b.q1_c, b.q1_s, st));
+    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(act_s, fs, T_, fs, nullptr, nullptr, 1, tp, tp, b.q2_c, b.q2_s, st));
+    LAUNCH_NAMED("gemm_mx_wgrad_down_shared", gemm_mx_wgrad(q1, d, q2, fs, tp, nullptr, 1, tp, dws2, 1, st));
+    if (T_ > 0) {
+      LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu_s, 2 * fs, 0, 1, T_, 2 * fs, b.qa_c, b.qa_s, st));
+      LAUNCH_NAMED("gemm_mx_gateup_dgrad_shared",
+                   gemm_mx_gateup_dgrad(qa, nullptr, nullptr, 1, mxq(w->ws13_t), dx_partial, true, T_, d, fs, st));
+    }
+    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dhu_s, 2 * fs, T_, 2 * fs, nullptr, nullptr, 1, tp, tp, b.q1_c, b.q1_s, st));
+    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(x, d, T_, d, nullptr, nullptr, 1, tp, tp, b.q2_c, b.q2_s, st));
+    LAUNCH_NAMED("gemm_mx_wgrad_gateup_shared", gemm_mx_wgrad(q1, 2 * fs, q2, d, tp, nullptr, 1, tp, dws13, 0, st));
+  } else {
+    LAUNCH_NAMED("fill_f32", launch_fill_f32(dx_partial, (int64_t)T_ * d, 0.0f, st));
+  }
+  return ok();
+}
+
+moe_status check_mx_tensor(const moe_mx_tensor& t, const char* name) {
+  if (!t.codes || !t.scales) return fail(MOE_ERR_INVALID_ARGUMENT, "weights.%s: codes and scales must not be NULL", name);
+  if (((uintptr_t)t.codes & 15) || ((uintptr_t)t.scales & 3))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "weights.%s: codes must be 16-byte and scales 4-byte aligned", name);
+  return MOE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -357,7 +509,7 @@ moe_status moe_router_topk(const moe_cfg* cfg, const void* x, const void* w_rout
   CHECK(check_ws(cfg, workspace, workspace_bytes));
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
-  if (cfg->dtype == MOE_BF16)
+  if (cfg->dtype != MOE_F32)
     return router_topk_impl<bf16>(cfg, x, w_router, bias, logits, topk_idx, topk_gates, expert_counts,
                                   aux_loss, workspace, st);
   return router_topk_impl<float>(cfg, x, w_router, bias, logits, topk_idx, topk_gates, expert_counts,
@@ -388,6 +540,7 @@ moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm, const
                                    void* act_shared, void* y_shared, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
+  CHECK(check_not_mx(cfg));
   CHECK(check_gemm_shapes(cfg));
   REQ(x_perm); REQ(expert_offsets); REQ(w13); REQ(w2); REQ(act); REQ(y_perm);
   ALIGNED(x_perm); ALIGNED(w13); ALIGNED(w2); ALIGNED(hu_save); ALIGNED(act); ALIGNED(y_perm);
@@ -398,7 +551,7 @@ moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm, const
   CHECK(check_ws(cfg, workspace, workspace_bytes));
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
-  if (cfg->dtype == MOE_BF16)
+  if (cfg->dtype != MOE_F32)
     return gemm_fwd_impl<bf16>(cfg, x_perm, expert_offsets, w13, w2, hu_save, act, y_perm, x, ws13, ws2,
                                hu_shared_save, act_shared, y_shared, workspace, st);
   return gemm_fwd_impl<float>(cfg, x_perm, expert_offsets, w13, w2, hu_save, act, y_perm, x, ws13, ws2,
@@ -413,7 +566,7 @@ moe_status moe_unpermute_combine(const moe_cfg* cfg, const void* y_perm, const i
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
   const int T_ = (int)cfg->T, k = (int)cfg->k, d = (int)cfg->d;
-  if (cfg->dtype == MOE_BF16)
+  if (cfg->dtype != MOE_F32)
     LAUNCH_NAMED("combine", launch_combine<bf16>((const bf16*)y_perm, row_id_map, topk_gates, (const bf16*)y_shared, (bf16*)y,
                                 T_, k, d, st));
   else
@@ -431,7 +584,7 @@ moe_status moe_unpermute_combine_bwd(const moe_cfg* cfg, const void* dy, const v
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
   const int T_ = (int)cfg->T, k = (int)cfg->k, d = (int)cfg->d;
-  if (cfg->dtype == MOE_BF16)
+  if (cfg->dtype != MOE_F32)
     LAUNCH_NAMED("combine_bwd", launch_combine_bwd<bf16>((const bf16*)dy, (const bf16*)y_perm, row_id_map, topk_gates,
                                     (bf16*)dy_perm, d_gates, T_, k, d, st));
   else
@@ -448,6 +601,7 @@ moe_status moe_grouped_gemm_swiglu_bwd(const moe_cfg* cfg, const void* dy_perm, 
                                        void* dhu_shared, float* dx_partial, void* dws13, void* dws2,
                                        void* workspace, size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
+  CHECK(check_not_mx(cfg));
   CHECK(check_gemm_shapes(cfg));
   REQ(dy_perm); REQ(x_perm); REQ(expert_offsets); REQ(hu_save); REQ(act); REQ(w13); REQ(w2);
   REQ(dhu); REQ(dx_perm); REQ(dw13); REQ(dw2); REQ(dx_partial);
@@ -462,7 +616,7 @@ moe_status moe_grouped_gemm_swiglu_bwd(const moe_cfg* cfg, const void* dy_perm, 
   CHECK(check_ws(cfg, workspace, workspace_bytes));
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
-  if (cfg->dtype == MOE_BF16)
+  if (cfg->dtype != MOE_F32)
     return gemm_bwd_impl<bf16>(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, w13, w2, dhu, dx_perm, dw13,
                                dw2, dy, x, hu_shared_save, act_shared, ws13, ws2, dhu_shared, dx_partial,
                                dws13, dws2, workspace, st);
@@ -484,7 +638,7 @@ moe_status moe_router_topk_bwd(const moe_cfg* cfg, const void* x, const void* w_
   CHECK(check_ws(cfg, workspace, workspace_bytes));
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
-  if (cfg->dtype == MOE_BF16)
+  if (cfg->dtype != MOE_F32)
     return router_bwd_impl<bf16>(cfg, x, w_router, logits, topk_idx, topk_gates, expert_counts, d_gates, d_aux,
                                  d_logits, dw_router, dx_partial, workspace, st);
   return router_bwd_impl<float>(cfg, x, w_router, logits, topk_idx, topk_gates, expert_counts, d_gates, d_aux,
@@ -499,11 +653,86 @@ moe_status moe_permute_bwd(const moe_cfg* cfg, const void* dx_perm, const int32_
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
   const int T_ = (int)cfg->T, k = (int)cfg->k, d = (int)cfg->d;
-  if (cfg->dtype == MOE_BF16)
+  if (cfg->dtype != MOE_F32)
     LAUNCH_NAMED("unpermute_sum", launch_unpermute_sum<bf16>((const bf16*)dx_perm, row_id_map, dx_partial, (bf16*)dx, T_, k, d, st));
   else
     LAUNCH_NAMED("unpermute_sum", launch_unpermute_sum<float>((const float*)dx_perm, row_id_map, dx_partial, (float*)dx, T_, k, d, st));
   return ok();
 }
 
+
+moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t orientation,
+                              uint8_t* codes, uint8_t* scales, void* stream) {
+  REQ(src); REQ(codes); REQ(scales);
+  ALIGNED(src); ALIGNED(codes);
+  if (batch < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "negative size");
+  if (batch > 65535) return fail(MOE_ERR_INVALID_ARGUMENT, "batch = %lld above 65535", (long long)batch);
+  if (rows * cols >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "rows * cols must stay below 2^31");
+  if (orientation != MOE_MX_ROWS && orientation != MOE_MX_COLS)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "orientation %d unknown", orientation);
+  if (orientation == MOE_MX_ROWS && cols % 32)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "row orientation needs cols %% 32 == 0 (cols = %lld)", (long long)cols);
+  if (orientation == MOE_MX_COLS && rows % 32)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "column orientation needs rows %% 32 == 0 (rows = %lld)", (long long)rows);
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (orientation == MOE_MX_ROWS)
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(src, cols, rows * cols, (int)batch, (int)rows, (int)cols,
+                                                       codes, scales, st));
+  else
+    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols_batched(src, (int)batch, (int)rows, (int)cols, codes,
+                                                               scales, st));
+  return ok();
+}
+
+moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm, const int32_t* expert_offsets,
+                                         const moe_mx_weights* weights, void* hu_save, void* act, void* y_perm,
+                                         const void* x, void* hu_shared_save, void* act_shared, void* y_shared,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_mx_shapes(cfg));
+  REQ(x_perm); REQ(expert_offsets); REQ(weights); REQ(act); REQ(y_perm);
+  ALIGNED(x_perm); ALIGNED(hu_save); ALIGNED(act); ALIGNED(y_perm);
+  CHECK(check_mx_tensor(weights->w13, "w13"));
+  CHECK(check_mx_tensor(weights->w2, "w2"));
+  if (cfg->f_shared > 0) {
+    REQ(x); REQ(act_shared); REQ(y_shared);
+    ALIGNED(x); ALIGNED(hu_shared_save); ALIGNED(act_shared); ALIGNED(y_shared);
+    CHECK(check_mx_tensor(weights->ws13, "ws13"));
+    CHECK(check_mx_tensor(weights->ws2, "ws2"));
+  }
+  CHECK(check_ws(cfg, workspace, workspace_bytes));
+  CHECK(check_current_device());
+  return mx_fwd_impl(cfg, x_perm, expert_offsets, weights, hu_save, act, y_perm, x, hu_shared_save, act_shared,
+                     y_shared, workspace, (hipStream_t)stream);
+}
+
+moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_perm, const void* x_perm,
+                                             const int32_t* expert_offsets, const void* hu_save, const void* act,
+                                             const moe_mx_weights* weights, void* dhu, void* dx_perm, void* dw13,
+                                             void* dw2, const void* dy, const void* x, const void* hu_shared_save,
+                                             const void* act_shared, void* dhu_shared, float* dx_partial,
+                                             void* dws13, void* dws2, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_mx_shapes(cfg));
+  REQ(dy_perm); REQ(x_perm); REQ(expert_offsets); REQ(hu_save); REQ(act); REQ(weights);
+  REQ(dhu); REQ(dx_perm); REQ(dw13); REQ(dw2); REQ(dx_partial);
+  ALIGNED(dy_perm); ALIGNED(x_perm); ALIGNED(hu_save); ALIGNED(act); ALIGNED(dhu); ALIGNED(dx_perm);
+  ALIGNED(dw13); ALIGNED(dw2); ALIGNED(dx_partial);
+  CHECK(check_mx_tensor(weights->w13_t, "w13_t"));
+  CHECK(check_mx_tensor(weights->w2_t, "w2_t"));
+  if (cfg->f_shared > 0) {
+    REQ(dy); REQ(x); REQ(hu_shared_save); REQ(act_shared); REQ(dhu_shared); REQ(dws13); REQ(dws2);
+    ALIGNED(dy); ALIGNED(x); ALIGNED(hu_shared_save); ALIGNED(act_shared); ALIGNED(dhu_shared);
+    ALIGNED(dws13); ALIGNED(dws2);
+    CHECK(check_mx_tensor(weights->ws13_t, "ws13_t"));
+    CHECK(check_mx_tensor(weights->ws2_t, "ws2_t"));
+  }
+  CHECK(check_ws(cfg, workspace, workspace_bytes));
+  CHECK(check_current_device());
+  return mx_bwd_impl(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, weights, dhu, dx_perm, dw13, dw2, dy, x,
+                     hu_shared_save, act_shared, dhu_shared, dx_partial, dws13, dws2, workspace,
+                     (hipStream_t)stream);
+}
 }  // extern "C"

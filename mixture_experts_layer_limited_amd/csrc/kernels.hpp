@@ -79,4 +79,30 @@ template <class T>
 hipError_t gemm_router_dgrad(const void* dl, int Ep, int E, const void* w_r, int T_, int d,
                              float* dx_partial, hipStream_t st);
 
+// mxfp8.hip
+constexpr int kMxRowAlign = 128;        // column-form groups start on multiples of this row count
+struct MxQ {                            // fp8 e4m3 codes and e8m0 scales of one quantised tensor
+  const uint8_t* codes;
+  const uint8_t* scales;
+};
+hipError_t launch_mx_quant_rows(const void* src, int64_t ld, int64_t src_bstride, int batch, int R, int C,
+                                uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_padded_offsets(const int* off, int G, int* poff, hipStream_t st);
+hipError_t launch_mx_quant_cols(const void* src, int64_t ld, int rows, int C, const int* off, const int* poff,
+                                int G, int rows_pad_max, int64_t ldq, uint8_t* codes, uint8_t* scales,
+                                hipStream_t st);
+hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C, uint8_t* codes,
+                                        uint8_t* scales, hipStream_t st);
+hipError_t gemm_mx_swiglu_fwd(const MxQ& x, const int* off, const int* prefix, int G, const MxQ& w13, void* hu,
+                              void* act, int rows, int d, int f, hipStream_t st);
+hipError_t gemm_mx_down_fwd(const MxQ& act, const int* off, const int* prefix, int G, const MxQ& w2, void* y,
+                            int rows, int d, int f, hipStream_t st);
+hipError_t gemm_mx_down_dgrad_swiglu_bwd(const MxQ& dy, const int* off, const int* prefix, int G,
+                                         const MxQ& w2t, const void* hu, void* dhu, int rows, int d, int f,
+                                         hipStream_t st);
+hipError_t gemm_mx_gateup_dgrad(const MxQ& dhu, const int* off, const int* prefix, int G, const MxQ& w13t,
+                                void* dx, bool f32_out, int rows, int d, int f, hipStream_t st);
+hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G, int K,
+                         void* dw, int site, hipStream_t st);
+
 }  // namespace moe

@@ -1,0 +1,294 @@
+// MXFP8 path: quantisation of bf16 tensors to fp8 e4m3 codes with one e8m0
+// scale per 32 consecutive values, and the scaled-MFMA grouped GEMMs.
+//
+// Quantisation rule (block of 32 values, amax = largest magnitude): the scale
+// is 2^e with e the smallest integer such that 448 * 2^e >= amax, clamped to
+// [-127, 127] (amax = 0 gives e = -127 and zero codes); it is stored as the
+// byte e + 127.  Each value v becomes the e4m3fn code nearest to v / 2^e
+// (ties to the even code), saturating at +-448.  Both steps are exact integer
+// and power-of-two arithmetic on the fp32 image of the bf16 input.
+//
+// Layouts:
+//   rows  : codes [R][C], scales [R][C/32]   (blocks along the contiguous C)
+//   cols  : codes [C][Rp], scales [C][Rp/32] (transposed copy, blocks along R)
+// In the column form the rows come in groups (experts); group g's rows start a
+// new block sequence at padded row poff[g] (a multiple of 128), and rows past
+// the group's end up to the next 128 are zero codes with zero-amax scales.
+#include <stdint.h>
+
+#include "common.hpp"
+#include "gemm.hpp"
+#include "gemm_mx.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// smallest e with 448 * 2^e >= amax, clamped to [-127, 127]
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0x1.cp-119f)) return -127;            // amax <= 448 * 2^-127 (or 0)
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)((b >> 23) & 0xFF) - 127;         // amax = m 2^E, m in [1, 2)
+  const int e = (b & 0x7FFFFFu) <= 0x600000u ? E - 8 : E - 7;   // m <= 1.75 : 1.75 2^E >= amax
+  return e > 127 ? 127 : e;
+}
+
+// e4m3fn code of v (finite), round to nearest even, saturating at 448
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7E;
+  } else if (a < 0x1p-6f) {                            // subnormal range, step 2^-9
+    code = (uint32_t)rintf(a * 512.0f);                // 8 is the first normal, 2^-6
+  } else {
+    int E = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;   // -6 .. 8
+    uint32_t q = (uint32_t)rintf(ldexpf(a, 3 - E));    // 8 .. 16
+    if (q == 16) { q = 8; ++E; }
+    code = ((uint32_t)(E + 7) << 3) | (q - 8);
+    if (code > 0x7E) code = 0x7E;
+  }
+  return sign | code;
+}
+
+// quantise 32 fp32 values; returns the scale byte
+__device__ __forceinline__ uint32_t mx_block(const float v[32], uint32_t out[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx_exponent(amax);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) word |= e4m3_code(ldexpf(v[4 * w + b], -e)) << (8 * b);
+    out[w] = word;
+  }
+  return (uint32_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------
+// Row form: one thread per 32-block.  src [batch][R][ld] bf16 ->
+// codes [batch][R][C], scales [batch][R][C/32].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __restrict__ src, int64_t ld,
+                                                            int64_t src_bstride, int R, int C,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const int nb = C / 32;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)R * nb) return;
+  const int64_t bt = blockIdx.y;
+  const int r = (int)(t / nb), b = (int)(t % nb);
+  const u32x4* p = (const u32x4*)(src + bt * src_bstride + (int64_t)r * ld + b * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 w = p[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = bf16_bits_lo(w[j]);
+      v[8 * i + 2 * j + 1] = bf16_bits_hi(w[j]);
+    }
+  }
+  uint32_t out[8];
+  const uint32_t sb = mx_block(v, out);
+  u32x4* q = (u32x4*)(codes + (bt * R + r) * (int64_t)C + b * 32);
+  q[0] = u32x4{out[0], out[1], out[2], out[3]};
+  q[1] = u32x4{out[4], out[5], out[6], out[7]};
+  scales[(bt * R + r) * (int64_t)nb + b] = (uint8_t)sb;
+}
+
+hipError_t launch_mx_quant_rows(const void* src, int64_t ld, int64_t src_bstride, int batch, int R, int C,
+                                uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  const int64_t n = (int64_t)R * (C / 32);
+  if (n == 0 || batch == 0) return hipSuccess;
+  mx_quant_rows_kernel<<<dim3((unsigned)((n + 255) / 256), batch), 256, 0, st>>>(
+      (const uint16_t*)src, ld, src_bstride, R, C, codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Padded group offsets: poff[g] = sum over g' < g of n_g' rounded up to 128.
+// One workgroup (G <= 256).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void padded_offsets_kernel(const int* __restrict__ off, int G, int align,
+                                                             int* __restrict__ poff) {
+  __shared__ int s[kMaxExperts];
+  const int g = threadIdx.x;
+  int v = 0;
+  if (g < G) v = (off[g + 1] - off[g] + align - 1) / align * align;
+  s[g] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int add = (g >= o) ? s[g - o] : 0;
+    __syncthreads();
+    s[g] += add;
+    __syncthreads();
+  }
+  if (g < G) poff[g + 1] = s[g];
+  if (g == 0) poff[0] = 0;
+}
+
+hipError_t launch_padded_offsets(const int* off, int G, int* poff, hipStream_t st) {
+  padded_offsets_kernel<<<1, 256, 0, st>>>(off, G, kMxRowAlign, poff);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Column form: a workgroup takes one padded 32-row block and 256 columns, one
+// column per thread.  src [rows][ld] bf16 with groups off[G+1] (NULL: one
+// group of `rows` rows); poff[G+1] padded offsets (NULL with off NULL: the
+// single group starts at 0).  codes [C][ldq], scales [C][ldq/32].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __restrict__ src, int64_t ld,
+                                                            int rows, int C, const int* __restrict__ off,
+                                                            const int* __restrict__ poff, int G, int64_t ldq,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const int rp0 = blockIdx.x * 32;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  int src0, n;                                          // source rows of this block: src0 .. src0+n-1
+  if (off) {
+    if (rp0 >= poff[G]) return;
+    int lo = 0, hi = G;                                 // group g with poff[g] <= rp0 < poff[g+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (poff[mid] <= rp0) lo = mid; else hi = mid;
+    }
+    const int local = rp0 - poff[lo];
+    const int ng = off[lo + 1] - off[lo];
+    src0 = off[lo] + local;
+    n = ng - local;
+  } else {
+    if (rp0 >= ((rows + kMxRowAlign - 1) / kMxRowAlign) * kMxRowAlign) return;
+    src0 = rp0;
+    n = rows - rp0;
+  }
+  n = n < 0 ? 0 : (n > 32 ? 32 : n);
+  if (c >= C) return;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = i < n ? bf16_bits_lo(src[(int64_t)(src0 + i) * ld + c]) : 0.0f;
+  uint32_t out[8];
+  const uint32_t sb = mx_block(v, out);
+  u32x4* q = (u32x4*)(codes + (int64_t)c * ldq + rp0);
+  q[0] = u32x4{out[0], out[1], out[2], out[3]};
+  q[1] = u32x4{out[4], out[5], out[6], out[7]};
+  scales[(int64_t)c * (ldq / 32) + rp0 / 32] = (uint8_t)sb;
+}
+
+hipError_t launch_mx_quant_cols(const void* src, int64_t ld, int rows, int C, const int* off, const int* poff,
+                                int G, int rows_pad_max, int64_t ldq, uint8_t* codes, uint8_t* scales,
+                                hipStream_t st) {
+  if (rows_pad_max == 0 || C == 0) return hipSuccess;
+  mx_quant_cols_kernel<<<dim3(rows_pad_max / 32, (C + 255) / 256), 256, 0, st>>>(
+      (const uint16_t*)src, ld, rows, C, off, poff, G, ldq, codes, scales);
+  return hipGetLastError();
+}
+
+// batched transposed form for weights: src [batch][R][C] -> codes [batch][C][R]
+hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C, uint8_t* codes,
+                                        uint8_t* scales, hipStream_t st) {
+  for (int b = 0; b < batch; ++b) {
+    hipError_t e = launch_mx_quant_cols((const uint16_t*)src + (int64_t)b * R * C, C, R, C, nullptr, nullptr, 1,
+                                        R, R, codes + (int64_t)b * R * C, scales + (int64_t)b * R * C / 32, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 GEMM launchers (one tile per workgroup, RegTile shape).
+// ---------------------------------------------------------------------------
+template <GemmMode MODE, class Epi>
+static hipError_t launch_mx(const GemmArgs& a, const MxArgs& s, const typename Epi::P& ep, int n_logical,
+                            int rows_total, hipStream_t st) {
+  using C = RegTile;
+  const int bn_cols = Epi::kPaired ? C::BN / 2 : C::BN;
+  const int NT = (n_logical + bn_cols - 1) / bn_cols;
+  const int MT = (MODE == RAGGED_M) ? 0 : (a.M + C::BM - 1) / C::BM;
+  int64_t grid;
+  if (MODE == RAGGED_M) grid = (int64_t)((rows_total + C::BM - 1) / C::BM + a.G) * NT;
+  else if (MODE == RAGGED_K) grid = (int64_t)a.G * MT * NT;
+  else grid = (int64_t)MT * NT;
+  if (grid <= 0) return hipSuccess;
+  auto kern = gemm_mx_kernel<MODE, Epi>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
+  return hipGetLastError();
+}
+
+// Z[rows, N] = Q[rows, K] . W[g][N, K]^T over ragged row groups (or dense when
+// offsets is NULL): the operands are quantised row forms.
+template <class Epi>
+static hipError_t mx_rows_gemm(const MxQ& q, const int* offsets, const int* prefix, int G, const MxQ& w,
+                               int64_t w_gstride, int rows, int N, int K, const typename Epi::P& ep,
+                               int n_logical, hipStream_t st) {
+  GemmArgs a{};
+  a.A = q.codes; a.lda = K; a.B = w.codes; a.ldb = K; a.b_gstride = w_gstride;
+  a.M = rows; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
+  MxArgs s{q.scales, w.scales, K / 32, K / 32, w_gstride / 32};
+  if (offsets) {
+    a.offsets = offsets; a.tile_prefix = prefix; a.G = G;
+    return launch_mx<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
+  }
+  a.G = 1;
+  return launch_mx<DENSE, Epi>(a, s, ep, n_logical, rows, st);
+}
+
+hipError_t gemm_mx_swiglu_fwd(const MxQ& x, const int* off, const int* prefix, int G, const MxQ& w13, void* hu,
+                              void* act, int rows, int d, int f, hipStream_t st) {
+  typename EpiSwiGLU<bf16>::P ep{(bf16*)act, (bf16*)hu, f};
+  return mx_rows_gemm<EpiSwiGLU<bf16>>(x, off, prefix, G, w13, (int64_t)2 * f * d, rows, 2 * f, d, ep, f, st);
+}
+
+hipError_t gemm_mx_down_fwd(const MxQ& act, const int* off, const int* prefix, int G, const MxQ& w2, void* y,
+                            int rows, int d, int f, hipStream_t st) {
+  typename EpiStore<bf16, 5>::P ep{(bf16*)y, d, 0, rows, d};
+  return mx_rows_gemm<EpiStore<bf16, 5>>(act, off, prefix, G, w2, (int64_t)d * f, rows, d, f, ep, d, st);
+}
+
+// dA = dY W2 with W2 quantised along d (w2t [g][f][d]); SwiGLU backward epilogue
+hipError_t gemm_mx_down_dgrad_swiglu_bwd(const MxQ& dy, const int* off, const int* prefix, int G,
+                                         const MxQ& w2t, const void* hu, void* dhu, int rows, int d, int f,
+                                         hipStream_t st) {
+  typename EpiSwiGLUBwd<bf16>::P ep{(const bf16*)hu, (bf16*)dhu, f};
+  return mx_rows_gemm<EpiSwiGLUBwd<bf16>>(dy, off, prefix, G, w2t, (int64_t)f * d, rows, f, d, ep, f, st);
+}
+
+// dX = dHU W13 with W13 quantised along 2f (w13t [g][d][2f]); bf16 or fp32 out
+hipError_t gemm_mx_gateup_dgrad(const MxQ& dhu, const int* off, const int* prefix, int G, const MxQ& w13t,
+                                void* dx, bool f32_out, int rows, int d, int f, hipStream_t st) {
+  if (f32_out) {
+    EpiStoreF32T<1>::P ep{(float*)dx, d, 0, rows, d};
+    return mx_rows_gemm<EpiStoreF32T<1>>(dhu, off, prefix, G, w13t, (int64_t)d * 2 * f, rows, d, 2 * f, ep, d, st);
+  }
+  typename EpiStore<bf16, 6>::P ep{(bf16*)dx, d, 0, rows, d};
+  return mx_rows_gemm<EpiStore<bf16, 6>>(dhu, off, prefix, G, w13t, (int64_t)d * 2 * f, rows, d, 2 * f, ep, d, st);
+}
+
+// dW[g] (M x N) = P_g^T Q_g with both operands in column form (codes [M][ldq],
+// [N][ldq]) over padded row groups poff (NULL: one group of K rows)
+hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G, int K,
+                         void* dw, int site, hipStream_t st) {
+  GemmArgs a{};
+  a.A = p.codes; a.lda = ldq; a.B = q.codes; a.ldb = ldq;
+  a.M = M; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
+  a.offsets = poff; a.G = poff ? G : 1;
+  MxArgs s{p.scales, q.scales, ldq / 32, ldq / 32, 0};
+  if (site == 1) {
+    typename EpiStore<bf16, 8>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
+    return launch_mx<RAGGED_K, EpiStore<bf16, 8>>(a, s, ep, N, 0, st);
+  }
+  typename EpiStore<bf16, 7>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
+  return launch_mx<RAGGED_K, EpiStore<bf16, 7>>(a, s, ep, N, 0, st);
+}
+
+}  // namespace moe

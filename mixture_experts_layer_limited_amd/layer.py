@@ -109,8 +109,43 @@ class MoELayer:
         abi.moe_permute(self.cfg, x, b["idx"], b["offsets"], b["row_id_map"], b["src_token"], b["x_perm"],
                         self.ws, stream)
 
+    # -- MXFP8 weights -------------------------------------------------------
+    def prepare_mx_weights(self, w13, w2, ws13=None, ws2=None, stream=None):
+        """Quantise the expert weights once (per weight update) in the two
+        orientations the MXFP8 GEMMs contract them in; kept for later calls."""
+        s, dev = self.s, self.device
+        u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=dev)
+        q = {}
+
+        def quant(name, w, batch, rows, cols, orient):
+            if orient == abi.MOE_MX_ROWS:
+                c, sc = u8(batch, rows, cols), u8(batch, rows, cols // 32)
+            else:
+                c, sc = u8(batch, cols, rows), u8(batch, cols, rows // 32)
+            abi.moe_quantize_mxfp8(w, batch, rows, cols, orient, c, sc, stream)
+            q[name] = (c, sc)
+
+        quant("w13", w13, s.E, 2 * s.f, s.d, abi.MOE_MX_ROWS)
+        quant("w2", w2, s.E, s.d, s.f, abi.MOE_MX_ROWS)
+        quant("w13_t", w13, s.E, 2 * s.f, s.d, abi.MOE_MX_COLS)
+        quant("w2_t", w2, s.E, s.d, s.f, abi.MOE_MX_COLS)
+        if s.f_shared:
+            quant("ws13", ws13, 1, 2 * s.f_shared, s.d, abi.MOE_MX_ROWS)
+            quant("ws2", ws2, 1, s.d, s.f_shared, abi.MOE_MX_ROWS)
+            quant("ws13_t", ws13, 1, 2 * s.f_shared, s.d, abi.MOE_MX_COLS)
+            quant("ws2_t", ws2, 1, s.d, s.f_shared, abi.MOE_MX_COLS)
+        self.mx_tensors = q                          # keeps the device memory alive
+        self.mx_weights = abi.mx_weights(**q)
+
     def experts(self, x, w13, w2, ws13=None, ws2=None, stream=None):
         b = self.buf
+        if self.s.dtype == "mxfp8":
+            if getattr(self, "mx_weights", None) is None:
+                self.prepare_mx_weights(w13, w2, ws13, ws2, stream)
+            abi.moe_grouped_gemm_swiglu_mxfp8(self.cfg, b["x_perm"], b["offsets"], self.mx_weights, b.get("hu"),
+                                              b["act"], b["y_perm"], x if self.s.f_shared else None,
+                                              b.get("hu_s"), b.get("act_s"), b.get("y_s"), self.ws, stream)
+            return
         abi.moe_grouped_gemm_swiglu(self.cfg, b["x_perm"], b["offsets"], w13, w2, b.get("hu"), b["act"],
                                     b["y_perm"], x if self.s.f_shared else None, ws13, ws2, b.get("hu_s"),
                                     b.get("act_s"), b.get("y_s"), self.ws, stream)
@@ -133,13 +168,24 @@ class MoELayer:
         abi.moe_unpermute_combine_bwd(self.cfg, dy, b["y_perm"], b["row_id_map"], b["gates"], b["dy_perm"],
                                       b["d_gates"], stream)
         sh = bool(s.f_shared)
-        abi.moe_grouped_gemm_swiglu_bwd(
-            self.cfg, b["dy_perm"], b["x_perm"], b["offsets"], b["hu"], b["act"], w13, w2, b["dhu"],
-            b["dx_perm"], b["dw13"], b["dw2"], dy if sh else None, x if sh else None, b.get("hu_s"),
-            b.get("act_s"), ws13, ws2, b.get("dhu_s"), b["dx_partial"], b.get("dws13"), b.get("dws2"),
-            self.ws, stream)
+        if s.dtype == "mxfp8":
+            abi.moe_grouped_gemm_swiglu_bwd_mxfp8(
+                self.cfg, b["dy_perm"], b["x_perm"], b["offsets"], b["hu"], b["act"], self.mx_weights, b["dhu"],
+                b["dx_perm"], b["dw13"], b["dw2"], dy if sh else None, x if sh else None, b.get("hu_s"),
+                b.get("act_s"), b.get("dhu_s"), b["dx_partial"], b.get("dws13"), b.get("dws2"), self.ws, stream)
+        else:
+            self._gemm_bwd_bf16(dy, x, w13, w2, ws13, ws2, stream)
         abi.moe_router_topk_bwd(self.cfg, x, w_router, b["logits"], b["idx"], b["gates"], b["counts"],
                                 b["d_gates"], d_aux, b["d_logits"], b["dw_router"], b["dx_partial"],
                                 self.ws, stream)
         abi.moe_permute_bwd(self.cfg, b["dx_perm"], b["row_id_map"], b["dx_partial"], b["dx"], stream)
         return b["dx"]
+
+    def _gemm_bwd_bf16(self, dy, x, w13, w2, ws13, ws2, stream):
+        b, s = self.buf, self.s
+        sh = bool(s.f_shared)
+        abi.moe_grouped_gemm_swiglu_bwd(
+            self.cfg, b["dy_perm"], b["x_perm"], b["offsets"], b["hu"], b["act"], w13, w2, b["dhu"],
+            b["dx_perm"], b["dw13"], b["dw2"], dy if sh else None, x if sh else None, b.get("hu_s"),
+            b.get("act_s"), ws13, ws2, b.get("dhu_s"), b["dx_partial"], b.get("dws13"), b.get("dws2"),
+            self.ws, stream)

@@ -9,14 +9,16 @@ import moe_inputs as mi
 from mixture_experts_layer_limited_amd import LayerShape, MoELayer
 from oracle import moe_oracle as O
 
-TOL = {"f32": 1e-5, "bf16": 1e-2}     # relative L2 bound for floating outputs
+# relative L2 bound for floating outputs (MXFP8: against an oracle applying the
+# same quantisation)
+TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 1e-2}
 
 
 def shape_of(cfg: mi.MoEConfig) -> LayerShape:
     return LayerShape(T=cfg.T, d=cfg.d, E=cfg.E, k=cfg.k, f=cfg.f, f_shared=cfg.f_shared,
                       score=cfg.score, n_group=cfg.n_group, topk_group=cfg.topk_group,
                       renorm=cfg.renorm, scale=cfg.scale, aux_coeff=cfg.aux_coeff,
-                      dtype="f32" if cfg.dtype == "f32" else "bf16")
+                      dtype=cfg.dtype if cfg.dtype in ("f32", "mxfp8") else "bf16")
 
 
 def to_dev(inp: dict, dev="cuda") -> dict:
@@ -89,7 +91,7 @@ EXACT_PAIRS = [("idx", "idx"), ("counts", "counts"), ("offsets", "offsets"), ("r
 
 def compare_layer(cfg: mi.MoEConfig, g: dict, o: dict, backward: bool, tol: float | None = None) -> dict:
     """Assert every output of the layer against the oracle; returns the errors."""
-    tol = tol if tol is not None else TOL["f32" if cfg.dtype == "f32" else "bf16"]
+    tol = tol if tol is not None else TOL.get(cfg.dtype, TOL["bf16"])
     for gk, ok in EXACT_PAIRS:
         assert np.array_equal(g[gk].reshape(-1), np.asarray(o[ok]).reshape(-1)), f"{gk} differs"
     pairs = list(FWD_PAIRS)
