@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 import moe_inputs as mi  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the MXFP8 GEMMs)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 # HBM bytes per launch of a kernel as read from rocprofv3 counters: FETCH_SIZE
@@ -65,6 +66,36 @@ def step_flops(cfg: mi.MoEConfig, backward: bool = True) -> float:
     work is not counted, nor padded tile rows."""
     fwd = 2.0 * cfg.T * cfg.d * cfg.E + 6.0 * cfg.T * cfg.k * cfg.d * cfg.f + 6.0 * cfg.T * cfg.d * cfg.f_shared
     return fwd * (3.0 if backward else 1.0)
+
+
+def kernel_work_mx(cfg: mi.MoEConfig, counts) -> dict:
+    """Algorithmic (flops, HBM bytes) per launch of each MXFP8 expert GEMM:
+    quantised operands cost 1 + 1/32 bytes per value (codes + one scale per
+    32), bf16 outputs 2; weight-gradient operands are the column forms whose
+    expert segments are padded to 128 rows."""
+    q, B = 33.0 / 32.0, 2
+    rows, d, f, fs, T, E = cfg.T * cfg.k, cfg.d, cfg.f, cfg.f_shared, cfg.T, cfg.E
+    ne = int((counts > 0).sum())
+    rp = int(sum(-(-int(c) // 128) * 128 for c in counts))
+    tp = -(-T // 128) * 128
+    out = {
+        "gemm_mx_swiglu_fwd": (2.0 * rows * d * 2 * f, q * (ne * 2 * f * d + rows * d) + B * rows * 3 * f),
+        "gemm_mx_down_fwd": (2.0 * rows * f * d, q * (ne * d * f + rows * f) + B * rows * d),
+        "gemm_mx_down_dgrad_swiglu_bwd": (2.0 * rows * d * f, q * (ne * f * d + rows * d) + B * rows * 4 * f),
+        "gemm_mx_wgrad_down": (2.0 * rows * d * f, q * rp * (d + f) + B * E * d * f),
+        "gemm_mx_gateup_dgrad": (2.0 * rows * 2 * f * d, q * (ne * d * 2 * f + rows * 2 * f) + B * rows * d),
+        "gemm_mx_wgrad_gateup": (2.0 * rows * 2 * f * d, q * rp * (2 * f + d) + B * E * 2 * f * d),
+    }
+    if fs:
+        out.update({
+            "gemm_mx_swiglu_fwd_shared": (2.0 * T * d * 2 * fs, q * (2 * fs * d + T * d) + B * T * 3 * fs),
+            "gemm_mx_down_fwd_shared": (2.0 * T * fs * d, q * (d * fs + T * fs) + B * T * d),
+            "gemm_mx_down_dgrad_swiglu_bwd_shared": (2.0 * T * d * fs, q * (fs * d + T * d) + B * T * 4 * fs),
+            "gemm_mx_wgrad_down_shared": (2.0 * T * d * fs, q * tp * (d + fs) + B * d * fs),
+            "gemm_mx_gateup_dgrad_shared": (2.0 * T * 2 * fs * d, q * (d * 2 * fs + T * 2 * fs) + 4 * T * d),
+            "gemm_mx_wgrad_gateup_shared": (2.0 * T * 2 * fs * d, q * tp * (2 * fs + d) + B * 2 * fs * d),
+        })
+    return out
 
 
 def kernel_work(cfg: mi.MoEConfig, counts) -> dict:
@@ -170,16 +201,24 @@ def main():
     from mixture_experts_layer_limited_amd import LayerShape, MoELayer, _abi as abi
 
     cfg = mi.CONFIGS[args.workload]
-    if cfg.dtype == "mxfp8":
-        raise SystemExit("the MXFP8 expert path is not built yet")
+    mx = cfg.dtype == "mxfp8"
     torch.cuda.set_device(0)
     print(f"# generating {cfg.name} inputs on the GPU", file=sys.stderr, flush=True)
     inp = mi.make_inputs(cfg, seed=args.seed, device="cuda", with_grad_inputs=True)
     shape = LayerShape(T=cfg.T, d=cfg.d, E=cfg.E, k=cfg.k, f=cfg.f, f_shared=cfg.f_shared, score=cfg.score,
                        n_group=cfg.n_group, topk_group=cfg.topk_group, renorm=cfg.renorm, scale=cfg.scale,
-                       aux_coeff=cfg.aux_coeff, dtype="f32" if cfg.dtype == "f32" else "bf16")
+                       aux_coeff=cfg.aux_coeff, dtype=cfg.dtype)
     layer = MoELayer(shape, "cuda", backward=True)
     a = inp
+    quant_ms = None
+    if mx:
+        # expert weights are quantised once per weight update, outside the layer (timed apart)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.prepare_mx_weights(a["w13"], a["w2"], a["ws13"], a["ws2"])
+        e1.record()
+        torch.cuda.synchronize()
+        quant_ms = e0.elapsed_time(e1)
 
     def step():
         layer.forward(a["x"], a["w_router"], a["bias"], a["w13"], a["w2"], a["ws13"], a["ws2"])
@@ -215,14 +254,17 @@ def main():
     kern = {n: {"avg_ms": round(v[0] / v[1], 4), "launches_per_step": round(v[1] / max(args.steps, 1), 2)}
             for n, v in per_kernel.items()}
     counts = layer.buf["counts"].cpu()
-    work = kernel_work(cfg, counts)
-    # dominant kernel: largest total time among the traced kernels
-    dom = max(per_kernel.items(), key=lambda kv: kv[1][0])[0]
+    work = kernel_work_mx(cfg, counts) if mx else kernel_work(cfg, counts)
+    peak_mfma = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    # dominant kernel: largest total time among the expert GEMMs (which carry
+    # algorithmic work figures); every other kernel is far smaller at these shapes
+    gemms = {n: v for n, v in per_kernel.items() if n in work} or per_kernel
+    dom = max(gemms.items(), key=lambda kv: kv[1][0])[0]
     roof = None
     if dom in work:
         fl, by = work[dom]
         t = per_kernel[dom][0] / per_kernel[dom][1] * 1e-3
-        ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+        ridge = peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
         if fl / by < ridge:
             ach = by / t / 1e9
             roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
@@ -231,8 +273,8 @@ def main():
                     "achieved_tflops": round(fl / t / 1e12, 1)}
         else:
             ach = fl / t / 1e12
-            roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom),
+            roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak_mfma,
+                    "unit": "TFLOP/s", "frac": round(ach / peak_mfma, 4), "traffic": measured_traffic(dom),
                     "algorithmic_bytes": by, "algorithmic_flops": fl}
         for n, (fl2, by2) in work.items():
             if n in kern:
@@ -245,16 +287,23 @@ def main():
         "metric": "MoE layer fwd+bwd TFLOPS & tokens/s at DSv3 shape, 1 MI355X; % MFMA peak",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "mxfp8" if mx else "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name} MoE layer fwd+bwd", "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "k": cfg.k, "f": cfg.f, "f_shared": cfg.f_shared, "score": cfg.score,
                    "n_group": cfg.n_group, "topk_group": cfg.topk_group, "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
-        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "mfma_peak_frac": round(tflops / peak_mfma, 4),
         "roofline": roof,
         "kernels": kern,
         "expert_rows": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
     }
+    if quant_ms is not None:
+        out["weight_quant_ms"] = round(quant_ms, 3)
+    if mx and args.cpu_sample_tokens == 4 and not args.no_cpu_baseline:
+        # the MXFP8 oracle quantises every expert weight it touches (~1 min per
+        # token at this shape): only on request with an explicit sample size
+        out["cpu_baseline"] = None
+        args.no_cpu_baseline = True
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle on a token sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)

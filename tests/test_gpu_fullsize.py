@@ -14,7 +14,11 @@ rows (so errors do not compound across steps) and compares:
 * shared expert, combine, combine backward, router backward and dx on sampled
   tokens; sampled rows of dW_router and of the shared weight gradients.
 
-Tolerances: bf16 storage rel-L2 1e-2 (spec bound); fp32 outputs 1e-5.
+The MXFP8 workload (skewed DeepSeek-V3 routing with empty experts) is checked
+against the same oracle steps with MXFP8 GEMM operands.
+
+Tolerances: bf16 storage rel-L2 1e-2 (spec bound; MXFP8 against the
+same-quantisation oracle likewise); fp32 outputs 1e-5.
 """
 from __future__ import annotations
 
@@ -55,7 +59,31 @@ def _sample_experts(counts, rng, n=4):
     return sorted(pick)
 
 
-FULL = [mi.CONFIGS["deepseek_v3"], mi.CONFIGS["qwen3_235b"], mi.CONFIGS["mixtral"]]
+class _Ops:
+    """The oracle's expert arithmetic for one dtype: bf16 GEMMs, or MXFP8 GEMMs
+    whose operands are quantised along each contraction (weight-gradient
+    operands along the rows, blocks starting at the expert's first row)."""
+
+    def __init__(self, mx: bool):
+        self.mx = mx
+        self.ffn_fwd = O.swiglu_ffn_fwd_mx if mx else O.swiglu_ffn_fwd
+        self.ffn_bwd = O.swiglu_ffn_bwd_mx if mx else O.swiglu_ffn_bwd
+
+    def q(self, a, axis):
+        return O.mx_qdq(a, axis) if self.mx else a
+
+    def nt(self, a, w):          # a @ w.T, contraction along both last axes
+        return self.q(a, 1) @ self.q(w, 1).T
+
+    def nn(self, a, w):          # a @ w, contraction along a's columns and w's rows
+        return self.q(a, 1) @ self.q(w, 0)
+
+    def wgrad_rows(self, p, q, ridx):   # (p^T q)[ridx], contraction over all rows
+        return self.q(p, 0)[:, ridx].T @ self.q(q, 0)
+
+
+FULL = [mi.CONFIGS["deepseek_v3"], mi.CONFIGS["qwen3_235b"], mi.CONFIGS["mixtral"],
+        mi.CONFIGS["deepseek_v3_skew_mxfp8"]]
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
@@ -70,6 +98,7 @@ def test_fullsize_sampled_parity(cfg):
     b = run_gpu_tensors(cfg, inp, backward=bwd)
     T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.f_shared
     st = "bf16"
+    ops = _Ops(cfg.dtype == "mxfp8")
 
     # -- router -------------------------------------------------------------
     toks = _pick(rng, T, 48)
@@ -94,29 +123,29 @@ def test_fullsize_sampled_parity(cfg):
 
     # -- routed experts -----------------------------------------------------
     off = perm["offsets"]
-    experts = _sample_experts(counts, rng)
+    experts = _sample_experts(counts, rng, n=3 if ops.mx else 4)
     for e in experts:
         lo, hi = int(off[e]), int(off[e + 1])
         rows = lo + _pick(rng, hi - lo, 48)                    # row-wise checks
         rt = torch.as_tensor(rows, device="cuda")
         xe = _h(b["x_perm"][rt])
         w13, w2 = _h(inp["w13"][e]), _h(inp["w2"][e])
-        o = O.swiglu_ffn_fwd(xe, w13, w2, st)
+        o = ops.ffn_fwd(xe, w13, w2, st)
         got_act, got_y = _h(b["act"][rt]), _h(b["y_perm"][rt])
-        err = {"A": rel_l2(got_act, o["A"]), "Y": rel_l2(got_y, O.store(got_act @ w2.T, st))}
+        err = {"A": rel_l2(got_act, o["A"]), "Y": rel_l2(got_y, O.store(ops.nt(got_act, w2), st))}
         if bwd:
             hu = _h(b["hu"][rt])
             err["H"], err["U"] = rel_l2(hu[:, :f], o["H"]), rel_l2(hu[:, f:], o["U"])
-            ob = O.swiglu_ffn_bwd(xe, hu[:, :f], hu[:, f:], got_act, _h(b["dy_perm"][rt]), w13, w2, st)
+            ob = ops.ffn_bwd(xe, hu[:, :f], hu[:, f:], got_act, _h(b["dy_perm"][rt]), w13, w2, st)
             dhu = _h(b["dhu"][rt])
             err["dH"], err["dU"] = rel_l2(dhu[:, :f], ob["dH"]), rel_l2(dhu[:, f:], ob["dU"])
-            err["dX"] = rel_l2(_h(b["dx_perm"][rt]), O.store(dhu @ w13, st))   # from the GPU's own dH, dU
+            err["dX"] = rel_l2(_h(b["dx_perm"][rt]), O.store(ops.nn(dhu, w13), st))   # from the GPU's own dH, dU
             # weight-gradient rows contract over every row of the expert
             sl = slice(lo, hi)
             r13 = _pick(rng, 2 * f, 48)
             r2 = _pick(rng, d, 48)
-            w_dw13 = O.store(_h(b["dhu"][sl][:, torch.as_tensor(r13, device="cuda")]).T @ _h(b["x_perm"][sl]), st)
-            w_dw2 = O.store(_h(b["dy_perm"][sl][:, torch.as_tensor(r2, device="cuda")]).T @ _h(b["act"][sl]), st)
+            w_dw13 = O.store(ops.wgrad_rows(_h(b["dhu"][sl]), _h(b["x_perm"][sl]), r13), st)
+            w_dw2 = O.store(ops.wgrad_rows(_h(b["dy_perm"][sl]), _h(b["act"][sl]), r2), st)
             err["dW13"] = rel_l2(_h(b["dw13"][e][torch.as_tensor(r13, device="cuda")]), w_dw13)
             err["dW2"] = rel_l2(_h(b["dw2"][e][torch.as_tensor(r2, device="cuda")]), w_dw2)
         print(f"  expert {e} rows {hi - lo}: " + " ".join(f"{k_}={v:.2e}" for k_, v in err.items()), flush=True)
@@ -132,11 +161,11 @@ def test_fullsize_sampled_parity(cfg):
     ys = None
     if fs:
         ws13, ws2 = _h(inp["ws13"]), _h(inp["ws2"])
-        o = O.swiglu_ffn_fwd(x_s, ws13, ws2, st)
+        o = ops.ffn_fwd(x_s, ws13, ws2, st)
         a_s = _h(b["act_s"][tt])
         assert rel_l2(a_s, o["A"]) < BF16_TOL
         ys = _h(b["y_s"][tt])
-        assert rel_l2(ys, O.store(a_s @ ws2.T, st)) < BF16_TOL
+        assert rel_l2(ys, O.store(ops.nt(a_s, ws2), st)) < BF16_TOL
     rmap = perm["row_id_map"][toks]
     y_perm_rows = {int(r): _h(b["y_perm"][int(r)]) for r in np.unique(rmap)}
     yp_local = np.stack([y_perm_rows[int(r)] for r in rmap.ravel()]).reshape(len(toks), k, d)
@@ -170,17 +199,17 @@ def test_fullsize_sampled_parity(cfg):
     part = dl_all[toks] @ wr
     if fs:
         hus = _h(b["hu_s"][tt])
-        obs = O.swiglu_ffn_bwd(x_s, hus[:, :fs], hus[:, fs:], _h(b["act_s"][tt]), dy_s, ws13, ws2, st)
+        obs = ops.ffn_bwd(x_s, hus[:, :fs], hus[:, fs:], _h(b["act_s"][tt]), dy_s, ws13, ws2, st)
         dhus = _h(b["dhu_s"][tt])
         assert rel_l2(dhus[:, :fs], obs["dH"]) < BF16_TOL and rel_l2(dhus[:, fs:], obs["dU"]) < BF16_TOL
-        part = part + dhus @ ws13
+        part = part + ops.nn(dhus, ws13)
         dhus_all = _h(b["dhu_s"])
         rs13 = _pick(rng, 2 * fs, 32)
         assert rel_l2(_h(b["dws13"][torch.as_tensor(rs13, device="cuda")]),
-                      O.store(dhus_all[:, rs13].T @ x_all, st)) < BF16_TOL
+                      O.store(ops.wgrad_rows(dhus_all, x_all, rs13), st)) < BF16_TOL
         rs2 = _pick(rng, d, 32)
         assert rel_l2(_h(b["dws2"][torch.as_tensor(rs2, device="cuda")]),
-                      O.store(_h(inp["dy"])[:, rs2].T @ _h(b["act_s"]), st)) < BF16_TOL
+                      O.store(ops.wgrad_rows(_h(inp["dy"]), _h(b["act_s"]), rs2), st)) < BF16_TOL
     got_part = b["dx_partial"][tt].cpu().numpy().astype(np.float64)
     # fp32 sum of the shared dX and the router term (its d_logits enter the GEMM as bf16)
     assert rel_l2(got_part, part) < BF16_TOL
