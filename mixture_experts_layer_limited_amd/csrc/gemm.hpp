@@ -43,6 +43,16 @@ struct GemmArgs {
   int G;
 };
 
+// Scales of MXFP8 operands (e8m0 bytes, one per 32 K values, K/32 per row)
+struct MxArgs {
+  const uint8_t* A_s;      // A scales [..][K/32]
+  const uint8_t* B_s;      // B scales (per group: + g * b_s_gstride)
+  int64_t a_s_ld, b_s_ld;  // scale row strides (bytes)
+  int64_t b_s_gstride;
+};
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
 struct TileCoord {
   int g;        // group
   int m0;       // first row of the tile (absolute row of A/C for RAGGED_M)

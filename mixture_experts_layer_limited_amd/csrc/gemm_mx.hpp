@@ -28,15 +28,6 @@
 
 namespace moe {
 
-typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
-
-struct MxArgs {
-  const uint8_t* A_s;      // A scales [..][K/32]
-  const uint8_t* B_s;      // B scales (per group: + g * b_s_gstride)
-  int64_t a_s_ld, b_s_ld;  // scale row strides (bytes)
-  int64_t b_s_gstride;
-};
-
 template <GemmMode MODE, class Epi>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
   using C = RegTile;

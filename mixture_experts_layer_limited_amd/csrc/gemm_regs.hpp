@@ -320,8 +320,14 @@ __device__ __forceinline__ void store_b128(u32x4 v, __amdgpu_buffer_rsrc_t rs, u
 #endif
 }
 
-template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi, int BK_>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_pipe_kernel(GemmArgs a, typename Epi::P ep, int NT, int MT) {
+// MX = true: both operands are K-contiguous fp8 e4m3 codes with e8m0 scales
+// (`s`), multiplied with v_mfma_scale_f32_32x32x64_f8f6f4 (operand layout as in
+// gemm_mx.hpp).  GemmArgs then count K, lda, ldb in 2-byte units (a slice of
+// BK = 64 units is 128 fp8 values); ragged row offsets are rows, ragged
+// contraction offsets (padded rows of the column forms) are bytes.
+template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi, int BK_, bool MX = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_pipe_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
+  static_assert(!MX || (LA == KC && LB == KC && BK_ == 64), "MXFP8 operands are K-contiguous, 128-byte slices");
   using C = PipeCfg<BK_>;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, BK = C::BK, NTHR = C::NTHR;
   constexpr int FM = C::FM, FN = C::FN, CH = C::CH, NSTAGE = C::NSTAGE;
@@ -330,7 +336,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   int* s_pre = s_off + C::OFF_INTS;
 
   if (MODE != DENSE && a.offsets)
-    for (int i = threadIdx.x; i <= a.G; i += NTHR) s_off[i] = a.offsets[i];
+    for (int i = threadIdx.x; i <= a.G; i += NTHR)
+      s_off[i] = (MX && MODE == RAGGED_K) ? a.offsets[i] / 2 : a.offsets[i];   // MX: K bytes -> units
   if (MODE == RAGGED_M)
     for (int i = threadIdx.x; i <= a.G; i += NTHR) s_pre[i] = a.tile_prefix[i];
   __syncthreads();
@@ -369,9 +376,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   // the slice as it lies in memory, read with McFrag
   using LdA = std::conditional_t<LA == KC, RegLoader<KC, BM, NTHR, BK>, McLoader<BM, NTHR, BK>>;
   using LdB = std::conditional_t<LB == KC, RegLoader<KC, BN, NTHR, BK>, McLoader<BN, NTHR, BK>>;
+  const int lane_ = threadIdx.x & 63, wave_ = threadIdx.x >> 6;
+  uint32_t sn_a[FM], sn_b[FN];            // MX: scale words of the slice being loaded
   auto load_into = [&](LdA& xa, LdB& xb, const It& it) {
     const TileCoord& c = it.c;
     const int k0 = c.k_begin + it.ks * BK;
+    if constexpr (MX) {
+      const int kw = k0 / 16;                       // 2-byte units -> scale bytes (32 values each)
+      const uint8_t* Bs = s.B_s + (MODE == RAGGED_M ? (int64_t)c.g * s.b_s_gstride : 0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = c.m0 + (wave_ / WN) * (BM / WM) + i * 32 + (lane_ & 31);
+        sn_a[i] = row < c.m_end ? *(const uint32_t*)(s.A_s + row * s.a_s_ld + kw) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = (wave_ % WN) * (BN / WN) + j * 32 + (lane_ & 31);
+        int row;
+        if constexpr (Epi::kPaired) row = Epi::template b_row_paired<BN, WN>(ep, c.n0, r);
+        else row = c.n0 * BN + r;
+        sn_b[j] = row < a.b_next ? *(const uint32_t*)(Bs + row * s.b_s_ld + kw) : 0u;
+      }
+    }
     const uint16_t* A = (const uint16_t*)a.A;
     const uint16_t* B = (const uint16_t*)a.B + (MODE == RAGGED_M ? (int64_t)c.g * a.b_gstride : 0);
     if constexpr (LA == KC) {
@@ -491,7 +517,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   // iteration n: load slice n + 1, multiply slice n, store slice n + 1; on a
   // tile's last slice the epilogue comes between the multiply and that store
   int n = 0;
+  uint32_t sc_a[FM], sc_b[FN];            // MX: scale words of the slice being multiplied
   auto iteration = [&](auto last) {
+    if constexpr (MX) {
+      // the scales of this slice arrived with its data; lane half h passes block h
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sc_a[i] = sn_a[i] >> (8 * (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sc_b[j] = sn_b[j] >> (8 * (lane >> 5));
+    }
     bool loaded = false;
     if (ld.r >= 0) {
       load_into(la, lb, ld);
@@ -502,8 +536,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     const bf16x8* sb = sa + BM * CH;
     const uint32_t la_byte = lds0 + (uint32_t)(stage_of(n) * C::STAGE * 16);
     const uint32_t lb_byte = la_byte + BM * CH * 16;
+    if constexpr (MX) {
+      const u32x4* qa = (const u32x4*)sa;
+      const u32x4* qb = (const u32x4*)sb;
+      const int h = lane >> 5;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+      for (int st = 0; st < 2; ++st) {
+        i32x8 af[FM], bfr[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const u32x4 lo = qa[rswz_t<CH>(arow0 + i * 32, st * 4 + h)];
+          const u32x4 hi = qa[rswz_t<CH>(arow0 + i * 32, st * 4 + 2 + h)];
+          af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const u32x4 lo = qb[rswz_t<CH>(brow0 + j * 32, st * 4 + h)];
+          const u32x4 hi = qb[rswz_t<CH>(brow0 + j * 32, st * 4 + 2 + h)];
+          bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            if (st == 0)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0,
+                                                                          (int)sc_b[j], 0, (int)sc_a[i]);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 2,
+                                                                          (int)sc_b[j], 2, (int)sc_a[i]);
+          }
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < (MX ? 0 : BK / 16); ++kk) {
       const int ch = kk * 2 + (lane >> 5);
       bf16x8 af[FM], bfr[FN];
 #pragma unroll

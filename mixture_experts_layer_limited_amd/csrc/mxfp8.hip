@@ -15,6 +15,7 @@
 // new block sequence at padded row poff[g] (a multiple of 128), and rows past
 // the group's end up to the next 128 are zero codes with zero-amax scales.
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "common.hpp"
 #include "gemm.hpp"
@@ -225,6 +226,60 @@ static hipError_t launch_mx(const GemmArgs& a, const MxArgs& s, const typename E
   return hipGetLastError();
 }
 
+// Persistent pipelined form (gemm_pipe_kernel with MXFP8 operands): the
+// arguments in bytes, converted to the kernel's 2-byte units here.
+static int device_cus_mx() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <GemmMode MODE, class Epi>
+static hipError_t launch_mx_pipe(GemmArgs a, const MxArgs& s, const typename Epi::P& ep, int n_logical,
+                                 int rows_total, hipStream_t st) {
+  using C = PipeCfg<64>;
+  const int bn_cols = Epi::kPaired ? C::BN / 2 : C::BN;
+  const int NT = (n_logical + bn_cols - 1) / bn_cols;
+  const int MT = (MODE == RAGGED_M) ? 0 : (a.M + C::BM - 1) / C::BM;
+  int64_t tiles;
+  if (MODE == RAGGED_M) tiles = (int64_t)((rows_total + C::BM - 1) / C::BM + a.G) * NT;
+  else if (MODE == RAGGED_K) tiles = (int64_t)a.G * MT * NT;
+  else tiles = (int64_t)MT * NT;
+  if (tiles <= 0) return hipSuccess;
+  if (a.G > kMaxExperts) return hipErrorInvalidValue;
+  a.lda /= 2; a.ldb /= 2; a.K /= 2; a.b_kend /= 2; a.b_gstride /= 2;
+  int64_t grid = (int64_t)device_cus_mx() * 2;
+  if (tiles < grid) grid = tiles;
+  auto kern = gemm_pipe_kernel<KC, KC, MODE, Epi, 64, true>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
+  return hipGetLastError();
+}
+
+// MOE_TILE_WGRAD / MOE_TILE pick the one-tile (3) or pipelined (4) kernel
+static bool mx_pipe(bool wgrad) {
+  static int v = -1, w = -1;
+  if (v < 0) {
+    const char* e = getenv("MOE_TILE");
+    const char* f = getenv("MOE_TILE_WGRAD");
+    v = (e && atoi(e) == 4) ? 1 : 0;
+    w = f ? (atoi(f) == 4 ? 1 : 0) : (e ? v : 1);
+  }
+  return wgrad ? w : v;
+}
+
 // Z[rows, N] = Q[rows, K] . W[g][N, K]^T over ragged row groups (or dense when
 // offsets is NULL): the operands are quantised row forms.
 template <class Epi>
@@ -235,11 +290,16 @@ static hipError_t mx_rows_gemm(const MxQ& q, const int* offsets, const int* pref
   a.A = q.codes; a.lda = K; a.B = w.codes; a.ldb = K; a.b_gstride = w_gstride;
   a.M = rows; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
   MxArgs s{q.scales, w.scales, K / 32, K / 32, w_gstride / 32};
+  bool pipe = mx_pipe(false);           // its staged epilogue stores 16-byte row pieces
+  if constexpr (Epi::kStaged)
+    pipe = pipe && ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0;
   if (offsets) {
     a.offsets = offsets; a.tile_prefix = prefix; a.G = G;
+    if (pipe) return launch_mx_pipe<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
     return launch_mx<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
   }
   a.G = 1;
+  if (pipe) return launch_mx_pipe<DENSE, Epi>(a, s, ep, n_logical, rows, st);
   return launch_mx<DENSE, Epi>(a, s, ep, n_logical, rows, st);
 }
 
@@ -276,6 +336,17 @@ hipError_t gemm_mx_gateup_dgrad(const MxQ& dhu, const int* off, const int* prefi
 
 // dW[g] (M x N) = P_g^T Q_g with both operands in column form (codes [M][ldq],
 // [N][ldq]) over padded row groups poff (NULL: one group of K rows)
+// zero the weight gradients of groups without rows (poff NULL: one group of K rows)
+__global__ __launch_bounds__(256) void zero_empty_groups_mx_kernel(const int* __restrict__ poff,
+                                                                   u32x4* __restrict__ out, int64_t vec, int K) {
+  const int g = blockIdx.y;
+  if (poff ? poff[g + 1] != poff[g] : K != 0) return;
+  u32x4* o = out + g * vec;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vec; i += (int64_t)gridDim.x * blockDim.x)
+    o[i] = z;
+}
+
 hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G, int K,
                          void* dw, int site, hipStream_t st) {
   GemmArgs a{};
@@ -283,11 +354,22 @@ hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, 
   a.M = M; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
   a.offsets = poff; a.G = poff ? G : 1;
   MxArgs s{p.scales, q.scales, ldq / 32, ldq / 32, 0};
+  // the pipelined kernel stages 16-byte row pieces of the output and skips
+  // empty contractions: it needs aligned rows and zero-filled empty experts
+  const bool pipe = mx_pipe(true) && N % 8 == 0 && ((uintptr_t)dw & 15) == 0;
+  if (pipe) {
+    const int64_t vec = (int64_t)M * N * 2 / 16;
+    zero_empty_groups_mx_kernel<<<dim3(64, poff ? G : 1), 256, 0, st>>>(poff, (u32x4*)dw, vec, K);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (site == 1) {
     typename EpiStore<bf16, 8>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
+    if (pipe) return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 8>>(a, s, ep, N, 0, st);
     return launch_mx<RAGGED_K, EpiStore<bf16, 8>>(a, s, ep, N, 0, st);
   }
   typename EpiStore<bf16, 7>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
+  if (pipe) return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 7>>(a, s, ep, N, 0, st);
   return launch_mx<RAGGED_K, EpiStore<bf16, 7>>(a, s, ep, N, 0, st);
 }
 
