@@ -288,7 +288,7 @@ typedef enum moe_mx_orientation {
   MOE_MX_ROWS = 0,  /* blocks along the contiguous dimension: codes [B][R][C],
                        scales [B][R][C/32]; C % 32 == 0                        */
   MOE_MX_COLS = 1   /* transposed copy, blocks along R: codes [B][C][R],
-                       scales [B][C][R/32]; R % 32 == 0                        */
+                       scales [B][C][R/32]; R % 32 == 0, C % 8 == 0            */
 } moe_mx_orientation;
 
 /* Quantises `batch` row-major bf16 matrices src [batch][rows][cols] in the

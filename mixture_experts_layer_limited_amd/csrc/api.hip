@@ -672,8 +672,9 @@ moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int6
     return fail(MOE_ERR_INVALID_ARGUMENT, "orientation %d unknown", orientation);
   if (orientation == MOE_MX_ROWS && cols % 32)
     return fail(MOE_ERR_INVALID_ARGUMENT, "row orientation needs cols %% 32 == 0 (cols = %lld)", (long long)cols);
-  if (orientation == MOE_MX_COLS && rows % 32)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "column orientation needs rows %% 32 == 0 (rows = %lld)", (long long)rows);
+  if (orientation == MOE_MX_COLS && (rows % 32 || cols % 8))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "column orientation needs rows %% 32 == 0 and cols %% 8 == 0 (%lld x %lld)",
+                (long long)rows, (long long)cols);
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
   if (orientation == MOE_MX_ROWS)

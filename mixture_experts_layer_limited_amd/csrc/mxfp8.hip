@@ -137,19 +137,25 @@ hipError_t launch_padded_offsets(const int* off, int G, int* poff, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------
-// Column form: a workgroup takes one padded 32-row block and 256 columns, one
-// column per thread.  src [rows][ld] bf16 with groups off[G+1] (NULL: one
-// group of `rows` rows); poff[G+1] padded offsets (NULL with off NULL: the
-// single group starts at 0).  codes [C][ldq], scales [C][ldq/32].
+// Column form: a workgroup takes 128 padded rows (four 32-row blocks, never
+// straddling two groups since groups start on multiples of 128) by 64 columns.
+// The tile is read with 16-byte row loads into LDS; thread (column c, block b)
+// then quantises its 32 values and writes 32 contiguous code bytes, so the
+// four blocks of a column fill one 128-byte line.  src [rows][ld] bf16 with
+// groups off[G+1] (NULL: one group of `rows` rows); poff[G+1] padded offsets.
+// codes [C][ldq], scales [C][ldq/32]; rows at or past rp_limit are not written.
 // ---------------------------------------------------------------------------
+constexpr int kQcRows = 128, kQcCols = 64;
+
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __restrict__ src, int64_t ld,
                                                             int rows, int C, const int* __restrict__ off,
                                                             const int* __restrict__ poff, int G, int64_t ldq,
-                                                            uint8_t* __restrict__ codes,
+                                                            int rp_limit, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
-  const int rp0 = blockIdx.x * 32;
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  int src0, n;                                          // source rows of this block: src0 .. src0+n-1
+  __shared__ uint16_t tile[kQcRows][kQcCols];
+  const int rp0 = blockIdx.x * kQcRows;
+  const int c0 = blockIdx.y * kQcCols;
+  int src0, n;                                          // source rows of this tile: src0 .. src0+n-1
   if (off) {
     if (rp0 >= poff[G]) return;
     int lo = 0, hi = G;                                 // group g with poff[g] <= rp0 < poff[g+1]
@@ -158,33 +164,44 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
       if (poff[mid] <= rp0) lo = mid; else hi = mid;
     }
     const int local = rp0 - poff[lo];
-    const int ng = off[lo + 1] - off[lo];
     src0 = off[lo] + local;
-    n = ng - local;
+    n = off[lo + 1] - off[lo] - local;
   } else {
-    if (rp0 >= ((rows + kMxRowAlign - 1) / kMxRowAlign) * kMxRowAlign) return;
+    if (rp0 >= ((rows + kQcRows - 1) / kQcRows) * kQcRows) return;
     src0 = rp0;
     n = rows - rp0;
   }
-  n = n < 0 ? 0 : (n > 32 ? 32 : n);
-  if (c >= C) return;
+  n = n < 0 ? 0 : (n > kQcRows ? kQcRows : n);
+  // 128 rows x 8 chunks of 16 bytes; columns past C and rows past n read as 0
+  for (int q = threadIdx.x; q < kQcRows * (kQcCols / 8); q += 256) {
+    const int r = q >> 3, ch = q & 7;
+    const int c = c0 + ch * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < n && c + 8 <= C) v = *(const u32x4*)(src + (int64_t)(src0 + r) * ld + c);
+    *(u32x4*)&tile[r][ch * 8] = v;
+  }
+  __syncthreads();
+  const int c = threadIdx.x & (kQcCols - 1), b = threadIdx.x >> 6;
+  const int rb = rp0 + 32 * b;
+  if (c0 + c >= C || rb >= rp_limit) return;
   float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = i < n ? bf16_bits_lo(src[(int64_t)(src0 + i) * ld + c]) : 0.0f;
+  for (int i = 0; i < 32; ++i) v[i] = bf16_bits_lo(tile[32 * b + i][c]);
   uint32_t out[8];
   const uint32_t sb = mx_block(v, out);
-  u32x4* q = (u32x4*)(codes + (int64_t)c * ldq + rp0);
+  u32x4* q = (u32x4*)(codes + (int64_t)(c0 + c) * ldq + rb);
   q[0] = u32x4{out[0], out[1], out[2], out[3]};
   q[1] = u32x4{out[4], out[5], out[6], out[7]};
-  scales[(int64_t)c * (ldq / 32) + rp0 / 32] = (uint8_t)sb;
+  scales[(int64_t)(c0 + c) * (ldq / 32) + rb / 32] = (uint8_t)sb;
 }
 
 hipError_t launch_mx_quant_cols(const void* src, int64_t ld, int rows, int C, const int* off, const int* poff,
                                 int G, int rows_pad_max, int64_t ldq, uint8_t* codes, uint8_t* scales,
                                 hipStream_t st) {
   if (rows_pad_max == 0 || C == 0) return hipSuccess;
-  mx_quant_cols_kernel<<<dim3(rows_pad_max / 32, (C + 255) / 256), 256, 0, st>>>(
-      (const uint16_t*)src, ld, rows, C, off, poff, G, ldq, codes, scales);
+  const int tiles = (rows_pad_max + kQcRows - 1) / kQcRows;
+  mx_quant_cols_kernel<<<dim3(tiles, (C + kQcCols - 1) / kQcCols), 256, 0, st>>>(
+      (const uint16_t*)src, ld, rows, C, off, poff, G, ldq, rows_pad_max, codes, scales);
   return hipGetLastError();
 }
 
