@@ -128,20 +128,28 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
 // workgroup (gemm_regs.hpp); 4 / 5 = its persistent pipelined form with
 // K-slices of 64 (two LDS stages) / 128 (one stage); DMA-fed LDS ring (gemm_mfma.hpp)
 // with 0 = 128x128 x 4 stages, 1 = 128x256 x 3 stages, 2 = 256x128 x 3 stages.
-// MOE_TILE / MOE_TILE_WGRAD override the choice for tuning runs.
+// Defaults per contraction class, from measurements at the 256-expert,
+// d = 7168 shape: products with a K-contiguous weight (forward) run on the
+// 128x256 DMA ring, data gradients (row-contiguous weight) on the
+// register-staged kernel, weight gradients (short ragged contractions) on the
+// persistent pipelined kernel.  MOE_TILE overrides the first two classes,
+// MOE_TILE_WGRAD the third (MOE_TILE alone sets all three); both are for
+// tuning runs.
+enum GemmClass { kForward = 0, kDgrad = 1, kWgrad = 2 };
 static int env_choice(const char* name, int dflt) {
   const char* e = getenv(name);
   int v = e ? atoi(e) : dflt;
   return (v < 0 || v > 5) ? dflt : v;
 }
-// ragged-row and dense contractions (MOE_TILE) / weight gradients (MOE_TILE_WGRAD)
-static int tile_choice(bool wgrad = false) {
-  static int v = -1, w = -1;
-  if (v < 0) {
-    v = env_choice("MOE_TILE", 3);
-    w = env_choice("MOE_TILE_WGRAD", getenv("MOE_TILE") ? v : 4);
+static int tile_choice(GemmClass cls) {
+  static int v[3] = {-1, -1, -1};
+  if (v[0] < 0) {
+    const bool any = getenv("MOE_TILE") != nullptr;
+    v[0] = env_choice("MOE_TILE", 1);
+    v[1] = env_choice("MOE_TILE", 3);
+    v[2] = env_choice("MOE_TILE_WGRAD", any ? v[0] : 4);
   }
-  return wgrad ? w : v;
+  return v[cls];
 }
 
 template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
@@ -197,7 +205,9 @@ static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int 
 
 // Tile rows of the ragged-row schedule.  The device tile prefix is built with
 // this value and the kernel resolves its tiles with its own BM: they must agree.
-int gemm_tile_rows(bool bf16, int64_t, int) { return bf16 ? (tile_choice() == 2 ? 256 : 128) : 16; }
+// (the forward and data-gradient classes take the same override, and their
+// defaults both use 128-row tiles, so one prefix serves both)
+int gemm_tile_rows(bool bf16, int64_t, int) { return bf16 ? (tile_choice(kForward) == 2 ? 256 : 128) : 16; }
 
 template <class T, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
 static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int rows_total, hipStream_t st) {
@@ -207,13 +217,12 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
     // weight gradients (short contractions) run persistent so that a tile's
     // stores overlap the next tile's loads; the rest one tile per workgroup
     const bool persistent = MODE == RAGGED_K;
-    const int t = tile_choice(MODE == RAGGED_K);
-    if (t == 3) return launch_regs<LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st);
+    const int t = tile_choice(MODE == RAGGED_K ? kWgrad : LB == KC ? kForward : kDgrad);
+    bool aligned = true;        // staged epilogues store 16-byte row pieces
+    if constexpr (Epi::kStaged)
+      aligned = ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0;
+    if (t == 3 || !aligned) return launch_regs<LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st);
     if (t >= 4) {
-      bool aligned = true;      // the staged epilogue stores 16-byte row pieces
-      if constexpr (Epi::kStaged)
-        aligned = ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0;
-      if (!aligned) return launch_regs<LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st);
       if (t == 5) return launch_pipe<LA, LB, MODE, Epi, 128>(a, ep, n_logical, rows_total, st);
       return launch_pipe<LA, LB, MODE, Epi, 64>(a, ep, n_logical, rows_total, st);
     }

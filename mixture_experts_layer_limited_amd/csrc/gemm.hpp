@@ -28,6 +28,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 enum GemmMode { DENSE = 0, RAGGED_M = 1, RAGGED_K = 2 };
 
+// Position of the 16-byte chunk c of row r in an epilogue staging buffer of
+// 128-byte rows: 16 consecutive rows written 8 bytes per lane, or 8 lanes
+// reading each row's eight chunks, stay free of bank conflicts.
+__device__ __forceinline__ int stage_swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// 16-byte buffer store (device pass only: in the host pass a device builtin
+// inside a helper makes the compiler drop later kernels' launch stubs).
+// NT = true marks the store non-temporal (cache-policy bit 1, "nt" on gfx950):
+// the line is not kept for reuse, so an output stream does not push operand
+// panels out of L2.
+template <bool NT = false>
+__device__ __forceinline__ void store_b128(u32x4 v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, NT ? 2 : 0);
+#endif
+}
+
 struct GemmArgs {
   const void* A;
   int64_t lda;
@@ -42,6 +59,34 @@ struct GemmArgs {
   const int* tile_prefix;  // RAGGED_M: [G+1] cumulative m-tiles per group
   int G;
 };
+
+// Persistent schedule over XCDs.  Workgroups are dispatched round-robin over
+// the XCDs (block b -> XCD b % 8), so with X = min(G, 8) workgroup b is the
+// (b / X)-th of the workgroups of XCD b % X.  Each XCD owns one contiguous run
+// [lo, hi) of logical tiles for the whole launch and its workgroups stride
+// through it: the tiles one L2 serves are neighbours at any time, and later
+// tiles reuse the panels earlier ones brought in.  Runs split the work evenly:
+// by tile count, except for ragged contractions, where a tile of group g costs
+// kSplitAlpha + (off[g+1] - off[g]) (its store plus its contraction).
+constexpr int kSplitAlpha = 64;
+
+template <GemmMode MODE>
+__device__ __forceinline__ int xcd_run_start(const GemmArgs& a, const int* off, int total, int P, int x, int X) {
+  if (x <= 0) return 0;
+  if (x >= X) return total;
+  if (MODE != RAGGED_K || !a.offsets) return (int)((int64_t)total * x / X);
+  const int G = a.G;
+  auto cum = [&](int e) -> int64_t { return (int64_t)e * kSplitAlpha + (off[e] - off[0]); };
+  const int64_t T = (int64_t)P * cum(G) * x / X;             // work before the run, in tile units
+  int lo = 0, hi = G;                                        // last e < G with P cum(e) <= T
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)P * cum(mid) <= T) lo = mid; else hi = mid;
+  }
+  const int64_t ce = kSplitAlpha + (off[lo + 1] - off[lo]);
+  const int64_t in = (T - (int64_t)P * cum(lo)) / ce;
+  return lo * P + (int)(in < P ? in : P);
+}
 
 // Scales of MXFP8 operands (e8m0 bytes, one per 32 K values, K/32 per row)
 struct MxArgs {

@@ -179,6 +179,19 @@ __device__ __forceinline__ void wait_slices_after(int later) {
   }
 }
 
+// wait until at most n (0 <= n) vector-memory operations of this wave are
+// outstanding; n is uniform.  Counts above 63 (the counter's range) wait for 63.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_vmcnt_dyn<MID, HI>(n);
+    else wait_vmcnt_dyn<LO, MID - 1>(n);
+  }
+}
+
 __device__ __forceinline__ void bar() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -187,7 +200,7 @@ __device__ __forceinline__ void bar() {
 
 // position in the (tile, slice) sequence of one workgroup
 struct SliceIter {
-  int r;          // round of the current tile (-1: finished)
+  int r;          // step of the current tile in the workgroup's stride (-1: finished)
   int ks, nk;     // slice within the tile, slices of the tile
   TileCoord c;
 };
@@ -205,15 +218,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typ
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  // each XCD walks one contiguous run of tiles (xcd_run_start); with a grid
+  // of at least `total` workgroups every workgroup gets at most one tile
+  const int X = G < 8 ? G : 8, xcd = b % X, wi = b / X, nx = (G - xcd + X - 1) / X;
+  const int run_lo = xcd_run_start<MODE>(a, a.offsets, total, MT * NT, xcd, X);
+  const int run_hi = xcd_run_start<MODE>(a, a.offsets, total, MT * NT, xcd + 1, X);
 
-  // next round >= r holding a tile of this workgroup with a non-empty contraction
+  // next step >= r holding a tile of this workgroup with a non-empty contraction
   auto settle = [&](int r, SliceIter& it) {
     for (;; ++r) {
-      const int base = r * G;
-      if (base >= total) break;
-      const int cnt = min(G, total - base);
-      if (b >= cnt) break;
-      resolve_tile<MODE, BM>(a, base + xcd_remap(b, cnt), NT, MT, it.c);
+      const int L = run_lo + wi + r * nx;
+      if (L >= run_hi) break;
+      resolve_tile<MODE, BM>(a, L, NT, MT, it.c);
       it.nk = (it.c.k_end - it.c.k_begin + BK - 1) / BK;
       // a tile starting past its group's rows has nothing to do (only a tile
       // prefix built for another tile height could produce one)
@@ -294,6 +310,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typ
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   };
 
+  // Staged epilogue (bf16 stores): the wave's sub-tile goes out in units of
+  // 32 rows x 64 columns, each written to a 4 KB LDS buffer of its own (8-byte
+  // pieces, swizzled 128-byte rows) and read back as 16-byte row pieces, so
+  // that every store writes whole 128-byte row segments.  The buffers lie in
+  // the stage of the tile's last slice, which no DMA targets before the next
+  // slice's barrier; a barrier first lets every wave finish reading it.  Stores
+  // go through a buffer resource over the tile's valid rows (columns past N
+  // get an offset outside it), so every lane issues kEpiStores of them.
+  static_assert(!Epi::kStaged || (FN % 2 == 0 && C::NW * 4096 <= C::STAGE_BYTES), "staged epilogue");
+  constexpr int kEpiStores = Epi::kStaged ? FM * (FN / 2) * 4 : 0;
+  auto epilogue_staged = [&](const TileCoord& c, uint32_t stage_byte) {
+    if constexpr (Epi::kStaged) {
+      bar();
+      const int rows = min(c.m_end - c.m0, BM);
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(ep.C + c.g * ep.c_gstride + (int64_t)c.m0 * ep.ldc, (uint32_t)(rows * ep.ldc * 2));
+      MOE_LDS u32x2* w2 = (MOE_LDS u32x2*)(uintptr_t)(stage_byte + wave * 4096);
+      const MOE_LDS u32x4* r4 = (const MOE_LDS u32x4*)(uintptr_t)(stage_byte + wave * 4096);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; ++jp) {
+          const int row = lane & 31;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int j = jp * 2 + jj, chunk = jj * 4 + q;
+              const u32x2 v = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                               pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+              w2[(row * 8 + (chunk ^ stage_swz(row))) * 2 + (lane >> 5)] = v;
+            }
+          const int col = c.n0 * BN + wn * (BN / WN) + jp * 64 + (lane & 7) * 8;
+          const uint32_t col_off = col + 8 <= ep.N ? (uint32_t)col * 2 : kOffRange;
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const int rr = it * 8 + (lane >> 3), cc = lane & 7;
+            const u32x4 v = r4[rr * 8 + (cc ^ stage_swz(rr))];
+            const uint32_t off = col_off + (uint32_t)((wm * (BM / WM) + i * 32 + rr) * ep.ldc * 2);
+            store_b128<MODE == RAGGED_K>(v, rs, off);
+          }
+        }
+    }
+  };
+
   // epilogue: row = lane%32 of the block, columns 8*(e/4) + 4*(lane/32) + 0..3
   auto epilogue = [&](const TileCoord& c) {
     const int nt = c.n0;
@@ -345,10 +406,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typ
     }
   };
 
+  // epilogues run so far, and that count when each ring stage's slice was
+  // issued: the staged epilogue's stores issued after a slice's DMA are
+  // counted exactly in the wait for that slice
+  int epis = 0;
+  int epis_at[STAGES];
   // prologue: the first STAGES-1 slices
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
+    epis_at[s] = 0;
     if (ld.r >= 0) {
       issue(s);
       advance_ld();
@@ -365,9 +432,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typ
       // flight.  Vector memory operations complete in issue order, so the
       // epilogue's stores and loads (issued after every DMA in flight) only
       // make this wait more conservative, never too short.
-      wait_slices_after<STAGES - 2, DMA_PER_SLICE>(issued - n - 1);
+      if constexpr (Epi::kStaged)
+        wait_vmcnt_dyn<0, 63>((issued - n - 1) * DMA_PER_SLICE + (epis - epis_at[n % STAGES]) * kEpiStores);
+      else
+        wait_slices_after<STAGES - 2, DMA_PER_SLICE>(issued - n - 1);
       bar();
       if (ld.r >= 0) {
+        epis_at[issued % STAGES] = epis;
         issue(issued % STAGES);   // the stage multiplied in the previous iteration
         advance_ld();
         ++issued;
@@ -388,7 +459,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typ
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
       }
     }
-    epilogue(comp.c);
+    if constexpr (Epi::kStaged) {
+      epilogue_staged(comp.c, lds0 + ((n - 1) % STAGES) * C::STAGE_BYTES);
+      ++epis;
+    } else {
+      epilogue(comp.c);
+    }
     settle(comp.r + 1, comp);
   } while (comp.r >= 0);
 }

@@ -310,15 +310,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ int stage_swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-// 16-byte buffer store (device pass only: in the host pass a device builtin
-// inside a helper makes the compiler drop later kernels' launch stubs)
-__device__ __forceinline__ void store_b128(u32x4 v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, 0);
-#endif
-}
 
 // MX = true: both operands are K-contiguous fp8 e4m3 codes with e8m0 scales
 // (`s`), multiplied with v_mfma_scale_f32_32x32x64_f8f6f4 (operand layout as in
@@ -343,21 +334,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   __syncthreads();
   const int total = (MODE == RAGGED_M) ? s_pre[a.G] * NT : total_tiles<MODE>(a, NT, MT);
   const int G = gridDim.x, b = blockIdx.x;
+  const int X = G < 8 ? G : 8, xcd = b % X, wi = b / X, nx = (G - xcd + X - 1) / X;
+  const int run_lo = xcd_run_start<MODE>(a, s_off, total, MT * NT, xcd, X);
+  const int run_hi = xcd_run_start<MODE>(a, s_off, total, MT * NT, xcd + 1, X);
 
   struct It {
-    int r;         // round of the tile (-1: done)
+    int r;         // step of the tile in this workgroup's stride (-1: done)
     int ks, nk;    // slice within the tile, slices of the tile
     TileCoord c;
   };
-  // first round >= r with a tile of this workgroup that has a contraction
+  // first step >= r with a tile of this workgroup that has a contraction
   // (tiles without one are zero-filled by the caller)
   auto settle = [&](int r, It& it) {
     for (;; ++r) {
-      const int base = r * G;
-      if (base >= total) break;
-      const int cnt = min(G, total - base);
-      if (b >= cnt) break;
-      resolve_tile<MODE, BM>(a, s_off, s_pre, base + xcd_remap(b, cnt), NT, MT, it.c);
+      const int L = run_lo + wi + r * nx;
+      if (L >= run_hi) break;
+      resolve_tile<MODE, BM>(a, s_off, s_pre, L, NT, MT, it.c);
       it.nk = (it.c.k_end - it.c.k_begin + BK - 1) / BK;
       if (it.c.m0 >= it.c.m_end) it.nk = 0;
       if (it.nk > 0) {
@@ -480,7 +472,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         const int rr = it * 8 + (lane >> 3), cc = lane & 7;
         const u32x4 v = r4[rr * 8 + (cc ^ stage_swz(rr))];
         const uint32_t off = col_off + (uint32_t)((wm * (BM / WM) + rr) * ep.ldc * 2);
-        store_b128(v, rs, off);
+        store_b128<MODE == RAGGED_K>(v, rs, off);
       }
     } else {
 #pragma unroll
@@ -594,7 +586,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       epilogue(comp.c, stage_of(n + 1));
       if (Epi::kStaged) lds_barrier();   // every wave has read its staged rows
     }
-    if (loaded) store_stage(la, lb, stage_of(n + 1));
+    // stored even when nothing was loaded (the stage is not read again): every
+    // path then waits for the loads it issued here, so the compiler never
+    // carries them as possibly pending into the next tile, where the first
+    // reuse of their registers would wait for everything outstanding,
+    // including the epilogue's stores
+    store_stage(la, lb, stage_of(n + 1));
     lds_barrier();
     ++n;
   };
