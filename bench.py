@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "9d0430006e382630d192be9819c36b3bc40492b2ad22bac921983ffc58138097",
-                          "fetch_bytes": 10584568012, "write_bytes": 15032385536},
+    "gemm_wgrad_gateup": {"src_sha": "1fc9b7d4e95312e96f7025a2ab975135e26105cb215d87d0ea94bbeb503235e2",
+                          "fetch_bytes": 1798278400, "write_bytes": 15032391296},
 }
 
 

@@ -115,6 +115,10 @@ LAYER_CASES = [
          router_std=0.02),
     _cfg("bf16_mostly_empty_experts_bwd", T=40, d=128, E=64, k=2, f=64, backward=True),
     _cfg("bf16_mixtral_like_fwd", T=512, d=512, E=8, k=2, f=512),
+    # grids of fewer workgroups than XCDs (the per-XCD tile runs of the
+    # persistent kernels then split over G < 8 workgroups)
+    _cfg("bf16_two_experts_bwd", T=48, d=64, E=2, k=1, f=64, backward=True),
+    _cfg("bf16_one_expert_bwd", T=33, d=64, E=1, k=1, f=64, f_shared=64, backward=True),
 ]
 
 
