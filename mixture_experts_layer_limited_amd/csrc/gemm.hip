@@ -127,7 +127,8 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
 // Kernel of the bf16 path: 3 = register-staged 128x128, one tile per
 // workgroup (gemm_regs.hpp); 4 / 5 = its persistent pipelined form with
 // K-slices of 64 (two LDS stages) / 128 (one stage); DMA-fed LDS ring (gemm_mfma.hpp)
-// with 0 = 128x128 x 4 stages, 1 = 128x256 x 3 stages, 2 = 256x128 x 3 stages.
+// with 0 = 128x128 x 4 stages, 1 = 128x256 x 3 stages (2x4 waves of 64x64: two
+// waves per SIMD), 2 = 256x128 x 3 stages.
 // Defaults per contraction class, from measurements at the 256-expert,
 // d = 7168 shape: products with a K-contiguous weight (forward) run on the
 // 128x256 DMA ring, data gradients (row-contiguous weight) on the
@@ -227,7 +228,7 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
       return launch_pipe<LA, LB, MODE, Epi, 64>(a, ep, n_logical, rows_total, st);
     }
     if (t == 1)
-      return launch_mfma<128, 256, 2, 2, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+      return launch_mfma<128, 256, 2, 4, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
     if (t == 2)
       return launch_mfma<256, 128, 2, 2, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
     return launch_mfma<128, 128, 2, 2, 4, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
