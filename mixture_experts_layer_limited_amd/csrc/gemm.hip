@@ -120,7 +120,7 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, ep, NT, MT);
+  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, MxArgs{}, ep, NT, MT);
   return hipGetLastError();
 }
 

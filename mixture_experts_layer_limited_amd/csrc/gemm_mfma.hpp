@@ -62,7 +62,10 @@ namespace moe {
 
 constexpr uint32_t kOffRange = 0x80000000u;   // lane offset that is outside every range
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+// MX = true: fp8 operands with e8m0 scales; a stage then also holds the
+// slice's scale words (one 32-bit word = four block scales per row), A's at
+// word q < BM of an NW*64-word region, B's at word q < BN of a second one.
+template <int BM, int BN, int WM, int WN, int STAGES, bool MX = false>
 struct TileCfg {
   static constexpr int BK = 64;
   static constexpr int NW = WM * WN;
@@ -71,10 +74,14 @@ struct TileCfg {
   static constexpr int FN = BN / (32 * WN);
   static constexpr int A_BYTES = BM * 128;                 // one operand slice in LDS
   static constexpr int B_BYTES = BN * 128;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int SC_WORDS = MX ? NW * 64 : 0;        // words per scale region
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + 2 * SC_WORDS * 4;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int A_DMA = BM * 8 / 64 / NW;           // DMA instructions per wave per slice
   static constexpr int B_DMA = BN * 8 / 64 / NW;
+  static constexpr int SC_DMA = MX ? 2 : 0;                // one scale word per lane for A and for B
+  static_assert(!MX || (SC_WORDS >= BM && SC_WORDS >= BN), "scale regions");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(FM >= 1 && FN >= 1 && BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile");
   static_assert(A_DMA * 64 * NW == BM * 8 && B_DMA * 64 * NW == BN * 8, "DMA split");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "row-contiguous layout needs >= 16 chunks per K-row");
@@ -205,11 +212,18 @@ struct SliceIter {
   TileCoord c;
 };
 
-template <int BM, int BN, int WM, int WN, int STAGES, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typename Epi::P ep, int NT, int MT) {
-  using C = TileCfg<BM, BN, WM, WN, STAGES>;
+// MX = true: both operands K-contiguous fp8 e4m3 codes with e8m0 scales (`s`),
+// multiplied with v_mfma_scale_f32_32x32x64_f8f6f4 (operand layout as in
+// gemm_mx.hpp); GemmArgs then count K, lda, ldb in 2-byte units, so a slice of
+// BK = 64 units is 128 fp8 values and the data path is the bf16 one.
+template <int BM, int BN, int WM, int WN, int STAGES, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi,
+          bool MX = false>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT,
+                                                                 int MT) {
+  using C = TileCfg<BM, BN, WM, WN, STAGES, MX>;
+  static_assert(!MX || (LA == KC && LB == KC && MODE != RAGGED_K), "MXFP8: K-contiguous row-ragged products");
   constexpr int BK = C::BK, FM = C::FM, FN = C::FN;
-  constexpr int DMA_PER_SLICE = C::A_DMA + C::B_DMA;
+  constexpr int DMA_PER_SLICE = C::A_DMA + C::B_DMA + C::SC_DMA;
   extern __shared__ u32x4 smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MOE_LDS void*)smem;
 
@@ -250,6 +264,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typ
   const void* rb_base = nullptr;
   uint32_t ra_bytes = 0, rb_bytes = 0;
   uint32_t soa = 0, sob = 0;
+  // MX: scale-word resources, per-lane offsets and the slice's byte offset
+  const uint8_t* rsa_base = nullptr;
+  const uint8_t* rsb_base = nullptr;
+  uint32_t rsa_bytes = 0, rsb_bytes = 0, sa_off = kOffRange, sb_off = kOffRange, sos = 0;
   const uint32_t stride_a = LA == KC ? BK * 2 : (uint32_t)(BK * a.lda * 2);
   const uint32_t stride_b = LB == KC ? BK * 2 : (uint32_t)(BK * a.ldb * 2);
 
@@ -286,13 +304,42 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typ
     }
     soa = 0;
     sob = 0;
+    if constexpr (MX) {
+      // lane q = wave*64 + lane fetches the scale word of tile row q (A) and
+      // of B row q (its weight row), or nothing (an offset outside the range)
+      const int q = wave * 64 + lane;
+      const int nrows = min(c.m_end - c.m0, BM);
+      rsa_base = s.A_s + (int64_t)c.m0 * s.a_s_ld;
+      rsa_bytes = (uint32_t)(nrows * s.a_s_ld);
+      sa_off = q < nrows ? (uint32_t)(q * s.a_s_ld) : kOffRange;
+      rsb_base = s.B_s + (MODE == RAGGED_M ? (int64_t)c.g * s.b_s_gstride : 0);
+      rsb_bytes = (uint32_t)((int64_t)a.b_next * s.b_s_ld);
+      int g = -1;
+      if (q < BN) {
+        if constexpr (Epi::kPaired) g = Epi::template b_row_paired<BN, WN>(ep, nt, q);
+        else g = nt * BN + q;
+      }
+      sb_off = (g >= 0 && g < a.b_next) ? (uint32_t)((int64_t)g * s.b_s_ld) : kOffRange;
+      sos = (uint32_t)(c.k_begin / 16);             // 2-byte units -> scale bytes (one per 32 values)
+    }
   };
   auto issue = [&](int stage) {
-    const uint32_t s = lds0 + stage * C::STAGE_BYTES;
-    pa.issue(ra_base, ra_bytes, soa, s);
-    pb.issue(rb_base, rb_bytes, sob, s + C::A_BYTES);
+    const uint32_t sbase = lds0 + stage * C::STAGE_BYTES;
+    pa.issue(ra_base, ra_bytes, soa, sbase);
+    pb.issue(rb_base, rb_bytes, sob, sbase + C::A_BYTES);
     soa += stride_a;
     sob += stride_b;
+    if constexpr (MX) {
+#if defined(__HIP_DEVICE_COMPILE__)
+      const uint32_t sc = sbase + C::A_BYTES + C::B_BYTES + wave * 64 * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(rsa_base, rsa_bytes), (MOE_LDS void*)(uintptr_t)sc, 4,
+                                               sa_off, sos, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(rsb_base, rsb_bytes),
+                                               (MOE_LDS void*)(uintptr_t)(sc + C::SC_WORDS * 4), 4, sb_off, sos, 0,
+                                               0);
+#endif
+      sos += BK / 16;                               // four scale bytes per 128-value slice
+    }
   };
 
   FragPlan<LA, BM, FM> fa;
@@ -445,8 +492,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, typ
       }
       const uint32_t sa = lds0 + (n % STAGES) * C::STAGE_BYTES;
       const uint32_t sb = sa + C::A_BYTES;
+      if constexpr (MX) {
+        // two 64-deep steps per slice; lane half h takes 16-byte chunks
+        // 4 st + h and 4 st + 2 + h of its row and passes the scale of block h
+        const int h = lane >> 5;
+        const uint32_t sc = sb + C::B_BYTES;
+        uint32_t wa[FM], wb[FN];
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+        for (int i = 0; i < FM; ++i)
+          wa[i] = *(const MOE_LDS uint32_t*)(uintptr_t)(sc + (wm * (BM / WM) + i * 32 + (lane & 31)) * 4) >> (8 * h);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          wb[j] = *(const MOE_LDS uint32_t*)(uintptr_t)(sc + C::SC_WORDS * 4 +
+                                                        (wn * (BN / WN) + j * 32 + (lane & 31)) * 4) >> (8 * h);
+        auto chunk = [&](uint32_t base, int row, int c) -> u32x4 {
+          return *(const MOE_LDS u32x4*)(uintptr_t)(base + row * 128 + ((c ^ kc_swz(row)) * 16));
+        };
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          i32x8 af[FM], bfr[FN];
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int row = wm * (BM / WM) + i * 32 + (lane & 31);
+            const u32x4 lo = chunk(sa, row, st * 4 + h), hi = chunk(sa, row, st * 4 + 2 + h);
+            af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          }
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int row = wn * (BN / WN) + j * 32 + (lane & 31);
+            const u32x4 lo = chunk(sb, row, st * 4 + h), hi = chunk(sb, row, st * 4 + 2 + h);
+            bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          }
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              if (st == 0)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0,
+                                                                            (int)wb[j], 0, (int)wa[i]);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 2,
+                                                                            (int)wb[j], 2, (int)wa[i]);
+            }
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < (MX ? 0 : BK / 16); ++kk) {
         bf16x8 af[FM], bfr[FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) af[i] = fa.read(sa, i, kk);

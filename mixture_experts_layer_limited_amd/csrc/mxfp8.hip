@@ -19,6 +19,7 @@
 
 #include "common.hpp"
 #include "gemm.hpp"
+#include "gemm_mfma.hpp"
 #include "gemm_mx.hpp"
 #include "kernels.hpp"
 
@@ -285,14 +286,49 @@ static hipError_t launch_mx_pipe(GemmArgs a, const MxArgs& s, const typename Epi
   return hipGetLastError();
 }
 
-// MOE_TILE_WGRAD / MOE_TILE pick the one-tile (3) or pipelined (4) kernel
-static bool mx_pipe(bool wgrad) {
+// DMA-fed LDS ring (gemm_mfma_kernel in its MXFP8 form): 128x256 tiles, 2x4
+// waves, three stages; one tile per workgroup.  Arguments in bytes, converted
+// to the kernel's 2-byte units here.
+template <GemmMode MODE, class Epi>
+static hipError_t launch_mx_dma(GemmArgs a, const MxArgs& s, const typename Epi::P& ep, int n_logical,
+                                int rows_total, hipStream_t st) {
+  constexpr int BM = 128, BN = 256, WM = 2, WN = 4, STAGES = 3;
+  using C = TileCfg<BM, BN, WM, WN, STAGES, true>;
+  const int bn_cols = Epi::kPaired ? BN / 2 : BN;
+  const int NT = (n_logical + bn_cols - 1) / bn_cols;
+  const int MT = (MODE == RAGGED_M) ? 0 : (a.M + BM - 1) / BM;
+  int64_t tiles;
+  if (MODE == RAGGED_M) tiles = (int64_t)((rows_total + BM - 1) / BM + a.G) * NT;
+  else tiles = (int64_t)MT * NT;
+  if (tiles <= 0) return hipSuccess;
+  a.lda /= 2; a.ldb /= 2; a.K /= 2; a.b_kend /= 2; a.b_gstride /= 2;
+  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, STAGES, KC, KC, MODE, Epi, true>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<(unsigned)tiles, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
+  return hipGetLastError();
+}
+
+// Kernel of the MXFP8 products: 1 = DMA ring, 3 = one tile per workgroup,
+// 4 = persistent pipelined.  Row-ragged and dense products default to the DMA
+// ring, weight gradients to the persistent kernel; MOE_TILE / MOE_TILE_WGRAD
+// override them for tuning runs.
+static int mx_choice(bool wgrad) {
   static int v = -1, w = -1;
   if (v < 0) {
+    auto pick = [](const char* e, int dflt) {
+      const int x = e ? atoi(e) : dflt;
+      return (x == 1 || x == 3 || x == 4) ? x : dflt;
+    };
     const char* e = getenv("MOE_TILE");
     const char* f = getenv("MOE_TILE_WGRAD");
-    v = (e && atoi(e) == 4) ? 1 : 0;
-    w = f ? (atoi(f) == 4 ? 1 : 0) : (e ? v : 1);
+    v = pick(e, 1);
+    w = f ? pick(f, 4) : (e ? (v == 1 ? 4 : v) : 4);
   }
   return wgrad ? w : v;
 }
@@ -307,16 +343,18 @@ static hipError_t mx_rows_gemm(const MxQ& q, const int* offsets, const int* pref
   a.A = q.codes; a.lda = K; a.B = w.codes; a.ldb = K; a.b_gstride = w_gstride;
   a.M = rows; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
   MxArgs s{q.scales, w.scales, K / 32, K / 32, w_gstride / 32};
-  bool pipe = mx_pipe(false);           // its staged epilogue stores 16-byte row pieces
-  if constexpr (Epi::kStaged)
-    pipe = pipe && ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0;
+  int t = mx_choice(false);
+  if constexpr (Epi::kStaged)         // staged epilogues store 16-byte row pieces
+    if (!(ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0)) t = 3;
   if (offsets) {
     a.offsets = offsets; a.tile_prefix = prefix; a.G = G;
-    if (pipe) return launch_mx_pipe<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
+    if (t == 1) return launch_mx_dma<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
+    if (t == 4) return launch_mx_pipe<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
     return launch_mx<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
   }
   a.G = 1;
-  if (pipe) return launch_mx_pipe<DENSE, Epi>(a, s, ep, n_logical, rows, st);
+  if (t == 1) return launch_mx_dma<DENSE, Epi>(a, s, ep, n_logical, rows, st);
+  if (t == 4) return launch_mx_pipe<DENSE, Epi>(a, s, ep, n_logical, rows, st);
   return launch_mx<DENSE, Epi>(a, s, ep, n_logical, rows, st);
 }
 
@@ -373,7 +411,7 @@ hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, 
   MxArgs s{p.scales, q.scales, ldq / 32, ldq / 32, 0};
   // the pipelined kernel stages 16-byte row pieces of the output and skips
   // empty contractions: it needs aligned rows and zero-filled empty experts
-  const bool pipe = mx_pipe(true) && N % 8 == 0 && ((uintptr_t)dw & 15) == 0;
+  const bool pipe = mx_choice(true) == 4 && N % 8 == 0 && ((uintptr_t)dw & 15) == 0;
   if (pipe) {
     const int64_t vec = (int64_t)M * N * 2 / 16;
     zero_empty_groups_mx_kernel<<<dim3(64, poff ? G : 1), 256, 0, st>>>(poff, (u32x4*)dw, vec, K);
