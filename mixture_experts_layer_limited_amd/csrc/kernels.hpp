@@ -16,7 +16,7 @@ struct RouterParams {
   float aux_coeff;
 };
 
-constexpr int kRouterTokensPerBlock = 64;
+constexpr int kRouterTokensPerBlock = 16;
 constexpr int kPermTokensPerRange = 64;
 
 // router.hip

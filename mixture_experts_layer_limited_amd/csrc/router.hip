@@ -258,12 +258,26 @@ __global__ __launch_bounds__(256) void router_finalize_kernel(const int* __restr
   __shared__ double term[kMaxExperts];
   const int e = threadIdx.x;
   if (e < p.E) {
+    // eight independent partial sums (blocks b = r mod 8), combined in a fixed
+    // order: the loads overlap and the result does not depend on scheduling
+    constexpr int R = 8;
     int c = 0;
-    float cs = 0.0f;
-    for (int b = 0; b < nblk; ++b) {
-      c += cnt_part[(int64_t)b * p.E + e];
-      if (colsum_part) cs += colsum_part[(int64_t)b * p.E + e];
+    float part[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[r] = 0.0f;
+    int b = 0;
+    for (; b + R <= nblk; b += R) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        c += cnt_part[(int64_t)(b + r) * p.E + e];
+        if (colsum_part) part[r] += colsum_part[(int64_t)(b + r) * p.E + e];
+      }
     }
+    for (int r = 0; b < nblk; ++b, ++r) {
+      c += cnt_part[(int64_t)b * p.E + e];
+      if (colsum_part) part[r] += colsum_part[(int64_t)b * p.E + e];
+    }
+    const float cs = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
     counts[e] = c;
     term[e] = (p.T > 0) ? ((double)c / ((double)p.T * p.k)) * ((double)cs / p.T) : 0.0;
   }
