@@ -180,6 +180,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cold-steps", type=int, default=3,
+                    help="extra steps after the timed ones, each after a 512 MiB write that evicts "
+                         "L2 and MALL (reported apart as cold_ms_per_step)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 3 times (scale reference for HBM byte counters)")
     args = ap.parse_args()
@@ -233,16 +236,39 @@ def main():
     stream = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # one event per step boundary (on the compute stream) gives the per-step
+    # spread without adding work to the timed steps
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     abi.moe_trace_begin(cap)
     t_start.record(stream)
     for i in range(args.steps):
+        marks[i].record(stream)
         step()
+    marks[args.steps].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     trace = abi.moe_trace_end(cap)
     ms = t_start.elapsed_time(t_end) / max(args.steps, 1)
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     print("# timed steps done", file=sys.stderr, flush=True)
+
+    def pct(v, q):
+        return v[min(len(v) - 1, int(round(q * (len(v) - 1))))] if v else None
+
+    cold = []
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        for _ in range(args.cold_steps):
+            flush.zero_()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1))
+        del flush
+        cold.sort()
 
     flops = step_flops(cfg)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -291,6 +317,9 @@ def main():
         "config": {"workload": f"{cfg.name} MoE layer fwd+bwd", "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "k": cfg.k, "f": cfg.f, "f_shared": cfg.f_shared, "score": cfg.score,
                    "n_group": cfg.n_group, "topk_group": cfg.topk_group, "parallelism": "none (1 GPU)"},
+        "step_ms": {"median": round(pct(per_step, 0.5), 4), "p10": round(pct(per_step, 0.1), 4),
+                    "p90": round(pct(per_step, 0.9), 4)} if per_step else None,
+        "cold_ms_per_step": round(pct(cold, 0.5), 4) if cold else None,
         "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
         "mfma_peak_frac": round(tflops / peak_mfma, 4),
         "roofline": roof,

@@ -76,8 +76,13 @@ DSV3 = MoEConfig("deepseek_v3", T=4096, d=7168, E=256, k=8, f=2048, f_shared=204
                  backward=True, router_std=0.02, expert_std=0.02,
                  bias="normal", bias_std=0.01)
 DSV3_SKEW = DSV3.with_(name="deepseek_v3_skew_mxfp8", dtype="mxfp8", bias="zipf")
+# one GPU's share of the DeepSeek-V3 layer under 64-way expert parallelism: 4
+# local experts of 8192 rows each (every token reaches all four), no shared
+# expert; times the expert GEMMs at the per-GPU shape of an EP deployment
+DSV3_EP_SHARE = MoEConfig("deepseek_v3_ep_share", T=8192, d=7168, E=4, k=4, f=2048,
+                          backward=True, router_std=0.02, expert_std=0.02)
 
-CONFIGS = {c.name: c for c in (TINY, MIXTRAL, QWEN3, DSV3, DSV3_SKEW)}
+CONFIGS = {c.name: c for c in (TINY, MIXTRAL, QWEN3, DSV3, DSV3_SKEW, DSV3_EP_SHARE)}
 
 # tensor ids for per-tensor seeding
 _TID = {"x": 1, "w_router": 2, "bias": 3, "w13": 4, "w2": 5, "ws13": 6,

@@ -83,7 +83,7 @@ class _Ops:
 
 
 FULL = [mi.CONFIGS["deepseek_v3"], mi.CONFIGS["qwen3_235b"], mi.CONFIGS["mixtral"],
-        mi.CONFIGS["deepseek_v3_skew_mxfp8"]]
+        mi.CONFIGS["deepseek_v3_skew_mxfp8"], mi.CONFIGS["deepseek_v3_ep_share"]]
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
