@@ -131,10 +131,10 @@ __device__ __forceinline__ void resolve_tile(const GemmArgs& a, const int* off, 
     c.k_begin = 0; c.k_end = a.K;
   } else {
     // group-major; inside a group, bands of kBandM m-tiles walked n-tile by
-    // n-tile (m fastest inside the band).  A run of 64 consecutive tiles (what
-    // one XCD takes of a round) is then about 8 x 8 tiles: it reads 8 row
-    // blocks of each operand once and reuses each 8 times from L2, instead of
-    // re-reading one operand's whole panel for every row of tiles.
+    // n-tile (m fastest inside the band).  64 consecutive tiles (what the
+    // workgroups of one XCD hold at a time) are then about 8 x 8 tiles: they
+    // read 8 row blocks of each operand once and reuse each 8 times from L2,
+    // instead of re-reading one operand's whole panel for every row of tiles.
     constexpr int kBandM = 8;
     int per = MT * NT;
     int g = L / per, r = L % per;

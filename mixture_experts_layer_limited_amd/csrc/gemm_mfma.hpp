@@ -31,11 +31,11 @@
 //   Per-lane read offsets are computed once; the K step enters as an
 //   immediate offset and the ring stage as one add per slice.
 //
-// Schedule.  A workgroup walks rounds r = 0, 1, ...: round r covers logical
-// tiles [r G, (r+1) G) (G = grid size), spread so each XCD gets a contiguous run
-// (tiles running together on one XCD are neighbours in the expert-major order
-// and share weight / activation panels in its L2).  With G >= tiles this is one
-// tile per workgroup; with a smaller grid the kernel is persistent.  The
+// Schedule.  Each XCD owns one contiguous run of the logical tiles
+// (xcd_run_start) and its workgroups stride through it, so tiles running
+// together on one XCD are neighbours in the expert-major order and share
+// weight / activation panels in its L2.  With G >= tiles every workgroup gets
+// at most one tile; with a smaller grid the kernel is persistent.  The
 // loads walk (tile, slice) pairs: the DMA for the pair STAGES-1 ahead is issued
 // before the current pair is multiplied, so loads of the next tile overlap the
 // current tile's last slices and its epilogue.  The multiply side is a tile

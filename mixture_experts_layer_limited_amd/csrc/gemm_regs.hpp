@@ -274,10 +274,10 @@ __global__ __launch_bounds__(256) void gemm_regs_kernel(GemmArgs a, typename Epi
 // Persistent register-pipelined variant.
 //
 // The grid holds as many workgroups as fit on the chip (two per CU: their LDS,
-// and registers capped at 256 per lane so two waves share a SIMD); each walks
-// rounds of logical tiles (round r: tiles [r G, (r+1) G), spread with
-// xcd_remap).  The ragged offsets and tile prefix are copied to LDS once, so
-// finding a tile costs no global-memory round trip.  Loads walk the flat
+// and registers capped at 256 per lane so two waves share a SIMD); the
+// workgroups of each XCD stride through one contiguous run of the logical tiles
+// (xcd_run_start).  The ragged offsets and tile prefix are copied to LDS once,
+// so finding a tile costs no global-memory round trip.  Loads walk the flat
 // sequence of (tile, K-slice) pairs one slice ahead of the multiply, crossing
 // tile boundaries.  On a tile's last slice the epilogue runs before the
 // prefetched slice is written to LDS: the loads of the next tile are issued
@@ -287,7 +287,9 @@ __global__ __launch_bounds__(256) void gemm_regs_kernel(GemmArgs a, typename Epi
 //
 // Two-byte outputs of plain stores are staged through the LDS stage that the
 // prefetched slice will fill: each wave writes its 64x64 sub-tile there and
-// stores it back 8 columns (16 bytes) per lane, 128 contiguous bytes per row.
+// stores it back 8 columns (16 bytes) per lane, 128 contiguous bytes per row
+// (non-temporal for weight gradients, whose output stream would otherwise push
+// the operand panels out of L2).
 // ---------------------------------------------------------------------------
 // BK = 64: two LDS stages (the store of slice n+1 goes to the stage not being
 // read); BK = 128: one stage of 64 KB, refilled after a barrier that follows
