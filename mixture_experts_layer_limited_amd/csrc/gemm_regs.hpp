@@ -4,8 +4,10 @@
 // workgroups of the ragged schedule exit at once), 256 threads in 2x2 waves,
 // each wave owning 64x64 of a 128x128 tile as 2x2 blocks of 32x32
 // accumulators (v_mfma_f32_32x32x16_bf16), BK = 64.  Global loads of slice
-// k+1 go to registers while slice k is multiplied from LDS; two LDS stages, one
-// barrier per slice.  Every LDS row holds 64 bf16 = eight 16-byte chunks,
+// k+1 go to registers while slice k is multiplied from LDS.  One LDS stage
+// (32 KB) and registers capped at 168 per lane let three workgroups share a
+// CU, so more slices are in flight per CU; the stage costs a second barrier
+// per slice (every wave done reading it before slice k+1 is written).  Every LDS row holds 64 bf16 = eight 16-byte chunks,
 // K-contiguous, chunk c of row r at position c ^ ((r ^ (r >> 3)) & 7): the
 // fragment reads (16 consecutive rows per cycle on gfx950's 64 banks), the
 // 16-byte K-contiguous writes and the 8-byte transposed writes of
@@ -36,8 +38,10 @@ struct RegTile {
   static constexpr int NTHR = 256;
   static constexpr int FM = 2, FN = 2;
   static constexpr int STAGE = (BM + BN) * 8;              // 16-byte chunks per stage
-  static constexpr int LDS_BYTES = 2 * STAGE * 16;
+  static constexpr int LDS_BYTES = STAGE * 16;             // one stage
 };
+// the one-tile MXFP8 kernel keeps two stages of the same shape
+constexpr int kMxTileLdsBytes = 2 * RegTile::STAGE * 16;
 
 // Global -> register -> LDS staging of one operand slice: ROWS tile rows x BK
 // K values (CH = BK / 8 chunks per LDS row).  KC operands load 16 K values of
@@ -161,7 +165,7 @@ struct McLoader {
 };
 
 template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
-__global__ __launch_bounds__(256) void gemm_regs_kernel(GemmArgs a, typename Epi::P ep, int NT, int MT) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void gemm_regs_kernel(GemmArgs a, typename Epi::P ep, int NT, int MT) {
   using C = RegTile;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, BK = C::BK, NTHR = C::NTHR;
   constexpr int FM = C::FM, FN = C::FN;
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(256) void gemm_regs_kernel(GemmArgs a, typename Epi
   const int brow0 = wn * (BN / WN) + (lane & 31);
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) load(c.k_begin + (kt + 1) * BK);
-    const bf16x8* sa = (const bf16x8*)(smem + (kt & 1) * C::STAGE);
+    const bf16x8* sa = (const bf16x8*)smem;
     const bf16x8* sb = sa + BM * 8;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
@@ -235,7 +239,10 @@ __global__ __launch_bounds__(256) void gemm_regs_kernel(GemmArgs a, typename Epi
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store((kt + 1) & 1);
+    if (kt + 1 < nk) {
+      __syncthreads();                  // every wave has read slice k
+      store(0);
+    }
     __syncthreads();
   }
 

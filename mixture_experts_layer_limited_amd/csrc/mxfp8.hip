@@ -236,11 +236,11 @@ static hipError_t launch_mx(const GemmArgs& a, const MxArgs& s, const typename E
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_BYTES);
+                                       kMxTileLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
+  kern<<<(unsigned)grid, C::NTHR, kMxTileLdsBytes, st>>>(a, s, ep, NT, MT);
   return hipGetLastError();
 }
 
