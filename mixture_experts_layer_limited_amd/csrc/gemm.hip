@@ -180,7 +180,7 @@ static hipError_t launch_regs(const GemmArgs& a, const typename Epi::P& ep, int 
 template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi, int BK>
 static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int n_logical, int rows_total,
                               hipStream_t st) {
-  using C = PipeCfgFor<MODE, BK, false>;
+  using C = PipeCfg<BK>;
   const int bn_cols = Epi::kPaired ? C::BN / 2 : C::BN;
   const int NT = (n_logical + bn_cols - 1) / bn_cols;
   const int MT = (MODE == RAGGED_M) ? 0 : (a.M + C::BM - 1) / C::BM;
@@ -190,7 +190,7 @@ static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int 
   else tiles = (int64_t)MT * NT;
   if (tiles <= 0) return hipSuccess;
   if (a.G > kMaxExperts) return hipErrorInvalidValue;
-  int64_t grid = (int64_t)device_cus() * C::WG_PER_CU;   // as many as fit a CU
+  int64_t grid = (int64_t)device_cus() * 2;   // two workgroups fit a CU's LDS
   if (tiles < grid) grid = tiles;
   auto kern = gemm_pipe_kernel<LA, LB, MODE, Epi, BK>;
   static bool attr_set = false;

@@ -280,8 +280,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
 // ---------------------------------------------------------------------------
 // Persistent register-pipelined variant.
 //
-// The grid holds as many workgroups as fit on the chip (two or three per CU:
-// their LDS, and registers capped so that many waves share a SIMD); the
+// The grid holds as many workgroups as fit on the chip (two per CU: their LDS,
+// and registers capped at 256 per lane so two waves share a SIMD); the
 // workgroups of each XCD stride through one contiguous run of the logical tiles
 // (xcd_run_start).  The ragged offsets and tile prefix are copied to LDS once,
 // so finding a tile costs no global-memory round trip.  Loads walk the flat
@@ -299,27 +299,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
 // the operand panels out of L2).
 // ---------------------------------------------------------------------------
 // BK = 64: two LDS stages (the store of slice n+1 goes to the stage not being
-// read), or with ONE_STAGE one 32 KB stage and registers capped at 168 per
-// lane, so three workgroups share a CU (more slices in flight, a second
-// barrier per slice; used for the bf16 weight gradients, whose register use
-// fits the cap, while the MXFP8 form would spill under it); BK = 128: one
-// stage of 64 KB, refilled after a barrier that follows the multiply (same
-// LDS, twice the K per slice and per load in flight).
-template <int BK_, bool ONE_STAGE = false>
+// read); BK = 128: one stage of 64 KB, refilled after a barrier that follows
+// the multiply (same LDS, twice the K per slice and per load in flight).
+template <int BK_>
 struct PipeCfg {
   static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, BK = BK_, NTHR = 256;
   static constexpr int FM = 2, FN = 2, CH = BK / 8;
-  static constexpr int NSTAGE = (BK == 64 && !ONE_STAGE) ? 2 : 1;
-  static constexpr int WG_PER_CU = (BK == 64 && ONE_STAGE) ? 3 : 2;
+  static constexpr int NSTAGE = BK == 64 ? 2 : 1;
   static constexpr int STAGE = (BM + BN) * CH;             // 16-byte chunks per stage
   static constexpr int OFF_INTS = kMaxExperts + 1;
   static constexpr int LDS_BYTES = NSTAGE * STAGE * 16 + 2 * OFF_INTS * 4;
   static_assert(BK == 64 || BK == 128, "slice depth");
 };
-
-// the persistent kernel's configuration for an instantiation
-template <GemmMode MODE, int BK, bool MX>
-using PipeCfgFor = PipeCfg<BK, !MX && MODE == RAGGED_K && BK == 64>;
 
 // barrier for LDS traffic only: wait for this wave's LDS operations, then meet
 __device__ __forceinline__ void lds_barrier() {
@@ -335,9 +326,9 @@ __device__ __forceinline__ void lds_barrier() {
 // BK = 64 units is 128 fp8 values); ragged row offsets are rows, ragged
 // contraction offsets (padded rows of the column forms) are bytes.
 template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi, int BK_, bool MX = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PipeCfgFor<MODE, BK_, MX>::WG_PER_CU))) void gemm_pipe_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_pipe_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
   static_assert(!MX || (LA == KC && LB == KC && BK_ == 64), "MXFP8 operands are K-contiguous, 128-byte slices");
-  using C = PipeCfgFor<MODE, BK_, MX>;
+  using C = PipeCfg<BK_>;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, BK = C::BK, NTHR = C::NTHR;
   constexpr int FM = C::FM, FN = C::FN, CH = C::CH, NSTAGE = C::NSTAGE;
   extern __shared__ u32x4 smem[];

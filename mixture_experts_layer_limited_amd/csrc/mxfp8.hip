@@ -261,7 +261,7 @@ static int device_cus_mx() {
 template <GemmMode MODE, class Epi>
 static hipError_t launch_mx_pipe(GemmArgs a, const MxArgs& s, const typename Epi::P& ep, int n_logical,
                                  int rows_total, hipStream_t st) {
-  using C = PipeCfgFor<MODE, 64, true>;
+  using C = PipeCfg<64>;
   const int bn_cols = Epi::kPaired ? C::BN / 2 : C::BN;
   const int NT = (n_logical + bn_cols - 1) / bn_cols;
   const int MT = (MODE == RAGGED_M) ? 0 : (a.M + C::BM - 1) / C::BM;
@@ -272,7 +272,7 @@ static hipError_t launch_mx_pipe(GemmArgs a, const MxArgs& s, const typename Epi
   if (tiles <= 0) return hipSuccess;
   if (a.G > kMaxExperts) return hipErrorInvalidValue;
   a.lda /= 2; a.ldb /= 2; a.K /= 2; a.b_kend /= 2; a.b_gstride /= 2;
-  int64_t grid = (int64_t)device_cus_mx() * C::WG_PER_CU;
+  int64_t grid = (int64_t)device_cus_mx() * 2;
   if (tiles < grid) grid = tiles;
   auto kern = gemm_pipe_kernel<KC, KC, MODE, Epi, 64, true>;
   static bool attr_set = false;
