@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "276cc8d8085fd6280c2af5c0af026e144ebfd8ecd14b50d1c8616f960d0c38fa",
-                          "fetch_bytes": 1794337408, "write_bytes": 15032390784},
+    "gemm_wgrad_gateup": {"src_sha": "cbe42195b442bc5fc2a4519be0034506dba87ade71ba42707b3f49d426343b55",
+                          "fetch_bytes": 1761764896, "write_bytes": 15032392000},
 }
 
 
