@@ -245,8 +245,8 @@ moe_status router_topk_impl(const moe_cfg* c, const void* x, const void* w_route
   if (x) LAUNCH_NAMED("gemm_router_logits", gemm_router_logits<T>(x, w_router, logits, (int)c->T, (int)c->E, (int)c->d, st));
   const bool want_colsum = c->aux_coeff != 0.0f;
   LAUNCH_NAMED("router_topk", launch_router_topk(logits, bias, p, idx, gates, cnt_part, want_colsum ? colsum_part : nullptr, st));
-  LAUNCH_NAMED("router_finalize", launch_router_finalize(cnt_part, want_colsum ? colsum_part : nullptr, nblk, p, counts,
-                                want_colsum ? aux : nullptr, st));
+  LAUNCH_NAMED("router_finalize", launch_router_finalize(cnt_part, want_colsum ? colsum_part : nullptr, nblk, p, counts, st));
+  if (want_colsum && aux) LAUNCH_NAMED("router_aux", launch_router_aux(counts, colsum_part, p, aux, st));
   return ok();
 }
 

@@ -23,8 +23,10 @@ constexpr int kPermTokensPerRange = 64;
 hipError_t launch_router_topk(const float* logits, const float* bias, const RouterParams& p,
                               int32_t* idx, float* gates, int* cnt_part, float* colsum_part,
                               hipStream_t st);
-hipError_t launch_router_finalize(const int* cnt_part, const float* colsum_part, int nblk,
-                                  const RouterParams& p, int32_t* counts, float* aux, hipStream_t st);
+hipError_t launch_router_finalize(const int* cnt_part, float* colsum_part, int nblk, const RouterParams& p,
+                                  int32_t* counts, hipStream_t st);
+hipError_t launch_router_aux(const int32_t* counts, const float* colsum, const RouterParams& p, float* aux,
+                             hipStream_t st);
 template <class T>
 hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gates,
                              const float* d_gates, const int32_t* counts, const RouterParams& p,

@@ -249,49 +249,66 @@ hipError_t launch_router_topk(const float* logits, const float* bias, const Rout
   return hipGetLastError();
 }
 
-// counts[e] = sum over blocks; aux = coeff * E * sum_e (c_e / (T k)) (colsum_e / T)
+// counts[e] = sum over the router blocks' partial counts; with probability
+// sums, colsum_part[e] (the first block's row) becomes their total.  One
+// workgroup per expert: thread i sums blocks i, i + 256, ... and a fixed-shape
+// tree combines the 256 partial sums, so the result does not depend on
+// scheduling.
 __global__ __launch_bounds__(256) void router_finalize_kernel(const int* __restrict__ cnt_part,
-                                                              const float* __restrict__ colsum_part,
-                                                              int nblk, RouterParams p,
-                                                              int32_t* __restrict__ counts,
-                                                              float* __restrict__ aux) {
+                                                              float* __restrict__ colsum_part, int nblk,
+                                                              int E, int32_t* __restrict__ counts) {
+  __shared__ int sc[256];
+  __shared__ float sf[256];
+  const int e = blockIdx.x, t = threadIdx.x;
+  int c = 0;
+  float f = 0.0f;
+  for (int b = t; b < nblk; b += 256) {
+    c += cnt_part[(int64_t)b * E + e];
+    if (colsum_part) f += colsum_part[(int64_t)b * E + e];
+  }
+  sc[t] = c;
+  sf[t] = f;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+      sc[t] += sc[t + w];
+      sf[t] += sf[t + w];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    counts[e] = sc[0];
+    // only this workgroup reads column e; with no blocks there is no row to hold it
+    if (colsum_part && nblk > 0) colsum_part[e] = sf[0];
+  }
+}
+
+hipError_t launch_router_finalize(const int* cnt_part, float* colsum_part, int nblk, const RouterParams& p,
+                                  int32_t* counts, hipStream_t st) {
+  if (p.E <= 0) return hipSuccess;
+  router_finalize_kernel<<<p.E, 256, 0, st>>>(cnt_part, colsum_part, nblk, p.E, counts);
+  return hipGetLastError();
+}
+
+// aux = coeff * E * sum_e (c_e / (T k)) (colsum_e / T), summed in expert order
+__global__ __launch_bounds__(256) void router_aux_kernel(const int32_t* __restrict__ counts,
+                                                         const float* __restrict__ colsum, RouterParams p,
+                                                         float* __restrict__ aux) {
   __shared__ double term[kMaxExperts];
   const int e = threadIdx.x;
-  if (e < p.E) {
-    // eight independent partial sums (blocks b = r mod 8), combined in a fixed
-    // order: the loads overlap and the result does not depend on scheduling
-    constexpr int R = 8;
-    int c = 0;
-    float part[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) part[r] = 0.0f;
-    int b = 0;
-    for (; b + R <= nblk; b += R) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        c += cnt_part[(int64_t)(b + r) * p.E + e];
-        if (colsum_part) part[r] += colsum_part[(int64_t)(b + r) * p.E + e];
-      }
-    }
-    for (int r = 0; b < nblk; ++b, ++r) {
-      c += cnt_part[(int64_t)b * p.E + e];
-      if (colsum_part) part[r] += colsum_part[(int64_t)b * p.E + e];
-    }
-    const float cs = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-    counts[e] = c;
-    term[e] = (p.T > 0) ? ((double)c / ((double)p.T * p.k)) * ((double)cs / p.T) : 0.0;
-  }
+  if (e < p.E)
+    term[e] = (p.T > 0) ? ((double)counts[e] / ((double)p.T * p.k)) * ((double)colsum[e] / p.T) : 0.0;
   __syncthreads();
-  if (aux && e == 0) {
+  if (e == 0) {
     double s = 0.0;
     for (int q = 0; q < p.E; ++q) s += term[q];
     aux[0] = (float)((double)p.aux_coeff * p.E * s);
   }
 }
 
-hipError_t launch_router_finalize(const int* cnt_part, const float* colsum_part, int nblk,
-                                  const RouterParams& p, int32_t* counts, float* aux, hipStream_t st) {
-  router_finalize_kernel<<<1, 256, 0, st>>>(cnt_part, colsum_part, nblk, p, counts, aux);
+hipError_t launch_router_aux(const int32_t* counts, const float* colsum, const RouterParams& p, float* aux,
+                             hipStream_t st) {
+  router_aux_kernel<<<1, 256, 0, st>>>(counts, colsum, p, aux);
   return hipGetLastError();
 }
 

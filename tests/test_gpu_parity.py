@@ -68,6 +68,26 @@ def test_router_topk_from_logits_bitexact(cfg, ties):
         assert abs(float(host(aux)[0]) - want) <= 1e-5 * want
 
 
+def test_router_zero_tokens_writes_zero_counts_and_aux():
+    """T = 0: every count is 0 and the aux loss is exactly 0 (the per-block
+    partial sums are empty)."""
+    cfg = _cfg("softmax_aux_T0", T=0, E=128, k=8, aux_coeff=1e-3)
+    print("case router T=0", flush=True)
+    c = shape_of(cfg).cfg()
+    dev = "cuda"
+    # one-row buffers: the calls want non-NULL pointers, and T = 0 reads none of them
+    L = torch.empty(1, cfg.E, dtype=torch.float32, device=dev)
+    idx = torch.empty(1, cfg.k, dtype=torch.int32, device=dev)
+    gates = torch.empty(1, cfg.k, dtype=torch.float32, device=dev)
+    cnt = torch.full((cfg.E,), 7, dtype=torch.int32, device=dev)
+    aux = torch.full((1,), 3.0, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(abi.moe_workspace_size(c), 1), dtype=torch.uint8, device=dev)
+    abi.moe_router_topk(c, None, None, None, L, idx, gates, cnt, aux, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(cnt), np.zeros(cfg.E, np.int32))
+    assert float(host(aux)[0]) == 0.0
+
+
 # ---------------------------------------------------------------------------
 # permute: stable counting sort and row gather, bit-exact
 # ---------------------------------------------------------------------------
