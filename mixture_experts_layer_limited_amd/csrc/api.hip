@@ -259,7 +259,7 @@ moe_status gemm_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* of
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f;
   int* prefix = (int*)ws;
   if (rows > 0) {
-    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E), prefix, st));
+    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E, true), prefix, st));
     LAUNCH_NAMED("gemm_swiglu_fwd", gemm_swiglu_fwd<T>(x_perm, off, prefix, E, w13, hu, act, rows, d, f, st));
     LAUNCH_NAMED("gemm_down_fwd", gemm_down_fwd<T>(act, off, prefix, E, w2, y_perm, rows, d, f, st));
   }
@@ -281,7 +281,7 @@ moe_status gemm_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_pe
   const bool bf = sizeof(T) == 2;
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
   int* prefix = (int*)ws;
-  if (rows > 0) LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E), prefix, st));
+  if (rows > 0) LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E, false), prefix, st));
   if (rows > 0)
     LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd", gemm_down_dgrad_swiglu_bwd<T>(dy_perm, off, prefix, E, w2, hu, dhu, rows, d, f, st));
   // weight gradients cover every expert (empty experts get zeros)

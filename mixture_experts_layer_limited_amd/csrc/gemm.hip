@@ -208,7 +208,17 @@ static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int 
 // this value and the kernel resolves its tiles with its own BM: they must agree.
 // (the forward and data-gradient classes take the same override, and their
 // defaults both use 128-row tiles, so one prefix serves both)
-int gemm_tile_rows(bool bf16, int64_t, int) { return bf16 ? (tile_choice(kForward) == 2 ? 256 : 128) : 16; }
+// Forward products whose experts hold many rows (at least 512 on average: MFMA-bound) run the
+// ring on 256x256 tiles, 2x4 waves of 128x64, two stages: half the operand traffic per output
+// and a larger wave tile (the Qwen3 and Mixtral gate/up forwards ran 10% faster than on
+// 128x256); with fewer rows the 256-row tiles would be mostly padding.
+static bool big_tiles(int64_t rows, int G) { return G > 0 && rows >= (int64_t)512 * G; }
+int gemm_tile_rows(bool bf16, int64_t rows, int G, bool forward) {
+  if (!bf16) return 16;
+  const int t = tile_choice(forward ? kForward : kDgrad);
+  if (t == 2 || (forward && t == 1 && big_tiles(rows, G))) return 256;
+  return 128;
+}
 
 template <class T, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
 static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int rows_total, hipStream_t st) {
@@ -227,8 +237,14 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
       if (t == 5) return launch_pipe<LA, LB, MODE, Epi, 128>(a, ep, n_logical, rows_total, st);
       return launch_pipe<LA, LB, MODE, Epi, 64>(a, ep, n_logical, rows_total, st);
     }
-    if (t == 1)
+    if (t == 1) {
+      if constexpr (LB == KC && MODE != RAGGED_K) {
+        const bool big = MODE == RAGGED_M ? big_tiles(rows_total, a.G) : (a.M >= 1024 && n_logical >= 1024);
+        if (big)
+          return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+      }
       return launch_mfma<128, 256, 2, 4, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+    }
     if (t == 2)
       return launch_mfma<256, 128, 2, 2, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
     return launch_mfma<128, 128, 2, 2, 4, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);

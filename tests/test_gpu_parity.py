@@ -139,6 +139,9 @@ LAYER_CASES = [
     # persistent kernels then split over G < 8 workgroups)
     _cfg("bf16_two_experts_bwd", T=48, d=64, E=2, k=1, f=64, backward=True),
     _cfg("bf16_one_expert_bwd", T=33, d=64, E=1, k=1, f=64, f_shared=64, backward=True),
+    # experts of >= 512 rows on average and a wide dense shared expert: the
+    # forward products run on 256-row tiles (with their own tile prefix)
+    _cfg("bf16_big_experts_bwd", T=1024, d=128, E=2, k=2, f=256, f_shared=1024, backward=True),
 ]
 
 
