@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "cbe42195b442bc5fc2a4519be0034506dba87ade71ba42707b3f49d426343b55",
-                          "fetch_bytes": 1761764896, "write_bytes": 15032392000},
+    "gemm_wgrad_gateup": {"src_sha": "a5abbb391b13130cf8a0576b307e76849b9254362beb57e26e5934785ef73bb7",
+                          "fetch_bytes": 1772954400, "write_bytes": 15032393504},
 }
 
 
