@@ -3,6 +3,7 @@
 #include <stdlib.h>
 
 #include "gemm.hpp"
+#include "gemm_band.hpp"
 #include "gemm_mfma.hpp"
 #include "gemm_regs.hpp"
 #include "kernels.hpp"
@@ -125,30 +126,33 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
 }
 
 // Kernel of the bf16 path: 3 = register-staged 128x128, one tile per
-// workgroup (gemm_regs.hpp); 4 / 5 = its persistent pipelined form with
+// workgroup (gemm_regs.hpp); 6 = the stationary-band weight-gradient kernel
+// (gemm_band.hpp; weight gradients only); 4 / 5 = its persistent pipelined form with
 // K-slices of 64 (two LDS stages) / 128 (one stage); DMA-fed LDS ring (gemm_mfma.hpp)
 // with 0 = 128x128 x 4 stages, 1 = 128x256 x 3 stages (2x4 waves of 64x64: two
 // waves per SIMD), 2 = 256x128 x 3 stages.
 // Defaults per contraction class, from measurements at the 256-expert,
-// d = 7168 shape: products with a K-contiguous weight (forward) run on the
-// 128x256 DMA ring, data gradients (row-contiguous weight) on the
-// register-staged kernel, weight gradients (short ragged contractions) on the
-// persistent pipelined kernel.  MOE_TILE overrides the first two classes,
+// d = 7168 shape: forward products and data gradients run on the 128x256
+// DMA ring (data gradients read their row-contiguous weight with transposing
+// LDS reads; 10% faster than the register-staged kernel since the ring's DMA
+// is issued as assembly, see dma_b128), weight gradients (short ragged
+// contractions) on the band kernel (experts of at most 256 rows) plus the
+// persistent pipelined kernel (larger experts).  MOE_TILE overrides the first two classes,
 // MOE_TILE_WGRAD the third (MOE_TILE alone sets all three); both are for
 // tuning runs.
 enum GemmClass { kForward = 0, kDgrad = 1, kWgrad = 2 };
-static int env_choice(const char* name, int dflt) {
+static int env_choice(const char* name, int dflt, int vmax) {
   const char* e = getenv(name);
   int v = e ? atoi(e) : dflt;
-  return (v < 0 || v > 5) ? dflt : v;
+  return (v < 0 || v > vmax) ? dflt : v;
 }
 static int tile_choice(GemmClass cls) {
   static int v[3] = {-1, -1, -1};
   if (v[0] < 0) {
     const bool any = getenv("MOE_TILE") != nullptr;
-    v[0] = env_choice("MOE_TILE", 1);
-    v[1] = env_choice("MOE_TILE", 3);
-    v[2] = env_choice("MOE_TILE_WGRAD", any ? v[0] : 4);
+    v[0] = env_choice("MOE_TILE", 1, 5);
+    v[1] = env_choice("MOE_TILE", 1, 5);
+    v[2] = env_choice("MOE_TILE_WGRAD", any ? v[0] : 6, 6);
   }
   return v[cls];
 }
@@ -202,6 +206,51 @@ static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int 
   }
   kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, MxArgs{}, ep, NT, MT);
   return hipGetLastError();
+}
+
+// Stationary-band weight gradient (gemm_band.hpp) over the experts with
+// 1..KMAX rows; false when the shape does not fit it (the caller then runs the
+// general kernels on every expert).
+template <class Epi>
+static bool band_fits(const GemmArgs& a, const typename Epi::P& ep) {
+  using C = BandCfg;
+  if (!a.offsets || a.G < 1 || a.G > kMaxExperts) return false;
+  if (a.M % C::BM != 0 || a.N % C::BN != 0) return false;
+  if (a.lda != a.M || a.ldb != a.N || ep.ldc != a.N || ep.c_gstride != (int64_t)a.M * a.N) return false;
+  if (((uintptr_t)a.A & 15) || ((uintptr_t)a.B & 15) || ((uintptr_t)ep.C & 15)) return false;
+  // 32-bit buffer offsets: an expert's rows of either operand and a band's output rows
+  const int64_t lim = (int64_t)1 << 31;
+  return (int64_t)C::KMAX * a.lda * 2 < lim && (int64_t)C::KMAX * a.ldb * 2 < lim &&
+         (int64_t)C::BM * ep.ldc * 2 < lim;
+}
+
+template <class Epi>
+static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipStream_t st) {
+  using C = BandCfg;
+  // the band on the output's longer side: more, shorter units (measured at the
+  // 256-expert, d = 7168 shape: the gate/up gradient, 4096 x 7168, with the
+  // band along its columns, the down gradient, 7168 x 2048, along its rows).
+  // MOE_BAND_P = 0 / 1 forces the column / row side (tuning runs).
+  static const int force = getenv("MOE_BAND_P") ? atoi(getenv("MOE_BAND_P")) : -1;
+  const bool pband = force == 0 ? false : force == 1 ? true : a.M > a.N;
+  auto kern = pband ? gemm_band_kernel<Epi, false> : gemm_band_kernel<Epi, true>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    for (auto k : {gemm_band_kernel<Epi, false>, gemm_band_kernel<Epi, true>}) {
+      hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         C::LDS_BYTES);
+      if (e != hipSuccess) return e;
+    }
+    attr_set = true;
+  }
+  const int UB = pband ? a.M / C::BM : a.N / C::BN, TU = pband ? a.N / C::BN : a.M / C::BM;
+  kern<<<(unsigned)device_cus(), C::NTHR, C::LDS_BYTES, st>>>(a, ep, UB, TU);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // experts with more rows: the persistent kernel, skipping the others whole
+  GemmArgs big = a;
+  big.k_skip = C::KMAX;
+  return launch_pipe<MC, MC, RAGGED_K, Epi, 64>(big, ep, a.N, 0, st);
 }
 
 // Tile rows of the ragged-row schedule.  The device tile prefix is built with
@@ -364,6 +413,9 @@ hipError_t gemm_gateup_dgrad(const void* dhu, const int* offsets, const int* til
 template <class T, int kSite>
 static hipError_t wgrad_site(const GemmArgs& a, void* dw, int M, int N, hipStream_t st) {
   typename EpiStore<T, kSite>::P ep{(T*)dw, N, (int64_t)M * N, M, N};
+  if constexpr (sizeof(T) == 2)
+    if (tile_choice(kWgrad) == 6 && band_fits<EpiStore<T, kSite>>(a, ep))
+      return launch_band<EpiStore<T, kSite>>(a, ep, st);
   return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T, kSite>>(a, ep, 0, st);
 }
 

@@ -58,6 +58,7 @@ struct GemmArgs {
   const int* offsets;      // [G+1] ragged offsets (RAGGED_*); NULL + G=1 means [0,K)
   const int* tile_prefix;  // RAGGED_M: [G+1] cumulative m-tiles per group
   int G;
+  int k_skip;              // RAGGED_K: groups with at most this many rows are left to another kernel
 };
 
 // Persistent schedule over XCDs.  Workgroups are dispatched round-robin over

@@ -92,6 +92,36 @@ struct TileCfg {
 // logical chunk -> position helpers
 __device__ __forceinline__ int kc_swz(int r) { return (r >> 1) & 7; }
 
+// One DMA instruction per lane group: 16 bytes per lane from a raw buffer
+// (base, bytes: reads past the range give zeros) into LDS at `lds` + 16 x lane.
+// Written as assembly: the compiler does not track assembly DMA, so it inserts
+// no wait of its own before later LDS reads (for the transposing LDS reads it
+// would otherwise drain every DMA and store in flight); the kernel's explicit
+// vmcnt waits order the reads after the data.  The instruction has no output
+// register.
+__device__ __forceinline__ void dma_b128(const void* base, uint32_t bytes, uint32_t voff, uint32_t soff,
+                                         uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // every operand but the lane offset is uniform: pin them to scalar registers
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu)),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), (uint32_t)kRawBufferFlags};
+  const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
+  const uint32_t ld = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  uint32_t saved;
+  // M0 (the LDS destination base) is restored before the statement ends
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(ld), "v"(voff), "s"(rs), "s"(so)
+      : "memory");
+#endif
+}
+
 // Per-lane byte offsets of one operand slice's DMA (relative to the operand's
 // resource base); KC: element (i, k) at i*ld + k (i relative to the base row);
 // MC: element (i, k) at k*ld + i (k relative to the base K-row).
@@ -112,8 +142,10 @@ struct DmaPlan {
     }
   }
   // MC: columns i0 + 8c (relative to the base); every K-row 0..63 of the slice
-  __device__ __forceinline__ void plan_mc(int64_t ld, int i0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (`wave`: this wave's index among the NW waves that share the slice)
+  __device__ __forceinline__ void plan_mc(int64_t ld, int i0, int wave = -1) {
+    const int lane = threadIdx.x & 63;
+    if (wave < 0) wave = threadIdx.x >> 6;
     constexpr int CPR = ROWS / 8;
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
@@ -125,18 +157,11 @@ struct DmaPlan {
     }
   }
   // one slice: instruction j fills chunk positions (wave + j*NW)*64 .. +63
-  // (device pass only: in the host pass this builtin inside a helper makes the
-  // compiler drop the launch stubs of later kernel instantiations)
   __device__ __forceinline__ void issue(const void* rbase, uint32_t rbytes, uint32_t soff, uint32_t lds_byte) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const int wave = threadIdx.x >> 6;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(rbase, rbytes);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) {
-      const uint32_t dst = lds_byte + (uint32_t)((wave + j * NW) * 64 * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MOE_LDS void*)(uintptr_t)dst, 16, off[j], soff, 0, 0);
-    }
-#endif
+    for (int j = 0; j < NDMA; ++j)
+      dma_b128(rbase, rbytes, off[j], soff, lds_byte + (uint32_t)((wave + j * NW) * 64 * 16));
   }
 };
 

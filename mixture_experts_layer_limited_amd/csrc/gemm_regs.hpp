@@ -361,6 +361,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       resolve_tile<MODE, BM>(a, s_off, s_pre, L, NT, MT, it.c);
       it.nk = (it.c.k_end - it.c.k_begin + BK - 1) / BK;
       if (it.c.m0 >= it.c.m_end) it.nk = 0;
+      if (MODE == RAGGED_K && it.c.k_end - it.c.k_begin <= a.k_skip) {
+        // the whole group is skipped (empty, or left to another kernel): go
+        // to this workgroup's first step in the next group
+        const int next = (it.c.g + 1) * MT * NT - run_lo - wi;   // > r * nx
+        r = (next + nx - 1) / nx - 1;
+        continue;
+      }
       if (it.nk > 0) {
         it.r = r;
         it.ks = 0;
