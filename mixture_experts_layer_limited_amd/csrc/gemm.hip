@@ -247,10 +247,10 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
   kern<<<(unsigned)device_cus(), C::NTHR, C::LDS_BYTES, st>>>(a, ep, UB, TU);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // experts with more rows: the persistent kernel, skipping the others whole
+  // experts with more rows: the DMA ring, persistent, skipping the others whole
   GemmArgs big = a;
   big.k_skip = C::KMAX;
-  return launch_pipe<MC, MC, RAGGED_K, Epi, 64>(big, ep, a.N, 0, st);
+  return launch_mfma<128, 256, 2, 4, 3, MC, MC, RAGGED_K, Epi>(big, ep, a.N, 0, st, true);
 }
 
 // Tile rows of the ragged-row schedule.  The device tile prefix is built with
@@ -265,7 +265,7 @@ static bool big_tiles(int64_t rows, int G) { return G > 0 && rows >= (int64_t)51
 int gemm_tile_rows(bool bf16, int64_t rows, int G, bool forward) {
   if (!bf16) return 16;
   const int t = tile_choice(forward ? kForward : kDgrad);
-  if (t == 2 || (forward && t == 1 && big_tiles(rows, G))) return 256;
+  if (t == 2 || (t == 1 && big_tiles(rows, G))) return 256;
   return 128;
 }
 
@@ -277,7 +277,8 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
     // weight gradients (short contractions) run persistent so that a tile's
     // stores overlap the next tile's loads; the rest one tile per workgroup
     const bool persistent = MODE == RAGGED_K;
-    const int t = tile_choice(MODE == RAGGED_K ? kWgrad : LB == KC ? kForward : kDgrad);
+    int t = tile_choice(MODE == RAGGED_K ? kWgrad : LB == KC ? kForward : kDgrad);
+    if (t == 6) t = 1;          // weight gradients the band kernel does not take: the DMA ring
     bool aligned = true;        // staged epilogues store 16-byte row pieces
     if constexpr (Epi::kStaged)
       aligned = ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0;
@@ -287,7 +288,7 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
       return launch_pipe<LA, LB, MODE, Epi, 64>(a, ep, n_logical, rows_total, st);
     }
     if (t == 1) {
-      if constexpr (LB == KC && MODE != RAGGED_K) {
+      if constexpr (MODE != RAGGED_K) {
         const bool big = MODE == RAGGED_M ? big_tiles(rows_total, a.G) : (a.M >= 1024 && n_logical >= 1024);
         if (big)
           return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);

@@ -77,6 +77,28 @@ __device__ __forceinline__ int xcd_run_start(const GemmArgs& a, const int* off, 
   if (x >= X) return total;
   if (MODE != RAGGED_K || !a.offsets) return (int)((int64_t)total * x / X);
   const int G = a.G;
+  if (a.k_skip > 0) {
+    // groups of at most k_skip rows cost nothing here: walk the groups once
+    // (G <= 256) with their filtered costs
+    auto cost = [&](int e) -> int64_t {
+      const int n = off[e + 1] - off[e];
+      return n > a.k_skip ? (int64_t)P * (kSplitAlpha + n) : 0;
+    };
+    int64_t W = 0;
+    for (int e = 0; e < G; ++e) W += cost(e);
+    const int64_t T = W * x / X;
+    int64_t before = 0;
+    for (int e = 0; e < G; ++e) {
+      const int64_t c = cost(e);
+      if (before + c > T) {
+        const int64_t ce = c / P;                        // one tile of group e
+        const int64_t in = (T - before + ce - 1) / ce;
+        return e * P + (int)(in < P ? in : P);
+      }
+      before += c;
+    }
+    return total;
+  }
   auto cum = [&](int e) -> int64_t { return (int64_t)e * kSplitAlpha + (off[e] - off[0]); };
   const int64_t T = (int64_t)P * cum(G) * x / X;             // work before the run, in tile units
   int lo = 0, hi = G;                                        // last e < G with P cum(e) <= T

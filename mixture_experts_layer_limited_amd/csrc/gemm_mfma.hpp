@@ -273,6 +273,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
       // a tile starting past its group's rows has nothing to do (only a tile
       // prefix built for another tile height could produce one)
       if (it.c.m0 >= it.c.m_end) it.nk = 0;
+      if (MODE == RAGGED_K && it.c.k_end - it.c.k_begin <= a.k_skip) {
+        // the whole group is skipped (empty, or left to another kernel): go
+        // to this workgroup's first step in the next group
+        const int next = (it.c.g + 1) * MT * NT - run_lo - wi;   // > r * nx
+        r = (next + nx - 1) / nx - 1;
+        continue;
+      }
       if (it.nk > 0) {
         it.r = r;
         it.ks = 0;
