@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # (FETCH_SIZE reads 512 MiB for it: x2; WRITE_SIZE reads 1 GiB: x1).  A figure
 # only holds for the kernel sources it was taken with: `src_sha` is the sha256
 # of the GEMM sources at that time, and a mismatch reports traffic as null.
-GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm.hip")
+GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm_band.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
     "gemm_wgrad_gateup": {"src_sha": "a5abbb391b13130cf8a0576b307e76849b9254362beb57e26e5934785ef73bb7",

@@ -136,7 +136,7 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
 // DMA ring (data gradients read their row-contiguous weight with transposing
 // LDS reads; 10% faster than the register-staged kernel since the ring's DMA
 // is issued as assembly, see dma_b128), weight gradients (short ragged
-// contractions) on the band kernel (experts of at most 256 rows) plus the
+// contractions) on the band kernel (experts of at most 320 rows) plus the
 // persistent pipelined kernel (larger experts).  MOE_TILE overrides the first two classes,
 // MOE_TILE_WGRAD the third (MOE_TILE alone sets all three); both are for
 // tuning runs.
@@ -244,7 +244,11 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
     attr_set = true;
   }
   const int UB = pband ? a.M / C::BM : a.N / C::BN, TU = pband ? a.N / C::BN : a.M / C::BM;
-  kern<<<(unsigned)device_cus(), C::NTHR, C::LDS_BYTES, st>>>(a, ep, UB, TU);
+  // each unit walks its tiles starting at its band index (mod the tile count),
+  // so neighbouring units read different streamed tiles at any time (3% faster
+  // than all starting at tile 0); MOE_BAND_ROT changes the step (tuning runs)
+  static const int rot = getenv("MOE_BAND_ROT") ? atoi(getenv("MOE_BAND_ROT")) : 1;
+  kern<<<(unsigned)device_cus(), C::NTHR, C::LDS_BYTES, st>>>(a, ep, UB, TU, rot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // experts with more rows: the DMA ring, persistent, skipping the others whole

@@ -8,7 +8,7 @@
 // from L2 competes with them.
 //
 // Work unit: (expert g, band of 128 columns of P).  The band, n_g x 128 values
-// (n_g <= 256), goes into LDS by DMA once per unit; each wave then holds its 64
+// (n_g <= 320), goes into LDS by DMA once per unit; each wave then holds its 64
 // band columns for the whole contraction as MFMA fragments in registers (128
 // VGPRs) while the unit walks the N / 128 column tiles of Q_g.  Only Q's tiles
 // stream, in 64-row slices through a 4-stage DMA ring, so a 128 x 128 output
@@ -27,7 +27,7 @@
 // XCD owns one contiguous run of the expert-major unit list, split by estimated
 // cost, and its workgroups stride through it, so the workgroups of an XCD hold
 // neighbouring bands of one expert and stream the same tiles of Q_g through
-// its L2 at about the same time.  Experts with no rows or more than 256 rows
+// its L2 at about the same time.  Experts with no rows or more than 320 rows
 // are not units of this kernel (the caller zero-fills the first and runs the
 // general persistent kernel on the second).
 //
@@ -51,7 +51,7 @@ __device__ __forceinline__ void issue_slice_asm(const Plan& p, const void* base,
 }
 
 struct BandCfg {
-  static constexpr int BM = 128, BN = 128, BK = 64, KMAX = 256, KS = KMAX / BK;
+  static constexpr int BM = 128, BN = 128, BK = 64, KMAX = 320, KS = KMAX / BK;
   static constexpr int WM = 2, WN = 2, FM = 2, FN = 2;
   static constexpr int NCW = 4, NLW = 2;                 // compute and load waves
   static constexpr int NW = NCW + NLW, NTHR = 64 * NW;
@@ -60,7 +60,7 @@ struct BandCfg {
   static constexpr int A_OFF = 0;                         // KS slices of the band
   static constexpr int RING_OFF = KS * SLICE;
   static constexpr int STG_OFF = RING_OFF + STAGES * SLICE;
-  static constexpr int STG_WAVE = 64 * 64 * 2;            // one compute wave's 64 x 64 sub-tile
+  static constexpr int STG_WAVE = 32 * 64 * 2;            // half of a compute wave's 64 x 64 sub-tile
   static constexpr int LDS_BYTES = STG_OFF + NCW * STG_WAVE;
   static constexpr int DMA = SLICE / 16 / (64 * NLW);     // DMA instructions per load wave per slice
   static constexpr int UNIT_EPI_COST = 4;                 // a tile's stores, in slices, for run splitting
@@ -87,7 +87,8 @@ struct BandCfg {
 //                [compute: MFMAs of slice n]
 //   tile end:    [compute: sub-tile -> own staging area -> global stores]
 template <class Epi, bool QBAND>
-__global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, typename Epi::P ep, int UB, int TU) {
+__global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, typename Epi::P ep, int UB, int TU,
+                                                                 int rot) {
   using C = BandCfg;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, KMAX = C::KMAX, KS = C::KS, STAGES = C::STAGES;
   static_assert(Epi::kStaged, "bf16 output");
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
   const void* rb_base = nullptr;
   uint32_t rb_bytes = 0, sob = 0;
   auto plan_b = [&]() {
-    pb.plan_mc(ld_str, ld.j * 128, lw);
+    pb.plan_mc(ld_str, ((ld.j + rot * ld.u.band) % TU) * 128, lw);
     rb_base = So + (int64_t)ld.u.kb * ld_str;
     rb_bytes = (uint32_t)(ld.u.n * ld_str * 2);
     sob = 0;
@@ -320,31 +321,33 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
           ++n;
         }
       }
-      // tile end: the sub-tile through this wave's staging area (LDS
-      // operations of one wave execute in order) to 128-byte row pieces
+      // tile end: the sub-tile through this wave's staging area, 32 rows at a
+      // time (LDS operations of one wave execute in order), to 128-byte row pieces
       if (is_compute) {
+        const int jt = (j + rot * cu.band) % TU;   // the unit's tiles in rotated order
+        const int row0 = (QBAND ? jt : cu.band) * BM, col0 = (QBAND ? cu.band : jt) * BN;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(ep.C + cu.g * ep.c_gstride + (int64_t)row0 * ep.ldc, (uint32_t)(BM * ep.ldc * 2));
+        const uint32_t col_off = (uint32_t)(col0 + wn * (BN / C::WN) + (lane & 7) * 8) * 2;
         MOE_LDS u32x2* w2 = (MOE_LDS u32x2*)(uintptr_t)(stg + wave * C::STG_WAVE);
+        const MOE_LDS u32x4* r4 = (const MOE_LDS u32x4*)(uintptr_t)(stg + wave * C::STG_WAVE);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+        for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
           for (int jj = 0; jj < C::FN; ++jj)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int row = i * 32 + (lane & 31), chunk = jj * 4 + q;
+              const int row = lane & 31, chunk = jj * 4 + q;
               const u32x2 v = {pack_bf16x2(acc[i][jj][4 * q], acc[i][jj][4 * q + 1]),
                                pack_bf16x2(acc[i][jj][4 * q + 2], acc[i][jj][4 * q + 3])};
               w2[(row * 8 + (chunk ^ stage_swz(row))) * 2 + (lane >> 5)] = v;
             }
-        const MOE_LDS u32x4* r4 = (const MOE_LDS u32x4*)(uintptr_t)(stg + wave * C::STG_WAVE);
-        const int row0 = (QBAND ? j : cu.band) * BM, col0 = (QBAND ? cu.band : j) * BN;
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(ep.C + cu.g * ep.c_gstride + (int64_t)row0 * ep.ldc, (uint32_t)(BM * ep.ldc * 2));
-        const uint32_t col_off = (uint32_t)(col0 + wn * (BN / C::WN) + (lane & 7) * 8) * 2;
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int rr = it * 8 + (lane >> 3), cc = lane & 7;
-          const u32x4 v = r4[rr * 8 + (cc ^ stage_swz(rr))];
-          store_b128<true>(v, rs, col_off + (uint32_t)((wm * (BM / C::WM) + rr) * ep.ldc * 2));
+          for (int it = 0; it < 4; ++it) {
+            const int rr = it * 8 + (lane >> 3), cc = lane & 7;
+            const u32x4 v = r4[rr * 8 + (cc ^ stage_swz(rr))];
+            store_b128<true>(v, rs, col_off + (uint32_t)((wm * (BM / C::WM) + i * 32 + rr) * ep.ldc * 2));
+          }
         }
       }
     }
