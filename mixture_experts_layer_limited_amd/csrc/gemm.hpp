@@ -73,32 +73,57 @@ constexpr int kSplitAlpha = 64;
 
 template <GemmMode MODE>
 __device__ __forceinline__ int xcd_run_start(const GemmArgs& a, const int* off, int total, int P, int x, int X) {
-  if (x <= 0) return 0;
   if (x >= X) return total;
-  if (MODE != RAGGED_K || !a.offsets) return (int)((int64_t)total * x / X);
   const int G = a.G;
-  if (a.k_skip > 0) {
-    // groups of at most k_skip rows cost nothing here: walk the groups once
-    // (G <= 256) with their filtered costs
-    auto cost = [&](int e) -> int64_t {
-      const int n = off[e + 1] - off[e];
-      return n > a.k_skip ? (int64_t)P * (kSplitAlpha + n) : 0;
-    };
-    int64_t W = 0;
-    for (int e = 0; e < G; ++e) W += cost(e);
-    const int64_t T = W * x / X;
-    int64_t before = 0;
-    for (int e = 0; e < G; ++e) {
-      const int64_t c = cost(e);
-      if (before + c > T) {
-        const int64_t ce = c / P;                        // one tile of group e
-        const int64_t in = (T - before + ce - 1) / ce;
-        return e * P + (int)(in < P ? in : P);
-      }
-      before += c;
+  if (MODE == RAGGED_K && a.offsets && a.k_skip > 0) {
+    // groups of at most k_skip rows cost nothing here.  Wave-parallel over
+    // the groups (G <= 256): lane l owns groups 4l .. 4l+3, the lane sums are
+    // scanned across the wave, and the run starts in the first group whose
+    // cumulative cost passes W x / X (every wave computes the same value).
+    // The first run starts at the first group that is not skipped, and with
+    // no such group every run is empty.
+    const int lane = threadIdx.x & 63;
+    int64_t c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      const int n = e < G ? off[e + 1] - off[e] : 0;
+      c[i] = n > a.k_skip ? (int64_t)P * (kSplitAlpha + n) : 0;
+      sum += c[i];
     }
-    return total;
+    auto shfl64 = [](int64_t v, int src) -> int64_t {
+      const int lo = __shfl((int)(uint32_t)v, src, 64), hi = __shfl((int)(v >> 32), src, 64);
+      return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+    };
+    int64_t incl = sum;                                   // inclusive scan over lanes
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t v = shfl64(incl, lane >= o ? lane - o : lane);
+      if (lane >= o) incl += v;
+    }
+    const int64_t W = shfl64(incl, 63);
+    const int64_t T = W * x / X;
+    int64_t before = incl - sum;
+    int found = -1;
+    int64_t found_before = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (found < 0 && before + c[i] > T) {
+        found = 4 * lane + i;
+        found_before = before;
+      }
+      before += c[i];
+    }
+    const uint64_t m = __ballot(found >= 0);
+    if (m == 0) return total;
+    const int src = __ffsll((unsigned long long)m) - 1;
+    const int e = __shfl(found, src, 64);
+    const int64_t b = shfl64(found_before, src);
+    const int64_t ce = kSplitAlpha + (off[e + 1] - off[e]);   // one tile of group e
+    const int64_t in = (T - b + ce - 1) / ce;
+    return e * P + (int)(in < P ? in : P);
   }
+  if (x <= 0) return 0;
+  if (MODE != RAGGED_K || !a.offsets) return (int)((int64_t)total * x / X);
   auto cum = [&](int e) -> int64_t { return (int64_t)e * kSplitAlpha + (off[e] - off[0]); };
   const int64_t T = (int64_t)P * cum(G) * x / X;             // work before the run, in tile units
   int lo = 0, hi = G;                                        // last e < G with P cum(e) <= T
