@@ -454,6 +454,12 @@ hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T
   a.A = dl; a.lda = Ep; a.B = x; a.ldb = d;
   a.M = E; a.N = d; a.K = T_; a.a_mext = Ep; a.b_next = d; a.b_kend = T_; a.G = 1;
   typename EpiStore<T, 4>::P ep{(T*)dw_r, d, 0, E, d};
+  // E output rows: the persistent 128x128 kernel (the ring's 128x256 tiles are
+  // few and mostly padding: 4 experts, 32768 tokens, d = 7168 took 0.29 ms on
+  // the ring, 0.16 here; 256 experts, 4096 tokens 0.081 and 0.070)
+  if constexpr (sizeof(T) == 2)
+    if (tile_choice(kWgrad) == 6 && d % 8 == 0 && ((uintptr_t)dw_r & 15) == 0)
+      return launch_pipe<MC, MC, RAGGED_K, EpiStore<T, 4>, 64>(a, ep, d, 0, st);
   return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T, 4>>(a, ep, 0, st);
 }
 
