@@ -266,10 +266,17 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
 // and a larger wave tile (the Qwen3 and Mixtral gate/up forwards ran 10% faster than on
 // 128x256); with fewer rows the 256-row tiles would be mostly padding.
 static bool big_tiles(int64_t rows, int G) { return G > 0 && rows >= (int64_t)512 * G; }
+// The data gradients take the 256x256 tiles under the same rule (gate/up dgrad
+// on one box: Qwen3 2.06 -> 1.86 ms, Mixtral 2.54 -> 2.41, the EP share 2.23 ->
+// 1.87).  MOE_BIG_DGRAD=0 keeps them on 128-row tiles (tuning runs).
+static bool big_dgrad() {
+  static const bool v = !(getenv("MOE_BIG_DGRAD") && atoi(getenv("MOE_BIG_DGRAD")) == 0);
+  return v;
+}
 int gemm_tile_rows(bool bf16, int64_t rows, int G, bool forward) {
   if (!bf16) return 16;
   const int t = tile_choice(forward ? kForward : kDgrad);
-  if (t == 2 || (t == 1 && big_tiles(rows, G))) return 256;
+  if (t == 2 || (t == 1 && big_tiles(rows, G) && (forward || big_dgrad()))) return 256;
   return 128;
 }
 
@@ -293,7 +300,8 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
     }
     if (t == 1) {
       if constexpr (MODE != RAGGED_K) {
-        const bool big = MODE == RAGGED_M ? big_tiles(rows_total, a.G) : (a.M >= 1024 && n_logical >= 1024);
+        const bool big = (LB == KC || big_dgrad()) &&
+                         (MODE == RAGGED_M ? big_tiles(rows_total, a.G) : (a.M >= 1024 && n_logical >= 1024));
         if (big)
           return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
       }
