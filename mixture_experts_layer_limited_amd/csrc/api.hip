@@ -530,7 +530,7 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const int32_t* topk_id
   LAUNCH_NAMED("perm_hist", launch_perm_hist(topk_idx, T_, k, E, hist, st));
   LAUNCH_NAMED("perm_scan", launch_perm_scan(hist, (int)ranges(T_), E, rows, expert_offsets, st));
   LAUNCH_NAMED("perm_rank", launch_perm_rank(topk_idx, T_, k, E, hist, row_id_map, src_token, st));
-  LAUNCH_NAMED("gather_rows", launch_gather_rows(x, src_token, rows, (int)(cfg->d * elt(cfg)), x_perm, st));
+  LAUNCH_NAMED("scatter_rows", launch_scatter_rows(x, row_id_map, T_, k, (int)(cfg->d * elt(cfg)), x_perm, st));
   return ok();
 }
 

@@ -37,8 +37,8 @@ hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int E, int* hist, 
 hipError_t launch_perm_scan(int* hist, int R, int E, int rows, int32_t* offsets, hipStream_t st);
 hipError_t launch_perm_rank(const int32_t* idx, int T, int k, int E, int* base, int32_t* row_id_map,
                             int32_t* src_token, hipStream_t st);
-hipError_t launch_gather_rows(const void* x, const int32_t* src_token, int rows, int row_bytes,
-                              void* out, hipStream_t st);
+hipError_t launch_scatter_rows(const void* x, const int32_t* row_id_map, int T_, int k, int row_bytes,
+                               void* out, hipStream_t st);
 template <class T>
 hipError_t launch_combine(const T* y_perm, const int32_t* rmap, const float* gates, const T* y_shared,
                           T* y, int T_, int k, int d, hipStream_t st);

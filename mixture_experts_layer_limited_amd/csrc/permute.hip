@@ -1,7 +1,7 @@
 // Dispatch and combine on one GPU ("System Modules: Dispatcher" and
 // "Combiner"; memory-efficient permutation, Figure 7): a stable counting sort
-// of (token, choice) pairs by expert, the row gather into expert-contiguous
-// order, and the gate-weighted unpermute-combine with its backward.
+// of (token, choice) pairs by expert, the row scatter into expert-contiguous
+// order (each token row read once, written to its k places), and the gate-weighted unpermute-combine with its backward.
 //
 // Counting sort: tokens are cut into ranges of 64.  perm_hist counts each
 // range's assignments per expert, perm_scan turns the [range, expert] table
@@ -109,24 +109,39 @@ hipError_t launch_perm_rank(const int32_t* idx, int T, int k, int E, int* base, 
   return hipGetLastError();
 }
 
-// out[row] = x[src_token[row]], 16-byte vectors; one row per 64-thread group
-__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ x,
-                                                          const int32_t* __restrict__ src, int rows,
-                                                          int vec_per_row, u32x4* __restrict__ out) {
+// Permute as a scatter: x_perm[row_id_map[t, j]] = x[t] for j < k.  One wave
+// per token reads the token's row once (16 bytes per lane) and writes its k
+// copies, so the row is fetched once instead of once per copy; every
+// destination row is written exactly once (row_id_map is a bijection).
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4* __restrict__ x,
+                                                           const int32_t* __restrict__ rmap, int T_, int k,
+                                                           int vec_per_row, u32x4* __restrict__ out) {
   const int sub = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + sub;
-  if (row >= rows) return;
-  const int64_t s = src[row];
-  const u32x4* in = x + s * vec_per_row;
-  u32x4* o = out + (int64_t)row * vec_per_row;
-  for (int c = lane; c < vec_per_row; c += 64) o[c] = in[c];
+  const int t = blockIdx.x * 4 + sub;
+  if (t >= T_) return;
+  const u32x4* in = x + (int64_t)t * vec_per_row;
+  const int32_t* rm = rmap + (int64_t)t * k;
+  // four 16-byte loads per lane in flight before their stores
+  constexpr int U = 4;
+  for (int c0 = lane; c0 < vec_per_row; c0 += 64 * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c0 + 64 * u < vec_per_row) v[u] = in[c0 + 64 * u];
+    for (int j = 0; j < k; ++j) {
+      u32x4* o = out + (int64_t)rm[j] * vec_per_row;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (c0 + 64 * u < vec_per_row) o[c0 + 64 * u] = v[u];
+    }
+  }
 }
 
-hipError_t launch_gather_rows(const void* x, const int32_t* src_token, int rows, int row_bytes,
-                              void* out, hipStream_t st) {
-  if (rows == 0) return hipSuccess;
-  gather_rows_kernel<<<(rows + 3) / 4, 256, 0, st>>>((const u32x4*)x, src_token, rows, row_bytes / 16,
-                                                      (u32x4*)out);
+hipError_t launch_scatter_rows(const void* x, const int32_t* row_id_map, int T_, int k, int row_bytes,
+                               void* out, hipStream_t st) {
+  if (T_ == 0) return hipSuccess;
+  scatter_rows_kernel<<<(T_ + 3) / 4, 256, 0, st>>>((const u32x4*)x, row_id_map, T_, k, row_bytes / 16,
+                                                     (u32x4*)out);
   return hipGetLastError();
 }
 
@@ -174,24 +189,40 @@ __device__ void Vec8<float>::store(float* p) const {
   *(floatx4*)(p + 4) = b;
 }
 
-template <class T>
+// KC > 0: k = KC known at compile time, so the k row loads of a chunk are all
+// issued before the sum (0: any k, one row at a time).  The fp32 sum keeps the
+// j order either way.
+template <class T, int KC>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_perm,
                                                       const int32_t* __restrict__ rmap,
                                                       const float* __restrict__ gates,
                                                       const T* __restrict__ y_shared, T* __restrict__ y,
-                                                      int k, int d) {
+                                                      int k_rt, int d) {
   const int t = blockIdx.x;
+  const int k = KC > 0 ? KC : k_rt;
   for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
     Vec8<T> acc;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc.v[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int64_t row = rmap[(int64_t)t * k + j];
-      const float g = gates[(int64_t)t * k + j];
-      Vec8<T> r;
-      r.load(y_perm + row * d + c);
+    if constexpr (KC > 0) {
+      Vec8<T> r[KC];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc.v[i] += g * r.v[i];
+      for (int j = 0; j < KC; ++j) r[j].load(y_perm + (int64_t)rmap[(int64_t)t * KC + j] * d + c);
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const float g = gates[(int64_t)t * KC + j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc.v[i] += g * r[j].v[i];
+      }
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int64_t row = rmap[(int64_t)t * k + j];
+        const float g = gates[(int64_t)t * k + j];
+        Vec8<T> r;
+        r.load(y_perm + row * d + c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc.v[i] += g * r.v[i];
+      }
     }
     if (y_shared) {
       Vec8<T> s;
@@ -203,63 +234,125 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_pe
   }
 }
 
+// launch `kern<KC>` for the common k (1, 2, 4, 8), else the runtime-k form
+#define MOE_DISPATCH_K(k, LAUNCH) \
+  do {                               \
+    switch (k) {                     \
+      case 1: LAUNCH(1); break;      \
+      case 2: LAUNCH(2); break;      \
+      case 4: LAUNCH(4); break;      \
+      case 8: LAUNCH(8); break;      \
+      default: LAUNCH(0); break;     \
+    }                                \
+  } while (0)
+
 template <class T>
 hipError_t launch_combine(const T* y_perm, const int32_t* rmap, const float* gates, const T* y_shared,
                           T* y, int T_, int k, int d, hipStream_t st) {
   if (T_ == 0) return hipSuccess;
-  combine_kernel<T><<<T_, 256, 0, st>>>(y_perm, rmap, gates, y_shared, y, k, d);
+#define MOE_L(KC) combine_kernel<T, KC><<<T_, 256, 0, st>>>(y_perm, rmap, gates, y_shared, y, k, d)
+  MOE_DISPATCH_K(k, MOE_L);
+#undef MOE_L
   return hipGetLastError();
 }
 
 // dy_perm[row(t,j)] = storage(g dy[t]); d_gates[t,j] = <dy[t], y_perm[row(t,j)]>
-template <class T>
+// KC > 0 (k known at compile time): each chunk of dy is read once for all k
+// rows, the k row loads are issued together, and the k dot products are
+// reduced in one pass at the end.  Every thread accumulates its dot products
+// over its chunks in the same order as the runtime-k form (one j at a time),
+// and the wave sums and the sum of the four wave partials are the same, so
+// both forms give the same bits.
+template <class T, int KC>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy,
                                                           const T* __restrict__ y_perm,
                                                           const int32_t* __restrict__ rmap,
                                                           const float* __restrict__ gates,
                                                           T* __restrict__ dy_perm,
-                                                          float* __restrict__ d_gates, int k, int d) {
-  __shared__ float part[4];
+                                                          float* __restrict__ d_gates, int k_rt, int d) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int j = 0; j < k; ++j) {
-    const int64_t row = rmap[(int64_t)t * k + j];
-    const float g = gates[(int64_t)t * k + j];
-    float dot = 0.0f;
-    for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
-      Vec8<T> a, r, o;
-      a.load(dy + (int64_t)t * d + c);
-      r.load(y_perm + row * d + c);
+  if constexpr (KC > 0) {
+    __shared__ float part[4][KC];
+    int64_t row[KC];
+    float g[KC], dot[KC];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        dot += a.v[i] * r.v[i];
-        o.v[i] = g * a.v[i];
-      }
-      o.store(dy_perm + row * d + c);
+    for (int j = 0; j < KC; ++j) {
+      row[j] = rmap[(int64_t)t * KC + j];
+      g[j] = gates[(int64_t)t * KC + j];
+      dot[j] = 0.0f;
     }
-    dot = wave_sum(dot);
-    if (lane == 0) part[wave] = dot;
+    for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+      Vec8<T> a, r[KC];
+      a.load(dy + (int64_t)t * d + c);
+#pragma unroll
+      for (int j = 0; j < KC; ++j) r[j].load(y_perm + row[j] * d + c);
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        Vec8<T> o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dot[j] += a.v[i] * r[j].v[i];
+          o.v[i] = g[j] * a.v[i];
+        }
+        o.store(dy_perm + row[j] * d + c);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const float w = wave_sum(dot[j]);
+      if (lane == 0) part[wave][j] = w;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) d_gates[(int64_t)t * k + j] = ((part[0] + part[1]) + part[2]) + part[3];
-    __syncthreads();
+    if (threadIdx.x < KC) {
+      const int j = threadIdx.x;
+      d_gates[(int64_t)t * KC + j] = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
+    }
+  } else {
+    __shared__ float part[4];
+    const int k = k_rt;
+    for (int j = 0; j < k; ++j) {
+      const int64_t row = rmap[(int64_t)t * k + j];
+      const float g = gates[(int64_t)t * k + j];
+      float dot = 0.0f;
+      for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+        Vec8<T> a, r, o;
+        a.load(dy + (int64_t)t * d + c);
+        r.load(y_perm + row * d + c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dot += a.v[i] * r.v[i];
+          o.v[i] = g * a.v[i];
+        }
+        o.store(dy_perm + row * d + c);
+      }
+      dot = wave_sum(dot);
+      if (lane == 0) part[wave] = dot;
+      __syncthreads();
+      if (threadIdx.x == 0) d_gates[(int64_t)t * k + j] = ((part[0] + part[1]) + part[2]) + part[3];
+      __syncthreads();
+    }
   }
 }
 
 template <class T>
-hipError_t launch_combine_bwd(const T* dy, const T* y_perm, const int32_t* rmap, const float* gates,
-                              T* dy_perm, float* d_gates, int T_, int k, int d, hipStream_t st) {
+hipError_t launch_combine_bwd(const T* dy, const T* y_perm, const int32_t* rmap, const float* gates, T* dy_perm,
+                              float* d_gates, int T_, int k, int d, hipStream_t st) {
   if (T_ == 0) return hipSuccess;
-  combine_bwd_kernel<T><<<T_, 256, 0, st>>>(dy, y_perm, rmap, gates, dy_perm, d_gates, k, d);
+#define MOE_L(KC) combine_bwd_kernel<T, KC><<<T_, 256, 0, st>>>(dy, y_perm, rmap, gates, dy_perm, d_gates, k, d)
+  MOE_DISPATCH_K(k, MOE_L);
+#undef MOE_L
   return hipGetLastError();
 }
 
-// dx[t] = storage(partial[t] + sum_j dx_perm[row(t,j)])
-template <class T>
+// dx[t] = storage(partial[t] + sum_j dx_perm[row(t,j)]), j in order; KC as in combine
+template <class T, int KC>
 __global__ __launch_bounds__(256) void unpermute_sum_kernel(const T* __restrict__ dx_perm,
                                                             const int32_t* __restrict__ rmap,
                                                             const float* __restrict__ partial,
-                                                            T* __restrict__ dx, int k, int d) {
+                                                            T* __restrict__ dx, int k_rt, int d) {
   const int t = blockIdx.x;
+  const int k = KC > 0 ? KC : k_rt;
   for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
     Vec8<T> acc;
     if (partial) {
@@ -271,12 +364,22 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(const T* __restrict_
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc.v[i] = 0.0f;
     }
-    for (int j = 0; j < k; ++j) {
-      const int64_t row = rmap[(int64_t)t * k + j];
-      Vec8<T> r;
-      r.load(dx_perm + row * d + c);
+    if constexpr (KC > 0) {
+      Vec8<T> r[KC];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc.v[i] += r.v[i];
+      for (int j = 0; j < KC; ++j) r[j].load(dx_perm + (int64_t)rmap[(int64_t)t * KC + j] * d + c);
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc.v[i] += r[j].v[i];
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int64_t row = rmap[(int64_t)t * k + j];
+        Vec8<T> r;
+        r.load(dx_perm + row * d + c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc.v[i] += r.v[i];
+      }
     }
     acc.store(dx + (int64_t)t * d + c);
   }
@@ -286,7 +389,9 @@ template <class T>
 hipError_t launch_unpermute_sum(const T* dx_perm, const int32_t* rmap, const float* partial, T* dx,
                                 int T_, int k, int d, hipStream_t st) {
   if (T_ == 0) return hipSuccess;
-  unpermute_sum_kernel<T><<<T_, 256, 0, st>>>(dx_perm, rmap, partial, dx, k, d);
+#define MOE_L(KC) unpermute_sum_kernel<T, KC><<<T_, 256, 0, st>>>(dx_perm, rmap, partial, dx, k, d)
+  MOE_DISPATCH_K(k, MOE_L);
+#undef MOE_L
   return hipGetLastError();
 }
 
