@@ -126,6 +126,25 @@ def kernel_work(cfg: mi.MoEConfig, counts) -> dict:
     return out
 
 
+def bandwidth_work(cfg: mi.MoEConfig) -> dict:
+    """Algorithmic HBM bytes per launch of the row-moving kernels (bf16 rows;
+    routing tables of T*k entries counted too): the permute reads each token row
+    once and writes its k copies; the combine reads the k rows (and the shared
+    output) and writes y; its backward reads dy and the k rows and writes the k
+    gradient rows and the gate gradients; the unpermute-sum reads the k rows and
+    the fp32 partial dx and writes dx."""
+    B = 4 if cfg.dtype == "f32" else 2
+    T, k, d = cfg.T, cfg.k, cfg.d
+    tab = T * k * 4
+    sh = T * d * B if cfg.f_shared else 0
+    return {
+        "scatter_rows": T * d * B + T * k * d * B + tab,
+        "combine": T * k * d * B + sh + T * d * B + 2 * tab,
+        "combine_bwd": T * d * B + 2 * T * k * d * B + 3 * tab,
+        "unpermute_sum": T * k * d * B + T * d * 4 + T * d * B + tab,
+    }
+
+
 def cpu_baseline(cfg, dev_inp, sample_tokens: int) -> dict:
     """Time the CPU oracle (as it stands) on the first `sample_tokens` tokens of
     the same workload: full router over all experts, the sampled tokens' experts
@@ -308,6 +327,18 @@ def main():
                 if tt > 0:
                     kern[n]["tflops"] = round(fl2 / tt / 1e12, 1)
                     kern[n]["gbs"] = round(by2 / tt / 1e9, 1)
+                    # fraction of the roofline that bounds this kernel (MFMA peak
+                    # above the ridge, HBM peak below), and of both peaks
+                    kern[n]["mfma_frac"] = round(fl2 / tt / 1e12 / peak_mfma, 4)
+                    kern[n]["hbm_frac"] = round(by2 / tt / 1e9 / PEAK_HBM_GBS, 4)
+                    kern[n]["bound"] = "hbm" if fl2 / by2 < ridge else "mfma"
+                    kern[n]["roofline_frac"] = kern[n]["hbm_frac"] if kern[n]["bound"] == "hbm" else kern[n]["mfma_frac"]
+
+    for n, by2 in bandwidth_work(cfg).items():
+        if n in kern and kern[n]["avg_ms"] > 0:
+            kern[n]["gbs"] = round(by2 / (kern[n]["avg_ms"] * 1e-3) / 1e9, 1)
+            kern[n]["bound"] = "hbm"
+            kern[n]["hbm_frac"] = kern[n]["roofline_frac"] = round(kern[n]["gbs"] / PEAK_HBM_GBS, 4)
 
     out = {
         "metric": "MoE layer fwd+bwd TFLOPS & tokens/s at DSv3 shape, 1 MI355X; % MFMA peak",
