@@ -134,7 +134,8 @@ moe_status moe_router_topk(const moe_cfg* cfg, const void* x, const void* w_rout
 /* ---------------------------------------------------------------------------
  * Permute ("System Modules: Dispatcher" on one GPU; memory-efficient
  * permutation, Figure 7): a stable counting sort of the (token, choice) pairs
- * by expert and one gather of the token rows.
+ * by expert, then each token row is copied to its k permuted rows (read once,
+ * written k times).
  *
  *   expert_offsets[e] = number of assignments to experts < e  ([E+1] int32,
  *                       expert_offsets[E] = T*k)
