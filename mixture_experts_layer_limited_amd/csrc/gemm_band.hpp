@@ -3,37 +3,34 @@
 // Product: C[g] (M x N) = P_g^T Q_g, where P_g [n_g x M] and Q_g [n_g x N] are
 // the rows of group (expert) g in row-contiguous storage: the contraction runs
 // over the expert's rows, n_g of them.  At an average of a few hundred rows per
-// expert the output (all of C, bf16) is far larger than the operands, so the
-// product is bound by its stores, and every byte of operand that a tile reads
-// from L2 competes with them.
+// expert the output (all of C, bf16) is far larger than the operands.
 //
-// Work unit: (expert g, band of 128 columns of P).  The band, n_g x 128 values
-// (n_g <= 320), goes into LDS by DMA once per unit; each wave then holds its 64
-// band columns for the whole contraction as MFMA fragments in registers (128
-// VGPRs) while the unit walks the N / 128 column tiles of Q_g.  Only Q's tiles
-// stream, in 64-row slices through a 4-stage DMA ring, so a 128 x 128 output
-// tile costs 128 x n_g x 2 bytes of operand reads instead of twice that.  The
-// next unit's band is fetched into the band region right after the current
-// band has been read into registers, a whole unit ahead of its use.
+// Work unit: (expert g, band of 128 columns of one operand: of Q when the band
+// is on the output's column side, of P when on its row side).  The band,
+// n_g x 128 values (n_g <= 320), goes into LDS by DMA at the start of the unit,
+// and the unit walks the 128-wide tiles of the output's other side, streaming
+// the other operand in 64-row slices through a 4-stage DMA ring: a 128 x 128
+// output tile costs 128 x n_g x 2 bytes of operand reads instead of twice that.
+// Compute waves read the fragments of both operands from LDS.
 //
 // Waits.  Vector memory operations of a wave complete in issue order, so the
 // wait for a slice allows exactly the operations issued after that slice's DMA
-// (later slices, band prefetches, epilogue stores) to stay outstanding: the
-// wave counts what it issues and records the count after each slice and each
-// band.  Slices and stores issued later never lengthen a wait.
+// to stay outstanding: a load wave counts what it issues and records the count
+// after each slice.
 //
-// Schedule.  One workgroup per CU (the band, the ring and the epilogue staging
-// fill the 160 KB of LDS), 2 x 2 waves of 64 x 64 over a 128 x 128 tile.  Each
-// XCD owns one contiguous run of the expert-major unit list, split by estimated
-// cost, and its workgroups stride through it, so the workgroups of an XCD hold
-// neighbouring bands of one expert and stream the same tiles of Q_g through
-// its L2 at about the same time.  Experts with no rows or more than 320 rows
-// are not units of this kernel (the caller zero-fills the first and runs the
-// general persistent kernel on the second).
+// Schedule.  One workgroup of six waves per CU (the band, the ring and the
+// epilogue staging fill the 160 KB of LDS), four compute waves of 64 x 64 over a
+// 128 x 128 tile.  Each XCD owns one contiguous run of the expert-major unit
+// list, split by estimated cost, and its workgroups stride through it, so the
+// workgroups of an XCD hold neighbouring bands of one expert; each unit walks
+// its tiles from its band index on, so neighbours stream different tiles at
+// any time.  Experts with no rows or more than 320 rows are not units of this
+// kernel (the caller zero-fills the first and runs the DMA ring on the second).
 //
-// Epilogue: each wave writes its 64 x 64 sub-tile as bf16 into its own 8 KB
-// staging area (LDS operations of one wave execute in order, so no barrier is
-// needed) and stores it back as 128-byte row segments, non-temporal.
+// Epilogue: each compute wave writes its 64 x 64 sub-tile as bf16, 32 rows at
+// a time, into its own 4 KB staging area (LDS operations of one wave execute in
+// order, so no barrier is needed) and stores it back as 128-byte row segments,
+// non-temporal.
 #pragma once
 
 #include "gemm_mfma.hpp"

@@ -1,4 +1,6 @@
-// bf16 MFMA grouped-GEMM kernel for gfx950, register-staged variant.
+// bf16 MFMA grouped-GEMM kernel for gfx950, register-staged variant (selected
+// by MOE_TILE=3; its persistent form below runs the MXFP8 weight gradients and
+// the router's weight gradient).
 //
 // One tile per workgroup (the grid covers every logical tile; surplus
 // workgroups of the ragged schedule exit at once), 256 threads in 2x2 waves,
