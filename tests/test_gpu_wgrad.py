@@ -31,11 +31,17 @@ SIZES = {
 }
 
 
+# (d, f): with d = 768, f = 512 both weight gradients (gate/up 1024 x 768, down
+# 768 x 512) are taller than wide and keep the band on their row side; with
+# d = 1024, f = 256 the gate/up gradient (512 x 1024) keeps it on its column side
+SHAPES = [(768, 512), (1024, 256)]
+
+
+@pytest.mark.parametrize("d,f", SHAPES, ids=lambda v: str(v))
 @pytest.mark.parametrize("name", list(SIZES))
-def test_expert_wgrad_parity(name):
+def test_expert_wgrad_parity(name, d, f):
     sizes = np.asarray(SIZES[name], np.int64)
     E, rows = len(sizes), int(sizes.sum())
-    d, f = 768, 512
     print(f"case wgrad {name} E={E} rows={rows} d={d} f={f}", flush=True)
     cfg = mi.MoEConfig(f"wgrad_{name}", T=rows, d=d, E=E, k=1, f=f, dtype="bf16", backward=True)
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
