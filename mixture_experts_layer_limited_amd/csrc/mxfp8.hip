@@ -152,8 +152,14 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
                                                             int rows, int C, const int* __restrict__ off,
                                                             const int* __restrict__ poff, int G, int64_t ldq,
                                                             int rp_limit, uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales) {
+                                                            uint8_t* __restrict__ scales, int64_t z_src,
+                                                            int64_t z_codes) {
   __shared__ uint16_t tile[kQcRows][kQcCols];
+  // grid z: independent matrices (a batch of weights), z_src elements and
+  // z_codes code bytes apart (z_codes / 32 scale bytes)
+  src += blockIdx.z * z_src;
+  codes += blockIdx.z * z_codes;
+  scales += blockIdx.z * (z_codes / 32);
   const int rp0 = blockIdx.x * kQcRows;
   const int c0 = blockIdx.y * kQcCols;
   int src0, n;                                          // source rows of this tile: src0 .. src0+n-1
@@ -202,19 +208,20 @@ hipError_t launch_mx_quant_cols(const void* src, int64_t ld, int rows, int C, co
   if (rows_pad_max == 0 || C == 0) return hipSuccess;
   const int tiles = (rows_pad_max + kQcRows - 1) / kQcRows;
   mx_quant_cols_kernel<<<dim3(tiles, (C + kQcCols - 1) / kQcCols), 256, 0, st>>>(
-      (const uint16_t*)src, ld, rows, C, off, poff, G, ldq, rows_pad_max, codes, scales);
+      (const uint16_t*)src, ld, rows, C, off, poff, G, ldq, rows_pad_max, codes, scales, 0, 0);
   return hipGetLastError();
 }
 
-// batched transposed form for weights: src [batch][R][C] -> codes [batch][C][R]
+// batched transposed form for weights: src [batch][R][C] -> codes [batch][C][R],
+// one launch with the batch in the grid's z dimension (one launch per matrix
+// took 8.9 ms for 256 matrices of 4096 x 7168, dominated by launch and drain)
 hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C, uint8_t* codes,
                                         uint8_t* scales, hipStream_t st) {
-  for (int b = 0; b < batch; ++b) {
-    hipError_t e = launch_mx_quant_cols((const uint16_t*)src + (int64_t)b * R * C, C, R, C, nullptr, nullptr, 1,
-                                        R, R, codes + (int64_t)b * R * C, scales + (int64_t)b * R * C / 32, st);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  if (batch == 0 || R == 0 || C == 0) return hipSuccess;
+  const int tiles = (R + kQcRows - 1) / kQcRows;
+  mx_quant_cols_kernel<<<dim3(tiles, (C + kQcCols - 1) / kQcCols, batch), 256, 0, st>>>(
+      (const uint16_t*)src, C, R, C, nullptr, nullptr, 1, R, R, codes, scales, (int64_t)R * C, (int64_t)R * C);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
