@@ -142,7 +142,7 @@ hipError_t launch_padded_offsets(const int* off, int G, int* poff, hipStream_t s
 // straddling two groups since groups start on multiples of 128) by 64 columns.
 // The tile is read with 16-byte row loads into LDS; thread (column c, block b)
 // then quantises its 32 values and writes 32 contiguous code bytes, so the
-// four blocks of a column fill one 128-byte line.  src [rows][ld] bf16 with
+// four blocks of a column (four adjacent lanes) fill one 128-byte line.  src [rows][ld] bf16 with
 // groups off[G+1] (NULL: one group of `rows` rows); poff[G+1] padded offsets.
 // codes [C][ldq], scales [C][ldq/32]; rows at or past rp_limit are not written.
 // ---------------------------------------------------------------------------
@@ -185,15 +185,19 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
     const int c = c0 + ch * 8;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < n && c + 8 <= C) v = *(const u32x4*)(src + (int64_t)(src0 + r) * ld + c);
-    *(u32x4*)&tile[r][ch * 8] = v;
+    *(u32x4*)&tile[r][(ch ^ ((r >> 5) << 1)) * 8] = v;  // block b's chunks XOR 2b
   }
   __syncthreads();
-  const int c = threadIdx.x & (kQcCols - 1), b = threadIdx.x >> 6;
+  // wave w takes columns 16w .. 16w+15 and lane (4j + b) block b of column
+  // 16w + j: the four blocks of a column, one 128-byte code line, come from
+  // adjacent lanes; the XOR puts the 4 x 16 columns on 32 distinct banks
+  const int c = 16 * (threadIdx.x >> 6) + ((threadIdx.x & 63) >> 2), b = threadIdx.x & 3;
   const int rb = rp0 + 32 * b;
   if (c0 + c >= C || rb >= rp_limit) return;
+  const int pc = (((c >> 3) ^ (b << 1)) << 3) | (c & 7);
   float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = bf16_bits_lo(tile[32 * b + i][c]);
+  for (int i = 0; i < 32; ++i) v[i] = bf16_bits_lo(tile[32 * b + i][pc]);
   uint32_t out[8];
   const uint32_t sb = mx_block(v, out);
   u32x4* q = (u32x4*)(codes + (int64_t)(c0 + c) * ldq + rb);
