@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm_band.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "540ef88cbed6d4da1bbb66e192ca2b12ccb16e58f1147bb014f5dddf2f47ecbb",
-                          "fetch_bytes": 771815804, "write_bytes": 15032408608},
+    "gemm_wgrad_gateup": {"src_sha": "ce3b76040ce93ffd022d6aadc98e6ee2866ace0c60532b97e4700d30bb78784c",
+                          "fetch_bytes": 772733887, "write_bytes": 15032410496},
 }
 
 
