@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm_band.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "ce3b76040ce93ffd022d6aadc98e6ee2866ace0c60532b97e4700d30bb78784c",
-                          "fetch_bytes": 772733887, "write_bytes": 15032410496},
+    "gemm_wgrad_gateup": {"src_sha": "f83940f6d5db4d7b64bcd7b1f4dd412600161fc4f6453cfc3e2d362e65b5b79b",
+                          "fetch_bytes": 771860217, "write_bytes": 15032408544},
 }
 
 

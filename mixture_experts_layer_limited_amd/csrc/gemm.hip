@@ -114,13 +114,8 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
   int64_t grid = persistent ? (int64_t)device_cus() * per_cu : tiles;
   if (tiles < grid) grid = tiles;
   auto kern = gemm_mfma_kernel<BM, BN, WM, WN, STAGES, LA, LB, MODE, Epi>;
-  static bool attr_set = false;           // one attribute per instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
+  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, MxArgs{}, ep, NT, MT);
   return hipGetLastError();
 }
@@ -170,13 +165,8 @@ static hipError_t launch_regs(const GemmArgs& a, const typename Epi::P& ep, int 
   else grid = (int64_t)MT * NT;
   if (grid <= 0) return hipSuccess;
   auto kern = gemm_regs_kernel<LA, LB, MODE, Epi>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
+  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, ep, NT, MT);
   return hipGetLastError();
 }
@@ -197,13 +187,8 @@ static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int 
   int64_t grid = (int64_t)device_cus() * 2;   // two workgroups fit a CU's LDS
   if (tiles < grid) grid = tiles;
   auto kern = gemm_pipe_kernel<LA, LB, MODE, Epi, BK>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
+  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, MxArgs{}, ep, NT, MT);
   return hipGetLastError();
 }
@@ -234,15 +219,8 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
   static const int force = getenv("MOE_BAND_P") ? atoi(getenv("MOE_BAND_P")) : -1;
   const bool pband = force == 0 ? false : force == 1 ? true : a.M > a.N;
   auto kern = pband ? gemm_band_kernel<Epi, false> : gemm_band_kernel<Epi, true>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    for (auto k : {gemm_band_kernel<Epi, false>, gemm_band_kernel<Epi, true>}) {
-      hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         C::LDS_BYTES);
-      if (e != hipSuccess) return e;
-    }
-    attr_set = true;
-  }
+  static bool lds_done[2][kLdsAttrDevices] = {};  // per device, per orientation
+  if (hipError_t e = raise_lds_limit(lds_done[pband], (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   const int UB = pband ? a.M / C::BM : a.N / C::BN, TU = pband ? a.N / C::BN : a.M / C::BM;
   // each unit walks its tiles starting at its band index (mod the tile count),
   // so neighbouring units read different streamed tiles at any time (3% faster

@@ -7,6 +7,21 @@
 
 namespace moe {
 
+// A kernel's dynamic-LDS limit (hipFuncAttributeMaxDynamicSharedMemorySize)
+// is set per device: `done`, one array per kernel instantiation, records the
+// devices on which it has been raised to `bytes`.
+constexpr int kLdsAttrDevices = 64;
+inline hipError_t raise_lds_limit(bool (&done)[kLdsAttrDevices], const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kLdsAttrDevices) return hipErrorInvalidDevice;
+  if (done[dev]) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done[dev] = true;
+  return e;
+}
+
 struct RouterParams {
   int T, E, k;
   int score;        // 0 softmax, 1 sigmoid

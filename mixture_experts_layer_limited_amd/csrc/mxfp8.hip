@@ -244,13 +244,8 @@ static hipError_t launch_mx(const GemmArgs& a, const MxArgs& s, const typename E
   else grid = (int64_t)MT * NT;
   if (grid <= 0) return hipSuccess;
   auto kern = gemm_mx_kernel<MODE, Epi>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kMxTileLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
+  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, kMxTileLdsBytes); e != hipSuccess) return e;
   kern<<<(unsigned)grid, C::NTHR, kMxTileLdsBytes, st>>>(a, s, ep, NT, MT);
   return hipGetLastError();
 }
@@ -286,13 +281,8 @@ static hipError_t launch_mx_pipe(GemmArgs a, const MxArgs& s, const typename Epi
   int64_t grid = (int64_t)device_cus_mx() * 2;
   if (tiles < grid) grid = tiles;
   auto kern = gemm_pipe_kernel<KC, KC, MODE, Epi, 64, true>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
+  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
   return hipGetLastError();
 }
@@ -314,13 +304,8 @@ static hipError_t launch_mx_dma(GemmArgs a, const MxArgs& s, const typename Epi:
   if (tiles <= 0) return hipSuccess;
   a.lda /= 2; a.ldb /= 2; a.K /= 2; a.b_kend /= 2; a.b_gstride /= 2;
   auto kern = gemm_mfma_kernel<BM, BN, WM, WN, STAGES, KC, KC, MODE, Epi, true>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
+  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   kern<<<(unsigned)tiles, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
   return hipGetLastError();
 }
