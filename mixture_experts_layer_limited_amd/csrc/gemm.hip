@@ -277,17 +277,23 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
       return launch_pipe<LA, LB, MODE, Epi, 64>(a, ep, n_logical, rows_total, st);
     }
     if (t == 1) {
+      // dense products take 256x256 tiles only when those fill every CU: the
+      // shared expert's down-projection data gradient (4096 x 2048 outputs,
+      // 128 such tiles) runs 0.18 ms on 128x256 tiles against 0.25 ms
+      const int64_t big_count = (int64_t)((a.M + 255) / 256) *
+                                ((n_logical + (Epi::kPaired ? 127 : 255)) / (Epi::kPaired ? 128 : 256));
+      const bool dense_big = a.M >= 1024 && n_logical >= 1024 && big_count >= device_cus();
       if constexpr (MODE != RAGGED_K) {
-        // dense products take 256x256 tiles only when those fill every CU: the
-        // shared expert's down-projection data gradient (4096 x 2048 outputs,
-        // 128 such tiles) runs 0.18 ms on 128x256 tiles against 0.25 ms
-        const int64_t big_count = (int64_t)((a.M + 255) / 256) *
-                                  ((n_logical + (Epi::kPaired ? 127 : 255)) / (Epi::kPaired ? 128 : 256));
         const bool big = (LB == KC || big_dgrad()) &&
-                         (MODE == RAGGED_M ? big_tiles(rows_total, a.G)
-                                           : (a.M >= 1024 && n_logical >= 1024 && big_count >= device_cus()));
+                         (MODE == RAGGED_M ? big_tiles(rows_total, a.G) : dense_big);
         if (big)
           return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+      } else {
+        // a weight gradient over one dense contraction of many rows (the
+        // shared expert's, K = tokens) is MFMA-bound: 256x256 tiles, one per
+        // workgroup, as the dense data gradients
+        if (a.offsets == nullptr && a.K >= 1024 && dense_big)
+          return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, false);
       }
       return launch_mfma<128, 256, 2, 4, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
     }
