@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm_band.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "4c79687e09a0817b4557843e3c06af5fcd04b4705ed79b397a7afb832ed6dff3",
-                          "fetch_bytes": 772052138, "write_bytes": 15032417952},
+    "gemm_wgrad_gateup": {"src_sha": "2157eafbf987008b86a6b8f25cbce1febc6da0f2db6a5fbf3fedc2c6bea2f5e0",
+                          "fetch_bytes": 772583807, "write_bytes": 15032406176},
 }
 
 
