@@ -91,3 +91,55 @@ def test_expert_wgrad_parity(name, d, f):
             worst[k] = max(worst.get(k, 0.0), v)
             assert v <= TOL, f"expert {e} ({hi - lo} rows): {k} rel-L2 {v:.3e}"
     print(f"  worst rel-L2: {worst}", flush=True)
+
+
+def test_shared_expert_dense_wgrad():
+    """The shared expert's weight gradients contract over every token.  At T = 1024, d = 7168,
+    f_s = 2048 both of them (4096 x 7168 and 7168 x 2048 outputs, 448 and 224 tiles of 256 x 256)
+    run on 256 x 256 tiles, one per workgroup; every element of dWs13, dWs2 and dHU_s, and the fp32
+    shared dX, is compared with the oracle's SwiGLU backward.  The routed part is one expert
+    holding every row, with the identity as the permutation."""
+    T, d, fs, f = 1024, 7168, 2048, 256
+    print(f"case shared dense wgrad T={T} d={d} fs={fs}", flush=True)
+    cfg = mi.MoEConfig("shared_dense_wgrad", T=T, d=d, E=1, k=1, f=f, f_shared=fs, dtype="bf16",
+                       backward=True)
+    g = torch.Generator().manual_seed(13)
+
+    def bf(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g) * std).to(torch.bfloat16)
+
+    x, dy = bf(T, d), bf(T, d)
+    hu_s, act_s = bf(T, 2 * fs), bf(T, fs)
+    ws13, ws2 = bf(2 * fs, d, std=0.02), bf(d, fs, std=0.02)
+    hu, act = bf(T, 2 * f), bf(T, f)
+    w13, w2 = bf(1, 2 * f, d, std=0.02), bf(1, d, f, std=0.02)
+
+    dev = "cuda"
+    c = shape_of(cfg).cfg()
+    D = {k: v.to(dev) for k, v in dict(x=x, dy=dy, hu_s=hu_s, act_s=act_s, ws13=ws13, ws2=ws2,
+                                       hu=hu, act=act, w13=w13, w2=w2).items()}
+    off = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    e = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=dev)
+    dhu, dx_perm, dw13, dw2 = e(T, 2 * f), e(T, d), e(1, 2 * f, d), e(1, d, f)
+    dhu_s = e(T, 2 * fs)
+    dws13 = torch.full((2 * fs, d), 7.0, dtype=torch.bfloat16, device=dev)
+    dws2 = torch.full((d, fs), 7.0, dtype=torch.bfloat16, device=dev)
+    dx_partial = torch.empty(T, d, dtype=torch.float32, device=dev)
+    ws = torch.empty(abi.moe_workspace_size(c), dtype=torch.uint8, device=dev)
+    abi.moe_grouped_gemm_swiglu_bwd(c, D["dy"], D["x"], off, D["hu"], D["act"], D["w13"], D["w2"],
+                                    dhu, dx_perm, dw13, dw2, D["dy"], D["x"], D["hu_s"], D["act_s"],
+                                    D["ws13"], D["ws2"], dhu_s, dx_partial, dws13, dws2, ws)
+    torch.cuda.synchronize()
+
+    f64 = lambda t: t.float().double().numpy()
+    HU = f64(hu_s)
+    o = O.swiglu_ffn_bwd(f64(x), HU[:, :fs], HU[:, fs:], f64(act_s), f64(dy), f64(ws13), f64(ws2), "bf16")
+    errs = {
+        "dWs13": rel_l2(host(dws13), o["dW13"]),
+        "dWs2": rel_l2(host(dws2), o["dW2"]),
+        "dHU_s": rel_l2(host(dhu_s), np.concatenate([o["dH"], o["dU"]], axis=1)),
+        "dX_s": rel_l2(host(dx_partial), o["dX32"]),
+    }
+    print(f"  rel-L2: {errs}", flush=True)
+    for k, v in errs.items():
+        assert v <= TOL, f"{k} rel-L2 {v:.3e}"
