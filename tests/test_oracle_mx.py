@@ -151,3 +151,79 @@ def test_mx_backward_is_close_to_bf16_backward():
     for k in ("dH", "dU", "dX", "dW13", "dW2"):
         rel = np.linalg.norm(gm[k] - ga[k]) / np.linalg.norm(ga[k])
         assert 1e-4 < rel < 1e-1, (k, rel)
+
+
+# ---------------------------------------------------------------------------
+# Quantisation axis of every GEMM of the MXFP8 expert.  Each product
+# C[i, j] = sum_k P[i, k] Q[j, k] must see both operands quantised in blocks
+# of 32 along its contraction index k (the tensor layouts per GEMM of the
+# figures page, Figure 31).  The reference below writes each operand in its
+# K-major form, quantises it along that K, and sums one k at a time with the
+# block index k // 32 spelled out.  Inputs carry one large outlier per
+# operand: in the right blocks it only coarsens its own 32-value block, in a
+# block laid along the other axis it flushes the small values of 31 other
+# rows to zero, which moves whole rows of the product.
+# ---------------------------------------------------------------------------
+def _kmajor_product(P, Q):
+    """sum_k deq(P)[i, k] deq(Q)[j, k] with P [M, K], Q [N, K] quantised along K."""
+    cp, sp = O.mx_quantize(P, 1)
+    cq, sq = O.mx_quantize(Q, 1)
+    vp, vq = O.e4m3_decode(cp), O.e4m3_decode(cq)
+    C = np.zeros((P.shape[0], Q.shape[0]))
+    for k in range(P.shape[1]):
+        a = vp[:, k] * np.exp2(sp[:, k // 32].astype(np.float64) - 127)
+        b = vq[:, k] * np.exp2(sq[:, k // 32].astype(np.float64) - 127)
+        C += np.outer(a, b)
+    return C
+
+
+def _with_outliers(a, rng, n=2, big=600.0):
+    a = a.copy()
+    for _ in range(n):
+        i, j = rng.integers(0, a.shape[0]), rng.integers(0, a.shape[1])
+        a[i, j] = big * (1 if rng.random() < 0.5 else -1)
+    return a
+
+
+def _assert_product(got, want, what):
+    err = np.max(np.abs(got - want)) / np.max(np.abs(want))
+    assert err < 1e-12, f"{what}: max error {err:.3e} relative to the largest output"
+
+
+def test_mx_forward_gemms_quantise_along_their_contraction():
+    """H, U = X W13^T contract over d (X and W13 blocked along d); Y = A W2^T
+    contracts over f (A and W2 blocked along f).  The oracle runs unrounded
+    ("f64" storage) so that each product is compared exactly."""
+    rng = np.random.default_rng(21)
+    n, d, f = 40, 96, 64                         # 40 rows: a short last row block
+    x = _with_outliers(rng.normal(0, 1, (n, d)), rng)
+    w13 = _with_outliers(rng.normal(0, 0.05, (2 * f, d)), rng, big=30.0)
+    w2 = _with_outliers(rng.normal(0, 0.05, (d, f)), rng, big=30.0)
+    o = O.swiglu_ffn_fwd_mx(x, w13, w2, "f64")
+    _assert_product(o["H"], _kmajor_product(x, w13[:f]), "H")
+    _assert_product(o["U"], _kmajor_product(x, w13[f:]), "U")
+    _assert_product(o["Y"], _kmajor_product(o["A"], w2), "Y")
+
+
+def test_mx_backward_gemms_quantise_along_their_contraction():
+    """dA = dY W2 contracts over d (dY along d, W2 along its rows d);
+    dW2 = dY^T A and dW13 = dHU^T X contract over the expert's rows (blocks of
+    32 rows from its first row); dX = dHU W13 contracts over 2f (dHU along 2f,
+    W13 along its rows).  The outliers sit in X, dY, A, W13, W2 and in U
+    (which carries one into dH)."""
+    rng = np.random.default_rng(22)
+    n, d, f = 40, 96, 64
+    x = _with_outliers(rng.normal(0, 1, (n, d)), rng)
+    w13 = _with_outliers(rng.normal(0, 0.05, (2 * f, d)), rng, big=30.0)
+    w2 = _with_outliers(rng.normal(0, 0.05, (d, f)), rng, big=30.0)
+    H = rng.normal(0, 1, (n, f))
+    U = _with_outliers(rng.normal(0, 1, (n, f)), rng)
+    A = _with_outliers(rng.normal(0, 1, (n, f)), rng)
+    dY = _with_outliers(rng.normal(0, 1, (n, d)), rng)
+    o = O.swiglu_ffn_bwd_mx(x, H, U, A, dY, w13, w2, "f64")
+    dHU = np.concatenate([o["dH"], o["dU"]], axis=1)
+    assert np.max(np.abs(o["dH"])) > 50 * np.median(np.abs(o["dH"]))     # U's outlier reached dH
+    _assert_product(o["dA"], _kmajor_product(dY, w2.T), "dA")
+    _assert_product(o["dW2"], _kmajor_product(dY.T, A.T), "dW2")
+    _assert_product(o["dX32"], _kmajor_product(dHU, w13.T), "dX")
+    _assert_product(o["dW13"], _kmajor_product(dHU.T, x.T), "dW13")
