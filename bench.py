@@ -238,7 +238,7 @@ def main():
         # The first pass allocates the quantised copies; the timed second pass gets the same
         # buffers back from torch's cache, so it times the quantisation kernels alone.
         layer.prepare_mx_weights(a["w13"], a["w2"], a["ws13"], a["ws2"])
-        layer.mx_tensors, layer.mx_weights = None, None
+        layer.mx_tensors, layer.mx_weights, layer.mx_key, layer.mx_sources = None, None, None, None
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()

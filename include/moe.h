@@ -65,6 +65,37 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
 
 typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 
+/* Layer modes (moe_cfg.flags, any combination).
+ *
+ * MOE_FLAG_FORCE_BALANCED: the benchmark condition of the pages' throughput
+ *   runs (thelatestinai.com page, Table 11 caption: force-balanced routing).
+ *   moe_router_topk still computes logits and scores, but choice j of token t
+ *   is expert (t*k + j) mod E instead of the top-k: every expert receives
+ *   T*k/E rows when E divides T*k.  Gates follow the usual rule on the
+ *   assigned experts' logits or scores; group limits and the bias play no part.
+ *
+ * MOE_FLAG_FOLD_GATES: gate folding, a reading of the memory-efficient
+ *   permutation (figures page, Figure 7 and Table 6).  Each permuted row's
+ *   gate multiplies its SwiGLU output before the down projection (which is
+ *   linear), act[r] = storage(g_r silu(H) U), so y_perm rows already carry
+ *   their gates and the combine sums them unweighted.  The backward then needs
+ *   neither a saved y_perm nor a gate-weighted dy_perm: dy_perm rows are
+ *   copies of dy, and the gate gradient d_gates[t,j] = <dA, silu(H) U> of the
+ *   row is formed inside the grouped-GEMM backward (dA = dy_perm w2[e], fp32).
+ *   The calls then take row_gates / row_id_map / d_gates as described below.
+ *
+ * MOE_FLAG_RECOMPUTE_ACT: SwiGLU recomputation (figures page, Figure 8
+ *   "Selective Recomputation"; Table 4, "Activation Function (SwiGLU)").  The
+ *   forward forms act from the stored (rounded) H and U, and the backward
+ *   forms it again from hu_save (and hu_shared_save) into its workspace, so act
+ *   (and act_shared) are not read by the backward and need not be kept after
+ *   the forward; the re-formed act is bit-identical to the forward's. */
+typedef enum moe_flags {
+  MOE_FLAG_FORCE_BALANCED = 1,
+  MOE_FLAG_FOLD_GATES = 2,
+  MOE_FLAG_RECOMPUTE_ACT = 4
+} moe_flags;
+
 /* Shape and routing rule of one MoE layer (host memory). */
 typedef struct moe_cfg {
   int64_t T;          /* tokens (batch x sequence, flattened)                */
@@ -80,7 +111,7 @@ typedef struct moe_cfg {
   float scale;        /* gate multiplier applied after renormalisation        */
   float aux_coeff;    /* load-balancing loss coefficient (0 = off; softmax)   */
   int32_t dtype;      /* moe_dtype of activations and weights                 */
-  int32_t reserved;   /* must be 0                                            */
+  int32_t flags;      /* moe_flags bits (0: plain top-k, gated combine, act kept) */
 } moe_cfg;
 
 /* Human-readable name of a status code (static string). */
@@ -132,6 +163,23 @@ moe_status moe_router_topk(const moe_cfg* cfg, const void* x, const void* w_rout
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Selection-bias update without an auxiliary loss (figures page, Figure 39,
+ * load-balancing strategies; the pages name the strategy, not its rule: the
+ * plainest reading is taken).  After a step, each expert's selection bias
+ * moves one fixed step toward balance: up if it received fewer than the mean
+ * T*k/E assignments, down if more, unchanged at exactly the mean:
+ *
+ *   bias[e] = fp32( bias[e] + rate * sign(T*k - E*expert_counts[e]) )
+ *
+ * (the sign is taken on the integers, the add is one fp32 round-to-nearest).
+ * expert_counts [E] int32 (moe_router_topk's output), bias [E] fp32 updated
+ * in place.  Only meaningful for the sigmoid score, whose selection the bias
+ * steers; accepted for any cfg.
+ * ------------------------------------------------------------------------- */
+moe_status moe_router_bias_update(const moe_cfg* cfg, const int32_t* expert_counts, float rate,
+                                  float* bias, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Permute ("System Modules: Dispatcher" on one GPU; memory-efficient
  * permutation, Figure 7): a stable counting sort of the (token, choice) pairs
  * by expert, then each token row is copied to its k permuted rows (read once,
@@ -143,13 +191,18 @@ moe_status moe_router_topk(const moe_cfg* cfg, const void* x, const void* w_rout
  *                       e = topk_idx[t,j]                          ([T,k] int32)
  *   src_token[row]    = the token of that row                     ([T*k] int32)
  *   x_perm[row,:]     = x[src_token[row],:]                       ([T*k,d] storage)
+ *   row_gates[row_id_map[t,j]] = topk_gates[t,j]                  ([T*k] fp32)
  *
  * x [T,d] storage, topk_idx [T,k] int32 (each row k distinct ids in [0,E)).
- * x_perm is the only permuted copy of the activations kept by the layer.
+ * topk_gates [T,k] fp32 and row_gates: both or neither (the gate of each
+ * permuted row; required with MOE_FLAG_FOLD_GATES, where the grouped GEMMs
+ * apply it).  x_perm is the only permuted copy of the activations kept by the
+ * layer.
  * ------------------------------------------------------------------------- */
 moe_status moe_permute(const moe_cfg* cfg, const void* x, const int32_t* topk_idx,
-                       int32_t* expert_offsets, int32_t* row_id_map, int32_t* src_token,
-                       void* x_perm, void* workspace, size_t workspace_bytes, void* stream);
+                       const float* topk_gates, int32_t* expert_offsets, int32_t* row_id_map,
+                       int32_t* src_token, float* row_gates, void* x_perm, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Experts ("System Modules: Experts": FFNs run as a grouped GEMM over uneven
@@ -159,20 +212,25 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const int32_t* topk_id
  * For each expert e over its rows r in [off[e], off[e+1]) (empty experts
  * skipped):
  *   H = x_perm[r] w13[e][0:f]^T, U = x_perm[r] w13[e][f:2f]^T   (fp32 accumulate)
- *   act[r]    = storage(silu(H) * U), silu(h) = h / (1 + exp(-h))
+ *   act[r]    = storage(g_r silu(H) * U), silu(h) = h / (1 + exp(-h)),
+ *               g_r = row_gates[r] with MOE_FLAG_FOLD_GATES, else 1; with
+ *               MOE_FLAG_RECOMPUTE_ACT, H and U enter as storage(H), storage(U)
  *   y_perm[r] = storage(act[r] w2[e]^T)
  *   hu_save[r] = (storage(H) | storage(U))       [T*k, 2f], if non-NULL
  * Shared expert (cfg.f_shared > 0): the same FFN with ws13/ws2 on every token
  * of x, writing act_shared [T,fs], y_shared [T,d], hu_shared_save [T,2fs].
  *
  * x_perm [T*k,d], expert_offsets [E+1] (from moe_permute), w13, w2 storage;
- * act [T*k,f] and y_perm [T*k,d] required; hu_save optional (needed by the
- * backward call).  x, ws13, ws2, act_shared, y_shared required iff
- * f_shared > 0; hu_shared_save optional.
+ * row_gates [T*k] fp32 (moe_permute's) required with MOE_FLAG_FOLD_GATES,
+ * else ignored; act [T*k,f] and y_perm [T*k,d] required; hu_save optional
+ * (needed by the backward call).  x, ws13, ws2, act_shared, y_shared required
+ * iff f_shared > 0; hu_shared_save optional.  The shared expert's act is never
+ * gated.
  * ------------------------------------------------------------------------- */
 moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm,
-                                   const int32_t* expert_offsets, const void* w13,
-                                   const void* w2, void* hu_save, void* act, void* y_perm,
+                                   const int32_t* expert_offsets, const float* row_gates,
+                                   const void* w13, const void* w2, void* hu_save, void* act,
+                                   void* y_perm,
                                    const void* x, const void* ws13, const void* ws2,
                                    void* hu_shared_save, void* act_shared, void* y_shared,
                                    void* workspace, size_t workspace_bytes, void* stream);
@@ -182,6 +240,8 @@ moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm,
  * original position and the gate-weighted sum is formed).
  *   y[t] = storage( sum_{j=0}^{k-1} gates[t,j] * y_perm[row_id_map[t,j]]
  *                   + y_shared[t] )        fp32 sum in j order, one rounding
+ * With MOE_FLAG_FOLD_GATES the rows carry their gates: the sum is unweighted
+ * and topk_gates is ignored (may be NULL).
  * y_perm [T*k,d], row_id_map [T,k], topk_gates [T,k] fp32, y_shared [T,d] or
  * NULL, y [T,d].
  * ------------------------------------------------------------------------- */
@@ -197,7 +257,10 @@ moe_status moe_unpermute_combine(const moe_cfg* cfg, const void* y_perm,
  * ========================================================================= */
 
 /* dy_perm[row_id_map[t,j]] = storage(gates[t,j] * dy[t])          [T*k,d]
- * d_gates[t,j] = sum_i dy[t,i] * y_perm[row_id_map[t,j], i]      [T,k] fp32 */
+ * d_gates[t,j] = sum_i dy[t,i] * y_perm[row_id_map[t,j], i]      [T,k] fp32
+ * With MOE_FLAG_FOLD_GATES: dy_perm[row_id_map[t,j]] = dy[t] (a copy: the gate
+ * is inside the expert), and y_perm, topk_gates, d_gates are not used (may be
+ * NULL); moe_grouped_gemm_swiglu_bwd writes d_gates. */
 moe_status moe_unpermute_combine_bwd(const moe_cfg* cfg, const void* dy,
                                      const void* y_perm, const int32_t* row_id_map,
                                      const float* topk_gates, void* dy_perm,
@@ -210,6 +273,15 @@ moe_status moe_unpermute_combine_bwd(const moe_cfg* cfg, const void* dy,
  *   dw2[e]  = dy_perm[rows]^T act[rows]                  [d, f]   storage
  *   dx_perm = dhu w13[e]                                 [T*k, d] storage
  *   dw13[e] = dhu[rows]^T x_perm[rows]                   [2f, d]  storage
+ * MOE_FLAG_FOLD_GATES (dy_perm holds copies of dy, act carries the gates):
+ *   dH, dU as above with g_r dA in place of dA, g_r = row_gates[r], and the
+ *   gate gradient d_gates[t,j] = sum_c dA[r,c] silu(H[r,c]) U[r,c] of row
+ *   r = row_id_map[t,j] (fp32; per row, partial sums over 64-column blocks
+ *   added in order); row_gates [T*k], row_id_map [T,k], d_gates [T,k]
+ *   required, else ignored.
+ * MOE_FLAG_RECOMPUTE_ACT: act (and act_shared) are not read (may be NULL): the
+ *   dA product forms act = storage(g_r silu(H) U) again from hu_save into the
+ *   workspace, bit-identical to the forward's, and dw2 uses that.
  * Shared expert (f_shared > 0), on all tokens with upstream gradient dy:
  *   the same with ws13/ws2, hu_shared_save, act_shared, x -> dhu_shared,
  *   dws13, dws2, and its input gradient dhu_shared ws13 written in fp32 to
@@ -218,9 +290,10 @@ moe_status moe_unpermute_combine_bwd(const moe_cfg* cfg, const void* dy,
  * moe_permute_bwd (reads). */
 moe_status moe_grouped_gemm_swiglu_bwd(const moe_cfg* cfg, const void* dy_perm,
                                        const void* x_perm, const int32_t* expert_offsets,
+                                       const float* row_gates, const int32_t* row_id_map,
                                        const void* hu_save, const void* act,
                                        const void* w13, const void* w2, void* dhu,
-                                       void* dx_perm, void* dw13, void* dw2,
+                                       void* dx_perm, void* dw13, void* dw2, float* d_gates,
                                        const void* dy, const void* x,
                                        const void* hu_shared_save, const void* act_shared,
                                        const void* ws13, const void* ws2, void* dhu_shared,
@@ -325,7 +398,7 @@ typedef struct moe_mx_weights {
  * (host pointer to the struct; its members are device pointers).  fp32
  * accumulation, bf16 outputs. */
 moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm,
-                                         const int32_t* expert_offsets,
+                                         const int32_t* expert_offsets, const float* row_gates,
                                          const moe_mx_weights* weights, void* hu_save, void* act,
                                          void* y_perm, const void* x, void* hu_shared_save,
                                          void* act_shared, void* y_shared, void* workspace,
@@ -340,9 +413,11 @@ moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm,
  * Same outputs as the bf16 call (dx_partial written, not accumulated). */
 moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_perm,
                                              const void* x_perm, const int32_t* expert_offsets,
+                                             const float* row_gates, const int32_t* row_id_map,
                                              const void* hu_save, const void* act,
                                              const moe_mx_weights* weights, void* dhu, void* dx_perm,
-                                             void* dw13, void* dw2, const void* dy, const void* x,
+                                             void* dw13, void* dw2, float* d_gates, const void* dy,
+                                             const void* x,
                                              const void* hu_shared_save, const void* act_shared,
                                              void* dhu_shared, float* dx_partial, void* dws13,
                                              void* dws2, void* workspace, size_t workspace_bytes,

@@ -19,6 +19,7 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMA
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 MOE_MX_ROWS, MOE_MX_COLS = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_FLAG_FORCE_BALANCED, MOE_FLAG_FOLD_GATES, MOE_FLAG_RECOMPUTE_ACT = 1, 2, 4
 
 
 class moe_cfg(ctypes.Structure):
@@ -27,7 +28,7 @@ class moe_cfg(ctypes.Structure):
                 ("score", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("renorm", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("aux_coeff", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class moe_mx_tensor(ctypes.Structure):
@@ -52,21 +53,22 @@ _SIGS = {
     "moe_init": (ctypes.c_int, [ctypes.c_int]),
     "moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(moe_cfg)]),
     "moe_router_topk": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]),
-    "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 6 + [_P, ctypes.c_size_t, _P]),
-    "moe_grouped_gemm_swiglu": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 13 + [_P, ctypes.c_size_t, _P]),
+    "moe_router_bias_update": (ctypes.c_int, [ctypes.POINTER(moe_cfg), _P, ctypes.c_float, _P, _P]),
+    "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]),
+    "moe_grouped_gemm_swiglu": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 14 + [_P, ctypes.c_size_t, _P]),
     "moe_unpermute_combine": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 5 + [_P]),
     "moe_unpermute_combine_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 6 + [_P]),
-    "moe_grouped_gemm_swiglu_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 21 + [_P, ctypes.c_size_t, _P]),
+    "moe_grouped_gemm_swiglu_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 24 + [_P, ctypes.c_size_t, _P]),
     "moe_router_topk_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 7 + [ctypes.c_float] + [_P] * 3
                             + [_P, ctypes.c_size_t, _P]),
     "moe_permute_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 4 + [_P]),
     "moe_quantize_mxfp8": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                           _P, _P, _P]),
-    "moe_grouped_gemm_swiglu_mxfp8": (ctypes.c_int, [ctypes.POINTER(moe_cfg), _P, _P,
+    "moe_grouped_gemm_swiglu_mxfp8": (ctypes.c_int, [ctypes.POINTER(moe_cfg), _P, _P, _P,
                                                      ctypes.POINTER(moe_mx_weights)] + [_P] * 7
                                       + [_P, ctypes.c_size_t, _P]),
-    "moe_grouped_gemm_swiglu_bwd_mxfp8": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 5
-                                          + [ctypes.POINTER(moe_mx_weights)] + [_P] * 12
+    "moe_grouped_gemm_swiglu_bwd_mxfp8": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 7
+                                          + [ctypes.POINTER(moe_mx_weights)] + [_P] * 13
                                           + [_P, ctypes.c_size_t, _P]),
     "moe_trace_begin": (ctypes.c_int, [ctypes.c_int]),
     "moe_trace_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
@@ -97,12 +99,30 @@ def _status_name(s: int) -> str:
         return str(s)
 
 
-def _ptr(t):
+def _ptr(t, dtype=None):
+    """Device address of a tensor argument (None -> NULL, an int passes as is).
+    The C calls read row-major contiguous device memory of a fixed element
+    type, so a view with other strides, a host tensor or another dtype is
+    refused here instead of being misread."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError(f"tensor argument of shape {tuple(t.shape)} must be contiguous (strides {t.stride()})")
+    if t.device.type != "cuda":
+        raise ValueError(f"tensor argument must live on a CUDA (HIP) device, not {t.device}")
+    if dtype is not None and t.dtype not in ((dtype,) if not isinstance(dtype, tuple) else dtype):
+        raise TypeError(f"tensor argument has dtype {t.dtype}, expected {dtype}")
     return t.data_ptr()
+
+
+_F32, _I32, _U8 = torch.float32, torch.int32, torch.uint8
+
+
+def _st(cfg):
+    """Element type of the layer's storage tensors for `cfg`."""
+    return torch.float32 if cfg.dtype == MOE_F32 else torch.bfloat16
 
 
 def _stream(stream):
@@ -119,12 +139,15 @@ def _check(status: int, where: str):
 
 
 def make_cfg(T, d, E, k, f, f_shared=0, score="softmax", n_group=1, topk_group=1, renorm=True,
-             scale=1.0, aux_coeff=0.0, dtype="bf16") -> moe_cfg:
+             scale=1.0, aux_coeff=0.0, dtype="bf16", force_balanced=False, fold_gates=False,
+             recompute_act=False) -> moe_cfg:
+    flags = ((MOE_FLAG_FORCE_BALANCED if force_balanced else 0) | (MOE_FLAG_FOLD_GATES if fold_gates else 0)
+             | (MOE_FLAG_RECOMPUTE_ACT if recompute_act else 0))
     return moe_cfg(T=T, d=d, E=E, k=k, f=f, f_shared=f_shared,
                    score=MOE_SCORE_SIGMOID if score == "sigmoid" else MOE_SCORE_SOFTMAX,
                    n_group=n_group, topk_group=topk_group, renorm=int(bool(renorm)),
                    scale=scale, aux_coeff=aux_coeff,
-                   dtype={"f32": MOE_F32, "mxfp8": MOE_MXFP8}.get(dtype, MOE_BF16), reserved=0)
+                   dtype={"f32": MOE_F32, "mxfp8": MOE_MXFP8}.get(dtype, MOE_BF16), flags=flags)
 
 
 def moe_status_string(s: int) -> str:
@@ -153,67 +176,86 @@ def _ws(ws):
 def moe_router_topk(cfg, x, w_router, bias, logits, topk_idx, topk_gates, expert_counts, aux_loss,
                     workspace, stream=None):
     w, n = _ws(workspace)
-    _check(lib().moe_router_topk(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits),
-                                 _ptr(topk_idx), _ptr(topk_gates), _ptr(expert_counts), _ptr(aux_loss),
+    S = _st(cfg)
+    _check(lib().moe_router_topk(ctypes.byref(cfg), _ptr(x, S), _ptr(w_router, S), _ptr(bias, _F32),
+                                 _ptr(logits, _F32), _ptr(topk_idx, _I32), _ptr(topk_gates, _F32),
+                                 _ptr(expert_counts, _I32), _ptr(aux_loss, _F32),
                                  w, n, _stream(stream)), "moe_router_topk")
 
 
-def moe_permute(cfg, x, topk_idx, expert_offsets, row_id_map, src_token, x_perm, workspace, stream=None):
+def moe_router_bias_update(cfg, expert_counts, rate, bias, stream=None):
+    _check(lib().moe_router_bias_update(ctypes.byref(cfg), _ptr(expert_counts, _I32), float(rate), _ptr(bias, _F32),
+                                        _stream(stream)), "moe_router_bias_update")
+
+
+def moe_permute(cfg, x, topk_idx, topk_gates, expert_offsets, row_id_map, src_token, row_gates, x_perm, workspace,
+                stream=None):
     w, n = _ws(workspace)
-    _check(lib().moe_permute(ctypes.byref(cfg), _ptr(x), _ptr(topk_idx), _ptr(expert_offsets),
-                             _ptr(row_id_map), _ptr(src_token), _ptr(x_perm), w, n, _stream(stream)),
-           "moe_permute")
+    S = _st(cfg)
+    _check(lib().moe_permute(ctypes.byref(cfg), _ptr(x, S), _ptr(topk_idx, _I32), _ptr(topk_gates, _F32),
+                             _ptr(expert_offsets, _I32), _ptr(row_id_map, _I32), _ptr(src_token, _I32),
+                             _ptr(row_gates, _F32), _ptr(x_perm, S), w, n, _stream(stream)), "moe_permute")
 
 
-def moe_grouped_gemm_swiglu(cfg, x_perm, expert_offsets, w13, w2, hu_save, act, y_perm, x, ws13, ws2,
+def moe_grouped_gemm_swiglu(cfg, x_perm, expert_offsets, row_gates, w13, w2, hu_save, act, y_perm, x, ws13, ws2,
                             hu_shared_save, act_shared, y_shared, workspace, stream=None):
     w, n = _ws(workspace)
+    S = _st(cfg)
     _check(lib().moe_grouped_gemm_swiglu(
-        ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_offsets), _ptr(w13), _ptr(w2), _ptr(hu_save),
-        _ptr(act), _ptr(y_perm), _ptr(x), _ptr(ws13), _ptr(ws2), _ptr(hu_shared_save),
-        _ptr(act_shared), _ptr(y_shared), w, n, _stream(stream)), "moe_grouped_gemm_swiglu")
+        ctypes.byref(cfg), _ptr(x_perm, S), _ptr(expert_offsets, _I32), _ptr(row_gates, _F32), _ptr(w13, S),
+        _ptr(w2, S),
+        _ptr(hu_save, S), _ptr(act, S), _ptr(y_perm, S), _ptr(x, S), _ptr(ws13, S), _ptr(ws2, S),
+        _ptr(hu_shared_save, S), _ptr(act_shared, S), _ptr(y_shared, S), w, n, _stream(stream)),
+        "moe_grouped_gemm_swiglu")
 
 
 def moe_unpermute_combine(cfg, y_perm, row_id_map, topk_gates, y_shared, y, stream=None):
-    _check(lib().moe_unpermute_combine(ctypes.byref(cfg), _ptr(y_perm), _ptr(row_id_map),
-                                       _ptr(topk_gates), _ptr(y_shared), _ptr(y), _stream(stream)),
+    S = _st(cfg)
+    _check(lib().moe_unpermute_combine(ctypes.byref(cfg), _ptr(y_perm, S), _ptr(row_id_map, _I32),
+                                       _ptr(topk_gates, _F32), _ptr(y_shared, S), _ptr(y, S), _stream(stream)),
            "moe_unpermute_combine")
 
 
 def moe_unpermute_combine_bwd(cfg, dy, y_perm, row_id_map, topk_gates, dy_perm, d_gates, stream=None):
-    _check(lib().moe_unpermute_combine_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(y_perm), _ptr(row_id_map),
-                                           _ptr(topk_gates), _ptr(dy_perm), _ptr(d_gates),
-                                           _stream(stream)), "moe_unpermute_combine_bwd")
+    S = _st(cfg)
+    _check(lib().moe_unpermute_combine_bwd(ctypes.byref(cfg), _ptr(dy, S), _ptr(y_perm, S),
+                                           _ptr(row_id_map, _I32), _ptr(topk_gates, _F32), _ptr(dy_perm, S),
+                                           _ptr(d_gates, _F32), _stream(stream)), "moe_unpermute_combine_bwd")
 
 
-def moe_grouped_gemm_swiglu_bwd(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, w13, w2, dhu,
-                                dx_perm, dw13, dw2, dy, x, hu_shared_save, act_shared, ws13, ws2,
+def moe_grouped_gemm_swiglu_bwd(cfg, dy_perm, x_perm, expert_offsets, row_gates, row_id_map, hu_save, act, w13,
+                                w2, dhu, dx_perm, dw13, dw2, d_gates, dy, x, hu_shared_save, act_shared, ws13, ws2,
                                 dhu_shared, dx_partial, dws13, dws2, workspace, stream=None):
     w, n = _ws(workspace)
+    S = _st(cfg)
     _check(lib().moe_grouped_gemm_swiglu_bwd(
-        ctypes.byref(cfg), _ptr(dy_perm), _ptr(x_perm), _ptr(expert_offsets), _ptr(hu_save), _ptr(act),
-        _ptr(w13), _ptr(w2), _ptr(dhu), _ptr(dx_perm), _ptr(dw13), _ptr(dw2), _ptr(dy), _ptr(x),
-        _ptr(hu_shared_save), _ptr(act_shared), _ptr(ws13), _ptr(ws2), _ptr(dhu_shared),
-        _ptr(dx_partial), _ptr(dws13), _ptr(dws2), w, n, _stream(stream)), "moe_grouped_gemm_swiglu_bwd")
+        ctypes.byref(cfg), _ptr(dy_perm, S), _ptr(x_perm, S), _ptr(expert_offsets, _I32), _ptr(row_gates, _F32),
+        _ptr(row_id_map, _I32), _ptr(hu_save, S), _ptr(act, S), _ptr(w13, S), _ptr(w2, S), _ptr(dhu, S),
+        _ptr(dx_perm, S), _ptr(dw13, S), _ptr(dw2, S), _ptr(d_gates, _F32), _ptr(dy, S), _ptr(x, S), _ptr(hu_shared_save, S), _ptr(act_shared, S), _ptr(ws13, S), _ptr(ws2, S),
+        _ptr(dhu_shared, S), _ptr(dx_partial, _F32), _ptr(dws13, S), _ptr(dws2, S), w, n, _stream(stream)),
+        "moe_grouped_gemm_swiglu_bwd")
 
 
 def moe_router_topk_bwd(cfg, x, w_router, logits, topk_idx, topk_gates, expert_counts, d_gates, d_aux,
                         d_logits, dw_router, dx_partial, workspace, stream=None):
     w, n = _ws(workspace)
+    S = _st(cfg)
     _check(lib().moe_router_topk_bwd(
-        ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(topk_idx), _ptr(topk_gates),
-        _ptr(expert_counts), _ptr(d_gates), float(d_aux), _ptr(d_logits), _ptr(dw_router),
-        _ptr(dx_partial), w, n, _stream(stream)), "moe_router_topk_bwd")
+        ctypes.byref(cfg), _ptr(x, S), _ptr(w_router, S), _ptr(logits, _F32), _ptr(topk_idx, _I32),
+        _ptr(topk_gates, _F32), _ptr(expert_counts, _I32), _ptr(d_gates, _F32), float(d_aux),
+        _ptr(d_logits, _F32), _ptr(dw_router, S), _ptr(dx_partial, _F32), w, n, _stream(stream)),
+        "moe_router_topk_bwd")
 
 
 def moe_permute_bwd(cfg, dx_perm, row_id_map, dx_partial, dx, stream=None):
-    _check(lib().moe_permute_bwd(ctypes.byref(cfg), _ptr(dx_perm), _ptr(row_id_map), _ptr(dx_partial),
-                                 _ptr(dx), _stream(stream)), "moe_permute_bwd")
+    S = _st(cfg)
+    _check(lib().moe_permute_bwd(ctypes.byref(cfg), _ptr(dx_perm, S), _ptr(row_id_map, _I32),
+                                 _ptr(dx_partial, _F32), _ptr(dx, S), _stream(stream)), "moe_permute_bwd")
 
 
 def moe_quantize_mxfp8(src, batch, rows, cols, orientation, codes, scales, stream=None):
-    _check(lib().moe_quantize_mxfp8(_ptr(src), batch, rows, cols, orientation, _ptr(codes), _ptr(scales),
-                                    _stream(stream)), "moe_quantize_mxfp8")
+    _check(lib().moe_quantize_mxfp8(_ptr(src, torch.bfloat16), batch, rows, cols, orientation, _ptr(codes, _U8),
+                                    _ptr(scales, _U8), _stream(stream)), "moe_quantize_mxfp8")
 
 
 def mx_weights(**tensors) -> moe_mx_weights:
@@ -222,28 +264,32 @@ def mx_weights(**tensors) -> moe_mx_weights:
     w = moe_mx_weights()
     for name, pair in tensors.items():
         if pair is not None:
-            setattr(w, name, moe_mx_tensor(_ptr(pair[0]), _ptr(pair[1])))
+            setattr(w, name, moe_mx_tensor(_ptr(pair[0], _U8), _ptr(pair[1], _U8)))
     return w
 
 
-def moe_grouped_gemm_swiglu_mxfp8(cfg, x_perm, expert_offsets, weights, hu_save, act, y_perm, x,
+def moe_grouped_gemm_swiglu_mxfp8(cfg, x_perm, expert_offsets, row_gates, weights, hu_save, act, y_perm, x,
                                   hu_shared_save, act_shared, y_shared, workspace, stream=None):
     w, n = _ws(workspace)
+    S = torch.bfloat16
     _check(lib().moe_grouped_gemm_swiglu_mxfp8(
-        ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_offsets), ctypes.byref(weights), _ptr(hu_save),
-        _ptr(act), _ptr(y_perm), _ptr(x), _ptr(hu_shared_save), _ptr(act_shared), _ptr(y_shared),
-        w, n, _stream(stream)), "moe_grouped_gemm_swiglu_mxfp8")
+        ctypes.byref(cfg), _ptr(x_perm, S), _ptr(expert_offsets, _I32), _ptr(row_gates, _F32), ctypes.byref(weights),
+        _ptr(hu_save, S),
+        _ptr(act, S), _ptr(y_perm, S), _ptr(x, S), _ptr(hu_shared_save, S), _ptr(act_shared, S),
+        _ptr(y_shared, S), w, n, _stream(stream)), "moe_grouped_gemm_swiglu_mxfp8")
 
 
-def moe_grouped_gemm_swiglu_bwd_mxfp8(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, weights, dhu,
-                                      dx_perm, dw13, dw2, dy, x, hu_shared_save, act_shared, dhu_shared,
-                                      dx_partial, dws13, dws2, workspace, stream=None):
+def moe_grouped_gemm_swiglu_bwd_mxfp8(cfg, dy_perm, x_perm, expert_offsets, row_gates, row_id_map, hu_save, act,
+                                      weights, dhu, dx_perm, dw13, dw2, d_gates, dy, x, hu_shared_save, act_shared,
+                                      dhu_shared, dx_partial, dws13, dws2, workspace, stream=None):
     w, n = _ws(workspace)
+    S = torch.bfloat16
     _check(lib().moe_grouped_gemm_swiglu_bwd_mxfp8(
-        ctypes.byref(cfg), _ptr(dy_perm), _ptr(x_perm), _ptr(expert_offsets), _ptr(hu_save), _ptr(act),
-        ctypes.byref(weights), _ptr(dhu), _ptr(dx_perm), _ptr(dw13), _ptr(dw2), _ptr(dy), _ptr(x),
-        _ptr(hu_shared_save), _ptr(act_shared), _ptr(dhu_shared), _ptr(dx_partial), _ptr(dws13),
-        _ptr(dws2), w, n, _stream(stream)), "moe_grouped_gemm_swiglu_bwd_mxfp8")
+        ctypes.byref(cfg), _ptr(dy_perm, S), _ptr(x_perm, S), _ptr(expert_offsets, _I32), _ptr(row_gates, _F32),
+        _ptr(row_id_map, _I32), _ptr(hu_save, S), _ptr(act, S), ctypes.byref(weights), _ptr(dhu, S),
+        _ptr(dx_perm, S), _ptr(dw13, S), _ptr(dw2, S), _ptr(d_gates, _F32), _ptr(dy, S), _ptr(x, S), _ptr(hu_shared_save, S), _ptr(act_shared, S), _ptr(dhu_shared, S),
+        _ptr(dx_partial, _F32), _ptr(dws13, S), _ptr(dws2, S), w, n, _stream(stream)),
+        "moe_grouped_gemm_swiglu_bwd_mxfp8")
 
 
 def moe_trace_begin(capacity: int):

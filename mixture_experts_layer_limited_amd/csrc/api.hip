@@ -77,7 +77,8 @@ moe_status check_current_device() {
 // ---- argument validation ---------------------------------------------------
 moe_status check_cfg(const moe_cfg* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg is NULL");
-  if (c->reserved != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.reserved must be 0");
+  if (c->flags & ~(MOE_FLAG_FORCE_BALANCED | MOE_FLAG_FOLD_GATES | MOE_FLAG_RECOMPUTE_ACT))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.flags = 0x%x has unknown bits", (unsigned)c->flags);
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_MXFP8)
     return fail(MOE_ERR_UNSUPPORTED, "cfg.dtype %d not supported", c->dtype);
   if (c->T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.T = %lld < 0", (long long)c->T);
@@ -108,10 +109,31 @@ moe_status check_cfg(const moe_cfg* c) {
   return MOE_OK;
 }
 
+// The MFMA kernels address an operand through a buffer resource with a 32-bit
+// byte range and 32-bit per-lane offsets: one expert's (or the dense
+// products') rows of any operand or output, and one expert's weight matrix,
+// must span fewer than 2^31 bytes.  Expert sizes are only known on the
+// device, so the bound is taken with all T*k rows in one expert.
+moe_status check_offsets_32bit(const moe_cfg* c, int64_t elt_bytes) {
+  const int64_t lim = (int64_t)1 << 31;
+  int64_t width = c->d;                              // widest row of any operand or output
+  if (2 * c->f > width) width = 2 * c->f;
+  if (2 * c->f_shared > width) width = 2 * c->f_shared;
+  if (c->E > width) width = c->E;
+  const int64_t rows = c->T * c->k > c->T ? c->T * c->k : c->T;
+  const int64_t wmax = 2 * (c->f > c->f_shared ? c->f : c->f_shared) * c->d;
+  if (rows * width * elt_bytes >= lim || wmax * elt_bytes >= lim)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "shape too large for 32-bit buffer offsets: T*k rows x %lld columns and one expert's "
+                "2f x d weight must each stay below 2^31 bytes", (long long)width);
+  return MOE_OK;
+}
+
 // the bf16 GEMM path streams K-contiguous operands in 64-wide slices
 moe_status check_gemm_shapes(const moe_cfg* c) {
   if (c->dtype != MOE_F32 && (c->d % 64 || c->f % 64 || c->f_shared % 64))
     return fail(MOE_ERR_INVALID_ARGUMENT, "bf16 GEMMs need d, f and f_shared to be multiples of 64");
+  if (c->dtype != MOE_F32) return check_offsets_32bit(c, 2);
   return MOE_OK;
 }
 
@@ -127,7 +149,7 @@ moe_status check_mx_shapes(const moe_cfg* c) {
   if (c->dtype != MOE_MXFP8) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.dtype must be MOE_MXFP8");
   if (c->d % 128 || c->f % 128 || c->f_shared % 128)
     return fail(MOE_ERR_INVALID_ARGUMENT, "MXFP8 GEMMs need d, f and f_shared to be multiples of 128");
-  return MOE_OK;
+  return check_offsets_32bit(c, 2);               // bf16 operands and outputs beside the codes
 }
 
 #define REQ(p)                                                                          \
@@ -178,13 +200,38 @@ inline int64_t ranges(int64_t T) { return (T + kPermTokensPerRange - 1) / kPermT
 inline int64_t router_blocks(int64_t T) { return (T + kRouterTokensPerBlock - 1) / kRouterTokensPerBlock; }
 inline int64_t pad64(int64_t e) { return (e + 63) & ~int64_t(63); }
 inline size_t elt(const moe_cfg* c) { return c->dtype == MOE_F32 ? 4 : 2; }
+inline bool fold(const moe_cfg* c) { return (c->flags & MOE_FLAG_FOLD_GATES) != 0; }
+inline bool recompute(const moe_cfg* c) { return (c->flags & MOE_FLAG_RECOMPUTE_ACT) != 0; }
+
+// Workspace regions of the grouped-GEMM calls beyond their own first region
+// (the tile prefix, or the MXFP8 buffers): act formed again from hu_save
+// (recomputation; the routed experts' rows and later the shared expert's, so
+// one region of the larger size) and the folded gates' gradient partials.
+struct GemmExtra {
+  size_t act, dg, bytes;       // offsets from the region start, total size
+};
+GemmExtra gemm_extra(const moe_cfg* c, size_t at, bool bf16_gemms) {
+  GemmExtra w;
+  const int64_t rows = c->T * c->k;
+  size_t o = at;
+  w.act = o;
+  if (recompute(c)) {
+    const int64_t n = rows * c->f > c->T * c->f_shared ? rows * c->f : c->T * c->f_shared;
+    o += align256((size_t)n * elt(c));
+  }
+  w.dg = o;
+  if (fold(c)) o += align256((size_t)rows * gemm_dg_parts(bf16_gemms, (int)c->f) * 4);
+  w.bytes = o - at;
+  return w;
+}
 
 // MXFP8 workspace: two int arrays (tile prefix, padded offsets), one row-form
 // quantised activation (codes + scales) and two column-form ones
 struct MxWs {
   int64_t rows_max, cmax_rows, cmax_cols, rp_max;
   size_t ints, qa, qt;            // region sizes
-  size_t total() const { return ints + qa + 2 * qt; }
+  GemmExtra extra;                // recomputed act, gate-gradient partials (after the others)
+  size_t total() const { return ints + qa + 2 * qt + extra.bytes; }
 };
 inline int64_t pad128(int64_t v) { return (v + 127) / 128 * 128; }
 MxWs mx_ws(const moe_cfg* c) {
@@ -200,13 +247,15 @@ MxWs mx_ws(const moe_cfg* c) {
   w.ints = 2 * align256((size_t)(c->E + 2) * 4);
   w.qa = align256((size_t)(w.rows_max * w.cmax_rows)) + align256((size_t)(w.rows_max * w.cmax_rows / 32));
   w.qt = align256((size_t)(w.cmax_cols * w.rp_max)) + align256((size_t)(w.cmax_cols * w.rp_max / 32));
+  w.extra = gemm_extra(c, w.ints + w.qa + 2 * w.qt, true);
   return w;
 }
 
 size_t ws_bytes_for(const moe_cfg* c) {
   size_t router = 2 * align256((size_t)router_blocks(c->T) * c->E * 4);
   size_t perm = align256((size_t)ranges(c->T) * c->E * 4);
-  size_t gemm = align256((size_t)(c->E + 2) * 4);
+  const size_t prefix = align256((size_t)(c->E + 2) * 4);
+  size_t gemm = prefix + gemm_extra(c, prefix, c->dtype != MOE_F32).bytes;
   size_t rbwd = align256((size_t)c->T * pad64(c->E) * elt(c));
   size_t m = router;
   if (perm > m) m = perm;
@@ -230,6 +279,7 @@ RouterParams router_params(const moe_cfg* c) {
   p.T = (int)c->T; p.E = (int)c->E; p.k = (int)c->k; p.score = c->score;
   p.n_group = c->n_group; p.topk_group = c->topk_group; p.renorm = c->renorm;
   p.scale = c->scale; p.aux_coeff = c->aux_coeff;
+  p.balanced = (c->flags & MOE_FLAG_FORCE_BALANCED) ? 1 : 0;
   return p;
 }
 
@@ -251,21 +301,24 @@ moe_status router_topk_impl(const moe_cfg* c, const void* x, const void* w_route
 }
 
 template <class T>
-moe_status gemm_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off, const void* w13,
-                         const void* w2, void* hu, void* act, void* y_perm, const void* x,
+moe_status gemm_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off, const float* row_gates,
+                         const void* w13, const void* w2, void* hu, void* act, void* y_perm, const void* x,
                          const void* ws13, const void* ws2, void* hu_s, void* act_s, void* y_s,
                          void* ws, hipStream_t st) {
   const bool bf = sizeof(T) == 2;
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f;
+  const bool rc = recompute(c);
   int* prefix = (int*)ws;
   if (rows > 0) {
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E, true), prefix, st));
-    LAUNCH_NAMED("gemm_swiglu_fwd", gemm_swiglu_fwd<T>(x_perm, off, prefix, E, w13, hu, act, rows, d, f, st));
+    LAUNCH_NAMED("gemm_swiglu_fwd", gemm_swiglu_fwd<T>(x_perm, off, prefix, E, w13, hu, act, rows, d, f,
+                                                       fold(c) ? row_gates : nullptr, rc, st));
     LAUNCH_NAMED("gemm_down_fwd", gemm_down_fwd<T>(act, off, prefix, E, w2, y_perm, rows, d, f, st));
   }
   if (c->f_shared > 0 && c->T > 0) {
     const int fs = (int)c->f_shared, T_ = (int)c->T;
-    LAUNCH_NAMED("gemm_swiglu_fwd_shared", gemm_swiglu_fwd<T>(x, nullptr, nullptr, 1, ws13, hu_s, act_s, T_, d, fs, st));
+    LAUNCH_NAMED("gemm_swiglu_fwd_shared", gemm_swiglu_fwd<T>(x, nullptr, nullptr, 1, ws13, hu_s, act_s, T_, d, fs,
+                                                              nullptr, rc, st));
     LAUNCH_NAMED("gemm_down_fwd_shared", gemm_down_fwd<T>(act_s, nullptr, nullptr, 1, ws2, y_s, T_, d, fs, st));
   }
   return ok();
@@ -273,25 +326,36 @@ moe_status gemm_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* of
 
 template <class T>
 moe_status gemm_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm, const int32_t* off,
-                         const void* hu, const void* act, const void* w13, const void* w2, void* dhu,
-                         void* dx_perm, void* dw13, void* dw2, const void* dy, const void* x,
-                         const void* hu_s, const void* act_s, const void* ws13, const void* ws2,
-                         void* dhu_s, float* dx_partial, void* dws13, void* dws2, void* ws,
-                         hipStream_t st) {
+                         const float* row_gates, const int32_t* row_id_map, const void* hu, const void* act,
+                         const void* w13, const void* w2, void* dhu, void* dx_perm, void* dw13, void* dw2,
+                         float* d_gates, const void* dy, const void* x, const void* hu_s, const void* act_s,
+                         const void* ws13, const void* ws2, void* dhu_s, float* dx_partial, void* dws13,
+                         void* dws2, void* ws, hipStream_t st) {
   const bool bf = sizeof(T) == 2;
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
   int* prefix = (int*)ws;
+  const size_t prefix_bytes = align256((size_t)(c->E + 2) * 4);
+  const GemmExtra X = gemm_extra(c, prefix_bytes, bf);
+  // recomputation: the down-projection dgrad forms act again into the workspace
+  void* act_rec = recompute(c) ? (char*)ws + X.act : nullptr;
+  float* dg_part = fold(c) ? (float*)((char*)ws + X.dg) : nullptr;
+  const float* rg = fold(c) ? row_gates : nullptr;
   if (rows > 0) LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E, false), prefix, st));
   if (rows > 0)
-    LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd", gemm_down_dgrad_swiglu_bwd<T>(dy_perm, off, prefix, E, w2, hu, dhu, rows, d, f, st));
+    LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd", gemm_down_dgrad_swiglu_bwd<T>(dy_perm, off, prefix, E, w2, hu, dhu, rows, d, f,
+                                                                             rg, dg_part, act_rec, st));
+  if (rg && rows > 0)
+    LAUNCH_NAMED("gate_grad_sum", launch_gate_grad_sum(dg_part, gemm_dg_parts(bf, f), row_id_map, rows, d_gates, st));
   // weight gradients cover every expert (empty experts get zeros)
-  LAUNCH_NAMED("gemm_wgrad_down", gemm_wgrad<T>(dy_perm, d, act, f, off, E, 0, dw2, 1, st));
+  LAUNCH_NAMED("gemm_wgrad_down", gemm_wgrad<T>(dy_perm, d, act_rec ? act_rec : act, f, off, E, 0, dw2, 1, st));
   if (rows > 0) LAUNCH_NAMED("gemm_gateup_dgrad", gemm_gateup_dgrad<T>(dhu, off, prefix, E, w13, dx_perm, false, rows, d, f, st));
   LAUNCH_NAMED("gemm_wgrad_gateup", gemm_wgrad<T>(dhu, 2 * f, x_perm, d, off, E, 0, dw13, 0, st));
   if (c->f_shared > 0) {
     const int fs = (int)c->f_shared;
-    if (T_ > 0) LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd_shared", gemm_down_dgrad_swiglu_bwd<T>(dy, nullptr, nullptr, 1, ws2, hu_s, dhu_s, T_, d, fs, st));
-    LAUNCH_NAMED("gemm_wgrad_down_shared", gemm_wgrad<T>(dy, d, act_s, fs, nullptr, 1, T_, dws2, 3, st));
+    // (the routed experts are done with act_rec: the shared expert's act goes there)
+    if (T_ > 0) LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd_shared", gemm_down_dgrad_swiglu_bwd<T>(dy, nullptr, nullptr, 1, ws2, hu_s, dhu_s, T_, d, fs,
+                                                                                               nullptr, nullptr, act_rec, st));
+    LAUNCH_NAMED("gemm_wgrad_down_shared", gemm_wgrad<T>(dy, d, act_rec ? act_rec : act_s, fs, nullptr, 1, T_, dws2, 3, st));
     if (T_ > 0) LAUNCH_NAMED("gemm_gateup_dgrad_shared", gemm_gateup_dgrad<T>(dhu_s, nullptr, nullptr, 1, ws13, dx_partial, true, T_, d, fs, st));
     LAUNCH_NAMED("gemm_wgrad_gateup_shared", gemm_wgrad<T>(dhu_s, 2 * fs, x, d, nullptr, 1, T_, dws13, 2, st));
   } else {
@@ -324,6 +388,8 @@ struct MxBufs {
   int* poff;
   uint8_t *qa_c, *qa_s, *q1_c, *q1_s, *q2_c, *q2_s;
   int64_t rp_max;
+  void* act_rec;        // act formed again (recomputation) or NULL
+  float* dg_part;       // folded gates' gradient partials or NULL
 };
 MxBufs mx_bufs(const moe_cfg* c, void* ws) {
   const MxWs w = mx_ws(c);
@@ -341,21 +407,26 @@ MxBufs mx_bufs(const moe_cfg* c, void* ws) {
   b.q2_c = p;
   b.q2_s = p + align256((size_t)(w.cmax_cols * w.rp_max));
   b.rp_max = w.rp_max;
+  b.act_rec = recompute(c) ? (uint8_t*)ws + w.extra.act : nullptr;
+  b.dg_part = fold(c) ? (float*)((uint8_t*)ws + w.extra.dg) : nullptr;
   return b;
 }
 inline MxQ mxq(const uint8_t* c, const uint8_t* s) { return MxQ{c, s}; }
 inline MxQ mxq(const moe_mx_tensor& t) { return MxQ{t.codes, t.scales}; }
 
-moe_status mx_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off, const moe_mx_weights* w,
-                       void* hu, void* act, void* y_perm, const void* x, void* hu_s, void* act_s, void* y_s,
-                       void* ws, hipStream_t st) {
+moe_status mx_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off, const float* row_gates,
+                       const moe_mx_weights* w, void* hu, void* act, void* y_perm, const void* x, void* hu_s,
+                       void* act_s, void* y_s, void* ws, hipStream_t st) {
+  const bool rc = recompute(c);
+  const float* rg = fold(c) ? row_gates : nullptr;
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
   MxBufs b = mx_bufs(c, ws);
   const MxQ qa = mxq(b.qa_c, b.qa_s);
   if (rows > 0) {
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, st));
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
-    LAUNCH_NAMED("gemm_mx_swiglu_fwd", gemm_mx_swiglu_fwd(qa, off, b.prefix, E, mxq(w->w13), hu, act, rows, d, f, st));
+    LAUNCH_NAMED("gemm_mx_swiglu_fwd", gemm_mx_swiglu_fwd(qa, off, b.prefix, E, mxq(w->w13), hu, act, rows, d, f, rg, rc,
+                                                          st));
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act, f, 0, 1, rows, f, b.qa_c, b.qa_s, st));
     LAUNCH_NAMED("gemm_mx_down_fwd", gemm_mx_down_fwd(qa, off, b.prefix, E, mxq(w->w2), y_perm, rows, d, f, st));
   }
@@ -363,7 +434,7 @@ moe_status mx_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off,
     const int fs = (int)c->f_shared;
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x, d, 0, 1, T_, d, b.qa_c, b.qa_s, st));
     LAUNCH_NAMED("gemm_mx_swiglu_fwd_shared",
-                 gemm_mx_swiglu_fwd(qa, nullptr, nullptr, 1, mxq(w->ws13), hu_s, act_s, T_, d, fs, st));
+                 gemm_mx_swiglu_fwd(qa, nullptr, nullptr, 1, mxq(w->ws13), hu_s, act_s, T_, d, fs, nullptr, rc, st));
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act_s, fs, 0, 1, T_, fs, b.qa_c, b.qa_s, st));
     LAUNCH_NAMED("gemm_mx_down_fwd_shared",
                  gemm_mx_down_fwd(qa, nullptr, nullptr, 1, mxq(w->ws2), y_s, T_, d, fs, st));
@@ -372,18 +443,27 @@ moe_status mx_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off,
 }
 
 moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm, const int32_t* off,
-                       const void* hu, const void* act, const moe_mx_weights* w, void* dhu, void* dx_perm,
-                       void* dw13, void* dw2, const void* dy, const void* x, const void* hu_s, const void* act_s,
-                       void* dhu_s, float* dx_partial, void* dws13, void* dws2, void* ws, hipStream_t st) {
+                       const float* row_gates, const int32_t* row_id_map, const void* hu, const void* act,
+                       const moe_mx_weights* w, void* dhu, void* dx_perm, void* dw13, void* dw2, float* d_gates,
+                       const void* dy, const void* x, const void* hu_s, const void* act_s, void* dhu_s,
+                       float* dx_partial, void* dws13, void* dws2, void* ws, hipStream_t st) {
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
   MxBufs b = mx_bufs(c, ws);
+  const float* rg = fold(c) ? row_gates : nullptr;
+  if (b.act_rec) {                  // recomputation: the backward reads the act it forms again
+    act = b.act_rec;
+    act_s = b.act_rec;              // (the shared expert's, after the routed experts are done with it)
+  }
   const MxQ qa = mxq(b.qa_c, b.qa_s), q1 = mxq(b.q1_c, b.q1_s), q2 = mxq(b.q2_c, b.q2_s);
   const int rp = (int)b.rp_max;
   if (rows > 0) {
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, st));
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
     LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd",
-                 gemm_mx_down_dgrad_swiglu_bwd(qa, off, b.prefix, E, mxq(w->w2_t), hu, dhu, rows, d, f, st));
+                 gemm_mx_down_dgrad_swiglu_bwd(qa, off, b.prefix, E, mxq(w->w2_t), hu, dhu, rows, d, f, rg, b.dg_part,
+                                               b.act_rec, st));
+    if (rg)
+      LAUNCH_NAMED("gate_grad_sum", launch_gate_grad_sum(b.dg_part, gemm_dg_parts(true, f), row_id_map, rows, d_gates, st));
   }
   // weight gradients cover every expert: experts without rows get zeros
   LAUNCH_NAMED("padded_offsets", launch_padded_offsets(off, E, b.poff, st));
@@ -404,7 +484,8 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
     if (T_ > 0) {
       LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy, d, 0, 1, T_, d, b.qa_c, b.qa_s, st));
       LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd_shared",
-                   gemm_mx_down_dgrad_swiglu_bwd(qa, nullptr, nullptr, 1, mxq(w->ws2_t), hu_s, dhu_s, T_, d, fs, st));
+                   gemm_mx_down_dgrad_swiglu_bwd(qa, nullptr, nullptr, 1, mxq(w->ws2_t), hu_s, dhu_s, T_, d, fs, nullptr,
+                                                 nullptr, b.act_rec, st));
     }
     LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dy, d, T_, d, nullptr, nullptr, 1, tp, tp, b.q1_c, b.q1_s, st));
     LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(act_s, fs, T_, fs, nullptr, nullptr, 1, tp, tp, b.q2_c, b.q2_s, st));
@@ -516,11 +597,26 @@ moe_status moe_router_topk(const moe_cfg* cfg, const void* x, const void* w_rout
                                  aux_loss, workspace, st);
 }
 
-moe_status moe_permute(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, int32_t* expert_offsets,
-                       int32_t* row_id_map, int32_t* src_token, void* x_perm, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+moe_status moe_router_bias_update(const moe_cfg* cfg, const int32_t* expert_counts, float rate, float* bias,
+                                  void* stream) {
+  CHECK(check_cfg(cfg));
+  REQ(expert_counts); REQ(bias);
+  if (!(rate >= 0.0f && rate <= 3.0e38f)) return fail(MOE_ERR_INVALID_ARGUMENT, "rate must be finite and >= 0");
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  LAUNCH_NAMED("router_bias_update",
+               launch_router_bias_update(expert_counts, (int)cfg->E, cfg->T * cfg->k, rate, bias, st));
+  return ok();
+}
+
+moe_status moe_permute(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, const float* topk_gates,
+                       int32_t* expert_offsets, int32_t* row_id_map, int32_t* src_token, float* row_gates,
+                       void* x_perm, void* workspace, size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
   REQ(x); REQ(topk_idx); REQ(expert_offsets); REQ(row_id_map); REQ(src_token); REQ(x_perm);
+  if (fold(cfg)) { REQ(topk_gates); REQ(row_gates); }
+  if ((topk_gates == nullptr) != (row_gates == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "topk_gates and row_gates must both be given or both be NULL");
   ALIGNED(x); ALIGNED(x_perm);
   CHECK(check_ws(cfg, workspace, workspace_bytes));
   CHECK(check_current_device());
@@ -529,20 +625,22 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const int32_t* topk_id
   int* hist = (int*)workspace;
   LAUNCH_NAMED("perm_hist", launch_perm_hist(topk_idx, T_, k, E, hist, st));
   LAUNCH_NAMED("perm_scan", launch_perm_scan(hist, (int)ranges(T_), E, rows, expert_offsets, st));
-  LAUNCH_NAMED("perm_rank", launch_perm_rank(topk_idx, T_, k, E, hist, row_id_map, src_token, st));
+  LAUNCH_NAMED("perm_rank", launch_perm_rank(topk_idx, T_, k, E, hist, row_id_map, src_token, topk_gates, row_gates,
+                                             st));
   LAUNCH_NAMED("scatter_rows", launch_scatter_rows(x, row_id_map, T_, k, (int)(cfg->d * elt(cfg)), x_perm, st));
   return ok();
 }
 
 moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm, const int32_t* expert_offsets,
-                                   const void* w13, const void* w2, void* hu_save, void* act, void* y_perm,
-                                   const void* x, const void* ws13, const void* ws2, void* hu_shared_save,
-                                   void* act_shared, void* y_shared, void* workspace,
+                                   const float* row_gates, const void* w13, const void* w2, void* hu_save,
+                                   void* act, void* y_perm, const void* x, const void* ws13, const void* ws2,
+                                   void* hu_shared_save, void* act_shared, void* y_shared, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
   CHECK(check_not_mx(cfg));
   CHECK(check_gemm_shapes(cfg));
   REQ(x_perm); REQ(expert_offsets); REQ(w13); REQ(w2); REQ(act); REQ(y_perm);
+  if (fold(cfg)) REQ(row_gates);
   ALIGNED(x_perm); ALIGNED(w13); ALIGNED(w2); ALIGNED(hu_save); ALIGNED(act); ALIGNED(y_perm);
   if (cfg->f_shared > 0) {
     REQ(x); REQ(ws13); REQ(ws2); REQ(act_shared); REQ(y_shared);
@@ -552,20 +650,22 @@ moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm, const
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
   if (cfg->dtype != MOE_F32)
-    return gemm_fwd_impl<bf16>(cfg, x_perm, expert_offsets, w13, w2, hu_save, act, y_perm, x, ws13, ws2,
-                               hu_shared_save, act_shared, y_shared, workspace, st);
-  return gemm_fwd_impl<float>(cfg, x_perm, expert_offsets, w13, w2, hu_save, act, y_perm, x, ws13, ws2,
-                              hu_shared_save, act_shared, y_shared, workspace, st);
+    return gemm_fwd_impl<bf16>(cfg, x_perm, expert_offsets, row_gates, w13, w2, hu_save, act, y_perm, x, ws13,
+                               ws2, hu_shared_save, act_shared, y_shared, workspace, st);
+  return gemm_fwd_impl<float>(cfg, x_perm, expert_offsets, row_gates, w13, w2, hu_save, act, y_perm, x, ws13,
+                              ws2, hu_shared_save, act_shared, y_shared, workspace, st);
 }
 
 moe_status moe_unpermute_combine(const moe_cfg* cfg, const void* y_perm, const int32_t* row_id_map,
                                  const float* topk_gates, const void* y_shared, void* y, void* stream) {
   CHECK(check_cfg(cfg));
-  REQ(y_perm); REQ(row_id_map); REQ(topk_gates); REQ(y);
+  REQ(y_perm); REQ(row_id_map); REQ(y);
+  if (!fold(cfg)) REQ(topk_gates);
   ALIGNED(y_perm); ALIGNED(y_shared); ALIGNED(y);
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
   const int T_ = (int)cfg->T, k = (int)cfg->k, d = (int)cfg->d;
+  if (fold(cfg)) topk_gates = nullptr;      // the rows carry their gates: an unweighted sum
   if (cfg->dtype != MOE_F32)
     LAUNCH_NAMED("combine", launch_combine<bf16>((const bf16*)y_perm, row_id_map, topk_gates, (const bf16*)y_shared, (bf16*)y,
                                 T_, k, d, st));
@@ -579,8 +679,19 @@ moe_status moe_unpermute_combine_bwd(const moe_cfg* cfg, const void* dy, const v
                                      const int32_t* row_id_map, const float* topk_gates, void* dy_perm,
                                      float* d_gates, void* stream) {
   CHECK(check_cfg(cfg));
-  REQ(dy); REQ(y_perm); REQ(row_id_map); REQ(topk_gates); REQ(dy_perm); REQ(d_gates);
-  ALIGNED(dy); ALIGNED(y_perm); ALIGNED(dy_perm);
+  REQ(dy); REQ(row_id_map); REQ(dy_perm);
+  ALIGNED(dy); ALIGNED(dy_perm);
+  if (fold(cfg)) {
+    // the rows carry their gates: dy_perm[row(t,j)] = dy[t]; d_gates comes from
+    // the grouped-GEMM backward
+    CHECK(check_current_device());
+    hipStream_t st = (hipStream_t)stream;
+    LAUNCH_NAMED("scatter_rows", launch_scatter_rows(dy, row_id_map, (int)cfg->T, (int)cfg->k,
+                                                     (int)(cfg->d * elt(cfg)), dy_perm, st));
+    return ok();
+  }
+  REQ(y_perm); REQ(topk_gates); REQ(d_gates);
+  ALIGNED(y_perm);
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
   const int T_ = (int)cfg->T, k = (int)cfg->k, d = (int)cfg->d;
@@ -594,22 +705,26 @@ moe_status moe_unpermute_combine_bwd(const moe_cfg* cfg, const void* dy, const v
 }
 
 moe_status moe_grouped_gemm_swiglu_bwd(const moe_cfg* cfg, const void* dy_perm, const void* x_perm,
-                                       const int32_t* expert_offsets, const void* hu_save, const void* act,
+                                       const int32_t* expert_offsets, const float* row_gates,
+                                       const int32_t* row_id_map, const void* hu_save, const void* act,
                                        const void* w13, const void* w2, void* dhu, void* dx_perm, void* dw13,
-                                       void* dw2, const void* dy, const void* x, const void* hu_shared_save,
-                                       const void* act_shared, const void* ws13, const void* ws2,
-                                       void* dhu_shared, float* dx_partial, void* dws13, void* dws2,
-                                       void* workspace, size_t workspace_bytes, void* stream) {
+                                       void* dw2, float* d_gates, const void* dy, const void* x,
+                                       const void* hu_shared_save, const void* act_shared, const void* ws13,
+                                       const void* ws2, void* dhu_shared, float* dx_partial, void* dws13,
+                                       void* dws2, void* workspace, size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
   CHECK(check_not_mx(cfg));
   CHECK(check_gemm_shapes(cfg));
-  REQ(dy_perm); REQ(x_perm); REQ(expert_offsets); REQ(hu_save); REQ(act); REQ(w13); REQ(w2);
+  REQ(dy_perm); REQ(x_perm); REQ(expert_offsets); REQ(hu_save); REQ(w13); REQ(w2);
   REQ(dhu); REQ(dx_perm); REQ(dw13); REQ(dw2); REQ(dx_partial);
+  if (!recompute(cfg)) REQ(act);
+  if (fold(cfg)) { REQ(row_gates); REQ(row_id_map); REQ(d_gates); }
   ALIGNED(dy_perm); ALIGNED(x_perm); ALIGNED(hu_save); ALIGNED(act); ALIGNED(w13); ALIGNED(w2);
   ALIGNED(dhu); ALIGNED(dx_perm); ALIGNED(dw13); ALIGNED(dw2); ALIGNED(dx_partial);
   if (cfg->f_shared > 0) {
-    REQ(dy); REQ(x); REQ(hu_shared_save); REQ(act_shared); REQ(ws13); REQ(ws2); REQ(dhu_shared);
+    REQ(dy); REQ(x); REQ(hu_shared_save); REQ(ws13); REQ(ws2); REQ(dhu_shared);
     REQ(dws13); REQ(dws2);
+    if (!recompute(cfg)) REQ(act_shared);
     ALIGNED(dy); ALIGNED(x); ALIGNED(hu_shared_save); ALIGNED(act_shared); ALIGNED(ws13); ALIGNED(ws2);
     ALIGNED(dhu_shared); ALIGNED(dws13); ALIGNED(dws2);
   }
@@ -617,12 +732,12 @@ moe_status moe_grouped_gemm_swiglu_bwd(const moe_cfg* cfg, const void* dy_perm, 
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
   if (cfg->dtype != MOE_F32)
-    return gemm_bwd_impl<bf16>(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, w13, w2, dhu, dx_perm, dw13,
-                               dw2, dy, x, hu_shared_save, act_shared, ws13, ws2, dhu_shared, dx_partial,
-                               dws13, dws2, workspace, st);
-  return gemm_bwd_impl<float>(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, w13, w2, dhu, dx_perm, dw13,
-                              dw2, dy, x, hu_shared_save, act_shared, ws13, ws2, dhu_shared, dx_partial,
-                              dws13, dws2, workspace, st);
+    return gemm_bwd_impl<bf16>(cfg, dy_perm, x_perm, expert_offsets, row_gates, row_id_map, hu_save, act, w13, w2,
+                               dhu, dx_perm, dw13, dw2, d_gates, dy, x, hu_shared_save, act_shared, ws13, ws2,
+                               dhu_shared, dx_partial, dws13, dws2, workspace, st);
+  return gemm_bwd_impl<float>(cfg, dy_perm, x_perm, expert_offsets, row_gates, row_id_map, hu_save, act, w13, w2,
+                              dhu, dx_perm, dw13, dw2, d_gates, dy, x, hu_shared_save, act_shared, ws13, ws2,
+                              dhu_shared, dx_partial, dws13, dws2, workspace, st);
 }
 
 moe_status moe_router_topk_bwd(const moe_cfg* cfg, const void* x, const void* w_router, const float* logits,
@@ -687,12 +802,14 @@ moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int6
 }
 
 moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm, const int32_t* expert_offsets,
-                                         const moe_mx_weights* weights, void* hu_save, void* act, void* y_perm,
-                                         const void* x, void* hu_shared_save, void* act_shared, void* y_shared,
-                                         void* workspace, size_t workspace_bytes, void* stream) {
+                                         const float* row_gates, const moe_mx_weights* weights, void* hu_save,
+                                         void* act, void* y_perm, const void* x, void* hu_shared_save,
+                                         void* act_shared, void* y_shared, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
   CHECK(check_cfg(cfg));
   CHECK(check_mx_shapes(cfg));
   REQ(x_perm); REQ(expert_offsets); REQ(weights); REQ(act); REQ(y_perm);
+  if (fold(cfg)) REQ(row_gates);
   ALIGNED(x_perm); ALIGNED(hu_save); ALIGNED(act); ALIGNED(y_perm);
   CHECK(check_mx_tensor(weights->w13, "w13"));
   CHECK(check_mx_tensor(weights->w2, "w2"));
@@ -704,27 +821,31 @@ moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm,
   }
   CHECK(check_ws(cfg, workspace, workspace_bytes));
   CHECK(check_current_device());
-  return mx_fwd_impl(cfg, x_perm, expert_offsets, weights, hu_save, act, y_perm, x, hu_shared_save, act_shared,
-                     y_shared, workspace, (hipStream_t)stream);
+  return mx_fwd_impl(cfg, x_perm, expert_offsets, row_gates, weights, hu_save, act, y_perm, x, hu_shared_save,
+                     act_shared, y_shared, workspace, (hipStream_t)stream);
 }
 
 moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_perm, const void* x_perm,
-                                             const int32_t* expert_offsets, const void* hu_save, const void* act,
+                                             const int32_t* expert_offsets, const float* row_gates,
+                                             const int32_t* row_id_map, const void* hu_save, const void* act,
                                              const moe_mx_weights* weights, void* dhu, void* dx_perm, void* dw13,
-                                             void* dw2, const void* dy, const void* x, const void* hu_shared_save,
-                                             const void* act_shared, void* dhu_shared, float* dx_partial,
-                                             void* dws13, void* dws2, void* workspace, size_t workspace_bytes,
-                                             void* stream) {
+                                             void* dw2, float* d_gates, const void* dy, const void* x,
+                                             const void* hu_shared_save, const void* act_shared, void* dhu_shared,
+                                             float* dx_partial, void* dws13, void* dws2, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
   CHECK(check_mx_shapes(cfg));
-  REQ(dy_perm); REQ(x_perm); REQ(expert_offsets); REQ(hu_save); REQ(act); REQ(weights);
+  REQ(dy_perm); REQ(x_perm); REQ(expert_offsets); REQ(hu_save); REQ(weights);
   REQ(dhu); REQ(dx_perm); REQ(dw13); REQ(dw2); REQ(dx_partial);
+  if (!recompute(cfg)) REQ(act);
+  if (fold(cfg)) { REQ(row_gates); REQ(row_id_map); REQ(d_gates); }
   ALIGNED(dy_perm); ALIGNED(x_perm); ALIGNED(hu_save); ALIGNED(act); ALIGNED(dhu); ALIGNED(dx_perm);
   ALIGNED(dw13); ALIGNED(dw2); ALIGNED(dx_partial);
   CHECK(check_mx_tensor(weights->w13_t, "w13_t"));
   CHECK(check_mx_tensor(weights->w2_t, "w2_t"));
   if (cfg->f_shared > 0) {
-    REQ(dy); REQ(x); REQ(hu_shared_save); REQ(act_shared); REQ(dhu_shared); REQ(dws13); REQ(dws2);
+    REQ(dy); REQ(x); REQ(hu_shared_save); REQ(dhu_shared); REQ(dws13); REQ(dws2);
+    if (!recompute(cfg)) REQ(act_shared);
     ALIGNED(dy); ALIGNED(x); ALIGNED(hu_shared_save); ALIGNED(act_shared); ALIGNED(dhu_shared);
     ALIGNED(dws13); ALIGNED(dws2);
     CHECK(check_mx_tensor(weights->ws13_t, "ws13_t"));
@@ -732,8 +853,8 @@ moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_
   }
   CHECK(check_ws(cfg, workspace, workspace_bytes));
   CHECK(check_current_device());
-  return mx_bwd_impl(cfg, dy_perm, x_perm, expert_offsets, hu_save, act, weights, dhu, dx_perm, dw13, dw2, dy, x,
-                     hu_shared_save, act_shared, dhu_shared, dx_partial, dws13, dws2, workspace,
-                     (hipStream_t)stream);
+  return mx_bwd_impl(cfg, dy_perm, x_perm, expert_offsets, row_gates, row_id_map, hu_save, act, weights, dhu,
+                     dx_perm, dw13, dw2, d_gates, dy, x, hu_shared_save, act_shared, dhu_shared, dx_partial, dws13,
+                     dws2, workspace, (hipStream_t)stream);
 }
 }  // extern "C"

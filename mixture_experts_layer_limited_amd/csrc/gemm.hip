@@ -1,7 +1,5 @@
 // Grouped GEMM kernels: the bf16 MFMA path (gfx950 v_mfma_f32_32x32x16_bf16)
 // and a plain fp32 path, over the tile schedules of gemm.hpp.
-#include <stdlib.h>
-
 #include "gemm.hpp"
 #include "gemm_band.hpp"
 #include "gemm_mfma.hpp"
@@ -70,18 +68,29 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(GemmArgs a, typename E
     Epi::at_pair(ep, row, col, h, u);
   } else {
     const int col = c.n0 * 16 + tx;
-    if (col >= a.N) return;
     float s = 0.0f;
-    for (int k = c.k_begin; k < c.k_end; ++k) s += Ael(row, k) * Bel(col, k);
-    Epi::at(ep, c.g, row, col, s);
+    if (col < a.N)
+      for (int k = c.k_begin; k < c.k_end; ++k) s += Ael(row, k) * Bel(col, k);
+    if constexpr (Epi::kRowDot) {
+      // the row's 16 columns sit in 16 consecutive lanes: a fixed tree sums
+      // their terms into one partial per row and 16-column block
+      float dot = col < a.N ? Epi::at(ep, c.g, row, col, s) : 0.0f;
+      if (ep.dg_part) {
+        for (int o = 8; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 16);
+        if (tx == 0 && c.n0 < ep.dg_ld) ep.dg_part[(int64_t)row * ep.dg_ld + c.n0] = dot;
+      }
+    } else {
+      if (col < a.N) Epi::at(ep, c.g, row, col, s);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Launchers.  The bf16 path runs a persistent grid of 128x128 tiles with 2x2
-// waves; the fp32 path one 16x16 tile per workgroup.  For RAGGED_M the tile
-// count is only bounded on the host (sum over experts of ceil(n_e/BM) <=
-// rows/BM + G); the kernels read the exact count on the device.
+// Launchers.  The bf16 path runs the MFMA kernels (gemm_mfma.hpp,
+// gemm_band.hpp, gemm_regs.hpp); the fp32 path one 16x16 tile per workgroup.
+// For RAGGED_M the tile count is only bounded on the host (sum over experts
+// of ceil(n_e/BM) <= rows/BM + G); the kernels read the exact count on the
+// device.
 // ---------------------------------------------------------------------------
 
 static int device_cus() {
@@ -120,56 +129,14 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
   return hipGetLastError();
 }
 
-// Kernel of the bf16 path: 3 = register-staged 128x128, one tile per
-// workgroup (gemm_regs.hpp); 6 = the stationary-band weight-gradient kernel
-// (gemm_band.hpp; weight gradients only); 4 / 5 = its persistent pipelined form with
-// K-slices of 64 (two LDS stages) / 128 (one stage); DMA-fed LDS ring (gemm_mfma.hpp)
-// with 0 = 128x128 x 4 stages, 1 = 128x256 x 3 stages (2x4 waves of 64x64: two
-// waves per SIMD), 2 = 256x128 x 3 stages.
-// Defaults per contraction class, from measurements at the 256-expert,
-// d = 7168 shape: forward products and data gradients run on the 128x256
-// DMA ring (data gradients read their row-contiguous weight with transposing
-// LDS reads; 10% faster than the register-staged kernel since the ring's DMA
-// is issued as assembly, see dma_b128), weight gradients (short ragged
-// contractions) on the band kernel (experts of at most 320 rows) plus the
-// persistent pipelined kernel (larger experts).  MOE_TILE overrides the first two classes,
-// MOE_TILE_WGRAD the third (MOE_TILE alone sets all three); both are for
-// tuning runs.
-enum GemmClass { kForward = 0, kDgrad = 1, kWgrad = 2 };
-static int env_choice(const char* name, int dflt, int vmax) {
-  const char* e = getenv(name);
-  int v = e ? atoi(e) : dflt;
-  return (v < 0 || v > vmax) ? dflt : v;
-}
-static int tile_choice(GemmClass cls) {
-  static int v[3] = {-1, -1, -1};
-  if (v[0] < 0) {
-    const bool any = getenv("MOE_TILE") != nullptr;
-    v[0] = env_choice("MOE_TILE", 1, 5);
-    v[1] = env_choice("MOE_TILE", 1, 5);
-    v[2] = env_choice("MOE_TILE_WGRAD", any ? v[0] : 6, 6);
-  }
-  return v[cls];
-}
-
-template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
-static hipError_t launch_regs(const GemmArgs& a, const typename Epi::P& ep, int n_logical, int rows_total,
-                              hipStream_t st) {
-  using C = RegTile;
-  const int bn_cols = Epi::kPaired ? C::BN / 2 : C::BN;
-  const int NT = (n_logical + bn_cols - 1) / bn_cols;
-  const int MT = (MODE == RAGGED_M) ? 0 : (a.M + C::BM - 1) / C::BM;
-  int64_t grid;
-  if (MODE == RAGGED_M) grid = (int64_t)((rows_total + C::BM - 1) / C::BM + a.G) * NT;
-  else if (MODE == RAGGED_K) grid = (int64_t)a.G * MT * NT;
-  else grid = (int64_t)MT * NT;
-  if (grid <= 0) return hipSuccess;
-  auto kern = gemm_regs_kernel<LA, LB, MODE, Epi>;
-  static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
-  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
-  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, ep, NT, MT);
-  return hipGetLastError();
-}
+// Kernel per contraction class, from measurements at the 256-expert,
+// d = 7168 shape: forward products and data gradients run on the DMA ring
+// (128x256 tiles; 256x256 where experts are large, see big_tiles; data
+// gradients read their row-contiguous weight with transposing LDS reads),
+// expert weight gradients (short ragged contractions) on the band kernel for
+// experts of at most BandCfg::KMAX rows plus the persistent DMA ring for
+// larger ones, and the router's weight gradient on the persistent pipelined
+// kernel.
 
 template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi, int BK>
 static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int n_logical, int rows_total,
@@ -214,18 +181,16 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
   using C = BandCfg;
   // the band on the output's longer side: more, shorter units (measured at the
   // 256-expert, d = 7168 shape: the gate/up gradient, 4096 x 7168, with the
-  // band along its columns, the down gradient, 7168 x 2048, along its rows).
-  // MOE_BAND_P = 0 / 1 forces the column / row side (tuning runs).
-  static const int force = getenv("MOE_BAND_P") ? atoi(getenv("MOE_BAND_P")) : -1;
-  const bool pband = force == 0 ? false : force == 1 ? true : a.M > a.N;
+  // band along its columns, the down gradient, 7168 x 2048, along its rows)
+  const bool pband = a.M > a.N;
   auto kern = pband ? gemm_band_kernel<Epi, false> : gemm_band_kernel<Epi, true>;
   static bool lds_done[2][kLdsAttrDevices] = {};  // per device, per orientation
   if (hipError_t e = raise_lds_limit(lds_done[pband], (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   const int UB = pband ? a.M / C::BM : a.N / C::BN, TU = pband ? a.N / C::BN : a.M / C::BM;
   // each unit walks its tiles starting at its band index (mod the tile count),
   // so neighbouring units read different streamed tiles at any time (3% faster
-  // than all starting at tile 0); MOE_BAND_ROT changes the step (tuning runs)
-  static const int rot = getenv("MOE_BAND_ROT") ? atoi(getenv("MOE_BAND_ROT")) : 1;
+  // than all starting at tile 0)
+  constexpr int rot = 1;
   kern<<<(unsigned)device_cus(), C::NTHR, C::LDS_BYTES, st>>>(a, ep, UB, TU, rot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -246,16 +211,10 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
 static bool big_tiles(int64_t rows, int G) { return G > 0 && rows >= (int64_t)512 * G; }
 // The data gradients take the 256x256 tiles under the same rule (gate/up dgrad
 // on one box: Qwen3 2.06 -> 1.86 ms, Mixtral 2.54 -> 2.41, the EP share 2.23 ->
-// 1.87).  MOE_BIG_DGRAD=0 keeps them on 128-row tiles (tuning runs).
-static bool big_dgrad() {
-  static const bool v = !(getenv("MOE_BIG_DGRAD") && atoi(getenv("MOE_BIG_DGRAD")) == 0);
-  return v;
-}
-int gemm_tile_rows(bool bf16, int64_t rows, int G, bool forward) {
+// 1.87).
+int gemm_tile_rows(bool bf16, int64_t rows, int G, bool /*forward*/) {
   if (!bf16) return 16;
-  const int t = tile_choice(forward ? kForward : kDgrad);
-  if (t == 2 || (t == 1 && big_tiles(rows, G) && (forward || big_dgrad()))) return 256;
-  return 128;
+  return big_tiles(rows, G) ? 256 : 128;
 }
 
 template <class T, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
@@ -266,42 +225,31 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
     // weight gradients (short contractions) run persistent so that a tile's
     // stores overlap the next tile's loads; the rest one tile per workgroup
     const bool persistent = MODE == RAGGED_K;
-    int t = tile_choice(MODE == RAGGED_K ? kWgrad : LB == KC ? kForward : kDgrad);
-    if (t == 6) t = 1;          // weight gradients the band kernel does not take: the DMA ring
-    bool aligned = true;        // staged epilogues store 16-byte row pieces
+    // staged epilogues store 16-byte row pieces: the calls' shape checks (d, f,
+    // f_shared multiples of 64) and 16-byte aligned outputs guarantee them
     if constexpr (Epi::kStaged)
-      aligned = ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0;
-    if (t == 3 || !aligned) return launch_regs<LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st);
-    if (t >= 4) {
-      if (t == 5) return launch_pipe<LA, LB, MODE, Epi, 128>(a, ep, n_logical, rows_total, st);
-      return launch_pipe<LA, LB, MODE, Epi, 64>(a, ep, n_logical, rows_total, st);
+      if (!(ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0))
+        return hipErrorInvalidValue;
+    // dense products take 256x256 tiles only when those fill every CU: the
+    // shared expert's down-projection data gradient (4096 x 2048 outputs,
+    // 128 such tiles) runs 0.18 ms on 128x256 tiles against 0.25 ms
+    const int64_t big_count = (int64_t)((a.M + 255) / 256) *
+                              ((n_logical + (Epi::kPaired ? 127 : 255)) / (Epi::kPaired ? 128 : 256));
+    const bool dense_big = a.M >= 1024 && n_logical >= 1024 && big_count >= device_cus();
+    if constexpr (MODE != RAGGED_K) {
+      const bool big = MODE == RAGGED_M ? big_tiles(rows_total, a.G) : dense_big;
+      if (big)
+        return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+    } else {
+      // a weight gradient over one dense contraction of many rows (the
+      // shared expert's, K = tokens) is MFMA-bound: 256x256 tiles, one per
+      // workgroup, once they cover 7/8 of the CUs (gate/up 448 tiles: 0.35 ->
+      // 0.27 ms; down 224 tiles: 0.18 -> 0.14 ms against persistent 128x256)
+      if (a.offsets == nullptr && a.K >= 1024 && a.M >= 1024 && n_logical >= 1024 &&
+          big_count * 8 >= (int64_t)device_cus() * 7)
+        return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, false);
     }
-    if (t == 1) {
-      // dense products take 256x256 tiles only when those fill every CU: the
-      // shared expert's down-projection data gradient (4096 x 2048 outputs,
-      // 128 such tiles) runs 0.18 ms on 128x256 tiles against 0.25 ms
-      const int64_t big_count = (int64_t)((a.M + 255) / 256) *
-                                ((n_logical + (Epi::kPaired ? 127 : 255)) / (Epi::kPaired ? 128 : 256));
-      const bool dense_big = a.M >= 1024 && n_logical >= 1024 && big_count >= device_cus();
-      if constexpr (MODE != RAGGED_K) {
-        const bool big = (LB == KC || big_dgrad()) &&
-                         (MODE == RAGGED_M ? big_tiles(rows_total, a.G) : dense_big);
-        if (big)
-          return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
-      } else {
-        // a weight gradient over one dense contraction of many rows (the
-        // shared expert's, K = tokens) is MFMA-bound: 256x256 tiles, one per
-        // workgroup, once they cover 7/8 of the CUs (gate/up 448 tiles: 0.35 ->
-        // 0.27 ms; down 224 tiles: 0.18 -> 0.14 ms against persistent 128x256)
-        if (a.offsets == nullptr && a.K >= 1024 && a.M >= 1024 && n_logical >= 1024 &&
-            big_count * 8 >= (int64_t)device_cus() * 7)
-          return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, false);
-      }
-      return launch_mfma<128, 256, 2, 4, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
-    }
-    if (t == 2)
-      return launch_mfma<256, 128, 2, 2, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
-    return launch_mfma<128, 128, 2, 2, 4, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+    return launch_mfma<128, 256, 2, 4, 3, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
   } else {
     const int NT = (n_logical + 15) / 16;
     const int MT = (MODE == RAGGED_M) ? 0 : (a.M + 15) / 16;
@@ -341,11 +289,11 @@ hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int
 template <class T>
 hipError_t gemm_swiglu_fwd(const void* xin, const int* offsets, const int* tile_prefix, int G,
                            const void* w13, void* hu, void* act, int rows, int d, int f,
-                           hipStream_t st) {
+                           const float* row_gates, bool from_stored, hipStream_t st) {
   GemmArgs a{};
   a.A = xin; a.lda = d; a.B = w13; a.ldb = d; a.b_gstride = (int64_t)2 * f * d;
   a.M = rows; a.N = 2 * f; a.K = d; a.b_next = 2 * f; a.b_kend = d;
-  typename EpiSwiGLU<T>::P ep{(T*)act, (T*)hu, f};
+  typename EpiSwiGLU<T>::P ep{(T*)act, (T*)hu, f, row_gates, from_stored ? 1 : 0};
   if (offsets) {
     a.offsets = offsets; a.tile_prefix = tile_prefix; a.G = G;
     return run_gemm<T, KC, KC, RAGGED_M, EpiSwiGLU<T>>(a, ep, rows, st);
@@ -369,15 +317,42 @@ hipError_t gemm_down_fwd(const void* act, const int* offsets, const int* tile_pr
   return run_gemm<T, KC, KC, DENSE, EpiStore<T>>(a, ep, rows, st);
 }
 
-// dA = dY W2 (B = W2 [d, f] read as (n=f-col, k=d-row): MC), SwiGLU backward epilogue
+// Gate-gradient partials per row of the down-projection data gradient: one
+// per 64-column block on the MFMA path, per 16-column block on the fp32 one.
+int gemm_dg_parts(bool bf16, int f) { return bf16 ? (f + 63) / 64 : (f + 15) / 16; }
+
+// d_gates[n] = sum over p < P, in order, of part[row_id_map[n] * P + p]
+__global__ __launch_bounds__(256) void gate_grad_sum_kernel(const float* __restrict__ part, int P,
+                                                            const int32_t* __restrict__ row_id_map,
+                                                            int64_t n_total, float* __restrict__ d_gates) {
+  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= n_total) return;
+  const float* q = part + (int64_t)row_id_map[n] * P;
+  float s = 0.0f;
+  for (int i = 0; i < P; ++i) s += q[i];
+  d_gates[n] = s;
+}
+
+hipError_t launch_gate_grad_sum(const float* part, int P, const int32_t* row_id_map, int64_t n_total,
+                                float* d_gates, hipStream_t st) {
+  if (n_total == 0) return hipSuccess;
+  gate_grad_sum_kernel<<<(unsigned)((n_total + 255) / 256), 256, 0, st>>>(part, P, row_id_map, n_total, d_gates);
+  return hipGetLastError();
+}
+
+// dA = dY W2 (B = W2 [d, f] read as (n=f-col, k=d-row): MC), SwiGLU backward
+// epilogue (folded gates: row_gates with the gate-gradient partials dg_part
+// [rows, gemm_dg_parts]; act recomputation: act_out)
 template <class T>
 hipError_t gemm_down_dgrad_swiglu_bwd(const void* dy, const int* offsets, const int* tile_prefix,
                                       int G, const void* w2, const void* hu, void* dhu, int rows,
-                                      int d, int f, hipStream_t st) {
+                                      int d, int f, const float* row_gates, float* dg_part, void* act_out,
+                                      hipStream_t st) {
   GemmArgs a{};
   a.A = dy; a.lda = d; a.B = w2; a.ldb = f; a.b_gstride = (int64_t)d * f;
   a.M = rows; a.N = f; a.K = d; a.b_next = f; a.b_kend = d;
-  typename EpiSwiGLUBwd<T>::P ep{(const T*)hu, (T*)dhu, f};
+  typename EpiSwiGLUBwd<T>::P ep{(const T*)hu, (T*)dhu, f, row_gates, row_gates ? dg_part : nullptr,
+                                 gemm_dg_parts(sizeof(T) == 2, f), (T*)act_out};
   if (offsets) {
     a.offsets = offsets; a.tile_prefix = tile_prefix; a.G = G;
     return run_gemm<T, KC, MC, RAGGED_M, EpiSwiGLUBwd<T>>(a, ep, rows, st);
@@ -419,8 +394,7 @@ template <class T, int kSite>
 static hipError_t wgrad_site(const GemmArgs& a, void* dw, int M, int N, hipStream_t st) {
   typename EpiStore<T, kSite>::P ep{(T*)dw, N, (int64_t)M * N, M, N};
   if constexpr (sizeof(T) == 2)
-    if (tile_choice(kWgrad) == 6 && band_fits<EpiStore<T, kSite>>(a, ep))
-      return launch_band<EpiStore<T, kSite>>(a, ep, st);
+    if (band_fits<EpiStore<T, kSite>>(a, ep)) return launch_band<EpiStore<T, kSite>>(a, ep, st);
   return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T, kSite>>(a, ep, 0, st);
 }
 
@@ -458,7 +432,7 @@ hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T
   // few and mostly padding: 4 experts, 32768 tokens, d = 7168 took 0.29 ms on
   // the ring, 0.16 here; 256 experts, 4096 tokens 0.081 and 0.070)
   if constexpr (sizeof(T) == 2)
-    if (tile_choice(kWgrad) == 6 && d % 8 == 0 && ((uintptr_t)dw_r & 15) == 0)
+    if (d % 8 == 0 && ((uintptr_t)dw_r & 15) == 0)
       return launch_pipe<MC, MC, RAGGED_K, EpiStore<T, 4>, 64>(a, ep, d, 0, st);
   return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T, 4>>(a, ep, 0, st);
 }
@@ -478,12 +452,14 @@ hipError_t gemm_router_dgrad(const void* dl, int Ep, int E, const void* w_r, int
   template hipError_t gemm_router_logits<T>(const void*, const void*, float*, int, int, int,     \
                                             hipStream_t);                                        \
   template hipError_t gemm_swiglu_fwd<T>(const void*, const int*, const int*, int, const void*,  \
-                                         void*, void*, int, int, int, hipStream_t);              \
+                                         void*, void*, int, int, int, const float*, bool,        \
+                                         hipStream_t);                                           \
   template hipError_t gemm_down_fwd<T>(const void*, const int*, const int*, int, const void*,    \
                                        void*, int, int, int, hipStream_t);                       \
   template hipError_t gemm_down_dgrad_swiglu_bwd<T>(const void*, const int*, const int*, int,    \
                                                     const void*, const void*, void*, int, int,   \
-                                                    int, hipStream_t);                           \
+                                                    int, const float*, float*, void*,            \
+                                                    hipStream_t);                                \
   template hipError_t gemm_gateup_dgrad<T>(const void*, const int*, const int*, int,             \
                                            const void*, void*, bool, int, int, int,              \
                                            hipStream_t);                                         \

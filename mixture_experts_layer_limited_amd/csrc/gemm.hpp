@@ -136,7 +136,17 @@ __device__ __forceinline__ int xcd_run_start(const GemmArgs& a, const int* off, 
   return lo * P + (int)(in < P ? in : P);
 }
 
-// Scales of MXFP8 operands (e8m0 bytes, one per 32 K values, K/32 per row)
+// Scales of MXFP8 operands (e8m0 bytes, one per 32 K values, K/32 per row).
+//
+// Operand layout of the scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (32 rows
+// x 64 K per step, 32 bytes per lane), as a probe on the GPU fixed it: lane l
+// (h = l / 32) holds row l % 32, bytes 0-15 = 16 K values of the step's first
+// 32-block and bytes 16-31 = 16 K values of its second; lanes l and l + 32
+// together cover each block.  With a 128-value slice as eight 16-byte chunks
+// per row, lane half h takes chunks 4 s + h and 4 s + 2 + h in step s.  The
+// scale of (row, block b) comes from lane row + 32 b, so each lane passes the
+// scale of block h of its own row; a row's scale word holds the slice's four
+// block scales, shifted by 8 h per lane, and op_sel picks byte 2 s for step s.
 struct MxArgs {
   const uint8_t* A_s;      // A scales [..][K/32]
   const uint8_t* B_s;      // B scales (per group: + g * b_s_gstride)
@@ -309,6 +319,7 @@ template <class T, int kSite = 0>
 struct EpiStore {                       // C[row, col] = storage(v)
   struct P { T* C; int64_t ldc; int64_t c_gstride; int M; int N; };
   static constexpr bool kPaired = false;
+  static constexpr bool kRowDot = false;
   // 2-byte outputs may be staged through LDS and stored 8 columns at a time
   static constexpr bool kStaged = sizeof(T) == 2;
   __device__ static void store8(const P& p, int g, int row, int col, u32x4 v) {
@@ -337,6 +348,7 @@ template <int kUnused>
 struct EpiStoreF32T {                   // C[row, col] = v   (fp32 output)
   struct P { float* C; int64_t ldc; int64_t c_gstride; int M; int N; };
   static constexpr bool kPaired = false;
+  static constexpr bool kRowDot = false;
   static constexpr bool kStaged = false;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void at(const P& p, int g, int row, int col, float v) {
@@ -356,6 +368,7 @@ template <int kUnused>
 struct EpiAccumF32T {                   // C[row, col] += v  (fp32, one writer per element)
   struct P { float* C; int64_t ldc; int64_t c_gstride; int M; int N; };
   static constexpr bool kPaired = false;
+  static constexpr bool kRowDot = false;
   static constexpr bool kStaged = false;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void at(const P& p, int g, int row, int col, float v) {
@@ -382,14 +395,31 @@ struct EpiAccumF32T {                   // C[row, col] += v  (fp32, one writer p
 using EpiStoreF32 = EpiStoreF32T<0>;
 using EpiAccumF32 = EpiAccumF32T<0>;
 
+// SwiGLU output of one element: silu(h) * u, times the row's gate g when gates
+// are folded.  The forward (with act formed from the stored H, U) and the
+// backward that forms act again both go through this one function, so the two
+// are the same instructions on the same inputs and agree bit for bit.
+__device__ __forceinline__ float swiglu_act(float h, float u, float g) { return g * (h / (1.0f + expf(-h)) * u); }
+
+// value of v after a round trip through storage type T (identity for fp32)
+template <class T>
+__device__ __forceinline__ float through(float v) { return to_f32(from_f32<T>(v)); }
+
 // SwiGLU forward.  In the MFMA kernel each wave's B rows hold its gate
 // columns followed by the matching up columns, so one lane holds H and U of
 // the same (row, col).  The fp32 kernel reads gate row col and up row f+col.
+// row_gates (folded gates, [rows] fp32) multiplies act; from_stored forms act
+// from H and U as stored (rounded to T) rather than from the fp32 results.
 template <class T>
 struct EpiSwiGLU {
-  struct P { T* act; T* hu; int64_t f; };  // act [rows, f], hu [rows, 2f] or NULL
+  struct P {
+    T* act; T* hu; int64_t f;             // act [rows, f], hu [rows, 2f] or NULL
+    const float* row_gates = nullptr;     // gate of each row (folded gates) or NULL
+    int from_stored = 0;
+  };
   static constexpr bool kPaired = true;
   static constexpr bool kStaged = false;
+  static constexpr bool kRowDot = false;
   // tile-row r of a BN-row tile split over WN waves: wave part w = r / (BN/WN);
   // its first half are gate rows, its second half the matching up rows
   template <int BN, int WN>
@@ -400,11 +430,14 @@ struct EpiSwiGLU {
     if (col >= p.f) return 1 << 30;
     return o >= HALF ? (int)p.f + col : col;
   }
-  __device__ static void act_of(float h, float u, float& a) { a = h / (1.0f + expf(-h)) * u; }
+  __device__ static float act_of(const P& p, float h, float u, float g) {
+    if (p.from_stored) return swiglu_act(through<T>(h), through<T>(u), g);
+    return swiglu_act(h, u, g);
+  }
+  __device__ static float gate_of(const P& p, int row) { return p.row_gates ? p.row_gates[row] : 1.0f; }
   __device__ static void at_pair(const P& p, int row, int col, float h, float u) {
     if (col >= p.f) return;
-    float a;
-    act_of(h, u, a);
+    const float a = act_of(p, h, u, gate_of(p, row));
     p.act[(int64_t)row * p.f + col] = from_f32<T>(a);
     if (p.hu) {
       p.hu[(int64_t)row * 2 * p.f + col] = from_f32<T>(h);
@@ -417,8 +450,9 @@ struct EpiSwiGLU {
       return;
     }
     float a[4];
+    const float g = gate_of(p, row);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) act_of(h[i], u[i], a[i]);
+    for (int i = 0; i < 4; ++i) a[i] = act_of(p, h[i], u[i], g);
     const bool vec = (p.f & 3) == 0;
     store4<T>(p.act + (int64_t)row * p.f + col, a, vec);
     if (p.hu) {
@@ -428,39 +462,71 @@ struct EpiSwiGLU {
   }
 };
 
-// SwiGLU backward inside the down-projection dgrad: v = dA[row, col]
+// SwiGLU backward inside the down-projection dgrad: v = dA[row, col].
+// Folded gates (row_gates): the product gives dA of g*act, so the row's gate
+// gradient gets the term dA * silu(h) u (returned by at / at4, summed by the
+// kernel over each 64-column block of the row into dg_part) and dH, dU use
+// g * dA.  act_out (act formed again from the stored H, U, times g) is written
+// when the backward recomputes act.
 template <class T>
 struct EpiSwiGLUBwd {
-  struct P { const T* hu; T* dhu; int64_t f; };
+  struct P {
+    const T* hu; T* dhu; int64_t f;
+    const float* row_gates = nullptr;     // folded gates [rows] or NULL
+    float* dg_part = nullptr;             // [rows, dg_ld] gate-gradient partials (with row_gates)
+    int dg_ld = 0;
+    T* act_out = nullptr;                 // [rows, f] act formed again, or NULL
+  };
   static constexpr bool kPaired = false;
   static constexpr bool kStaged = false;
+  static constexpr bool kRowDot = true;   // the kernels reduce at's return value when dg_part is set
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void grad(float dA, float h, float u, float& dh, float& du) {
     float sg = 1.0f / (1.0f + expf(-h));
     dh = dA * u * sg * (1.0f + h * (1.0f - sg));
     du = dA * h * sg;
   }
-  __device__ static void at(const P& p, int, int row, int col, float dA) {
-    if (col >= p.f) return;
+  __device__ static float at(const P& p, int, int row, int col, float dA) {
+    if (col >= p.f) return 0.0f;
     int64_t base = (int64_t)row * 2 * p.f;
+    const float h = to_f32(p.hu[base + col]), u = to_f32(p.hu[base + p.f + col]);
+    const float g = p.row_gates ? p.row_gates[row] : 1.0f;
+    float dot = 0.0f;
+    if (p.row_gates) dot = dA * swiglu_act(h, u, 1.0f);
+    if (p.act_out) p.act_out[(int64_t)row * p.f + col] = from_f32<T>(swiglu_act(h, u, g));
     float dh, du;
-    grad(dA, to_f32(p.hu[base + col]), to_f32(p.hu[base + p.f + col]), dh, du);
+    grad(g * dA, h, u, dh, du);
     p.dhu[base + col] = from_f32<T>(dh);
     p.dhu[base + p.f + col] = from_f32<T>(du);
+    return dot;
   }
-  __device__ static void at4(const P& p, int g, int row, int col, const float v[4]) {
+  __device__ static float at4(const P& p, int g_, int row, int col, const float v[4]) {
     if (col + 4 > p.f || (p.f & 3) != 0) {
-      for (int i = 0; i < 4; ++i) at(p, g, row, col + i, v[i]);
-      return;
+      float dot = 0.0f;
+      for (int i = 0; i < 4; ++i) dot += at(p, g_, row, col + i, v[i]);
+      return dot;
     }
     int64_t base = (int64_t)row * 2 * p.f;
     float h[4], u[4], dh[4], du[4];
     load4<T>(p.hu + base + col, h);
     load4<T>(p.hu + base + p.f + col, u);
+    const float g = p.row_gates ? p.row_gates[row] : 1.0f;
+    float dot = 0.0f;
+    if (p.row_gates) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) grad(v[i], h[i], u[i], dh[i], du[i]);
+      for (int i = 0; i < 4; ++i) dot += v[i] * swiglu_act(h[i], u[i], 1.0f);
+    }
+    if (p.act_out) {
+      float a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = swiglu_act(h[i], u[i], g);
+      store4<T>(p.act_out + (int64_t)row * p.f + col, a, true);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) grad(g * v[i], h[i], u[i], dh[i], du[i]);
     store4<T>(p.dhu + base + col, dh, true);
     store4<T>(p.dhu + base + p.f + col, du, true);
+    return dot;
   }
 };
 

@@ -238,8 +238,8 @@ struct SliceIter {
 };
 
 // MX = true: both operands K-contiguous fp8 e4m3 codes with e8m0 scales (`s`),
-// multiplied with v_mfma_scale_f32_32x32x64_f8f6f4 (operand layout as in
-// gemm_mx.hpp); GemmArgs then count K, lda, ldb in 2-byte units, so a slice of
+// multiplied with v_mfma_scale_f32_32x32x64_f8f6f4 (operand layout at
+// MxArgs in gemm.hpp); GemmArgs then count K, lda, ldb in 2-byte units, so a slice of
 // BK = 64 units is 128 fp8 values and the data path is the bf16 one.
 template <int BM, int BN, int WM, int WN, int STAGES, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi,
           bool MX = false>
@@ -434,12 +434,41 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
     }
   };
 
-  // epilogue: row = lane%32 of the block, columns 8*(e/4) + 4*(lane/32) + 0..3
+  // epilogue: row = lane%32 of the block, columns 8*(e/4) + 4*(lane/32) + 0..3.
+  // Epilogues with a row reduction (kRowDot: the folded-gate gradient) return
+  // a term per 4-column vector; a row's terms over the wave's 64 columns are
+  // summed in a fixed order (j, q, then the lane pair l, l + 32) into one
+  // partial per row and 64-column block.
+  static_assert(!Epi::kRowDot || BN / WN == 64, "row partials cover 64 columns per wave");
   auto epilogue = [&](const TileCoord& c) {
     const int nt = c.n0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = c.m0 + wm * (BM / WM) + i * 32 + (lane & 31);
+      if constexpr (Epi::kRowDot) {
+        float dot = 0.0f;
+        if (row < c.m_end) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int col = nt * BN + wn * (BN / WN) + j * 32 + q * 8 + (lane >> 5) * 4;
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+              dot += Epi::at4(ep, c.g, row, col, v);
+            }
+          }
+        }
+        if (ep.dg_part) {                       // uniform: every lane reaches the shuffle
+          dot += __shfl_xor(dot, 32, 64);
+          // a tile wider than the rest of the row leaves blocks past its end
+          // (dg_ld blocks per row) to no one
+          const int blk = (nt * BN + wn * (BN / WN)) / 64;
+          if (row < c.m_end && lane < 32 && blk < ep.dg_ld) ep.dg_part[(int64_t)row * ep.dg_ld + blk] = dot;
+        }
+        continue;
+      }
       if (row >= c.m_end) continue;
       if constexpr (Epi::kPaired) {
 #pragma unroll

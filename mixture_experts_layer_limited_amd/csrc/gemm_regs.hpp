@@ -1,27 +1,21 @@
-// bf16 MFMA grouped-GEMM kernel for gfx950, register-staged variant (selected
-// by MOE_TILE=3; its persistent form below runs the MXFP8 weight gradients and
-// the router's weight gradient).
+// bf16 / MXFP8 MFMA grouped-GEMM kernel for gfx950, persistent and
+// register-pipelined: it runs the router's weight gradient and the MXFP8
+// weight gradients.
 //
-// One tile per workgroup (the grid covers every logical tile; surplus
-// workgroups of the ragged schedule exit at once), 256 threads in 2x2 waves,
-// each wave owning 64x64 of a 128x128 tile as 2x2 blocks of 32x32
-// accumulators (v_mfma_f32_32x32x16_bf16), BK = 64.  Global loads of slice
-// k+1 go to registers while slice k is multiplied from LDS.  One LDS stage
-// (32 KB) and registers capped at 168 per lane let three workgroups share a
-// CU, so more slices are in flight per CU; the stage costs a second barrier
-// per slice (every wave done reading it before slice k+1 is written).  Every LDS row holds 64 bf16 = eight 16-byte chunks,
-// K-contiguous, chunk c of row r at position c ^ ((r ^ (r >> 3)) & 7): the
-// fragment reads (16 consecutive rows per cycle on gfx950's 64 banks), the
-// 16-byte K-contiguous writes and the 8-byte transposed writes of
-// row-contiguous operands all stay free of bank conflicts.  Row-contiguous
-// operands ("MC": the weight in dgrad, both operands in wgrad) are loaded as
-// 4 K-rows x 8 columns per thread and transposed in registers on the way in.
+// The grid holds two workgroups per CU (256 threads in 2x2 waves, each wave
+// owning 64x64 of a 128x128 tile as 2x2 blocks of 32x32 accumulators,
+// v_mfma_f32_32x32x16_bf16 or, for MXFP8, v_mfma_scale_f32_32x32x64_f8f6f4).
+// Global loads of slice k+1 go to registers while slice k is multiplied from
+// LDS.  K-contiguous operand rows hold 64 bf16 = eight 16-byte chunks, chunk c
+// of row r at position c ^ ((r ^ (r >> 3)) & 7): fragment reads (16
+// consecutive rows per cycle on gfx950's 64 banks) and 16-byte writes stay
+// free of bank conflicts.  Row-contiguous operands ("MC": both operands of a
+// weight gradient) are kept in LDS as they lie in memory and read with
+// transposing LDS reads (McFrag).
 //
-// Logical tiles are spread with xcd_remap over their exact count, so each XCD
-// receives a contiguous run of the expert-major tile order.  The MFMA takes the
-// B fragment first, so a lane's accumulator holds four consecutive output
-// columns (element e of a block: column 8*(e/4) + 4*(lane/32) + e%4, row
-// lane%32) and the epilogue stores 4-column vectors.
+// The MFMA takes the B fragment first, so a lane's accumulator holds four
+// consecutive output columns (element e of a block: column 8*(e/4) +
+// 4*(lane/32) + e%4, row lane%32) and the epilogue stores 4-column vectors.
 #pragma once
 
 #include <type_traits>
@@ -33,17 +27,6 @@ namespace moe {
 // rows of CH 16-byte chunks: chunk c of row r sits at c ^ ((r ^ (r >> 3)) & (CH - 1))
 template <int CH>
 __device__ __forceinline__ int rswz_t(int row, int c) { return row * CH + (c ^ ((row ^ (row >> 3)) & (CH - 1))); }
-__device__ __forceinline__ int rswz(int row, int c) { return rswz_t<8>(row, c); }
-
-struct RegTile {
-  static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, BK = 64;
-  static constexpr int NTHR = 256;
-  static constexpr int FM = 2, FN = 2;
-  static constexpr int STAGE = (BM + BN) * 8;              // 16-byte chunks per stage
-  static constexpr int LDS_BYTES = STAGE * 16;             // one stage
-};
-// the one-tile MXFP8 kernel keeps two stages of the same shape
-constexpr int kMxTileLdsBytes = 2 * RegTile::STAGE * 16;
 
 // Global -> register -> LDS staging of one operand slice: ROWS tile rows x BK
 // K values (CH = BK / 8 chunks per LDS row).  KC operands load 16 K values of
@@ -166,121 +149,8 @@ struct McLoader {
   }
 };
 
-template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void gemm_regs_kernel(GemmArgs a, typename Epi::P ep, int NT, int MT) {
-  using C = RegTile;
-  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, BK = C::BK, NTHR = C::NTHR;
-  constexpr int FM = C::FM, FN = C::FN;
-  extern __shared__ u32x4 smem[];
-
-  const int total = total_tiles<MODE>(a, NT, MT);
-  if ((int)blockIdx.x >= total) return;
-  TileCoord c;
-  resolve_tile<MODE, BM>(a, xcd_remap(blockIdx.x, total), NT, MT, c);
-  if (c.m0 >= c.m_end) return;              // only a mismatched tile prefix could produce this
-  const int nt = c.n0;
-
-  const uint16_t* __restrict__ A = (const uint16_t*)a.A;
-  const uint16_t* __restrict__ B = (const uint16_t*)a.B + (MODE == RAGGED_M ? (int64_t)c.g * a.b_gstride : 0);
-  const int b_kend = (MODE == RAGGED_K) ? c.k_end : min(c.k_end, a.b_kend);
-
-  RegLoader<LA, BM, NTHR> la;
-  RegLoader<LB, BN, NTHR> lb;
-  auto a_row = [&](int r) -> int { int g = c.m0 + r; return g < c.m_end ? g : -1; };
-  auto b_row = [&](int r) -> int {
-    int g;
-    if constexpr (Epi::kPaired) g = Epi::template b_row_paired<BN, WN>(ep, nt, r);
-    else g = nt * BN + r;
-    return g < a.b_next ? g : -1;
-  };
-  auto load = [&](int k0) {
-    if (LA == KC) la.load_kc(A, a.lda, k0, c.k_end, a_row);
-    else la.load_mc(A, a.lda, k0, c.k_end, c.m0, a.a_mext);
-    if (LB == KC) lb.load_kc(B, a.ldb, k0, c.k_end, b_row);
-    else lb.load_mc(B, a.ldb, k0, b_kend, nt * BN, a.b_next);
-  };
-  auto store = [&](int buf) {
-    u32x4* s = smem + buf * C::STAGE;
-    la.store(s);
-    lb.store(s + BM * 8);
-  };
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  floatx16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  const int nk = (c.k_end - c.k_begin + BK - 1) / BK;
-  if (nk > 0) {
-    load(c.k_begin);
-    store(0);
-  }
-  __syncthreads();
-  const int arow0 = wm * (BM / WM) + (lane & 31);
-  const int brow0 = wn * (BN / WN) + (lane & 31);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load(c.k_begin + (kt + 1) * BK);
-    const bf16x8* sa = (const bf16x8*)smem;
-    const bf16x8* sb = sa + BM * 8;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + (lane >> 5);
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = sa[rswz(arow0 + i * 32, ch)];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = sb[rswz(brow0 + j * 32, ch)];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      __syncthreads();                  // every wave has read slice k
-      store(0);
-    }
-    __syncthreads();
-  }
-
-  // epilogue: row = lane%32 of the block, columns 8*(e/4) + 4*(lane/32) + 0..3
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int row = c.m0 + wm * (BM / WM) + i * 32 + (lane & 31);
-    if (row >= c.m_end) continue;
-    if constexpr (Epi::kPaired) {
-#pragma unroll
-      for (int j = 0; j < FN / 2; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * (BN / 2) + wn * (BN / WN / 2) + j * 32 + q * 8 + (lane >> 5) * 4;
-          float h[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          float u[4] = {acc[i][j + FN / 2][4 * q], acc[i][j + FN / 2][4 * q + 1], acc[i][j + FN / 2][4 * q + 2],
-                        acc[i][j + FN / 2][4 * q + 3]};
-          Epi::at_pair4(ep, row, col, h, u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * BN + wn * (BN / WN) + j * 32 + q * 8 + (lane >> 5) * 4;
-          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          Epi::at4(ep, c.g, row, col, v);
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Persistent register-pipelined variant.
+// Schedule.
 //
 // The grid holds as many workgroups as fit on the chip (two per CU: their LDS,
 // and registers capped at 256 per lane so two waves share a SIMD); the
@@ -301,17 +171,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
 // the operand panels out of L2).
 // ---------------------------------------------------------------------------
 // BK = 64: two LDS stages (the store of slice n+1 goes to the stage not being
-// read); BK = 128: one stage of 64 KB, refilled after a barrier that follows
-// the multiply (same LDS, twice the K per slice and per load in flight).
+// read).
 template <int BK_>
 struct PipeCfg {
   static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, BK = BK_, NTHR = 256;
   static constexpr int FM = 2, FN = 2, CH = BK / 8;
-  static constexpr int NSTAGE = BK == 64 ? 2 : 1;
+  static constexpr int NSTAGE = 2;
   static constexpr int STAGE = (BM + BN) * CH;             // 16-byte chunks per stage
   static constexpr int OFF_INTS = kMaxExperts + 1;
   static constexpr int LDS_BYTES = NSTAGE * STAGE * 16 + 2 * OFF_INTS * 4;
-  static_assert(BK == 64 || BK == 128, "slice depth");
+  static_assert(BK == 64, "slice depth");
 };
 
 // barrier for LDS traffic only: wait for this wave's LDS operations, then meet
@@ -323,8 +192,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 
 // MX = true: both operands are K-contiguous fp8 e4m3 codes with e8m0 scales
-// (`s`), multiplied with v_mfma_scale_f32_32x32x64_f8f6f4 (operand layout as in
-// gemm_mx.hpp).  GemmArgs then count K, lda, ldb in 2-byte units (a slice of
+// (`s`), multiplied with v_mfma_scale_f32_32x32x64_f8f6f4 (operand layout at
+// MxArgs in gemm.hpp).  GemmArgs then count K, lda, ldb in 2-byte units (a slice of
 // BK = 64 units is 128 fp8 values); ragged row offsets are rows, ragged
 // contraction offsets (padded rows of the column forms) are bytes.
 template <OpLayout LA, OpLayout LB, GemmMode MODE, class Epi, int BK_, bool MX = false>
@@ -433,7 +302,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     xa.store(st);
     xb.store(st + BM * CH);
   };
-  auto stage_of = [](int slice) { return NSTAGE == 2 ? (slice & 1) : 0; };
+  auto stage_of = [](int slice) { return slice & 1; };
 
   It comp, ld;
   settle(0, comp);
@@ -598,7 +467,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
-    if (NSTAGE == 1) lds_barrier();      // every wave is done reading the stage
     if constexpr (decltype(last)::value) {
       // the stage slice n + 1 goes to is not being read now: stage the tile there
       epilogue(comp.c, stage_of(n + 1));

@@ -29,6 +29,7 @@ struct RouterParams {
   int renorm;
   float scale;
   float aux_coeff;
+  int balanced;     // force-balanced routing: choice j of token t is expert (t k + j) mod E
 };
 
 constexpr int kRouterTokensPerBlock = 16;
@@ -42,6 +43,8 @@ hipError_t launch_router_finalize(const int* cnt_part, float* colsum_part, int n
                                   int32_t* counts, hipStream_t st);
 hipError_t launch_router_aux(const int32_t* counts, const float* colsum, const RouterParams& p, float* aux,
                              hipStream_t st);
+hipError_t launch_router_bias_update(const int32_t* counts, int E, int64_t Tk, float rate, float* bias,
+                                     hipStream_t st);
 template <class T>
 hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gates,
                              const float* d_gates, const int32_t* counts, const RouterParams& p,
@@ -50,8 +53,9 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const floa
 // permute.hip
 hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int E, int* hist, hipStream_t st);
 hipError_t launch_perm_scan(int* hist, int R, int E, int rows, int32_t* offsets, hipStream_t st);
+// gates / row_gates (optional pair): row_gates[row_id_map[n]] = gates[n]
 hipError_t launch_perm_rank(const int32_t* idx, int T, int k, int E, int* base, int32_t* row_id_map,
-                            int32_t* src_token, hipStream_t st);
+                            int32_t* src_token, const float* gates, float* row_gates, hipStream_t st);
 hipError_t launch_scatter_rows(const void* x, const int32_t* row_id_map, int T_, int k, int row_bytes,
                                void* out, hipStream_t st);
 template <class T>
@@ -73,17 +77,24 @@ int gemm_tile_rows(bool bf16, int64_t rows, int G, bool forward);
 template <class T>
 hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int T_, int E, int d,
                               hipStream_t st);
+// row_gates: folded gates (act = g silu(H) U) or NULL; from_stored: act from H, U as stored
 template <class T>
 hipError_t gemm_swiglu_fwd(const void* xin, const int* offsets, const int* tile_prefix, int G,
                            const void* w13, void* hu, void* act, int rows, int d, int f,
-                           hipStream_t st);
+                           const float* row_gates, bool from_stored, hipStream_t st);
 template <class T>
 hipError_t gemm_down_fwd(const void* act, const int* offsets, const int* tile_prefix, int G,
                          const void* w2, void* y, int rows, int d, int f, hipStream_t st);
+// row_gates (folded gates) with dg_part [rows, gemm_dg_parts] gate-gradient
+// partials, or NULL; act_out: act formed again from hu (recomputation) or NULL
 template <class T>
 hipError_t gemm_down_dgrad_swiglu_bwd(const void* dy, const int* offsets, const int* tile_prefix,
                                       int G, const void* w2, const void* hu, void* dhu, int rows,
-                                      int d, int f, hipStream_t st);
+                                      int d, int f, const float* row_gates, float* dg_part, void* act_out,
+                                      hipStream_t st);
+int gemm_dg_parts(bool bf16, int f);
+hipError_t launch_gate_grad_sum(const float* part, int P, const int32_t* row_id_map, int64_t n_total,
+                                float* d_gates, hipStream_t st);
 template <class T>
 hipError_t gemm_gateup_dgrad(const void* dhu, const int* offsets, const int* tile_prefix, int G,
                              const void* w13, void* dx, bool f32_out, int rows, int d, int f,
@@ -113,12 +124,13 @@ hipError_t launch_mx_quant_cols(const void* src, int64_t ld, int rows, int C, co
 hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C, uint8_t* codes,
                                         uint8_t* scales, hipStream_t st);
 hipError_t gemm_mx_swiglu_fwd(const MxQ& x, const int* off, const int* prefix, int G, const MxQ& w13, void* hu,
-                              void* act, int rows, int d, int f, hipStream_t st);
+                              void* act, int rows, int d, int f, const float* row_gates, bool from_stored,
+                              hipStream_t st);
 hipError_t gemm_mx_down_fwd(const MxQ& act, const int* off, const int* prefix, int G, const MxQ& w2, void* y,
                             int rows, int d, int f, hipStream_t st);
 hipError_t gemm_mx_down_dgrad_swiglu_bwd(const MxQ& dy, const int* off, const int* prefix, int G,
                                          const MxQ& w2t, const void* hu, void* dhu, int rows, int d, int f,
-                                         hipStream_t st);
+                                         const float* row_gates, float* dg_part, void* act_out, hipStream_t st);
 hipError_t gemm_mx_gateup_dgrad(const MxQ& dhu, const int* off, const int* prefix, int G, const MxQ& w13t,
                                 void* dx, bool f32_out, int rows, int d, int f, hipStream_t st);
 hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G, int K,

@@ -15,12 +15,11 @@
 // new block sequence at padded row poff[g] (a multiple of 128), and rows past
 // the group's end up to the next 128 are zero codes with zero-amax scales.
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "common.hpp"
 #include "gemm.hpp"
 #include "gemm_mfma.hpp"
-#include "gemm_mx.hpp"
+#include "gemm_regs.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -229,27 +228,8 @@ hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C
 }
 
 // ---------------------------------------------------------------------------
-// MXFP8 GEMM launchers (one tile per workgroup, RegTile shape).
+// MXFP8 GEMM launchers.
 // ---------------------------------------------------------------------------
-template <GemmMode MODE, class Epi>
-static hipError_t launch_mx(const GemmArgs& a, const MxArgs& s, const typename Epi::P& ep, int n_logical,
-                            int rows_total, hipStream_t st) {
-  using C = RegTile;
-  const int bn_cols = Epi::kPaired ? C::BN / 2 : C::BN;
-  const int NT = (n_logical + bn_cols - 1) / bn_cols;
-  const int MT = (MODE == RAGGED_M) ? 0 : (a.M + C::BM - 1) / C::BM;
-  int64_t grid;
-  if (MODE == RAGGED_M) grid = (int64_t)((rows_total + C::BM - 1) / C::BM + a.G) * NT;
-  else if (MODE == RAGGED_K) grid = (int64_t)a.G * MT * NT;
-  else grid = (int64_t)MT * NT;
-  if (grid <= 0) return hipSuccess;
-  auto kern = gemm_mx_kernel<MODE, Epi>;
-  static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
-  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, kMxTileLdsBytes); e != hipSuccess) return e;
-  kern<<<(unsigned)grid, C::NTHR, kMxTileLdsBytes, st>>>(a, s, ep, NT, MT);
-  return hipGetLastError();
-}
-
 // Persistent pipelined form (gemm_pipe_kernel with MXFP8 operands): the
 // arguments in bytes, converted to the kernel's 2-byte units here.
 static int device_cus_mx() {
@@ -310,25 +290,6 @@ static hipError_t launch_mx_dma(GemmArgs a, const MxArgs& s, const typename Epi:
   return hipGetLastError();
 }
 
-// Kernel of the MXFP8 products: 1 = DMA ring, 3 = one tile per workgroup,
-// 4 = persistent pipelined.  Row-ragged and dense products default to the DMA
-// ring, weight gradients to the persistent kernel; MOE_TILE / MOE_TILE_WGRAD
-// override them for tuning runs.
-static int mx_choice(bool wgrad) {
-  static int v = -1, w = -1;
-  if (v < 0) {
-    auto pick = [](const char* e, int dflt) {
-      const int x = e ? atoi(e) : dflt;
-      return (x == 1 || x == 3 || x == 4) ? x : dflt;
-    };
-    const char* e = getenv("MOE_TILE");
-    const char* f = getenv("MOE_TILE_WGRAD");
-    v = pick(e, 1);
-    w = f ? pick(f, 4) : (e ? (v == 1 ? 4 : v) : 4);
-  }
-  return wgrad ? w : v;
-}
-
 // Z[rows, N] = Q[rows, K] . W[g][N, K]^T over ragged row groups (or dense when
 // offsets is NULL): the operands are quantised row forms.
 template <class Epi>
@@ -339,24 +300,23 @@ static hipError_t mx_rows_gemm(const MxQ& q, const int* offsets, const int* pref
   a.A = q.codes; a.lda = K; a.B = w.codes; a.ldb = K; a.b_gstride = w_gstride;
   a.M = rows; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
   MxArgs s{q.scales, w.scales, K / 32, K / 32, w_gstride / 32};
-  int t = mx_choice(false);
-  if constexpr (Epi::kStaged)         // staged epilogues store 16-byte row pieces
-    if (!(ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0)) t = 3;
+  // staged epilogues store 16-byte row pieces (the call's shape checks and
+  // 16-byte aligned outputs guarantee them)
+  if constexpr (Epi::kStaged)
+    if (!(ep.N % 8 == 0 && ep.ldc % 8 == 0 && ep.c_gstride % 8 == 0 && ((uintptr_t)ep.C & 15) == 0))
+      return hipErrorInvalidValue;
   if (offsets) {
     a.offsets = offsets; a.tile_prefix = prefix; a.G = G;
-    if (t == 1) return launch_mx_dma<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
-    if (t == 4) return launch_mx_pipe<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
-    return launch_mx<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
+    return launch_mx_dma<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
   }
   a.G = 1;
-  if (t == 1) return launch_mx_dma<DENSE, Epi>(a, s, ep, n_logical, rows, st);
-  if (t == 4) return launch_mx_pipe<DENSE, Epi>(a, s, ep, n_logical, rows, st);
-  return launch_mx<DENSE, Epi>(a, s, ep, n_logical, rows, st);
+  return launch_mx_dma<DENSE, Epi>(a, s, ep, n_logical, rows, st);
 }
 
 hipError_t gemm_mx_swiglu_fwd(const MxQ& x, const int* off, const int* prefix, int G, const MxQ& w13, void* hu,
-                              void* act, int rows, int d, int f, hipStream_t st) {
-  typename EpiSwiGLU<bf16>::P ep{(bf16*)act, (bf16*)hu, f};
+                              void* act, int rows, int d, int f, const float* row_gates, bool from_stored,
+                              hipStream_t st) {
+  typename EpiSwiGLU<bf16>::P ep{(bf16*)act, (bf16*)hu, f, row_gates, from_stored ? 1 : 0};
   return mx_rows_gemm<EpiSwiGLU<bf16>>(x, off, prefix, G, w13, (int64_t)2 * f * d, rows, 2 * f, d, ep, f, st);
 }
 
@@ -369,8 +329,9 @@ hipError_t gemm_mx_down_fwd(const MxQ& act, const int* off, const int* prefix, i
 // dA = dY W2 with W2 quantised along d (w2t [g][f][d]); SwiGLU backward epilogue
 hipError_t gemm_mx_down_dgrad_swiglu_bwd(const MxQ& dy, const int* off, const int* prefix, int G,
                                          const MxQ& w2t, const void* hu, void* dhu, int rows, int d, int f,
-                                         hipStream_t st) {
-  typename EpiSwiGLUBwd<bf16>::P ep{(const bf16*)hu, (bf16*)dhu, f};
+                                         const float* row_gates, float* dg_part, void* act_out, hipStream_t st) {
+  typename EpiSwiGLUBwd<bf16>::P ep{(const bf16*)hu, (bf16*)dhu, f, row_gates, row_gates ? dg_part : nullptr,
+                                    gemm_dg_parts(true, f), (bf16*)act_out};
   return mx_rows_gemm<EpiSwiGLUBwd<bf16>>(dy, off, prefix, G, w2t, (int64_t)f * d, rows, f, d, ep, f, st);
 }
 
@@ -405,23 +366,20 @@ hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, 
   a.M = M; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
   a.offsets = poff; a.G = poff ? G : 1;
   MxArgs s{p.scales, q.scales, ldq / 32, ldq / 32, 0};
-  // the pipelined kernel stages 16-byte row pieces of the output and skips
-  // empty contractions: it needs aligned rows and zero-filled empty experts
-  const bool pipe = mx_choice(true) == 4 && N % 8 == 0 && ((uintptr_t)dw & 15) == 0;
-  if (pipe) {
-    const int64_t vec = (int64_t)M * N * 2 / 16;
-    zero_empty_groups_mx_kernel<<<dim3(64, poff ? G : 1), 256, 0, st>>>(poff, (u32x4*)dw, vec, K);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // the pipelined kernel stages 16-byte row pieces of the output (the call's
+  // shape checks and 16-byte aligned outputs guarantee them) and skips empty
+  // contractions, whose outputs are zero-filled here
+  if (N % 8 != 0 || ((uintptr_t)dw & 15) != 0) return hipErrorInvalidValue;
+  const int64_t vec = (int64_t)M * N * 2 / 16;
+  zero_empty_groups_mx_kernel<<<dim3(64, poff ? G : 1), 256, 0, st>>>(poff, (u32x4*)dw, vec, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (site == 1) {
     typename EpiStore<bf16, 8>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
-    if (pipe) return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 8>>(a, s, ep, N, 0, st);
-    return launch_mx<RAGGED_K, EpiStore<bf16, 8>>(a, s, ep, N, 0, st);
+    return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 8>>(a, s, ep, N, 0, st);
   }
   typename EpiStore<bf16, 7>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
-  if (pipe) return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 7>>(a, s, ep, N, 0, st);
-  return launch_mx<RAGGED_K, EpiStore<bf16, 7>>(a, s, ep, N, 0, st);
+  return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 7>>(a, s, ep, N, 0, st);
 }
 
 }  // namespace moe

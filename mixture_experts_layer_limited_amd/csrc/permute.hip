@@ -66,11 +66,15 @@ hipError_t launch_perm_scan(int* hist, int R, int E, int rows, int32_t* offsets,
   return hipGetLastError();
 }
 
-// one wave per token range; entries n = t*k + j in increasing order
+// one wave per token range; entries n = t*k + j in increasing order.  With
+// gates, each entry's gate also goes to its row (row_gates: the gate of each
+// permuted row, for gate folding).
 __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict__ idx, int T, int k,
                                                        int E, const int* __restrict__ base,
                                                        int32_t* __restrict__ row_id_map,
-                                                       int32_t* __restrict__ src_token) {
+                                                       int32_t* __restrict__ src_token,
+                                                       const float* __restrict__ gates,
+                                                       float* __restrict__ row_gates) {
   __shared__ int run[kMaxExperts];
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += 64) run[e] = base[(int64_t)blockIdx.x * E + e];
@@ -93,6 +97,7 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict
       row = run[e] + __popcll(m & below);
       row_id_map[n] = row;
       src_token[row] = (int32_t)(n / k);
+      if (row_gates) row_gates[row] = gates[n];
     }
     __syncthreads();
     // the highest lane of each id group advances that expert's running row
@@ -102,10 +107,10 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict
 }
 
 hipError_t launch_perm_rank(const int32_t* idx, int T, int k, int E, int* base, int32_t* row_id_map,
-                            int32_t* src_token, hipStream_t st) {
+                            int32_t* src_token, const float* gates, float* row_gates, hipStream_t st) {
   int R = (T + kPermTokensPerRange - 1) / kPermTokensPerRange;
   if (R == 0) return hipSuccess;
-  perm_rank_kernel<<<R, 64, 0, st>>>(idx, T, k, E, base, row_id_map, src_token);
+  perm_rank_kernel<<<R, 64, 0, st>>>(idx, T, k, E, base, row_id_map, src_token, gates, row_gates);
   return hipGetLastError();
 }
 
@@ -146,7 +151,8 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* row_id_map, int T_,
 }
 
 // ---------------------------------------------------------------------------
-// Combine: y[t] = sum_j g[t,j] y_perm[row(t,j)] (+ y_shared[t]), fp32, j order.
+// Combine: y[t] = sum_j g[t,j] y_perm[row(t,j)] (+ y_shared[t]), fp32, j order;
+// gates NULL (folded into the rows already): the unweighted sum.
 // One workgroup per token; each thread owns 8 consecutive elements.
 // ---------------------------------------------------------------------------
 template <class T>
@@ -210,14 +216,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_pe
       for (int j = 0; j < KC; ++j) r[j].load(y_perm + (int64_t)rmap[(int64_t)t * KC + j] * d + c);
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
-        const float g = gates[(int64_t)t * KC + j];
+        const float g = gates ? gates[(int64_t)t * KC + j] : 1.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc.v[i] += g * r[j].v[i];
       }
     } else {
       for (int j = 0; j < k; ++j) {
         const int64_t row = rmap[(int64_t)t * k + j];
-        const float g = gates[(int64_t)t * k + j];
+        const float g = gates ? gates[(int64_t)t * k + j] : 1.0f;
         Vec8<T> r;
         r.load(y_perm + row * d + c);
 #pragma unroll

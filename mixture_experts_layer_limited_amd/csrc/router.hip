@@ -106,7 +106,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     }
 
     // group-limited routing: score groups by the sum of their two best keys
-    if (p.n_group > 1) {
+    // (force-balanced routing assigns experts without looking at the keys)
+    if (p.n_group > 1 && !p.balanced) {
       float gs[kNI];
 #pragma unroll
       for (int i = 0; i < kNI; ++i) gs[i] = -INFINITY;
@@ -164,20 +165,26 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       }
     }
 
-    // top-k: k rounds of a wave argmax; lane j%64 keeps choice j
+    // top-k: k rounds of a wave argmax; lane j%64 keeps choice j.  Force-
+    // balanced routing: choice j is expert (t k + j) mod E (uniform over the wave)
     int my_id[kNI];
     float my_val[kNI], my_p[kNI];
 #pragma unroll
     for (int i = 0; i < kNI; ++i) { my_id[i] = 0; my_val[i] = 0.0f; my_p[i] = 0.0f; }
     for (int j = 0; j < k; ++j) {
-      float bk = -INFINITY;
-      int bi = 0x7fffffff;
+      int bi;
+      if (p.balanced) {
+        bi = (int)(((int64_t)t * k + j) % E);
+      } else {
+        float bk = -INFINITY;
+        bi = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < kNI; ++i) {
-        int e = lane + 64 * i;
-        if (elig[i] && !taken[i] && better(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
+        for (int i = 0; i < kNI; ++i) {
+          int e = lane + 64 * i;
+          if (elig[i] && !taken[i] && better(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
+        }
+        wave_argmax(bk, bi);
       }
-      wave_argmax(bk, bi);
       // the owner lane publishes the winner's logit (softmax) / score (sigmoid) and p
       float ov = 0.0f, op = 0.0f;
 #pragma unroll
@@ -309,6 +316,24 @@ __global__ __launch_bounds__(256) void router_aux_kernel(const int32_t* __restri
 hipError_t launch_router_aux(const int32_t* counts, const float* colsum, const RouterParams& p, float* aux,
                              hipStream_t st) {
   router_aux_kernel<<<1, 256, 0, st>>>(counts, colsum, p, aux);
+  return hipGetLastError();
+}
+
+// Selection-bias step toward balance: bias[e] += rate * sign(T k - E c_e).
+// The sign is integer arithmetic; rate * sign is exact, so the update is one
+// fp32 add whatever the compiler contracts.
+__global__ __launch_bounds__(256) void router_bias_update_kernel(const int32_t* __restrict__ counts, int E,
+                                                                 int64_t Tk, float rate, float* __restrict__ bias) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  const int64_t diff = Tk - (int64_t)E * counts[e];
+  const float sgn = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);
+  bias[e] = bias[e] + rate * sgn;
+}
+
+hipError_t launch_router_bias_update(const int32_t* counts, int E, int64_t Tk, float rate, float* bias,
+                                     hipStream_t st) {
+  router_bias_update_kernel<<<1, 256, 0, st>>>(counts, E, Tk, rate, bias);
   return hipGetLastError();
 }
 

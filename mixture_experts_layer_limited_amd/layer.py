@@ -29,11 +29,15 @@ class LayerShape:
     scale: float = 1.0
     aux_coeff: float = 0.0
     dtype: str = "bf16"
+    force_balanced: bool = False   # round-robin expert assignment (moe_cfg.flags)
+    fold_gates: bool = False       # gates applied to act before the down projection
+    recompute_act: bool = False    # the backward forms act again from the saved H, U
 
     def cfg(self) -> abi.moe_cfg:
         return abi.make_cfg(self.T, self.d, self.E, self.k, self.f, self.f_shared, self.score,
                             self.n_group, self.topk_group, self.renorm, self.scale,
-                            self.aux_coeff, self.dtype)
+                            self.aux_coeff, self.dtype, self.force_balanced, self.fold_gates,
+                            self.recompute_act)
 
     @property
     def torch_dtype(self):
@@ -75,6 +79,7 @@ class MoELayer:
             "offsets": e(s.E + 1, dtype=torch.int32),
             "row_id_map": e(s.T, s.k, dtype=torch.int32),
             "src_token": e(rows, dtype=torch.int32),
+            "row_gates": e(rows, dtype=torch.float32) if s.fold_gates else None,
             "x_perm": e(rows, s.d),
             "hu": e(rows, 2 * s.f) if self.backward_enabled else None,
             "act": e(rows, s.f),
@@ -106,13 +111,33 @@ class MoELayer:
 
     def permute(self, x, stream=None):
         b = self.buf
-        abi.moe_permute(self.cfg, x, b["idx"], b["offsets"], b["row_id_map"], b["src_token"], b["x_perm"],
-                        self.ws, stream)
+        fold = self.s.fold_gates
+        abi.moe_permute(self.cfg, x, b["idx"], b["gates"] if fold else None, b["offsets"], b["row_id_map"],
+                        b["src_token"], b.get("row_gates"), b["x_perm"], self.ws, stream)
 
     # -- MXFP8 weights -------------------------------------------------------
+    @staticmethod
+    def _mx_source_key(*ws):
+        """Identity of the bf16 weights the quantised copies were made from:
+        each tensor's address, shape and torch's in-place version counter
+        (shared by all views of a storage).  The layer also holds references to
+        those tensors (mx_sources), so their memory cannot be freed and handed
+        to other tensors while the copies exist: an equal address is the same
+        memory, and an in-place update (e.g. an optimizer step) bumps the
+        version.  Writes that bypass the version counter (through .data or a raw
+        pointer) are not seen: call prepare_mx_weights after those."""
+        return tuple(None if w is None else (w.data_ptr(), w._version, tuple(w.shape), tuple(w.stride()))
+                     for w in ws)
+
+    def _ensure_mx_weights(self, w13, w2, ws13, ws2, stream):
+        if getattr(self, "mx_key", None) != self._mx_source_key(w13, w2, ws13, ws2):
+            self.prepare_mx_weights(w13, w2, ws13, ws2, stream)
+
     def prepare_mx_weights(self, w13, w2, ws13=None, ws2=None, stream=None):
-        """Quantise the expert weights once (per weight update) in the two
-        orientations the MXFP8 GEMMs contract them in; kept for later calls."""
+        """Quantise the expert weights (once per weight update) in the two
+        orientations the MXFP8 GEMMs contract them in.  The copies are reused
+        by later forward and backward calls for as long as they are given the
+        same, unmodified weight tensors; other weights are quantised anew."""
         s, dev = self.s, self.device
         u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=dev)
         q = {}
@@ -136,24 +161,27 @@ class MoELayer:
             quant("ws2_t", ws2, 1, s.d, s.f_shared, abi.MOE_MX_COLS)
         self.mx_tensors = q                          # keeps the device memory alive
         self.mx_weights = abi.mx_weights(**q)
+        self.mx_sources = (w13, w2, ws13, ws2)       # their memory stays theirs while the copies exist
+        self.mx_key = self._mx_source_key(w13, w2, ws13, ws2)
 
     def experts(self, x, w13, w2, ws13=None, ws2=None, stream=None):
         b = self.buf
         if self.s.dtype == "mxfp8":
-            if getattr(self, "mx_weights", None) is None:
-                self.prepare_mx_weights(w13, w2, ws13, ws2, stream)
-            abi.moe_grouped_gemm_swiglu_mxfp8(self.cfg, b["x_perm"], b["offsets"], self.mx_weights, b.get("hu"),
-                                              b["act"], b["y_perm"], x if self.s.f_shared else None,
-                                              b.get("hu_s"), b.get("act_s"), b.get("y_s"), self.ws, stream)
+            self._ensure_mx_weights(w13, w2, ws13, ws2, stream)
+            abi.moe_grouped_gemm_swiglu_mxfp8(self.cfg, b["x_perm"], b["offsets"], b.get("row_gates"),
+                                              self.mx_weights, b.get("hu"), b["act"], b["y_perm"],
+                                              x if self.s.f_shared else None, b.get("hu_s"), b.get("act_s"),
+                                              b.get("y_s"), self.ws, stream)
             return
-        abi.moe_grouped_gemm_swiglu(self.cfg, b["x_perm"], b["offsets"], w13, w2, b.get("hu"), b["act"],
+        abi.moe_grouped_gemm_swiglu(self.cfg, b["x_perm"], b["offsets"], b.get("row_gates"), w13, w2, b.get("hu"),
+                                    b["act"],
                                     b["y_perm"], x if self.s.f_shared else None, ws13, ws2, b.get("hu_s"),
                                     b.get("act_s"), b.get("y_s"), self.ws, stream)
 
     def combine(self, stream=None):
         b = self.buf
-        abi.moe_unpermute_combine(self.cfg, b["y_perm"], b["row_id_map"], b["gates"], b.get("y_s"), b["y"],
-                                  stream)
+        abi.moe_unpermute_combine(self.cfg, b["y_perm"], b["row_id_map"], None if self.s.fold_gates else b["gates"],
+                                  b.get("y_s"), b["y"], stream)
 
     def forward(self, x, w_router, bias, w13, w2, ws13=None, ws2=None, stream=None):
         self.route(x, w_router, bias, stream)
@@ -164,15 +192,25 @@ class MoELayer:
 
     # -- backward -----------------------------------------------------------
     def backward(self, dy, x, w_router, w13, w2, ws13=None, ws2=None, d_aux: float = 1.0, stream=None):
+        """Gradients of <y, dy>.  With fold_gates the combine's backward only
+        copies dy to the permuted rows and the experts' backward forms d_gates;
+        with recompute_act the experts' backward does not read act."""
         b, s = self.buf, self.s
-        abi.moe_unpermute_combine_bwd(self.cfg, dy, b["y_perm"], b["row_id_map"], b["gates"], b["dy_perm"],
-                                      b["d_gates"], stream)
+        fold = s.fold_gates
+        abi.moe_unpermute_combine_bwd(self.cfg, dy, None if fold else b["y_perm"], b["row_id_map"],
+                                      None if fold else b["gates"], b["dy_perm"], None if fold else b["d_gates"],
+                                      stream)
         sh = bool(s.f_shared)
+        act = None if s.recompute_act else b["act"]
+        act_s = None if s.recompute_act else b.get("act_s")
+        rg = (b["row_gates"], b["row_id_map"], b["d_gates"]) if fold else (None, None, None)
         if s.dtype == "mxfp8":
+            self._ensure_mx_weights(w13, w2, ws13, ws2, stream)
             abi.moe_grouped_gemm_swiglu_bwd_mxfp8(
-                self.cfg, b["dy_perm"], b["x_perm"], b["offsets"], b["hu"], b["act"], self.mx_weights, b["dhu"],
-                b["dx_perm"], b["dw13"], b["dw2"], dy if sh else None, x if sh else None, b.get("hu_s"),
-                b.get("act_s"), b.get("dhu_s"), b["dx_partial"], b.get("dws13"), b.get("dws2"), self.ws, stream)
+                self.cfg, b["dy_perm"], b["x_perm"], b["offsets"], rg[0], rg[1], b["hu"], act, self.mx_weights,
+                b["dhu"], b["dx_perm"], b["dw13"], b["dw2"], rg[2], dy if sh else None, x if sh else None,
+                b.get("hu_s"), act_s, b.get("dhu_s"), b["dx_partial"], b.get("dws13"), b.get("dws2"), self.ws,
+                stream)
         else:
             self._gemm_bwd_bf16(dy, x, w13, w2, ws13, ws2, stream)
         abi.moe_router_topk_bwd(self.cfg, x, w_router, b["logits"], b["idx"], b["gates"], b["counts"],
@@ -184,8 +222,11 @@ class MoELayer:
     def _gemm_bwd_bf16(self, dy, x, w13, w2, ws13, ws2, stream):
         b, s = self.buf, self.s
         sh = bool(s.f_shared)
+        fold = s.fold_gates
+        act = None if s.recompute_act else b["act"]
+        act_s = None if s.recompute_act else b.get("act_s")
         abi.moe_grouped_gemm_swiglu_bwd(
-            self.cfg, b["dy_perm"], b["x_perm"], b["offsets"], b["hu"], b["act"], w13, w2, b["dhu"],
-            b["dx_perm"], b["dw13"], b["dw2"], dy if sh else None, x if sh else None, b.get("hu_s"),
-            b.get("act_s"), ws13, ws2, b.get("dhu_s"), b["dx_partial"], b.get("dws13"), b.get("dws2"),
-            self.ws, stream)
+            self.cfg, b["dy_perm"], b["x_perm"], b["offsets"], b["row_gates"] if fold else None,
+            b["row_id_map"] if fold else None, b["hu"], act, w13, w2, b["dhu"], b["dx_perm"], b["dw13"], b["dw2"],
+            b["d_gates"] if fold else None, dy if sh else None, x if sh else None, b.get("hu_s"), act_s, ws13, ws2,
+            b.get("dhu_s"), b["dx_partial"], b.get("dws13"), b.get("dws2"), self.ws, stream)

@@ -57,6 +57,10 @@ class MoEConfig:
     expert_std: float = 0.0    # 0: 1/sqrt(fan_in)
     bias: str = "none"         # "none" | "normal" | "zipf"
     bias_std: float = 0.0
+    # layer modes (the C ABI's moe_cfg.flags)
+    force_balanced: bool = False   # round-robin expert assignment instead of top-k
+    fold_gates: bool = False       # gates applied to the SwiGLU output before the down projection
+    recompute_act: bool = False    # act formed from the stored H, U and re-formed in the backward
 
     def with_(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)

@@ -46,6 +46,22 @@ bias, 8 groups / top-4 by top-2 sum, renormalise then x2.5, aux coefficient
       first row, rows past its end count as zeros
   R17 expert weights enter the MXFP8 GEMMs quantised along whichever of their
       dimensions the GEMM contracts
+  R21 force-balanced routing (the benchmark condition of Table 11): choice j of
+      token t goes to expert (t k + j) mod E, so every expert gets T k / E rows
+      when E divides T k; gates come from the scores of the assigned experts
+      by the usual rule
+  R22 bias update without an auxiliary loss (Figure 39, load balancing): after
+      a step, b_e <- fp32(b_e + rate * sign(T k / E - c_e)), the sign taken
+      on the integers T k - E c_e
+  R23 gate folding (a reading of memory-efficient permutation, Figure 7 and
+      Table 6): the gate of each permuted row multiplies the SwiGLU output
+      before the down projection, A_g = g silu(H) U, so the combine is an
+      unweighted sum; the backward gets dg = <dA, silu(H) U> with dA = dy W2
+      and silu(H) U formed from the stored H, U
+  R24 SwiGLU recomputation (Figure 8, Table 4): act is formed from the stored
+      (rounded) H and U in the forward, and the backward forms it again from
+      them, so it is not kept between the passes and both forms agree bit for
+      bit
 
 Pins that tie this oracle to facts outside itself live in tests/test_oracle_*.py.
 """
@@ -162,6 +178,30 @@ def select_topk(keys, cfg) -> np.ndarray:
     return idx
 
 
+def select_balanced(T: int, E: int, k: int) -> np.ndarray:
+    """Force-balanced routing (R21): choice j of token t is expert (t k + j) mod E.
+    The k choices of a token are k consecutive experts modulo E, so they are
+    distinct for k <= E."""
+    idx = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        for j in range(k):
+            idx[t, j] = (t * k + j) % E
+    return idx
+
+
+def bias_update(bias, counts, T: int, k: int, rate: float) -> np.ndarray:
+    """Aux-loss-free balancing step (R22): raise the selection bias of experts
+    below the mean load T k / E by `rate`, lower it for those above, leave it
+    where the load is exactly the mean.  One fp32 add per expert."""
+    b = np.asarray(bias, F32).copy()
+    c = np.asarray(counts, np.int64)
+    E = b.shape[0]
+    sign = np.sign(T * k - E * c)                      # integer: no rounding in the comparison
+    for e in range(E):
+        b[e] = F32(b[e] + F32(rate) * F32(sign[e]))
+    return b
+
+
 def gates_from_selection(logits, idx, cfg, exact: bool = False) -> np.ndarray:
     """Gate weights g[t, j] of the selected experts (R7).
     softmax + renorm: softmax restricted to the selection;
@@ -189,7 +229,10 @@ def route(x, w_router, bias, cfg, storage: str = None) -> dict:
     exact = storage == "f64"
     logits = router_logits(x, w_router, "f64" if exact else "f32")
     keys = selection_keys(logits, cfg, bias, exact)
-    idx = select_topk(keys, cfg)
+    if getattr(cfg, "force_balanced", False):
+        idx = select_balanced(logits.shape[0], logits.shape[1], cfg.k)
+    else:
+        idx = select_topk(keys, cfg)
     gates = gates_from_selection(logits, idx, cfg, exact)
     out = {"logits": logits, "keys": keys, "idx": idx, "gates": gates}
     if cfg.score == "softmax":
@@ -258,35 +301,50 @@ def silu(h):
     return h / (1.0 + np.exp(-h))
 
 
-def swiglu_ffn_fwd(xe, w13_e, w2_e, storage: str) -> dict:
+def _act(h, u, gate):
+    """SwiGLU output silu(h) * u, times the row's gate when gates are folded (R23)."""
+    a = silu(h) * u
+    return a if gate is None else np.asarray(gate, F64)[:, None] * a
+
+
+def swiglu_ffn_fwd(xe, w13_e, w2_e, storage: str, gate=None, act_from_stored: bool = False) -> dict:
     """One SwiGLU FFN on rows xe [n, d] with W13 [2f, d] (gate rows then up
     rows) and W2 [d, f]:  H = xe Wg^T, U = xe Wu^T, A = silu(H) * U, Y = A W2^T.
     H and U are kept as stored (for backward); A is formed from the unrounded
-    H, U and then stored; Y is stored."""
+    H, U (from the stored ones with act_from_stored, R24), times the row gates
+    `gate` [n] if given (R23), and then stored; Y is stored."""
     f = w2_e.shape[1]
     xe = np.asarray(xe, F64)
     w13_e = np.asarray(w13_e, F64)
     h = xe @ w13_e[:f].T
     u = xe @ w13_e[f:].T
-    a = store(silu(h) * u, storage)
+    H, U = store(h, storage), store(u, storage)
+    a = store(_act(H, U, gate) if act_from_stored else _act(h, u, gate), storage)
     y = store(a @ np.asarray(w2_e, F64).T, storage)
-    return {"H": store(h, storage), "U": store(u, storage), "A": a, "Y": y}
+    return {"H": H, "U": U, "A": a, "Y": y}
 
 
-def swiglu_ffn_bwd(xe, H, U, A, dY, w13_e, w2_e, storage: str) -> dict:
+def swiglu_ffn_bwd(xe, H, U, A, dY, w13_e, w2_e, storage: str, gate=None) -> dict:
     """Backward of swiglu_ffn_fwd given the stored H, U, A and the incoming dY:
       dA  = dY W2                       dW2 = dY^T A
       dH  = dA * U * sig(H) * (1 + H (1 - sig(H)))      (d silu)
       dU  = dA * silu(H)
       dX  = dH Wg + dU Wu               dWg = dH^T X,  dWu = dU^T X
+    With folded gates (R23, `gate` [n]) A holds g silu(H) U and dY the
+    unweighted upstream rows: the gate gradient of each row is
+    dg = <dY W2, silu(H) U> and dH, dU take dA = g (dY W2).
     dA stays unrounded (it lives only inside the producing kernel); dH, dU, dX
-    and the weight gradients are stored."""
+    and the weight gradients are stored; dg is returned unrounded."""
     f = w2_e.shape[1]
     dY = np.asarray(dY, F64)
     H = np.asarray(H, F64)
     U = np.asarray(U, F64)
     w13_e = np.asarray(w13_e, F64)
     dA = dY @ np.asarray(w2_e, F64)
+    dg = None
+    if gate is not None:
+        dg = np.sum(dA * (silu(H) * U), axis=1)
+        dA = np.asarray(gate, F64)[:, None] * dA
     dW2 = store(dY.T @ np.asarray(A, F64), storage)
     sig = 1.0 / (1.0 + np.exp(-H))
     dH = store(dA * U * sig * (1.0 + H * (1.0 - sig)), storage)
@@ -296,7 +354,7 @@ def swiglu_ffn_bwd(xe, H, U, A, dY, w13_e, w2_e, storage: str) -> dict:
     dX_unrounded = dHU @ w13_e
     dW13 = store(dHU.T @ xe, storage)
     return {"dA": dA, "dH": dH, "dU": dU, "dX32": dX_unrounded,
-            "dX": store(dX_unrounded, storage), "dW13": dW13, "dW2": dW2}
+            "dX": store(dX_unrounded, storage), "dW13": dW13, "dW2": dW2, "dg": dg}
 
 
 # ----------------------------------------------------------------------------
@@ -385,7 +443,7 @@ def mx_qdq(a, axis: int) -> np.ndarray:
     return mx_dequantize(*mx_quantize(a, axis), axis)
 
 
-def swiglu_ffn_fwd_mx(xe, w13_e, w2_e, storage: str) -> dict:
+def swiglu_ffn_fwd_mx(xe, w13_e, w2_e, storage: str, gate=None, act_from_stored: bool = False) -> dict:
     """swiglu_ffn_fwd with MXFP8 GEMM operands: X and W13 quantised along d,
     A (after its bf16 store) and W2 along f."""
     f = w2_e.shape[1]
@@ -393,19 +451,25 @@ def swiglu_ffn_fwd_mx(xe, w13_e, w2_e, storage: str) -> dict:
     wq = mx_qdq(w13_e, 1)
     h = xq @ wq[:f].T
     u = xq @ wq[f:].T
-    a = store(silu(h) * u, storage)
+    H, U = store(h, storage), store(u, storage)
+    a = store(_act(H, U, gate) if act_from_stored else _act(h, u, gate), storage)
     y = store(mx_qdq(a, 1) @ mx_qdq(w2_e, 1).T, storage)
-    return {"H": store(h, storage), "U": store(u, storage), "A": a, "Y": y}
+    return {"H": H, "U": U, "A": a, "Y": y}
 
 
-def swiglu_ffn_bwd_mx(xe, H, U, A, dY, w13_e, w2_e, storage: str) -> dict:
+def swiglu_ffn_bwd_mx(xe, H, U, A, dY, w13_e, w2_e, storage: str, gate=None) -> dict:
     """swiglu_ffn_bwd with MXFP8 GEMM operands, each quantised along the
     dimension its GEMM contracts: dA = dY W2 (d), dW2 = dY^T A (rows),
-    dX = dHU W13 (2f), dW13 = dHU^T X (rows; blocks start at the first row)."""
+    dX = dHU W13 (2f), dW13 = dHU^T X (rows; blocks start at the first row).
+    Folded gates (`gate`) as in swiglu_ffn_bwd."""
     H = np.asarray(H, F64)
     U = np.asarray(U, F64)
     dY = np.asarray(dY, F64)
     dA = mx_qdq(dY, 1) @ mx_qdq(w2_e, 0)
+    dg = None
+    if gate is not None:
+        dg = np.sum(dA * (silu(H) * U), axis=1)
+        dA = np.asarray(gate, F64)[:, None] * dA
     dW2 = store(mx_qdq(dY, 0).T @ mx_qdq(A, 0), storage)
     sig = 1.0 / (1.0 + np.exp(-H))
     dH = store(dA * U * sig * (1.0 + H * (1.0 - sig)), storage)
@@ -414,7 +478,7 @@ def swiglu_ffn_bwd_mx(xe, H, U, A, dY, w13_e, w2_e, storage: str) -> dict:
     dX_unrounded = mx_qdq(dHU, 1) @ mx_qdq(w13_e, 0)
     dW13 = store(mx_qdq(dHU, 0).T @ mx_qdq(xe, 0), storage)
     return {"dA": dA, "dH": dH, "dU": dU, "dX32": dX_unrounded,
-            "dX": store(dX_unrounded, storage), "dW13": dW13, "dW2": dW2}
+            "dX": store(dX_unrounded, storage), "dW13": dW13, "dW2": dW2, "dg": dg}
 
 
 # ----------------------------------------------------------------------------
@@ -422,11 +486,13 @@ def swiglu_ffn_bwd_mx(xe, H, U, A, dY, w13_e, w2_e, storage: str) -> dict:
 # ----------------------------------------------------------------------------
 def combine(Yp, gates, row_id_map, Ys, storage: str) -> np.ndarray:
     """y[t] = sum_{j<k} g[t,j] * Yp[row(t,j)]  (+ Ys[t]), summed in j order and
-    stored once (R13)."""
+    stored once (R13).  gates = None: the rows already carry their gates (R23)
+    and are summed unweighted."""
     T, k = row_id_map.shape
     y = np.zeros((T, Yp.shape[1]), F64)
     for j in range(k):
-        y += np.asarray(gates, F64)[:, j:j + 1] * Yp[row_id_map[:, j].astype(np.int64)]
+        w = 1.0 if gates is None else np.asarray(gates, F64)[:, j:j + 1]
+        y += w * Yp[row_id_map[:, j].astype(np.int64)]
     if Ys is not None:
         y += Ys
     return store(y, storage)
@@ -438,12 +504,17 @@ def layer_forward(inp: dict, cfg, storage: str = None) -> dict:
     by moe_inputs.make_inputs."""
     storage = storage or storage_of(cfg)
     ffn_fwd = swiglu_ffn_fwd_mx if cfg.dtype == "mxfp8" else swiglu_ffn_fwd
+    fold = getattr(cfg, "fold_gates", False)
+    from_stored = getattr(cfg, "recompute_act", False)
     x = _np(inp["x"])
     T = x.shape[0]
     r = route(x, _np(inp["w_router"]), _np(inp.get("bias")), cfg, storage)
     p = permutation(r["idx"], cfg.E)
     Xp = permute_rows(x, p["src_token"])
     rows, f = T * cfg.k, cfg.f
+    # gate of each permuted row: row_gates[row(t, j)] = gates[t, j]
+    row_gates = np.zeros(rows)
+    row_gates[p["row_id_map"].reshape(-1).astype(np.int64)] = np.asarray(r["gates"], F64).reshape(-1)
     H = np.zeros((rows, f)); U = np.zeros((rows, f)); A = np.zeros((rows, f))
     Yp = np.zeros((rows, cfg.d))
     w13, w2 = inp["w13"], inp["w2"]
@@ -452,17 +523,18 @@ def layer_forward(inp: dict, cfg, storage: str = None) -> dict:
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
             continue
-        o = ffn_fwd(Xp[lo:hi], _np(w13[e]), _np(w2[e]), storage)
+        o = ffn_fwd(Xp[lo:hi], _np(w13[e]), _np(w2[e]), storage,
+                    gate=row_gates[lo:hi] if fold else None, act_from_stored=from_stored)
         H[lo:hi], U[lo:hi], A[lo:hi], Yp[lo:hi] = o["H"], o["U"], o["A"], o["Y"]
     out = dict(r)
     out.update(p)
-    out.update({"Xp": Xp, "H": H, "U": U, "A": A, "Yp": Yp})
+    out.update({"Xp": Xp, "H": H, "U": U, "A": A, "Yp": Yp, "row_gates": row_gates})
     Ys = None
     if cfg.f_shared > 0:
-        s = ffn_fwd(x, _np(inp["ws13"]), _np(inp["ws2"]), storage)
+        s = ffn_fwd(x, _np(inp["ws13"]), _np(inp["ws2"]), storage, act_from_stored=from_stored)
         out.update({"Hs": s["H"], "Us": s["U"], "As": s["A"], "Ys": s["Y"]})
         Ys = s["Y"]
-    out["y"] = combine(Yp, r["gates"], p["row_id_map"], Ys, storage)
+    out["y"] = combine(Yp, None if fold else r["gates"], p["row_id_map"], Ys, storage)
     if cfg.aux_coeff != 0.0:
         out["aux"] = aux_loss(r["probs"], p["counts"], T, cfg.k, cfg.aux_coeff)
     return out
@@ -522,6 +594,8 @@ def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
     the experts that received rows only (all others are exactly zero)."""
     storage = storage or storage_of(cfg)
     ffn_bwd = swiglu_ffn_bwd_mx if cfg.dtype == "mxfp8" else swiglu_ffn_bwd
+    fold = getattr(cfg, "fold_gates", False)
+    recompute = getattr(cfg, "recompute_act", False)
     exact = storage == "f64"
     x = _np(inp["x"])
     dy = _np(inp["dy"])
@@ -529,16 +603,18 @@ def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
     rmap = fwd["row_id_map"].astype(np.int64)
     gates = np.asarray(fwd["gates"], F64)
     Yp = fwd["Yp"]
-    # combine backward: dYp[row(t,j)] = g[t,j] dy[t]; dg[t,j] = <dy[t], Yp[row]>
+    rows = T * cfg.k
+    # combine backward: dYp[row(t,j)] = g[t,j] dy[t]; dg[t,j] = <dy[t], Yp[row]>.
+    # With folded gates the rows already carry g: dYp[row(t,j)] = dy[t], and dg
+    # comes from the experts' backward (R23).
     dYp = np.zeros_like(Yp)
     d_gates = np.zeros((T, cfg.k), F64)
     for j in range(cfg.k):
-        dYp[rmap[:, j]] = gates[:, j:j + 1] * dy
-        d_gates[:, j] = np.sum(dy * Yp[rmap[:, j]], axis=1)
+        dYp[rmap[:, j]] = dy if fold else gates[:, j:j + 1] * dy
+        if not fold:
+            d_gates[:, j] = np.sum(dy * Yp[rmap[:, j]], axis=1)
     dYp = store(dYp, storage)
-    if not exact:
-        d_gates = d_gates.astype(F32)
-    rows = T * cfg.k
+    row_dg = np.zeros(rows)
     dHU = np.zeros((rows, 2 * cfg.f))
     dXp32 = np.zeros((rows, d))
     dXp = np.zeros((rows, d))
@@ -546,21 +622,35 @@ def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
     dw2 = np.zeros(inp["w2"].shape) if dense else {}
     off = fwd["offsets"]
     Xp = fwd["Xp"]
+
+    def act_for_bwd(H, U, gate, A_fwd):
+        # with recomputation the backward forms act again from the stored H, U (R24)
+        return store(_act(H, U, gate), storage) if recompute else A_fwd
+
     for e in range(cfg.E):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
             continue            # empty expert: exact zero weight gradients
-        b = ffn_bwd(Xp[lo:hi], fwd["H"][lo:hi], fwd["U"][lo:hi], fwd["A"][lo:hi],
-                           dYp[lo:hi], _np(inp["w13"][e]), _np(inp["w2"][e]), storage)
+        g_rows = fwd["row_gates"][lo:hi] if fold else None
+        A_e = act_for_bwd(fwd["H"][lo:hi], fwd["U"][lo:hi], g_rows, fwd["A"][lo:hi])
+        b = ffn_bwd(Xp[lo:hi], fwd["H"][lo:hi], fwd["U"][lo:hi], A_e,
+                    dYp[lo:hi], _np(inp["w13"][e]), _np(inp["w2"][e]), storage, gate=g_rows)
         dHU[lo:hi] = np.concatenate([b["dH"], b["dU"]], axis=1)
         dXp32[lo:hi], dXp[lo:hi] = b["dX32"], b["dX"]
         dw13[e], dw2[e] = b["dW13"], b["dW2"]
+        if fold:
+            row_dg[lo:hi] = b["dg"]
+    if fold:
+        d_gates = row_dg[rmap]
+    if not exact:
+        d_gates = d_gates.astype(F32)
     out = {"dYp": dYp, "d_gates": d_gates, "dHU": dHU, "dXp": dXp,
            "dw13": dw13, "dw2": dw2}
     dx_partial = np.zeros((T, d))
     if cfg.f_shared > 0:
-        s = ffn_bwd(x, fwd["Hs"], fwd["Us"], fwd["As"], dy,
-                           _np(inp["ws13"]), _np(inp["ws2"]), storage)
+        As = act_for_bwd(fwd["Hs"], fwd["Us"], None, fwd["As"])
+        s = ffn_bwd(x, fwd["Hs"], fwd["Us"], As, dy,
+                    _np(inp["ws13"]), _np(inp["ws2"]), storage)
         out.update({"dHUs": np.concatenate([s["dH"], s["dU"]], axis=1),
                     "dws13": s["dW13"], "dws2": s["dW2"]})
         dx_partial += s["dX32"]

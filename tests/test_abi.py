@@ -108,15 +108,23 @@ def test_rejects_null_misaligned_and_small_workspace():
     assert st == abi.MOE_ERR_INVALID_ARGUMENT and "both" in abi.moe_last_error()
     st = L.moe_router_topk(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws - 1, None)
     assert st == abi.MOE_ERR_WORKSPACE_TOO_SMALL
-    st = L.moe_permute(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None)
+    st = L.moe_permute(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE, ws, None)
     assert st == abi.MOE_ERR_INVALID_ARGUMENT and "src_token" in abi.moe_last_error()
+    st = L.moe_permute(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "both" in abi.moe_last_error()
+    folded = abi.make_cfg(16, 64, 8, 2, 128, fold_gates=True)
+    st = L.moe_permute(ctypes.byref(folded), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "topk_gates" in abi.moe_last_error()
     shared = abi.make_cfg(16, 64, 8, 2, 128, f_shared=64)
-    st = L.moe_grouped_gemm_swiglu(ctypes.byref(shared), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+    st = L.moe_grouped_gemm_swiglu(ctypes.byref(shared), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None,
                                    FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None)
     assert st == abi.MOE_ERR_INVALID_ARGUMENT and "'x'" in abi.moe_last_error()
     cfg.dtype = 7
-    st = L.moe_permute(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    st = L.moe_permute(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None)
     assert st == abi.MOE_ERR_UNSUPPORTED
+    cfg.dtype, cfg.flags = abi.MOE_BF16, 8
+    st = L.moe_permute(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "flags" in abi.moe_last_error()
 
 
 @no_gpu
@@ -127,3 +135,43 @@ def test_valid_call_without_gpu_reports_device_error():
     assert st == abi.MOE_ERR_DEVICE
     assert abi.lib().moe_init(0) == abi.MOE_ERR_DEVICE
     del ws
+
+
+@no_gpu
+@pytest.mark.parametrize("shape", [
+    dict(T=65536, d=8192, E=64, k=8, f=2048),          # 524288 rows x 8192 x 2 B = 8 GiB of x_perm
+    dict(T=1024, d=16384, E=8, k=2, f=32768),          # one expert's W13: 65536 x 16384 x 2 B
+])
+def test_gemm_calls_reject_shapes_past_32bit_offsets(shape):
+    """The MFMA kernels address each expert's rows and weights with 32-bit
+    buffer ranges: shapes whose spans reach 2^31 bytes are rejected on the host."""
+    cfg = abi.make_cfg(**shape)
+    L = abi.lib()
+    st = L.moe_grouped_gemm_swiglu(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None, None,
+                                   None, None, None, None, FAKE, 1 << 40, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "32-bit" in abi.moe_last_error()
+    st = L.moe_grouped_gemm_swiglu_bwd(ctypes.byref(cfg), FAKE, FAKE, FAKE, None, None, *([FAKE] * 8), None,
+                                       *([None] * 7), FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == abi.MOE_ERR_INVALID_ARGUMENT and "32-bit" in abi.moe_last_error()
+    # the same shape scaled down passes validation and only fails for want of a device
+    small = abi.make_cfg(**dict(shape, T=64))
+    if 2 * shape["f"] * shape["d"] * 2 < (1 << 31):
+        st = L.moe_grouped_gemm_swiglu(ctypes.byref(small), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None,
+                                       None, None, None, None, None, FAKE, 1 << 40, None)
+        assert st == abi.MOE_ERR_DEVICE
+
+
+def test_binding_refuses_views_host_tensors_and_wrong_dtypes():
+    """The binding passes raw addresses: a strided view, a host tensor or a
+    tensor of the wrong element type would be misread, so it is refused."""
+    with pytest.raises(ValueError, match="contiguous"):
+        abi._ptr(torch.zeros(8, 4).t())
+    with pytest.raises(ValueError, match="contiguous"):
+        abi._ptr(torch.zeros(8, 8)[:, :4])
+    with pytest.raises(ValueError, match="device"):
+        abi._ptr(torch.zeros(8))
+    assert abi._ptr(None) is None and abi._ptr(1234) == 1234
+    cfg = abi.make_cfg(16, 64, 8, 2, 128)
+    with pytest.raises(ValueError):
+        abi.moe_permute(cfg, torch.zeros(16, 64, dtype=torch.bfloat16).t(), None, None, None, None, None, None,
+                        None, None)

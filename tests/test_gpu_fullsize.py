@@ -18,7 +18,8 @@ The MXFP8 workload (skewed DeepSeek-V3 routing with empty experts) is checked
 against the same oracle steps with MXFP8 GEMM operands.
 
 Tolerances: bf16 storage rel-L2 1e-2 (spec bound; MXFP8 against the
-same-quantisation oracle likewise); fp32 outputs 1e-5.
+same-quantisation oracle likewise), and 2e-2 on every single row of the
+expert products; fp32 outputs 1e-5.
 """
 from __future__ import annotations
 
@@ -28,12 +29,17 @@ import torch
 
 import moe_inputs as mi
 from oracle import moe_oracle as O
-from tests.harness import rel_l2, run_gpu_tensors
+from tests.harness import rel_l2, row_errors, run_gpu_tensors
 
 pytestmark = pytest.mark.gpu
 
 BF16_TOL = 1e-2
 F32_TOL = 1e-5
+# every row of a product computed from the GPU's own upstream tensors (both
+# sides round and quantise the same bits) stays within twice the tensor bound,
+# and every element within 4e-2 of itself or its row's RMS
+ROW_TOL = 2e-2
+ELEM_TOL = 4e-2
 
 
 def _h(t) -> np.ndarray:
@@ -121,6 +127,14 @@ def test_fullsize_sampled_parity(cfg):
     src = torch.as_tensor(perm["src_token"].astype(np.int64), device="cuda")
     assert torch.equal(b["x_perm"], inp["x"][src]), "x_perm is not a bit copy of x"
 
+    if cfg.bias == "zipf":
+        # the skewed workload: several experts without tokens, the hottest one
+        # above ten times the mean load
+        n_empty = int((counts == 0).sum())
+        print(f"  skew: {n_empty} empty experts, hottest {counts.max()} rows = "
+              f"{counts.max() / counts.mean():.1f} x mean", flush=True)
+        assert counts.min() == 0 and n_empty >= 3 and counts.max() > 10 * counts.mean()
+
     # -- routed experts -----------------------------------------------------
     off = perm["offsets"]
     experts = _sample_experts(counts, rng, n=3 if ops.mx else 4)
@@ -131,30 +145,45 @@ def test_fullsize_sampled_parity(cfg):
         xe = _h(b["x_perm"][rt])
         w13, w2 = _h(inp["w13"][e]), _h(inp["w2"][e])
         o = ops.ffn_fwd(xe, w13, w2, st)
+        err, rows_err, elem_err = {}, {}, {}
+
+        def cmp(name, got, want):
+            err[name] = rel_l2(got, want)
+            rows_err[name], elem_err[name] = row_errors(got, want)
+
         got_act, got_y = _h(b["act"][rt]), _h(b["y_perm"][rt])
-        err = {"A": rel_l2(got_act, o["A"]), "Y": rel_l2(got_y, O.store(ops.nt(got_act, w2), st))}
+        cmp("A", got_act, o["A"])
+        cmp("Y", got_y, O.store(ops.nt(got_act, w2), st))
         if bwd:
             hu = _h(b["hu"][rt])
-            err["H"], err["U"] = rel_l2(hu[:, :f], o["H"]), rel_l2(hu[:, f:], o["U"])
+            cmp("H", hu[:, :f], o["H"])
+            cmp("U", hu[:, f:], o["U"])
             ob = ops.ffn_bwd(xe, hu[:, :f], hu[:, f:], got_act, _h(b["dy_perm"][rt]), w13, w2, st)
             dhu = _h(b["dhu"][rt])
-            err["dH"], err["dU"] = rel_l2(dhu[:, :f], ob["dH"]), rel_l2(dhu[:, f:], ob["dU"])
-            err["dX"] = rel_l2(_h(b["dx_perm"][rt]), O.store(ops.nn(dhu, w13), st))   # from the GPU's own dH, dU
+            cmp("dH", dhu[:, :f], ob["dH"])
+            cmp("dU", dhu[:, f:], ob["dU"])
+            cmp("dX", _h(b["dx_perm"][rt]), O.store(ops.nn(dhu, w13), st))   # from the GPU's own dH, dU
             # weight-gradient rows contract over every row of the expert
             sl = slice(lo, hi)
             r13 = _pick(rng, 2 * f, 48)
             r2 = _pick(rng, d, 48)
             w_dw13 = O.store(ops.wgrad_rows(_h(b["dhu"][sl]), _h(b["x_perm"][sl]), r13), st)
             w_dw2 = O.store(ops.wgrad_rows(_h(b["dy_perm"][sl]), _h(b["act"][sl]), r2), st)
-            err["dW13"] = rel_l2(_h(b["dw13"][e][torch.as_tensor(r13, device="cuda")]), w_dw13)
-            err["dW2"] = rel_l2(_h(b["dw2"][e][torch.as_tensor(r2, device="cuda")]), w_dw2)
+            cmp("dW13", _h(b["dw13"][e][torch.as_tensor(r13, device="cuda")]), w_dw13)
+            cmp("dW2", _h(b["dw2"][e][torch.as_tensor(r2, device="cuda")]), w_dw2)
         print(f"  expert {e} rows {hi - lo}: " + " ".join(f"{k_}={v:.2e}" for k_, v in err.items()), flush=True)
+        print(f"  expert {e} worst row/element: " + " ".join(f"{k_}={rows_err[k_]:.1e}/{elem_err[k_]:.1e}"
+                                                         for k_ in rows_err), flush=True)
         for k_, v in err.items():
             assert v < BF16_TOL, (cfg.name, e, k_, v)
+        for k_ in rows_err:
+            assert rows_err[k_] < ROW_TOL and elem_err[k_] < ELEM_TOL, (cfg.name, e, k_, rows_err[k_], elem_err[k_])
     if bwd:
+        # every expert without rows has exact zero weight gradients
         empty = np.nonzero(counts == 0)[0]
-        for e in empty[:4]:
-            assert float(b["dw13"][int(e)].abs().max()) == 0.0 and float(b["dw2"][int(e)].abs().max()) == 0.0
+        if len(empty):
+            et = torch.as_tensor(empty, device="cuda")
+            assert int(torch.count_nonzero(b["dw13"][et])) == 0 and int(torch.count_nonzero(b["dw2"][et])) == 0
 
     # -- shared expert, combine ---------------------------------------------
     tt = torch.as_tensor(toks, device="cuda")

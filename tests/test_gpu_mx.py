@@ -17,7 +17,7 @@ import torch
 import moe_inputs as mi
 from mixture_experts_layer_limited_amd import _abi as abi
 from oracle import moe_oracle as O
-from tests.harness import compare_layer, rel_l2, run_gpu, run_oracle
+from tests.harness import compare_layer, mx_stepwise_check, rel_l2, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +73,9 @@ MX_CASES = [
          topk_group=2, renorm=True, scale=2.5, bias="zipf"),
     # softmax, no shared expert, a contraction of several 128-slices
     _cfg("mx_softmax", T=192, d=384, E=8, k=2, f=256, score="softmax"),
+    # gates folded into act and act formed again in the backward
+    _cfg("mx_dsv3_like_fold_recompute", T=256, d=256, E=32, k=4, f=128, f_shared=128, score="sigmoid",
+         n_group=4, topk_group=2, renorm=True, scale=2.5, bias="zipf", fold_gates=True, recompute_act=True),
 ]
 
 
@@ -86,9 +89,38 @@ def test_mx_layer_parity(cfg):
     counts = np.asarray(o["counts"])
     print(f"  rows per expert: min {counts.min()} max {counts.max()} empty {(counts == 0).sum()}", flush=True)
     compare_layer(cfg, g, o, backward=True)
+    mx_stepwise_check(cfg, inp, g)
     # against the bf16 oracle the forward output moves by the quantisation
     # itself: as far as the same-quantisation oracle moves (both reported)
     ob = run_oracle(cfg.with_(dtype="bf16"), inp, backward=False)
     e_gpu, e_orc = rel_l2(g["y"], ob["y"]), rel_l2(o["y"], ob["y"])
     print(f"  y vs bf16 oracle: GPU {e_gpu:.2e}, MX oracle {e_orc:.2e}", flush=True)
     assert e_gpu <= 1.1 * e_orc + 1e-3
+
+
+def test_mx_layer_requantises_changed_weights():
+    """The layer keeps the quantised copies of its expert weights only while it
+    is given the same, unmodified weight tensors: a forward with other weights,
+    or after an in-place update, must use the new values."""
+    _needs_gpu()
+    print("\n[mx layer] weights change between calls", flush=True)
+    from mixture_experts_layer_limited_amd import MoELayer
+    from tests.harness import shape_of, to_dev
+    cfg = MX_CASES[1]
+    layer = MoELayer(shape_of(cfg), "cuda", backward=False)
+
+    def check(inp, dev, what):
+        y = layer.forward(dev["x"], dev["w_router"], dev["bias"], dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+        torch.cuda.synchronize()
+        err = rel_l2(y.float().cpu().double().numpy(), O.layer_forward(inp, cfg)["y"])
+        print(f"  {what}: rel-L2 {err:.2e}", flush=True)
+        assert err <= 1e-2, what
+
+    inp0 = mi.make_inputs(cfg, seed=0, device="cpu")
+    check(inp0, to_dev(inp0), "weights of seed 0")
+    inp1 = mi.make_inputs(cfg, seed=1, device="cpu")
+    dev1 = to_dev(inp1)
+    check(inp1, dev1, "weights of seed 1")
+    dev1["w13"].mul_(0.5)                        # in place: the same tensor, a new version
+    inp1["w13"] = inp1["w13"] * 0.5              # exact in bf16 (a power of two)
+    check(inp1, dev1, "seed 1 with w13 halved in place")

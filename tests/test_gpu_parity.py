@@ -2,7 +2,7 @@
 
 Integer results (top-k ids, counts, offsets, row maps) are compared bit for
 bit; floating outputs and gradients by relative L2 error (1e-5 fp32, 1e-2
-bf16).  Layer-level cases use inputs on an exact grid (moe_inputs.
+bf16) over each whole tensor and, at twice that bound, over every row.  Layer-level cases use inputs on an exact grid (moe_inputs.
 exact_grid_inputs) so that the fp32 router logits -- and therefore every routing
 decision -- are the same on both sides whatever the summation order.
 """
@@ -36,6 +36,10 @@ ROUTER_CASES = [
     _cfg("softmax_k_eq_E_norenorm", T=70, E=6, k=6, renorm=False),
     _cfg("sigmoid_one_expert_groups", T=130, E=16, k=3, score="sigmoid", n_group=16, topk_group=4),
     _cfg("softmax_e200_k17", T=65, E=200, k=17),
+    # force-balanced routing: (t k + j) mod E whatever the keys; groups and bias ignored
+    _cfg("balanced_sigmoid_groups", T=300, E=256, k=8, score="sigmoid", n_group=8, topk_group=4, scale=2.5,
+         bias="normal", bias_std=0.01, force_balanced=True),
+    _cfg("balanced_softmax_aux", T=77, E=12, k=5, aux_coeff=1e-3, force_balanced=True),
 ]
 
 
@@ -46,7 +50,7 @@ def test_router_topk_from_logits_bitexact(cfg, ties):
     logits = mi.fixed_logits(cfg.T, cfg.E, seed=5, std=2.0, ties=ties)
     bias = mi.make_inputs(cfg, seed=5, experts=False)["bias"]
     o_keys = O.selection_keys(logits.numpy(), cfg, None if bias is None else bias.numpy())
-    o_idx = O.select_topk(o_keys, cfg)
+    o_idx = O.select_balanced(cfg.T, cfg.E, cfg.k) if cfg.force_balanced else O.select_topk(o_keys, cfg)
     o_g = O.gates_from_selection(logits.numpy(), o_idx, cfg)
     o_cnt = O.expert_counts(o_idx, cfg.E)
     c = shape_of(cfg).cfg()
@@ -109,7 +113,7 @@ def test_permute_bitexact(T, E, k):
     src = torch.empty(n, dtype=torch.int32, device=dev)
     xp = torch.empty(n, cfg.d, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(abi.moe_workspace_size(c), dtype=torch.uint8, device=dev)
-    abi.moe_permute(c, xd, idx, off, rmap, src, xp, ws)
+    abi.moe_permute(c, xd, idx, None, off, rmap, src, None, xp, ws)
     torch.cuda.synchronize()
     assert np.array_equal(host(off), p["offsets"])
     if T:
@@ -142,6 +146,38 @@ LAYER_CASES = [
     # experts of >= 512 rows on average and a wide dense shared expert: the
     # forward products run on 256-row tiles (with their own tile prefix)
     _cfg("bf16_big_experts_bwd", T=1024, d=128, E=2, k=2, f=256, f_shared=1024, backward=True),
+    # a single token: one row per chosen expert, the rest empty; dense shared
+    # products over one row
+    _cfg("bf16_one_token_bwd", T=1, d=128, E=8, k=2, f=64, aux_coeff=1e-3, backward=True),
+    _cfg("bf16_one_token_sigmoid_shared_bwd", T=1, d=128, E=16, k=4, f=64, f_shared=64, score="sigmoid",
+         n_group=4, topk_group=2, scale=2.5, bias="normal", bias_std=0.01, backward=True),
+    _cfg("f32_one_token_bwd", T=1, d=32, E=4, k=2, f=16, dtype="f32", backward=True),
+    # layer modes: gates folded into act (unweighted combine, gate gradient from the
+    # experts' backward), act formed again in the backward, force-balanced routing
+    _cfg("f32_fold_recompute_sigmoid_shared_bwd", T=160, d=64, E=16, k=4, f=48, f_shared=32, dtype="f32",
+         score="sigmoid", n_group=4, topk_group=2, scale=2.5, bias="normal", bias_std=0.05, backward=True,
+         fold_gates=True, recompute_act=True),
+    _cfg("f32_fold_softmax_aux_bwd", T=130, d=32, E=8, k=2, f=40, dtype="f32", aux_coeff=1e-2, backward=True,
+         fold_gates=True),
+    _cfg("bf16_fold_dsv3_like_bwd", T=256, d=384, E=32, k=8, f=256, f_shared=256, score="sigmoid", n_group=8,
+         topk_group=4, scale=2.5, bias="normal", bias_std=0.01, backward=True, expert_std=0.02,
+         router_std=0.02, fold_gates=True),
+    _cfg("bf16_recompute_dsv3_like_bwd", T=256, d=384, E=32, k=8, f=256, f_shared=256, score="sigmoid",
+         n_group=8, topk_group=4, scale=2.5, bias="normal", bias_std=0.01, backward=True, expert_std=0.02,
+         router_std=0.02, recompute_act=True),
+    _cfg("bf16_fold_recompute_qwen3_like_bwd", T=300, d=256, E=16, k=4, f=192, aux_coeff=1e-3, backward=True,
+         fold_gates=True, recompute_act=True),
+    _cfg("bf16_fold_mostly_empty_bwd", T=40, d=128, E=64, k=2, f=64, backward=True, fold_gates=True,
+         recompute_act=True),
+    _cfg("bf16_fold_big_experts_bwd", T=1024, d=128, E=2, k=2, f=256, f_shared=1024, backward=True,
+         fold_gates=True, recompute_act=True),
+    _cfg("bf16_fold_one_token_bwd", T=1, d=128, E=8, k=2, f=64, backward=True, fold_gates=True,
+         recompute_act=True),
+    _cfg("bf16_balanced_sigmoid_shared_bwd", T=256, d=256, E=32, k=8, f=128, f_shared=128, score="sigmoid",
+         n_group=8, topk_group=4, scale=2.5, bias="normal", bias_std=0.01, backward=True,
+         force_balanced=True),
+    _cfg("bf16_balanced_fold_recompute_bwd", T=200, d=192, E=10, k=3, f=128, aux_coeff=1e-3, backward=True,
+         force_balanced=True, fold_gates=True, recompute_act=True),
 ]
 
 
@@ -170,3 +206,51 @@ def test_layer_deterministic():
     b = run_gpu(cfg, inp, True)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_router_bias_update_bitexact():
+    """moe_router_bias_update against the oracle's rule, bit for bit, on counts
+    below, at and above the mean load."""
+    print("case router bias update", flush=True)
+    T, k, E = 96, 4, 24                                 # mean load 16
+    rng = np.random.default_rng(9)
+    counts = rng.integers(0, 40, E).astype(np.int32)
+    counts[:3] = 16
+    bias = rng.normal(0, 0.05, E).astype(np.float32)
+    cfg = abi.make_cfg(T, 64, E, k, 64, score="sigmoid")
+    b = torch.from_numpy(bias).cuda()
+    abi.moe_router_bias_update(cfg, torch.from_numpy(counts).cuda(), 1e-3, b)
+    torch.cuda.synchronize()
+    want = O.bias_update(bias, counts, T, k, 1e-3)
+    assert np.array_equal(b.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(b.cpu().numpy()[:3], bias[:3])
+
+
+def test_recompute_reforms_the_forward_act_bit_for_bit():
+    """With act recomputation the forward forms act from the stored H, U and the
+    backward forms it again into its workspace: the backward's results must be
+    the same bits as a backward that reads the forward's act (same kernels
+    otherwise), with and without folded gates."""
+    from mixture_experts_layer_limited_amd import MoELayer
+    from harness import to_dev
+    for fold in (False, True):
+        cfg = _cfg("recompute_bits", T=300, d=256, E=16, k=4, f=192, f_shared=128, score="sigmoid", n_group=4,
+                   topk_group=2, scale=2.5, bias="normal", bias_std=0.01, backward=True, fold_gates=fold,
+                   recompute_act=True)
+        print(f"case recompute bit-exact fold={fold}", flush=True)
+        dev = to_dev(mi.make_inputs(cfg, seed=2))
+        layer = MoELayer(shape_of(cfg), "cuda", backward=True)
+        layer.forward(dev["x"], dev["w_router"], dev["bias"], dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+        layer.backward(dev["dy"], dev["x"], dev["w_router"], dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+        torch.cuda.synchronize()
+        got = {k: layer.buf[k].clone() for k in ("dw2", "dws2", "dw13", "dhu", "dx_perm")}
+        b = layer.buf
+        plain = shape_of(cfg.with_(recompute_act=False)).cfg()
+        abi.moe_grouped_gemm_swiglu_bwd(
+            plain, b["dy_perm"], b["x_perm"], b["offsets"], b["row_gates"] if fold else None,
+            b["row_id_map"] if fold else None, b["hu"], b["act"], dev["w13"], dev["w2"], b["dhu"], b["dx_perm"],
+            b["dw13"], b["dw2"], b["d_gates"] if fold else None, dev["dy"], dev["x"], b["hu_s"], b["act_s"],
+            dev["ws13"], dev["ws2"], b["dhu_s"], b["dx_partial"], b["dws13"], b["dws2"], layer.ws)
+        torch.cuda.synchronize()
+        for k, v in got.items():
+            assert torch.equal(v, layer.buf[k]), k

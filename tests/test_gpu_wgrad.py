@@ -65,9 +65,9 @@ def test_expert_wgrad_parity(name, d, f):
     dw2 = torch.full((E, d, f), 7.0, dtype=torch.bfloat16, device=dev)
     dx_partial = torch.empty(rows, d, dtype=torch.float32, device=dev)   # zero-filled by the call
     ws = torch.empty(abi.moe_workspace_size(c), dtype=torch.uint8, device=dev)
-    abi.moe_grouped_gemm_swiglu_bwd(c, D["dy_perm"], D["x_perm"], off, D["hu"], D["act"], D["w13"], D["w2"],
-                                    dhu, dx_perm, dw13, dw2, None, None, None, None, None, None, None,
-                                    dx_partial, None, None, ws)
+    abi.moe_grouped_gemm_swiglu_bwd(c, D["dy_perm"], D["x_perm"], off, None, None, D["hu"], D["act"], D["w13"],
+                                    D["w2"], dhu, dx_perm, dw13, dw2, None, None, None, None, None, None, None,
+                                    None, dx_partial, None, None, ws)
     torch.cuda.synchronize()
 
     g_dhu, g_dw13, g_dw2 = host(dhu), host(dw13), host(dw2)
@@ -126,8 +126,8 @@ def test_shared_expert_dense_wgrad():
     dws2 = torch.full((d, fs), 7.0, dtype=torch.bfloat16, device=dev)
     dx_partial = torch.empty(T, d, dtype=torch.float32, device=dev)
     ws = torch.empty(abi.moe_workspace_size(c), dtype=torch.uint8, device=dev)
-    abi.moe_grouped_gemm_swiglu_bwd(c, D["dy"], D["x"], off, D["hu"], D["act"], D["w13"], D["w2"],
-                                    dhu, dx_perm, dw13, dw2, D["dy"], D["x"], D["hu_s"], D["act_s"],
+    abi.moe_grouped_gemm_swiglu_bwd(c, D["dy"], D["x"], off, None, None, D["hu"], D["act"], D["w13"], D["w2"],
+                                    dhu, dx_perm, dw13, dw2, None, D["dy"], D["x"], D["hu_s"], D["act_s"],
                                     D["ws13"], D["ws2"], dhu_s, dx_partial, dws13, dws2, ws)
     torch.cuda.synchronize()
 
