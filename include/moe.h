@@ -235,6 +235,23 @@ moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm,
                                    void* hu_shared_save, void* act_shared, void* y_shared,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_grouped_gemm_swiglu for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, kernels and results (bit-identical), with
+ * no workspace argument.  Its scratch (the tile prefix, E + 2 ints) lives in a
+ * static device array of 4 KiB inside the library, one per GPU, held until
+ * the process ends; the call allocates nothing.  cfg.dtype MOE_F32 or MOE_BF16
+ * (MOE_MXFP8 -> MOE_ERR_UNSUPPORTED); E + 2 above the array's 1024 ints ->
+ * MOE_ERR_INVALID_ARGUMENT (unreachable while E <= 256).  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different streams
+ * without ordering between them) race. */
+moe_status moe_grouped_gemm_swiglu_noalloc(const moe_cfg* cfg, const void* x_perm,
+                                           const int32_t* expert_offsets, const float* row_gates,
+                                           const void* w13, const void* w2, void* hu_save, void* act,
+                                           void* y_perm, const void* x, const void* ws13, const void* ws2,
+                                           void* hu_shared_save, void* act_shared, void* y_shared,
+                                           void* stream);
+
 /* ---------------------------------------------------------------------------
  * Unpermute-combine ("System Modules: Combiner": tokens go back to their
  * original position and the gate-weighted sum is formed).

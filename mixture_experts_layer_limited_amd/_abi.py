@@ -56,6 +56,7 @@ _SIGS = {
     "moe_router_bias_update": (ctypes.c_int, [ctypes.POINTER(moe_cfg), _P, ctypes.c_float, _P, _P]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]),
     "moe_grouped_gemm_swiglu": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 14 + [_P, ctypes.c_size_t, _P]),
+    "moe_grouped_gemm_swiglu_noalloc": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 14 + [_P]),
     "moe_unpermute_combine": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 5 + [_P]),
     "moe_unpermute_combine_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 6 + [_P]),
     "moe_grouped_gemm_swiglu_bwd": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 24 + [_P, ctypes.c_size_t, _P]),
@@ -207,6 +208,16 @@ def moe_grouped_gemm_swiglu(cfg, x_perm, expert_offsets, row_gates, w13, w2, hu_
         _ptr(hu_save, S), _ptr(act, S), _ptr(y_perm, S), _ptr(x, S), _ptr(ws13, S), _ptr(ws2, S),
         _ptr(hu_shared_save, S), _ptr(act_shared, S), _ptr(y_shared, S), w, n, _stream(stream)),
         "moe_grouped_gemm_swiglu")
+
+
+def moe_grouped_gemm_swiglu_noalloc(cfg, x_perm, expert_offsets, row_gates, w13, w2, hu_save, act, y_perm, x,
+                                    ws13, ws2, hu_shared_save, act_shared, y_shared, stream=None):
+    S = _st(cfg)
+    _check(lib().moe_grouped_gemm_swiglu_noalloc(
+        ctypes.byref(cfg), _ptr(x_perm, S), _ptr(expert_offsets, _I32), _ptr(row_gates, _F32), _ptr(w13, S),
+        _ptr(w2, S), _ptr(hu_save, S), _ptr(act, S), _ptr(y_perm, S), _ptr(x, S), _ptr(ws13, S), _ptr(ws2, S),
+        _ptr(hu_shared_save, S), _ptr(act_shared, S), _ptr(y_shared, S), _stream(stream)),
+        "moe_grouped_gemm_swiglu_noalloc")
 
 
 def moe_unpermute_combine(cfg, y_perm, row_id_map, topk_gates, y_shared, y, stream=None):

@@ -504,6 +504,34 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
   return ok();
 }
 
+// ---- the grouped-GEMM forward without a caller workspace ----------------------
+// Its one scratch buffer, the device-built tile prefix (E + 2 <= 258 ints), lives
+// in this file-scope device array instead: every GPU the library runs on holds
+// its own copy until the process ends.  Host code never uses the array's name
+// as an address (on the host it is only a stand-in): the device address of each
+// GPU's copy is looked up once, with that device current, and kept per device.
+constexpr int kNoAllocScratchInts = 1024;            // 4 KiB
+static __device__ __align__(256) int g_noalloc_scratch[kNoAllocScratchInts];
+void* g_noalloc_ptr[kMaxDevices] = {};
+std::mutex g_noalloc_mu;
+
+moe_status noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_INVALID_ARGUMENT, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_noalloc_scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return MOE_OK;
+}
+
 moe_status check_mx_tensor(const moe_mx_tensor& t, const char* name) {
   if (!t.codes || !t.scales) return fail(MOE_ERR_INVALID_ARGUMENT, "weights.%s: codes and scales must not be NULL", name);
   if (((uintptr_t)t.codes & 15) || ((uintptr_t)t.scales & 3))
@@ -654,6 +682,37 @@ moe_status moe_grouped_gemm_swiglu(const moe_cfg* cfg, const void* x_perm, const
                                ws2, hu_shared_save, act_shared, y_shared, workspace, st);
   return gemm_fwd_impl<float>(cfg, x_perm, expert_offsets, row_gates, w13, w2, hu_save, act, y_perm, x, ws13,
                               ws2, hu_shared_save, act_shared, y_shared, workspace, st);
+}
+
+moe_status moe_grouped_gemm_swiglu_noalloc(const moe_cfg* cfg, const void* x_perm,
+                                           const int32_t* expert_offsets, const float* row_gates,
+                                           const void* w13, const void* w2, void* hu_save, void* act,
+                                           void* y_perm, const void* x, const void* ws13, const void* ws2,
+                                           void* hu_shared_save, void* act_shared, void* y_shared,
+                                           void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_not_mx(cfg));
+  CHECK(check_gemm_shapes(cfg));
+  REQ(x_perm); REQ(expert_offsets); REQ(w13); REQ(w2); REQ(act); REQ(y_perm);
+  if (fold(cfg)) REQ(row_gates);
+  ALIGNED(x_perm); ALIGNED(w13); ALIGNED(w2); ALIGNED(hu_save); ALIGNED(act); ALIGNED(y_perm);
+  if (cfg->f_shared > 0) {
+    REQ(x); REQ(ws13); REQ(ws2); REQ(act_shared); REQ(y_shared);
+    ALIGNED(x); ALIGNED(ws13); ALIGNED(ws2); ALIGNED(hu_shared_save); ALIGNED(act_shared); ALIGNED(y_shared);
+  }
+  // the forward's scratch is the tile prefix: E + 2 ints
+  if (cfg->E + 2 > kNoAllocScratchInts)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "E = %lld needs %lld scratch ints, the static scratch holds %d",
+                (long long)cfg->E, (long long)cfg->E + 2, kNoAllocScratchInts);
+  CHECK(check_current_device());
+  void* scratch = nullptr;
+  CHECK(noalloc_scratch(&scratch));
+  hipStream_t st = (hipStream_t)stream;
+  if (cfg->dtype != MOE_F32)
+    return gemm_fwd_impl<bf16>(cfg, x_perm, expert_offsets, row_gates, w13, w2, hu_save, act, y_perm, x, ws13,
+                               ws2, hu_shared_save, act_shared, y_shared, scratch, st);
+  return gemm_fwd_impl<float>(cfg, x_perm, expert_offsets, row_gates, w13, w2, hu_save, act, y_perm, x, ws13,
+                              ws2, hu_shared_save, act_shared, y_shared, scratch, st);
 }
 
 moe_status moe_unpermute_combine(const moe_cfg* cfg, const void* y_perm, const int32_t* row_id_map,
