@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm_band.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "2157eafbf987008b86a6b8f25cbce1febc6da0f2db6a5fbf3fedc2c6bea2f5e0",
-                          "fetch_bytes": 772583807, "write_bytes": 15032406176},
+    "gemm_wgrad_gateup": {"src_sha": "eff7f6ad2fe3aac98d922d92acab72bd572d042529375adff9e593375372a469",
+                          "fetch_bytes": 772643948, "write_bytes": 15032409376},
 }
 
 
@@ -145,49 +145,103 @@ def bandwidth_work(cfg: mi.MoEConfig) -> dict:
     }
 
 
-def cpu_baseline(cfg, dev_inp, sample_tokens: int) -> dict:
-    """Time the CPU oracle (as it stands) on the first `sample_tokens` tokens of
-    the same workload: full router over all experts, the sampled tokens' experts
-    and the shared expert, forward and backward."""
+def _threads() -> int:
+    try:
+        import threadpoolctl
+        return max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(cfg, dev_inp, backward: bool, flop_budget: float) -> dict:
+    """Time the CPU oracle (as it stands: numpy float64) on a bounded sample of
+    the same workload, as an algorithmic-FLOP rate in the metric's unit:
+
+    * the router (logits, scores, selection, gates) and the permutation of all
+      T tokens;
+    * the SwiGLU forward (+ backward) of a sample of experts with all of their
+      rows, experts taken evenly over the id range until the sample's FLOPs
+      pass `flop_budget`; each expert's bf16 weights and rows are converted to
+      float64 before its timed calls (the conversion is not timed);
+    * the shared expert on the same fraction of the tokens.
+    """
     from oracle import moe_oracle as O
     import numpy as np
 
-    Ts = sample_tokens
-    scfg = cfg.with_(T=Ts)
-    x = dev_inp["x"][:Ts].float().cpu()
-    wr = dev_inp["w_router"].float().cpu()
-    bias = None if dev_inp["bias"] is None else dev_inp["bias"].cpu()
-    # which experts the sample reaches (routing input only; the timed run routes again)
-    r = O.route(O._np(x), O._np(wr), O._np(bias), scfg)
-    used = sorted(set(np.asarray(r["idx"]).ravel().tolist()))
+    f64 = lambda t: t.float().cpu().double().numpy()
+    T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.f_shared
+    x, wr = f64(dev_inp["x"]), f64(dev_inp["w_router"])
+    bias = None if dev_inp["bias"] is None else dev_inp["bias"].cpu().numpy()
+    dy = f64(dev_inp["dy"]) if backward else None
+    mx = cfg.dtype == "mxfp8"
+    ffn_fwd = O.swiglu_ffn_fwd_mx if mx else O.swiglu_ffn_fwd
+    ffn_bwd = O.swiglu_ffn_bwd_mx if mx else O.swiglu_ffn_bwd
 
-    class Experts:
-        """Host copies of the experts the sample uses (bf16 values, copied
-        before timing); indexing any other expert is an error."""
-        def __init__(self, t):
-            self.shape = tuple(t.shape)
-            self.h = {e: t[e].cpu() for e in used}
-
-        def __getitem__(self, e):
-            return self.h[e]
-
-    inp = {"x": x, "w_router": wr, "bias": bias, "w13": Experts(dev_inp["w13"]),
-           "w2": Experts(dev_inp["w2"]), "dy": dev_inp["dy"][:Ts].float().cpu(),
-           "ws13": None if dev_inp["ws13"] is None else dev_inp["ws13"].cpu(),
-           "ws2": None if dev_inp["ws2"] is None else dev_inp["ws2"].cpu()}
-    try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        threads = os.cpu_count() or 1
     t0 = time.perf_counter()
-    fwd = O.layer_forward(inp, scfg)
-    O.layer_backward(inp, fwd, scfg, dense=False)
-    dt = time.perf_counter() - t0
-    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "tflops": step_flops(scfg) / dt / 1e12,
-            "sample": f"first {Ts} of {cfg.T} tokens of the {cfg.name} workload, fwd+bwd "
-                      f"({len(used)} experts reached + shared), numpy float64, {dt:.1f} s"}
+    r = O.route(x, wr, bias, cfg)
+    p = O.permutation(r["idx"], E)
+    t_router = time.perf_counter() - t0
+    flops = 2.0 * T * d * E
+    timed = t_router
+
+    counts = np.asarray(p["counts"])
+    order = [e for e in np.argsort(np.arange(E) * 7919 % E) if counts[e] > 0]   # spread over the ids
+    used, rows_done = [], 0
+    for e in order:
+        if flops >= flop_budget:
+            break
+        lo, hi = int(p["offsets"][e]), int(p["offsets"][e + 1])
+        src = p["src_token"][lo:hi].astype(np.int64)
+        xe = x[src]
+        w13, w2 = f64(dev_inp["w13"][int(e)]), f64(dev_inp["w2"][int(e)])
+        if backward:
+            g = np.zeros(hi - lo)
+            for j in range(k):                         # the gate of each of the expert's rows
+                hit = r["idx"][src, j] == e
+                g[hit] = np.asarray(r["gates"], np.float64)[src[hit], j]
+            dye = O.store(g[:, None] * dy[src], "bf16")
+        t0 = time.perf_counter()
+        o = ffn_fwd(xe, w13, w2, "bf16")
+        if backward:
+            ffn_bwd(xe, o["H"], o["U"], o["A"], dye, w13, w2, "bf16")
+        timed += time.perf_counter() - t0
+        flops += (18.0 if backward else 6.0) * (hi - lo) * d * f
+        used.append(int(e))
+        rows_done += hi - lo
+        print(f"# cpu baseline: expert {int(e)} ({hi - lo} rows) done, {timed:.1f} s", file=sys.stderr, flush=True)
+    ts = 0
+    if fs:
+        ts = max(1, round(T * len(used) / E))
+        ws13, ws2 = f64(dev_inp["ws13"]), f64(dev_inp["ws2"])
+        t0 = time.perf_counter()
+        o = ffn_fwd(x[:ts], ws13, ws2, "bf16")
+        if backward:
+            ffn_bwd(x[:ts], o["H"], o["U"], o["A"], dy[:ts], ws13, ws2, "bf16")
+        timed += time.perf_counter() - t0
+        flops += (18.0 if backward else 6.0) * ts * d * fs
+    return {"value": round(flops / timed / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "seconds": round(timed, 2),
+            "sample": f"{cfg.name} {'fwd+bwd' if backward else 'fwd'}: router + permutation of all {T} tokens "
+                      f"({t_router:.1f} s), the experts' SwiGLU {'fwd+bwd' if backward else 'fwd'} for "
+                      f"{len(used)} of {E} experts with all their rows ({rows_done} of {T * k} rows)"
+                      + (f", the shared expert on {ts} tokens" if fs else "")
+                      + "; numpy float64, bf16->float64 weight conversion outside the timed region"}
+
+
+def cpu_baseline_tiny() -> dict:
+    """The oracle on the whole tiny workload (T=128, d=64, E=8, k=2, f=128,
+    fp32, forward): median of three runs."""
+    from oracle import moe_oracle as O
+    cfg = mi.TINY
+    inp = mi.make_inputs(cfg, seed=0)
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        O.layer_forward(inp, cfg)
+        ts.append(time.perf_counter() - t0)
+    t = sorted(ts)[1]
+    return {"workload": "tiny fwd, whole", "seconds": round(t, 4), "tokens_per_s": round(cfg.T / t, 1),
+            "tflops": round(step_flops(cfg, backward=False) / t / 1e12, 6), "cores": _threads()}
 
 
 def main():
@@ -196,8 +250,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="deepseek_v3", choices=sorted(mi.CONFIGS))
+    ap.add_argument("--pass", dest="passes", default="auto", choices=["auto", "fwd", "fwd+bwd"],
+                    help="auto: the workload's own pass (forward only for the Mixtral shape)")
+    ap.add_argument("--fold-gates", action="store_true", help="gates applied to act before the down projection")
+    ap.add_argument("--recompute-act", action="store_true", help="the backward forms act again from H, U")
+    ap.add_argument("--force-balanced", action="store_true", help="round-robin expert assignment")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4)
+    ap.add_argument("--cpu-flop-budget", type=float, default=0.0,
+                    help="algorithmic FLOPs of the oracle's expert sample (default 2e12 for bf16 layers, "
+                         "1.5e11 for MXFP8, whose oracle quantises every operand in numpy: about 10-60 s "
+                         "on 16 cores)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cold-steps", type=int, default=3,
                     help="extra steps after the timed ones, each after a 512 MiB write that evicts "
@@ -222,15 +284,18 @@ def main():
 
     from mixture_experts_layer_limited_amd import LayerShape, MoELayer, _abi as abi
 
-    cfg = mi.CONFIGS[args.workload]
+    cfg = mi.CONFIGS[args.workload].with_(fold_gates=args.fold_gates, recompute_act=args.recompute_act,
+                                           force_balanced=args.force_balanced)
+    backward = cfg.backward if args.passes == "auto" else args.passes == "fwd+bwd"
     mx = cfg.dtype == "mxfp8"
     torch.cuda.set_device(0)
     print(f"# generating {cfg.name} inputs on the GPU", file=sys.stderr, flush=True)
     inp = mi.make_inputs(cfg, seed=args.seed, device="cuda", with_grad_inputs=True)
     shape = LayerShape(T=cfg.T, d=cfg.d, E=cfg.E, k=cfg.k, f=cfg.f, f_shared=cfg.f_shared, score=cfg.score,
                        n_group=cfg.n_group, topk_group=cfg.topk_group, renorm=cfg.renorm, scale=cfg.scale,
-                       aux_coeff=cfg.aux_coeff, dtype=cfg.dtype)
-    layer = MoELayer(shape, "cuda", backward=True)
+                       aux_coeff=cfg.aux_coeff, dtype=cfg.dtype, force_balanced=cfg.force_balanced,
+                       fold_gates=cfg.fold_gates, recompute_act=cfg.recompute_act)
+    layer = MoELayer(shape, "cuda", backward=backward)
     a = inp
     quant_ms = None
     if mx:
@@ -249,7 +314,8 @@ def main():
 
     def step():
         layer.forward(a["x"], a["w_router"], a["bias"], a["w13"], a["w2"], a["ws13"], a["ws2"])
-        layer.backward(a["dy"], a["x"], a["w_router"], a["w13"], a["w2"], a["ws13"], a["ws2"], d_aux=1.0)
+        if backward:
+            layer.backward(a["dy"], a["x"], a["w_router"], a["w13"], a["w2"], a["ws13"], a["ws2"], d_aux=1.0)
 
     for i in range(args.warmup):
         step()
@@ -294,7 +360,7 @@ def main():
         del flush
         cold.sort()
 
-    flops = step_flops(cfg)
+    flops = step_flops(cfg, backward)
     tflops = flops / (ms * 1e-3) / 1e12
     per_kernel = {}
     for name, t in trace:
@@ -350,9 +416,11 @@ def main():
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp8" if mx else "bf16", "data": "synthetic",
-        "config": {"workload": f"{cfg.name} MoE layer fwd+bwd", "T": cfg.T, "d": cfg.d, "E": cfg.E,
+        "config": {"workload": f"{cfg.name} MoE layer {'fwd+bwd' if backward else 'fwd'}", "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "k": cfg.k, "f": cfg.f, "f_shared": cfg.f_shared, "score": cfg.score,
-                   "n_group": cfg.n_group, "topk_group": cfg.topk_group, "parallelism": "none (1 GPU)"},
+                   "n_group": cfg.n_group, "topk_group": cfg.topk_group, "parallelism": "none (1 GPU)",
+                   "pass": "fwd+bwd" if backward else "fwd", "fold_gates": cfg.fold_gates,
+                   "recompute_act": cfg.recompute_act, "force_balanced": cfg.force_balanced},
         "step_ms": {"median": round(pct(per_step, 0.5), 4), "p10": round(pct(per_step, 0.1), 4),
                     "p90": round(pct(per_step, 0.9), 4)} if per_step else None,
         "cold_ms_per_step": round(pct(cold, 0.5), 4) if cold else None,
@@ -364,14 +432,11 @@ def main():
     }
     if quant_ms is not None:
         out["weight_quant_ms"] = round(quant_ms, 3)
-    if mx and args.cpu_sample_tokens == 4 and not args.no_cpu_baseline:
-        # the MXFP8 oracle quantises every expert weight it touches (~1 min per
-        # token at this shape): only on request with an explicit sample size
-        out["cpu_baseline"] = None
-        args.no_cpu_baseline = True
     if not args.no_cpu_baseline:
-        print("# cpu baseline (oracle on a token sample)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+        print("# cpu baseline (the oracle on a bounded sample of the workload)", file=sys.stderr, flush=True)
+        budget = args.cpu_flop_budget or (1.5e11 if mx else 2e12)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, backward, budget)
+        out["cpu_baseline"]["tiny_whole"] = cpu_baseline_tiny()
     print(json.dumps(out), flush=True)
 
 
