@@ -46,6 +46,11 @@ bias, 8 groups / top-4 by top-2 sum, renormalise then x2.5, aux coefficient
       first row, rows past its end count as zeros
   R17 expert weights enter the MXFP8 GEMMs quantised along whichever of their
       dimensions the GEMM contracts
+  R25 MXFP4 (the gfx950 counterpart of the NVFP4 the pages support): the R15
+      block structure with fp4 e2m1 elements (largest magnitude 6), e the
+      smallest integer with 6 * 2^e >= block amax; the same seven expert
+      products as MXFP8; codes stored two per byte, element 2i in the low
+      nibble
   R21 force-balanced routing (the benchmark condition of Table 11): choice j of
       token t goes to expert (t k + j) mod E, so every expert gets T k / E rows
       when E divides T k; gates come from the scores of the assigned experts
@@ -401,84 +406,160 @@ def e4m3_encode(v) -> np.ndarray:
     return np.where(np.signbit(v), c | np.uint8(0x80), c).astype(np.uint8)
 
 
-def mx_scale_exp(amax) -> np.ndarray:
-    """Smallest integer e with 448 * 2^e >= amax, clamped to [-127, 127]
-    (amax = 0 gives -127).  Stored as the e8m0 byte e + 127."""
+# ----------------------------------------------------------------------------
+# MXFP4 (R25): the same block structure with fp4 e2m1 elements -- one sign
+# bit, two exponent bits (bias 1), one mantissa bit, no infinities or NaN;
+# magnitudes 0, 0.5 (the one subnormal), 1, 1.5, 2, 3, 4, 6
+# ----------------------------------------------------------------------------
+E2M1_MAX = 6.0
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of each 4-bit e2m1 code (the low nibble of the byte): exponent
+    field 0 is subnormal, m/2; otherwise (1 + m/2) * 2^(ex - 1)."""
+    c = np.asarray(codes, np.uint8).astype(np.int64) & 15
+    sgn = np.where(c >> 3, -1.0, 1.0)
+    ex = (c >> 1) & 3
+    man = c & 1
+    mag = np.where(ex == 0, man / 2.0, (1.0 + man / 2.0) * np.exp2(ex - 1.0))
+    return sgn * mag
+
+
+def e2m1_encode(v) -> np.ndarray:
+    """Round each finite value to the nearest e2m1 value (ties to the code
+    with an even mantissa bit, i.e. an even code), saturating at +-6; the sign
+    of zero is kept.  Found by searching the table of the 8 magnitudes."""
+    v = np.asarray(v, F64)
+    codes = np.arange(8, dtype=np.uint8)
+    mags = e2m1_decode(codes)
+    a = np.minimum(np.abs(v), E2M1_MAX)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, len(mags) - 1)
+    lo = np.clip(hi - 1, 0, len(mags) - 1)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
+    c = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    return np.where(np.signbit(v), c | np.uint8(0x8), c).astype(np.uint8)
+
+
+def pack_e2m1(codes) -> np.ndarray:
+    """Two codes per byte along the last axis (even length): element 2i in the
+    low nibble, 2i+1 in the high nibble -- the storage form of MXFP4 codes."""
+    c = np.asarray(codes, np.uint8)
+    return (c[..., 0::2] & 15) | ((c[..., 1::2] & 15) << 4)
+
+
+def unpack_e2m1(packed) -> np.ndarray:
+    b = np.asarray(packed, np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+# element formats of the microscaled GEMM operands: largest magnitude, encoder, decoder
+MX_FORMATS = {
+    "e4m3": (E4M3_MAX, e4m3_encode, e4m3_decode),   # MXFP8 (R15)
+    "e2m1": (E2M1_MAX, e2m1_encode, e2m1_decode),   # MXFP4 (R25)
+}
+
+
+def mx_scale_exp(amax, fmt: str = "e4m3") -> np.ndarray:
+    """Smallest integer e with emax * 2^e >= amax (emax: the format's largest
+    magnitude, 448 for e4m3 and 6 for e2m1), clamped to [-127, 127] (amax = 0
+    gives -127).  Stored as the e8m0 byte e + 127."""
+    top = MX_FORMATS[fmt][0]
     amax = np.asarray(amax, F64)
     with np.errstate(divide="ignore"):
-        e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / E4M3_MAX))
+        e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / top))
     # the float log2 may sit one off near powers of two: settle on the exact rule
-    e = np.where(E4M3_MAX * np.exp2(e) < amax, e + 1, e)
-    e = np.where(E4M3_MAX * np.exp2(e - 1) >= amax, e - 1, e)
+    e = np.where(top * np.exp2(e) < amax, e + 1, e)
+    e = np.where(top * np.exp2(e - 1) >= amax, e - 1, e)
     e = np.where(amax > 0, e, -127.0)
     return np.clip(e, -127, 127).astype(np.int64)
 
 
-def mx_quantize(a, axis: int):
-    """Codes and e8m0 scale bytes of `a` with blocks of 32 consecutive values
-    along `axis`, the first block starting at index 0 of that axis and a short
-    last block padded with zeros.  Returns (codes shaped like a, scale bytes
-    with the blocked axis of length ceil(n/32))."""
+def mx_quantize(a, axis: int, fmt: str = "e4m3"):
+    """Codes (one per value, unpacked) and e8m0 scale bytes of `a` with blocks
+    of 32 consecutive values along `axis`, the first block starting at index 0
+    of that axis and a short last block padded with zeros.  Returns (codes
+    shaped like a, scale bytes with the blocked axis of length ceil(n/32))."""
+    encode = MX_FORMATS[fmt][1]
     a = np.moveaxis(np.asarray(a, F64), axis, -1)
     n = a.shape[-1]
     nb = -(-n // MX_BLOCK)
     pad = np.zeros(a.shape[:-1] + (nb * MX_BLOCK,))
     pad[..., :n] = a
     blk = pad.reshape(a.shape[:-1] + (nb, MX_BLOCK))
-    e = mx_scale_exp(np.max(np.abs(blk), axis=-1))
-    codes = e4m3_encode(blk / np.exp2(e)[..., None]).reshape(pad.shape)[..., :n]
+    e = mx_scale_exp(np.max(np.abs(blk), axis=-1), fmt)
+    codes = encode(blk / np.exp2(e)[..., None]).reshape(pad.shape)[..., :n]
     return np.moveaxis(codes, -1, axis), np.moveaxis((e + 127).astype(np.uint8), -1, axis)
 
 
-def mx_dequantize(codes, scale_bytes, axis: int) -> np.ndarray:
+def mx_dequantize(codes, scale_bytes, axis: int, fmt: str = "e4m3") -> np.ndarray:
+    decode = MX_FORMATS[fmt][2]
     c = np.moveaxis(np.asarray(codes, np.uint8), axis, -1)
     sb = np.moveaxis(np.asarray(scale_bytes, np.uint8), axis, -1).astype(np.int64)
     n = c.shape[-1]
     scale = np.repeat(np.exp2(sb - 127.0), MX_BLOCK, axis=-1)[..., :n]
-    return np.moveaxis(e4m3_decode(c) * scale, -1, axis)
+    return np.moveaxis(decode(c) * scale, -1, axis)
 
 
-def mx_qdq(a, axis: int) -> np.ndarray:
-    """What an MXFP8 GEMM sees of `a` when it contracts along `axis`."""
-    return mx_dequantize(*mx_quantize(a, axis), axis)
+def mx_qdq(a, axis: int, fmt: str = "e4m3") -> np.ndarray:
+    """What a microscaled GEMM sees of `a` when it contracts along `axis`."""
+    return mx_dequantize(*mx_quantize(a, axis, fmt), axis, fmt)
 
 
-def swiglu_ffn_fwd_mx(xe, w13_e, w2_e, storage: str, gate=None, act_from_stored: bool = False) -> dict:
-    """swiglu_ffn_fwd with MXFP8 GEMM operands: X and W13 quantised along d,
-    A (after its bf16 store) and W2 along f."""
+def mx_format_of(dtype: str) -> str:
+    return {"mxfp8": "e4m3", "mxfp4": "e2m1"}[dtype]
+
+
+def swiglu_ffn_fwd_mx(xe, w13_e, w2_e, storage: str, gate=None, act_from_stored: bool = False,
+                      fmt: str = "e4m3") -> dict:
+    """swiglu_ffn_fwd with microscaled GEMM operands (MXFP8: fmt e4m3,
+    MXFP4: e2m1): X and W13 quantised along d, A (after its bf16 store) and
+    W2 along f."""
     f = w2_e.shape[1]
-    xq = mx_qdq(xe, 1)
-    wq = mx_qdq(w13_e, 1)
+    xq = mx_qdq(xe, 1, fmt)
+    wq = mx_qdq(w13_e, 1, fmt)
     h = xq @ wq[:f].T
     u = xq @ wq[f:].T
     H, U = store(h, storage), store(u, storage)
     a = store(_act(H, U, gate) if act_from_stored else _act(h, u, gate), storage)
-    y = store(mx_qdq(a, 1) @ mx_qdq(w2_e, 1).T, storage)
+    y = store(mx_qdq(a, 1, fmt) @ mx_qdq(w2_e, 1, fmt).T, storage)
     return {"H": H, "U": U, "A": a, "Y": y}
 
 
-def swiglu_ffn_bwd_mx(xe, H, U, A, dY, w13_e, w2_e, storage: str, gate=None) -> dict:
-    """swiglu_ffn_bwd with MXFP8 GEMM operands, each quantised along the
+def swiglu_ffn_bwd_mx(xe, H, U, A, dY, w13_e, w2_e, storage: str, gate=None, fmt: str = "e4m3") -> dict:
+    """swiglu_ffn_bwd with microscaled GEMM operands, each quantised along the
     dimension its GEMM contracts: dA = dY W2 (d), dW2 = dY^T A (rows),
     dX = dHU W13 (2f), dW13 = dHU^T X (rows; blocks start at the first row).
     Folded gates (`gate`) as in swiglu_ffn_bwd."""
     H = np.asarray(H, F64)
     U = np.asarray(U, F64)
     dY = np.asarray(dY, F64)
-    dA = mx_qdq(dY, 1) @ mx_qdq(w2_e, 0)
+    dA = mx_qdq(dY, 1, fmt) @ mx_qdq(w2_e, 0, fmt)
     dg = None
     if gate is not None:
         dg = np.sum(dA * (silu(H) * U), axis=1)
         dA = np.asarray(gate, F64)[:, None] * dA
-    dW2 = store(mx_qdq(dY, 0).T @ mx_qdq(A, 0), storage)
+    dW2 = store(mx_qdq(dY, 0, fmt).T @ mx_qdq(A, 0, fmt), storage)
     sig = 1.0 / (1.0 + np.exp(-H))
     dH = store(dA * U * sig * (1.0 + H * (1.0 - sig)), storage)
     dU = store(dA * H * sig, storage)
     dHU = np.concatenate([dH, dU], axis=1)
-    dX_unrounded = mx_qdq(dHU, 1) @ mx_qdq(w13_e, 0)
-    dW13 = store(mx_qdq(dHU, 0).T @ mx_qdq(xe, 0), storage)
+    dX_unrounded = mx_qdq(dHU, 1, fmt) @ mx_qdq(w13_e, 0, fmt)
+    dW13 = store(mx_qdq(dHU, 0, fmt).T @ mx_qdq(xe, 0, fmt), storage)
     return {"dA": dA, "dH": dH, "dU": dU, "dX32": dX_unrounded,
             "dX": store(dX_unrounded, storage), "dW13": dW13, "dW2": dW2, "dg": dg}
+
+
+def _ffn_fns(dtype: str):
+    """(forward, backward) expert FFN of a layer of storage mode `dtype`."""
+    if dtype in ("mxfp8", "mxfp4"):
+        fmt = mx_format_of(dtype)
+        return (lambda *a, **k: swiglu_ffn_fwd_mx(*a, fmt=fmt, **k),
+                lambda *a, **k: swiglu_ffn_bwd_mx(*a, fmt=fmt, **k))
+    return swiglu_ffn_fwd, swiglu_ffn_bwd
 
 
 # ----------------------------------------------------------------------------
@@ -503,7 +584,7 @@ def layer_forward(inp: dict, cfg, storage: str = None) -> dict:
     expert) -> unpermute/combine.  `inp` holds numpy/torch CPU arrays as made
     by moe_inputs.make_inputs."""
     storage = storage or storage_of(cfg)
-    ffn_fwd = swiglu_ffn_fwd_mx if cfg.dtype == "mxfp8" else swiglu_ffn_fwd
+    ffn_fwd = _ffn_fns(cfg.dtype)[0]
     fold = getattr(cfg, "fold_gates", False)
     from_stored = getattr(cfg, "recompute_act", False)
     x = _np(inp["x"])
@@ -593,7 +674,7 @@ def layer_backward(inp: dict, fwd: dict, cfg, d_aux: float = 1.0,
     dense=False the expert weight gradients come back as {expert: array} for
     the experts that received rows only (all others are exactly zero)."""
     storage = storage or storage_of(cfg)
-    ffn_bwd = swiglu_ffn_bwd_mx if cfg.dtype == "mxfp8" else swiglu_ffn_bwd
+    ffn_bwd = _ffn_fns(cfg.dtype)[1]
     fold = getattr(cfg, "fold_gates", False)
     recompute = getattr(cfg, "recompute_act", False)
     exact = storage == "f64"
