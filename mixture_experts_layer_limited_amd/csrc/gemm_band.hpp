@@ -260,6 +260,34 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
       if (ld.u.r >= 0) issue_b();
   }
 
+  // The roles run separate loops over the same unit / tile / slice sequence
+  // and meet at the same barriers: 2 per unit, then one per slice.
+  if (is_load) {
+    int n = 0;                                // slice being multiplied
+    do {
+      // unit start: after the first barrier every compute wave is done with
+      // the previous unit's band; fetch this unit's band
+      bar();
+      issue_band(cu);
+      wait_vmcnt_dyn<0, 0>(0);
+      bar();
+      Unit nu;
+      settle(cu.r + 1, nu);
+      for (int j = 0; j < TU; ++j) {
+#pragma unroll 1
+        for (int s = 0; s < cu.ns; ++s) {
+          wait_vmcnt_dyn<0, 63>(vm - __builtin_amdgcn_readlane(marks, n % STAGES));
+          bar();
+          if (ld.u.r >= 0) issue_b();         // into the stage of slice n - 1
+          ++n;
+        }
+      }
+      cu = nu;
+    } while (cu.r >= 0);
+    return;
+  }
+  if (!is_compute) return;                    // (no other roles: NW = NCW + NLW)
+
   // ---- compute waves ------------------------------------------------------
   McFrag<BM, C::FM> fa;
   McFrag<BN, C::FN> fb;
@@ -270,57 +298,66 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
 
   int n = 0;                                  // slice being multiplied
   do {
-    // unit start: after this barrier every compute wave is done with the
-    // previous unit's band (its last slice); then fetch this unit's band
     bar();
-    if (is_load) {
-      issue_band(cu);
-      wait_vmcnt_dyn<0, 0>(0);
-    }
     bar();
     Unit nu;
     settle(cu.r + 1, nu);
 
     for (int j = 0; j < TU; ++j) {
-      if (is_compute) {
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-          for (int jj = 0; jj < C::FN; ++jj)
+        for (int jj = 0; jj < C::FN; ++jj)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.0f;
-      }
+          for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.0f;
+      // a runtime loop over the tile's slices keeps the accumulators in one
+      // register set
+#pragma unroll 1
+      for (int s = 0; s < cu.ns; ++s) {
+        bar();
+        const uint32_t sb = lds0 + C::RING_OFF + (n % STAGES) * C::SLICE;   // streamed slice
+        const uint32_t sband = lds0 + C::A_OFF + s * C::SLICE;               // band slice
+        const uint32_t sm = QBAND ? sb : sband, sn = QBAND ? sband : sb;      // m side, n side
+        // Fragments of K-step kk + 1 are read while the MFMAs of step kk run
+        // (two register sets); the scheduling groups below keep that order
+        // (the compiler otherwise serialises each step's reads before its
+        // MFMAs and exposes the LDS latency on every step)
+        bf16x8 fm[2][C::FM], fn[2][C::FN];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s < cu.ns) {
-          if (is_load) wait_vmcnt_dyn<0, 63>(vm - __builtin_amdgcn_readlane(marks, n % STAGES));
-          bar();
-          if (is_load) {
-            if (ld.u.r >= 0) issue_b();       // into the stage of slice n - 1
-          } else if (is_compute) {
-            const uint32_t sb = lds0 + C::RING_OFF + (n % STAGES) * C::SLICE;   // streamed slice
-            const uint32_t sband = lds0 + C::A_OFF + s * C::SLICE;               // band slice
-            const uint32_t sm = QBAND ? sb : sband, sn = QBAND ? sband : sb;      // m side, n side
+        for (int i = 0; i < C::FM; ++i) fm[0][i] = fa.read(sm, i, 0);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-              bf16x8 fm[C::FM], fn[C::FN];
+        for (int jj = 0; jj < C::FN; ++jj) fn[0][jj] = fb.read(sn, jj, 0);
 #pragma unroll
-              for (int i = 0; i < C::FM; ++i) fm[i] = fa.read(sm, i, kk);
+        for (int kk = 0; kk < 4; ++kk) {
+          const int cur = kk & 1;
+          if (kk + 1 < 4) {
 #pragma unroll
-              for (int jj = 0; jj < C::FN; ++jj) fn[jj] = fb.read(sn, jj, kk);
+            for (int i = 0; i < C::FM; ++i) fm[cur ^ 1][i] = fa.read(sm, i, kk + 1);
 #pragma unroll
-              for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-                for (int jj = 0; jj < C::FN; ++jj)   // n-side fragment first: acc[i][jj] is m-block i x n-block jj
-                  acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fn[jj], fm[i], acc[i][jj], 0, 0, 0);
-            }
+            for (int jj = 0; jj < C::FN; ++jj) fn[cur ^ 1][jj] = fb.read(sn, jj, kk + 1);
           }
-          ++n;
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < C::FN; ++jj)   // n-side fragment first: acc[i][jj] is m-block i x n-block jj
+              acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fn[cur][jj], fm[cur][i], acc[i][jj], 0, 0, 0);
         }
+        // order: step 0's reads (2 per fragment), then for steps 0..2 the next
+        // step's reads two at a time between this step's MFMAs, then step 3
+        constexpr int RD = 2 * (C::FM + C::FN), MF = C::FM * C::FN;
+        static_assert(RD == 2 * MF, "two reads per MFMA");
+        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+        for (int q = 0; q < 3 * MF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+        ++n;
       }
       // tile end: the sub-tile through this wave's staging area, 32 rows at a
       // time (LDS operations of one wave execute in order), to 128-byte row pieces
-      if (is_compute) {
+      {
         const int jt = (j + rot * cu.band) % TU;   // the unit's tiles in rotated order
         const int row0 = (QBAND ? jt : cu.band) * BM, col0 = (QBAND ? cu.band : jt) * BN;
         const __amdgpu_buffer_rsrc_t rs =
