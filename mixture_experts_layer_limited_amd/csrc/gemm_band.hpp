@@ -318,10 +318,8 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
         const uint32_t sb = lds0 + C::RING_OFF + (n % STAGES) * C::SLICE;   // streamed slice
         const uint32_t sband = lds0 + C::A_OFF + s * C::SLICE;               // band slice
         const uint32_t sm = QBAND ? sb : sband, sn = QBAND ? sband : sb;      // m side, n side
-        // Fragments of K-step kk + 1 are read while the MFMAs of step kk run
-        // (two register sets); the scheduling groups below keep that order
-        // (the compiler otherwise serialises each step's reads before its
-        // MFMAs and exposes the LDS latency on every step)
+        // fragments of K-step kk + 1 are read while the MFMAs of step kk run
+        // (two register sets), in the order the scheduling groups fix
         bf16x8 fm[2][C::FM], fn[2][C::FN];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) fm[0][i] = fa.read(sm, i, 0);
@@ -342,17 +340,7 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
             for (int jj = 0; jj < C::FN; ++jj)   // n-side fragment first: acc[i][jj] is m-block i x n-block jj
               acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fn[cur][jj], fm[cur][i], acc[i][jj], 0, 0, 0);
         }
-        // order: step 0's reads (2 per fragment), then for steps 0..2 the next
-        // step's reads two at a time between this step's MFMAs, then step 3
-        constexpr int RD = 2 * (C::FM + C::FN), MF = C::FM * C::FN;
-        static_assert(RD == 2 * MF, "two reads per MFMA");
-        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-#pragma unroll
-        for (int q = 0; q < 3 * MF; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+        sched_pipelined_slice<2 * (C::FM + C::FN), C::FM * C::FN>();
         ++n;
       }
       // tile end: the sub-tile through this wave's staging area, 32 rows at a

@@ -237,6 +237,31 @@ struct SliceIter {
   TileCoord c;
 };
 
+// Scheduling groups of one 64-deep slice (four K-steps) whose fragments are
+// double-buffered: step 0's R LDS reads, then for steps 0..2 the next step's R
+// reads interleaved with the first of this step's MF MFMAs, then step 3's MFMAs.  Without
+// them the compiler issues each step's reads right before its MFMAs and waits
+// for them, exposing the LDS latency on every step.
+template <int R, int MF, int Q>
+__device__ __forceinline__ void sched_step_groups() {
+  if constexpr (Q < MF) {
+    // front-loaded: ceil(R / MF) reads before each MFMA until the R are issued
+    constexpr int per = (R + MF - 1) / MF;
+    constexpr int reads = R - per * Q >= per ? per : (R - per * Q > 0 ? R - per * Q : 0);
+    if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    sched_step_groups<R, MF, Q + 1>();
+  }
+}
+template <int R, int MF>
+__device__ __forceinline__ void sched_pipelined_slice() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  sched_step_groups<R, MF, 0>();
+  sched_step_groups<R, MF, 0>();
+  sched_step_groups<R, MF, 0>();
+  __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+}
+
 // MX = true: both operands K-contiguous fp8 e4m3 codes with e8m0 scales (`s`),
 // multiplied with v_mfma_scale_f32_32x32x64_f8f6f4 (operand layout at
 // MxArgs in gemm.hpp); GemmArgs then count K, lda, ldb in 2-byte units, so a slice of
@@ -597,18 +622,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
             }
         }
       }
+      if constexpr (!MX) {
+        // fragments of K-step kk + 1 are read while the MFMAs of step kk run
+        // (two register sets), in the order the scheduling groups fix
+        bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
-      for (int kk = 0; kk < (MX ? 0 : BK / 16); ++kk) {
-        bf16x8 af[FM], bfr[FN];
+        for (int i = 0; i < FM; ++i) af[0][i] = fa.read(sa, i, 0);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = fa.read(sa, i, kk);
+        for (int j = 0; j < FN; ++j) bfr[0][j] = fb.read(sb, j, 0);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bfr[j] = fb.read(sb, j, kk);
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          const int cur = kk & 1;
+          if (kk + 1 < BK / 16) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i) af[cur ^ 1][i] = fa.read(sa, i, kk + 1);
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < FN; ++j) bfr[cur ^ 1][j] = fb.read(sb, j, kk + 1);
+          }
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+        }
+        sched_pipelined_slice<FM * (LA == KC ? 1 : 2) + FN * (LB == KC ? 1 : 2), FM * FN>();
       }
     }
     if constexpr (Epi::kStaged) {
