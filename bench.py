@@ -27,6 +27,7 @@ import moe_inputs as mi  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the MXFP8 GEMMs)
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 MFMA (the MXFP4 GEMMs)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 # HBM bytes per launch of a kernel as read from rocprofv3 counters: FETCH_SIZE
@@ -69,15 +70,18 @@ def step_flops(cfg: mi.MoEConfig, backward: bool = True) -> float:
 
 
 def kernel_work_mx(cfg: mi.MoEConfig, counts) -> dict:
-    """Algorithmic (flops, HBM bytes) per launch of each MXFP8 expert GEMM:
-    quantised operands cost 1 + 1/32 bytes per value (codes + one scale per
-    32), bf16 outputs 2; weight-gradient operands are the column forms whose
-    expert segments are padded to 128 rows."""
-    q, B = 33.0 / 32.0, 2
+    """Algorithmic (flops, HBM bytes) per launch of each MXFP8 / MXFP4 expert
+    GEMM: quantised operands cost 1 + 1/32 bytes per value for fp8 and
+    1/2 + 1/32 for fp4 (codes + one scale per 32), bf16 outputs 2;
+    weight-gradient operands are the column forms whose expert segments are
+    padded to 128 rows (fp8) or 256 (fp4)."""
+    fp4 = cfg.dtype == "mxfp4"
+    q, B = (0.5 if fp4 else 1.0) + 1.0 / 32.0, 2
+    al = 256 if fp4 else 128
     rows, d, f, fs, T, E = cfg.T * cfg.k, cfg.d, cfg.f, cfg.f_shared, cfg.T, cfg.E
     ne = int((counts > 0).sum())
-    rp = int(sum(-(-int(c) // 128) * 128 for c in counts))
-    tp = -(-T // 128) * 128
+    rp = int(sum(-(-int(c) // al) * al for c in counts))
+    tp = -(-T // al) * al
     out = {
         "gemm_mx_swiglu_fwd": (2.0 * rows * d * 2 * f, q * (ne * 2 * f * d + rows * d) + B * rows * 3 * f),
         "gemm_mx_down_fwd": (2.0 * rows * f * d, q * (ne * d * f + rows * f) + B * rows * d),
@@ -173,9 +177,7 @@ def cpu_baseline(cfg, dev_inp, backward: bool, flop_budget: float) -> dict:
     x, wr = f64(dev_inp["x"]), f64(dev_inp["w_router"])
     bias = None if dev_inp["bias"] is None else dev_inp["bias"].cpu().numpy()
     dy = f64(dev_inp["dy"]) if backward else None
-    mx = cfg.dtype == "mxfp8"
-    ffn_fwd = O.swiglu_ffn_fwd_mx if mx else O.swiglu_ffn_fwd
-    ffn_bwd = O.swiglu_ffn_bwd_mx if mx else O.swiglu_ffn_bwd
+    ffn_fwd, ffn_bwd = O._ffn_fns(cfg.dtype)
 
     t0 = time.perf_counter()
     r = O.route(x, wr, bias, cfg)
@@ -287,7 +289,7 @@ def main():
     cfg = mi.CONFIGS[args.workload].with_(fold_gates=args.fold_gates, recompute_act=args.recompute_act,
                                            force_balanced=args.force_balanced)
     backward = cfg.backward if args.passes == "auto" else args.passes == "fwd+bwd"
-    mx = cfg.dtype == "mxfp8"
+    mx = cfg.dtype in ("mxfp8", "mxfp4")
     torch.cuda.set_device(0)
     print(f"# generating {cfg.name} inputs on the GPU", file=sys.stderr, flush=True)
     inp = mi.make_inputs(cfg, seed=args.seed, device="cuda", with_grad_inputs=True)
@@ -371,7 +373,7 @@ def main():
             for n, v in per_kernel.items()}
     counts = layer.buf["counts"].cpu()
     work = kernel_work_mx(cfg, counts) if mx else kernel_work(cfg, counts)
-    peak_mfma = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    peak_mfma = {"mxfp8": PEAK_FP8_TFLOPS, "mxfp4": PEAK_FP4_TFLOPS}.get(cfg.dtype, PEAK_BF16_TFLOPS)
     # dominant kernel: largest total time among the expert GEMMs (which carry
     # algorithmic work figures); every other kernel is far smaller at these shapes
     gemms = {n: v for n, v in per_kernel.items() if n in work} or per_kernel
@@ -415,7 +417,7 @@ def main():
         "metric": "MoE layer fwd+bwd TFLOPS & tokens/s at DSv3 shape, 1 MI355X; % MFMA peak",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "mxfp8" if mx else "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": cfg.dtype if mx else "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name} MoE layer {'fwd+bwd' if backward else 'fwd'}", "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "k": cfg.k, "f": cfg.f, "f_shared": cfg.f_shared, "score": cfg.score,
                    "n_group": cfg.n_group, "topk_group": cfg.topk_group, "parallelism": "none (1 GPU)",

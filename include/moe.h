@@ -60,8 +60,9 @@ typedef enum moe_status {
 } moe_status;
 
 /* MOE_MXFP8: bf16 storage everywhere, expert GEMMs (routed and shared) on fp8
- * e4m3 operands with e8m0 block scales -- see moe_quantize_mxfp8. */
-typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
+ * e4m3 operands with e8m0 block scales -- see moe_quantize_mxfp8.
+ * MOE_MXFP4: the same with fp4 e2m1 operands -- see moe_quantize_mxfp4. */
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2, MOE_MXFP4 = 3 } moe_dtype;
 
 typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 
@@ -429,6 +430,53 @@ moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm,
  * expert's end count as zeros); the shared expert likewise over all T rows.
  * Same outputs as the bf16 call (dx_partial written, not accumulated). */
 moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_perm,
+                                             const void* x_perm, const int32_t* expert_offsets,
+                                             const float* row_gates, const int32_t* row_id_map,
+                                             const void* hu_save, const void* act,
+                                             const moe_mx_weights* weights, void* dhu, void* dx_perm,
+                                             void* dw13, void* dw2, float* d_gates, const void* dy,
+                                             const void* x,
+                                             const void* hu_shared_save, const void* act_shared,
+                                             void* dhu_shared, float* dx_partial, void* dws13,
+                                             void* dws2, void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
+/* ---------------------------------------------------------------------------
+ * MXFP4 (the gfx950 counterpart of the NVFP4 format the pages' system trains
+ * with: papers.lunadong.com summary, "Technical Details" and "Key Terms";
+ * thelatestinai.com page, Table 8 on FP4 activation memory).  The MXFP8 block
+ * structure with fp4 e2m1 elements -- one sign bit, two exponent bits (bias 1),
+ * one mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6:
+ *
+ *   scale byte = e + 127, e the smallest integer with 6 * 2^e >= the block's
+ *                largest magnitude, clamped to [-127, 127] (all-zero block:
+ *                byte 0, zero codes)
+ *   code       = the e2m1 value nearest to v / 2^e, ties to the even code,
+ *                saturating at +-6
+ *
+ * Codes are stored two per byte along the blocked dimension, element 2i in the
+ * low nibble: MOE_MX_ROWS gives codes [B][R][C/2] and scales [B][R][C/32],
+ * MOE_MX_COLS codes [B][C][R/2] and scales [B][C][R/32] (same size rules as
+ * moe_quantize_mxfp8).
+ * ------------------------------------------------------------------------- */
+moe_status moe_quantize_mxfp4(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t orientation,
+                              uint8_t* codes, uint8_t* scales, void* stream);
+
+/* moe_grouped_gemm_swiglu_mxfp8 and moe_grouped_gemm_swiglu_bwd_mxfp8 with
+ * MXFP4 operands (cfg.dtype = MOE_MXFP4; d, f, f_shared multiples of 256, one
+ * 128-byte code slice per row).  `weights` holds moe_quantize_mxfp4 forms in
+ * the moe_mx_weights layouts (code widths halved: w13 codes [E][2f][d/2],
+ * w13_t [E][d][f], ...); the same seven expert products are quantised along
+ * their contractions inside the calls; the weight gradients' 32-row blocks
+ * restart at each expert's first row as in MXFP8.  Same outputs, workspace
+ * (moe_workspace_size of the MOE_MXFP4 cfg) and errors. */
+moe_status moe_grouped_gemm_swiglu_mxfp4(const moe_cfg* cfg, const void* x_perm,
+                                         const int32_t* expert_offsets, const float* row_gates,
+                                         const moe_mx_weights* weights, void* hu_save, void* act,
+                                         void* y_perm, const void* x, void* hu_shared_save,
+                                         void* act_shared, void* y_shared, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+moe_status moe_grouped_gemm_swiglu_bwd_mxfp4(const moe_cfg* cfg, const void* dy_perm,
                                              const void* x_perm, const int32_t* expert_offsets,
                                              const float* row_gates, const int32_t* row_id_map,
                                              const void* hu_save, const void* act,

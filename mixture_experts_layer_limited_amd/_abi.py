@@ -16,7 +16,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_gfx950.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
-MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2, 3
 MOE_MX_ROWS, MOE_MX_COLS = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_FLAG_FORCE_BALANCED, MOE_FLAG_FOLD_GATES, MOE_FLAG_RECOMPUTE_ACT = 1, 2, 4
@@ -69,6 +69,14 @@ _SIGS = {
                                                      ctypes.POINTER(moe_mx_weights)] + [_P] * 7
                                       + [_P, ctypes.c_size_t, _P]),
     "moe_grouped_gemm_swiglu_bwd_mxfp8": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 7
+                                          + [ctypes.POINTER(moe_mx_weights)] + [_P] * 13
+                                          + [_P, ctypes.c_size_t, _P]),
+    "moe_quantize_mxfp4": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                          _P, _P, _P]),
+    "moe_grouped_gemm_swiglu_mxfp4": (ctypes.c_int, [ctypes.POINTER(moe_cfg), _P, _P, _P,
+                                                     ctypes.POINTER(moe_mx_weights)] + [_P] * 7
+                                      + [_P, ctypes.c_size_t, _P]),
+    "moe_grouped_gemm_swiglu_bwd_mxfp4": (ctypes.c_int, [ctypes.POINTER(moe_cfg)] + [_P] * 7
                                           + [ctypes.POINTER(moe_mx_weights)] + [_P] * 13
                                           + [_P, ctypes.c_size_t, _P]),
     "moe_trace_begin": (ctypes.c_int, [ctypes.c_int]),
@@ -148,7 +156,8 @@ def make_cfg(T, d, E, k, f, f_shared=0, score="softmax", n_group=1, topk_group=1
                    score=MOE_SCORE_SIGMOID if score == "sigmoid" else MOE_SCORE_SOFTMAX,
                    n_group=n_group, topk_group=topk_group, renorm=int(bool(renorm)),
                    scale=scale, aux_coeff=aux_coeff,
-                   dtype={"f32": MOE_F32, "mxfp8": MOE_MXFP8}.get(dtype, MOE_BF16), flags=flags)
+                   dtype={"f32": MOE_F32, "mxfp8": MOE_MXFP8, "mxfp4": MOE_MXFP4}.get(dtype, MOE_BF16),
+                   flags=flags)
 
 
 def moe_status_string(s: int) -> str:
@@ -269,6 +278,11 @@ def moe_quantize_mxfp8(src, batch, rows, cols, orientation, codes, scales, strea
                                     _ptr(scales, _U8), _stream(stream)), "moe_quantize_mxfp8")
 
 
+def moe_quantize_mxfp4(src, batch, rows, cols, orientation, codes, scales, stream=None):
+    _check(lib().moe_quantize_mxfp4(_ptr(src, torch.bfloat16), batch, rows, cols, orientation, _ptr(codes, _U8),
+                                    _ptr(scales, _U8), _stream(stream)), "moe_quantize_mxfp4")
+
+
 def mx_weights(**tensors) -> moe_mx_weights:
     """moe_mx_weights from (codes, scales) tensor pairs keyed by member name;
     missing members stay NULL."""
@@ -301,6 +315,30 @@ def moe_grouped_gemm_swiglu_bwd_mxfp8(cfg, dy_perm, x_perm, expert_offsets, row_
         _ptr(dx_perm, S), _ptr(dw13, S), _ptr(dw2, S), _ptr(d_gates, _F32), _ptr(dy, S), _ptr(x, S), _ptr(hu_shared_save, S), _ptr(act_shared, S), _ptr(dhu_shared, S),
         _ptr(dx_partial, _F32), _ptr(dws13, S), _ptr(dws2, S), w, n, _stream(stream)),
         "moe_grouped_gemm_swiglu_bwd_mxfp8")
+
+
+def moe_grouped_gemm_swiglu_mxfp4(cfg, x_perm, expert_offsets, row_gates, weights, hu_save, act, y_perm, x,
+                                  hu_shared_save, act_shared, y_shared, workspace, stream=None):
+    w, n = _ws(workspace)
+    S = torch.bfloat16
+    _check(lib().moe_grouped_gemm_swiglu_mxfp4(
+        ctypes.byref(cfg), _ptr(x_perm, S), _ptr(expert_offsets, _I32), _ptr(row_gates, _F32), ctypes.byref(weights),
+        _ptr(hu_save, S),
+        _ptr(act, S), _ptr(y_perm, S), _ptr(x, S), _ptr(hu_shared_save, S), _ptr(act_shared, S),
+        _ptr(y_shared, S), w, n, _stream(stream)), "moe_grouped_gemm_swiglu_mxfp4")
+
+
+def moe_grouped_gemm_swiglu_bwd_mxfp4(cfg, dy_perm, x_perm, expert_offsets, row_gates, row_id_map, hu_save, act,
+                                      weights, dhu, dx_perm, dw13, dw2, d_gates, dy, x, hu_shared_save, act_shared,
+                                      dhu_shared, dx_partial, dws13, dws2, workspace, stream=None):
+    w, n = _ws(workspace)
+    S = torch.bfloat16
+    _check(lib().moe_grouped_gemm_swiglu_bwd_mxfp4(
+        ctypes.byref(cfg), _ptr(dy_perm, S), _ptr(x_perm, S), _ptr(expert_offsets, _I32), _ptr(row_gates, _F32),
+        _ptr(row_id_map, _I32), _ptr(hu_save, S), _ptr(act, S), ctypes.byref(weights), _ptr(dhu, S),
+        _ptr(dx_perm, S), _ptr(dw13, S), _ptr(dw2, S), _ptr(d_gates, _F32), _ptr(dy, S), _ptr(x, S), _ptr(hu_shared_save, S), _ptr(act_shared, S), _ptr(dhu_shared, S),
+        _ptr(dx_partial, _F32), _ptr(dws13, S), _ptr(dws2, S), w, n, _stream(stream)),
+        "moe_grouped_gemm_swiglu_bwd_mxfp4")
 
 
 def moe_trace_begin(capacity: int):

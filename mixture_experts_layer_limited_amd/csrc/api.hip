@@ -79,7 +79,7 @@ moe_status check_cfg(const moe_cfg* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg is NULL");
   if (c->flags & ~(MOE_FLAG_FORCE_BALANCED | MOE_FLAG_FOLD_GATES | MOE_FLAG_RECOMPUTE_ACT))
     return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.flags = 0x%x has unknown bits", (unsigned)c->flags);
-  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_MXFP8)
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_MXFP8 && c->dtype != MOE_MXFP4)
     return fail(MOE_ERR_UNSUPPORTED, "cfg.dtype %d not supported", c->dtype);
   if (c->T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.T = %lld < 0", (long long)c->T);
   if (c->E < 1 || c->E > kMaxExperts)
@@ -137,18 +137,24 @@ moe_status check_gemm_shapes(const moe_cfg* c) {
   return MOE_OK;
 }
 
+inline bool is_mx(const moe_cfg* c) { return c->dtype == MOE_MXFP8 || c->dtype == MOE_MXFP4; }
+inline bool is_fp4(const moe_cfg* c) { return c->dtype == MOE_MXFP4; }
+
 // expert GEMM calls of the bf16 / fp32 path
 moe_status check_not_mx(const moe_cfg* c) {
-  if (c->dtype == MOE_MXFP8)
-    return fail(MOE_ERR_UNSUPPORTED, "cfg.dtype is MXFP8: use the *_mxfp8 expert GEMM calls");
+  if (is_mx(c))
+    return fail(MOE_ERR_UNSUPPORTED, "cfg.dtype is MXFP8 / MXFP4: use the *_mxfp8 / *_mxfp4 expert GEMM calls");
   return MOE_OK;
 }
 
-// the MXFP8 GEMMs contract in 128-deep slices
-moe_status check_mx_shapes(const moe_cfg* c) {
-  if (c->dtype != MOE_MXFP8) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.dtype must be MOE_MXFP8");
-  if (c->d % 128 || c->f % 128 || c->f_shared % 128)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "MXFP8 GEMMs need d, f and f_shared to be multiples of 128");
+// the microscaled GEMMs contract in slices of 128 code bytes per row: 128 fp8
+// or 256 fp4 values
+moe_status check_mx_shapes(const moe_cfg* c, int32_t want) {
+  const char* name = want == MOE_MXFP4 ? "MXFP4" : "MXFP8";
+  if (c->dtype != want) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg.dtype must be MOE_%s for this call", name);
+  const int64_t m = want == MOE_MXFP4 ? 256 : 128;
+  if (c->d % m || c->f % m || c->f_shared % m)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s GEMMs need d, f and f_shared to be multiples of %lld", name, (long long)m);
   return check_offsets_32bit(c, 2);               // bf16 operands and outputs beside the codes
 }
 
@@ -234,6 +240,11 @@ struct MxWs {
   size_t total() const { return ints + qa + 2 * qt + extra.bytes; }
 };
 inline int64_t pad128(int64_t v) { return (v + 127) / 128 * 128; }
+// padded row count of a dense column form (the shared expert's contraction over T)
+inline int64_t pad_rows(int64_t v, bool fp4) {
+  const int64_t a = mx_row_align(fp4);
+  return (v + a - 1) / a * a;
+}
 MxWs mx_ws(const moe_cfg* c) {
   MxWs w;
   const int64_t rows = c->T * c->k;
@@ -243,7 +254,9 @@ MxWs mx_ws(const moe_cfg* c) {
   if (2 * c->f_shared > cm) cm = 2 * c->f_shared;
   w.cmax_rows = cm;
   w.cmax_cols = cm;
-  w.rp_max = pad128(w.rows_max) + (int64_t)kMxRowAlign * c->E;
+  // every group padded to the column form's row alignment (codes sized for
+  // fp8: an fp4 form takes half of each region)
+  w.rp_max = pad_rows(w.rows_max, is_fp4(c)) + (int64_t)mx_row_align(is_fp4(c)) * c->E;
   w.ints = 2 * align256((size_t)(c->E + 2) * 4);
   w.qa = align256((size_t)(w.rows_max * w.cmax_rows)) + align256((size_t)(w.rows_max * w.cmax_rows / 32));
   w.qt = align256((size_t)(w.cmax_cols * w.rp_max)) + align256((size_t)(w.cmax_cols * w.rp_max / 32));
@@ -261,7 +274,7 @@ size_t ws_bytes_for(const moe_cfg* c) {
   if (perm > m) m = perm;
   if (gemm > m) m = gemm;
   if (rbwd > m) m = rbwd;
-  if (c->dtype == MOE_MXFP8 && mx_ws(c).total() > m) m = mx_ws(c).total();
+  if (is_mx(c) && mx_ws(c).total() > m) m = mx_ws(c).total();
   return m < 256 ? 256 : m;
 }
 
@@ -417,27 +430,27 @@ inline MxQ mxq(const moe_mx_tensor& t) { return MxQ{t.codes, t.scales}; }
 moe_status mx_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off, const float* row_gates,
                        const moe_mx_weights* w, void* hu, void* act, void* y_perm, const void* x, void* hu_s,
                        void* act_s, void* y_s, void* ws, hipStream_t st) {
-  const bool rc = recompute(c);
+  const bool rc = recompute(c), fp4 = is_fp4(c);
   const float* rg = fold(c) ? row_gates : nullptr;
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
   MxBufs b = mx_bufs(c, ws);
   const MxQ qa = mxq(b.qa_c, b.qa_s);
   if (rows > 0) {
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, fp4, st));
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
     LAUNCH_NAMED("gemm_mx_swiglu_fwd", gemm_mx_swiglu_fwd(qa, off, b.prefix, E, mxq(w->w13), hu, act, rows, d, f, rg, rc,
-                                                          st));
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act, f, 0, 1, rows, f, b.qa_c, b.qa_s, st));
-    LAUNCH_NAMED("gemm_mx_down_fwd", gemm_mx_down_fwd(qa, off, b.prefix, E, mxq(w->w2), y_perm, rows, d, f, st));
+                                                          fp4, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act, f, 0, 1, rows, f, b.qa_c, b.qa_s, fp4, st));
+    LAUNCH_NAMED("gemm_mx_down_fwd", gemm_mx_down_fwd(qa, off, b.prefix, E, mxq(w->w2), y_perm, rows, d, f, fp4, st));
   }
   if (c->f_shared > 0 && T_ > 0) {
     const int fs = (int)c->f_shared;
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x, d, 0, 1, T_, d, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x, d, 0, 1, T_, d, b.qa_c, b.qa_s, fp4, st));
     LAUNCH_NAMED("gemm_mx_swiglu_fwd_shared",
-                 gemm_mx_swiglu_fwd(qa, nullptr, nullptr, 1, mxq(w->ws13), hu_s, act_s, T_, d, fs, nullptr, rc, st));
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act_s, fs, 0, 1, T_, fs, b.qa_c, b.qa_s, st));
+                 gemm_mx_swiglu_fwd(qa, nullptr, nullptr, 1, mxq(w->ws13), hu_s, act_s, T_, d, fs, nullptr, rc, fp4, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act_s, fs, 0, 1, T_, fs, b.qa_c, b.qa_s, fp4, st));
     LAUNCH_NAMED("gemm_mx_down_fwd_shared",
-                 gemm_mx_down_fwd(qa, nullptr, nullptr, 1, mxq(w->ws2), y_s, T_, d, fs, st));
+                 gemm_mx_down_fwd(qa, nullptr, nullptr, 1, mxq(w->ws2), y_s, T_, d, fs, fp4, st));
   }
   return ok();
 }
@@ -449,6 +462,7 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
                        float* dx_partial, void* dws13, void* dws2, void* ws, hipStream_t st) {
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
   MxBufs b = mx_bufs(c, ws);
+  const bool fp4 = is_fp4(c);
   const float* rg = fold(c) ? row_gates : nullptr;
   if (b.act_rec) {                  // recomputation: the backward reads the act it forms again
     act = b.act_rec;
@@ -457,47 +471,47 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
   const MxQ qa = mxq(b.qa_c, b.qa_s), q1 = mxq(b.q1_c, b.q1_s), q2 = mxq(b.q2_c, b.q2_s);
   const int rp = (int)b.rp_max;
   if (rows > 0) {
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, fp4, st));
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
     LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd",
                  gemm_mx_down_dgrad_swiglu_bwd(qa, off, b.prefix, E, mxq(w->w2_t), hu, dhu, rows, d, f, rg, b.dg_part,
-                                               b.act_rec, st));
+                                               b.act_rec, fp4, st));
     if (rg)
       LAUNCH_NAMED("gate_grad_sum", launch_gate_grad_sum(b.dg_part, gemm_dg_parts(true, f), row_id_map, rows, d_gates, st));
   }
   // weight gradients cover every expert: experts without rows get zeros
-  LAUNCH_NAMED("padded_offsets", launch_padded_offsets(off, E, b.poff, st));
-  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dy_perm, d, rows, d, off, b.poff, E, rp, rp, b.q1_c, b.q1_s, st));
-  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(act, f, rows, f, off, b.poff, E, rp, rp, b.q2_c, b.q2_s, st));
-  LAUNCH_NAMED("gemm_mx_wgrad_down", gemm_mx_wgrad(q1, d, q2, f, rp, b.poff, E, 0, dw2, 1, st));
+  LAUNCH_NAMED("padded_offsets", launch_padded_offsets(off, E, b.poff, fp4, st));
+  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dy_perm, d, rows, d, off, b.poff, E, rp, rp, b.q1_c, b.q1_s, fp4, st));
+  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(act, f, rows, f, off, b.poff, E, rp, rp, b.q2_c, b.q2_s, fp4, st));
+  LAUNCH_NAMED("gemm_mx_wgrad_down", gemm_mx_wgrad(q1, d, q2, f, rp, b.poff, E, 0, dw2, 1, fp4, st));
   if (rows > 0) {
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu, 2 * f, 0, 1, rows, 2 * f, b.qa_c, b.qa_s, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu, 2 * f, 0, 1, rows, 2 * f, b.qa_c, b.qa_s, fp4, st));
     LAUNCH_NAMED("gemm_mx_gateup_dgrad",
-                 gemm_mx_gateup_dgrad(qa, off, b.prefix, E, mxq(w->w13_t), dx_perm, false, rows, d, f, st));
+                 gemm_mx_gateup_dgrad(qa, off, b.prefix, E, mxq(w->w13_t), dx_perm, false, rows, d, f, fp4, st));
   }
-  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dhu, 2 * f, rows, 2 * f, off, b.poff, E, rp, rp, b.q1_c, b.q1_s, st));
-  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(x_perm, d, rows, d, off, b.poff, E, rp, rp, b.q2_c, b.q2_s, st));
-  LAUNCH_NAMED("gemm_mx_wgrad_gateup", gemm_mx_wgrad(q1, 2 * f, q2, d, rp, b.poff, E, 0, dw13, 0, st));
+  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dhu, 2 * f, rows, 2 * f, off, b.poff, E, rp, rp, b.q1_c, b.q1_s, fp4, st));
+  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(x_perm, d, rows, d, off, b.poff, E, rp, rp, b.q2_c, b.q2_s, fp4, st));
+  LAUNCH_NAMED("gemm_mx_wgrad_gateup", gemm_mx_wgrad(q1, 2 * f, q2, d, rp, b.poff, E, 0, dw13, 0, fp4, st));
   if (c->f_shared > 0) {
     const int fs = (int)c->f_shared;
-    const int tp = (int)pad128(T_);
+    const int tp = (int)pad_rows(T_, fp4);
     if (T_ > 0) {
-      LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy, d, 0, 1, T_, d, b.qa_c, b.qa_s, st));
+      LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy, d, 0, 1, T_, d, b.qa_c, b.qa_s, fp4, st));
       LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd_shared",
                    gemm_mx_down_dgrad_swiglu_bwd(qa, nullptr, nullptr, 1, mxq(w->ws2_t), hu_s, dhu_s, T_, d, fs, nullptr,
-                                                 nullptr, b.act_rec, st));
+                                                 nullptr, b.act_rec, fp4, st));
     }
-    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dy, d, T_, d, nullptr, nullptr, 1, tp, tp, b.q1_c, b.q1_s, st));
-    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(act_s, fs, T_, fs, nullptr, nullptr, 1, tp, tp, b.q2_c, b.q2_s, st));
-    LAUNCH_NAMED("gemm_mx_wgrad_down_shared", gemm_mx_wgrad(q1, d, q2, fs, tp, nullptr, 1, tp, dws2, 1, st));
+    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dy, d, T_, d, nullptr, nullptr, 1, tp, tp, b.q1_c, b.q1_s, fp4, st));
+    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(act_s, fs, T_, fs, nullptr, nullptr, 1, tp, tp, b.q2_c, b.q2_s, fp4, st));
+    LAUNCH_NAMED("gemm_mx_wgrad_down_shared", gemm_mx_wgrad(q1, d, q2, fs, tp, nullptr, 1, tp, dws2, 1, fp4, st));
     if (T_ > 0) {
-      LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu_s, 2 * fs, 0, 1, T_, 2 * fs, b.qa_c, b.qa_s, st));
+      LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu_s, 2 * fs, 0, 1, T_, 2 * fs, b.qa_c, b.qa_s, fp4, st));
       LAUNCH_NAMED("gemm_mx_gateup_dgrad_shared",
-                   gemm_mx_gateup_dgrad(qa, nullptr, nullptr, 1, mxq(w->ws13_t), dx_partial, true, T_, d, fs, st));
+                   gemm_mx_gateup_dgrad(qa, nullptr, nullptr, 1, mxq(w->ws13_t), dx_partial, true, T_, d, fs, fp4, st));
     }
-    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dhu_s, 2 * fs, T_, 2 * fs, nullptr, nullptr, 1, tp, tp, b.q1_c, b.q1_s, st));
-    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(x, d, T_, d, nullptr, nullptr, 1, tp, tp, b.q2_c, b.q2_s, st));
-    LAUNCH_NAMED("gemm_mx_wgrad_gateup_shared", gemm_mx_wgrad(q1, 2 * fs, q2, d, tp, nullptr, 1, tp, dws13, 0, st));
+    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dhu_s, 2 * fs, T_, 2 * fs, nullptr, nullptr, 1, tp, tp, b.q1_c, b.q1_s, fp4, st));
+    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(x, d, T_, d, nullptr, nullptr, 1, tp, tp, b.q2_c, b.q2_s, fp4, st));
+    LAUNCH_NAMED("gemm_mx_wgrad_gateup_shared", gemm_mx_wgrad(q1, 2 * fs, q2, d, tp, nullptr, 1, tp, dws13, 0, fp4, st));
   } else {
     LAUNCH_NAMED("fill_f32", launch_fill_f32(dx_partial, (int64_t)T_ * d, 0.0f, st));
   }
@@ -835,8 +849,8 @@ moe_status moe_permute_bwd(const moe_cfg* cfg, const void* dx_perm, const int32_
 }
 
 
-moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t orientation,
-                              uint8_t* codes, uint8_t* scales, void* stream) {
+static moe_status quantize_mx(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t orientation,
+                              uint8_t* codes, uint8_t* scales, bool fp4, void* stream) {
   REQ(src); REQ(codes); REQ(scales);
   ALIGNED(src); ALIGNED(codes);
   if (batch < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "negative size");
@@ -853,20 +867,30 @@ moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int6
   hipStream_t st = (hipStream_t)stream;
   if (orientation == MOE_MX_ROWS)
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(src, cols, rows * cols, (int)batch, (int)rows, (int)cols,
-                                                       codes, scales, st));
+                                                       codes, scales, fp4, st));
   else
     LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols_batched(src, (int)batch, (int)rows, (int)cols, codes,
-                                                               scales, st));
+                                                               scales, fp4, st));
   return ok();
 }
 
-moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm, const int32_t* expert_offsets,
-                                         const float* row_gates, const moe_mx_weights* weights, void* hu_save,
-                                         void* act, void* y_perm, const void* x, void* hu_shared_save,
-                                         void* act_shared, void* y_shared, void* workspace, size_t workspace_bytes,
-                                         void* stream) {
+moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t orientation,
+                              uint8_t* codes, uint8_t* scales, void* stream) {
+  return quantize_mx(src, batch, rows, cols, orientation, codes, scales, false, stream);
+}
+
+moe_status moe_quantize_mxfp4(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t orientation,
+                              uint8_t* codes, uint8_t* scales, void* stream) {
+  return quantize_mx(src, batch, rows, cols, orientation, codes, scales, true, stream);
+}
+
+static moe_status grouped_swiglu_mx(int32_t want, const moe_cfg* cfg, const void* x_perm,
+                                    const int32_t* expert_offsets, const float* row_gates,
+                                    const moe_mx_weights* weights, void* hu_save, void* act, void* y_perm,
+                                    const void* x, void* hu_shared_save, void* act_shared, void* y_shared,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
-  CHECK(check_mx_shapes(cfg));
+  CHECK(check_mx_shapes(cfg, want));
   REQ(x_perm); REQ(expert_offsets); REQ(weights); REQ(act); REQ(y_perm);
   if (fold(cfg)) REQ(row_gates);
   ALIGNED(x_perm); ALIGNED(hu_save); ALIGNED(act); ALIGNED(y_perm);
@@ -884,16 +908,34 @@ moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm,
                      act_shared, y_shared, workspace, (hipStream_t)stream);
 }
 
-moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_perm, const void* x_perm,
-                                             const int32_t* expert_offsets, const float* row_gates,
-                                             const int32_t* row_id_map, const void* hu_save, const void* act,
-                                             const moe_mx_weights* weights, void* dhu, void* dx_perm, void* dw13,
-                                             void* dw2, float* d_gates, const void* dy, const void* x,
-                                             const void* hu_shared_save, const void* act_shared, void* dhu_shared,
-                                             float* dx_partial, void* dws13, void* dws2, void* workspace,
-                                             size_t workspace_bytes, void* stream) {
+moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm, const int32_t* expert_offsets,
+                                         const float* row_gates, const moe_mx_weights* weights, void* hu_save,
+                                         void* act, void* y_perm, const void* x, void* hu_shared_save,
+                                         void* act_shared, void* y_shared, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  return grouped_swiglu_mx(MOE_MXFP8, cfg, x_perm, expert_offsets, row_gates, weights, hu_save, act, y_perm, x,
+                           hu_shared_save, act_shared, y_shared, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_grouped_gemm_swiglu_mxfp4(const moe_cfg* cfg, const void* x_perm, const int32_t* expert_offsets,
+                                         const float* row_gates, const moe_mx_weights* weights, void* hu_save,
+                                         void* act, void* y_perm, const void* x, void* hu_shared_save,
+                                         void* act_shared, void* y_shared, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  return grouped_swiglu_mx(MOE_MXFP4, cfg, x_perm, expert_offsets, row_gates, weights, hu_save, act, y_perm, x,
+                           hu_shared_save, act_shared, y_shared, workspace, workspace_bytes, stream);
+}
+
+static moe_status grouped_swiglu_bwd_mx(int32_t want, const moe_cfg* cfg, const void* dy_perm,
+                                        const void* x_perm, const int32_t* expert_offsets, const float* row_gates,
+                                        const int32_t* row_id_map, const void* hu_save, const void* act,
+                                        const moe_mx_weights* weights, void* dhu, void* dx_perm, void* dw13,
+                                        void* dw2, float* d_gates, const void* dy, const void* x,
+                                        const void* hu_shared_save, const void* act_shared, void* dhu_shared,
+                                        float* dx_partial, void* dws13, void* dws2, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
   CHECK(check_cfg(cfg));
-  CHECK(check_mx_shapes(cfg));
+  CHECK(check_mx_shapes(cfg, want));
   REQ(dy_perm); REQ(x_perm); REQ(expert_offsets); REQ(hu_save); REQ(weights);
   REQ(dhu); REQ(dx_perm); REQ(dw13); REQ(dw2); REQ(dx_partial);
   if (!recompute(cfg)) REQ(act);
@@ -916,4 +958,31 @@ moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_
                      dx_perm, dw13, dw2, d_gates, dy, x, hu_shared_save, act_shared, dhu_shared, dx_partial, dws13,
                      dws2, workspace, (hipStream_t)stream);
 }
+
+moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_perm, const void* x_perm,
+                                             const int32_t* expert_offsets, const float* row_gates,
+                                             const int32_t* row_id_map, const void* hu_save, const void* act,
+                                             const moe_mx_weights* weights, void* dhu, void* dx_perm, void* dw13,
+                                             void* dw2, float* d_gates, const void* dy, const void* x,
+                                             const void* hu_shared_save, const void* act_shared, void* dhu_shared,
+                                             float* dx_partial, void* dws13, void* dws2, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return grouped_swiglu_bwd_mx(MOE_MXFP8, cfg, dy_perm, x_perm, expert_offsets, row_gates, row_id_map, hu_save, act,
+                              weights, dhu, dx_perm, dw13, dw2, d_gates, dy, x, hu_shared_save, act_shared,
+                              dhu_shared, dx_partial, dws13, dws2, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_grouped_gemm_swiglu_bwd_mxfp4(const moe_cfg* cfg, const void* dy_perm, const void* x_perm,
+                                             const int32_t* expert_offsets, const float* row_gates,
+                                             const int32_t* row_id_map, const void* hu_save, const void* act,
+                                             const moe_mx_weights* weights, void* dhu, void* dx_perm, void* dw13,
+                                             void* dw2, float* d_gates, const void* dy, const void* x,
+                                             const void* hu_shared_save, const void* act_shared, void* dhu_shared,
+                                             float* dx_partial, void* dws13, void* dws2, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return grouped_swiglu_bwd_mx(MOE_MXFP4, cfg, dy_perm, x_perm, expert_offsets, row_gates, row_id_map, hu_save, act,
+                              weights, dhu, dx_perm, dw13, dw2, d_gates, dy, x, hu_shared_save, act_shared,
+                              dhu_shared, dx_partial, dws13, dws2, workspace, workspace_bytes, stream);
+}
+
 }  // extern "C"

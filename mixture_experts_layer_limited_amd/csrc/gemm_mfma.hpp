@@ -267,11 +267,13 @@ __device__ __forceinline__ void sched_pipelined_slice() {
 // MxArgs in gemm.hpp); GemmArgs then count K, lda, ldb in 2-byte units, so a slice of
 // BK = 64 units is 128 fp8 values and the data path is the bf16 one.
 template <int BM, int BN, int WM, int WN, int STAGES, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi,
-          bool MX = false>
+          bool MX = false, bool FP4 = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT,
                                                                  int MT) {
   using C = TileCfg<BM, BN, WM, WN, STAGES, MX>;
   static_assert(!MX || (LA == KC && LB == KC && MODE != RAGGED_K), "MXFP8: K-contiguous row-ragged products");
+  // FP4: two scale words per row and slice, fetched by lanes 2 r and 2 r + 1
+  static_assert(!FP4 || (MX && 2 * BM <= C::SC_WORDS && 2 * BN <= C::SC_WORDS), "fp4 scale regions");
   constexpr int BK = C::BK, FM = C::FM, FN = C::FN;
   constexpr int DMA_PER_SLICE = C::A_DMA + C::B_DMA + C::SC_DMA;
   extern __shared__ u32x4 smem[];
@@ -366,18 +368,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
       // of B row q (its weight row), or nothing (an offset outside the range)
       const int q = wave * 64 + lane;
       const int nrows = min(c.m_end - c.m0, BM);
+      // fp8: lane q fetches the slice's word of row q; fp4: word q & 1 of row q >> 1
+      const int qr = FP4 ? q >> 1 : q;
+      const uint32_t qw = FP4 ? (uint32_t)(q & 1) * 4 : 0u;
       rsa_base = s.A_s + (int64_t)c.m0 * s.a_s_ld;
       rsa_bytes = (uint32_t)(nrows * s.a_s_ld);
-      sa_off = q < nrows ? (uint32_t)(q * s.a_s_ld) : kOffRange;
+      sa_off = qr < nrows ? (uint32_t)(qr * s.a_s_ld) + qw : kOffRange;
       rsb_base = s.B_s + (MODE == RAGGED_M ? (int64_t)c.g * s.b_s_gstride : 0);
       rsb_bytes = (uint32_t)((int64_t)a.b_next * s.b_s_ld);
       int g = -1;
-      if (q < BN) {
-        if constexpr (Epi::kPaired) g = Epi::template b_row_paired<BN, WN>(ep, nt, q);
-        else g = nt * BN + q;
+      if (qr < BN) {
+        if constexpr (Epi::kPaired) g = Epi::template b_row_paired<BN, WN>(ep, nt, qr);
+        else g = nt * BN + qr;
       }
-      sb_off = (g >= 0 && g < a.b_next) ? (uint32_t)((int64_t)g * s.b_s_ld) : kOffRange;
-      sos = (uint32_t)(c.k_begin / 16);             // 2-byte units -> scale bytes (one per 32 values)
+      sb_off = (g >= 0 && g < a.b_next) ? (uint32_t)((int64_t)g * s.b_s_ld) + qw : kOffRange;
+      // 2-byte units -> scale bytes (one per 32 values: 16 units of fp8, 8 of fp4)
+      sos = (uint32_t)(c.k_begin / (FP4 ? 8 : 16));
     }
   };
   auto issue = [&](int stage) {
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
                                                (MOE_LDS void*)(uintptr_t)(sc + C::SC_WORDS * 4), 4, sb_off, sos, 0,
                                                0);
 #endif
-      sos += BK / 16;                               // four scale bytes per 128-value slice
+      sos += FP4 ? BK / 8 : BK / 16;                // scale bytes per slice: 8 (256 fp4), 4 (128 fp8)
     }
   };
 
@@ -578,7 +584,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
       }
       const uint32_t sa = lds0 + (n % STAGES) * C::STAGE_BYTES;
       const uint32_t sb = sa + C::A_BYTES;
-      if constexpr (MX) {
+      if constexpr (MX && FP4) {
+        // four 64-deep steps per slice (32 bytes of a row each); lane half h
+        // takes 16-byte chunk 2 st + h of its row -- the 32 values of block h
+        // of the step -- and passes the scale of that block: byte 2 st + h of
+        // the row's two scale words
+        const int h = lane >> 5;
+        const uint32_t sc = sb + C::B_BYTES;
+        u32x2 wa[FM], wb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          wa[i] = *(const MOE_LDS u32x2*)(uintptr_t)(sc + (wm * (BM / WM) + i * 32 + (lane & 31)) * 8);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          wb[j] = *(const MOE_LDS u32x2*)(uintptr_t)(sc + C::SC_WORDS * 4 + (wn * (BN / WN) + j * 32 + (lane & 31)) * 8);
+        auto chunk = [&](uint32_t base, int row, int c) -> i32x8 {
+          const u32x4 v = *(const MOE_LDS u32x4*)(uintptr_t)(base + row * 128 + ((c ^ kc_swz(row)) * 16));
+          return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};   // e2m1 uses the low four
+        };
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          i32x8 af[FM], bfr[FN];
+#pragma unroll
+          for (int i = 0; i < FM; ++i) af[i] = chunk(sa, wm * (BM / WM) + i * 32 + (lane & 31), 2 * st + h);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bfr[j] = chunk(sb, wn * (BN / WN) + j * 32 + (lane & 31), 2 * st + h);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int sa_w = (int)(wa[i][st >> 1] >> (8 * h)), sb_w = (int)(wb[j][st >> 1] >> (8 * h));
+              if ((st & 1) == 0)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 4, 4, 0, sb_w,
+                                                                            0, sa_w);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 4, 4, 2, sb_w,
+                                                                            2, sa_w);
+            }
+        }
+      }
+      if constexpr (MX && !FP4) {
         // two 64-deep steps per slice; lane half h takes 16-byte chunks
         // 4 st + h and 4 st + 2 + h of its row and passes the scale of block h
         const int h = lane >> 5;

@@ -1,5 +1,10 @@
-// MXFP8 path: quantisation of bf16 tensors to fp8 e4m3 codes with one e8m0
-// scale per 32 consecutive values, and the scaled-MFMA grouped GEMMs.
+// MXFP8 / MXFP4 path: quantisation of bf16 tensors to fp8 e4m3 (or fp4
+// e2m1) codes with one e8m0 scale per 32 consecutive values, and the
+// scaled-MFMA grouped GEMMs.
+//
+// MXFP4 follows the same rule with e2m1 elements (largest magnitude 6: e is
+// the smallest integer with 6 * 2^e >= amax) and stores two codes per byte,
+// element 2i in the low nibble; a 128-byte slice row then holds 256 values.
 //
 // Quantisation rule (block of 32 values, amax = largest magnitude): the scale
 // is 2^e with e the smallest integer such that 448 * 2^e >= amax, clamped to
@@ -68,10 +73,47 @@ __device__ __forceinline__ uint32_t mx_block(const float v[32], uint32_t out[8])
   return (uint32_t)(e + 127);
 }
 
+// smallest e with 6 * 2^e >= amax, clamped to [-127, 127]
+__device__ __forceinline__ int mx4_exponent(float amax) {
+  if (!(amax > 0x1.8p-125f)) return -127;            // amax <= 6 * 2^-127 (or 0)
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)((b >> 23) & 0xFF) - 127;         // amax = m 2^E, m in [1, 2)
+  const int e = (b & 0x7FFFFFu) <= 0x400000u ? E - 2 : E - 1;   // m <= 1.5 : 1.5 2^E >= amax
+  return e > 127 ? 127 : e;
+}
+
+// e2m1 code of v (finite): the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to
+// the even code, saturating at 6; the midpoints are exact in fp32
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 3;
+  const float a = fabsf(v);
+  const uint32_t code = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                      : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return sign | code;
+}
+
+// quantise 32 fp32 values to e2m1 (16 bytes, element 2i in the low nibble);
+// returns the scale byte
+__device__ __forceinline__ uint32_t mx4_block(const float v[32], uint32_t out[4]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx4_exponent(amax);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) word |= e2m1_code(ldexpf(v[8 * w + b], -e)) << (4 * b);
+    out[w] = word;
+  }
+  return (uint32_t)(e + 127);
+}
+
 // ---------------------------------------------------------------------------
 // Row form: one thread per 32-block.  src [batch][R][ld] bf16 ->
 // codes [batch][R][C], scales [batch][R][C/32].
 // ---------------------------------------------------------------------------
+template <bool FP4>
 __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __restrict__ src, int64_t ld,
                                                             int64_t src_bstride, int R, int C,
                                                             uint8_t* __restrict__ codes,
@@ -92,20 +134,30 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __re
       v[8 * i + 2 * j + 1] = bf16_bits_hi(w[j]);
     }
   }
-  uint32_t out[8];
-  const uint32_t sb = mx_block(v, out);
-  u32x4* q = (u32x4*)(codes + (bt * R + r) * (int64_t)C + b * 32);
-  q[0] = u32x4{out[0], out[1], out[2], out[3]};
-  q[1] = u32x4{out[4], out[5], out[6], out[7]};
+  uint32_t sb;
+  if constexpr (FP4) {
+    uint32_t out[4];
+    sb = mx4_block(v, out);
+    *(u32x4*)(codes + (bt * R + r) * (int64_t)(C / 2) + b * 16) = u32x4{out[0], out[1], out[2], out[3]};
+  } else {
+    uint32_t out[8];
+    sb = mx_block(v, out);
+    u32x4* q = (u32x4*)(codes + (bt * R + r) * (int64_t)C + b * 32);
+    q[0] = u32x4{out[0], out[1], out[2], out[3]};
+    q[1] = u32x4{out[4], out[5], out[6], out[7]};
+  }
   scales[(bt * R + r) * (int64_t)nb + b] = (uint8_t)sb;
 }
 
 hipError_t launch_mx_quant_rows(const void* src, int64_t ld, int64_t src_bstride, int batch, int R, int C,
-                                uint8_t* codes, uint8_t* scales, hipStream_t st) {
+                                uint8_t* codes, uint8_t* scales, bool fp4, hipStream_t st) {
   const int64_t n = (int64_t)R * (C / 32);
   if (n == 0 || batch == 0) return hipSuccess;
-  mx_quant_rows_kernel<<<dim3((unsigned)((n + 255) / 256), batch), 256, 0, st>>>(
-      (const uint16_t*)src, ld, src_bstride, R, C, codes, scales);
+  const dim3 grid((unsigned)((n + 255) / 256), batch);
+  if (fp4)
+    mx_quant_rows_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, src_bstride, R, C, codes, scales);
+  else
+    mx_quant_rows_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, src_bstride, R, C, codes, scales);
   return hipGetLastError();
 }
 
@@ -131,8 +183,8 @@ __global__ __launch_bounds__(256) void padded_offsets_kernel(const int* __restri
   if (g == 0) poff[0] = 0;
 }
 
-hipError_t launch_padded_offsets(const int* off, int G, int* poff, hipStream_t st) {
-  padded_offsets_kernel<<<1, 256, 0, st>>>(off, G, kMxRowAlign, poff);
+hipError_t launch_padded_offsets(const int* off, int G, int* poff, bool fp4, hipStream_t st) {
+  padded_offsets_kernel<<<1, 256, 0, st>>>(off, G, mx_row_align(fp4), poff);
   return hipGetLastError();
 }
 
@@ -147,6 +199,8 @@ hipError_t launch_padded_offsets(const int* off, int G, int* poff, hipStream_t s
 // ---------------------------------------------------------------------------
 constexpr int kQcRows = 128, kQcCols = 64;
 
+// FP4: codes [C][ldq / 2] (two per byte), 16 bytes per block
+template <bool FP4>
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __restrict__ src, int64_t ld,
                                                             int rows, int C, const int* __restrict__ off,
                                                             const int* __restrict__ poff, int G, int64_t ldq,
@@ -155,9 +209,10 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
                                                             int64_t z_codes) {
   __shared__ uint16_t tile[kQcRows][kQcCols];
   // grid z: independent matrices (a batch of weights), z_src elements and
-  // z_codes code bytes apart (z_codes / 32 scale bytes)
+  // z_codes values apart (z_codes code bytes for fp8, half that for fp4;
+  // z_codes / 32 scale bytes)
   src += blockIdx.z * z_src;
-  codes += blockIdx.z * z_codes;
+  codes += blockIdx.z * (FP4 ? z_codes / 2 : z_codes);
   scales += blockIdx.z * (z_codes / 32);
   const int rp0 = blockIdx.x * kQcRows;
   const int c0 = blockIdx.y * kQcCols;
@@ -173,7 +228,9 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
     src0 = off[lo] + local;
     n = off[lo + 1] - off[lo] - local;
   } else {
-    if (rp0 >= ((rows + kQcRows - 1) / kQcRows) * kQcRows) return;
+    // one group: every tile below the padded length is written (rows past
+    // `rows` as zero codes), so an fp4 form padded to 256 rows is complete
+    if (rp0 >= rp_limit) return;
     src0 = rp0;
     n = rows - rp0;
   }
@@ -197,21 +254,33 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
   float v[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = bf16_bits_lo(tile[32 * b + i][pc]);
-  uint32_t out[8];
-  const uint32_t sb = mx_block(v, out);
-  u32x4* q = (u32x4*)(codes + (int64_t)(c0 + c) * ldq + rb);
-  q[0] = u32x4{out[0], out[1], out[2], out[3]};
-  q[1] = u32x4{out[4], out[5], out[6], out[7]};
+  uint32_t sb;
+  if constexpr (FP4) {
+    uint32_t out[4];
+    sb = mx4_block(v, out);
+    *(u32x4*)(codes + (int64_t)(c0 + c) * (ldq / 2) + rb / 2) = u32x4{out[0], out[1], out[2], out[3]};
+  } else {
+    uint32_t out[8];
+    sb = mx_block(v, out);
+    u32x4* q = (u32x4*)(codes + (int64_t)(c0 + c) * ldq + rb);
+    q[0] = u32x4{out[0], out[1], out[2], out[3]};
+    q[1] = u32x4{out[4], out[5], out[6], out[7]};
+  }
   scales[(int64_t)(c0 + c) * (ldq / 32) + rb / 32] = (uint8_t)sb;
 }
 
 hipError_t launch_mx_quant_cols(const void* src, int64_t ld, int rows, int C, const int* off, const int* poff,
-                                int G, int rows_pad_max, int64_t ldq, uint8_t* codes, uint8_t* scales,
+                                int G, int rows_pad_max, int64_t ldq, uint8_t* codes, uint8_t* scales, bool fp4,
                                 hipStream_t st) {
   if (rows_pad_max == 0 || C == 0) return hipSuccess;
   const int tiles = (rows_pad_max + kQcRows - 1) / kQcRows;
-  mx_quant_cols_kernel<<<dim3(tiles, (C + kQcCols - 1) / kQcCols), 256, 0, st>>>(
-      (const uint16_t*)src, ld, rows, C, off, poff, G, ldq, rows_pad_max, codes, scales, 0, 0);
+  const dim3 grid(tiles, (C + kQcCols - 1) / kQcCols);
+  if (fp4)
+    mx_quant_cols_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, rows, C, off, poff, G, ldq,
+                                                     rows_pad_max, codes, scales, 0, 0);
+  else
+    mx_quant_cols_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, rows, C, off, poff, G, ldq,
+                                                      rows_pad_max, codes, scales, 0, 0);
   return hipGetLastError();
 }
 
@@ -219,19 +288,24 @@ hipError_t launch_mx_quant_cols(const void* src, int64_t ld, int rows, int C, co
 // one launch with the batch in the grid's z dimension (one launch per matrix
 // took 8.9 ms for 256 matrices of 4096 x 7168, dominated by launch and drain)
 hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C, uint8_t* codes,
-                                        uint8_t* scales, hipStream_t st) {
+                                        uint8_t* scales, bool fp4, hipStream_t st) {
   if (batch == 0 || R == 0 || C == 0) return hipSuccess;
   const int tiles = (R + kQcRows - 1) / kQcRows;
-  mx_quant_cols_kernel<<<dim3(tiles, (C + kQcCols - 1) / kQcCols, batch), 256, 0, st>>>(
-      (const uint16_t*)src, C, R, C, nullptr, nullptr, 1, R, R, codes, scales, (int64_t)R * C, (int64_t)R * C);
+  const dim3 grid(tiles, (C + kQcCols - 1) / kQcCols, batch);
+  if (fp4)
+    mx_quant_cols_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, nullptr, nullptr, 1, R, R,
+                                                     codes, scales, (int64_t)R * C, (int64_t)R * C);
+  else
+    mx_quant_cols_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, nullptr, nullptr, 1, R, R,
+                                                      codes, scales, (int64_t)R * C, (int64_t)R * C);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// MXFP8 GEMM launchers.
+// MXFP8 / MXFP4 GEMM launchers.  Callers give K, leading dimensions and group
+// strides in values; the kernels count them in 2-byte units of the code
+// bytes (two fp8 values or four fp4 values per unit).
 // ---------------------------------------------------------------------------
-// Persistent pipelined form (gemm_pipe_kernel with MXFP8 operands): the
-// arguments in bytes, converted to the kernel's 2-byte units here.
 static int device_cus_mx() {
   static int cus[64] = {0};
   int dev = 0;
@@ -244,7 +318,14 @@ static int device_cus_mx() {
   return cus[dev];
 }
 
-template <GemmMode MODE, class Epi>
+template <bool FP4>
+static void to_units(GemmArgs& a) {
+  constexpr int per = FP4 ? 4 : 2;        // values per 2-byte unit
+  a.lda /= per; a.ldb /= per; a.K /= per; a.b_kend /= per; a.b_gstride /= per;
+}
+
+// Persistent pipelined form (gemm_pipe_kernel with microscaled operands)
+template <GemmMode MODE, class Epi, bool FP4>
 static hipError_t launch_mx_pipe(GemmArgs a, const MxArgs& s, const typename Epi::P& ep, int n_logical,
                                  int rows_total, hipStream_t st) {
   using C = PipeCfg<64>;
@@ -257,20 +338,19 @@ static hipError_t launch_mx_pipe(GemmArgs a, const MxArgs& s, const typename Epi
   else tiles = (int64_t)MT * NT;
   if (tiles <= 0) return hipSuccess;
   if (a.G > kMaxExperts) return hipErrorInvalidValue;
-  a.lda /= 2; a.ldb /= 2; a.K /= 2; a.b_kend /= 2; a.b_gstride /= 2;
+  to_units<FP4>(a);
   int64_t grid = (int64_t)device_cus_mx() * 2;
   if (tiles < grid) grid = tiles;
-  auto kern = gemm_pipe_kernel<KC, KC, MODE, Epi, 64, true>;
+  auto kern = gemm_pipe_kernel<KC, KC, MODE, Epi, 64, true, FP4>;
   static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
   if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
   return hipGetLastError();
 }
 
-// DMA-fed LDS ring (gemm_mfma_kernel in its MXFP8 form): 128x256 tiles, 2x4
-// waves, three stages; one tile per workgroup.  Arguments in bytes, converted
-// to the kernel's 2-byte units here.
-template <GemmMode MODE, class Epi>
+// DMA-fed LDS ring (gemm_mfma_kernel in its microscaled form): 128x256 tiles,
+// 2x4 waves, three stages; one tile per workgroup.
+template <GemmMode MODE, class Epi, bool FP4>
 static hipError_t launch_mx_dma(GemmArgs a, const MxArgs& s, const typename Epi::P& ep, int n_logical,
                                 int rows_total, hipStream_t st) {
   constexpr int BM = 128, BN = 256, WM = 2, WN = 4, STAGES = 3;
@@ -282,8 +362,8 @@ static hipError_t launch_mx_dma(GemmArgs a, const MxArgs& s, const typename Epi:
   if (MODE == RAGGED_M) tiles = (int64_t)((rows_total + BM - 1) / BM + a.G) * NT;
   else tiles = (int64_t)MT * NT;
   if (tiles <= 0) return hipSuccess;
-  a.lda /= 2; a.ldb /= 2; a.K /= 2; a.b_kend /= 2; a.b_gstride /= 2;
-  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, STAGES, KC, KC, MODE, Epi, true>;
+  to_units<FP4>(a);
+  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, STAGES, KC, KC, MODE, Epi, true, FP4>;
   static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
   if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   kern<<<(unsigned)tiles, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
@@ -295,7 +375,7 @@ static hipError_t launch_mx_dma(GemmArgs a, const MxArgs& s, const typename Epi:
 template <class Epi>
 static hipError_t mx_rows_gemm(const MxQ& q, const int* offsets, const int* prefix, int G, const MxQ& w,
                                int64_t w_gstride, int rows, int N, int K, const typename Epi::P& ep,
-                               int n_logical, hipStream_t st) {
+                               int n_logical, bool fp4, hipStream_t st) {
   GemmArgs a{};
   a.A = q.codes; a.lda = K; a.B = w.codes; a.ldb = K; a.b_gstride = w_gstride;
   a.M = rows; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
@@ -307,47 +387,50 @@ static hipError_t mx_rows_gemm(const MxQ& q, const int* offsets, const int* pref
       return hipErrorInvalidValue;
   if (offsets) {
     a.offsets = offsets; a.tile_prefix = prefix; a.G = G;
-    return launch_mx_dma<RAGGED_M, Epi>(a, s, ep, n_logical, rows, st);
+    return fp4 ? launch_mx_dma<RAGGED_M, Epi, true>(a, s, ep, n_logical, rows, st)
+               : launch_mx_dma<RAGGED_M, Epi, false>(a, s, ep, n_logical, rows, st);
   }
   a.G = 1;
-  return launch_mx_dma<DENSE, Epi>(a, s, ep, n_logical, rows, st);
+  return fp4 ? launch_mx_dma<DENSE, Epi, true>(a, s, ep, n_logical, rows, st)
+             : launch_mx_dma<DENSE, Epi, false>(a, s, ep, n_logical, rows, st);
 }
 
 hipError_t gemm_mx_swiglu_fwd(const MxQ& x, const int* off, const int* prefix, int G, const MxQ& w13, void* hu,
-                              void* act, int rows, int d, int f, const float* row_gates, bool from_stored,
+                              void* act, int rows, int d, int f, const float* row_gates, bool from_stored, bool fp4,
                               hipStream_t st) {
   typename EpiSwiGLU<bf16>::P ep{(bf16*)act, (bf16*)hu, f, row_gates, from_stored ? 1 : 0};
-  return mx_rows_gemm<EpiSwiGLU<bf16>>(x, off, prefix, G, w13, (int64_t)2 * f * d, rows, 2 * f, d, ep, f, st);
+  return mx_rows_gemm<EpiSwiGLU<bf16>>(x, off, prefix, G, w13, (int64_t)2 * f * d, rows, 2 * f, d, ep, f, fp4, st);
 }
 
 hipError_t gemm_mx_down_fwd(const MxQ& act, const int* off, const int* prefix, int G, const MxQ& w2, void* y,
-                            int rows, int d, int f, hipStream_t st) {
+                            int rows, int d, int f, bool fp4, hipStream_t st) {
   typename EpiStore<bf16, 5>::P ep{(bf16*)y, d, 0, rows, d};
-  return mx_rows_gemm<EpiStore<bf16, 5>>(act, off, prefix, G, w2, (int64_t)d * f, rows, d, f, ep, d, st);
+  return mx_rows_gemm<EpiStore<bf16, 5>>(act, off, prefix, G, w2, (int64_t)d * f, rows, d, f, ep, d, fp4, st);
 }
 
 // dA = dY W2 with W2 quantised along d (w2t [g][f][d]); SwiGLU backward epilogue
 hipError_t gemm_mx_down_dgrad_swiglu_bwd(const MxQ& dy, const int* off, const int* prefix, int G,
                                          const MxQ& w2t, const void* hu, void* dhu, int rows, int d, int f,
-                                         const float* row_gates, float* dg_part, void* act_out, hipStream_t st) {
+                                         const float* row_gates, float* dg_part, void* act_out, bool fp4,
+                                         hipStream_t st) {
   typename EpiSwiGLUBwd<bf16>::P ep{(const bf16*)hu, (bf16*)dhu, f, row_gates, row_gates ? dg_part : nullptr,
                                     gemm_dg_parts(true, f), (bf16*)act_out};
-  return mx_rows_gemm<EpiSwiGLUBwd<bf16>>(dy, off, prefix, G, w2t, (int64_t)f * d, rows, f, d, ep, f, st);
+  return mx_rows_gemm<EpiSwiGLUBwd<bf16>>(dy, off, prefix, G, w2t, (int64_t)f * d, rows, f, d, ep, f, fp4, st);
 }
 
 // dX = dHU W13 with W13 quantised along 2f (w13t [g][d][2f]); bf16 or fp32 out
 hipError_t gemm_mx_gateup_dgrad(const MxQ& dhu, const int* off, const int* prefix, int G, const MxQ& w13t,
-                                void* dx, bool f32_out, int rows, int d, int f, hipStream_t st) {
+                                void* dx, bool f32_out, int rows, int d, int f, bool fp4, hipStream_t st) {
   if (f32_out) {
     EpiStoreF32T<1>::P ep{(float*)dx, d, 0, rows, d};
-    return mx_rows_gemm<EpiStoreF32T<1>>(dhu, off, prefix, G, w13t, (int64_t)d * 2 * f, rows, d, 2 * f, ep, d, st);
+    return mx_rows_gemm<EpiStoreF32T<1>>(dhu, off, prefix, G, w13t, (int64_t)d * 2 * f, rows, d, 2 * f, ep, d, fp4,
+                                         st);
   }
   typename EpiStore<bf16, 6>::P ep{(bf16*)dx, d, 0, rows, d};
-  return mx_rows_gemm<EpiStore<bf16, 6>>(dhu, off, prefix, G, w13t, (int64_t)d * 2 * f, rows, d, 2 * f, ep, d, st);
+  return mx_rows_gemm<EpiStore<bf16, 6>>(dhu, off, prefix, G, w13t, (int64_t)d * 2 * f, rows, d, 2 * f, ep, d, fp4,
+                                         st);
 }
 
-// dW[g] (M x N) = P_g^T Q_g with both operands in column form (codes [M][ldq],
-// [N][ldq]) over padded row groups poff (NULL: one group of K rows)
 // zero the weight gradients of groups without rows (poff NULL: one group of K rows)
 __global__ __launch_bounds__(256) void zero_empty_groups_mx_kernel(const int* __restrict__ poff,
                                                                    u32x4* __restrict__ out, int64_t vec, int K) {
@@ -359,13 +442,26 @@ __global__ __launch_bounds__(256) void zero_empty_groups_mx_kernel(const int* __
     o[i] = z;
 }
 
-hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G, int K,
-                         void* dw, int site, hipStream_t st) {
+// dW[g] (M x N) = P_g^T Q_g with both operands in column form (codes [M][ldq],
+// [N][ldq] values) over padded row groups poff (NULL: one group of K rows)
+template <bool FP4>
+static hipError_t mx_wgrad_launch(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G,
+                                  int K, void* dw, int site, hipStream_t st) {
   GemmArgs a{};
   a.A = p.codes; a.lda = ldq; a.B = q.codes; a.ldb = ldq;
   a.M = M; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
   a.offsets = poff; a.G = poff ? G : 1;
   MxArgs s{p.scales, q.scales, ldq / 32, ldq / 32, 0};
+  if (site == 1) {
+    typename EpiStore<bf16, 8>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
+    return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 8>, FP4>(a, s, ep, N, 0, st);
+  }
+  typename EpiStore<bf16, 7>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
+  return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 7>, FP4>(a, s, ep, N, 0, st);
+}
+
+hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G, int K,
+                         void* dw, int site, bool fp4, hipStream_t st) {
   // the pipelined kernel stages 16-byte row pieces of the output (the call's
   // shape checks and 16-byte aligned outputs guarantee them) and skips empty
   // contractions, whose outputs are zero-filled here
@@ -374,12 +470,8 @@ hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, 
   zero_empty_groups_mx_kernel<<<dim3(64, poff ? G : 1), 256, 0, st>>>(poff, (u32x4*)dw, vec, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (site == 1) {
-    typename EpiStore<bf16, 8>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
-    return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 8>>(a, s, ep, N, 0, st);
-  }
-  typename EpiStore<bf16, 7>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
-  return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 7>>(a, s, ep, N, 0, st);
+  return fp4 ? mx_wgrad_launch<true>(p, M, q, N, ldq, poff, G, K, dw, site, st)
+             : mx_wgrad_launch<false>(p, M, q, N, ldq, poff, G, K, dw, site, st);
 }
 
 }  // namespace moe

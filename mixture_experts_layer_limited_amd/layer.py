@@ -115,7 +115,7 @@ class MoELayer:
         abi.moe_permute(self.cfg, x, b["idx"], b["gates"] if fold else None, b["offsets"], b["row_id_map"],
                         b["src_token"], b.get("row_gates"), b["x_perm"], self.ws, stream)
 
-    # -- MXFP8 weights -------------------------------------------------------
+    # -- MXFP8 / MXFP4 weights ----------------------------------------------
     @staticmethod
     def _mx_source_key(*ws):
         """Identity of the bf16 weights the quantised copies were made from:
@@ -135,19 +135,23 @@ class MoELayer:
 
     def prepare_mx_weights(self, w13, w2, ws13=None, ws2=None, stream=None):
         """Quantise the expert weights (once per weight update) in the two
-        orientations the MXFP8 GEMMs contract them in.  The copies are reused
-        by later forward and backward calls for as long as they are given the
-        same, unmodified weight tensors; other weights are quantised anew."""
+        orientations the microscaled GEMMs contract them in (MXFP4 codes two
+        per byte).  The copies are reused by later forward and backward calls
+        for as long as they are given the same, unmodified weight tensors;
+        other weights are quantised anew."""
         s, dev = self.s, self.device
         u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=dev)
         q = {}
+        fp4 = s.dtype == "mxfp4"
+        per_byte = 2 if fp4 else 1
+        quantize = abi.moe_quantize_mxfp4 if fp4 else abi.moe_quantize_mxfp8
 
         def quant(name, w, batch, rows, cols, orient):
             if orient == abi.MOE_MX_ROWS:
-                c, sc = u8(batch, rows, cols), u8(batch, rows, cols // 32)
+                c, sc = u8(batch, rows, cols // per_byte), u8(batch, rows, cols // 32)
             else:
-                c, sc = u8(batch, cols, rows), u8(batch, cols, rows // 32)
-            abi.moe_quantize_mxfp8(w, batch, rows, cols, orient, c, sc, stream)
+                c, sc = u8(batch, cols, rows // per_byte), u8(batch, cols, rows // 32)
+            quantize(w, batch, rows, cols, orient, c, sc, stream)
             q[name] = (c, sc)
 
         quant("w13", w13, s.E, 2 * s.f, s.d, abi.MOE_MX_ROWS)
@@ -166,12 +170,12 @@ class MoELayer:
 
     def experts(self, x, w13, w2, ws13=None, ws2=None, stream=None):
         b = self.buf
-        if self.s.dtype == "mxfp8":
+        if self.s.dtype in ("mxfp8", "mxfp4"):
             self._ensure_mx_weights(w13, w2, ws13, ws2, stream)
-            abi.moe_grouped_gemm_swiglu_mxfp8(self.cfg, b["x_perm"], b["offsets"], b.get("row_gates"),
-                                              self.mx_weights, b.get("hu"), b["act"], b["y_perm"],
-                                              x if self.s.f_shared else None, b.get("hu_s"), b.get("act_s"),
-                                              b.get("y_s"), self.ws, stream)
+            call = abi.moe_grouped_gemm_swiglu_mxfp4 if self.s.dtype == "mxfp4" else abi.moe_grouped_gemm_swiglu_mxfp8
+            call(self.cfg, b["x_perm"], b["offsets"], b.get("row_gates"), self.mx_weights, b.get("hu"), b["act"],
+                 b["y_perm"], x if self.s.f_shared else None, b.get("hu_s"), b.get("act_s"), b.get("y_s"), self.ws,
+                 stream)
             return
         abi.moe_grouped_gemm_swiglu(self.cfg, b["x_perm"], b["offsets"], b.get("row_gates"), w13, w2, b.get("hu"),
                                     b["act"],
@@ -204,9 +208,10 @@ class MoELayer:
         act = None if s.recompute_act else b["act"]
         act_s = None if s.recompute_act else b.get("act_s")
         rg = (b["row_gates"], b["row_id_map"], b["d_gates"]) if fold else (None, None, None)
-        if s.dtype == "mxfp8":
+        if s.dtype in ("mxfp8", "mxfp4"):
             self._ensure_mx_weights(w13, w2, ws13, ws2, stream)
-            abi.moe_grouped_gemm_swiglu_bwd_mxfp8(
+            call = abi.moe_grouped_gemm_swiglu_bwd_mxfp4 if s.dtype == "mxfp4" else abi.moe_grouped_gemm_swiglu_bwd_mxfp8
+            call(
                 self.cfg, b["dy_perm"], b["x_perm"], b["offsets"], rg[0], rg[1], b["hu"], act, self.mx_weights,
                 b["dhu"], b["dx_perm"], b["dw13"], b["dw2"], rg[2], dy if sh else None, x if sh else None,
                 b.get("hu_s"), act_s, b.get("dhu_s"), b["dx_partial"], b.get("dws13"), b.get("dws2"), self.ws,

@@ -11,7 +11,7 @@ from oracle import moe_oracle as O
 
 # relative L2 bound for floating outputs (MXFP8: against an oracle applying the
 # same quantisation)
-TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 1e-2}
+TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 1e-2, "mxfp4": 1e-2}
 # Bound on any single row (last axis) of an output, as a multiple of TOL.  A
 # whole-tensor relative L2 lets one wrong element or a small wrong patch of a
 # large tensor through; every row is held to twice the tensor bound instead.
@@ -36,7 +36,7 @@ def shape_of(cfg: mi.MoEConfig) -> LayerShape:
     return LayerShape(T=cfg.T, d=cfg.d, E=cfg.E, k=cfg.k, f=cfg.f, f_shared=cfg.f_shared,
                       score=cfg.score, n_group=cfg.n_group, topk_group=cfg.topk_group,
                       renorm=cfg.renorm, scale=cfg.scale, aux_coeff=cfg.aux_coeff,
-                      dtype=cfg.dtype if cfg.dtype in ("f32", "mxfp8") else "bf16",
+                      dtype=cfg.dtype if cfg.dtype in ("f32", "mxfp8", "mxfp4") else "bf16",
                       force_balanced=cfg.force_balanced, fold_gates=cfg.fold_gates,
                       recompute_act=cfg.recompute_act)
 
@@ -161,7 +161,7 @@ def compare_layer(cfg: mi.MoEConfig, g: dict, o: dict, backward: bool, tol: floa
           flush=True)
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"relative L2 above {tol}: {bad}"
-    checked = lambda k: cfg.dtype != "mxfp8" or k in MX_ROW_CHECKED
+    checked = lambda k: cfg.dtype not in ("mxfp8", "mxfp4") or k in MX_ROW_CHECKED
     bad = {k: v for k, v in rows.items() if not v <= ROW_FACTOR * tol and checked(k)}
     assert not bad, f"a row's relative L2 above {ROW_FACTOR * tol}: {bad}"
     bad = {k: v for k, v in elems.items() if not v <= ELEM_FACTOR * tol and checked(k)}
@@ -175,15 +175,16 @@ def compare_layer(cfg: mi.MoEConfig, g: dict, o: dict, backward: bool, tol: floa
 
 
 def mx_stepwise_check(cfg: mi.MoEConfig, inp: dict, g: dict) -> dict:
-    """Every MXFP8 expert product of every expert, row by row, recomputed by the
+    """Every MXFP8 / MXFP4 expert product of every expert, row by row, recomputed by the
     oracle from the GPU's own upstream tensors (so both sides quantise the same
     bits): A and H, U from x_perm; Y from act; dH, dU from dy_perm and the
     saved H, U, act; dX from the GPU's dH, dU; the weight gradients over all of
     the expert's rows; the shared expert likewise.  Tensor bound TOL, row bound
     ROW_FACTOR * TOL.  Returns the worst errors."""
-    tol = TOL["mxfp8"]
+    tol = TOL[cfg.dtype]
     f = cfg.f
-    q = O.mx_qdq
+    fmt = O.mx_format_of(cfg.dtype)
+    q = lambda a, axis: O.mx_qdq(a, axis, fmt)
     w13, w2 = inp["w13"], inp["w2"]
     worst, worst_row = {}, {}
 
@@ -195,11 +196,11 @@ def mx_stepwise_check(cfg: mi.MoEConfig, inp: dict, g: dict) -> dict:
         assert e <= tol and r <= ROW_FACTOR * tol and el <= ELEM_FACTOR * tol, (name, e, r, el)
 
     def expert(xe, hu, act, dyp, dhu, dxp, dw13, dw2, W13, W2, fe, tag, gate=None):
-        o = O.swiglu_ffn_fwd_mx(xe, W13, W2, "bf16", gate=gate, act_from_stored=cfg.recompute_act)
+        o = O.swiglu_ffn_fwd_mx(xe, W13, W2, "bf16", gate=gate, act_from_stored=cfg.recompute_act, fmt=fmt)
         chk(tag + "H", hu[:, :fe], o["H"])
         chk(tag + "U", hu[:, fe:], o["U"])
         chk(tag + "A", act, o["A"])
-        b = O.swiglu_ffn_bwd_mx(xe, hu[:, :fe], hu[:, fe:], act, dyp, W13, W2, "bf16", gate=gate)
+        b = O.swiglu_ffn_bwd_mx(xe, hu[:, :fe], hu[:, fe:], act, dyp, W13, W2, "bf16", gate=gate, fmt=fmt)
         chk(tag + "dH", dhu[:, :fe], b["dH"])
         chk(tag + "dU", dhu[:, fe:], b["dU"])
         chk(tag + "dW2", dw2, O.store(q(dyp, 0).T @ q(act, 0), "bf16"))

@@ -66,17 +66,23 @@ def _sample_experts(counts, rng, n=4):
 
 
 class _Ops:
-    """The oracle's expert arithmetic for one dtype: bf16 GEMMs, or MXFP8 GEMMs
-    whose operands are quantised along each contraction (weight-gradient
-    operands along the rows, blocks starting at the expert's first row)."""
+    """The oracle's expert arithmetic for one dtype: bf16 GEMMs, or MXFP8 /
+    MXFP4 GEMMs whose operands are quantised along each contraction
+    (weight-gradient operands along the rows, blocks starting at the expert's
+    first row)."""
 
-    def __init__(self, mx: bool):
-        self.mx = mx
-        self.ffn_fwd = O.swiglu_ffn_fwd_mx if mx else O.swiglu_ffn_fwd
-        self.ffn_bwd = O.swiglu_ffn_bwd_mx if mx else O.swiglu_ffn_bwd
+    def __init__(self, dtype: str):
+        self.mx = dtype in ("mxfp8", "mxfp4")
+        fmt = O.mx_format_of(dtype) if self.mx else None
+        self.fmt = fmt
+        if self.mx:
+            self.ffn_fwd = lambda *a, **k: O.swiglu_ffn_fwd_mx(*a, fmt=fmt, **k)
+            self.ffn_bwd = lambda *a, **k: O.swiglu_ffn_bwd_mx(*a, fmt=fmt, **k)
+        else:
+            self.ffn_fwd, self.ffn_bwd = O.swiglu_ffn_fwd, O.swiglu_ffn_bwd
 
     def q(self, a, axis):
-        return O.mx_qdq(a, axis) if self.mx else a
+        return O.mx_qdq(a, axis, self.fmt) if self.mx else a
 
     def nt(self, a, w):          # a @ w.T, contraction along both last axes
         return self.q(a, 1) @ self.q(w, 1).T
@@ -89,7 +95,7 @@ class _Ops:
 
 
 FULL = [mi.CONFIGS["deepseek_v3"], mi.CONFIGS["qwen3_235b"], mi.CONFIGS["mixtral"],
-        mi.CONFIGS["deepseek_v3_skew_mxfp8"], mi.CONFIGS["deepseek_v3_ep_share"]]
+        mi.CONFIGS["deepseek_v3_skew_mxfp8"], mi.CONFIGS["deepseek_v3_skew_mxfp4"], mi.CONFIGS["deepseek_v3_ep_share"]]
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
@@ -104,7 +110,7 @@ def test_fullsize_sampled_parity(cfg):
     b = run_gpu_tensors(cfg, inp, backward=bwd)
     T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.f_shared
     st = "bf16"
-    ops = _Ops(cfg.dtype == "mxfp8")
+    ops = _Ops(cfg.dtype)
 
     # -- router -------------------------------------------------------------
     toks = _pick(rng, T, 48)

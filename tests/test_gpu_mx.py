@@ -1,12 +1,14 @@
-"""MXFP8 path on the GPU against the oracle.
+"""MXFP8 and MXFP4 paths on the GPU against the oracle.
 
-* moe_quantize_mxfp8: codes and scales bit-exact to the oracle's rule, in both
-  orientations, on values spanning many binades, zero blocks and exact ties.
-* The whole layer (bf16 router / permute / combine, MXFP8 expert GEMMs routed
-  and shared, forward and backward) on skewed routing with empty experts:
-  rel-L2 <= 1e-2 against the oracle applying the same quantisation.  Against
-  the bf16 oracle the output moves by what the quantisation rule itself moves
-  it (the same-quantisation oracle's own distance, reported beside it).
+* moe_quantize_mxfp8 / moe_quantize_mxfp4: codes (fp4 packed two per byte)
+  and scales bit-exact to the oracle's rule, in both orientations, on values
+  spanning many binades, zero blocks and exact ties.
+* The whole layer (bf16 router / permute / combine, microscaled expert GEMMs
+  routed and shared, forward and backward) on skewed routing with empty
+  experts: rel-L2 <= 1e-2 against the oracle applying the same quantisation,
+  and every expert product row by row on the GPU's own inputs.  Against the
+  bf16 oracle the output moves by what the quantisation rule itself moves it
+  (the same-quantisation oracle's own distance, reported beside it).
 """
 from __future__ import annotations
 
@@ -37,27 +39,34 @@ def _bf16_matrix(batch, rows, cols, seed):
     return x.to(torch.bfloat16)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 @pytest.mark.parametrize("batch,rows,cols", [(1, 64, 96), (3, 96, 128), (2, 160, 64)])
-def test_quantize_mxfp8_bitexact(batch, rows, cols):
+def test_quantize_mx_bitexact(batch, rows, cols, fmt):
     _needs_gpu()
-    print(f"\n[mx quant] batch={batch} rows={rows} cols={cols}", flush=True)
+    fp4 = fmt == "e2m1"
+    print(f"\n[mx quant] {fmt} batch={batch} rows={rows} cols={cols}", flush=True)
     x = _bf16_matrix(batch, rows, cols, seed=rows * 7 + cols)
+    if fp4:
+        x[:, 6, :] = 2.5 * 2.0 ** -5                      # scaled to 5.0, an e2m1 tie (-> 4, the even code)
     xd = x.cuda()
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    quant = abi.moe_quantize_mxfp4 if fp4 else abi.moe_quantize_mxfp8
+    packed = (lambda c: O.pack_e2m1(c)) if fp4 else (lambda c: c)
+    per = 2 if fp4 else 1
     xf = x.double().numpy()
     # rows: blocks along cols
-    c, s = u8(batch, rows, cols), u8(batch, rows, cols // 32)
-    abi.moe_quantize_mxfp8(xd, batch, rows, cols, abi.MOE_MX_ROWS, c, s)
-    oc, osc = O.mx_quantize(xf, 2)
+    c, s = u8(batch, rows, cols // per), u8(batch, rows, cols // 32)
+    quant(xd, batch, rows, cols, abi.MOE_MX_ROWS, c, s)
+    oc, osc = O.mx_quantize(xf, 2, fmt)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(c.cpu().numpy(), oc)
+    np.testing.assert_array_equal(c.cpu().numpy(), packed(oc))
     np.testing.assert_array_equal(s.cpu().numpy(), osc)
     # cols: transposed copy, blocks along rows
-    c2, s2 = u8(batch, cols, rows), u8(batch, cols, rows // 32)
-    abi.moe_quantize_mxfp8(xd, batch, rows, cols, abi.MOE_MX_COLS, c2, s2)
-    oc2, osc2 = O.mx_quantize(np.swapaxes(xf, 1, 2), 2)
+    c2, s2 = u8(batch, cols, rows // per), u8(batch, cols, rows // 32)
+    quant(xd, batch, rows, cols, abi.MOE_MX_COLS, c2, s2)
+    oc2, osc2 = O.mx_quantize(np.swapaxes(xf, 1, 2), 2, fmt)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(c2.cpu().numpy(), oc2)
+    np.testing.assert_array_equal(c2.cpu().numpy(), packed(oc2))
     np.testing.assert_array_equal(s2.cpu().numpy(), osc2)
 
 
@@ -76,6 +85,14 @@ MX_CASES = [
     # gates folded into act and act formed again in the backward
     _cfg("mx_dsv3_like_fold_recompute", T=256, d=256, E=32, k=4, f=128, f_shared=128, score="sigmoid",
          n_group=4, topk_group=2, renorm=True, scale=2.5, bias="zipf", fold_gates=True, recompute_act=True),
+    # MXFP4 (d, f, f_shared multiples of 256): the same three kinds, a ragged
+    # token count whose shared-expert contraction pads to 256 rows
+    _cfg("mx4_dsv3_like", T=200, d=256, E=32, k=4, f=256, f_shared=256, score="sigmoid", n_group=4,
+         topk_group=2, renorm=True, scale=2.5, bias="zipf", dtype="mxfp4"),
+    _cfg("mx4_softmax", T=192, d=512, E=8, k=2, f=256, score="softmax", dtype="mxfp4"),
+    _cfg("mx4_dsv3_like_fold_recompute", T=256, d=256, E=32, k=4, f=256, f_shared=256, score="sigmoid",
+         n_group=4, topk_group=2, renorm=True, scale=2.5, bias="zipf", fold_gates=True, recompute_act=True,
+         dtype="mxfp4"),
 ]
 
 
@@ -94,7 +111,7 @@ def test_mx_layer_parity(cfg):
     # itself: as far as the same-quantisation oracle moves (both reported)
     ob = run_oracle(cfg.with_(dtype="bf16"), inp, backward=False)
     e_gpu, e_orc = rel_l2(g["y"], ob["y"]), rel_l2(o["y"], ob["y"])
-    print(f"  y vs bf16 oracle: GPU {e_gpu:.2e}, MX oracle {e_orc:.2e}", flush=True)
+    print(f"  y vs bf16 oracle: GPU {e_gpu:.2e}, {cfg.dtype} oracle {e_orc:.2e}", flush=True)
     assert e_gpu <= 1.1 * e_orc + 1e-3
 
 
