@@ -280,8 +280,8 @@ def main():
                           "launches": 3}))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this layer runs on one GPU; multi-GPU sharding is not built "
-                                   "(see DESIGN.md: how the path would shard)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this layer runs on one GPU; sharding it over several GPUs (expert "
+                                   "parallelism with all-to-all exchanges) is not built", "n_gpus": args.gpus}))
         sys.exit(2)
 
     from mixture_experts_layer_limited_amd import LayerShape, MoELayer, _abi as abi

@@ -24,7 +24,8 @@ with numpy (a matmul is the only library primitive used), following the pages
 The pages give no formula for scores, groups, gates, the aux loss or the
 backward pass.  Those follow the workload descriptions (sigmoid + selection-only
 bias, 8 groups / top-4 by top-2 sum, renormalise then x2.5, aux coefficient
-1e-3) and the readings listed in the design doc (R1..R20):
+1e-3) and, where both are silent, the plainest readings; the ones this module
+depends on:
 
   R3  softmax selection key = fp32 logit (softmax is monotone), ties -> lower id
   R4  sigmoid score s = fp32(1 / (1 + exp(-(double) l))); key = fp32(s + b)
