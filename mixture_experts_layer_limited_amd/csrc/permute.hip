@@ -32,17 +32,27 @@ hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int E, int* hist, 
   return hipGetLastError();
 }
 
-// hist[r][e] (counts) -> base[r][e] = offsets[e] + sum_{r' < r} hist[r'][e]; offsets[E] = rows
+// hist[r][e] (counts) -> base[r][e] = offsets[e] + sum_{r' < r} hist[r'][e]; offsets[E] = rows.
+// Thread e walks its column in batches of kScanBatch ranges: the batch's loads
+// are all issued before the running sum uses them, so a column of R entries
+// costs R / kScanBatch memory round trips instead of R (the loads and stores
+// of one batch are independent).
+constexpr int kScanBatch = 16;
 __global__ __launch_bounds__(256) void perm_scan_kernel(int* __restrict__ hist, int R, int E, int rows,
                                                         int32_t* __restrict__ offsets) {
   __shared__ int tot[kMaxExperts];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int r = 0; r < R; ++r) {
-      int c = hist[(int64_t)r * E + e];
-      hist[(int64_t)r * E + e] = run;
-      run += c;
+    for (int r0 = 0; r0 < R; r0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) c[i] = r0 + i < R ? hist[(int64_t)(r0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (r0 + i < R) hist[(int64_t)(r0 + i) * E + e] = run;
+        run += c[i];
+      }
     }
   }
   tot[e] = (e < E) ? run : 0;
@@ -54,9 +64,16 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int* __restrict__ hist, 
     __syncthreads();
   }
   if (e < E) {
-    int off = tot[e] - run;                  // exclusive
+    const int off = tot[e] - run;            // exclusive
     offsets[e] = off;
-    for (int r = 0; r < R; ++r) hist[(int64_t)r * E + e] += off;
+    for (int r0 = 0; r0 < R; r0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) c[i] = r0 + i < R ? hist[(int64_t)(r0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (r0 + i < R) hist[(int64_t)(r0 + i) * E + e] = c[i] + off;
+    }
   }
   if (e == 0) offsets[E] = rows;
 }
@@ -195,25 +212,50 @@ __device__ void Vec8<float>::store(float* p) const {
   *(floatx4*)(p + 4) = b;
 }
 
+// Streaming loads of rows read once (the permuted rows of the combine and of
+// the permute backward): non-temporal, so they do not displace lines the
+// other reads of the kernel reuse.
+template <class T>
+__device__ __forceinline__ void load_nt(Vec8<T>& v, const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 w = __builtin_nontemporal_load((const u32x4*)p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v.v[2 * i] = bf16_bits_lo(w[i]); v.v[2 * i + 1] = bf16_bits_hi(w[i]); }
+  } else {
+    v.load(p);
+  }
+}
+
+// Work split of the row kernels: a block of kRowThreads threads takes
+// kRowTokens consecutive tokens, and its threads walk the tokens' 8-element
+// chunks as one sequence (chunk q of the block: token q / vec, chunk q % vec),
+// so no pass leaves threads idle when a row's chunk count is not a multiple of
+// the block size (d = 7168: 896 chunks a row, 1792 for two tokens = 7 passes
+// of 256).
+constexpr int kRowThreads = 256, kRowTokens = 2;
+
 // KC > 0: k = KC known at compile time, so the k row loads of a chunk are all
 // issued before the sum (0: any k, one row at a time).  The fp32 sum keeps the
 // j order either way.
 template <class T, int KC>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_perm,
-                                                      const int32_t* __restrict__ rmap,
-                                                      const float* __restrict__ gates,
-                                                      const T* __restrict__ y_shared, T* __restrict__ y,
-                                                      int k_rt, int d) {
-  const int t = blockIdx.x;
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(const T* __restrict__ y_perm,
+                                                              const int32_t* __restrict__ rmap,
+                                                              const float* __restrict__ gates,
+                                                              const T* __restrict__ y_shared, T* __restrict__ y,
+                                                              int T_, int k_rt, int d) {
   const int k = KC > 0 ? KC : k_rt;
-  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+  const int vec = d / 8;
+  const int t0 = blockIdx.x * kRowTokens;
+  const int nq = min(kRowTokens, T_ - t0) * vec;
+  for (int q = threadIdx.x; q < nq; q += kRowThreads) {
+    const int t = t0 + q / vec, c = (q % vec) * 8;
     Vec8<T> acc;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc.v[i] = 0.0f;
     if constexpr (KC > 0) {
       Vec8<T> r[KC];
 #pragma unroll
-      for (int j = 0; j < KC; ++j) r[j].load(y_perm + (int64_t)rmap[(int64_t)t * KC + j] * d + c);
+      for (int j = 0; j < KC; ++j) load_nt(r[j], y_perm + (int64_t)rmap[(int64_t)t * KC + j] * d + c);
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         const float g = gates ? gates[(int64_t)t * KC + j] : 1.0f;
@@ -225,16 +267,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_pe
         const int64_t row = rmap[(int64_t)t * k + j];
         const float g = gates ? gates[(int64_t)t * k + j] : 1.0f;
         Vec8<T> r;
-        r.load(y_perm + row * d + c);
+        load_nt(r, y_perm + row * d + c);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc.v[i] += g * r.v[i];
       }
     }
     if (y_shared) {
-      Vec8<T> s;
-      s.load(y_shared + (int64_t)t * d + c);
+      Vec8<T> sh;
+      load_nt(sh, y_shared + (int64_t)t * d + c);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc.v[i] += s.v[i];
+      for (int i = 0; i < 8; ++i) acc.v[i] += sh.v[i];
     }
     acc.store(y + (int64_t)t * d + c);
   }
@@ -256,75 +298,97 @@ template <class T>
 hipError_t launch_combine(const T* y_perm, const int32_t* rmap, const float* gates, const T* y_shared,
                           T* y, int T_, int k, int d, hipStream_t st) {
   if (T_ == 0) return hipSuccess;
-#define MOE_L(KC) combine_kernel<T, KC><<<T_, 256, 0, st>>>(y_perm, rmap, gates, y_shared, y, k, d)
+#define MOE_L(KC)                                                                                   \
+  combine_kernel<T, KC><<<(T_ + kRowTokens - 1) / kRowTokens, kRowThreads, 0, st>>>(y_perm, rmap, gates, \
+                                                                                      y_shared, y, T_, k, d)
   MOE_DISPATCH_K(k, MOE_L);
 #undef MOE_L
   return hipGetLastError();
 }
 
 // dy_perm[row(t,j)] = storage(g dy[t]); d_gates[t,j] = <dy[t], y_perm[row(t,j)]>
-// KC > 0 (k known at compile time): each chunk of dy is read once for all k
-// rows, the k row loads are issued together, and the k dot products are
-// reduced in one pass at the end.  Every thread accumulates its dot products
-// over its chunks in the same order as the runtime-k form (one j at a time),
-// and the wave sums and the sum of the four wave partials are the same, so
-// both forms give the same bits.
+// KC > 0 (k known at compile time): the block takes kRowTokens tokens with the
+// work split of the combine; each chunk of dy is read once for all k rows, the
+// k row loads are issued together, and every thread keeps one dot product per
+// (token, j) over its chunks, which are reduced over the block in a fixed order
+// (the wave sum, then the waves' partials in wave order).  KC = 0: one token
+// per block, one j at a time.
 template <class T, int KC>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy,
-                                                          const T* __restrict__ y_perm,
-                                                          const int32_t* __restrict__ rmap,
-                                                          const float* __restrict__ gates,
-                                                          T* __restrict__ dy_perm,
-                                                          float* __restrict__ d_gates, int k_rt, int d) {
-  const int t = blockIdx.x;
+__global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(const T* __restrict__ dy,
+                                                                  const T* __restrict__ y_perm,
+                                                                  const int32_t* __restrict__ rmap,
+                                                                  const float* __restrict__ gates,
+                                                                  T* __restrict__ dy_perm,
+                                                                  float* __restrict__ d_gates, int T_, int k_rt,
+                                                                  int d) {
+  constexpr int NWV = kRowThreads / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if constexpr (KC > 0) {
-    __shared__ float part[4][KC];
-    int64_t row[KC];
-    float g[KC], dot[KC];
+    __shared__ float part[NWV][kRowTokens][KC];
+    const int vec = d / 8;
+    const int t0 = blockIdx.x * kRowTokens;
+    const int ntok = min(kRowTokens, T_ - t0);
+    float dot[kRowTokens][KC];
 #pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      row[j] = rmap[(int64_t)t * KC + j];
-      g[j] = gates[(int64_t)t * KC + j];
-      dot[j] = 0.0f;
-    }
-    for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    for (int tt = 0; tt < kRowTokens; ++tt)
+#pragma unroll
+      for (int j = 0; j < KC; ++j) dot[tt][j] = 0.0f;
+    for (int q = threadIdx.x; q < ntok * vec; q += kRowThreads) {
+      const int tt = q / vec, c = (q % vec) * 8, t = t0 + tt;
+      int64_t row[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) row[j] = rmap[(int64_t)t * KC + j];
       Vec8<T> a, r[KC];
-      a.load(dy + (int64_t)t * d + c);
+      load_nt(a, dy + (int64_t)t * d + c);
 #pragma unroll
-      for (int j = 0; j < KC; ++j) r[j].load(y_perm + row[j] * d + c);
+      for (int j = 0; j < KC; ++j) load_nt(r[j], y_perm + row[j] * d + c);
+      float dj[KC];
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
+        const float g = gates[(int64_t)t * KC + j];
         Vec8<T> o;
+        dj[j] = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          dot[j] += a.v[i] * r[j].v[i];
-          o.v[i] = g[j] * a.v[i];
+          dj[j] += a.v[i] * r[j].v[i];
+          o.v[i] = g * a.v[i];
         }
         o.store(dy_perm + row[j] * d + c);
       }
+      // a chunk belongs to one token: add its terms to that token's sums
+#pragma unroll
+      for (int u = 0; u < kRowTokens; ++u)
+        if (u == tt)
+#pragma unroll
+          for (int j = 0; j < KC; ++j) dot[u][j] += dj[j];
     }
 #pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      const float w = wave_sum(dot[j]);
-      if (lane == 0) part[wave][j] = w;
-    }
+    for (int tt = 0; tt < kRowTokens; ++tt)
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const float w = wave_sum(dot[tt][j]);
+        if (lane == 0) part[wave][tt][j] = w;
+      }
     __syncthreads();
-    if (threadIdx.x < KC) {
-      const int j = threadIdx.x;
-      d_gates[(int64_t)t * KC + j] = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
+    if (threadIdx.x < ntok * KC) {
+      const int tt = threadIdx.x / KC, j = threadIdx.x % KC;
+      float sum = part[0][tt][j];
+#pragma unroll
+      for (int w = 1; w < NWV; ++w) sum += part[w][tt][j];
+      d_gates[(int64_t)(t0 + tt) * KC + j] = sum;
     }
   } else {
-    __shared__ float part[4];
+    __shared__ float part[NWV];
+    const int t = blockIdx.x;
     const int k = k_rt;
     for (int j = 0; j < k; ++j) {
       const int64_t row = rmap[(int64_t)t * k + j];
       const float g = gates[(int64_t)t * k + j];
       float dot = 0.0f;
-      for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+      for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
         Vec8<T> a, r, o;
         a.load(dy + (int64_t)t * d + c);
-        r.load(y_perm + row * d + c);
+        load_nt(r, y_perm + row * d + c);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           dot += a.v[i] * r.v[i];
@@ -335,7 +399,11 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
       dot = wave_sum(dot);
       if (lane == 0) part[wave] = dot;
       __syncthreads();
-      if (threadIdx.x == 0) d_gates[(int64_t)t * k + j] = ((part[0] + part[1]) + part[2]) + part[3];
+      if (threadIdx.x == 0) {
+        float sum = part[0];
+        for (int w = 1; w < NWV; ++w) sum += part[w];
+        d_gates[(int64_t)t * k + j] = sum;
+      }
       __syncthreads();
     }
   }
@@ -345,21 +413,27 @@ template <class T>
 hipError_t launch_combine_bwd(const T* dy, const T* y_perm, const int32_t* rmap, const float* gates, T* dy_perm,
                               float* d_gates, int T_, int k, int d, hipStream_t st) {
   if (T_ == 0) return hipSuccess;
-#define MOE_L(KC) combine_bwd_kernel<T, KC><<<T_, 256, 0, st>>>(dy, y_perm, rmap, gates, dy_perm, d_gates, k, d)
+#define MOE_L(KC)                                                                                         \
+  combine_bwd_kernel<T, KC><<<KC > 0 ? (T_ + kRowTokens - 1) / kRowTokens : T_, kRowThreads, 0, st>>>(         \
+      dy, y_perm, rmap, gates, dy_perm, d_gates, T_, k, d)
   MOE_DISPATCH_K(k, MOE_L);
 #undef MOE_L
   return hipGetLastError();
 }
 
-// dx[t] = storage(partial[t] + sum_j dx_perm[row(t,j)]), j in order; KC as in combine
+// dx[t] = storage(partial[t] + sum_j dx_perm[row(t,j)]), j in order; KC and
+// the work split as in combine
 template <class T, int KC>
-__global__ __launch_bounds__(256) void unpermute_sum_kernel(const T* __restrict__ dx_perm,
-                                                            const int32_t* __restrict__ rmap,
-                                                            const float* __restrict__ partial,
-                                                            T* __restrict__ dx, int k_rt, int d) {
-  const int t = blockIdx.x;
+__global__ __launch_bounds__(kRowThreads) void unpermute_sum_kernel(const T* __restrict__ dx_perm,
+                                                                    const int32_t* __restrict__ rmap,
+                                                                    const float* __restrict__ partial,
+                                                                    T* __restrict__ dx, int T_, int k_rt, int d) {
   const int k = KC > 0 ? KC : k_rt;
-  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+  const int vec = d / 8;
+  const int t0 = blockIdx.x * kRowTokens;
+  const int nq = min(kRowTokens, T_ - t0) * vec;
+  for (int q = threadIdx.x; q < nq; q += kRowThreads) {
+    const int t = t0 + q / vec, c = (q % vec) * 8;
     Vec8<T> acc;
     if (partial) {
       Vec8<float> p;
@@ -373,7 +447,7 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(const T* __restrict_
     if constexpr (KC > 0) {
       Vec8<T> r[KC];
 #pragma unroll
-      for (int j = 0; j < KC; ++j) r[j].load(dx_perm + (int64_t)rmap[(int64_t)t * KC + j] * d + c);
+      for (int j = 0; j < KC; ++j) load_nt(r[j], dx_perm + (int64_t)rmap[(int64_t)t * KC + j] * d + c);
 #pragma unroll
       for (int j = 0; j < KC; ++j)
 #pragma unroll
@@ -382,7 +456,7 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(const T* __restrict_
       for (int j = 0; j < k; ++j) {
         const int64_t row = rmap[(int64_t)t * k + j];
         Vec8<T> r;
-        r.load(dx_perm + row * d + c);
+        load_nt(r, dx_perm + row * d + c);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc.v[i] += r.v[i];
       }
@@ -395,7 +469,9 @@ template <class T>
 hipError_t launch_unpermute_sum(const T* dx_perm, const int32_t* rmap, const float* partial, T* dx,
                                 int T_, int k, int d, hipStream_t st) {
   if (T_ == 0) return hipSuccess;
-#define MOE_L(KC) unpermute_sum_kernel<T, KC><<<T_, 256, 0, st>>>(dx_perm, rmap, partial, dx, k, d)
+#define MOE_L(KC)                                                                                 \
+  unpermute_sum_kernel<T, KC><<<(T_ + kRowTokens - 1) / kRowTokens, kRowThreads, 0, st>>>(dx_perm, rmap, \
+                                                                                          partial, dx, T_, k, d)
   MOE_DISPATCH_K(k, MOE_L);
 #undef MOE_L
   return hipGetLastError();
