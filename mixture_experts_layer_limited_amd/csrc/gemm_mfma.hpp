@@ -55,8 +55,6 @@
 // lengthen a wait).
 #pragma once
 
-#include <type_traits>
-
 #include "gemm.hpp"
 
 namespace moe {
@@ -238,18 +236,6 @@ struct SliceIter {
   int ks, nk;     // slice within the tile, slices of the tile
   TileCoord c;
 };
-
-// f(std::integral_constant<int, n>) for a uniform n in 1..N (nothing for n = 0)
-template <int N, class F>
-__device__ __forceinline__ void with_count(int n, F&& f) {
-  if constexpr (N >= 1) {
-    if (n == N) {
-      f(std::integral_constant<int, N>{});
-      return;
-    }
-    with_count<N - 1>(n, f);
-  }
-}
 
 // Scheduling groups of one 64-deep slice (four K-steps) whose fragments are
 // double-buffered: step 0's R LDS reads, then for steps 0..2 the next step's R
@@ -682,17 +668,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
         }
       }
       if constexpr (!MX) {
-        // Only the wave's 32-row fragments that hold rows of the tile below
-        // m_end are multiplied: an expert's last tile is mostly padding (at
-        // 128 rows per expert on average, a third of the MFMAs of a ragged
-        // product fell on padding rows).  The count is uniform per wave.
-        // fragments of K-step kk + 1 are read while the MFMAs of step kk run
-        // (two register sets), in the order the scheduling groups fix
-        auto mma = [&](auto nv_c) {
-          constexpr int NV = decltype(nv_c)::value;
-          bf16x8 af[2][NV], bfr[2][FN];
+        // A wave whose rows of the tile all lie past m_end (the padding of an
+        // expert's last tile) skips its reads and MFMAs, which leaves the
+        // MFMA pipe to the waves of other workgroups on its SIMD.  Fragments
+        // of K-step kk + 1 are read while the MFMAs of step kk run (two
+        // register sets), in the order the scheduling groups fix.
+        if (comp.c.m0 + wm * (BM / WM) < comp.c.m_end) {
+          bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
-          for (int i = 0; i < NV; ++i) af[0][i] = fa.read(sa, i, 0);
+          for (int i = 0; i < FM; ++i) af[0][i] = fa.read(sa, i, 0);
 #pragma unroll
           for (int j = 0; j < FN; ++j) bfr[0][j] = fb.read(sb, j, 0);
 #pragma unroll
@@ -700,21 +684,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
             const int cur = kk & 1;
             if (kk + 1 < BK / 16) {
 #pragma unroll
-              for (int i = 0; i < NV; ++i) af[cur ^ 1][i] = fa.read(sa, i, kk + 1);
+              for (int i = 0; i < FM; ++i) af[cur ^ 1][i] = fa.read(sa, i, kk + 1);
 #pragma unroll
               for (int j = 0; j < FN; ++j) bfr[cur ^ 1][j] = fb.read(sb, j, kk + 1);
             }
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
               for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
           }
-          sched_pipelined_slice<NV * (LA == KC ? 1 : 2) + FN * (LB == KC ? 1 : 2), NV * FN>();
-        };
-        // (256-row tiles keep the plain form: the counted variants would push
-        // their 128 accumulators past the 256 registers a wave may hold)
-        if (comp.c.m0 + wm * (BM / WM) < comp.c.m_end) mma(std::integral_constant<int, FM>{});
+          sched_pipelined_slice<FM * (LA == KC ? 1 : 2) + FN * (LB == KC ? 1 : 2), FM * FN>();
+        }
       }
     }
     if constexpr (Epi::kStaged) {

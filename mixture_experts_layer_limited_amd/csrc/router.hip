@@ -18,9 +18,16 @@ namespace {
 constexpr int kNI = kMaxExperts / kWave;   // values per lane (E <= 256)
 constexpr int kRouterWaves = 4;
 
+// Key order: larger first, equal keys by lower id, and a NaN key below every
+// number (-inf included).  The search starts from (NaN, INT_MAX), which every
+// candidate beats, so a selection always returns a candidate's id, whatever
+// values the logits hold.
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
+  const bool na = ka != ka, nb = kb != kb;
+  if (na || nb) return nb && (!na || ia < ib);
   return ka > kb || (ka == kb && ia < ib);
 }
+constexpr int kNoId = 0x7fffffff;
 
 // wave-wide argmax of (key desc, id asc); every lane returns the winner
 __device__ __forceinline__ void wave_argmax(float& k, int& i) {
@@ -113,14 +120,19 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       for (int i = 0; i < kNI; ++i) gs[i] = -INFINITY;
       for (int g = 0; g < p.n_group; ++g) {
         float t1 = -INFINITY, t2 = -INFINITY;
+        bool has_nan = false;
 #pragma unroll
         for (int i = 0; i < kNI; ++i) {
           int e = lane + 64 * i;
           if (elig[i] && e / per == g) {
             float kv = key[i];
+            has_nan |= kv != kv;
             if (kv > t1) { t2 = t1; t1 = kv; } else if (kv > t2) { t2 = kv; }
           }
         }
+        // a group holding a NaN key scores NaN (it ranks below every group
+        // with a numeric score)
+        const bool group_nan = __any(has_nan);
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
           float o1 = __shfl_xor(t1, o, kWave), o2 = __shfl_xor(t2, o, kWave);
@@ -128,7 +140,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
           t2 = fmaxf(lo, fmaxf(t2, o2));
           t1 = hi;
         }
-        float score = per >= 2 ? t1 + t2 : t1;
+        float score = group_nan ? __builtin_nanf("") : per >= 2 ? t1 + t2 : t1;
 #pragma unroll
         for (int i = 0; i < kNI; ++i)
           if (lane + 64 * i == g) gs[i] = score;
@@ -137,8 +149,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       uint64_t gm[kNI] = {0, 0, 0, 0};
       bool gtaken[kNI] = {false, false, false, false};
       for (int r = 0; r < p.topk_group; ++r) {
-        float bk = -INFINITY;
-        int bi = 0x7fffffff;
+        float bk = __builtin_nanf("");
+        int bi = kNoId;
 #pragma unroll
         for (int i = 0; i < kNI; ++i) {
           int g = lane + 64 * i;
@@ -176,8 +188,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       if (p.balanced) {
         bi = (int)(((int64_t)t * k + j) % E);
       } else {
-        float bk = -INFINITY;
-        bi = 0x7fffffff;
+        float bk = __builtin_nanf("");
+        bi = kNoId;
 #pragma unroll
         for (int i = 0; i < kNI; ++i) {
           int e = lane + 64 * i;

@@ -68,6 +68,11 @@ depends on:
       (rounded) H and U in the forward, and the backward forms it again from
       them, so it is not kept between the passes and both forms agree bit for
       bit
+  R27 non-finite keys (the pages are silent): -inf and +inf order as numbers;
+      a NaN key ranks after every number, NaN keys among themselves by lower
+      id; a group holding a NaN key scores NaN and ranks after every group
+      with a numeric score.  So the k choices are k distinct eligible experts
+      whatever the logits hold
 
 Pins that tie this oracle to facts outside itself live in tests/test_oracle_*.py.
 """
@@ -146,24 +151,32 @@ def selection_keys(logits, cfg, bias=None, exact: bool = False) -> np.ndarray:
 
 
 def _desc_order(values, ids) -> np.ndarray:
-    """ids sorted by value descending, equal values by id ascending."""
+    """ids sorted by value descending, equal values by id ascending; NaN values
+    after every number (-inf included), among themselves by id (R27)."""
     values = np.asarray(values)
     ids = np.asarray(ids)
     o = np.argsort(ids, kind="stable")               # ids ascending first
-    o2 = np.argsort(-values[o], kind="stable")       # then a stable sort by value desc
-    return ids[o][o2]
+    v = values[o]
+    num = ~np.isnan(v)
+    o_num = o[num][np.argsort(-v[num], kind="stable")]   # numbers: stable sort by value desc
+    return np.concatenate([ids[o_num], ids[o[~num]]])
 
 
 def eligible_groups(keys_row, n_group: int, topk_group: int) -> np.ndarray:
     """Group-limited routing for one token (R5): split the E experts into
     n_group contiguous groups, score each group by the sum of its two largest
     keys (one fp32 add; a single-expert group scores its only key), keep the
-    topk_group best groups.  Returns the kept group ids in rank order."""
+    topk_group best groups.  Returns the kept group ids in rank order.  A group
+    holding a NaN key scores NaN and so ranks after every numeric score (R27)."""
     E = keys_row.shape[0]
     per = E // n_group
     gscore = np.empty(n_group, dtype=keys_row.dtype)
     for g in range(n_group):
-        member = np.sort(keys_row[g * per:(g + 1) * per])[::-1]
+        member = keys_row[g * per:(g + 1) * per]
+        if np.isnan(member).any():
+            gscore[g] = np.nan
+            continue
+        member = np.sort(member)[::-1]
         gscore[g] = member[0] + member[1] if per >= 2 else member[0]
     return _desc_order(gscore, np.arange(n_group))[:topk_group]
 

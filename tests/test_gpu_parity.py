@@ -72,6 +72,43 @@ def test_router_topk_from_logits_bitexact(cfg, ties):
         assert abs(float(host(aux)[0]) - want) <= 1e-5 * want
 
 
+NONFINITE_CASES = [ROUTER_CASES[i] for i in (0, 1, 2, 4, 5)]
+
+
+@pytest.mark.parametrize("cfg", NONFINITE_CASES, ids=lambda c: c.name)
+def test_router_topk_nonfinite_logits(cfg):
+    """Caller logits holding NaN and infinities: NaN keys rank after every
+    number and NaN-holding groups after every numeric group, so the ids stay
+    k distinct eligible experts, equal to the oracle's bit for bit."""
+    print(f"case router nonfinite {cfg.name}", flush=True)
+    logits = mi.fixed_logits(cfg.T, cfg.E, seed=9, std=2.0, ties=True).numpy()
+    pick = np.random.default_rng(3).random(logits.shape)
+    logits[pick < 0.15] = np.nan
+    logits[(pick >= 0.15) & (pick < 0.2)] = np.inf
+    logits[(pick >= 0.2) & (pick < 0.26)] = -np.inf
+    logits[0] = np.nan
+    logits[1] = -np.inf
+    logits[2] = np.inf
+    bias = mi.make_inputs(cfg, seed=5, experts=False)["bias"]
+    o_keys = O.selection_keys(logits, cfg, None if bias is None else bias.numpy())
+    o_idx = O.select_topk(o_keys, cfg)
+    c = shape_of(cfg).cfg()
+    dev = "cuda"
+    L = torch.from_numpy(logits).to(dev)
+    idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
+    gates = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev)
+    cnt = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(abi.moe_workspace_size(c), dtype=torch.uint8, device=dev)
+    abi.moe_router_topk(c, None, None, None if bias is None else bias.to(dev), L, idx, gates, cnt,
+                        aux if cfg.aux_coeff else None, ws)
+    torch.cuda.synchronize()
+    got = host(idx)
+    assert got.min() >= 0 and got.max() < cfg.E
+    assert np.array_equal(got, o_idx)
+    assert np.array_equal(host(cnt), O.expert_counts(o_idx, cfg.E))
+
+
 def test_router_zero_tokens_writes_zero_counts_and_aux():
     """T = 0: every count is 0 and the aux loss is exactly 0 (the per-block
     partial sums are empty)."""

@@ -201,6 +201,47 @@ def test_group_limited_brute_force(ties):
         assert tuple(sorted(idx[t].tolist())) == _brute_topk(keys[t], cand, cfg.k)
 
 
+def _rank(v, i):
+    """sort key of (value, id) under R27: numbers descending (infinities
+    included), then NaN, ties by id"""
+    return (1, 0.0, i) if np.isnan(v) else (0, -float(v), i)
+
+
+def test_nonfinite_keys_rank_last_and_choices_stay_valid():
+    """R27: NaN keys rank after every number, a NaN-holding group after every
+    numeric group; the choices are always k distinct eligible ids."""
+    rng = np.random.default_rng(11)
+    for E, k, n_group, topk_group in [(8, 3, 1, 1), (16, 3, 4, 2), (16, 5, 16, 8), (12, 12, 1, 1)]:
+        cfg = mi.MoEConfig("nf", T=200, d=8, E=E, k=k, f=8, score="sigmoid", n_group=n_group,
+                           topk_group=topk_group)
+        keys = np.round(rng.standard_normal((cfg.T, E)) * 8) / 8
+        pick = rng.random((cfg.T, E))
+        keys[pick < 0.15] = np.nan
+        keys[(pick >= 0.15) & (pick < 0.22)] = np.inf
+        keys[(pick >= 0.22) & (pick < 0.30)] = -np.inf
+        keys[0] = np.nan                                  # a row of NaN only
+        keys[1] = -np.inf                                 # a row of -inf only
+        keys = keys.astype(np.float32)
+        idx = O.select_topk(keys, cfg)
+        per = E // n_group
+        for t in range(cfg.T):
+            if n_group > 1:
+                gs = []
+                for g in range(n_group):
+                    mem = sorted(keys[t, g * per:(g + 1) * per].tolist(), reverse=True)
+                    bad = any(np.isnan(m) for m in mem)
+                    gs.append(np.nan if bad else (mem[0] + mem[1] if per >= 2 else mem[0]))
+                groups = sorted(range(n_group), key=lambda g: _rank(gs[g], g))[:topk_group]
+                cand = [e for g in groups for e in range(g * per, (g + 1) * per)]
+            else:
+                cand = list(range(E))
+            want = sorted(cand, key=lambda e: _rank(keys[t, e], e))[:k]
+            assert idx[t].tolist() == want, t
+            assert len(set(want)) == k and all(0 <= e < E for e in want)
+        assert idx[0].tolist() == (list(range(k)) if n_group == 1 else idx[0].tolist())
+        assert idx[1].tolist() == (list(range(k)) if n_group == 1 else idx[1].tolist())
+
+
 def test_sigmoid_score_rounding_and_bias_is_selection_only():
     from scipy.special import expit
     l = mi.fixed_logits(64, 32, seed=9, std=3.0).numpy()
