@@ -323,7 +323,7 @@ moe_status gemm_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* of
   const bool rc = recompute(c);
   int* prefix = (int*)ws;
   if (rows > 0) {
-    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E, true), prefix, st));
+    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E, false), prefix, st));
     LAUNCH_NAMED("gemm_swiglu_fwd", gemm_swiglu_fwd<T>(x_perm, off, prefix, E, w13, hu, act, rows, d, f,
                                                        fold(c) ? row_gates : nullptr, rc, st));
     LAUNCH_NAMED("gemm_down_fwd", gemm_down_fwd<T>(act, off, prefix, E, w2, y_perm, rows, d, f, st));
@@ -353,7 +353,10 @@ moe_status gemm_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_pe
   void* act_rec = recompute(c) ? (char*)ws + X.act : nullptr;
   float* dg_part = fold(c) ? (float*)((char*)ws + X.dg) : nullptr;
   const float* rg = fold(c) ? row_gates : nullptr;
-  if (rows > 0) LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, gemm_tile_rows(bf, rows, E, false), prefix, st));
+  // the SwiGLU-backward product and the gate/up data gradient may take
+  // different tile heights: the prefix is built again between them if so
+  const int bm_swiglu_bwd = gemm_tile_rows(bf, rows, E, true), bm_dgrad = gemm_tile_rows(bf, rows, E, false);
+  if (rows > 0) LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, bm_swiglu_bwd, prefix, st));
   if (rows > 0)
     LAUNCH_NAMED("gemm_down_dgrad_swiglu_bwd", gemm_down_dgrad_swiglu_bwd<T>(dy_perm, off, prefix, E, w2, hu, dhu, rows, d, f,
                                                                              rg, dg_part, act_rec, st));
@@ -361,6 +364,8 @@ moe_status gemm_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_pe
     LAUNCH_NAMED("gate_grad_sum", launch_gate_grad_sum(dg_part, gemm_dg_parts(bf, f), row_id_map, rows, d_gates, st));
   // weight gradients cover every expert (empty experts get zeros)
   LAUNCH_NAMED("gemm_wgrad_down", gemm_wgrad<T>(dy_perm, d, act_rec ? act_rec : act, f, off, E, 0, dw2, 1, st));
+  if (rows > 0 && bm_dgrad != bm_swiglu_bwd)
+    LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, bm_dgrad, prefix, st));
   if (rows > 0) LAUNCH_NAMED("gemm_gateup_dgrad", gemm_gateup_dgrad<T>(dhu, off, prefix, E, w13, dx_perm, false, rows, d, f, st));
   LAUNCH_NAMED("gemm_wgrad_gateup", gemm_wgrad<T>(dhu, 2 * f, x_perm, d, off, E, 0, dw13, 0, st));
   if (c->f_shared > 0) {

@@ -202,19 +202,19 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
 
 // Tile rows of the ragged-row schedule.  The device tile prefix is built with
 // this value and the kernel resolves its tiles with its own BM: they must agree.
-// (the forward and data-gradient classes take the same override, and their
-// defaults both use 128-row tiles, so one prefix serves both)
 // Forward products whose experts hold many rows (at least 512 on average: MFMA-bound) run the
 // ring on 256x256 tiles, 2x4 waves of 128x64, two stages: half the operand traffic per output
 // and a larger wave tile (the Qwen3 and Mixtral gate/up forwards ran 10% faster than on
 // 128x256); with fewer rows the 256-row tiles would be mostly padding.
 static bool big_tiles(int64_t rows, int G) { return G > 0 && rows >= (int64_t)512 * G; }
-// The data gradients take the 256x256 tiles under the same rule (gate/up dgrad
-// on one box: Qwen3 2.06 -> 1.86 ms, Mixtral 2.54 -> 2.41, the EP share 2.23 ->
-// 1.87).
-int gemm_tile_rows(bool bf16, int64_t rows, int G, bool /*forward*/) {
+// The gate/up data gradient takes the 256x256 tiles under the same rule (on one
+// box: Qwen3 2.06 -> 1.86 ms, Mixtral 2.54 -> 2.41, the EP share 2.23 -> 1.87).
+// The SwiGLU-backward product (swiglu_bwd = true) always runs on 128x256 tiles:
+// its epilogue reads H and U beside the accumulators and spilled at 256x256
+// (Qwen3 1.67 ms there, 1.36 ms on 128x256).
+int gemm_tile_rows(bool bf16, int64_t rows, int G, bool swiglu_bwd) {
   if (!bf16) return 16;
-  return big_tiles(rows, G) ? 256 : 128;
+  return !swiglu_bwd && big_tiles(rows, G) ? 256 : 128;
 }
 
 template <class T, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi>
@@ -237,9 +237,12 @@ static hipError_t run_gemm(const GemmArgs& a, const typename Epi::P& ep, int row
                               ((n_logical + (Epi::kPaired ? 127 : 255)) / (Epi::kPaired ? 128 : 256));
     const bool dense_big = a.M >= 1024 && n_logical >= 1024 && big_count >= device_cus();
     if constexpr (MODE != RAGGED_K) {
-      const bool big = MODE == RAGGED_M ? big_tiles(rows_total, a.G) : dense_big;
-      if (big)
-        return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+      // (not the SwiGLU-backward epilogue: see gemm_tile_rows)
+      if constexpr (!Epi::kRowDot) {
+        const bool big = MODE == RAGGED_M ? big_tiles(rows_total, a.G) : dense_big;
+        if (big)
+          return launch_mfma<256, 256, 2, 4, 2, LA, LB, MODE, Epi>(a, ep, n_logical, rows_total, st, persistent);
+      }
     } else {
       // a weight gradient over one dense contraction of many rows (the
       // shared expert's, K = tokens) is MFMA-bound: 256x256 tiles, one per

@@ -73,7 +73,7 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
 hipError_t launch_tile_prefix(const int* offsets, int G, int BM, int* prefix, hipStream_t st);
 // rows of the ragged tiles of the forward (forward = true) or the data-gradient
 // products; the device tile prefix must be built with it
-int gemm_tile_rows(bool bf16, int64_t rows, int G, bool forward);
+int gemm_tile_rows(bool bf16, int64_t rows, int G, bool swiglu_bwd);
 template <class T>
 hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int T_, int E, int d,
                               hipStream_t st);
