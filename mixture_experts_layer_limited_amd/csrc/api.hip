@@ -264,8 +264,16 @@ MxWs mx_ws(const moe_cfg* c) {
   return w;
 }
 
+// router workspace: per-block counts and column sums, then the split-K parts
+// of the logits GEMM
+size_t router_parts_bytes(const moe_cfg* c) {
+  int kchunk;
+  const int parts = router_logit_parts(c->dtype != MOE_F32, c->T, (int)c->E, (int)c->d, &kchunk);
+  return parts > 1 ? align256((size_t)parts * c->T * c->E * 4) : 0;
+}
+
 size_t ws_bytes_for(const moe_cfg* c) {
-  size_t router = 2 * align256((size_t)router_blocks(c->T) * c->E * 4);
+  size_t router = 2 * align256((size_t)router_blocks(c->T) * c->E * 4) + router_parts_bytes(c);
   size_t perm = align256((size_t)ranges(c->T) * c->E * 4);
   const size_t prefix = align256((size_t)(c->E + 2) * 4);
   size_t gemm = prefix + gemm_extra(c, prefix, c->dtype != MOE_F32).bytes;
@@ -305,7 +313,9 @@ moe_status router_topk_impl(const moe_cfg* c, const void* x, const void* w_route
   char* w = (char*)ws;
   int* cnt_part = (int*)w;
   float* colsum_part = (float*)(w + align256((size_t)nblk * c->E * 4));
-  if (x) LAUNCH_NAMED("gemm_router_logits", gemm_router_logits<T>(x, w_router, logits, (int)c->T, (int)c->E, (int)c->d, st));
+  float* logit_parts = (float*)(w + 2 * align256((size_t)nblk * c->E * 4));
+  if (x) LAUNCH_NAMED("gemm_router_logits", gemm_router_logits<T>(x, w_router, logits, (int)c->T, (int)c->E, (int)c->d,
+                                                                  logit_parts, st));
   const bool want_colsum = c->aux_coeff != 0.0f;
   LAUNCH_NAMED("router_topk", launch_router_topk(logits, bias, p, idx, gates, cnt_part, want_colsum ? colsum_part : nullptr, st));
   LAUNCH_NAMED("router_finalize", launch_router_finalize(cnt_part, want_colsum ? colsum_part : nullptr, nblk, p, counts, st));

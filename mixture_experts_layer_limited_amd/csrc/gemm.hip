@@ -116,7 +116,7 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
   int64_t tiles;                          // upper bound of the logical tiles
   if (MODE == RAGGED_M) tiles = (int64_t)((rows_total + BM - 1) / BM + a.G) * NT;
   else if (MODE == RAGGED_K) tiles = (int64_t)a.G * MT * NT;
-  else tiles = (int64_t)MT * NT;
+  else tiles = (int64_t)MT * NT * (a.kchunk > 0 ? (a.K + a.kchunk - 1) / a.kchunk : 1);
   if (tiles <= 0) return hipSuccess;
   constexpr int kLdsPerCU = 160 * 1024;
   const int per_cu = kLdsPerCU / C::LDS_BYTES > 0 ? kLdsPerCU / C::LDS_BYTES : 1;
@@ -279,14 +279,53 @@ __global__ __launch_bounds__(256) void zero_empty_groups_kernel(const int* __res
     o[i] = z;
 }
 
+// The router logits have few output tiles (T / 128 x E / 256: 32 for 4096
+// tokens and 256 experts) and a long contraction (d): split along d into
+// parts that fill the CUs (at most 8, each at least 512 deep), each part's
+// fp32 result in a block of its own, summed in part order afterwards (no
+// atomics: the sum is the same on every run).
+int router_logit_parts(bool bf16, int64_t T, int E, int d, int* kchunk) {
+  *kchunk = d;
+  if (!bf16 || d < 1024 || T <= 0) return 1;
+  const int64_t tiles = ((T + 127) / 128) * ((E + 255) / 256);
+  int64_t s = (256 + tiles - 1) / tiles;
+  if (s > 8) s = 8;
+  if (s > d / 512) s = d / 512;
+  if (s <= 1) return 1;
+  const int kc = (int)(((d + s - 1) / s + 63) / 64 * 64);
+  *kchunk = kc;
+  return (d + kc - 1) / kc;
+}
+
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part, int parts, int64_t n,
+                                                        float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float s = part[i];
+    for (int p = 1; p < parts; ++p) s += part[p * n + i];
+    out[i] = s;
+  }
+}
+
 template <class T>
-hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int T_, int E, int d,
+hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int T_, int E, int d, float* part,
                               hipStream_t st) {
   GemmArgs a{};
   a.A = x; a.lda = d; a.B = w_r; a.ldb = d; a.M = T_; a.N = E; a.K = d;
   a.b_next = E; a.b_kend = d; a.G = 1;
-  EpiStoreF32::P ep{logits, E, 0, T_, E};
-  return run_gemm<T, KC, KC, DENSE, EpiStoreF32>(a, ep, T_, st);
+  int kchunk;
+  const int parts = router_logit_parts(sizeof(T) == 2, T_, E, d, &kchunk);
+  if (parts <= 1) {
+    EpiStoreF32::P ep{logits, E, 0, T_, E};
+    return run_gemm<T, KC, KC, DENSE, EpiStoreF32>(a, ep, T_, st);
+  }
+  a.kchunk = kchunk;
+  const int64_t n = (int64_t)T_ * E;
+  EpiStoreF32::P ep{part, E, n, T_, E};
+  if (hipError_t e = run_gemm<T, KC, KC, DENSE, EpiStoreF32>(a, ep, T_, st); e != hipSuccess) return e;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  sum_parts_kernel<<<(unsigned)blocks, 256, 0, st>>>(part, parts, n, logits);
+  return hipGetLastError();
 }
 
 template <class T>
@@ -453,7 +492,7 @@ hipError_t gemm_router_dgrad(const void* dl, int Ep, int E, const void* w_r, int
 
 #define MOE_INSTANTIATE(T)                                                                       \
   template hipError_t gemm_router_logits<T>(const void*, const void*, float*, int, int, int,     \
-                                            hipStream_t);                                        \
+                                            float*, hipStream_t);                                \
   template hipError_t gemm_swiglu_fwd<T>(const void*, const int*, const int*, int, const void*,  \
                                          void*, void*, int, int, int, const float*, bool,        \
                                          hipStream_t);                                           \

@@ -59,6 +59,9 @@ struct GemmArgs {
   const int* tile_prefix;  // RAGGED_M: [G+1] cumulative m-tiles per group
   int G;
   int k_skip;              // RAGGED_K: groups with at most this many rows are left to another kernel
+  int kchunk;              // DENSE split-K (bf16 kernels): output tile (m, n) is computed ceil(K / kchunk)
+                           // times, part s over K range [s kchunk, (s+1) kchunk) into output block g = s
+                           // (kchunk a multiple of 64); 0: no split
 };
 
 // Persistent schedule over XCDs.  Workgroups are dispatched round-robin over
@@ -171,8 +174,12 @@ template <GemmMode MODE, int BM>
 __device__ __forceinline__ void resolve_tile(const GemmArgs& a, const int* off, const int* pre, int L, int NT,
                                              int MT, TileCoord& c) {
   if (MODE == DENSE) {
-    int mt = L % MT, nt = L / MT;
-    c.g = 0; c.m0 = mt * BM; c.m_end = a.M; c.n0 = nt; c.k_begin = 0; c.k_end = a.K;
+    // split-K: part s of every output tile, then part s + 1
+    const int s = L / (MT * NT), r = L % (MT * NT);
+    int mt = r % MT, nt = r / MT;
+    c.g = s; c.m0 = mt * BM; c.m_end = a.M; c.n0 = nt;
+    c.k_begin = a.kchunk > 0 ? s * a.kchunk : 0;
+    c.k_end = a.kchunk > 0 ? min(a.K, c.k_begin + a.kchunk) : a.K;
   } else if (MODE == RAGGED_M) {
     // expert-major order: all tiles of group g, n-tile major, m-tile fastest
     int lo = 0, hi = a.G;  // find g with pre[g]*NT <= L < pre[g+1]*NT
@@ -266,7 +273,7 @@ template <GemmMode MODE>
 __device__ __forceinline__ int total_tiles(const GemmArgs& a, int NT, int MT) {
   if (MODE == RAGGED_M) return a.tile_prefix[a.G] * NT;
   if (MODE == RAGGED_K) return a.G * MT * NT;
-  return MT * NT;
+  return MT * NT * (a.kchunk > 0 ? (a.K + a.kchunk - 1) / a.kchunk : 1);
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).

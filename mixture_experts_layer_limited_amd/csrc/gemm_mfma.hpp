@@ -361,8 +361,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
       rb_bytes = (uint32_t)((int64_t)max(b_kend - c.k_begin, 0) * a.ldb * 2);
       pb.plan_mc(a.ldb, nt * BN);
     }
-    soa = 0;
-    sob = 0;
+    // K-contiguous operands start at the tile's first K (a split-K part's;
+    // row-contiguous ones have it in their base)
+    soa = LA == KC ? (uint32_t)(c.k_begin * 2) : 0u;
+    sob = LB == KC ? (uint32_t)(c.k_begin * 2) : 0u;
     if constexpr (MX) {
       // lane q = wave*64 + lane fetches the scale word of tile row q (A) and
       // of B row q (its weight row), or nothing (an offset outside the range)

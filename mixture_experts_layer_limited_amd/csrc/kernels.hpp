@@ -71,11 +71,17 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
 
 // gemm.hip
 hipError_t launch_tile_prefix(const int* offsets, int G, int BM, int* prefix, hipStream_t st);
-// rows of the ragged tiles of the forward (forward = true) or the data-gradient
-// products; the device tile prefix must be built with it
+// rows of the ragged tiles of the forward and gate/up data-gradient products
+// (swiglu_bwd = false) or of the SwiGLU-backward product; the device tile
+// prefix must be built with it
 int gemm_tile_rows(bool bf16, int64_t rows, int G, bool swiglu_bwd);
+// Split-K parts of the router logits GEMM (1: none) and the K range of each
+// (*kchunk, a multiple of 64); the parts need [parts][T][E] fp32 of workspace.
+int router_logit_parts(bool bf16, int64_t T, int E, int d, int* kchunk);
+// logits = x w_r^T; with parts > 1 (router_logit_parts) the parts go to `part`
+// and are summed in part order into logits
 template <class T>
-hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int T_, int E, int d,
+hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int T_, int E, int d, float* part,
                               hipStream_t st);
 // row_gates: folded gates (act = g silu(H) U) or NULL; from_stored: act from H, U as stored
 template <class T>

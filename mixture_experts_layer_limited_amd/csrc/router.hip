@@ -6,6 +6,7 @@
 // Selection is an iterated wave-wide argmax on the key (ties -> lower id),
 // done with cross-lane shuffles, so equal fp32 inputs give the same choice as
 // any implementation of the same ordering rule.
+#include <limits.h>
 #include <math.h>
 
 #include "common.hpp"
@@ -19,23 +20,54 @@ constexpr int kNI = kMaxExperts / kWave;   // values per lane (E <= 256)
 constexpr int kRouterWaves = 4;
 
 // Key order: larger first, equal keys by lower id, and a NaN key below every
-// number (-inf included).  The search starts from (NaN, INT_MAX), which every
-// candidate beats, so a selection always returns a candidate's id, whatever
-// values the logits hold.
-__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
-  const bool na = ka != ka, nb = kb != kb;
-  if (na || nb) return nb && (!na || ia < ib);
+// number (-inf included).  Keys are compared as integers that keep the order
+// of the floats (negative ones with their magnitude bits flipped, -0 as +0)
+// with NaN mapped to INT_MIN.  The search starts from (INT_MIN, INT_MAX),
+// which every candidate beats, so a selection always returns a candidate's
+// id, whatever values the logits hold.
+__device__ __forceinline__ int order_key(float f) {
+  if (f != f) return INT_MIN;
+  const int b = __float_as_int(f == 0.0f ? 0.0f : f);
+  return b >= 0 ? b : b ^ 0x7fffffff;
+}
+__device__ __forceinline__ bool better(int ka, int ia, int kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 constexpr int kNoId = 0x7fffffff;
 
 // wave-wide argmax of (key desc, id asc); every lane returns the winner
-__device__ __forceinline__ void wave_argmax(float& k, int& i) {
+__device__ __forceinline__ void wave_argmax(int& k, int& i) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    float ok = __shfl_xor(k, o, kWave);
+    int ok = __shfl_xor(k, o, kWave);
     int oi = __shfl_xor(i, o, kWave);
     if (better(ok, oi, k, i)) { k = ok; i = oi; }
+  }
+}
+
+// Centered sums without cancellation.  The router gradients take the form
+// w_j (a_j - sum_i w_i a_i) with weights summing to one; when one weight is
+// close to 1 the bracket of that term is the difference of two nearly equal
+// numbers in fp32.  Written as w_j sum_i w_i (a_j - a_i) (over the k choices,
+// pairwise) or, over all E experts, with the largest weight's term split off
+// (its 1 - w from the sum of the other weights), every term keeps its
+// relative precision.
+
+// k choices, choice j in lane j % 64, slot j / 64: out_j = sum_i w_i (a_j - a_i)
+__device__ __forceinline__ void pairwise_centered(const float* w, const float* a, int k, float* out) {
+#pragma unroll
+  for (int s = 0; s < kNI; ++s) out[s] = 0.0f;
+  for (int i = 0; i < k; ++i) {
+    const int src = i & 63, slot = i >> 6;
+    float wi = 0.0f, ai = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kNI; ++s)
+      if (s == slot) {
+        wi = __shfl(w[s], src, kWave);
+        ai = __shfl(a[s], src, kWave);
+      }
+#pragma unroll
+    for (int s = 0; s < kNI; ++s) out[s] += wi * (a[s] - ai);
   }
 }
 
@@ -115,9 +147,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     // group-limited routing: score groups by the sum of their two best keys
     // (force-balanced routing assigns experts without looking at the keys)
     if (p.n_group > 1 && !p.balanced) {
-      float gs[kNI];
+      int gs[kNI];
 #pragma unroll
-      for (int i = 0; i < kNI; ++i) gs[i] = -INFINITY;
+      for (int i = 0; i < kNI; ++i) gs[i] = INT_MIN;
       for (int g = 0; g < p.n_group; ++g) {
         float t1 = -INFINITY, t2 = -INFINITY;
         bool has_nan = false;
@@ -140,16 +172,17 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
           t2 = fmaxf(lo, fmaxf(t2, o2));
           t1 = hi;
         }
-        float score = group_nan ? __builtin_nanf("") : per >= 2 ? t1 + t2 : t1;
+        const float score = group_nan ? __builtin_nanf("") : per >= 2 ? t1 + t2 : t1;
+        const int okey = order_key(score);
 #pragma unroll
         for (int i = 0; i < kNI; ++i)
-          if (lane + 64 * i == g) gs[i] = score;
+          if (lane + 64 * i == g) gs[i] = okey;
       }
       // keep topk_group groups (score desc, group id asc)
       uint64_t gm[kNI] = {0, 0, 0, 0};
       bool gtaken[kNI] = {false, false, false, false};
       for (int r = 0; r < p.topk_group; ++r) {
-        float bk = __builtin_nanf("");
+        int bk = INT_MIN;
         int bi = kNoId;
 #pragma unroll
         for (int i = 0; i < kNI; ++i) {
@@ -177,6 +210,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       }
     }
 
+    int okey[kNI];
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) okey[i] = order_key(key[i]);
     // top-k: k rounds of a wave argmax; lane j%64 keeps choice j.  Force-
     // balanced routing: choice j is expert (t k + j) mod E (uniform over the wave)
     int my_id[kNI];
@@ -188,12 +224,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       if (p.balanced) {
         bi = (int)(((int64_t)t * k + j) % E);
       } else {
-        float bk = __builtin_nanf("");
+        int bk = INT_MIN;
         bi = kNoId;
 #pragma unroll
         for (int i = 0; i < kNI; ++i) {
           int e = lane + 64 * i;
-          if (elig[i] && !taken[i] && better(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
+          if (elig[i] && !taken[i] && better(okey[i], e, bk, bi)) { bk = okey[i]; bi = e; }
         }
         wave_argmax(bk, bi);
       }
@@ -376,21 +412,50 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     pr[i] = 0.0f;
   }
   const bool need_p = softmax && (!p.renorm || p.aux_coeff != 0.0f);
+  // full softmax p; dom = the lowest expert id of largest logit, rest = 1 - p_dom
+  // summed from the other experts' terms
+  int dom = 0;
+  float rest = 0.0f;
   if (need_p) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kNI; ++i) mx = fmaxf(mx, v[i]);
     mx = wave_max(mx);
-    float z = 0.0f;
+    int cand = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kNI; ++i)
+      if (lane + 64 * i < E && v[i] == mx && lane + 64 * i < cand) cand = lane + 64 * i;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o, kWave));
+    dom = cand;
+    float z = 0.0f, zo = 0.0f;
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       pr[i] = (lane + 64 * i < E) ? expf(v[i] - mx) : 0.0f;
       z += pr[i];
+      if (lane + 64 * i != dom) zo += pr[i];
     }
     z = wave_sum(z);
+    zo = wave_sum(zo);
 #pragma unroll
     for (int i = 0; i < kNI; ++i) pr[i] /= z;
+    rest = zo / z;
   }
+  // over all E experts: out_e = p_e (a_e - sum_i p_i a_i), the dominant
+  // expert's term as p_dom (a_dom rest - sum_{i != dom} p_i a_i)
+  auto centered_all = [&](const float* a, float* out) {
+    float io = 0.0f, pa_dom = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+      if (lane + 64 * i != dom) io += pr[i] * a[i];
+      else pa_dom = pr[i] * a[i];
+    }
+    io = wave_sum(io);
+    const float inner = io + wave_sum(pa_dom);
+#pragma unroll
+    for (int i = 0; i < kNI; ++i)
+      out[i] = lane + 64 * i == dom ? pr[i] * (a[i] * rest - io) : pr[i] * (a[i] - inner);
+  };
   // choice j lives in lane j%64, slot j/64
   int sid[kNI];
   float sg[kNI], sdg[kNI], ss[kNI];
@@ -405,12 +470,14 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   }
   float dsel[kNI];
   if (softmax && p.renorm) {
-    float inner = 0.0f;
+    // g_j = scale q_j, q the softmax over the chosen logits:
+    // dl_j = scale q_j sum_i q_i (dg_j - dg_i)
+    float q[kNI], cen[kNI];
 #pragma unroll
-    for (int i = 0; i < kNI; ++i) inner += (sg[i] / p.scale) * sdg[i];
-    inner = wave_sum(inner);
+    for (int i = 0; i < kNI; ++i) q[i] = sg[i] / p.scale;
+    pairwise_centered(q, sdg, k, cen);
 #pragma unroll
-    for (int i = 0; i < kNI; ++i) dsel[i] = p.scale * (sg[i] / p.scale) * (sdg[i] - inner);
+    for (int i = 0; i < kNI; ++i) dsel[i] = p.scale * q[i] * cen[i];
   } else if (!softmax) {
     // recompute the selected sigmoid scores from the logits
 #pragma unroll
@@ -419,14 +486,18 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
       ss[i] = 0.0f;
       if (j < k) ss[i] = sigmoid_score(logits[(int64_t)t * E + sid[i]]);
     }
-    float S = 0.0f, inner = 0.0f;
+    // renormalised: g_j = scale s_j / S, dL/ds_j = (scale / S) sum_i (s_i / S) (dg_j - dg_i)
+    float S = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kNI; ++i) { S += ss[i]; inner += sdg[i] * ss[i]; }
+    for (int i = 0; i < kNI; ++i) S += ss[i];
     S = wave_sum(S);
-    inner = wave_sum(inner);
+    float w[kNI], cen[kNI];
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) w[i] = ss[i] / S;
+    if (p.renorm) pairwise_centered(w, sdg, k, cen);
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
-      float ds = p.renorm ? (p.scale / S) * (sdg[i] - inner / S) : p.scale * sdg[i];
+      float ds = p.renorm ? (p.scale / S) * cen[i] : p.scale * sdg[i];
       dsel[i] = ds * ss[i] * (1.0f - ss[i]);
     }
   } else {
@@ -452,27 +523,19 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     for (int i = 0; i < kNI; ++i)
       if (lane + 64 * i == e) { dl[i] += val; dgf[i] += dgv * p.scale; }
   }
-  if (softmax && !p.renorm) {
-    float inner = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kNI; ++i) inner += pr[i] * dgf[i];
-    inner = wave_sum(inner);
-#pragma unroll
-    for (int i = 0; i < kNI; ++i) dl[i] = pr[i] * (dgf[i] - inner);
-  }
+  if (softmax && !p.renorm) centered_all(dgf, dl);
   if (softmax && p.aux_coeff != 0.0f) {
     float a[kNI];
-    float inner = 0.0f;
     const float norm = p.aux_coeff * (float)E / ((float)p.T * (float)k * (float)p.T);
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       int e = lane + 64 * i;
       a[i] = e < E ? norm * (float)counts[e] : 0.0f;
-      inner += pr[i] * a[i];
     }
-    inner = wave_sum(inner);
+    float ca[kNI];
+    centered_all(a, ca);
 #pragma unroll
-    for (int i = 0; i < kNI; ++i) dl[i] += d_aux * pr[i] * (a[i] - inner);
+    for (int i = 0; i < kNI; ++i) dl[i] += d_aux * ca[i];
   }
 #pragma unroll
   for (int i = 0; i < kNI; ++i) {

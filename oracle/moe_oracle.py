@@ -640,7 +640,12 @@ def router_backward(logits, idx, gates, d_gates, counts, cfg, d_aux: float = 1.0
     """d loss / d logits, routing held fixed (top-k is piecewise constant and the
     selection bias receives no gradient).
 
-    softmax + renorm:  dl_m = g_m (dg_m - sum_j g_j dg_j) on the selection
+    softmax + renorm:  dl_m = q_m (dg_m - sum_j q_j dg_j) on the selection, q the
+                       softmax of the selected logits (the gates before the
+                       scale), evaluated here from the logits: the stored fp32
+                       gates sum to 1 only to fp32 precision, and with one gate
+                       near 1 the centred form turns that into an error of the
+                       size of the result
     softmax, no renorm: dl = p * (dg_full - sum_e p_e dg_full_e)
     aux (softmax):     dl[t,e] += d_aux * p[t,e] * (a_e - sum_e' p[t,e'] a_e'),
                        a_e = coeff * E * f_e / T
@@ -651,13 +656,15 @@ def router_backward(logits, idx, gates, d_gates, counts, cfg, d_aux: float = 1.0
     T, E = l.shape
     ii = idx.astype(np.int64)
     dg = np.asarray(d_gates, F64)
-    g = np.asarray(gates, F64) / cfg.scale          # unscaled gate values
     dgs = dg * cfg.scale                            # gradient w.r.t. unscaled gates
     dl = np.zeros((T, E), F64)
     if cfg.score == "softmax":
         if cfg.renorm:
-            inner = np.sum(g * dgs, axis=1, keepdims=True)
-            np.put_along_axis(dl, ii, g * (dgs - inner), axis=1)
+            sl = np.take_along_axis(l, ii, axis=1)
+            q = np.exp(sl - sl.max(axis=1, keepdims=True)) if T else sl
+            q = q / q.sum(axis=1, keepdims=True) if T else q
+            inner = np.sum(q * dgs, axis=1, keepdims=True)
+            np.put_along_axis(dl, ii, q * (dgs - inner), axis=1)
         else:
             p = softmax_probs(l)
             full = np.zeros((T, E), F64)

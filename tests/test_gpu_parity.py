@@ -210,6 +210,11 @@ LAYER_CASES = [
          fold_gates=True, recompute_act=True),
     _cfg("bf16_fold_one_token_bwd", T=1, d=128, E=8, k=2, f=64, backward=True, fold_gates=True,
          recompute_act=True),
+    # d >= 1024: the router logits run split-K (3 and 2 parts of 512) and
+    # sum their parts in order
+    _cfg("bf16_router_split_k_bwd", T=200, d=1536, E=64, k=4, f=64, score="sigmoid", n_group=8, topk_group=4,
+         scale=2.5, bias="normal", bias_std=0.01, backward=True),
+    _cfg("bf16_router_split_k_one_token_bwd", T=1, d=1024, E=16, k=2, f=64, aux_coeff=1e-3, backward=True),
     _cfg("bf16_balanced_sigmoid_shared_bwd", T=256, d=256, E=32, k=8, f=128, f_shared=128, score="sigmoid",
          n_group=8, topk_group=4, scale=2.5, bias="normal", bias_std=0.01, backward=True,
          force_balanced=True),

@@ -361,6 +361,30 @@ def test_router_backward_against_autograd_of_gates():
         assert np.allclose(dl, tl.grad.numpy(), rtol=1e-12, atol=1e-13), cfg.name
 
 
+def test_router_backward_peaked_softmax_fp32_gates():
+    """With one selected logit far above the others the renormalised gates
+    stored in fp32 round to (1, ~1e-8, ...) and no longer sum to 1; the gate
+    derivative must still be that of the gate function (autograd in float64
+    from the logits), not of the rounded values."""
+    rng = np.random.default_rng(13)
+    T, E, k = 6, 16, 3
+    logits = rng.standard_normal((T, E))
+    logits[np.arange(T), rng.integers(0, E, T)] += 18.0 + np.arange(T)
+    dg = rng.standard_normal((T, k))
+    cfg = mi.MoEConfig("peak", T=T, d=4, E=E, k=k, f=4, scale=2.5)
+    idx = O.select_topk(O.selection_keys(logits, cfg, exact=True), cfg)
+    gates32 = O.gates_from_selection(logits.astype(np.float32), idx, cfg).astype(np.float32)
+    assert np.any(gates32.astype(np.float64).sum(1) != 2.5)     # the rounded gates do not sum to the scale
+    dl = O.router_backward(logits, idx, gates32, dg, None, cfg)
+    tl = torch.from_numpy(logits).requires_grad_(True)
+    sel = torch.gather(torch.softmax(tl, dim=1), 1, torch.from_numpy(idx.astype(np.int64)))
+    (2.5 * sel / sel.sum(1, keepdim=True) * torch.from_numpy(dg)).sum().backward()
+    want = tl.grad.numpy()
+    # float64 itself keeps ~1e-16 / |result| of relative precision in either
+    # form (results down to ~1e-11 here); rounding the gates to fp32 would be off by ~1e-8 absolute
+    assert np.allclose(dl, want, rtol=1e-5, atol=1e-22)     # (autograd leaves ~1e-26 off the selection)
+
+
 # --------------------------------------------------------------------------
 # P9: aux-loss closed forms
 # --------------------------------------------------------------------------
