@@ -277,7 +277,10 @@ size_t ws_bytes_for(const moe_cfg* c) {
   size_t perm = align256((size_t)ranges(c->T) * c->E * 4);
   const size_t prefix = align256((size_t)(c->E + 2) * 4);
   size_t gemm = prefix + gemm_extra(c, prefix, c->dtype != MOE_F32).bytes;
-  size_t rbwd = align256((size_t)c->T * pad64(c->E) * elt(c));
+  int wchunk;
+  const int wparts = router_wgrad_parts(c->dtype != MOE_F32, c->T, (int)c->E, (int)c->d, &wchunk);
+  size_t rbwd = align256((size_t)c->T * pad64(c->E) * elt(c)) +
+                (wparts > 1 ? align256((size_t)wparts * c->E * c->d * 4) : 0);
   size_t m = router;
   if (perm > m) m = perm;
   if (gemm > m) m = gemm;
@@ -404,7 +407,8 @@ moe_status router_bwd_impl(const moe_cfg* c, const void* x, const void* w_router
   T* dl_store = bf ? (T*)ws : nullptr;
   LAUNCH_NAMED("router_bwd", launch_router_bwd<T>(logits, idx, gates, d_gates, counts, p, d_aux, d_logits, dl_store, Ep, st));
   const void* dl = bf ? (const void*)dl_store : (const void*)d_logits;
-  LAUNCH_NAMED("gemm_router_wgrad", gemm_router_wgrad<T>(dl, Ep, E, x, T_, d, dw_router, st));
+  float* wparts = (float*)((char*)ws + align256((size_t)T_ * Ep * sizeof(T)));
+  LAUNCH_NAMED("gemm_router_wgrad", gemm_router_wgrad<T>(dl, Ep, E, x, T_, d, dw_router, wparts, st));
   if (T_ > 0) LAUNCH_NAMED("gemm_router_dgrad", gemm_router_dgrad<T>(dl, Ep, E, w_router, T_, d, dx_partial, st));
   return ok();
 }

@@ -297,13 +297,24 @@ int router_logit_parts(bool bf16, int64_t T, int E, int d, int* kchunk) {
   return (d + kc - 1) / kc;
 }
 
+// out[i] = storage(part[0][i] + part[1][i] + ...), in part order
+template <class TO>
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part, int parts, int64_t n,
-                                                        float* __restrict__ out) {
+                                                        TO* __restrict__ out) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     float s = part[i];
     for (int p = 1; p < parts; ++p) s += part[p * n + i];
-    out[i] = s;
+    out[i] = from_f32<TO>(s);
   }
+}
+
+template <class TO>
+static hipError_t launch_sum_parts(const float* part, int parts, int64_t n, TO* out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  sum_parts_kernel<TO><<<(unsigned)blocks, 256, 0, st>>>(part, parts, n, out);
+  return hipGetLastError();
 }
 
 template <class T>
@@ -322,10 +333,7 @@ hipError_t gemm_router_logits(const void* x, const void* w_r, float* logits, int
   const int64_t n = (int64_t)T_ * E;
   EpiStoreF32::P ep{part, E, n, T_, E};
   if (hipError_t e = run_gemm<T, KC, KC, DENSE, EpiStoreF32>(a, ep, T_, st); e != hipSuccess) return e;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  sum_parts_kernel<<<(unsigned)blocks, 256, 0, st>>>(part, parts, n, logits);
-  return hipGetLastError();
+  return launch_sum_parts<float>(part, parts, n, logits, st);
 }
 
 template <class T>
@@ -462,9 +470,26 @@ hipError_t gemm_wgrad(const void* P_, int M, const void* Q_, int N, const int* o
   }
 }
 
+// The router weight gradient has E x d outputs (1 x 32 tiles of 128 x 128 for
+// 128 experts and d = 4096) and a contraction over all T tokens: split the
+// tokens into parts that fill both workgroup slots of every CU (at most 8,
+// each at least 256 tokens), fp32 parts summed in part order and rounded once.
+int router_wgrad_parts(bool bf16, int64_t T, int E, int d, int* kchunk) {
+  *kchunk = (int)T;
+  if (!bf16 || T < 512) return 1;
+  const int64_t tiles = (int64_t)((E + 127) / 128) * ((d + 127) / 128);
+  int64_t s = (512 + tiles - 1) / tiles;
+  if (s > 8) s = 8;
+  if (s > T / 256) s = T / 256;
+  if (s <= 1) return 1;
+  const int kc = (int)(((T + s - 1) / s + 63) / 64 * 64);
+  *kchunk = kc;
+  return (int)((T + kc - 1) / kc);
+}
+
 // router backward: dW_r = dl^T x   (dl [T, Ep] with Ep = E rounded up to 8, zero padded)
 template <class T>
-hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T_, int d, void* dw_r,
+hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T_, int d, void* dw_r, float* part,
                              hipStream_t st) {
   GemmArgs a{};
   a.A = dl; a.lda = Ep; a.B = x; a.ldb = d;
@@ -473,9 +498,21 @@ hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T
   // E output rows: the persistent 128x128 kernel (the ring's 128x256 tiles are
   // few and mostly padding: 4 experts, 32768 tokens, d = 7168 took 0.29 ms on
   // the ring, 0.16 here; 256 experts, 4096 tokens 0.081 and 0.070)
-  if constexpr (sizeof(T) == 2)
-    if (d % 8 == 0 && ((uintptr_t)dw_r & 15) == 0)
+  if constexpr (sizeof(T) == 2) {
+    if (d % 8 == 0 && ((uintptr_t)dw_r & 15) == 0) {
+      int kchunk;
+      const int parts = router_wgrad_parts(true, T_, E, d, &kchunk);
+      if (parts > 1) {
+        a.G = parts;
+        a.kchunk = kchunk;
+        const int64_t n = (int64_t)E * d;
+        EpiStoreF32::P pp{part, d, n, E, d};
+        if (hipError_t e = launch_pipe<MC, MC, RAGGED_K, EpiStoreF32, 64>(a, pp, d, 0, st); e != hipSuccess) return e;
+        return launch_sum_parts<T>(part, parts, n, (T*)dw_r, st);
+      }
       return launch_pipe<MC, MC, RAGGED_K, EpiStore<T, 4>, 64>(a, ep, d, 0, st);
+    }
+  }
   return run_gemm<T, MC, MC, RAGGED_K, EpiStore<T, 4>>(a, ep, 0, st);
 }
 
@@ -487,6 +524,10 @@ hipError_t gemm_router_dgrad(const void* dl, int Ep, int E, const void* w_r, int
   a.A = dl; a.lda = Ep; a.B = w_r; a.ldb = d;
   a.M = T_; a.N = d; a.K = Ep; a.b_next = d; a.b_kend = E; a.G = 1;
   EpiAccumF32::P ep{dx_partial, d, 0, T_, d};
+  // a short contraction (Ep) and an fp32 read-modify-write of every output:
+  // persistent 128x256 tiles, so that a tile's epilogue overlaps the next
+  // tile's loads
+  if constexpr (sizeof(T) == 2) return launch_mfma<128, 256, 2, 4, 3, KC, MC, DENSE, EpiAccumF32>(a, ep, d, T_, st, true);
   return run_gemm<T, KC, MC, DENSE, EpiAccumF32>(a, ep, T_, st);
 }
 
@@ -508,7 +549,7 @@ hipError_t gemm_router_dgrad(const void* dl, int Ep, int E, const void* w_r, int
   template hipError_t gemm_wgrad<T>(const void*, int, const void*, int, const int*, int, int,    \
                                     void*, int, hipStream_t);                                         \
   template hipError_t gemm_router_wgrad<T>(const void*, int, int, const void*, int, int, void*,  \
-                                           hipStream_t);                                         \
+                                           float*, hipStream_t);                                 \
   template hipError_t gemm_router_dgrad<T>(const void*, int, int, const void*, int, int, float*, \
                                            hipStream_t);
 

@@ -59,9 +59,9 @@ struct GemmArgs {
   const int* tile_prefix;  // RAGGED_M: [G+1] cumulative m-tiles per group
   int G;
   int k_skip;              // RAGGED_K: groups with at most this many rows are left to another kernel
-  int kchunk;              // DENSE split-K (bf16 kernels): output tile (m, n) is computed ceil(K / kchunk)
-                           // times, part s over K range [s kchunk, (s+1) kchunk) into output block g = s
-                           // (kchunk a multiple of 64); 0: no split
+  int kchunk;              // split-K (bf16 kernels; DENSE, or RAGGED_K without offsets and G parts): output
+                           // tile (m, n) is computed once per part s, over K range [s kchunk, (s+1) kchunk),
+                           // into output block g = s (DENSE: kchunk a multiple of 64); 0: no split
 };
 
 // Persistent schedule over XCDs.  Workgroups are dispatched round-robin over
@@ -207,8 +207,10 @@ __device__ __forceinline__ void resolve_tile(const GemmArgs& a, const int* off, 
     int bm = min(kBandM, MT - band * kBandM);
     int mt = band * kBandM + in % bm, nt = in / bm;
     c.g = g; c.m0 = mt * BM; c.m_end = a.M; c.n0 = nt;
-    c.k_begin = a.offsets ? off[g] : 0;
-    c.k_end = a.offsets ? off[g + 1] : a.K;
+    // no offsets: one contraction [0, K), or with kchunk > 0 group g's part
+    // [g kchunk, (g+1) kchunk) of it (split-K)
+    c.k_begin = a.offsets ? off[g] : a.kchunk > 0 ? g * a.kchunk : 0;
+    c.k_end = a.offsets ? off[g + 1] : a.kchunk > 0 ? min(a.K, (g + 1) * a.kchunk) : a.K;
   }
 }
 
@@ -329,6 +331,7 @@ struct EpiStore {                       // C[row, col] = storage(v)
   static constexpr bool kRowDot = false;
   // 2-byte outputs may be staged through LDS and stored 8 columns at a time
   static constexpr bool kStaged = sizeof(T) == 2;
+  static constexpr bool kAccum = false;
   __device__ static void store8(const P& p, int g, int row, int col, u32x4 v) {
     uint16_t* c = (uint16_t*)(p.C + g * p.c_gstride + (int64_t)row * p.ldc + col);
     if (col + 8 <= p.N && (p.ldc & 7) == 0) {
@@ -357,6 +360,7 @@ struct EpiStoreF32T {                   // C[row, col] = v   (fp32 output)
   static constexpr bool kPaired = false;
   static constexpr bool kRowDot = false;
   static constexpr bool kStaged = false;
+  static constexpr bool kAccum = false;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void at(const P& p, int g, int row, int col, float v) {
     if (col < p.N) p.C[g * p.c_gstride + (int64_t)row * p.ldc + col] = v;
@@ -377,6 +381,9 @@ struct EpiAccumF32T {                   // C[row, col] += v  (fp32, one writer p
   static constexpr bool kPaired = false;
   static constexpr bool kRowDot = false;
   static constexpr bool kStaged = false;
+  // the MFMA kernel reads a 32-row fragment's old values (old4) before it
+  // writes any of them (add4), so the reads' latency is paid once per fragment
+  static constexpr bool kAccum = true;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void at(const P& p, int g, int row, int col, float v) {
     if (col < p.N) {
@@ -393,6 +400,23 @@ struct EpiAccumF32T {                   // C[row, col] += v  (fp32, one writer p
       store4<float>(c, w, true);
     } else {
       for (int i = 0; i < 4 && col + i < p.N; ++i) c[i] = c[i] + v[i];
+    }
+  }
+  __device__ static void old4(const P& p, int g, int row, int col, float o[4]) {
+    const float* c = p.C + g * p.c_gstride + (int64_t)row * p.ldc + col;
+    if (col + 4 <= p.N && (p.ldc & 3) == 0) {
+      load4<float>(c, o);
+    } else {
+      for (int i = 0; i < 4; ++i) o[i] = col + i < p.N ? c[i] : 0.0f;
+    }
+  }
+  __device__ static void add4(const P& p, int g, int row, int col, const float v[4], const float o[4]) {
+    float* c = p.C + g * p.c_gstride + (int64_t)row * p.ldc + col;
+    const float w[4] = {o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
+    if (col + 4 <= p.N && (p.ldc & 3) == 0) {
+      store4<float>(c, w, true);
+    } else {
+      for (int i = 0; i < 4 && col + i < p.N; ++i) c[i] = w[i];
     }
   }
 };
@@ -426,6 +450,7 @@ struct EpiSwiGLU {
   };
   static constexpr bool kPaired = true;
   static constexpr bool kStaged = false;
+  static constexpr bool kAccum = false;
   static constexpr bool kRowDot = false;
   // tile-row r of a BN-row tile split over WN waves: wave part w = r / (BN/WN);
   // its first half are gate rows, its second half the matching up rows
@@ -486,6 +511,7 @@ struct EpiSwiGLUBwd {
   };
   static constexpr bool kPaired = false;
   static constexpr bool kStaged = false;
+  static constexpr bool kAccum = false;
   static constexpr bool kRowDot = true;   // the kernels reduce at's return value when dg_part is set
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void grad(float dA, float h, float u, float& dh, float& du) {

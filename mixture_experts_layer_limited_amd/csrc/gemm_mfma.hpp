@@ -503,6 +503,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
         continue;
       }
       if (row >= c.m_end) continue;
+      if constexpr (Epi::kAccum) {
+        float old[FN][4][4];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            Epi::old4(ep, c.g, row, nt * BN + wn * (BN / WN) + j * 32 + q * 8 + (lane >> 5) * 4, old[j][q]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+            Epi::add4(ep, c.g, row, nt * BN + wn * (BN / WN) + j * 32 + q * 8 + (lane >> 5) * 4, v, old[j][q]);
+          }
+        continue;
+      }
       if constexpr (Epi::kPaired) {
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {

@@ -108,8 +108,11 @@ hipError_t gemm_gateup_dgrad(const void* dhu, const int* offsets, const int* til
 template <class T>
 hipError_t gemm_wgrad(const void* P_, int M, const void* Q_, int N, const int* offsets, int G,
                       int K_dense, void* dw, int site, hipStream_t st);
+// Split-K parts of the router weight gradient (contraction over the T tokens)
+// and the rows of each (*kchunk); [parts][E][d] fp32 of workspace.
+int router_wgrad_parts(bool bf16, int64_t T, int E, int d, int* kchunk);
 template <class T>
-hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T_, int d, void* dw_r,
+hipError_t gemm_router_wgrad(const void* dl, int Ep, int E, const void* x, int T_, int d, void* dw_r, float* part,
                              hipStream_t st);
 template <class T>
 hipError_t gemm_router_dgrad(const void* dl, int Ep, int E, const void* w_r, int T_, int d,
