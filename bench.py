@@ -72,32 +72,29 @@ def step_flops(cfg: mi.MoEConfig, backward: bool = True) -> float:
 def kernel_work_mx(cfg: mi.MoEConfig, counts) -> dict:
     """Algorithmic (flops, HBM bytes) per launch of each MXFP8 / MXFP4 expert
     GEMM: quantised operands cost 1 + 1/32 bytes per value for fp8 and
-    1/2 + 1/32 for fp4 (codes + one scale per 32), bf16 outputs 2;
-    weight-gradient operands are the column forms whose expert segments are
-    padded to 128 rows (fp8) or 256 (fp4)."""
+    1/2 + 1/32 for fp4 (codes + one scale per 32), bf16 outputs 2; the
+    weight gradients' operands count as read once in their quantised size
+    (the kernels read them widened to bf16, see mx_qdq_rows)."""
     fp4 = cfg.dtype == "mxfp4"
     q, B = (0.5 if fp4 else 1.0) + 1.0 / 32.0, 2
-    al = 256 if fp4 else 128
     rows, d, f, fs, T, E = cfg.T * cfg.k, cfg.d, cfg.f, cfg.f_shared, cfg.T, cfg.E
     ne = int((counts > 0).sum())
-    rp = int(sum(-(-int(c) // al) * al for c in counts))
-    tp = -(-T // al) * al
     out = {
         "gemm_mx_swiglu_fwd": (2.0 * rows * d * 2 * f, q * (ne * 2 * f * d + rows * d) + B * rows * 3 * f),
         "gemm_mx_down_fwd": (2.0 * rows * f * d, q * (ne * d * f + rows * f) + B * rows * d),
         "gemm_mx_down_dgrad_swiglu_bwd": (2.0 * rows * d * f, q * (ne * f * d + rows * d) + B * rows * 4 * f),
-        "gemm_mx_wgrad_down": (2.0 * rows * d * f, q * rp * (d + f) + B * E * d * f),
+        "gemm_mx_wgrad_down": (2.0 * rows * d * f, q * rows * (d + f) + B * E * d * f),
         "gemm_mx_gateup_dgrad": (2.0 * rows * 2 * f * d, q * (ne * d * 2 * f + rows * 2 * f) + B * rows * d),
-        "gemm_mx_wgrad_gateup": (2.0 * rows * 2 * f * d, q * rp * (2 * f + d) + B * E * 2 * f * d),
+        "gemm_mx_wgrad_gateup": (2.0 * rows * 2 * f * d, q * rows * (2 * f + d) + B * E * 2 * f * d),
     }
     if fs:
         out.update({
             "gemm_mx_swiglu_fwd_shared": (2.0 * T * d * 2 * fs, q * (2 * fs * d + T * d) + B * T * 3 * fs),
             "gemm_mx_down_fwd_shared": (2.0 * T * fs * d, q * (d * fs + T * fs) + B * T * d),
             "gemm_mx_down_dgrad_swiglu_bwd_shared": (2.0 * T * d * fs, q * (fs * d + T * d) + B * T * 4 * fs),
-            "gemm_mx_wgrad_down_shared": (2.0 * T * d * fs, q * tp * (d + fs) + B * d * fs),
+            "gemm_mx_wgrad_down_shared": (2.0 * T * d * fs, q * T * (d + fs) + B * d * fs),
             "gemm_mx_gateup_dgrad_shared": (2.0 * T * 2 * fs * d, q * (d * 2 * fs + T * 2 * fs) + 4 * T * d),
-            "gemm_mx_wgrad_gateup_shared": (2.0 * T * 2 * fs * d, q * tp * (2 * fs + d) + B * 2 * fs * d),
+            "gemm_mx_wgrad_gateup_shared": (2.0 * T * 2 * fs * d, q * T * (2 * fs + d) + B * 2 * fs * d),
         })
     return out
 

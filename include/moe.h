@@ -428,6 +428,9 @@ moe_status moe_grouped_gemm_swiglu_mxfp8(const moe_cfg* cfg, const void* x_perm,
  * for the weight gradients dY_perm, act, dHU and x_perm along their rows, in
  * blocks of 32 rows that restart at each expert's first row (rows past the
  * expert's end count as zeros); the shared expert likewise over all T rows.
+ * The weight gradients multiply those quantised values widened to bf16 (every
+ * e4m3 or e2m1 value times its power-of-two scale is a bf16 value, blocks
+ * scaled at the clamp 2^-127 aside): the same products, accumulated in fp32.
  * Same outputs as the bf16 call (dx_partial written, not accumulated). */
 moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_perm,
                                              const void* x_perm, const int32_t* expert_offsets,

@@ -234,17 +234,11 @@ GemmExtra gemm_extra(const moe_cfg* c, size_t at, bool bf16_gemms) {
 // MXFP8 workspace: two int arrays (tile prefix, padded offsets), one row-form
 // quantised activation (codes + scales) and two column-form ones
 struct MxWs {
-  int64_t rows_max, cmax_rows, cmax_cols, rp_max;
-  size_t ints, qa, qt;            // region sizes
+  int64_t rows_max, cmax_rows, cmax_cols;
+  size_t ints, qa, qt;            // region sizes (qt: one weight-gradient operand, bf16)
   GemmExtra extra;                // recomputed act, gate-gradient partials (after the others)
   size_t total() const { return ints + qa + 2 * qt + extra.bytes; }
 };
-inline int64_t pad128(int64_t v) { return (v + 127) / 128 * 128; }
-// padded row count of a dense column form (the shared expert's contraction over T)
-inline int64_t pad_rows(int64_t v, bool fp4) {
-  const int64_t a = mx_row_align(fp4);
-  return (v + a - 1) / a * a;
-}
 MxWs mx_ws(const moe_cfg* c) {
   MxWs w;
   const int64_t rows = c->T * c->k;
@@ -254,12 +248,10 @@ MxWs mx_ws(const moe_cfg* c) {
   if (2 * c->f_shared > cm) cm = 2 * c->f_shared;
   w.cmax_rows = cm;
   w.cmax_cols = cm;
-  // every group padded to the column form's row alignment (codes sized for
-  // fp8: an fp4 form takes half of each region)
-  w.rp_max = pad_rows(w.rows_max, is_fp4(c)) + (int64_t)mx_row_align(is_fp4(c)) * c->E;
+  // (row-form codes sized for fp8: an fp4 form takes half the region)
   w.ints = 2 * align256((size_t)(c->E + 2) * 4);
   w.qa = align256((size_t)(w.rows_max * w.cmax_rows)) + align256((size_t)(w.rows_max * w.cmax_rows / 32));
-  w.qt = align256((size_t)(w.cmax_cols * w.rp_max)) + align256((size_t)(w.cmax_cols * w.rp_max / 32));
+  w.qt = align256((size_t)(w.rows_max * w.cmax_cols * 2));
   w.extra = gemm_extra(c, w.ints + w.qa + 2 * w.qt, true);
   return w;
 }
@@ -417,9 +409,9 @@ moe_status router_bwd_impl(const moe_cfg* c, const void* x, const void* w_router
 // ---- MXFP8 expert GEMMs --------------------------------------------------------
 struct MxBufs {
   int* prefix;
-  int* poff;
-  uint8_t *qa_c, *qa_s, *q1_c, *q1_s, *q2_c, *q2_s;
-  int64_t rp_max;
+  int* bpre;            // 32-row block prefix of the weight gradients' operands
+  uint8_t *qa_c, *qa_s;
+  void *qd1, *qd2;      // weight-gradient operands, quantised and widened to bf16
   void* act_rec;        // act formed again (recomputation) or NULL
   float* dg_part;       // folded gates' gradient partials or NULL
 };
@@ -428,17 +420,14 @@ MxBufs mx_bufs(const moe_cfg* c, void* ws) {
   uint8_t* p = (uint8_t*)ws;
   MxBufs b;
   b.prefix = (int*)p;
-  b.poff = (int*)(p + w.ints / 2);
+  b.bpre = (int*)(p + w.ints / 2);
   p += w.ints;
   b.qa_c = p;
   b.qa_s = p + align256((size_t)(w.rows_max * w.cmax_rows));
   p += w.qa;
-  b.q1_c = p;
-  b.q1_s = p + align256((size_t)(w.cmax_cols * w.rp_max));
+  b.qd1 = p;
   p += w.qt;
-  b.q2_c = p;
-  b.q2_s = p + align256((size_t)(w.cmax_cols * w.rp_max));
-  b.rp_max = w.rp_max;
+  b.qd2 = p;
   b.act_rec = recompute(c) ? (uint8_t*)ws + w.extra.act : nullptr;
   b.dg_part = fold(c) ? (float*)((uint8_t*)ws + w.extra.dg) : nullptr;
   return b;
@@ -487,8 +476,22 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
     act = b.act_rec;
     act_s = b.act_rec;              // (the shared expert's, after the routed experts are done with it)
   }
-  const MxQ qa = mxq(b.qa_c, b.qa_s), q1 = mxq(b.q1_c, b.q1_s), q2 = mxq(b.q2_c, b.q2_s);
-  const int rp = (int)b.rp_max;
+  const MxQ qa = mxq(b.qa_c, b.qa_s);
+  // Weight gradients contract over the rows: both operands are quantised along
+  // the rows (32-row blocks restarting at each expert's first row) and widened
+  // back to bf16, where every microscaled value is exact, and multiplied by the
+  // bf16 weight-gradient kernels.  These products are bound by writing their
+  // bf16 outputs, which the stationary-band kernel does best; the products are
+  // the microscaled ones (exact in either form, fp32 accumulation).
+  auto wgrad = [&](const void* P, int M, const void* Q, int N, const int* offs, int G, int rows_k, void* dw,
+                   int site) -> moe_status {
+    LAUNCH_NAMED("mx_qdq_rows", launch_mx_qdq_rows(P, M, rows_k, M, offs, b.bpre, G, b.qd1, M, fp4, st));
+    LAUNCH_NAMED("mx_qdq_rows", launch_mx_qdq_rows(Q, N, rows_k, N, offs, b.bpre, G, b.qd2, N, fp4, st));
+    static const char* const kName[4] = {"gemm_mx_wgrad_gateup", "gemm_mx_wgrad_down", "gemm_mx_wgrad_gateup_shared",
+                                         "gemm_mx_wgrad_down_shared"};
+    LAUNCH_NAMED(kName[site], gemm_wgrad<bf16>(b.qd1, M, b.qd2, N, offs, G, offs ? 0 : rows_k, dw, site, st));
+    return ok();
+  };
   if (rows > 0) {
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, fp4, st));
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
@@ -499,38 +502,29 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
       LAUNCH_NAMED("gate_grad_sum", launch_gate_grad_sum(b.dg_part, gemm_dg_parts(true, f), row_id_map, rows, d_gates, st));
   }
   // weight gradients cover every expert: experts without rows get zeros
-  LAUNCH_NAMED("padded_offsets", launch_padded_offsets(off, E, b.poff, fp4, st));
-  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dy_perm, d, rows, d, off, b.poff, E, rp, rp, b.q1_c, b.q1_s, fp4, st));
-  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(act, f, rows, f, off, b.poff, E, rp, rp, b.q2_c, b.q2_s, fp4, st));
-  LAUNCH_NAMED("gemm_mx_wgrad_down", gemm_mx_wgrad(q1, d, q2, f, rp, b.poff, E, 0, dw2, 1, fp4, st));
+  LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 32, b.bpre, st));
+  CHECK(wgrad(dy_perm, d, act, f, off, E, rows, dw2, 1));
   if (rows > 0) {
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu, 2 * f, 0, 1, rows, 2 * f, b.qa_c, b.qa_s, fp4, st));
     LAUNCH_NAMED("gemm_mx_gateup_dgrad",
                  gemm_mx_gateup_dgrad(qa, off, b.prefix, E, mxq(w->w13_t), dx_perm, false, rows, d, f, fp4, st));
   }
-  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dhu, 2 * f, rows, 2 * f, off, b.poff, E, rp, rp, b.q1_c, b.q1_s, fp4, st));
-  LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(x_perm, d, rows, d, off, b.poff, E, rp, rp, b.q2_c, b.q2_s, fp4, st));
-  LAUNCH_NAMED("gemm_mx_wgrad_gateup", gemm_mx_wgrad(q1, 2 * f, q2, d, rp, b.poff, E, 0, dw13, 0, fp4, st));
+  CHECK(wgrad(dhu, 2 * f, x_perm, d, off, E, rows, dw13, 0));
   if (c->f_shared > 0) {
     const int fs = (int)c->f_shared;
-    const int tp = (int)pad_rows(T_, fp4);
     if (T_ > 0) {
       LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy, d, 0, 1, T_, d, b.qa_c, b.qa_s, fp4, st));
       LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd_shared",
                    gemm_mx_down_dgrad_swiglu_bwd(qa, nullptr, nullptr, 1, mxq(w->ws2_t), hu_s, dhu_s, T_, d, fs, nullptr,
                                                  nullptr, b.act_rec, fp4, st));
     }
-    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dy, d, T_, d, nullptr, nullptr, 1, tp, tp, b.q1_c, b.q1_s, fp4, st));
-    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(act_s, fs, T_, fs, nullptr, nullptr, 1, tp, tp, b.q2_c, b.q2_s, fp4, st));
-    LAUNCH_NAMED("gemm_mx_wgrad_down_shared", gemm_mx_wgrad(q1, d, q2, fs, tp, nullptr, 1, tp, dws2, 1, fp4, st));
+    CHECK(wgrad(dy, d, act_s, fs, nullptr, 1, T_, dws2, 3));
     if (T_ > 0) {
       LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu_s, 2 * fs, 0, 1, T_, 2 * fs, b.qa_c, b.qa_s, fp4, st));
       LAUNCH_NAMED("gemm_mx_gateup_dgrad_shared",
                    gemm_mx_gateup_dgrad(qa, nullptr, nullptr, 1, mxq(w->ws13_t), dx_partial, true, T_, d, fs, fp4, st));
     }
-    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(dhu_s, 2 * fs, T_, 2 * fs, nullptr, nullptr, 1, tp, tp, b.q1_c, b.q1_s, fp4, st));
-    LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols(x, d, T_, d, nullptr, nullptr, 1, tp, tp, b.q2_c, b.q2_s, fp4, st));
-    LAUNCH_NAMED("gemm_mx_wgrad_gateup_shared", gemm_mx_wgrad(q1, 2 * fs, q2, d, tp, nullptr, 1, tp, dws13, 0, fp4, st));
+    CHECK(wgrad(dhu_s, 2 * fs, x, d, nullptr, 1, T_, dws13, 2));
   } else {
     LAUNCH_NAMED("fill_f32", launch_fill_f32(dx_partial, (int64_t)T_ * d, 0.0f, st));
   }

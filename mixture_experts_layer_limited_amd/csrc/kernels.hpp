@@ -119,21 +119,19 @@ hipError_t gemm_router_dgrad(const void* dl, int Ep, int E, const void* w_r, int
                              float* dx_partial, hipStream_t st);
 
 // mxfp8.hip (MXFP8 and MXFP4: `fp4` selects e2m1 codes, two per byte)
-constexpr int kMxRowAlign = 128;        // column-form groups start on multiples of this row count (fp8)
-// fp4 column forms: groups start on multiples of 256 rows, one 128-byte slice row
-inline int mx_row_align(bool fp4) { return fp4 ? 2 * kMxRowAlign : kMxRowAlign; }
 struct MxQ {                            // codes and e8m0 scales of one quantised tensor
   const uint8_t* codes;
   const uint8_t* scales;
 };
 hipError_t launch_mx_quant_rows(const void* src, int64_t ld, int64_t src_bstride, int batch, int R, int C,
                                 uint8_t* codes, uint8_t* scales, bool fp4, hipStream_t st);
-hipError_t launch_padded_offsets(const int* off, int G, int* poff, bool fp4, hipStream_t st);
-hipError_t launch_mx_quant_cols(const void* src, int64_t ld, int rows, int C, const int* off, const int* poff,
-                                int G, int rows_pad_max, int64_t ldq, uint8_t* codes, uint8_t* scales, bool fp4,
-                                hipStream_t st);
 hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C, uint8_t* codes,
                                         uint8_t* scales, bool fp4, hipStream_t st);
+// dst [rows][ldd] bf16 = the microscaled values of src [rows][ld] with 32-row
+// blocks per column, restarting at each group's first row (bpre: cumulative
+// 32-row block counts, launch_tile_prefix with 32; off NULL: one group)
+hipError_t launch_mx_qdq_rows(const void* src, int64_t ld, int rows, int C, const int* off, const int* bpre, int G,
+                              void* dst, int64_t ldd, bool fp4, hipStream_t st);
 hipError_t gemm_mx_swiglu_fwd(const MxQ& x, const int* off, const int* prefix, int G, const MxQ& w13, void* hu,
                               void* act, int rows, int d, int f, const float* row_gates, bool from_stored, bool fp4,
                               hipStream_t st);
@@ -145,7 +143,5 @@ hipError_t gemm_mx_down_dgrad_swiglu_bwd(const MxQ& dy, const int* off, const in
                                          hipStream_t st);
 hipError_t gemm_mx_gateup_dgrad(const MxQ& dhu, const int* off, const int* prefix, int G, const MxQ& w13t,
                                 void* dx, bool f32_out, int rows, int d, int f, bool fp4, hipStream_t st);
-hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G, int K,
-                         void* dw, int site, bool fp4, hipStream_t st);
 
 }  // namespace moe

@@ -15,10 +15,11 @@
 //
 // Layouts:
 //   rows  : codes [R][C], scales [R][C/32]   (blocks along the contiguous C)
-//   cols  : codes [C][Rp], scales [C][Rp/32] (transposed copy, blocks along R)
-// In the column form the rows come in groups (experts); group g's rows start a
-// new block sequence at padded row poff[g] (a multiple of 128), and rows past
-// the group's end up to the next 128 are zero codes with zero-amax scales.
+//   cols  : codes [C][R], scales [C][R/32]   (transposed copy, blocks along R:
+//           the weights for the products that contract over their rows)
+// The weight gradients contract over the token rows: their operands are
+// quantised along the rows (32-row blocks restarting at each expert's first
+// row) and widened back to bf16 (mx_qdq_rows).
 #include <stdint.h>
 
 #include "common.hpp"
@@ -162,48 +163,20 @@ hipError_t launch_mx_quant_rows(const void* src, int64_t ld, int64_t src_bstride
 }
 
 // ---------------------------------------------------------------------------
-// Padded group offsets: poff[g] = sum over g' < g of n_g' rounded up to 128.
-// One workgroup (G <= 256).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void padded_offsets_kernel(const int* __restrict__ off, int G, int align,
-                                                             int* __restrict__ poff) {
-  __shared__ int s[kMaxExperts];
-  const int g = threadIdx.x;
-  int v = 0;
-  if (g < G) v = (off[g + 1] - off[g] + align - 1) / align * align;
-  s[g] = v;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int add = (g >= o) ? s[g - o] : 0;
-    __syncthreads();
-    s[g] += add;
-    __syncthreads();
-  }
-  if (g < G) poff[g + 1] = s[g];
-  if (g == 0) poff[0] = 0;
-}
-
-hipError_t launch_padded_offsets(const int* off, int G, int* poff, bool fp4, hipStream_t st) {
-  padded_offsets_kernel<<<1, 256, 0, st>>>(off, G, mx_row_align(fp4), poff);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Column form: a workgroup takes 128 padded rows (four 32-row blocks, never
-// straddling two groups since groups start on multiples of 128) by 64 columns.
-// The tile is read with 16-byte row loads into LDS; thread (column c, block b)
-// then quantises its 32 values and writes 32 contiguous code bytes, so the
-// four blocks of a column (four adjacent lanes) fill one 128-byte line.  src [rows][ld] bf16 with
-// groups off[G+1] (NULL: one group of `rows` rows); poff[G+1] padded offsets.
-// codes [C][ldq], scales [C][ldq/32]; rows at or past rp_limit are not written.
+// Column form (the weights' transposed copies): a workgroup takes 128 rows
+// (four 32-row blocks) by 64 columns.  The tile is read with 16-byte row loads
+// into LDS; thread (column c, block b) then quantises its 32 values and writes
+// 32 contiguous code bytes, so the four blocks of a column (four adjacent
+// lanes) fill one 128-byte line.  src [rows][ld] bf16, codes [C][ldq],
+// scales [C][ldq/32]; rows past `rows` below rp_limit are zero codes, rows at
+// or past rp_limit are not written.
 // ---------------------------------------------------------------------------
 constexpr int kQcRows = 128, kQcCols = 64;
 
 // FP4: codes [C][ldq / 2] (two per byte), 16 bytes per block
 template <bool FP4>
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __restrict__ src, int64_t ld,
-                                                            int rows, int C, const int* __restrict__ off,
-                                                            const int* __restrict__ poff, int G, int64_t ldq,
+                                                            int rows, int C, int64_t ldq,
                                                             int rp_limit, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, int64_t z_src,
                                                             int64_t z_codes) {
@@ -216,24 +189,10 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
   scales += blockIdx.z * (z_codes / 32);
   const int rp0 = blockIdx.x * kQcRows;
   const int c0 = blockIdx.y * kQcCols;
-  int src0, n;                                          // source rows of this tile: src0 .. src0+n-1
-  if (off) {
-    if (rp0 >= poff[G]) return;
-    int lo = 0, hi = G;                                 // group g with poff[g] <= rp0 < poff[g+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (poff[mid] <= rp0) lo = mid; else hi = mid;
-    }
-    const int local = rp0 - poff[lo];
-    src0 = off[lo] + local;
-    n = off[lo + 1] - off[lo] - local;
-  } else {
-    // one group: every tile below the padded length is written (rows past
-    // `rows` as zero codes), so an fp4 form padded to 256 rows is complete
-    if (rp0 >= rp_limit) return;
-    src0 = rp0;
-    n = rows - rp0;
-  }
+  // every tile below rp_limit is written (rows past `rows` as zero codes)
+  if (rp0 >= rp_limit) return;
+  const int src0 = rp0;                                 // source rows of this tile: src0 .. src0+n-1
+  int n = rows - rp0;
   n = n < 0 ? 0 : (n > kQcRows ? kQcRows : n);
   // 128 rows x 8 chunks of 16 bytes; columns past C and rows past n read as 0
   for (int q = threadIdx.x; q < kQcRows * (kQcCols / 8); q += 256) {
@@ -269,18 +228,102 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
   scales[(int64_t)(c0 + c) * (ldq / 32) + rb / 32] = (uint8_t)sb;
 }
 
-hipError_t launch_mx_quant_cols(const void* src, int64_t ld, int rows, int C, const int* off, const int* poff,
-                                int G, int rows_pad_max, int64_t ldq, uint8_t* codes, uint8_t* scales, bool fp4,
-                                hipStream_t st) {
-  if (rows_pad_max == 0 || C == 0) return hipSuccess;
-  const int tiles = (rows_pad_max + kQcRows - 1) / kQcRows;
-  const dim3 grid(tiles, (C + kQcCols - 1) / kQcCols);
+// ---------------------------------------------------------------------------
+// Quantise-dequantise along rows: dst [rows][ld] bf16 holds the microscaled
+// value (code x 2^e) of each src value, the blocks being 32 consecutive rows of
+// one column; group g's blocks start at its first row off[g] (NULL: one group
+// of `rows` rows), a group's last block holding the rows that remain (the
+// missing ones count as zeros, which leaves the block's amax unchanged).  An
+// e4m3 or e2m1 value times 2^e has at most four significant bits, so it is a
+// bf16 value (except where 2^e is clamped at 2^-127 and the block's values lie
+// below 2^-118, among bf16's subnormals): a product over two such operands in
+// bf16 MFMAs with fp32 accumulation is the microscaled product.  bpre [G+1] =
+// cumulative 32-row block counts of the groups (tile prefix of 32-row tiles).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t E = (c >> 3) & 15, m = c & 7;
+  const float a = E == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8 + m), (int)E - 10);
+  return (c & 0x80u) ? -a : a;
+}
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t E = (c >> 1) & 3, m = c & 1;          // 0, .5 | 1, 1.5 | 2, 3 | 4, 6
+  const float a = E == 0 ? 0.5f * (float)m : ldexpf((float)(2 + m), (int)E - 2);
+  return (c & 8u) ? -a : a;
+}
+
+template <bool FP4>
+__device__ __forceinline__ void qdq_block(float v[32]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = FP4 ? mx4_exponent(amax) : mx_exponent(amax);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float s = ldexpf(v[i], -e);
+    v[i] = ldexpf(FP4 ? e2m1_value(e2m1_code(s)) : e4m3_value(e4m3_code(s)), e);
+  }
+}
+
+// A workgroup takes one 32-row block by 256 columns: 16-byte row loads into
+// LDS, thread c quantises column c's 32 values there, 16-byte row stores.
+template <bool FP4>
+__global__ __launch_bounds__(256) void mx_qdq_rows_kernel(const uint16_t* __restrict__ src, int64_t ld, int rows,
+                                                          int C, const int* __restrict__ off,
+                                                          const int* __restrict__ bpre, int G,
+                                                          uint16_t* __restrict__ dst, int64_t ldd) {
+  __shared__ uint16_t tile[32][256];
+  const int blk = blockIdx.x;
+  int r0, n;
+  if (off) {
+    if (blk >= bpre[G]) return;
+    int lo = 0, hi = G;                                 // group g with bpre[g] <= blk < bpre[g+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (bpre[mid] <= blk) lo = mid; else hi = mid;
+    }
+    r0 = off[lo] + 32 * (blk - bpre[lo]);
+    n = off[lo + 1] - r0;
+  } else {
+    r0 = 32 * blk;
+    n = rows - r0;
+  }
+  if (n <= 0) return;
+  if (n > 32) n = 32;
+  const int c0 = blockIdx.y * 256;
+  // 32 rows x 32 chunks of 8 columns; rows past n and columns past C read as 0
+  for (int q = threadIdx.x; q < 32 * 32; q += 256) {
+    const int r = q >> 5, ch = q & 31, c = c0 + ch * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < n && c + 8 <= C) v = *(const u32x4*)(src + (int64_t)(r0 + r) * ld + c);
+    *(u32x4*)&tile[r][ch * 8] = v;
+  }
+  __syncthreads();
+  float v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = bf16_bits_lo(tile[r][threadIdx.x]);
+  qdq_block<FP4>(v);
+#pragma unroll
+  for (int r = 0; r < 32; ++r) tile[r][threadIdx.x] = (uint16_t)(pack_bf16x2(v[r], 0.0f) & 0xFFFFu);
+  __syncthreads();
+  for (int q = threadIdx.x; q < 32 * 32; q += 256) {
+    const int r = q >> 5, ch = q & 31, c = c0 + ch * 8;
+    if (r < n && c + 8 <= C) *(u32x4*)(dst + (int64_t)(r0 + r) * ldd + c) = *(const u32x4*)&tile[r][ch * 8];
+  }
+}
+
+hipError_t launch_mx_qdq_rows(const void* src, int64_t ld, int rows, int C, const int* off, const int* bpre, int G,
+                              void* dst, int64_t ldd, bool fp4, hipStream_t st) {
+  if (rows <= 0 || C <= 0) return hipSuccess;
+  if (C % 8 != 0 || ld % 8 != 0 || ldd % 8 != 0 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
+    return hipErrorInvalidValue;
+  const int64_t blocks = (rows + 31) / 32 + (off ? G : 0);   // upper bound of the groups' 32-row blocks
+  const dim3 grid((unsigned)blocks, (unsigned)((C + 255) / 256));
   if (fp4)
-    mx_quant_cols_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, rows, C, off, poff, G, ldq,
-                                                     rows_pad_max, codes, scales, 0, 0);
+    mx_qdq_rows_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, rows, C, off, bpre, G,
+                                                   (uint16_t*)dst, ldd);
   else
-    mx_quant_cols_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, rows, C, off, poff, G, ldq,
-                                                      rows_pad_max, codes, scales, 0, 0);
+    mx_qdq_rows_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, rows, C, off, bpre, G,
+                                                    (uint16_t*)dst, ldd);
   return hipGetLastError();
 }
 
@@ -293,10 +336,10 @@ hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C
   const int tiles = (R + kQcRows - 1) / kQcRows;
   const dim3 grid(tiles, (C + kQcCols - 1) / kQcCols, batch);
   if (fp4)
-    mx_quant_cols_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, nullptr, nullptr, 1, R, R,
+    mx_quant_cols_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, R, R,
                                                      codes, scales, (int64_t)R * C, (int64_t)R * C);
   else
-    mx_quant_cols_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, nullptr, nullptr, 1, R, R,
+    mx_quant_cols_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, R, R,
                                                       codes, scales, (int64_t)R * C, (int64_t)R * C);
   return hipGetLastError();
 }
@@ -429,49 +472,6 @@ hipError_t gemm_mx_gateup_dgrad(const MxQ& dhu, const int* off, const int* prefi
   typename EpiStore<bf16, 6>::P ep{(bf16*)dx, d, 0, rows, d};
   return mx_rows_gemm<EpiStore<bf16, 6>>(dhu, off, prefix, G, w13t, (int64_t)d * 2 * f, rows, d, 2 * f, ep, d, fp4,
                                          st);
-}
-
-// zero the weight gradients of groups without rows (poff NULL: one group of K rows)
-__global__ __launch_bounds__(256) void zero_empty_groups_mx_kernel(const int* __restrict__ poff,
-                                                                   u32x4* __restrict__ out, int64_t vec, int K) {
-  const int g = blockIdx.y;
-  if (poff ? poff[g + 1] != poff[g] : K != 0) return;
-  u32x4* o = out + g * vec;
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vec; i += (int64_t)gridDim.x * blockDim.x)
-    o[i] = z;
-}
-
-// dW[g] (M x N) = P_g^T Q_g with both operands in column form (codes [M][ldq],
-// [N][ldq] values) over padded row groups poff (NULL: one group of K rows)
-template <bool FP4>
-static hipError_t mx_wgrad_launch(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G,
-                                  int K, void* dw, int site, hipStream_t st) {
-  GemmArgs a{};
-  a.A = p.codes; a.lda = ldq; a.B = q.codes; a.ldb = ldq;
-  a.M = M; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
-  a.offsets = poff; a.G = poff ? G : 1;
-  MxArgs s{p.scales, q.scales, ldq / 32, ldq / 32, 0};
-  if (site == 1) {
-    typename EpiStore<bf16, 8>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
-    return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 8>, FP4>(a, s, ep, N, 0, st);
-  }
-  typename EpiStore<bf16, 7>::P ep{(bf16*)dw, N, (int64_t)M * N, M, N};
-  return launch_mx_pipe<RAGGED_K, EpiStore<bf16, 7>, FP4>(a, s, ep, N, 0, st);
-}
-
-hipError_t gemm_mx_wgrad(const MxQ& p, int M, const MxQ& q, int N, int64_t ldq, const int* poff, int G, int K,
-                         void* dw, int site, bool fp4, hipStream_t st) {
-  // the pipelined kernel stages 16-byte row pieces of the output (the call's
-  // shape checks and 16-byte aligned outputs guarantee them) and skips empty
-  // contractions, whose outputs are zero-filled here
-  if (N % 8 != 0 || ((uintptr_t)dw & 15) != 0) return hipErrorInvalidValue;
-  const int64_t vec = (int64_t)M * N * 2 / 16;
-  zero_empty_groups_mx_kernel<<<dim3(64, poff ? G : 1), 256, 0, st>>>(poff, (u32x4*)dw, vec, K);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return fp4 ? mx_wgrad_launch<true>(p, M, q, N, ldq, poff, G, K, dw, site, st)
-             : mx_wgrad_launch<false>(p, M, q, N, ldq, poff, G, K, dw, site, st);
 }
 
 }  // namespace moe
