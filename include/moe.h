@@ -389,6 +389,15 @@ typedef enum moe_mx_orientation {
 moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int64_t cols,
                               int32_t orientation, uint8_t* codes, uint8_t* scales, void* stream);
 
+/* Both orientations of the same matrices in one pass, each bf16 value read
+ * once: codes_rows / scales_rows exactly as MOE_MX_ROWS, codes_cols /
+ * scales_cols exactly as MOE_MX_COLS would give them.  rows and cols
+ * multiples of 32; other limits and errors as moe_quantize_mxfp8.  For the
+ * callers that quantise expert weights (both forms, once per update). */
+moe_status moe_quantize_mxfp8_both(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                                   uint8_t* codes_rows, uint8_t* scales_rows, uint8_t* codes_cols,
+                                   uint8_t* scales_cols, void* stream);
+
 /* One quantised operand (device memory): codes 16-byte, scales 4-byte aligned. */
 typedef struct moe_mx_tensor {
   const uint8_t* codes;
@@ -464,6 +473,10 @@ moe_status moe_grouped_gemm_swiglu_bwd_mxfp8(const moe_cfg* cfg, const void* dy_
  * ------------------------------------------------------------------------- */
 moe_status moe_quantize_mxfp4(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t orientation,
                               uint8_t* codes, uint8_t* scales, void* stream);
+/* moe_quantize_mxfp8_both with e2m1 codes (two per byte) */
+moe_status moe_quantize_mxfp4_both(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                                   uint8_t* codes_rows, uint8_t* scales_rows, uint8_t* codes_cols,
+                                   uint8_t* scales_cols, void* stream);
 
 /* moe_grouped_gemm_swiglu_mxfp8 and moe_grouped_gemm_swiglu_bwd_mxfp8 with
  * MXFP4 operands (cfg.dtype = MOE_MXFP4; d, f, f_shared multiples of 256, one

@@ -73,6 +73,8 @@ _SIGS = {
                                           + [_P, ctypes.c_size_t, _P]),
     "moe_quantize_mxfp4": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                           _P, _P, _P]),
+    "moe_quantize_mxfp8_both": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + [_P] * 5),
+    "moe_quantize_mxfp4_both": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + [_P] * 5),
     "moe_grouped_gemm_swiglu_mxfp4": (ctypes.c_int, [ctypes.POINTER(moe_cfg), _P, _P, _P,
                                                      ctypes.POINTER(moe_mx_weights)] + [_P] * 7
                                       + [_P, ctypes.c_size_t, _P]),
@@ -281,6 +283,18 @@ def moe_quantize_mxfp8(src, batch, rows, cols, orientation, codes, scales, strea
 def moe_quantize_mxfp4(src, batch, rows, cols, orientation, codes, scales, stream=None):
     _check(lib().moe_quantize_mxfp4(_ptr(src, torch.bfloat16), batch, rows, cols, orientation, _ptr(codes, _U8),
                                     _ptr(scales, _U8), _stream(stream)), "moe_quantize_mxfp4")
+
+
+def moe_quantize_mxfp8_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, stream=None):
+    _check(lib().moe_quantize_mxfp8_both(_ptr(src, torch.bfloat16), batch, rows, cols, _ptr(codes_rows, _U8),
+                                         _ptr(scales_rows, _U8), _ptr(codes_cols, _U8), _ptr(scales_cols, _U8),
+                                         _stream(stream)), "moe_quantize_mxfp8_both")
+
+
+def moe_quantize_mxfp4_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, stream=None):
+    _check(lib().moe_quantize_mxfp4_both(_ptr(src, torch.bfloat16), batch, rows, cols, _ptr(codes_rows, _U8),
+                                         _ptr(scales_rows, _U8), _ptr(codes_cols, _U8), _ptr(scales_cols, _U8),
+                                         _stream(stream)), "moe_quantize_mxfp4_both")
 
 
 def mx_weights(**tensors) -> moe_mx_weights:

@@ -892,6 +892,33 @@ moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int6
   return quantize_mx(src, batch, rows, cols, orientation, codes, scales, false, stream);
 }
 
+static moe_status quantize_mx_both(const void* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes_r,
+                                   uint8_t* scales_r, uint8_t* codes_c, uint8_t* scales_c, bool fp4, void* stream) {
+  REQ(src); REQ(codes_r); REQ(scales_r); REQ(codes_c); REQ(scales_c);
+  ALIGNED(src); ALIGNED(codes_r); ALIGNED(codes_c);
+  if (batch < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "negative size");
+  if (batch > 65535) return fail(MOE_ERR_INVALID_ARGUMENT, "batch = %lld above 65535", (long long)batch);
+  if (rows * cols >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "rows * cols must stay below 2^31");
+  if (rows % 32 || cols % 32)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "both orientations need rows and cols multiples of 32 (%lld x %lld)",
+                (long long)rows, (long long)cols);
+  CHECK(check_current_device());
+  hipStream_t st = (hipStream_t)stream;
+  LAUNCH_NAMED("mx_quant_both", launch_mx_quant_both(src, (int)batch, (int)rows, (int)cols, codes_r, scales_r,
+                                                     codes_c, scales_c, fp4, st));
+  return ok();
+}
+
+moe_status moe_quantize_mxfp8_both(const void* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes_rows,
+                                   uint8_t* scales_rows, uint8_t* codes_cols, uint8_t* scales_cols, void* stream) {
+  return quantize_mx_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, false, stream);
+}
+
+moe_status moe_quantize_mxfp4_both(const void* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes_rows,
+                                   uint8_t* scales_rows, uint8_t* codes_cols, uint8_t* scales_cols, void* stream) {
+  return quantize_mx_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, true, stream);
+}
+
 moe_status moe_quantize_mxfp4(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t orientation,
                               uint8_t* codes, uint8_t* scales, void* stream) {
   return quantize_mx(src, batch, rows, cols, orientation, codes, scales, true, stream);

@@ -39,37 +39,19 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return e > 127 ? 127 : e;
 }
 
-// e4m3fn code of v (finite), round to nearest even, saturating at 448
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (a >= 448.0f) {
-    code = 0x7E;
-  } else if (a < 0x1p-6f) {                            // subnormal range, step 2^-9
-    code = (uint32_t)rintf(a * 512.0f);                // 8 is the first normal, 2^-6
-  } else {
-    int E = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;   // -6 .. 8
-    uint32_t q = (uint32_t)rintf(ldexpf(a, 3 - E));    // 8 .. 16
-    if (q == 16) { q = 8; ++E; }
-    code = ((uint32_t)(E + 7) << 3) | (q - 8);
-    if (code > 0x7E) code = 0x7E;
-  }
-  return sign | code;
-}
-
 // quantise 32 fp32 values; returns the scale byte
 __device__ __forceinline__ uint32_t mx_block(const float v[32], uint32_t out[8]) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const int e = mx_exponent(amax);
+  // v_cvt_pk_fp8_f32: the nearest e4m3fn code, ties to the even code (|v| / 2^e
+  // <= 448 by the choice of e, so nothing reaches the saturation)
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) word |= e4m3_code(ldexpf(v[4 * w + b], -e)) << (8 * b);
-    out[w] = word;
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * w], -e), ldexpf(v[4 * w + 1], -e), 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * w + 2], -e), ldexpf(v[4 * w + 3], -e), word, true);
+    out[w] = (uint32_t)word;
   }
   return (uint32_t)(e + 127);
 }
@@ -174,12 +156,16 @@ hipError_t launch_mx_quant_rows(const void* src, int64_t ld, int64_t src_bstride
 constexpr int kQcRows = 128, kQcCols = 64;
 
 // FP4: codes [C][ldq / 2] (two per byte), 16 bytes per block
-template <bool FP4>
+// ROWS_TOO: the same launch also writes the row form of the tile (codes_r
+// [R][C], scales_r [R][C/32] per matrix; rows = rp_limit = R, a multiple of
+// 32, C of 32), so a weight is read once for both forms.
+template <bool FP4, bool ROWS_TOO = false>
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __restrict__ src, int64_t ld,
                                                             int rows, int C, int64_t ldq,
                                                             int rp_limit, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, int64_t z_src,
-                                                            int64_t z_codes) {
+                                                            int64_t z_codes, uint8_t* __restrict__ codes_r = nullptr,
+                                                            uint8_t* __restrict__ scales_r = nullptr) {
   __shared__ uint16_t tile[kQcRows][kQcCols];
   // grid z: independent matrices (a batch of weights), z_src elements and
   // z_codes values apart (z_codes code bytes for fp8, half that for fp4;
@@ -203,6 +189,36 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
     *(u32x4*)&tile[r][(ch ^ ((r >> 5) << 1)) * 8] = v;  // block b's chunks XOR 2b
   }
   __syncthreads();
+  if constexpr (ROWS_TOO) {
+    // thread t: row t / 2 of the tile, its 32-column block t % 2
+    const int r = threadIdx.x >> 1, bb = threadIdx.x & 1, cb = c0 + 32 * bb;
+    if (r < n && cb + 32 <= C) {
+      float v[32];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 w = *(const u32x4*)&tile[r][((4 * bb + k) ^ ((r >> 5) << 1)) * 8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * k + 2 * j] = bf16_bits_lo(w[j]);
+          v[8 * k + 2 * j + 1] = bf16_bits_hi(w[j]);
+        }
+      }
+      const int64_t row = (int64_t)blockIdx.z * rows + src0 + r;
+      uint32_t sb;
+      if constexpr (FP4) {
+        uint32_t out[4];
+        sb = mx4_block(v, out);
+        *(u32x4*)(codes_r + row * (C / 2) + cb / 2) = u32x4{out[0], out[1], out[2], out[3]};
+      } else {
+        uint32_t out[8];
+        sb = mx_block(v, out);
+        u32x4* q = (u32x4*)(codes_r + row * C + cb);
+        q[0] = u32x4{out[0], out[1], out[2], out[3]};
+        q[1] = u32x4{out[4], out[5], out[6], out[7]};
+      }
+      scales_r[row * (C / 32) + cb / 32] = (uint8_t)sb;
+    }
+  }
   // wave w takes columns 16w .. 16w+15 and lane (4j + b) block b of column
   // 16w + j: the four blocks of a column, one 128-byte code line, come from
   // adjacent lanes; the XOR puts the 4 x 16 columns on 32 distinct banks
@@ -228,6 +244,21 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
   scales[(int64_t)(c0 + c) * (ldq / 32) + rb / 32] = (uint8_t)sb;
 }
 
+hipError_t launch_mx_quant_both(const void* src, int batch, int R, int C, uint8_t* codes_r, uint8_t* scales_r,
+                                uint8_t* codes_c, uint8_t* scales_c, bool fp4, hipStream_t st) {
+  if (batch == 0 || R == 0 || C == 0) return hipSuccess;
+  if (R % 32 || C % 32) return hipErrorInvalidValue;
+  const dim3 grid((R + kQcRows - 1) / kQcRows, (C + kQcCols - 1) / kQcCols, batch);
+  const int64_t z = (int64_t)R * C;
+  if (fp4)
+    mx_quant_cols_kernel<true, true><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, R, R, codes_c, scales_c, z, z,
+                                                           codes_r, scales_r);
+  else
+    mx_quant_cols_kernel<false, true><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, R, R, codes_c, scales_c, z,
+                                                            z, codes_r, scales_r);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Quantise-dequantise along rows: dst [rows][ld] bf16 holds the microscaled
 // value (code x 2^e) of each src value, the blocks being 32 consecutive rows of
@@ -240,11 +271,6 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
 // bf16 MFMAs with fp32 accumulation is the microscaled product.  bpre [G+1] =
 // cumulative 32-row block counts of the groups (tile prefix of 32-row tiles).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t E = (c >> 3) & 15, m = c & 7;
-  const float a = E == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8 + m), (int)E - 10);
-  return (c & 0x80u) ? -a : a;
-}
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
   const uint32_t E = (c >> 1) & 3, m = c & 1;          // 0, .5 | 1, 1.5 | 2, 3 | 4, 6
   const float a = E == 0 ? 0.5f * (float)m : ldexpf((float)(2 + m), (int)E - 2);
@@ -257,10 +283,18 @@ __device__ __forceinline__ void qdq_block(float v[32]) {
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const int e = FP4 ? mx4_exponent(amax) : mx_exponent(amax);
+  if constexpr (FP4) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float s = ldexpf(v[i], -e);
-    v[i] = ldexpf(FP4 ? e2m1_value(e2m1_code(s)) : e4m3_value(e4m3_code(s)), e);
+    for (int i = 0; i < 32; ++i) v[i] = ldexpf(e2m1_value(e2m1_code(ldexpf(v[i], -e))), e);
+  } else {
+    // to the e4m3fn grid and back with the hardware conversions (nearest
+    // code, ties to even)
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+      const int w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[i], -e), ldexpf(v[i + 1], -e), 0, false);
+      v[i] = ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 0), e);
+      v[i + 1] = ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 1), e);
+    }
   }
 }
 

@@ -144,25 +144,20 @@ class MoELayer:
         q = {}
         fp4 = s.dtype == "mxfp4"
         per_byte = 2 if fp4 else 1
-        quantize = abi.moe_quantize_mxfp4 if fp4 else abi.moe_quantize_mxfp8
+        quantize_both = abi.moe_quantize_mxfp4_both if fp4 else abi.moe_quantize_mxfp8_both
 
-        def quant(name, w, batch, rows, cols, orient):
-            if orient == abi.MOE_MX_ROWS:
-                c, sc = u8(batch, rows, cols // per_byte), u8(batch, rows, cols // 32)
-            else:
-                c, sc = u8(batch, cols, rows // per_byte), u8(batch, cols, rows // 32)
-            quantize(w, batch, rows, cols, orient, c, sc, stream)
-            q[name] = (c, sc)
+        def quant(name, w, batch, rows, cols):
+            # the row form (name) and the transposed form (name_t) in one pass
+            c, sc = u8(batch, rows, cols // per_byte), u8(batch, rows, cols // 32)
+            ct, sct = u8(batch, cols, rows // per_byte), u8(batch, cols, rows // 32)
+            quantize_both(w, batch, rows, cols, c, sc, ct, sct, stream)
+            q[name], q[name + "_t"] = (c, sc), (ct, sct)
 
-        quant("w13", w13, s.E, 2 * s.f, s.d, abi.MOE_MX_ROWS)
-        quant("w2", w2, s.E, s.d, s.f, abi.MOE_MX_ROWS)
-        quant("w13_t", w13, s.E, 2 * s.f, s.d, abi.MOE_MX_COLS)
-        quant("w2_t", w2, s.E, s.d, s.f, abi.MOE_MX_COLS)
+        quant("w13", w13, s.E, 2 * s.f, s.d)
+        quant("w2", w2, s.E, s.d, s.f)
         if s.f_shared:
-            quant("ws13", ws13, 1, 2 * s.f_shared, s.d, abi.MOE_MX_ROWS)
-            quant("ws2", ws2, 1, s.d, s.f_shared, abi.MOE_MX_ROWS)
-            quant("ws13_t", ws13, 1, 2 * s.f_shared, s.d, abi.MOE_MX_COLS)
-            quant("ws2_t", ws2, 1, s.d, s.f_shared, abi.MOE_MX_COLS)
+            quant("ws13", ws13, 1, 2 * s.f_shared, s.d)
+            quant("ws2", ws2, 1, s.d, s.f_shared)
         self.mx_tensors = q                          # keeps the device memory alive
         self.mx_weights = abi.mx_weights(**q)
         self.mx_sources = (w13, w2, ws13, ws2)       # their memory stays theirs while the copies exist

@@ -70,6 +70,32 @@ def test_quantize_mx_bitexact(batch, rows, cols, fmt):
     np.testing.assert_array_equal(s2.cpu().numpy(), osc2)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("batch,rows,cols", [(2, 160, 96), (1, 64, 320), (3, 256, 128)])
+def test_quantize_both_orientations_in_one_pass(batch, rows, cols, fmt):
+    """moe_quantize_mx*_both gives, byte for byte, what the two single-
+    orientation calls give (both already pinned to the oracle above)."""
+    _needs_gpu()
+    fp4 = fmt == "e2m1"
+    print(f"\n[mx quant both] {fmt} batch={batch} rows={rows} cols={cols}", flush=True)
+    xd = _bf16_matrix(batch, rows, cols, seed=rows + 3 * cols).cuda()
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    per = 2 if fp4 else 1
+    single = abi.moe_quantize_mxfp4 if fp4 else abi.moe_quantize_mxfp8
+    both = abi.moe_quantize_mxfp4_both if fp4 else abi.moe_quantize_mxfp8_both
+    c, s = u8(batch, rows, cols // per), u8(batch, rows, cols // 32)
+    ct, st = u8(batch, cols, rows // per), u8(batch, cols, rows // 32)
+    single(xd, batch, rows, cols, abi.MOE_MX_ROWS, c, s)
+    single(xd, batch, rows, cols, abi.MOE_MX_COLS, ct, st)
+    b = [torch.full_like(t, 0xA5) for t in (c, s, ct, st)]
+    both(xd, batch, rows, cols, *b)
+    torch.cuda.synchronize()
+    for want, got in zip((c, s, ct, st), b):
+        assert torch.equal(want, got)
+    with pytest.raises(RuntimeError):
+        both(xd, batch, rows - 16, cols, *b)            # rows not a multiple of 32
+
+
 def _cfg(name, **kw):
     base = dict(dtype="mxfp8", backward=True, router_std=0.02, expert_std=0.02)
     base.update(kw)
