@@ -180,33 +180,45 @@ def mx_stepwise_check(cfg: mi.MoEConfig, inp: dict, g: dict) -> dict:
     bits): A and H, U from x_perm; Y from act; dH, dU from dy_perm and the
     saved H, U, act; dX from the GPU's dH, dU; the weight gradients over all of
     the expert's rows; the shared expert likewise.  Tensor bound TOL, row bound
-    ROW_FACTOR * TOL.  Returns the worst errors."""
+    ROW_FACTOR * TOL.  Returns the worst errors.
+
+    Beside each check it also measures what the microscaling itself costs that
+    product: the same-quantisation oracle against the product of the same
+    (unquantised) bf16 operands, relative L2 over the whole product; the
+    table `quant` of the return value (and the printed line) holds the worst
+    over the experts."""
     tol = TOL[cfg.dtype]
     f = cfg.f
     fmt = O.mx_format_of(cfg.dtype)
     q = lambda a, axis: O.mx_qdq(a, axis, fmt)
     w13, w2 = inp["w13"], inp["w2"]
-    worst, worst_row = {}, {}
+    worst, worst_row, quant = {}, {}, {}
 
-    def chk(name, got, want):
+    def chk(name, got, want, plain=None):
         e = rel_l2(got, want)
         r, el = row_errors(got, want)
         worst[name] = max(worst.get(name, 0.0), e)
         worst_row[name] = max(worst_row.get(name, 0.0), r, el)
+        if plain is not None:
+            quant[name] = max(quant.get(name, 0.0), rel_l2(want, plain))
         assert e <= tol and r <= ROW_FACTOR * tol and el <= ELEM_FACTOR * tol, (name, e, r, el)
 
     def expert(xe, hu, act, dyp, dhu, dxp, dw13, dw2, W13, W2, fe, tag, gate=None):
         o = O.swiglu_ffn_fwd_mx(xe, W13, W2, "bf16", gate=gate, act_from_stored=cfg.recompute_act, fmt=fmt)
-        chk(tag + "H", hu[:, :fe], o["H"])
-        chk(tag + "U", hu[:, fe:], o["U"])
+        p = O.swiglu_ffn_fwd(xe, W13, W2, "bf16", gate=gate, act_from_stored=cfg.recompute_act)
+        chk(tag + "H", hu[:, :fe], o["H"], p["H"])
+        chk(tag + "U", hu[:, fe:], o["U"], p["U"])
         chk(tag + "A", act, o["A"])
-        b = O.swiglu_ffn_bwd_mx(xe, hu[:, :fe], hu[:, fe:], act, dyp, W13, W2, "bf16", gate=gate, fmt=fmt)
-        chk(tag + "dH", dhu[:, :fe], b["dH"])
-        chk(tag + "dU", dhu[:, fe:], b["dU"])
-        chk(tag + "dW2", dw2, O.store(q(dyp, 0).T @ q(act, 0), "bf16"))
-        chk(tag + "dW13", dw13, O.store(q(dhu, 0).T @ q(xe, 0), "bf16"))
+        H, U = hu[:, :fe], hu[:, fe:]
+        b = O.swiglu_ffn_bwd_mx(xe, H, U, act, dyp, W13, W2, "bf16", gate=gate, fmt=fmt)
+        pb = O.swiglu_ffn_bwd(xe, H, U, act, dyp, W13, W2, "bf16", gate=gate)
+        chk(tag + "dH", dhu[:, :fe], b["dH"], pb["dH"])
+        chk(tag + "dU", dhu[:, fe:], b["dU"], pb["dU"])
+        n64 = lambda a: np.asarray(a, np.float64)
+        chk(tag + "dW2", dw2, O.store(q(dyp, 0).T @ q(act, 0), "bf16"), O.store(n64(dyp).T @ n64(act), "bf16"))
+        chk(tag + "dW13", dw13, O.store(q(dhu, 0).T @ q(xe, 0), "bf16"), O.store(n64(dhu).T @ n64(xe), "bf16"))
         if dxp is not None:
-            chk(tag + "dX", dxp, O.store(q(dhu, 1) @ q(W13, 0), "bf16"))
+            chk(tag + "dX", dxp, O.store(q(dhu, 1) @ q(W13, 0), "bf16"), O.store(n64(dhu) @ n64(W13), "bf16"))
         return o
 
     off = np.asarray(g["offsets"])
@@ -218,13 +230,24 @@ def mx_stepwise_check(cfg: mi.MoEConfig, inp: dict, g: dict) -> dict:
         W13, W2 = O._np(w13[e]), O._np(w2[e])
         expert(g["x_perm"][sl], g["hu"][sl], g["act"][sl], g["dy_perm"][sl], g["dhu"][sl], g["dx_perm"][sl],
                g["dw13"][e], g["dw2"][e], W13, W2, f, "", gate=g["row_gates"][sl] if cfg.fold_gates else None)
-        chk("Y", g["y_perm"][sl], O.store(q(g["act"][sl], 1) @ q(W2, 1).T, "bf16"))
+        a = g["act"][sl]
+        chk("Y", g["y_perm"][sl], O.store(q(a, 1) @ q(W2, 1).T, "bf16"),
+            O.store(np.asarray(a, np.float64) @ np.asarray(W2, np.float64).T, "bf16"))
     if cfg.f_shared:
         x, dy = O._np(inp["x"]), O._np(inp["dy"])
         Ws13, Ws2 = O._np(inp["ws13"]), O._np(inp["ws2"])
         expert(x, g["hu_s"], g["act_s"], dy, g["dhu_s"], None, g["dws13"], g["dws2"], Ws13, Ws2,
                cfg.f_shared, "shared_")
-        chk("shared_Y", g["y_s"], O.store(q(g["act_s"], 1) @ q(Ws2, 1).T, "bf16"))
+        a = g["act_s"]
+        chk("shared_Y", g["y_s"], O.store(q(a, 1) @ q(Ws2, 1).T, "bf16"),
+            O.store(np.asarray(a, np.float64) @ np.asarray(Ws2, np.float64).T, "bf16"))
     print(f"{cfg.name} stepwise: " + " ".join(f"{k}={v:.1e}/{worst_row[k]:.1e}" for k, v in worst.items()),
           flush=True)
-    return worst
+    print(f"{cfg.name} {fmt} quantisation error per product (same-quantisation oracle vs bf16 operands): "
+          + " ".join(f"{k}={v:.2e}" for k, v in quant.items()), flush=True)
+    # the rule rounds each operand to 4 (e4m3) or 2 (e2m1) significant bits:
+    # an RMS relative error of at most 2^-4/sqrt(3) or 2^-2/sqrt(3) per operand,
+    # about sqrt(2) of that on a product of two; bounds with a margin of 1.6
+    qb = 1.6 * 2 ** 0.5 * (2.0 ** -4 if fmt == "e4m3" else 2.0 ** -2) / 3 ** 0.5
+    assert all(v <= qb for v in quant.values()), (qb, quant)
+    return {"worst": worst, "quant": quant}
