@@ -268,8 +268,10 @@ __device__ __forceinline__ void sched_pipelined_slice() {
 // BK = 64 units is 128 fp8 values and the data path is the bf16 one.
 template <int BM, int BN, int WM, int WN, int STAGES, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi,
           bool MX = false, bool FP4 = false>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT,
-                                                                 int MT) {
+// (every configuration fills a CU's LDS with one workgroup, so at most two
+// waves share a SIMD: the compiler may give each the registers of two)
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_mfma_kernel(
+    GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
   using C = TileCfg<BM, BN, WM, WN, STAGES, MX>;
   static_assert(!MX || (LA == KC && LB == KC && MODE != RAGGED_K), "MXFP8: K-contiguous row-ragged products");
   // FP4: two scale words per row and slice, fetched by lanes 2 r and 2 r + 1
@@ -659,33 +661,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, MxA
         auto chunk = [&](uint32_t base, int row, int c) -> u32x4 {
           return *(const MOE_LDS u32x4*)(uintptr_t)(base + row * 128 + ((c ^ kc_swz(row)) * 16));
         };
+        auto frag = [&](uint32_t base, int row, int st) -> i32x8 {
+          const u32x4 lo = chunk(base, row, st * 4 + h), hi = chunk(base, row, st * 4 + 2 + h);
+          return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        // step 1's fragments go to a second register set, read before step 0's
+        // MFMAs so that the LDS reads can overlap them (iglp_opt(0) below lets
+        // the scheduler interleave the two)
+        i32x8 af[2][FM], bfr[2][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[0][i] = frag(sa, wm * (BM / WM) + i * 32 + (lane & 31), 0);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[0][j] = frag(sb, wn * (BN / WN) + j * 32 + (lane & 31), 0);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          i32x8 af[FM], bfr[FN];
+          if (st == 0) {
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int row = wm * (BM / WM) + i * 32 + (lane & 31);
-            const u32x4 lo = chunk(sa, row, st * 4 + h), hi = chunk(sa, row, st * 4 + 2 + h);
-            af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          }
+            for (int i = 0; i < FM; ++i) af[1][i] = frag(sa, wm * (BM / WM) + i * 32 + (lane & 31), 1);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int row = wn * (BN / WN) + j * 32 + (lane & 31);
-            const u32x4 lo = chunk(sb, row, st * 4 + h), hi = chunk(sb, row, st * 4 + 2 + h);
-            bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            for (int j = 0; j < FN; ++j) bfr[1][j] = frag(sb, wn * (BN / WN) + j * 32 + (lane & 31), 1);
           }
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
               if (st == 0)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0,
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[0][j], af[0][i], acc[i][j], 0, 0, 0,
                                                                             (int)wb[j], 0, (int)wa[i]);
               else
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 2,
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[1][j], af[1][i], acc[i][j], 0, 0, 2,
                                                                             (int)wb[j], 2, (int)wa[i]);
             }
         }
+        __builtin_amdgcn_iglp_opt(0);
       }
       if constexpr (!MX) {
         // A wave whose rows of the tile all lie past m_end (the padding of an
