@@ -235,9 +235,10 @@ GemmExtra gemm_extra(const moe_cfg* c, size_t at, bool bf16_gemms) {
 // quantised activation (codes + scales) and two column-form ones
 struct MxWs {
   int64_t rows_max, cmax_rows, cmax_cols;
-  size_t ints, qa, qt;            // region sizes (qt: one weight-gradient operand, bf16)
+  size_t ints, qa, qt;            // region sizes (qa: one activation's row form; qt: one
+                                  // weight-gradient operand, bf16)
   GemmExtra extra;                // recomputed act, gate-gradient partials (after the others)
-  size_t total() const { return ints + qa + 2 * qt + extra.bytes; }
+  size_t total() const { return ints + 2 * qa + 2 * qt + extra.bytes; }
 };
 MxWs mx_ws(const moe_cfg* c) {
   MxWs w;
@@ -252,7 +253,7 @@ MxWs mx_ws(const moe_cfg* c) {
   w.ints = 2 * align256((size_t)(c->E + 2) * 4);
   w.qa = align256((size_t)(w.rows_max * w.cmax_rows)) + align256((size_t)(w.rows_max * w.cmax_rows / 32));
   w.qt = align256((size_t)(w.rows_max * w.cmax_cols * 2));
-  w.extra = gemm_extra(c, w.ints + w.qa + 2 * w.qt, true);
+  w.extra = gemm_extra(c, w.ints + 2 * w.qa + 2 * w.qt, true);
   return w;
 }
 
@@ -410,7 +411,8 @@ moe_status router_bwd_impl(const moe_cfg* c, const void* x, const void* w_router
 struct MxBufs {
   int* prefix;
   int* bpre;            // 32-row block prefix of the weight gradients' operands
-  uint8_t *qa_c, *qa_s;
+  uint8_t *qa_c, *qa_s;  // row form of a GEMM's activation operand
+  uint8_t *qb_c, *qb_s;  // row form of act / dHU, written by the product that forms them
   void *qd1, *qd2;      // weight-gradient operands, quantised and widened to bf16
   void* act_rec;        // act formed again (recomputation) or NULL
   float* dg_part;       // folded gates' gradient partials or NULL
@@ -424,6 +426,9 @@ MxBufs mx_bufs(const moe_cfg* c, void* ws) {
   p += w.ints;
   b.qa_c = p;
   b.qa_s = p + align256((size_t)(w.rows_max * w.cmax_rows));
+  p += w.qa;
+  b.qb_c = p;
+  b.qb_s = p + align256((size_t)(w.rows_max * w.cmax_rows));
   p += w.qa;
   b.qd1 = p;
   p += w.qt;
@@ -442,23 +447,23 @@ moe_status mx_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off,
   const float* rg = fold(c) ? row_gates : nullptr;
   const int E = (int)c->E, rows = (int)(c->T * c->k), d = (int)c->d, f = (int)c->f, T_ = (int)c->T;
   MxBufs b = mx_bufs(c, ws);
-  const MxQ qa = mxq(b.qa_c, b.qa_s);
+  const MxQ qa = mxq(b.qa_c, b.qa_s), qb = mxq(b.qb_c, b.qb_s);
   if (rows > 0) {
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, fp4, st));
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
+    // the SwiGLU epilogue writes act's row form beside act
     LAUNCH_NAMED("gemm_mx_swiglu_fwd", gemm_mx_swiglu_fwd(qa, off, b.prefix, E, mxq(w->w13), hu, act, rows, d, f, rg, rc,
-                                                          fp4, st));
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act, f, 0, 1, rows, f, b.qa_c, b.qa_s, fp4, st));
-    LAUNCH_NAMED("gemm_mx_down_fwd", gemm_mx_down_fwd(qa, off, b.prefix, E, mxq(w->w2), y_perm, rows, d, f, fp4, st));
+                                                          fp4, b.qb_c, b.qb_s, st));
+    LAUNCH_NAMED("gemm_mx_down_fwd", gemm_mx_down_fwd(qb, off, b.prefix, E, mxq(w->w2), y_perm, rows, d, f, fp4, st));
   }
   if (c->f_shared > 0 && T_ > 0) {
     const int fs = (int)c->f_shared;
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x, d, 0, 1, T_, d, b.qa_c, b.qa_s, fp4, st));
     LAUNCH_NAMED("gemm_mx_swiglu_fwd_shared",
-                 gemm_mx_swiglu_fwd(qa, nullptr, nullptr, 1, mxq(w->ws13), hu_s, act_s, T_, d, fs, nullptr, rc, fp4, st));
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(act_s, fs, 0, 1, T_, fs, b.qa_c, b.qa_s, fp4, st));
+                 gemm_mx_swiglu_fwd(qa, nullptr, nullptr, 1, mxq(w->ws13), hu_s, act_s, T_, d, fs, nullptr, rc, fp4,
+                                    b.qb_c, b.qb_s, st));
     LAUNCH_NAMED("gemm_mx_down_fwd_shared",
-                 gemm_mx_down_fwd(qa, nullptr, nullptr, 1, mxq(w->ws2), y_s, T_, d, fs, fp4, st));
+                 gemm_mx_down_fwd(qb, nullptr, nullptr, 1, mxq(w->ws2), y_s, T_, d, fs, fp4, st));
   }
   return ok();
 }
@@ -476,7 +481,7 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
     act = b.act_rec;
     act_s = b.act_rec;              // (the shared expert's, after the routed experts are done with it)
   }
-  const MxQ qa = mxq(b.qa_c, b.qa_s);
+  const MxQ qa = mxq(b.qa_c, b.qa_s), qb = mxq(b.qb_c, b.qb_s);
   // Weight gradients contract over the rows: both operands are quantised along
   // the rows (32-row blocks restarting at each expert's first row) and widened
   // back to bf16, where every microscaled value is exact, and multiplied by the
@@ -497,7 +502,7 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
     LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd",
                  gemm_mx_down_dgrad_swiglu_bwd(qa, off, b.prefix, E, mxq(w->w2_t), hu, dhu, rows, d, f, rg, b.dg_part,
-                                               b.act_rec, fp4, st));
+                                               b.act_rec, fp4, b.qb_c, b.qb_s, st));
     if (rg)
       LAUNCH_NAMED("gate_grad_sum", launch_gate_grad_sum(b.dg_part, gemm_dg_parts(true, f), row_id_map, rows, d_gates, st));
   }
@@ -505,9 +510,9 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
   LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 32, b.bpre, st));
   CHECK(wgrad(dy_perm, d, act, f, off, E, rows, dw2, 1));
   if (rows > 0) {
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu, 2 * f, 0, 1, rows, 2 * f, b.qa_c, b.qa_s, fp4, st));
+    // (dHU's row form was written by the SwiGLU-backward epilogue)
     LAUNCH_NAMED("gemm_mx_gateup_dgrad",
-                 gemm_mx_gateup_dgrad(qa, off, b.prefix, E, mxq(w->w13_t), dx_perm, false, rows, d, f, fp4, st));
+                 gemm_mx_gateup_dgrad(qb, off, b.prefix, E, mxq(w->w13_t), dx_perm, false, rows, d, f, fp4, st));
   }
   CHECK(wgrad(dhu, 2 * f, x_perm, d, off, E, rows, dw13, 0));
   if (c->f_shared > 0) {
@@ -516,13 +521,12 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
       LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy, d, 0, 1, T_, d, b.qa_c, b.qa_s, fp4, st));
       LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd_shared",
                    gemm_mx_down_dgrad_swiglu_bwd(qa, nullptr, nullptr, 1, mxq(w->ws2_t), hu_s, dhu_s, T_, d, fs, nullptr,
-                                                 nullptr, b.act_rec, fp4, st));
+                                                 nullptr, b.act_rec, fp4, b.qb_c, b.qb_s, st));
     }
     CHECK(wgrad(dy, d, act_s, fs, nullptr, 1, T_, dws2, 3));
     if (T_ > 0) {
-      LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dhu_s, 2 * fs, 0, 1, T_, 2 * fs, b.qa_c, b.qa_s, fp4, st));
       LAUNCH_NAMED("gemm_mx_gateup_dgrad_shared",
-                   gemm_mx_gateup_dgrad(qa, nullptr, nullptr, 1, mxq(w->ws13_t), dx_partial, true, T_, d, fs, fp4, st));
+                   gemm_mx_gateup_dgrad(qb, nullptr, nullptr, 1, mxq(w->ws13_t), dx_partial, true, T_, d, fs, fp4, st));
     }
     CHECK(wgrad(dhu_s, 2 * fs, x, d, nullptr, 1, T_, dws13, 2));
   } else {

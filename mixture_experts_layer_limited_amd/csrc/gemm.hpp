@@ -332,6 +332,7 @@ struct EpiStore {                       // C[row, col] = storage(v)
   // 2-byte outputs may be staged through LDS and stored 8 columns at a time
   static constexpr bool kStaged = sizeof(T) == 2;
   static constexpr bool kAccum = false;
+  static constexpr bool kQuant = false;
   __device__ static void store8(const P& p, int g, int row, int col, u32x4 v) {
     uint16_t* c = (uint16_t*)(p.C + g * p.c_gstride + (int64_t)row * p.ldc + col);
     if (col + 8 <= p.N && (p.ldc & 7) == 0) {
@@ -361,6 +362,7 @@ struct EpiStoreF32T {                   // C[row, col] = v   (fp32 output)
   static constexpr bool kRowDot = false;
   static constexpr bool kStaged = false;
   static constexpr bool kAccum = false;
+  static constexpr bool kQuant = false;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void at(const P& p, int g, int row, int col, float v) {
     if (col < p.N) p.C[g * p.c_gstride + (int64_t)row * p.ldc + col] = v;
@@ -384,6 +386,7 @@ struct EpiAccumF32T {                   // C[row, col] += v  (fp32, one writer p
   // the MFMA kernel reads a 32-row fragment's old values (old4) before it
   // writes any of them (add4), so the reads' latency is paid once per fragment
   static constexpr bool kAccum = true;
+  static constexpr bool kQuant = false;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void at(const P& p, int g, int row, int col, float v) {
     if (col < p.N) {
@@ -426,6 +429,88 @@ struct EpiAccumF32T {                   // C[row, col] += v  (fp32, one writer p
 using EpiStoreF32 = EpiStoreF32T<0>;
 using EpiAccumF32 = EpiAccumF32T<0>;
 
+// ---- MX block quantisation (one e8m0 scale per 32 consecutive values) -----
+// The rule itself is stated where the quantisation kernels are (mxfp8.hip);
+// these are its per-block steps, shared with the GEMM epilogues that emit the
+// row form of their output.
+// smallest e with 448 * 2^e >= amax, clamped to [-127, 127]
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0x1.cp-119f)) return -127;            // amax <= 448 * 2^-127 (or 0)
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)((b >> 23) & 0xFF) - 127;         // amax = m 2^E, m in [1, 2)
+  const int e = (b & 0x7FFFFFu) <= 0x600000u ? E - 8 : E - 7;   // m <= 1.75 : 1.75 2^E >= amax
+  return e > 127 ? 127 : e;
+}
+
+// smallest e with 6 * 2^e >= amax, clamped to [-127, 127]
+__device__ __forceinline__ int mx4_exponent(float amax) {
+  if (!(amax > 0x1.8p-125f)) return -127;            // amax <= 6 * 2^-127 (or 0)
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)((b >> 23) & 0xFF) - 127;         // amax = m 2^E, m in [1, 2)
+  const int e = (b & 0x7FFFFFu) <= 0x400000u ? E - 2 : E - 1;   // m <= 1.5 : 1.5 2^E >= amax
+  return e > 127 ? 127 : e;
+}
+
+// e2m1 codes of v0 (low nibble) and v1 (high nibble) into byte SEL of `old`:
+// each the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with v's sign, ties to the
+// even code, saturating at 6.  gfx950's scaled conversion with scale 1 rounds
+// exactly so (compared value by value, ties and saturation included).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pk(uint32_t old, float v0, float v1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, v0, v1, 1.0f, SEL);
+}
+
+// 16 bf16 values from 8 pairs (element 2i in the low half of word i)
+__device__ __forceinline__ void unpack_bf16x16(const uint32_t w[8], float v[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = bf16_bits_lo(w[i]);
+    v[2 * i + 1] = bf16_bits_hi(w[i]);
+  }
+}
+
+// One block of 32 values of a row held by the lane pair (l, l ^ 32) of a wave,
+// as an MFMA accumulator row holds them: the lane of half h = (l >> 5) & 1 has
+// v[4q + e] = value 8q + 4h + e of the block (q, e = 0..3).  Writes the
+// block's codes at `codes` (fp8: 32 bytes; fp4: 16, element 2i in the low
+// nibble) and, from half 0, its scale byte at `scale`: the codes and scale the
+// row quantiser gives the same 32 values.  Both lanes of the pair must run it.
+__device__ __forceinline__ void mx_quant_pair(const float v[16], bool fp4, uint8_t* codes, uint8_t* scale) {
+  const int h = (int)((threadIdx.x >> 5) & 1);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  // each lane ends with 16 contiguous code bytes (fp4: 8): half 0 the first
+  // 16 values of the block, half 1 the rest, swapping the pieces it lacks
+  if (!fp4) {
+    const int e = mx_exponent(amax);
+    uint32_t w[4];                                     // codes of values 8q + 4h .. +3
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * q], -e), ldexpf(v[4 * q + 1], -e), 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * q + 2], -e), ldexpf(v[4 * q + 3], -e), word, true);
+      w[q] = (uint32_t)word;
+    }
+    const uint32_t r0 = (uint32_t)__shfl_xor((int)(h ? w[0] : w[2]), 32, 64);
+    const uint32_t r1 = (uint32_t)__shfl_xor((int)(h ? w[1] : w[3]), 32, 64);
+    *(u32x4*)(codes + 16 * h) = h ? u32x4{r0, w[2], r1, w[3]} : u32x4{w[0], r0, w[1], r1};
+    if (h == 0) *scale = (uint8_t)(e + 127);
+  } else {
+    const int e = mx4_exponent(amax);
+    uint32_t hw[4];                                    // 16 bits: values 8q + 4h .. +3
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x = e2m1_pk<0>(0u, ldexpf(v[4 * q], -e), ldexpf(v[4 * q + 1], -e));
+      hw[q] = e2m1_pk<1>(x, ldexpf(v[4 * q + 2], -e), ldexpf(v[4 * q + 3], -e));
+    }
+    const uint32_t r = (uint32_t)__shfl_xor((int)(h ? (hw[0] | hw[1] << 16) : (hw[2] | hw[3] << 16)), 32, 64);
+    *(u32x2*)(codes + 8 * h) = h ? u32x2{(r & 0xFFFFu) | hw[2] << 16, (r >> 16) | hw[3] << 16}
+                                 : u32x2{hw[0] | (r & 0xFFFFu) << 16, hw[1] | (r >> 16) << 16};
+    if (h == 0) *scale = (uint8_t)(e + 127);
+  }
+}
+
 // SwiGLU output of one element: silu(h) * u, times the row's gate g when gates
 // are folded.  The forward (with act formed from the stored H, U) and the
 // backward that forms act again both go through this one function, so the two
@@ -447,11 +532,17 @@ struct EpiSwiGLU {
     T* act; T* hu; int64_t f;             // act [rows, f], hu [rows, 2f] or NULL
     const float* row_gates = nullptr;     // gate of each row (folded gates) or NULL
     int from_stored = 0;
+    // the MX row form of act as stored, or NULL: codes [rows, f] (fp4:
+    // [rows, f/2]) and scales [rows, f/32] (MFMA kernel only)
+    uint8_t* q_codes = nullptr;
+    uint8_t* q_scales = nullptr;
+    int q_fp4 = 0;
   };
   static constexpr bool kPaired = true;
   static constexpr bool kStaged = false;
   static constexpr bool kAccum = false;
   static constexpr bool kRowDot = false;
+  static constexpr bool kQuant = true;
   // tile-row r of a BN-row tile split over WN waves: wave part w = r / (BN/WN);
   // its first half are gate rows, its second half the matching up rows
   template <int BN, int WN>
@@ -476,7 +567,14 @@ struct EpiSwiGLU {
       p.hu[(int64_t)row * 2 * p.f + p.f + col] = from_f32<T>(u);
     }
   }
-  __device__ static void at_pair4(const P& p, int row, int col, const float h[4], const float u[4]) {
+  // Q: a_st receives the four act values as stored (zeros past f)
+  template <bool Q>
+  __device__ __forceinline__ static void at_pair4_impl(const P& p, int row, int col, const float h[4],
+                                                       const float u[4], float* a_st) {
+    if constexpr (Q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_st[i] = 0.0f;
+    }
     if (col + 4 > p.f) {
       for (int i = 0; i < 4; ++i) at_pair(p, row, col + i, h[i], u[i]);
       return;
@@ -491,6 +589,24 @@ struct EpiSwiGLU {
       store4<T>(p.hu + (int64_t)row * 2 * p.f + col, h, vec);
       store4<T>(p.hu + (int64_t)row * 2 * p.f + p.f + col, u, vec);
     }
+    if constexpr (Q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_st[i] = through<T>(a[i]);
+    }
+  }
+  __device__ static void at_pair4(const P& p, int row, int col, const float h[4], const float u[4], float a_st[4]) {
+    at_pair4_impl<true>(p, row, col, h, u, a_st);
+  }
+  __device__ static void at_pair4(const P& p, int row, int col, const float h[4], const float u[4]) {
+    at_pair4_impl<false>(p, row, col, h, u, nullptr);
+  }
+  // the MX block of act at columns col0 .. col0 + 31 of `row`: the lane's 16
+  // values of it (mx_quant_pair's layout) as bf16 pairs
+  __device__ static void quant_block(const P& p, int row, int col0, const uint32_t a_st[8]) {
+    float v[16];
+    unpack_bf16x16(a_st, v);
+    uint8_t* codes = p.q_codes + (p.q_fp4 ? (int64_t)row * (p.f / 2) + col0 / 2 : (int64_t)row * p.f + col0);
+    mx_quant_pair(v, p.q_fp4 != 0, codes, p.q_scales + (int64_t)row * (p.f / 32) + col0 / 32);
   }
 };
 
@@ -508,11 +624,17 @@ struct EpiSwiGLUBwd {
     float* dg_part = nullptr;             // [rows, dg_ld] gate-gradient partials (with row_gates)
     int dg_ld = 0;
     T* act_out = nullptr;                 // [rows, f] act formed again, or NULL
+    // the MX row form of dHU as stored (blocks along its 2f columns), or
+    // NULL: codes [rows, 2f] (fp4: [rows, f]) and scales [rows, 2f/32]
+    uint8_t* q_codes = nullptr;
+    uint8_t* q_scales = nullptr;
+    int q_fp4 = 0;
   };
   static constexpr bool kPaired = false;
   static constexpr bool kStaged = false;
   static constexpr bool kAccum = false;
   static constexpr bool kRowDot = true;   // the kernels reduce at's return value when dg_part is set
+  static constexpr bool kQuant = true;
   __device__ static int b_row(const P&, int nt, int r, int BN) { return nt * BN + r; }
   __device__ static void grad(float dA, float h, float u, float& dh, float& du) {
     float sg = 1.0f / (1.0f + expf(-h));
@@ -533,7 +655,14 @@ struct EpiSwiGLUBwd {
     p.dhu[base + p.f + col] = from_f32<T>(du);
     return dot;
   }
-  __device__ static float at4(const P& p, int g_, int row, int col, const float v[4]) {
+  // Q: dh_st, du_st receive the dH and dU values as stored (zeros past f)
+  template <bool Q>
+  __device__ __forceinline__ static float at4_impl(const P& p, int g_, int row, int col, const float v[4],
+                                                   float* dh_st, float* du_st) {
+    if constexpr (Q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dh_st[i] = du_st[i] = 0.0f;
+    }
     if (col + 4 > p.f || (p.f & 3) != 0) {
       float dot = 0.0f;
       for (int i = 0; i < 4; ++i) dot += at(p, g_, row, col + i, v[i]);
@@ -559,7 +688,34 @@ struct EpiSwiGLUBwd {
     for (int i = 0; i < 4; ++i) grad(g * v[i], h[i], u[i], dh[i], du[i]);
     store4<T>(p.dhu + base + col, dh, true);
     store4<T>(p.dhu + base + p.f + col, du, true);
+    if constexpr (Q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dh_st[i] = through<T>(dh[i]);
+        du_st[i] = through<T>(du[i]);
+      }
+    }
     return dot;
+  }
+  __device__ static float at4(const P& p, int g_, int row, int col, const float v[4], float dh_st[4],
+                              float du_st[4]) {
+    return at4_impl<true>(p, g_, row, col, v, dh_st, du_st);
+  }
+  __device__ static float at4(const P& p, int g_, int row, int col, const float v[4]) {
+    return at4_impl<false>(p, g_, row, col, v, nullptr, nullptr);
+  }
+  // the MX blocks of dH and dU at columns col0 .. col0 + 31 of `row` (each
+  // lane's 16 values of each as bf16 pairs)
+  __device__ static void quant_block(const P& p, int row, int col0, const uint32_t dh_st[8], const uint32_t du_st[8]) {
+    const int64_t f2 = 2 * p.f;
+    uint8_t* cr = p.q_codes + (p.q_fp4 ? (int64_t)row * p.f : (int64_t)row * f2);
+    uint8_t* sr = p.q_scales + (int64_t)row * (f2 / 32);
+    const bool fp4 = p.q_fp4 != 0;
+    float v[16];
+    unpack_bf16x16(dh_st, v);
+    mx_quant_pair(v, fp4, cr + (fp4 ? col0 / 2 : col0), sr + col0 / 32);
+    unpack_bf16x16(du_st, v);
+    mx_quant_pair(v, fp4, cr + (fp4 ? (p.f + col0) / 2 : p.f + col0), sr + (p.f + col0) / 32);
   }
 };
 

@@ -485,13 +485,30 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
         if (row < c.m_end) {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
+            // the values as stored (bf16 pairs), for the MX row form of block
+            // j (32 columns); only the MX kernels form it
+            uint32_t qh[8], qu[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int col = nt * BN + wn * (BN / WN) + j * 32 + q * 8 + (lane >> 5) * 4;
               float v[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-              dot += Epi::at4(ep, c.g, row, col, v);
+              if constexpr (Epi::kQuant && MX) {
+                float dh[4], du[4];
+                dot += Epi::at4(ep, c.g, row, col, v, dh, du);
+                qh[2 * q] = pack_bf16x2(dh[0], dh[1]);
+                qh[2 * q + 1] = pack_bf16x2(dh[2], dh[3]);
+                qu[2 * q] = pack_bf16x2(du[0], du[1]);
+                qu[2 * q + 1] = pack_bf16x2(du[2], du[3]);
+              } else {
+                dot += Epi::at4(ep, c.g, row, col, v);
+              }
+            }
+            if constexpr (Epi::kQuant && MX) {
+              // (both lanes of a row's pair are here: the row decides)
+              const int col0 = nt * BN + wn * (BN / WN) + j * 32;
+              if (ep.q_codes && col0 < ep.f) Epi::quant_block(ep, row, col0, qh, qu);
             }
           }
         }
@@ -526,6 +543,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
       if constexpr (Epi::kPaired) {
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {
+          uint32_t qa[8];                       // act as stored (bf16 pairs), for the MX row form
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int col = nt * (BN / 2) + wn * (BN / WN / 2) + j * 32 + q * 8 + (lane >> 5) * 4;
@@ -535,7 +553,18 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
               h[e] = acc[i][j][4 * q + e];
               u[e] = acc[i][j + FN / 2][4 * q + e];
             }
-            Epi::at_pair4(ep, row, col, h, u);
+            if constexpr (Epi::kQuant && MX) {
+              float a[4];
+              Epi::at_pair4(ep, row, col, h, u, a);
+              qa[2 * q] = pack_bf16x2(a[0], a[1]);
+              qa[2 * q + 1] = pack_bf16x2(a[2], a[3]);
+            } else {
+              Epi::at_pair4(ep, row, col, h, u);
+            }
+          }
+          if constexpr (Epi::kQuant && MX) {
+            const int col0 = nt * (BN / 2) + wn * (BN / WN / 2) + j * 32;
+            if (ep.q_codes && col0 < ep.f) Epi::quant_block(ep, row, col0, qa);
           }
         }
       } else {

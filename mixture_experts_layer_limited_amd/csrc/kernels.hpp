@@ -135,15 +135,18 @@ hipError_t launch_mx_quant_both(const void* src, int batch, int R, int C, uint8_
 // 32-row block counts, launch_tile_prefix with 32; off NULL: one group)
 hipError_t launch_mx_qdq_rows(const void* src, int64_t ld, int rows, int C, const int* off, const int* bpre, int G,
                               void* dst, int64_t ldd, bool fp4, hipStream_t st);
+// act_codes / act_scales: the row form of act (blocks of 32 along f) written by
+// the epilogue from the stored act, or NULL
 hipError_t gemm_mx_swiglu_fwd(const MxQ& x, const int* off, const int* prefix, int G, const MxQ& w13, void* hu,
                               void* act, int rows, int d, int f, const float* row_gates, bool from_stored, bool fp4,
-                              hipStream_t st);
+                              uint8_t* act_codes, uint8_t* act_scales, hipStream_t st);
 hipError_t gemm_mx_down_fwd(const MxQ& act, const int* off, const int* prefix, int G, const MxQ& w2, void* y,
                             int rows, int d, int f, bool fp4, hipStream_t st);
+// dhu_codes / dhu_scales: the row form of dHU (blocks of 32 along 2f), or NULL
 hipError_t gemm_mx_down_dgrad_swiglu_bwd(const MxQ& dy, const int* off, const int* prefix, int G,
                                          const MxQ& w2t, const void* hu, void* dhu, int rows, int d, int f,
                                          const float* row_gates, float* dg_part, void* act_out, bool fp4,
-                                         hipStream_t st);
+                                         uint8_t* dhu_codes, uint8_t* dhu_scales, hipStream_t st);
 hipError_t gemm_mx_gateup_dgrad(const MxQ& dhu, const int* off, const int* prefix, int G, const MxQ& w13t,
                                 void* dx, bool f32_out, int rows, int d, int f, bool fp4, hipStream_t st);
 

@@ -30,15 +30,6 @@
 
 namespace moe {
 
-// smallest e with 448 * 2^e >= amax, clamped to [-127, 127]
-__device__ __forceinline__ int mx_exponent(float amax) {
-  if (!(amax > 0x1.cp-119f)) return -127;            // amax <= 448 * 2^-127 (or 0)
-  const uint32_t b = __float_as_uint(amax);
-  const int E = (int)((b >> 23) & 0xFF) - 127;         // amax = m 2^E, m in [1, 2)
-  const int e = (b & 0x7FFFFFu) <= 0x600000u ? E - 8 : E - 7;   // m <= 1.75 : 1.75 2^E >= amax
-  return e > 127 ? 127 : e;
-}
-
 // quantise 32 fp32 values; returns the scale byte
 __device__ __forceinline__ uint32_t mx_block(const float v[32], uint32_t out[8]) {
   float amax = 0.0f;
@@ -56,25 +47,6 @@ __device__ __forceinline__ uint32_t mx_block(const float v[32], uint32_t out[8])
   return (uint32_t)(e + 127);
 }
 
-// smallest e with 6 * 2^e >= amax, clamped to [-127, 127]
-__device__ __forceinline__ int mx4_exponent(float amax) {
-  if (!(amax > 0x1.8p-125f)) return -127;            // amax <= 6 * 2^-127 (or 0)
-  const uint32_t b = __float_as_uint(amax);
-  const int E = (int)((b >> 23) & 0xFF) - 127;         // amax = m 2^E, m in [1, 2)
-  const int e = (b & 0x7FFFFFu) <= 0x400000u ? E - 2 : E - 1;   // m <= 1.5 : 1.5 2^E >= amax
-  return e > 127 ? 127 : e;
-}
-
-// e2m1 code of v (finite): the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to
-// the even code, saturating at 6; the midpoints are exact in fp32
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 3;
-  const float a = fabsf(v);
-  const uint32_t code = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-                      : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
-  return sign | code;
-}
-
 // quantise 32 fp32 values to e2m1 (16 bytes, element 2i in the low nibble);
 // returns the scale byte
 __device__ __forceinline__ uint32_t mx4_block(const float v[32], uint32_t out[4]) {
@@ -84,10 +56,11 @@ __device__ __forceinline__ uint32_t mx4_block(const float v[32], uint32_t out[4]
   const int e = mx4_exponent(amax);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) word |= e2m1_code(ldexpf(v[8 * w + b], -e)) << (4 * b);
-    out[w] = word;
+    const float* x = v + 8 * w;
+    uint32_t word = e2m1_pk<0>(0u, ldexpf(x[0], -e), ldexpf(x[1], -e));
+    word = e2m1_pk<1>(word, ldexpf(x[2], -e), ldexpf(x[3], -e));
+    word = e2m1_pk<2>(word, ldexpf(x[4], -e), ldexpf(x[5], -e));
+    out[w] = e2m1_pk<3>(word, ldexpf(x[6], -e), ldexpf(x[7], -e));
   }
   return (uint32_t)(e + 127);
 }
@@ -285,7 +258,11 @@ __device__ __forceinline__ void qdq_block(float v[32]) {
   const int e = FP4 ? mx4_exponent(amax) : mx_exponent(amax);
   if constexpr (FP4) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = ldexpf(e2m1_value(e2m1_code(ldexpf(v[i], -e))), e);
+    for (int i = 0; i < 32; i += 2) {
+      const uint32_t b = e2m1_pk<0>(0u, ldexpf(v[i], -e), ldexpf(v[i + 1], -e));
+      v[i] = ldexpf(e2m1_value(b & 15u), e);
+      v[i + 1] = ldexpf(e2m1_value((b >> 4) & 15u), e);
+    }
   } else {
     // to the e4m3fn grid and back with the hardware conversions (nearest
     // code, ties to even)
@@ -474,8 +451,9 @@ static hipError_t mx_rows_gemm(const MxQ& q, const int* offsets, const int* pref
 
 hipError_t gemm_mx_swiglu_fwd(const MxQ& x, const int* off, const int* prefix, int G, const MxQ& w13, void* hu,
                               void* act, int rows, int d, int f, const float* row_gates, bool from_stored, bool fp4,
-                              hipStream_t st) {
-  typename EpiSwiGLU<bf16>::P ep{(bf16*)act, (bf16*)hu, f, row_gates, from_stored ? 1 : 0};
+                              uint8_t* act_codes, uint8_t* act_scales, hipStream_t st) {
+  typename EpiSwiGLU<bf16>::P ep{(bf16*)act, (bf16*)hu, f, row_gates, from_stored ? 1 : 0,
+                                 act_codes, act_scales, fp4 ? 1 : 0};
   return mx_rows_gemm<EpiSwiGLU<bf16>>(x, off, prefix, G, w13, (int64_t)2 * f * d, rows, 2 * f, d, ep, f, fp4, st);
 }
 
@@ -489,9 +467,9 @@ hipError_t gemm_mx_down_fwd(const MxQ& act, const int* off, const int* prefix, i
 hipError_t gemm_mx_down_dgrad_swiglu_bwd(const MxQ& dy, const int* off, const int* prefix, int G,
                                          const MxQ& w2t, const void* hu, void* dhu, int rows, int d, int f,
                                          const float* row_gates, float* dg_part, void* act_out, bool fp4,
-                                         hipStream_t st) {
+                                         uint8_t* dhu_codes, uint8_t* dhu_scales, hipStream_t st) {
   typename EpiSwiGLUBwd<bf16>::P ep{(const bf16*)hu, (bf16*)dhu, f, row_gates, row_gates ? dg_part : nullptr,
-                                    gemm_dg_parts(true, f), (bf16*)act_out};
+                                    gemm_dg_parts(true, f), (bf16*)act_out, dhu_codes, dhu_scales, fp4 ? 1 : 0};
   return mx_rows_gemm<EpiSwiGLUBwd<bf16>>(dy, off, prefix, G, w2t, (int64_t)f * d, rows, f, d, ep, f, fp4, st);
 }
 

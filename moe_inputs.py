@@ -13,7 +13,8 @@ pages' own training data is not reported, so every tensor is synthetic):
   deepseek_v3      T=4096 d=7168 E=256 k=8  f=2048  bf16, sigmoid+bias, 8 groups top-4,
                                                      renorm x2.5, shared f=2048, fwd+bwd
   deepseek_v3_skew same as deepseek_v3, Zipf(1.2) skewed bias, MXFP8 expert GEMMs
-                   (deepseek_v3_skew_mxfp4: the same with MXFP4 expert GEMMs)
+                   (deepseek_v3_skew_mxfp4: the same with MXFP4 expert GEMMs;
+                   deepseek_v3_skew_bf16: the same routing with bf16 expert GEMMs)
 
 Distributions ("N(0, v)" read as a variance when v is 1/d or 1/fan_in, as a
 standard deviation when v is 0.02 or 0.01):
@@ -83,13 +84,16 @@ DSV3 = MoEConfig("deepseek_v3", T=4096, d=7168, E=256, k=8, f=2048, f_shared=204
 DSV3_SKEW = DSV3.with_(name="deepseek_v3_skew_mxfp8", dtype="mxfp8", bias="zipf")
 # the same skewed layer with MXFP4 expert GEMMs (e2m1 codes, 1x32 e8m0 scales)
 DSV3_SKEW_MX4 = DSV3.with_(name="deepseek_v3_skew_mxfp4", dtype="mxfp4", bias="zipf")
+# and with bf16 expert GEMMs: the unquantised layer on the same routing
+DSV3_SKEW_BF16 = DSV3.with_(name="deepseek_v3_skew_bf16", bias="zipf")
 # one GPU's share of the DeepSeek-V3 layer under 64-way expert parallelism: 4
 # local experts of 8192 rows each (every token reaches all four), no shared
 # expert; times the expert GEMMs at the per-GPU shape of an EP deployment
 DSV3_EP_SHARE = MoEConfig("deepseek_v3_ep_share", T=8192, d=7168, E=4, k=4, f=2048,
                           backward=True, router_std=0.02, expert_std=0.02)
 
-CONFIGS = {c.name: c for c in (TINY, MIXTRAL, QWEN3, DSV3, DSV3_SKEW, DSV3_SKEW_MX4, DSV3_EP_SHARE)}
+CONFIGS = {c.name: c for c in (TINY, MIXTRAL, QWEN3, DSV3, DSV3_SKEW, DSV3_SKEW_MX4, DSV3_SKEW_BF16,
+                                DSV3_EP_SHARE)}
 
 # tensor ids for per-tensor seeding
 _TID = {"x": 1, "w_router": 2, "bias": 3, "w13": 4, "w2": 5, "ws13": 6,
