@@ -194,10 +194,15 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
   kern<<<(unsigned)device_cus(), C::NTHR, C::LDS_BYTES, st>>>(a, ep, UB, TU, rot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // experts with more rows: the DMA ring, persistent, skipping the others whole
+  // experts with more rows: the DMA ring, persistent, skipping the others
+  // whole, on 256x256 tiles: a CU's operand traffic per flop is what bounds
+  // it, and these take a third less of it than 128x256 tiles (Qwen3, 512 rows
+  // per expert: gate/up 2.88 -> 2.36 ms, down 1.49 -> 1.22 ms).  On experts of
+  // the band kernel's size the same ring is slower than the band (DeepSeek-V3
+  // gate/up 5.13 ms against 3.90).
   GemmArgs big = a;
   big.k_skip = C::KMAX;
-  return launch_mfma<128, 256, 2, 4, 3, MC, MC, RAGGED_K, Epi>(big, ep, a.N, 0, st, true);
+  return launch_mfma<256, 256, 2, 4, 2, MC, MC, RAGGED_K, Epi>(big, ep, a.N, 0, st, true);
 }
 
 // Tile rows of the ragged-row schedule.  The device tile prefix is built with
