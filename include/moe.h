@@ -379,9 +379,22 @@ int moe_trace_end(const char** names, float* ms, int capacity);
 typedef enum moe_mx_orientation {
   MOE_MX_ROWS = 0,  /* blocks along the contiguous dimension: codes [B][R][C],
                        scales [B][R][C/32]; C % 32 == 0                        */
-  MOE_MX_COLS = 1   /* transposed copy, blocks along R: codes [B][C][R],
+  MOE_MX_COLS = 1,  /* transposed copy, blocks along R: codes [B][C][R],
                        scales [B][C][R/32]; R % 32 == 0, C % 8 == 0            */
+  MOE_MX_GROUPED = 2 /* flag (OR-ed into the orientation, or the `flags` of the
+                       _both calls): scales in the grouped layout below       */
 } moe_mx_orientation;
+
+/* Grouped scale layout.  For a quantised matrix of R' rows (R for
+ * MOE_MX_ROWS, C for MOE_MX_COLS) with nb blocks of 32 per row (nb a multiple
+ * of 4: the blocked dimension a multiple of 128), the four scales of blocks
+ * 4q .. 4q+3 of row r form one 4-byte word, and word (q, r) is at index
+ * q * R' + r: the scale of block b of row r is byte 4 (floor(b/4) R' + r) +
+ * b % 4 of the matrix's R' nb bytes (a batch's matrices follow each other as
+ * in the plain layout).  Codes are unchanged.  The microscaled layer calls
+ * read the expert weights' scales in this layout: a slice of 128 fp8 (256
+ * fp4) values along K is one (two) word(s) per row, and a tile's rows then
+ * fetch adjacent words. */
 
 /* Quantises `batch` row-major bf16 matrices src [batch][rows][cols] in the
  * given orientation.  codes 16-byte aligned; rows * cols < 2^31; batch <=
@@ -390,13 +403,14 @@ moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int6
                               int32_t orientation, uint8_t* codes, uint8_t* scales, void* stream);
 
 /* Both orientations of the same matrices in one pass, each bf16 value read
- * once: codes_rows / scales_rows exactly as MOE_MX_ROWS, codes_cols /
- * scales_cols exactly as MOE_MX_COLS would give them.  rows and cols
+ * once: codes_rows / scales_rows exactly as MOE_MX_ROWS | flags, codes_cols /
+ * scales_cols exactly as MOE_MX_COLS | flags would give them.  flags: 0 or
+ * MOE_MX_GROUPED (then rows and cols multiples of 128).  rows and cols
  * multiples of 32; other limits and errors as moe_quantize_mxfp8.  For the
  * callers that quantise expert weights (both forms, once per update). */
 moe_status moe_quantize_mxfp8_both(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                    uint8_t* codes_rows, uint8_t* scales_rows, uint8_t* codes_cols,
-                                   uint8_t* scales_cols, void* stream);
+                                   uint8_t* scales_cols, int32_t flags, void* stream);
 
 /* One quantised operand (device memory): codes 16-byte, scales 4-byte aligned. */
 typedef struct moe_mx_tensor {
@@ -405,14 +419,16 @@ typedef struct moe_mx_tensor {
 } moe_mx_tensor;
 
 /* Expert weights for the MXFP8 calls, each in the orientation its GEMM
- * contracts (MOE_MX_ROWS of the tensor named, or of its per-expert transpose):
+ * contracts (MOE_MX_ROWS of the tensor named, or of its per-expert transpose),
+ * scales in the grouped layout (MOE_MX_GROUPED):
  *   w13   codes [E][2f][d]  scales [E][2f][d/32]   forward gate/up (along d)
  *   w2    codes [E][d][f]   scales [E][d][f/32]    forward down (along f)
  *   w13_t codes [E][d][2f]  scales [E][d][2f/32]   dX = dHU W13 (along 2f)
  *   w2_t  codes [E][f][d]   scales [E][f][d/32]    dA = dY W2 (along d)
  *   ws13, ws2, ws13_t, ws2_t: the shared expert's, same layouts without [E]
  *                                        (ignored when f_shared = 0)
- * w13_t and w2_t are moe_quantize_mxfp8(w, E, rows, cols, MOE_MX_COLS). */
+ * w13 and w13_t are moe_quantize_mxfp8_both(w13, E, 2f, d, ..., MOE_MX_GROUPED)
+ * (w13_t alone: moe_quantize_mxfp8(w13, E, 2f, d, MOE_MX_COLS | MOE_MX_GROUPED)). */
 typedef struct moe_mx_weights {
   moe_mx_tensor w13, w2, w13_t, w2_t;
   moe_mx_tensor ws13, ws2, ws13_t, ws2_t;
@@ -476,7 +492,7 @@ moe_status moe_quantize_mxfp4(const void* src, int64_t batch, int64_t rows, int6
 /* moe_quantize_mxfp8_both with e2m1 codes (two per byte) */
 moe_status moe_quantize_mxfp4_both(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                    uint8_t* codes_rows, uint8_t* scales_rows, uint8_t* codes_cols,
-                                   uint8_t* scales_cols, void* stream);
+                                   uint8_t* scales_cols, int32_t flags, void* stream);
 
 /* moe_grouped_gemm_swiglu_mxfp8 and moe_grouped_gemm_swiglu_bwd_mxfp8 with
  * MXFP4 operands (cfg.dtype = MOE_MXFP4; d, f, f_shared multiples of 256, one

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_gfx9
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
 MOE_F32, MOE_BF16, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2, 3
-MOE_MX_ROWS, MOE_MX_COLS = 0, 1
+MOE_MX_ROWS, MOE_MX_COLS, MOE_MX_GROUPED = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_FLAG_FORCE_BALANCED, MOE_FLAG_FOLD_GATES, MOE_FLAG_RECOMPUTE_ACT = 1, 2, 4
 
@@ -73,8 +73,10 @@ _SIGS = {
                                           + [_P, ctypes.c_size_t, _P]),
     "moe_quantize_mxfp4": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                           _P, _P, _P]),
-    "moe_quantize_mxfp8_both": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + [_P] * 5),
-    "moe_quantize_mxfp4_both": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + [_P] * 5),
+    "moe_quantize_mxfp8_both": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + [_P] * 4
+                                + [ctypes.c_int32, _P]),
+    "moe_quantize_mxfp4_both": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + [_P] * 4
+                                + [ctypes.c_int32, _P]),
     "moe_grouped_gemm_swiglu_mxfp4": (ctypes.c_int, [ctypes.POINTER(moe_cfg), _P, _P, _P,
                                                      ctypes.POINTER(moe_mx_weights)] + [_P] * 7
                                       + [_P, ctypes.c_size_t, _P]),
@@ -285,16 +287,18 @@ def moe_quantize_mxfp4(src, batch, rows, cols, orientation, codes, scales, strea
                                     _ptr(scales, _U8), _stream(stream)), "moe_quantize_mxfp4")
 
 
-def moe_quantize_mxfp8_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, stream=None):
+def moe_quantize_mxfp8_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, flags=0,
+                            stream=None):
     _check(lib().moe_quantize_mxfp8_both(_ptr(src, torch.bfloat16), batch, rows, cols, _ptr(codes_rows, _U8),
                                          _ptr(scales_rows, _U8), _ptr(codes_cols, _U8), _ptr(scales_cols, _U8),
-                                         _stream(stream)), "moe_quantize_mxfp8_both")
+                                         flags, _stream(stream)), "moe_quantize_mxfp8_both")
 
 
-def moe_quantize_mxfp4_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, stream=None):
+def moe_quantize_mxfp4_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, flags=0,
+                            stream=None):
     _check(lib().moe_quantize_mxfp4_both(_ptr(src, torch.bfloat16), batch, rows, cols, _ptr(codes_rows, _U8),
                                          _ptr(scales_rows, _U8), _ptr(codes_cols, _U8), _ptr(scales_cols, _U8),
-                                         _stream(stream)), "moe_quantize_mxfp4_both")
+                                         flags, _stream(stream)), "moe_quantize_mxfp4_both")
 
 
 def mx_weights(**tensors) -> moe_mx_weights:

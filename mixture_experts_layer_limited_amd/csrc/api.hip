@@ -449,7 +449,7 @@ moe_status mx_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off,
   MxBufs b = mx_bufs(c, ws);
   const MxQ qa = mxq(b.qa_c, b.qa_s), qb = mxq(b.qb_c, b.qb_s);
   if (rows > 0) {
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, fp4, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, fp4, true, st));
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
     // the SwiGLU epilogue writes act's row form beside act
     LAUNCH_NAMED("gemm_mx_swiglu_fwd", gemm_mx_swiglu_fwd(qa, off, b.prefix, E, mxq(w->w13), hu, act, rows, d, f, rg, rc,
@@ -458,7 +458,7 @@ moe_status mx_fwd_impl(const moe_cfg* c, const void* x_perm, const int32_t* off,
   }
   if (c->f_shared > 0 && T_ > 0) {
     const int fs = (int)c->f_shared;
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x, d, 0, 1, T_, d, b.qa_c, b.qa_s, fp4, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(x, d, 0, 1, T_, d, b.qa_c, b.qa_s, fp4, true, st));
     LAUNCH_NAMED("gemm_mx_swiglu_fwd_shared",
                  gemm_mx_swiglu_fwd(qa, nullptr, nullptr, 1, mxq(w->ws13), hu_s, act_s, T_, d, fs, nullptr, rc, fp4,
                                     b.qb_c, b.qb_s, st));
@@ -498,7 +498,7 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
     return ok();
   };
   if (rows > 0) {
-    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, fp4, st));
+    LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy_perm, d, 0, 1, rows, d, b.qa_c, b.qa_s, fp4, true, st));
     LAUNCH_NAMED("tile_prefix", launch_tile_prefix(off, E, 128, b.prefix, st));
     LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd",
                  gemm_mx_down_dgrad_swiglu_bwd(qa, off, b.prefix, E, mxq(w->w2_t), hu, dhu, rows, d, f, rg, b.dg_part,
@@ -518,7 +518,7 @@ moe_status mx_bwd_impl(const moe_cfg* c, const void* dy_perm, const void* x_perm
   if (c->f_shared > 0) {
     const int fs = (int)c->f_shared;
     if (T_ > 0) {
-      LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy, d, 0, 1, T_, d, b.qa_c, b.qa_s, fp4, st));
+      LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(dy, d, 0, 1, T_, d, b.qa_c, b.qa_s, fp4, true, st));
       LAUNCH_NAMED("gemm_mx_down_dgrad_swiglu_bwd_shared",
                    gemm_mx_down_dgrad_swiglu_bwd(qa, nullptr, nullptr, 1, mxq(w->ws2_t), hu_s, dhu_s, T_, d, fs, nullptr,
                                                  nullptr, b.act_rec, fp4, b.qb_c, b.qb_s, st));
@@ -873,8 +873,13 @@ static moe_status quantize_mx(const void* src, int64_t batch, int64_t rows, int6
   if (batch < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "negative size");
   if (batch > 65535) return fail(MOE_ERR_INVALID_ARGUMENT, "batch = %lld above 65535", (long long)batch);
   if (rows * cols >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "rows * cols must stay below 2^31");
+  const bool grouped = (orientation & MOE_MX_GROUPED) != 0;
+  orientation &= ~MOE_MX_GROUPED;
   if (orientation != MOE_MX_ROWS && orientation != MOE_MX_COLS)
     return fail(MOE_ERR_INVALID_ARGUMENT, "orientation %d unknown", orientation);
+  if (grouped && (orientation == MOE_MX_ROWS ? cols : rows) % 128)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "grouped scales need the blocked dimension %% 128 == 0 (%lld x %lld)",
+                (long long)rows, (long long)cols);
   if (orientation == MOE_MX_ROWS && cols % 32)
     return fail(MOE_ERR_INVALID_ARGUMENT, "row orientation needs cols %% 32 == 0 (cols = %lld)", (long long)cols);
   if (orientation == MOE_MX_COLS && (rows % 32 || cols % 8))
@@ -884,10 +889,10 @@ static moe_status quantize_mx(const void* src, int64_t batch, int64_t rows, int6
   hipStream_t st = (hipStream_t)stream;
   if (orientation == MOE_MX_ROWS)
     LAUNCH_NAMED("mx_quant_rows", launch_mx_quant_rows(src, cols, rows * cols, (int)batch, (int)rows, (int)cols,
-                                                       codes, scales, fp4, st));
+                                                       codes, scales, fp4, grouped, st));
   else
     LAUNCH_NAMED("mx_quant_cols", launch_mx_quant_cols_batched(src, (int)batch, (int)rows, (int)cols, codes,
-                                                               scales, fp4, st));
+                                                               scales, fp4, grouped, st));
   return ok();
 }
 
@@ -897,30 +902,40 @@ moe_status moe_quantize_mxfp8(const void* src, int64_t batch, int64_t rows, int6
 }
 
 static moe_status quantize_mx_both(const void* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes_r,
-                                   uint8_t* scales_r, uint8_t* codes_c, uint8_t* scales_c, bool fp4, void* stream) {
+                                   uint8_t* scales_r, uint8_t* codes_c, uint8_t* scales_c, int32_t flags, bool fp4,
+                                   void* stream) {
   REQ(src); REQ(codes_r); REQ(scales_r); REQ(codes_c); REQ(scales_c);
   ALIGNED(src); ALIGNED(codes_r); ALIGNED(codes_c);
   if (batch < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "negative size");
   if (batch > 65535) return fail(MOE_ERR_INVALID_ARGUMENT, "batch = %lld above 65535", (long long)batch);
   if (rows * cols >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "rows * cols must stay below 2^31");
+  if (flags != 0 && flags != MOE_MX_GROUPED) return fail(MOE_ERR_INVALID_ARGUMENT, "flags %d unknown", flags);
+  const bool grouped = flags == MOE_MX_GROUPED;
   if (rows % 32 || cols % 32)
     return fail(MOE_ERR_INVALID_ARGUMENT, "both orientations need rows and cols multiples of 32 (%lld x %lld)",
+                (long long)rows, (long long)cols);
+  if (grouped && (rows % 128 || cols % 128))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "grouped scales need rows and cols multiples of 128 (%lld x %lld)",
                 (long long)rows, (long long)cols);
   CHECK(check_current_device());
   hipStream_t st = (hipStream_t)stream;
   LAUNCH_NAMED("mx_quant_both", launch_mx_quant_both(src, (int)batch, (int)rows, (int)cols, codes_r, scales_r,
-                                                     codes_c, scales_c, fp4, st));
+                                                     codes_c, scales_c, fp4, grouped, st));
   return ok();
 }
 
 moe_status moe_quantize_mxfp8_both(const void* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes_rows,
-                                   uint8_t* scales_rows, uint8_t* codes_cols, uint8_t* scales_cols, void* stream) {
-  return quantize_mx_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, false, stream);
+                                   uint8_t* scales_rows, uint8_t* codes_cols, uint8_t* scales_cols, int32_t flags,
+                                   void* stream) {
+  return quantize_mx_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, flags, false,
+                          stream);
 }
 
 moe_status moe_quantize_mxfp4_both(const void* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes_rows,
-                                   uint8_t* scales_rows, uint8_t* codes_cols, uint8_t* scales_cols, void* stream) {
-  return quantize_mx_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, true, stream);
+                                   uint8_t* scales_rows, uint8_t* codes_cols, uint8_t* scales_cols, int32_t flags,
+                                   void* stream) {
+  return quantize_mx_both(src, batch, rows, cols, codes_rows, scales_rows, codes_cols, scales_cols, flags, true,
+                          stream);
 }
 
 moe_status moe_quantize_mxfp4(const void* src, int64_t batch, int64_t rows, int64_t cols, int32_t orientation,

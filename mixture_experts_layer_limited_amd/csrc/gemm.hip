@@ -156,7 +156,7 @@ static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int 
   auto kern = gemm_pipe_kernel<LA, LB, MODE, Epi, BK>;
   static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
   if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
-  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, MxArgs{}, ep, NT, MT);
+  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, ep, NT, MT);
   return hipGetLastError();
 }
 

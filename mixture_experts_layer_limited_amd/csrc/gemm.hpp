@@ -150,10 +150,21 @@ __device__ __forceinline__ int xcd_run_start(const GemmArgs& a, const int* off, 
 // scale of (row, block b) comes from lane row + 32 b, so each lane passes the
 // scale of block h of its own row; a row's scale word holds the slice's four
 // block scales, shifted by 8 h per lane, and op_sel picks byte 2 s for step s.
+// Scale layouts of a quantised matrix of R rows with nb blocks (of 32 values)
+// per row.  Plain: the scale of block b of row r at byte r nb + b.  Grouped
+// (nb a multiple of 4): the scales of blocks 4q .. 4q+3 of a row form one
+// 4-byte word, and the words of group q for rows 0 .. R-1 are consecutive:
+// byte 4 (q R + r) + b % 4.  A GEMM slice of 128 fp8 (or 256 fp4) values then
+// needs one (two) such words per row, and the words of a tile's rows are
+// adjacent in memory.
+__host__ __device__ __forceinline__ int64_t mx_scale_at(int64_t r, int b, int64_t R, int nb, bool grouped) {
+  return grouped ? ((int64_t)(b >> 2) * R + r) * 4 + (b & 3) : r * nb + b;
+}
+
 struct MxArgs {
-  const uint8_t* A_s;      // A scales [..][K/32]
-  const uint8_t* B_s;      // B scales (per group: + g * b_s_gstride)
-  int64_t a_s_ld, b_s_ld;  // scale row strides (bytes)
+  const uint8_t* A_s;      // A scales, grouped over a_rows rows
+  const uint8_t* B_s;      // B scales, grouped over b_rows rows (per group: + g * b_s_gstride)
+  int64_t a_rows, b_rows;
   int64_t b_s_gstride;
 };
 
@@ -535,8 +546,9 @@ struct EpiSwiGLU {
     // the MX row form of act as stored, or NULL: codes [rows, f] (fp4:
     // [rows, f/2]) and scales [rows, f/32] (MFMA kernel only)
     uint8_t* q_codes = nullptr;
-    uint8_t* q_scales = nullptr;
+    uint8_t* q_scales = nullptr;          // grouped over q_rows rows
     int q_fp4 = 0;
+    int64_t q_rows = 0;
   };
   static constexpr bool kPaired = true;
   static constexpr bool kStaged = false;
@@ -606,7 +618,7 @@ struct EpiSwiGLU {
     float v[16];
     unpack_bf16x16(a_st, v);
     uint8_t* codes = p.q_codes + (p.q_fp4 ? (int64_t)row * (p.f / 2) + col0 / 2 : (int64_t)row * p.f + col0);
-    mx_quant_pair(v, p.q_fp4 != 0, codes, p.q_scales + (int64_t)row * (p.f / 32) + col0 / 32);
+    mx_quant_pair(v, p.q_fp4 != 0, codes, p.q_scales + mx_scale_at(row, col0 / 32, p.q_rows, (int)(p.f / 32), true));
   }
 };
 
@@ -625,10 +637,11 @@ struct EpiSwiGLUBwd {
     int dg_ld = 0;
     T* act_out = nullptr;                 // [rows, f] act formed again, or NULL
     // the MX row form of dHU as stored (blocks along its 2f columns), or
-    // NULL: codes [rows, 2f] (fp4: [rows, f]) and scales [rows, 2f/32]
+    // NULL: codes [rows, 2f] (fp4: [rows, f]) and scales grouped over q_rows rows
     uint8_t* q_codes = nullptr;
     uint8_t* q_scales = nullptr;
     int q_fp4 = 0;
+    int64_t q_rows = 0;
   };
   static constexpr bool kPaired = false;
   static constexpr bool kStaged = false;
@@ -709,13 +722,14 @@ struct EpiSwiGLUBwd {
   __device__ static void quant_block(const P& p, int row, int col0, const uint32_t dh_st[8], const uint32_t du_st[8]) {
     const int64_t f2 = 2 * p.f;
     uint8_t* cr = p.q_codes + (p.q_fp4 ? (int64_t)row * p.f : (int64_t)row * f2);
-    uint8_t* sr = p.q_scales + (int64_t)row * (f2 / 32);
     const bool fp4 = p.q_fp4 != 0;
+    const int nb = (int)(f2 / 32);
     float v[16];
     unpack_bf16x16(dh_st, v);
-    mx_quant_pair(v, fp4, cr + (fp4 ? col0 / 2 : col0), sr + col0 / 32);
+    mx_quant_pair(v, fp4, cr + (fp4 ? col0 / 2 : col0), p.q_scales + mx_scale_at(row, col0 / 32, p.q_rows, nb, true));
     unpack_bf16x16(du_st, v);
-    mx_quant_pair(v, fp4, cr + (fp4 ? (p.f + col0) / 2 : p.f + col0), sr + (p.f + col0) / 32);
+    mx_quant_pair(v, fp4, cr + (fp4 ? (p.f + col0) / 2 : p.f + col0),
+                  p.q_scales + mx_scale_at(row, (int)((p.f + col0) / 32), p.q_rows, nb, true));
   }
 };
 

@@ -325,10 +325,13 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
   const void* rb_base = nullptr;
   uint32_t ra_bytes = 0, rb_bytes = 0;
   uint32_t soa = 0, sob = 0;
-  // MX: scale-word resources, per-lane offsets and the slice's byte offset
+  // MX: scale-word resources, per-lane offsets and the slice's byte offsets
   const uint8_t* rsa_base = nullptr;
   const uint8_t* rsb_base = nullptr;
-  uint32_t rsa_bytes = 0, rsb_bytes = 0, sa_off = kOffRange, sb_off = kOffRange, sos = 0;
+  uint32_t rsa_bytes = 0, rsb_bytes = 0, sa_off = kOffRange, sb_off = kOffRange, sosa = 0, sosb = 0;
+  // grouped scale words per slice: one (fp8, 128 values) or two (fp4, 256)
+  constexpr int kWordsPerSlice = FP4 ? 2 : 1;
+  const int nb = MX ? a.K / (FP4 ? 8 : 16) : 0;     // blocks of 32 values along K (K in 2-byte units)
   const uint32_t stride_a = LA == KC ? BK * 2 : (uint32_t)(BK * a.lda * 2);
   const uint32_t stride_b = LB == KC ? BK * 2 : (uint32_t)(BK * a.ldb * 2);
 
@@ -368,26 +371,31 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
     soa = LA == KC ? (uint32_t)(c.k_begin * 2) : 0u;
     sob = LB == KC ? (uint32_t)(c.k_begin * 2) : 0u;
     if constexpr (MX) {
-      // lane q = wave*64 + lane fetches the scale word of tile row q (A) and
-      // of B row q (its weight row), or nothing (an offset outside the range)
+      // lane q = wave*64 + lane fetches the slice's scale word of tile row q
+      // (A) and of B row q (its weight row), or nothing (an offset outside the
+      // range); fp4: word q & 1 of row q >> 1.  In the grouped layout the
+      // words of consecutive rows are adjacent: a slice's words for a tile are
+      // a few contiguous lines.
       const int q = wave * 64 + lane;
       const int nrows = min(c.m_end - c.m0, BM);
-      // fp8: lane q fetches the slice's word of row q; fp4: word q & 1 of row q >> 1
       const int qr = FP4 ? q >> 1 : q;
-      const uint32_t qw = FP4 ? (uint32_t)(q & 1) * 4 : 0u;
-      rsa_base = s.A_s + (int64_t)c.m0 * s.a_s_ld;
-      rsa_bytes = (uint32_t)(nrows * s.a_s_ld);
-      sa_off = qr < nrows ? (uint32_t)(qr * s.a_s_ld) + qw : kOffRange;
+      const uint32_t ga = FP4 ? (uint32_t)(q & 1) * (uint32_t)s.a_rows * 4 : 0u;
+      const uint32_t gb = FP4 ? (uint32_t)(q & 1) * (uint32_t)s.b_rows * 4 : 0u;
+      rsa_base = s.A_s;
+      rsa_bytes = (uint32_t)(s.a_rows * nb);
+      sa_off = qr < nrows ? (uint32_t)((c.m0 + qr) * 4) + ga : kOffRange;
       rsb_base = s.B_s + (MODE == RAGGED_M ? (int64_t)c.g * s.b_s_gstride : 0);
-      rsb_bytes = (uint32_t)((int64_t)a.b_next * s.b_s_ld);
+      rsb_bytes = (uint32_t)(s.b_rows * nb);
       int g = -1;
       if (qr < BN) {
         if constexpr (Epi::kPaired) g = Epi::template b_row_paired<BN, WN>(ep, nt, qr);
         else g = nt * BN + qr;
       }
-      sb_off = (g >= 0 && g < a.b_next) ? (uint32_t)((int64_t)g * s.b_s_ld) + qw : kOffRange;
-      // 2-byte units -> scale bytes (one per 32 values: 16 units of fp8, 8 of fp4)
-      sos = (uint32_t)(c.k_begin / (FP4 ? 8 : 16));
+      sb_off = (g >= 0 && g < a.b_next) ? (uint32_t)(g * 4) + gb : kOffRange;
+      // the tile's first slice: group (k_begin / BK) * kWordsPerSlice
+      const uint32_t g0 = (uint32_t)(c.k_begin / BK) * kWordsPerSlice;
+      sosa = g0 * (uint32_t)s.a_rows * 4;
+      sosb = g0 * (uint32_t)s.b_rows * 4;
     }
   };
   auto issue = [&](int stage) {
@@ -400,12 +408,13 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
 #if defined(__HIP_DEVICE_COMPILE__)
       const uint32_t sc = sbase + C::A_BYTES + C::B_BYTES + wave * 64 * 4;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(rsa_base, rsa_bytes), (MOE_LDS void*)(uintptr_t)sc, 4,
-                                               sa_off, sos, 0, 0);
+                                               sa_off, sosa, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(rsb_base, rsb_bytes),
-                                               (MOE_LDS void*)(uintptr_t)(sc + C::SC_WORDS * 4), 4, sb_off, sos, 0,
+                                               (MOE_LDS void*)(uintptr_t)(sc + C::SC_WORDS * 4), 4, sb_off, sosb, 0,
                                                0);
 #endif
-      sos += FP4 ? BK / 8 : BK / 16;                // scale bytes per slice: 8 (256 fp4), 4 (128 fp8)
+      sosa += kWordsPerSlice * (uint32_t)s.a_rows * 4;   // the next slice's group(s)
+      sosb += kWordsPerSlice * (uint32_t)s.b_rows * 4;
     }
   };
 

@@ -123,13 +123,15 @@ struct MxQ {                            // codes and e8m0 scales of one quantise
   const uint8_t* codes;
   const uint8_t* scales;
 };
+// grouped: scales in the grouped layout (mx_scale_at; the blocked dimension
+// a multiple of 128), else plain
 hipError_t launch_mx_quant_rows(const void* src, int64_t ld, int64_t src_bstride, int batch, int R, int C,
-                                uint8_t* codes, uint8_t* scales, bool fp4, hipStream_t st);
+                                uint8_t* codes, uint8_t* scales, bool fp4, bool grouped, hipStream_t st);
 hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C, uint8_t* codes,
-                                        uint8_t* scales, bool fp4, hipStream_t st);
+                                        uint8_t* scales, bool fp4, bool grouped, hipStream_t st);
 // both forms of [batch][R][C] in one pass (R and C multiples of 32)
 hipError_t launch_mx_quant_both(const void* src, int batch, int R, int C, uint8_t* codes_r, uint8_t* scales_r,
-                                uint8_t* codes_c, uint8_t* scales_c, bool fp4, hipStream_t st);
+                                uint8_t* codes_c, uint8_t* scales_c, bool fp4, bool grouped, hipStream_t st);
 // dst [rows][ldd] bf16 = the microscaled values of src [rows][ld] with 32-row
 // blocks per column, restarting at each group's first row (bpre: cumulative
 // 32-row block counts, launch_tile_prefix with 32; off NULL: one group)

@@ -73,7 +73,7 @@ template <bool FP4>
 __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __restrict__ src, int64_t ld,
                                                             int64_t src_bstride, int R, int C,
                                                             uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales) {
+                                                            uint8_t* __restrict__ scales, bool grouped) {
   const int nb = C / 32;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= (int64_t)R * nb) return;
@@ -102,18 +102,21 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __re
     q[0] = u32x4{out[0], out[1], out[2], out[3]};
     q[1] = u32x4{out[4], out[5], out[6], out[7]};
   }
-  scales[(bt * R + r) * (int64_t)nb + b] = (uint8_t)sb;
+  scales[bt * R * (int64_t)nb + mx_scale_at(r, b, R, nb, grouped)] = (uint8_t)sb;
 }
 
 hipError_t launch_mx_quant_rows(const void* src, int64_t ld, int64_t src_bstride, int batch, int R, int C,
-                                uint8_t* codes, uint8_t* scales, bool fp4, hipStream_t st) {
+                                uint8_t* codes, uint8_t* scales, bool fp4, bool grouped, hipStream_t st) {
   const int64_t n = (int64_t)R * (C / 32);
   if (n == 0 || batch == 0) return hipSuccess;
+  if (grouped && C % 128) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((n + 255) / 256), batch);
   if (fp4)
-    mx_quant_rows_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, src_bstride, R, C, codes, scales);
+    mx_quant_rows_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, src_bstride, R, C, codes, scales,
+                                                     grouped);
   else
-    mx_quant_rows_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, src_bstride, R, C, codes, scales);
+    mx_quant_rows_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, ld, src_bstride, R, C, codes, scales,
+                                                      grouped);
   return hipGetLastError();
 }
 
@@ -137,7 +140,8 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
                                                             int rows, int C, int64_t ldq,
                                                             int rp_limit, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, int64_t z_src,
-                                                            int64_t z_codes, uint8_t* __restrict__ codes_r = nullptr,
+                                                            int64_t z_codes, bool grouped,
+                                                            uint8_t* __restrict__ codes_r = nullptr,
                                                             uint8_t* __restrict__ scales_r = nullptr) {
   __shared__ uint16_t tile[kQcRows][kQcCols];
   // grid z: independent matrices (a batch of weights), z_src elements and
@@ -189,7 +193,8 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
         q[0] = u32x4{out[0], out[1], out[2], out[3]};
         q[1] = u32x4{out[4], out[5], out[6], out[7]};
       }
-      scales_r[row * (C / 32) + cb / 32] = (uint8_t)sb;
+      scales_r[(int64_t)blockIdx.z * rows * (C / 32) + mx_scale_at(src0 + r, cb / 32, rows, C / 32, grouped)] =
+          (uint8_t)sb;
     }
   }
   // wave w takes columns 16w .. 16w+15 and lane (4j + b) block b of column
@@ -214,21 +219,22 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
     q[0] = u32x4{out[0], out[1], out[2], out[3]};
     q[1] = u32x4{out[4], out[5], out[6], out[7]};
   }
-  scales[(int64_t)(c0 + c) * (ldq / 32) + rb / 32] = (uint8_t)sb;
+  // (the column form's rows are the C columns, blocks along ldq)
+  scales[mx_scale_at(c0 + c, rb / 32, C, (int)(ldq / 32), grouped)] = (uint8_t)sb;
 }
 
 hipError_t launch_mx_quant_both(const void* src, int batch, int R, int C, uint8_t* codes_r, uint8_t* scales_r,
-                                uint8_t* codes_c, uint8_t* scales_c, bool fp4, hipStream_t st) {
+                                uint8_t* codes_c, uint8_t* scales_c, bool fp4, bool grouped, hipStream_t st) {
   if (batch == 0 || R == 0 || C == 0) return hipSuccess;
-  if (R % 32 || C % 32) return hipErrorInvalidValue;
+  if (R % 32 || C % 32 || (grouped && (R % 128 || C % 128))) return hipErrorInvalidValue;
   const dim3 grid((R + kQcRows - 1) / kQcRows, (C + kQcCols - 1) / kQcCols, batch);
   const int64_t z = (int64_t)R * C;
   if (fp4)
     mx_quant_cols_kernel<true, true><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, R, R, codes_c, scales_c, z, z,
-                                                           codes_r, scales_r);
+                                                           grouped, codes_r, scales_r);
   else
     mx_quant_cols_kernel<false, true><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, R, R, codes_c, scales_c, z,
-                                                            z, codes_r, scales_r);
+                                                            z, grouped, codes_r, scales_r);
   return hipGetLastError();
 }
 
@@ -342,16 +348,17 @@ hipError_t launch_mx_qdq_rows(const void* src, int64_t ld, int rows, int C, cons
 // one launch with the batch in the grid's z dimension (one launch per matrix
 // took 8.9 ms for 256 matrices of 4096 x 7168, dominated by launch and drain)
 hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C, uint8_t* codes,
-                                        uint8_t* scales, bool fp4, hipStream_t st) {
+                                        uint8_t* scales, bool fp4, bool grouped, hipStream_t st) {
   if (batch == 0 || R == 0 || C == 0) return hipSuccess;
+  if (grouped && R % 128) return hipErrorInvalidValue;
   const int tiles = (R + kQcRows - 1) / kQcRows;
   const dim3 grid(tiles, (C + kQcCols - 1) / kQcCols, batch);
   if (fp4)
     mx_quant_cols_kernel<true><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, R, R,
-                                                     codes, scales, (int64_t)R * C, (int64_t)R * C);
+                                                     codes, scales, (int64_t)R * C, (int64_t)R * C, grouped);
   else
     mx_quant_cols_kernel<false><<<grid, 256, 0, st>>>((const uint16_t*)src, C, R, C, R, R,
-                                                      codes, scales, (int64_t)R * C, (int64_t)R * C);
+                                                      codes, scales, (int64_t)R * C, (int64_t)R * C, grouped);
   return hipGetLastError();
 }
 
@@ -360,46 +367,10 @@ hipError_t launch_mx_quant_cols_batched(const void* src, int batch, int R, int C
 // strides in values; the kernels count them in 2-byte units of the code
 // bytes (two fp8 values or four fp4 values per unit).
 // ---------------------------------------------------------------------------
-static int device_cus_mx() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <bool FP4>
 static void to_units(GemmArgs& a) {
   constexpr int per = FP4 ? 4 : 2;        // values per 2-byte unit
   a.lda /= per; a.ldb /= per; a.K /= per; a.b_kend /= per; a.b_gstride /= per;
-}
-
-// Persistent pipelined form (gemm_pipe_kernel with microscaled operands)
-template <GemmMode MODE, class Epi, bool FP4>
-static hipError_t launch_mx_pipe(GemmArgs a, const MxArgs& s, const typename Epi::P& ep, int n_logical,
-                                 int rows_total, hipStream_t st) {
-  using C = PipeCfg<64>;
-  const int bn_cols = Epi::kPaired ? C::BN / 2 : C::BN;
-  const int NT = (n_logical + bn_cols - 1) / bn_cols;
-  const int MT = (MODE == RAGGED_M) ? 0 : (a.M + C::BM - 1) / C::BM;
-  int64_t tiles;
-  if (MODE == RAGGED_M) tiles = (int64_t)((rows_total + C::BM - 1) / C::BM + a.G) * NT;
-  else if (MODE == RAGGED_K) tiles = (int64_t)a.G * MT * NT;
-  else tiles = (int64_t)MT * NT;
-  if (tiles <= 0) return hipSuccess;
-  if (a.G > kMaxExperts) return hipErrorInvalidValue;
-  to_units<FP4>(a);
-  int64_t grid = (int64_t)device_cus_mx() * 2;
-  if (tiles < grid) grid = tiles;
-  auto kern = gemm_pipe_kernel<KC, KC, MODE, Epi, 64, true, FP4>;
-  static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
-  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
-  kern<<<(unsigned)grid, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
-  return hipGetLastError();
 }
 
 // DMA-fed LDS ring (gemm_mfma_kernel in its microscaled form): 128x256 tiles,
@@ -433,7 +404,8 @@ static hipError_t mx_rows_gemm(const MxQ& q, const int* offsets, const int* pref
   GemmArgs a{};
   a.A = q.codes; a.lda = K; a.B = w.codes; a.ldb = K; a.b_gstride = w_gstride;
   a.M = rows; a.N = N; a.K = K; a.b_next = N; a.b_kend = K;
-  MxArgs s{q.scales, w.scales, K / 32, K / 32, w_gstride / 32};
+  // grouped scales: A's over its `rows` rows, each group's B over its N rows
+  MxArgs s{q.scales, w.scales, rows, N, w_gstride / 32};
   // staged epilogues store 16-byte row pieces (the call's shape checks and
   // 16-byte aligned outputs guarantee them)
   if constexpr (Epi::kStaged)
@@ -453,7 +425,7 @@ hipError_t gemm_mx_swiglu_fwd(const MxQ& x, const int* off, const int* prefix, i
                               void* act, int rows, int d, int f, const float* row_gates, bool from_stored, bool fp4,
                               uint8_t* act_codes, uint8_t* act_scales, hipStream_t st) {
   typename EpiSwiGLU<bf16>::P ep{(bf16*)act, (bf16*)hu, f, row_gates, from_stored ? 1 : 0,
-                                 act_codes, act_scales, fp4 ? 1 : 0};
+                                 act_codes, act_scales, fp4 ? 1 : 0, rows};
   return mx_rows_gemm<EpiSwiGLU<bf16>>(x, off, prefix, G, w13, (int64_t)2 * f * d, rows, 2 * f, d, ep, f, fp4, st);
 }
 
@@ -469,7 +441,8 @@ hipError_t gemm_mx_down_dgrad_swiglu_bwd(const MxQ& dy, const int* off, const in
                                          const float* row_gates, float* dg_part, void* act_out, bool fp4,
                                          uint8_t* dhu_codes, uint8_t* dhu_scales, hipStream_t st) {
   typename EpiSwiGLUBwd<bf16>::P ep{(const bf16*)hu, (bf16*)dhu, f, row_gates, row_gates ? dg_part : nullptr,
-                                    gemm_dg_parts(true, f), (bf16*)act_out, dhu_codes, dhu_scales, fp4 ? 1 : 0};
+                                    gemm_dg_parts(true, f), (bf16*)act_out, dhu_codes, dhu_scales, fp4 ? 1 : 0,
+                                    rows};
   return mx_rows_gemm<EpiSwiGLUBwd<bf16>>(dy, off, prefix, G, w2t, (int64_t)f * d, rows, f, d, ep, f, fp4, st);
 }
 

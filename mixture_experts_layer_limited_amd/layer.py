@@ -147,10 +147,11 @@ class MoELayer:
         quantize_both = abi.moe_quantize_mxfp4_both if fp4 else abi.moe_quantize_mxfp8_both
 
         def quant(name, w, batch, rows, cols):
-            # the row form (name) and the transposed form (name_t) in one pass
+            # the row form (name) and the transposed form (name_t) in one
+            # pass, scales grouped as the microscaled GEMMs read them
             c, sc = u8(batch, rows, cols // per_byte), u8(batch, rows, cols // 32)
             ct, sct = u8(batch, cols, rows // per_byte), u8(batch, cols, rows // 32)
-            quantize_both(w, batch, rows, cols, c, sc, ct, sct, stream)
+            quantize_both(w, batch, rows, cols, c, sc, ct, sct, abi.MOE_MX_GROUPED, stream)
             q[name], q[name + "_t"] = (c, sc), (ct, sct)
 
         quant("w13", w13, s.E, 2 * s.f, s.d)

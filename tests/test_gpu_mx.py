@@ -96,6 +96,49 @@ def test_quantize_both_orientations_in_one_pass(batch, rows, cols, fmt):
         both(xd, batch, rows - 16, cols, *b)            # rows not a multiple of 32
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("batch,rows,cols", [(2, 128, 256), (1, 384, 128)])
+def test_quantize_grouped_scales_are_the_plain_ones_regrouped(batch, rows, cols, fmt):
+    """MOE_MX_GROUPED moves each scale byte to 4 (floor(b/4) R' + r) + b % 4 of
+    its matrix and changes nothing else: the grouped outputs of the single
+    and the two-orientation calls are the plain outputs (pinned above) with
+    their scales regrouped."""
+    _needs_gpu()
+    fp4 = fmt == "e2m1"
+    print(f"\n[mx quant grouped] {fmt} batch={batch} rows={rows} cols={cols}", flush=True)
+    xd = _bf16_matrix(batch, rows, cols, seed=5 * rows + cols).cuda()
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    per = 2 if fp4 else 1
+    single = abi.moe_quantize_mxfp4 if fp4 else abi.moe_quantize_mxfp8
+    both = abi.moe_quantize_mxfp4_both if fp4 else abi.moe_quantize_mxfp8_both
+    G = abi.MOE_MX_GROUPED
+
+    def regroup(sc):                                   # [B][R'][nb] -> [B][nb/4][R'][4]
+        B, Rp, nb = sc.shape
+        return sc.reshape(B, Rp, nb // 4, 4).transpose(1, 2).contiguous()
+
+    plain = {}
+    for name, orient, shape in (("rows", abi.MOE_MX_ROWS, (rows, cols)), ("cols", abi.MOE_MX_COLS, (cols, rows))):
+        c, sc = u8(batch, shape[0], shape[1] // per), u8(batch, shape[0], shape[1] // 32)
+        single(xd, batch, rows, cols, orient, c, sc)
+        gc, gs = u8(batch, shape[0], shape[1] // per), u8(batch, shape[0], shape[1] // 32)
+        single(xd, batch, rows, cols, orient | G, gc, gs)
+        torch.cuda.synchronize()
+        assert torch.equal(gc, c)
+        assert torch.equal(gs.view(batch, shape[1] // 128, shape[0], 4), regroup(sc))
+        plain[name] = (c, sc)
+    b = [torch.full_like(t, 0xA5) for t in (*plain["rows"], *plain["cols"])]
+    both(xd, batch, rows, cols, *b, G)
+    torch.cuda.synchronize()
+    assert torch.equal(b[0], plain["rows"][0]) and torch.equal(b[2], plain["cols"][0])
+    assert torch.equal(b[1].view(batch, cols // 128, rows, 4), regroup(plain["rows"][1]))
+    assert torch.equal(b[3].view(batch, rows // 128, cols, 4), regroup(plain["cols"][1]))
+    with pytest.raises(RuntimeError):
+        single(xd, batch, rows, cols - 32, abi.MOE_MX_ROWS | G, *plain["rows"])   # cols not a multiple of 128
+    with pytest.raises(RuntimeError):
+        both(xd, batch, rows, cols - 32, *b, G)
+
+
 def _cfg(name, **kw):
     base = dict(dtype="mxfp8", backward=True, router_std=0.02, expert_std=0.02)
     base.update(kw)
