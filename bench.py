@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm_band.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "7fbf67d5b02d63f472149e5e1a5f0a6d210c34429eab389ea90035b1f42f9955",
-                          "fetch_bytes": 782110806, "write_bytes": 15032428768},
+    "gemm_wgrad_gateup": {"src_sha": "db981bb05c8e14bc119cdeb9e50ff6b206de53f0405e80958a72e6690f54010a",
+                          "fetch_bytes": 782402130, "write_bytes": 15032428416},
 }
 
 
