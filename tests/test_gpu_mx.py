@@ -162,6 +162,14 @@ MX_CASES = [
     _cfg("mx4_dsv3_like_fold_recompute", T=256, d=256, E=32, k=4, f=256, f_shared=256, score="sigmoid",
          n_group=4, topk_group=2, renorm=True, scale=2.5, bias="zipf", fold_gates=True, recompute_act=True,
          dtype="mxfp4"),
+    # one token: two rows in all (the grouped scales of every operand span
+    # two rows), with a shared expert of one row
+    _cfg("mx_one_token", T=1, d=256, E=8, k=2, f=128, f_shared=128, score="softmax"),
+    _cfg("mx4_one_token", T=1, d=256, E=8, k=2, f=256, f_shared=256, score="softmax", dtype="mxfp4"),
+    # four experts of about 128 rows over a long contraction (eight fp8
+    # slices of d, four of fp4): several row tiles per expert, ragged ends
+    _cfg("mx_long_k", T=256, d=1024, E=4, k=2, f=256, score="softmax"),
+    _cfg("mx4_long_k", T=256, d=1024, E=4, k=2, f=256, score="softmax", dtype="mxfp4"),
 ]
 
 
