@@ -17,6 +17,9 @@
 //   rows  : codes [R][C], scales [R][C/32]   (blocks along the contiguous C)
 //   cols  : codes [C][R], scales [C][R/32]   (transposed copy, blocks along R:
 //           the weights for the products that contract over their rows)
+// Scales come plain (as above) or grouped (mx_scale_at in gemm.hpp: four
+// block scales of a row per word, the words of consecutive rows adjacent),
+// the layout the microscaled GEMMs read; codes are the same in both.
 // The weight gradients contract over the token rows: their operands are
 // quantised along the rows (32-row blocks restarting at each expert's first
 // row) and widened back to bf16 (mx_qdq_rows).
