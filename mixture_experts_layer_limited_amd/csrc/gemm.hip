@@ -134,7 +134,7 @@ static hipError_t launch_mfma(const GemmArgs& a, const typename Epi::P& ep, int 
 // (128x256 tiles; 256x256 where experts are large, see big_tiles; data
 // gradients read their row-contiguous weight with transposing LDS reads),
 // expert weight gradients (short ragged contractions) on the band kernel for
-// experts of at most BandCfg::KMAX rows plus the persistent DMA ring for
+// experts of at most kBandMaxRows rows plus the persistent DMA ring for
 // larger ones, and the router's weight gradient on the persistent pipelined
 // kernel.
 
@@ -165,35 +165,43 @@ static hipError_t launch_pipe(const GemmArgs& a, const typename Epi::P& ep, int 
 // general kernels on every expert).
 template <class Epi>
 static bool band_fits(const GemmArgs& a, const typename Epi::P& ep) {
-  using C = BandCfg;
+  using S = BandShape<true, true>;          // (the wide unit; the narrow one's limits are within these)
   if (!a.offsets || a.G < 1 || a.G > kMaxExperts) return false;
-  if (a.M % C::BM != 0 || a.N % C::BN != 0) return false;
+  // the band on the output's longer side (a multiple of the wide band), the
+  // streamed tiles on the other
+  const bool pband = a.M > a.N;
+  if ((pband ? a.M : a.N) % S::BW != 0 || (pband ? a.N : a.M) % BandCfg::SW != 0) return false;
   if (a.lda != a.M || a.ldb != a.N || ep.ldc != a.N || ep.c_gstride != (int64_t)a.M * a.N) return false;
   if (((uintptr_t)a.A & 15) || ((uintptr_t)a.B & 15) || ((uintptr_t)ep.C & 15)) return false;
   // 32-bit buffer offsets: an expert's rows of either operand and a band's output rows
   const int64_t lim = (int64_t)1 << 31;
-  return (int64_t)C::KMAX * a.lda * 2 < lim && (int64_t)C::KMAX * a.ldb * 2 < lim &&
-         (int64_t)C::BM * ep.ldc * 2 < lim;
+  return (int64_t)kBandMaxRows * a.lda * 2 < lim && (int64_t)kBandMaxRows * a.ldb * 2 < lim &&
+         (int64_t)S::BW * ep.ldc * 2 < lim;   // a tile's output rows (up to the wide band's width)
 }
 
 template <class Epi>
 static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipStream_t st) {
-  using C = BandCfg;
   // the band on the output's longer side: more, shorter units (measured at the
   // 256-expert, d = 7168 shape: the gate/up gradient, 4096 x 7168, with the
-  // band along its columns, the down gradient, 7168 x 2048, along its rows)
+  // band along its columns, the down gradient, 7168 x 2048, along its rows).
+  // One launch holds both unit shapes: experts of 1 .. kBandWideRows rows take
+  // 256-column bands, up to kBandMaxRows 128-column ones (at 128 rows per
+  // expert the wide units took gate/up 3.93 -> 3.77 ms, down 2.06 -> 1.96 ms;
+  // as a second launch the narrow units cost 0.5 ms more on skewed routing
+  // than when they share the persistent grid).
   const bool pband = a.M > a.N;
   auto kern = pband ? gemm_band_kernel<Epi, false> : gemm_band_kernel<Epi, true>;
-  static bool lds_done[2][kLdsAttrDevices] = {};  // per device, per orientation
-  if (hipError_t e = raise_lds_limit(lds_done[pband], (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
-  const int UB = pband ? a.M / C::BM : a.N / C::BN, TU = pband ? a.N / C::BN : a.M / C::BM;
+  static bool lds_done[2][kLdsAttrDevices] = {};     // per kernel, per device
+  if (hipError_t e = raise_lds_limit(lds_done[pband], (const void*)kern, BandCfg::LDS_BYTES); e != hipSuccess)
+    return e;
+  // 128-column bands along the band side, 128-wide streamed tiles along the other
+  const int UB = (pband ? a.M : a.N) / BandCfg::SW, TU = (pband ? a.N : a.M) / BandCfg::SW;
   // each unit walks its tiles starting at its band index (mod the tile count),
   // so neighbouring units read different streamed tiles at any time (3% faster
   // than all starting at tile 0)
   constexpr int rot = 1;
-  kern<<<(unsigned)device_cus(), C::NTHR, C::LDS_BYTES, st>>>(a, ep, UB, TU, rot);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  kern<<<(unsigned)device_cus(), BandCfg::NTHR, BandCfg::LDS_BYTES, st>>>(a, ep, UB, TU, rot);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   // experts with more rows: the DMA ring, persistent, skipping the others
   // whole, on 256x256 tiles: a CU's operand traffic per flop is what bounds
   // it, and these take a third less of it than 128x256 tiles (Qwen3, 512 rows
@@ -201,7 +209,7 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
   // the band kernel's size the same ring is slower than the band (DeepSeek-V3
   // gate/up 5.13 ms against 3.90).
   GemmArgs big = a;
-  big.k_skip = C::KMAX;
+  big.k_skip = kBandMaxRows;
   return launch_mfma<256, 256, 2, 4, 2, MC, MC, RAGGED_K, Epi>(big, ep, a.N, 0, st, true);
 }
 

@@ -5,31 +5,37 @@
 // over the expert's rows, n_g of them.  At an average of a few hundred rows per
 // expert the output (all of C, bf16) is far larger than the operands.
 //
-// Work unit: (expert g, band of 128 columns of one operand: of Q when the band
-// is on the output's column side, of P when on its row side).  The band,
-// n_g x 128 values (n_g <= 320), goes into LDS by DMA at the start of the unit,
-// and the unit walks the 128-wide tiles of the output's other side, streaming
-// the other operand in 64-row slices through a 4-stage DMA ring: a 128 x 128
-// output tile costs 128 x n_g x 2 bytes of operand reads instead of twice that.
-// Compute waves read the fragments of both operands from LDS.
+// Work unit: (expert g, band of columns of one operand: of Q when the band is
+// on the output's column side, of P when on its row side).  The band goes into
+// LDS by DMA at the start of the unit, and the unit walks the 128-wide tiles of
+// the output's other side, streaming the other operand in 64-row slices
+// through a 3-stage DMA ring: a tile costs 128 x n_g x 2 bytes of operand
+// reads.  Compute waves read the fragments of both operands from LDS.  Two unit
+// shapes share one launch and one LDS layout (a 96 KB band region, the ring,
+// the epilogue staging: 160 KB):
+//   wide:   experts of 1..192 rows, a 256-column band, 128 x 256 output tiles
+//           (each streamed slice feeds twice the outputs, so the per-slice
+//           costs -- a barrier, a DMA wait -- weigh half as much);
+//   narrow: experts of 193..320 rows, a 128-column band, 128 x 128 tiles.
 //
 // Waits.  Vector memory operations of a wave complete in issue order, so the
 // wait for a slice allows exactly the operations issued after that slice's DMA
 // to stay outstanding: a load wave counts what it issues and records the count
 // after each slice.
 //
-// Schedule.  One workgroup of six waves per CU (the band, the ring and the
-// epilogue staging fill the 160 KB of LDS), four compute waves of 64 x 64 over a
-// 128 x 128 tile.  Each XCD owns one contiguous run of the expert-major unit
-// list, split by estimated cost, and its workgroups stride through it, so the
-// workgroups of an XCD hold neighbouring bands of one expert; each unit walks
-// its tiles from its band index on, so neighbours stream different tiles at
-// any time.  Experts with no rows or more than 320 rows are not units of this
-// kernel (the caller zero-fills the first and runs the DMA ring on the second).
+// Schedule.  One workgroup of six waves per CU, four compute waves over a
+// 2 x 2 grid of the tile.  The units are numbered expert-major (the bands of
+// expert g follow those of g - 1; an expert has a wide unit per 256 columns or
+// a narrow one per 128); each XCD owns one contiguous run of that list, split
+// by estimated cost, and its workgroups stride through it, so the workgroups
+// of an XCD hold neighbouring bands of one expert; each unit walks its tiles
+// from its band index on, so neighbours stream different tiles at any time.
+// Experts with no rows or more than 320 rows have no units here (the caller
+// zero-fills the first and runs the DMA ring on the second).
 //
-// Epilogue: each compute wave writes its 64 x 64 sub-tile as bf16, 32 rows at
-// a time, into its own 4 KB staging area (LDS operations of one wave execute in
-// order, so no barrier is needed) and stores it back as 128-byte row segments,
+// Epilogue: each compute wave writes its sub-tile as bf16, 32 x 64 at a time,
+// into its own 4 KB staging area (LDS operations of one wave execute in order,
+// so no barrier is needed) and stores it back as 128-byte row segments,
 // non-temporal.
 #pragma once
 
@@ -47,36 +53,168 @@ __device__ __forceinline__ void issue_slice_asm(const Plan& p, const void* base,
     dma_b128(base, bytes, p.off[j], soff, lds + (uint32_t)((wave + j * NW) * 64 * 16));
 }
 
+// LDS layout and wave roles, common to both unit shapes
 struct BandCfg {
-  static constexpr int BM = 128, BN = 128, BK = 64, KMAX = 320, KS = KMAX / BK;
-  static constexpr int WM = 2, WN = 2, FM = 2, FN = 2;
-  static constexpr int NCW = 4, NLW = 2;                 // compute and load waves
+  static constexpr int BK = 64, SW = 128;                 // slice rows, streamed tile width
+  static constexpr int WM = 2, WN = 2;                    // compute waves over a tile
+  static constexpr int NCW = 4, NLW = 2;                  // compute and load waves
   static constexpr int NW = NCW + NLW, NTHR = 64 * NW;
-  static constexpr int STAGES = 4;
-  static constexpr int SLICE = BK * 128 * 2;              // 64 rows x 128 columns, bf16
-  static constexpr int A_OFF = 0;                         // KS slices of the band
-  static constexpr int RING_OFF = KS * SLICE;
+  static constexpr int STAGES = 3;
+  static constexpr int BAND_BYTES = 96 * 1024;            // band region at offset 0
+  static constexpr int SLICE = BK * SW * 2;               // 64 rows x 128 columns streamed
+  static constexpr int RING_OFF = BAND_BYTES;
   static constexpr int STG_OFF = RING_OFF + STAGES * SLICE;
-  static constexpr int STG_WAVE = 32 * 64 * 2;            // half of a compute wave's 64 x 64 sub-tile
+  static constexpr int STG_WAVE = 32 * 64 * 2;            // 32 rows x 64 columns of a compute wave's sub-tile
   static constexpr int LDS_BYTES = STG_OFF + NCW * STG_WAVE;
-  static constexpr int DMA = SLICE / 16 / (64 * NLW);     // DMA instructions per load wave per slice
-  static constexpr int UNIT_EPI_COST = 4;                 // a tile's stores, in slices, for run splitting
+  static constexpr int DMA = SLICE / 16 / (64 * NLW);     // DMA instructions per load wave per streamed slice
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(DMA * 16 * 64 * NLW == SLICE, "DMA split");
-  static_assert(WM * WN == NCW, "waves");
 };
 
-// QBAND = true: the band is 128 columns of Q (the output's column side) and
-// the unit walks the output's row tiles, streaming P; false: the band is 128
-// columns of P and the unit walks column tiles, streaming Q.  UB = bands per
-// expert, TU = tiles per unit.
+// One unit shape: band width, output tile, rows it takes
+template <bool QBAND, bool WIDE>
+struct BandShape {
+  using C = BandCfg;
+  static constexpr int BW = WIDE ? 256 : 128;             // band width
+  static constexpr int BM = QBAND ? C::SW : BW, BN = QBAND ? BW : C::SW;   // output tile
+  static constexpr int KMAX = WIDE ? 192 : 320, KS = KMAX / C::BK;
+  static constexpr int FM = BM / (32 * C::WM), FN = BN / (32 * C::WN);
+  static constexpr int BAND_SLICE = C::BK * BW * 2;       // 64 rows of the band, bf16
+  static constexpr int BAND_DMA = BAND_SLICE / 16 / (64 * C::NLW);   // per load wave per band slice
+  static_assert(KS * BAND_SLICE <= C::BAND_BYTES, "band region");
+  static_assert(BAND_DMA * 16 * 64 * C::NLW == BAND_SLICE && FN % 2 == 0, "split");
+};
+// experts of 1 .. kBandWideRows rows take wide units, up to kBandMaxRows
+// narrow ones; the larger go to the ring
+constexpr int kBandWideRows = BandShape<true, true>::KMAX;
+constexpr int kBandMaxRows = BandShape<true, false>::KMAX;
+
+// DMA of an expert's band (ns slices of 64 rows; rows past n read as zero);
+// returns the DMA instructions issued by this load wave
+template <class S>
+__device__ __forceinline__ int issue_band_dma(const uint16_t* Bo, int64_t ld_band, int kb, int n, int ns, int band,
+                                              uint32_t lds, int lw) {
+  constexpr int NLW = BandCfg::NLW;
+  DmaPlan<MC, S::BW, S::BAND_DMA, NLW> pa;
+  pa.plan_mc(ld_band, band * S::BW, lw);
+  const void* base = Bo + (int64_t)kb * ld_band;
+  const uint32_t bytes = (uint32_t)(n * ld_band * 2);
+  const uint32_t band_slice = (uint32_t)(BandCfg::BK * ld_band * 2);
+  int vm = 0;
+#pragma unroll
+  for (int s = 0; s < S::KS; ++s)
+    if (s < ns) {
+      issue_slice_asm<decltype(pa), S::BAND_DMA, NLW>(pa, base, bytes, (uint32_t)s * band_slice,
+                                                      lds + s * S::BAND_SLICE, lw);
+      vm += S::BAND_DMA;
+    }
+  return vm;
+}
+
+// Compute waves: the TU tiles of one unit (expert g, band `band`, ns slices).
+// `n` counts the streamed slices multiplied so far (their ring stages).
+template <class Epi, bool QBAND, bool WIDE>
+__device__ __forceinline__ void band_unit_tiles(uint32_t lds0, const typename Epi::P& ep, int g, int band, int ns,
+                                                int TU, int rot, int wave, int& n) {
+  using C = BandCfg;
+  using S = BandShape<QBAND, WIDE>;
+  constexpr int BM = S::BM, BN = S::BN, FM = S::FM, FN = S::FN;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  McFrag<BM, FM> fa;
+  McFrag<BN, FN> fb;
+  fa.init(wm * (BM / C::WM));
+  fb.init(wn * (BN / C::WN));
+  const uint32_t stg = lds0 + C::STG_OFF;     // sub-tile of compute wave w at stg + w * STG_WAVE
+  floatx16 acc[FM][FN];
+
+  for (int j = 0; j < TU; ++j) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.0f;
+    // a runtime loop over the tile's slices keeps the accumulators in one
+    // register set
+#pragma unroll 1
+    for (int s = 0; s < ns; ++s) {
+      bar();
+      const uint32_t sb = lds0 + C::RING_OFF + (n % C::STAGES) * C::SLICE;   // streamed slice
+      const uint32_t sband = lds0 + s * S::BAND_SLICE;                       // band slice
+      const uint32_t sm = QBAND ? sb : sband, sn = QBAND ? sband : sb;       // m side, n side
+      // fragments of K-step kk + 1 are read while the MFMAs of step kk run
+      // (two register sets), in the order the scheduling groups fix
+      bf16x8 fm[2][FM], fn[2][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fm[0][i] = fa.read(sm, i, 0);
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) fn[0][jj] = fb.read(sn, jj, 0);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < 4) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) fm[cur ^ 1][i] = fa.read(sm, i, kk + 1);
+#pragma unroll
+          for (int jj = 0; jj < FN; ++jj) fn[cur ^ 1][jj] = fb.read(sn, jj, kk + 1);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < FN; ++jj)   // n-side fragment first: acc[i][jj] is m-block i x n-block jj
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fn[cur][jj], fm[cur][i], acc[i][jj], 0, 0, 0);
+      }
+      sched_pipelined_slice<2 * (FM + FN), FM * FN>();
+      ++n;
+    }
+    // tile end: the sub-tile through this wave's staging area, 32 x 64 at a
+    // time (LDS operations of one wave execute in order), to 128-byte row pieces
+    const int jt = (j + rot * band) % TU;     // the unit's tiles in rotated order
+    const int row0 = (QBAND ? jt : band) * BM, col0 = (QBAND ? band : jt) * BN;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(ep.C + g * ep.c_gstride + (int64_t)row0 * ep.ldc, (uint32_t)(BM * ep.ldc * 2));
+    const uint32_t col_off = (uint32_t)(col0 + wn * (BN / C::WN) + (lane & 7) * 8) * 2;
+    MOE_LDS u32x2* w2 = (MOE_LDS u32x2*)(uintptr_t)(stg + wave * C::STG_WAVE);
+    const MOE_LDS u32x4* r4 = (const MOE_LDS u32x4*)(uintptr_t)(stg + wave * C::STG_WAVE);
+    // one 32 x 64 piece per round: row block i, columns 64 jp .. 64 jp + 63
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int jp = 0; jp < FN / 2; ++jp) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = lane & 31, chunk = jj * 4 + q;
+            const floatx16& a4 = acc[i][2 * jp + jj];
+            const u32x2 v = {pack_bf16x2(a4[4 * q], a4[4 * q + 1]), pack_bf16x2(a4[4 * q + 2], a4[4 * q + 3])};
+            w2[(row * 8 + (chunk ^ stage_swz(row))) * 2 + (lane >> 5)] = v;
+          }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int rr = it * 8 + (lane >> 3), cc = lane & 7;
+          const u32x4 v = r4[rr * 8 + (cc ^ stage_swz(rr))];
+          store_b128<true>(v, rs, col_off + (uint32_t)(jp * 128) +
+                                      (uint32_t)((wm * (BM / C::WM) + i * 32 + rr) * ep.ldc * 2));
+        }
+      }
+    }
+  }
+}
+
+// QBAND = true: the band is columns of Q (the output's column side) and the
+// unit walks the output's row tiles, streaming P; false: the band is columns
+// of P and the unit walks column tiles, streaming Q.  UB = 128-column bands
+// per expert (even: an expert has UB / 2 wide units or UB narrow ones), TU =
+// 128-wide tiles per unit.
 //
 // Wave roles.  A wave's loads and stores share one in-order completion
 // counter, so a wave that stores a tile's outputs and then waits for a DMA
 // issued after them waits for the stores as well, and stops feeding the store
 // queue while it waits.  The roles are therefore split: four compute waves
-// (MFMA, LDS, and the stores of their own 64 x 64 sub-tiles; they never wait
-// on memory, so their stores stream, up to the 63 operations a wave may have
+// (MFMA, LDS, and the stores of their own sub-tiles; they never wait on
+// memory, so their stores stream, up to the 63 operations a wave may have
 // outstanding) and two load waves (every DMA, and every wait for one).  All
 // six run the same unit / tile / slice skeleton and meet at the same barriers:
 //   unit start:  B [load: DMA of the band, and the wait for it] B
@@ -87,7 +225,7 @@ template <class Epi, bool QBAND>
 __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, typename Epi::P ep, int UB, int TU,
                                                                  int rot) {
   using C = BandCfg;
-  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, KMAX = C::KMAX, KS = C::KS, STAGES = C::STAGES;
+  constexpr int BK = C::BK, STAGES = C::STAGES;
   static_assert(Epi::kStaged, "bf16 output");
   extern __shared__ u32x4 smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MOE_LDS void*)smem;
@@ -95,8 +233,7 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool is_compute = wave < C::NCW;
   const bool is_load = wave >= C::NCW && wave < C::NCW + C::NLW;
-  const int wm = (wave % C::NCW) / C::WN, wn = (wave % C::NCW) % C::WN;   // compute waves
-  const int lw = wave - C::NCW;                                          // load waves
+  const int lw = wave - C::NCW;               // load waves
   const int* off = a.offsets;
   const int G = a.G;
 
@@ -110,32 +247,55 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
   // a wait the compiler sees (vmcnt 0, other counters at their maximum): it
   // then knows the offsets are in place and adds no waits before their uses
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  auto off_at = [&](int i) -> int {
+  auto lane_at = [&](const int (&r)[5], int i) -> int {
     const int l = i & 63, q = i >> 6;
-    const int v0 = __builtin_amdgcn_readlane(ov[0], l), v1 = __builtin_amdgcn_readlane(ov[1], l);
-    const int v2 = __builtin_amdgcn_readlane(ov[2], l), v3 = __builtin_amdgcn_readlane(ov[3], l);
-    const int v4 = __builtin_amdgcn_readlane(ov[4], l);
+    const int v0 = __builtin_amdgcn_readlane(r[0], l), v1 = __builtin_amdgcn_readlane(r[1], l);
+    const int v2 = __builtin_amdgcn_readlane(r[2], l), v3 = __builtin_amdgcn_readlane(r[3], l);
+    const int v4 = __builtin_amdgcn_readlane(r[4], l);
     return q == 0 ? v0 : q == 1 ? v1 : q == 2 ? v2 : q == 3 ? v3 : v4;
   };
-  // unit cost of expert g (0: not handled here); a unit is one band of one expert
+  auto off_at = [&](int i) { return lane_at(ov, i); };
   auto rows_of = [&](int g) { return off_at(g + 1) - off_at(g); };
-  auto cost_of = [&](int n) { return (n > 0 && n <= KMAX) ? (n + BK - 1) / BK + C::UNIT_EPI_COST : 0; };
+  // units of an expert of n rows, and the estimated cost of one (its slices
+  // plus its tiles' stores, in slices: a wide tile stores twice the bytes)
+  auto units_of = [&](int n) { return (n > 0 && n <= kBandMaxRows) ? (n <= kBandWideRows ? UB / 2 : UB) : 0; };
+  auto cost_of = [&](int n) { return (n + BK - 1) / BK + (n <= kBandWideRows ? 8 : 4); };
 
-  // cumulative unit cost per expert (inclusive scan in the staging area, which
-  // no epilogue uses before the barriers below)
+  // inclusive scans per expert, in the staging area (no epilogue uses it
+  // before the barriers below): the units' cost, and their count
   int64_t* pre = (int64_t*)((char*)smem + C::STG_OFF);
-  static_assert(kMaxExperts <= C::NTHR, "one thread per expert");
+  int* ucum = (int*)((char*)smem + C::STG_OFF + kMaxExperts * 8);
+  static_assert(kMaxExperts <= C::NTHR && kMaxExperts * 12 <= C::NCW * C::STG_WAVE, "one thread per expert");
   {
     const int g = threadIdx.x;
-    if (g < kMaxExperts) pre[g] = g < G ? (int64_t)UB * cost_of(off[g + 1] - off[g]) : 0;
+    if (g < kMaxExperts) {
+      const int n = g < G ? off[g + 1] - off[g] : 0;
+      const int u = units_of(n);
+      pre[g] = u > 0 ? (int64_t)u * cost_of(n) : 0;
+      ucum[g] = u;
+    }
     __syncthreads();
     for (int o = 1; o < kMaxExperts; o <<= 1) {
       const int64_t add = (g < kMaxExperts && g >= o) ? pre[g - o] : 0;
+      const int uadd = (g < kMaxExperts && g >= o) ? ucum[g - o] : 0;
       __syncthreads();
-      if (g < kMaxExperts) pre[g] += add;
+      if (g < kMaxExperts) {
+        pre[g] += add;
+        ucum[g] += uadd;
+      }
       __syncthreads();
     }
   }
+  // units before expert i (i = 0..G; i = G: all of them), in registers like
+  // the offsets
+  int uv[5];
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int i = q * 64 + lane;
+    uv[q] = i == 0 || i > G ? 0 : ucum[i - 1];
+  }
+  auto ubefore = [&](int i) { return lane_at(uv, i); };
+  const int U = ubefore(G);
   // values read from LDS are uniform: keep them (and all that derives from
   // them: experts, offsets, branch conditions) in scalar registers
   const int64_t W = (int64_t)__builtin_amdgcn_readfirstlane((int)(pre[G - 1] >> 32)) << 32 |
@@ -145,44 +305,52 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
   // first unit of XCD x's run: the first unit whose cumulative cost reaches W x / X
   auto run_start = [&](int x) -> int {
     if (x <= 0) return 0;
-    if (x >= X) return G * UB;
+    if (x >= X) return U;
     const int64_t T = W * x / X;
     int lo = 0, hi = G;                       // first g with pre[g] > T (inclusive prefix)
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (pre[mid] > T) hi = mid; else lo = mid + 1;
     }
-    if (lo >= G) return G * UB;
+    if (lo >= G) return U;
     const int64_t before = lo > 0 ? pre[lo - 1] : 0;
-    const int64_t ce = cost_of(rows_of(lo));
-    const int64_t in = (T - before + ce - 1) / ce;
-    return lo * UB + (int)(in < UB ? in : UB);
+    const int n = rows_of(lo);                // has units: its cost is above the previous prefix
+    const int64_t in = (T - before + cost_of(n) - 1) / cost_of(n);
+    const int u = units_of(n);
+    return ubefore(lo) + (int)(in < u ? in : u);
   };
   const int run_lo = __builtin_amdgcn_readfirstlane(run_start(xcd));
   const int run_hi = __builtin_amdgcn_readfirstlane(run_start(xcd + 1));
-  __syncthreads();                            // the scan's LDS is staging from here on
+  __syncthreads();                            // the scans' LDS is staging from here on
 
   struct Unit {
     int r;         // step in this workgroup's stride (-1: finished)
     int g, band;   // expert and band
     int kb, n;     // first row and row count of the expert
     int ns;        // 64-row slices
+    bool wide;
   };
-  // first step >= r holding a unit of this kernel; other experts are skipped whole
+  // the unit of step r: unit L of the expert-major list belongs to the last
+  // expert with at most L units before it
   auto settle = [&](int r, Unit& u) {
-    for (;;) {
-      const int L = run_lo + wi + r * nx;
-      if (L >= run_hi) break;
-      const int g = __builtin_amdgcn_readfirstlane(L / UB);
-      const int n = rows_of(g);
-      if (n > 0 && n <= KMAX) {
-        u.r = r; u.g = g; u.band = L % UB; u.kb = off_at(g); u.n = n; u.ns = (n + BK - 1) / BK;
-        return;
-      }
-      const int next = (g + 1) * UB - run_lo - wi;       // > r * nx: L is below the next expert
-      r = (next + nx - 1) / nx;                          // first step in the next expert
+    const int L = run_lo + wi + r * nx;
+    if (L >= run_hi) {
+      u.r = -1;
+      return;
     }
-    u.r = -1;
+    int lo = 0, hi = G;                       // ubefore(lo) <= L < ubefore(hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ubefore(mid) <= L) lo = mid; else hi = mid;
+    }
+    const int g = __builtin_amdgcn_readfirstlane(lo);
+    u.r = r;
+    u.g = g;
+    u.band = L - ubefore(g);
+    u.kb = off_at(g);
+    u.n = rows_of(g);
+    u.ns = (u.n + BK - 1) / BK;
+    u.wide = u.n <= kBandWideRows;
   };
 
   const uint16_t* P = (const uint16_t*)a.A;
@@ -191,24 +359,14 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
   const uint16_t* Bo = QBAND ? Q : P;
   const uint16_t* So = QBAND ? P : Q;
   const int64_t ld_band = QBAND ? a.ldb : a.lda, ld_str = QBAND ? a.lda : a.ldb;
-  const uint32_t band_slice = (uint32_t)(BK * ld_band * 2);
   const uint32_t str_slice = (uint32_t)(BK * ld_str * 2);
 
   // ---- load waves: DMA issue and the waits for it --------------------------
   int vm = 0;                                 // DMA instructions issued by this load wave
-  DmaPlan<MC, 128, C::DMA, C::NLW> pb;
+  DmaPlan<MC, C::SW, C::DMA, C::NLW> pb;
   auto issue_band = [&](const Unit& u) {
-    DmaPlan<MC, 128, C::DMA, C::NLW> pa;
-    pa.plan_mc(ld_band, u.band * 128, lw);
-    const void* base = Bo + (int64_t)u.kb * ld_band;
-    const uint32_t bytes = (uint32_t)(u.n * ld_band * 2);
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      if (s < u.ns) {
-        issue_slice_asm<decltype(pa), C::DMA, C::NLW>(pa, base, bytes, (uint32_t)s * band_slice,
-                                                      lds0 + C::A_OFF + s * C::SLICE, lw);
-        vm += C::DMA;
-      }
+    vm += u.wide ? issue_band_dma<BandShape<QBAND, true>>(Bo, ld_band, u.kb, u.n, u.ns, u.band, lds0, lw)
+                 : issue_band_dma<BandShape<QBAND, false>>(Bo, ld_band, u.kb, u.n, u.ns, u.band, lds0, lw);
   };
   struct LdIt {
     Unit u;
@@ -217,7 +375,7 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
   const void* rb_base = nullptr;
   uint32_t rb_bytes = 0, sob = 0;
   auto plan_b = [&]() {
-    pb.plan_mc(ld_str, ((ld.j + rot * ld.u.band) % TU) * 128, lw);
+    pb.plan_mc(ld_str, ((ld.j + rot * ld.u.band) % TU) * C::SW, lw);
     rb_base = So + (int64_t)ld.u.kb * ld_str;
     rb_bytes = (uint32_t)(ld.u.n * ld_str * 2);
     sob = 0;
@@ -289,90 +447,14 @@ __global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, ty
   if (!is_compute) return;                    // (no other roles: NW = NCW + NLW)
 
   // ---- compute waves ------------------------------------------------------
-  McFrag<BM, C::FM> fa;
-  McFrag<BN, C::FN> fb;
-  fa.init(wm * (BM / C::WM));
-  fb.init(wn * (BN / C::WN));
-  const uint32_t stg = lds0 + C::STG_OFF;     // sub-tile of compute wave w at stg + w * STG_WAVE
-  floatx16 acc[C::FM][C::FN];
-
   int n = 0;                                  // slice being multiplied
   do {
     bar();
     bar();
     Unit nu;
     settle(cu.r + 1, nu);
-
-    for (int j = 0; j < TU; ++j) {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < C::FN; ++jj)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.0f;
-      // a runtime loop over the tile's slices keeps the accumulators in one
-      // register set
-#pragma unroll 1
-      for (int s = 0; s < cu.ns; ++s) {
-        bar();
-        const uint32_t sb = lds0 + C::RING_OFF + (n % STAGES) * C::SLICE;   // streamed slice
-        const uint32_t sband = lds0 + C::A_OFF + s * C::SLICE;               // band slice
-        const uint32_t sm = QBAND ? sb : sband, sn = QBAND ? sband : sb;      // m side, n side
-        // fragments of K-step kk + 1 are read while the MFMAs of step kk run
-        // (two register sets), in the order the scheduling groups fix
-        bf16x8 fm[2][C::FM], fn[2][C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) fm[0][i] = fa.read(sm, i, 0);
-#pragma unroll
-        for (int jj = 0; jj < C::FN; ++jj) fn[0][jj] = fb.read(sn, jj, 0);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int cur = kk & 1;
-          if (kk + 1 < 4) {
-#pragma unroll
-            for (int i = 0; i < C::FM; ++i) fm[cur ^ 1][i] = fa.read(sm, i, kk + 1);
-#pragma unroll
-            for (int jj = 0; jj < C::FN; ++jj) fn[cur ^ 1][jj] = fb.read(sn, jj, kk + 1);
-          }
-#pragma unroll
-          for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int jj = 0; jj < C::FN; ++jj)   // n-side fragment first: acc[i][jj] is m-block i x n-block jj
-              acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fn[cur][jj], fm[cur][i], acc[i][jj], 0, 0, 0);
-        }
-        sched_pipelined_slice<2 * (C::FM + C::FN), C::FM * C::FN>();
-        ++n;
-      }
-      // tile end: the sub-tile through this wave's staging area, 32 rows at a
-      // time (LDS operations of one wave execute in order), to 128-byte row pieces
-      {
-        const int jt = (j + rot * cu.band) % TU;   // the unit's tiles in rotated order
-        const int row0 = (QBAND ? jt : cu.band) * BM, col0 = (QBAND ? cu.band : jt) * BN;
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(ep.C + cu.g * ep.c_gstride + (int64_t)row0 * ep.ldc, (uint32_t)(BM * ep.ldc * 2));
-        const uint32_t col_off = (uint32_t)(col0 + wn * (BN / C::WN) + (lane & 7) * 8) * 2;
-        MOE_LDS u32x2* w2 = (MOE_LDS u32x2*)(uintptr_t)(stg + wave * C::STG_WAVE);
-        const MOE_LDS u32x4* r4 = (const MOE_LDS u32x4*)(uintptr_t)(stg + wave * C::STG_WAVE);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-#pragma unroll
-          for (int jj = 0; jj < C::FN; ++jj)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int row = lane & 31, chunk = jj * 4 + q;
-              const u32x2 v = {pack_bf16x2(acc[i][jj][4 * q], acc[i][jj][4 * q + 1]),
-                               pack_bf16x2(acc[i][jj][4 * q + 2], acc[i][jj][4 * q + 3])};
-              w2[(row * 8 + (chunk ^ stage_swz(row))) * 2 + (lane >> 5)] = v;
-            }
-#pragma unroll
-          for (int it = 0; it < 4; ++it) {
-            const int rr = it * 8 + (lane >> 3), cc = lane & 7;
-            const u32x4 v = r4[rr * 8 + (cc ^ stage_swz(rr))];
-            store_b128<true>(v, rs, col_off + (uint32_t)((wm * (BM / C::WM) + i * 32 + rr) * ep.ldc * 2));
-          }
-        }
-      }
-    }
+    if (cu.wide) band_unit_tiles<Epi, QBAND, true>(lds0, ep, cu.g, cu.band, cu.ns, TU, rot, wave, n);
+    else band_unit_tiles<Epi, QBAND, false>(lds0, ep, cu.g, cu.band, cu.ns, TU, rot, wave, n);
     cu = nu;
   } while (cu.r >= 0);
 }
