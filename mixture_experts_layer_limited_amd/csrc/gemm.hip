@@ -170,13 +170,29 @@ static bool band_fits(const GemmArgs& a, const typename Epi::P& ep) {
   // the band on the output's longer side (a multiple of the wide band), the
   // streamed tiles on the other
   const bool pband = a.M > a.N;
-  if ((pband ? a.M : a.N) % S::BW != 0 || (pband ? a.N : a.M) % BandCfg::SW != 0) return false;
+  if ((pband ? a.M : a.N) % S::BW != 0 || (pband ? a.N : a.M) % BandCfg<true>::SW != 0) return false;
   if (a.lda != a.M || a.ldb != a.N || ep.ldc != a.N || ep.c_gstride != (int64_t)a.M * a.N) return false;
   if (((uintptr_t)a.A & 15) || ((uintptr_t)a.B & 15) || ((uintptr_t)ep.C & 15)) return false;
   // 32-bit buffer offsets: an expert's rows of either operand and a band's output rows
   const int64_t lim = (int64_t)1 << 31;
   return (int64_t)kBandMaxRows * a.lda * 2 < lim && (int64_t)kBandMaxRows * a.ldb * 2 < lim &&
          (int64_t)S::BW * ep.ldc * 2 < lim;   // a tile's output rows (up to the wide band's width)
+}
+
+template <class Epi, bool QBAND>
+static hipError_t launch_band_kernel(const GemmArgs& a, const typename Epi::P& ep, hipStream_t st) {
+  using C = BandCfg<QBAND>;
+  auto kern = gemm_band_kernel<Epi, QBAND>;
+  static bool lds_done[kLdsAttrDevices] = {};     // per device
+  if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
+  // 128-column bands along the band side, 128-wide streamed tiles along the other
+  const int UB = (QBAND ? a.N : a.M) / C::SW, TU = (QBAND ? a.M : a.N) / C::SW;
+  // each unit walks its tiles starting at its band index (mod the tile count),
+  // so neighbouring units read different streamed tiles at any time (3% faster
+  // than all starting at tile 0)
+  constexpr int rot = 1;
+  kern<<<(unsigned)device_cus(), C::NTHR, C::LDS_BYTES, st>>>(a, ep, UB, TU, rot);
+  return hipGetLastError();
 }
 
 template <class Epi>
@@ -189,19 +205,8 @@ static hipError_t launch_band(const GemmArgs& a, const typename Epi::P& ep, hipS
   // expert the wide units took gate/up 3.93 -> 3.77 ms, down 2.06 -> 1.96 ms;
   // as a second launch the narrow units cost 0.5 ms more on skewed routing
   // than when they share the persistent grid).
-  const bool pband = a.M > a.N;
-  auto kern = pband ? gemm_band_kernel<Epi, false> : gemm_band_kernel<Epi, true>;
-  static bool lds_done[2][kLdsAttrDevices] = {};     // per kernel, per device
-  if (hipError_t e = raise_lds_limit(lds_done[pband], (const void*)kern, BandCfg::LDS_BYTES); e != hipSuccess)
-    return e;
-  // 128-column bands along the band side, 128-wide streamed tiles along the other
-  const int UB = (pband ? a.M : a.N) / BandCfg::SW, TU = (pband ? a.N : a.M) / BandCfg::SW;
-  // each unit walks its tiles starting at its band index (mod the tile count),
-  // so neighbouring units read different streamed tiles at any time (3% faster
-  // than all starting at tile 0)
-  constexpr int rot = 1;
-  kern<<<(unsigned)device_cus(), BandCfg::NTHR, BandCfg::LDS_BYTES, st>>>(a, ep, UB, TU, rot);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipError_t e = a.M > a.N ? launch_band_kernel<Epi, false>(a, ep, st) : launch_band_kernel<Epi, true>(a, ep, st);
+  if (e != hipSuccess) return e;
   // experts with more rows: the DMA ring, persistent, skipping the others
   // whole, on 256x256 tiles: a CU's operand traffic per flop is what bounds
   // it, and these take a third less of it than 128x256 tiles (Qwen3, 512 rows

@@ -9,10 +9,9 @@
 // on the output's column side, of P when on its row side).  The band goes into
 // LDS by DMA at the start of the unit, and the unit walks the 128-wide tiles of
 // the output's other side, streaming the other operand in 64-row slices
-// through a 3-stage DMA ring: a tile costs 128 x n_g x 2 bytes of operand
-// reads.  Compute waves read the fragments of both operands from LDS.  Two unit
+// through a DMA ring: a tile costs 128 x n_g x 2 bytes of operand reads.  Compute waves read the fragments of both operands from LDS.  Two unit
 // shapes share one launch and one LDS layout (a 96 KB band region, the ring,
-// the epilogue staging: 160 KB):
+// the epilogue staging: 160 KB; BandCfg):
 //   wide:   experts of 1..192 rows, a 256-column band, 128 x 256 output tiles
 //           (each streamed slice feeds twice the outputs, so the per-slice
 //           costs -- a barrier, a DMA wait -- weigh half as much);
@@ -23,8 +22,8 @@
 // to stay outstanding: a load wave counts what it issues and records the count
 // after each slice.
 //
-// Schedule.  One workgroup of six waves per CU, four compute waves over a
-// 2 x 2 grid of the tile.  The units are numbered expert-major (the bands of
+// Schedule.  One workgroup per CU: two load waves and four or eight compute
+// waves over a grid of the tile (BandShape).  The units are numbered expert-major (the bands of
 // expert g follow those of g - 1; an expert has a wide unit per 256 columns or
 // a narrow one per 128); each XCD owns one contiguous run of that list, split
 // by estimated cost, and its workgroups stride through it, so the workgroups
@@ -53,13 +52,17 @@ __device__ __forceinline__ void issue_slice_asm(const Plan& p, const void* base,
     dma_b128(base, bytes, p.off[j], soff, lds + (uint32_t)((wave + j * NW) * 64 * 16));
 }
 
-// LDS layout and wave roles, common to both unit shapes
+// LDS layout and wave roles, common to both unit shapes.  With the band on
+// the output's row side (QBAND = false) eight compute waves (two per SIMD)
+// and a 2-stage ring: the down-projection gradient at DeepSeek-V3's shape
+// 1.92 -> 1.81 ms, where the gate/up one (band on the column side) went from
+// 3.66 to 3.75 ms and keeps four compute waves and three stages.
+template <bool QBAND>
 struct BandCfg {
   static constexpr int BK = 64, SW = 128;                 // slice rows, streamed tile width
-  static constexpr int WM = 2, WN = 2;                    // compute waves over a tile
-  static constexpr int NCW = 4, NLW = 2;                  // compute and load waves
+  static constexpr int NCW = QBAND ? 4 : 8, NLW = 2;      // compute and load waves
   static constexpr int NW = NCW + NLW, NTHR = 64 * NW;
-  static constexpr int STAGES = 3;
+  static constexpr int STAGES = QBAND ? 3 : 2;
   static constexpr int BAND_BYTES = 96 * 1024;            // band region at offset 0
   static constexpr int SLICE = BK * SW * 2;               // 64 rows x 128 columns streamed
   static constexpr int RING_OFF = BAND_BYTES;
@@ -74,15 +77,16 @@ struct BandCfg {
 // One unit shape: band width, output tile, rows it takes
 template <bool QBAND, bool WIDE>
 struct BandShape {
-  using C = BandCfg;
+  using C = BandCfg<QBAND>;
   static constexpr int BW = WIDE ? 256 : 128;             // band width
   static constexpr int BM = QBAND ? C::SW : BW, BN = QBAND ? BW : C::SW;   // output tile
   static constexpr int KMAX = WIDE ? 192 : 320, KS = KMAX / C::BK;
-  static constexpr int FM = BM / (32 * C::WM), FN = BN / (32 * C::WN);
+  static constexpr int WM = QBAND ? 2 : 4, WN = C::NCW / WM;   // compute waves over a tile
+  static constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
   static constexpr int BAND_SLICE = C::BK * BW * 2;       // 64 rows of the band, bf16
   static constexpr int BAND_DMA = BAND_SLICE / 16 / (64 * C::NLW);   // per load wave per band slice
   static_assert(KS * BAND_SLICE <= C::BAND_BYTES, "band region");
-  static_assert(BAND_DMA * 16 * 64 * C::NLW == BAND_SLICE && FN % 2 == 0, "split");
+  static_assert(BAND_DMA * 16 * 64 * C::NLW == BAND_SLICE && FN % 2 == 0 && FM >= 1, "split");
 };
 // experts of 1 .. kBandWideRows rows take wide units, up to kBandMaxRows
 // narrow ones; the larger go to the ring
@@ -94,12 +98,12 @@ constexpr int kBandMaxRows = BandShape<true, false>::KMAX;
 template <class S>
 __device__ __forceinline__ int issue_band_dma(const uint16_t* Bo, int64_t ld_band, int kb, int n, int ns, int band,
                                               uint32_t lds, int lw) {
-  constexpr int NLW = BandCfg::NLW;
+  constexpr int NLW = S::C::NLW;
   DmaPlan<MC, S::BW, S::BAND_DMA, NLW> pa;
   pa.plan_mc(ld_band, band * S::BW, lw);
   const void* base = Bo + (int64_t)kb * ld_band;
   const uint32_t bytes = (uint32_t)(n * ld_band * 2);
-  const uint32_t band_slice = (uint32_t)(BandCfg::BK * ld_band * 2);
+  const uint32_t band_slice = (uint32_t)(S::C::BK * ld_band * 2);
   int vm = 0;
 #pragma unroll
   for (int s = 0; s < S::KS; ++s)
@@ -116,15 +120,15 @@ __device__ __forceinline__ int issue_band_dma(const uint16_t* Bo, int64_t ld_ban
 template <class Epi, bool QBAND, bool WIDE>
 __device__ __forceinline__ void band_unit_tiles(uint32_t lds0, const typename Epi::P& ep, int g, int band, int ns,
                                                 int TU, int rot, int wave, int& n) {
-  using C = BandCfg;
   using S = BandShape<QBAND, WIDE>;
+  using C = typename S::C;
   constexpr int BM = S::BM, BN = S::BN, FM = S::FM, FN = S::FN;
   const int lane = threadIdx.x & 63;
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int wm = wave / S::WN, wn = wave % S::WN;
   McFrag<BM, FM> fa;
   McFrag<BN, FN> fb;
-  fa.init(wm * (BM / C::WM));
-  fb.init(wn * (BN / C::WN));
+  fa.init(wm * (BM / S::WM));
+  fb.init(wn * (BN / S::WN));
   const uint32_t stg = lds0 + C::STG_OFF;     // sub-tile of compute wave w at stg + w * STG_WAVE
   floatx16 acc[FM][FN];
 
@@ -174,7 +178,7 @@ __device__ __forceinline__ void band_unit_tiles(uint32_t lds0, const typename Ep
     const int row0 = (QBAND ? jt : band) * BM, col0 = (QBAND ? band : jt) * BN;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(ep.C + g * ep.c_gstride + (int64_t)row0 * ep.ldc, (uint32_t)(BM * ep.ldc * 2));
-    const uint32_t col_off = (uint32_t)(col0 + wn * (BN / C::WN) + (lane & 7) * 8) * 2;
+    const uint32_t col_off = (uint32_t)(col0 + wn * (BN / S::WN) + (lane & 7) * 8) * 2;
     MOE_LDS u32x2* w2 = (MOE_LDS u32x2*)(uintptr_t)(stg + wave * C::STG_WAVE);
     const MOE_LDS u32x4* r4 = (const MOE_LDS u32x4*)(uintptr_t)(stg + wave * C::STG_WAVE);
     // one 32 x 64 piece per round: row block i, columns 64 jp .. 64 jp + 63
@@ -196,7 +200,7 @@ __device__ __forceinline__ void band_unit_tiles(uint32_t lds0, const typename Ep
           const int rr = it * 8 + (lane >> 3), cc = lane & 7;
           const u32x4 v = r4[rr * 8 + (cc ^ stage_swz(rr))];
           store_b128<true>(v, rs, col_off + (uint32_t)(jp * 128) +
-                                      (uint32_t)((wm * (BM / C::WM) + i * 32 + rr) * ep.ldc * 2));
+                                      (uint32_t)((wm * (BM / S::WM) + i * 32 + rr) * ep.ldc * 2));
         }
       }
     }
@@ -212,19 +216,19 @@ __device__ __forceinline__ void band_unit_tiles(uint32_t lds0, const typename Ep
 // Wave roles.  A wave's loads and stores share one in-order completion
 // counter, so a wave that stores a tile's outputs and then waits for a DMA
 // issued after them waits for the stores as well, and stops feeding the store
-// queue while it waits.  The roles are therefore split: four compute waves
+// queue while it waits.  The roles are therefore split: compute waves
 // (MFMA, LDS, and the stores of their own sub-tiles; they never wait on
 // memory, so their stores stream, up to the 63 operations a wave may have
 // outstanding) and two load waves (every DMA, and every wait for one).  All
-// six run the same unit / tile / slice skeleton and meet at the same barriers:
+// run the same unit / tile / slice skeleton and meet at the same barriers:
 //   unit start:  B [load: DMA of the band, and the wait for it] B
 //   slice n:     [load: wait for slice n] B [load: DMA of slice n + STAGES - 1]
 //                [compute: MFMAs of slice n]
 //   tile end:    [compute: sub-tile -> own staging area -> global stores]
 template <class Epi, bool QBAND>
-__global__ __launch_bounds__(BandCfg::NTHR) void gemm_band_kernel(GemmArgs a, typename Epi::P ep, int UB, int TU,
+__global__ __launch_bounds__(BandCfg<QBAND>::NTHR) void gemm_band_kernel(GemmArgs a, typename Epi::P ep, int UB, int TU,
                                                                  int rot) {
-  using C = BandCfg;
+  using C = BandCfg<QBAND>;
   constexpr int BK = C::BK, STAGES = C::STAGES;
   static_assert(Epi::kStaged, "bf16 output");
   extern __shared__ u32x4 smem[];
