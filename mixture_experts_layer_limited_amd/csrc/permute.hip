@@ -237,6 +237,10 @@ constexpr int kRowThreads = 256, kRowTokens = 2;
 // KC > 0: k = KC known at compile time, so the k row loads of a chunk are all
 // issued before the sum (0: any k, one row at a time).  The fp32 sum keeps the
 // j order either way.
+// tokens per block of the forward combine (1, 2, 4, 8 tokens: DeepSeek-V3
+// 0.108, 0.109, 0.113, 0.123 ms; Qwen3 0.103, 0.106, 0.108, 0.110 ms)
+constexpr int kCombineTokens = 1;
+
 template <class T, int KC>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(const T* __restrict__ y_perm,
                                                               const int32_t* __restrict__ rmap,
@@ -245,8 +249,8 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const T* __restric
                                                               int T_, int k_rt, int d) {
   const int k = KC > 0 ? KC : k_rt;
   const int vec = d / 8;
-  const int t0 = blockIdx.x * kRowTokens;
-  const int nq = min(kRowTokens, T_ - t0) * vec;
+  const int t0 = blockIdx.x * kCombineTokens;
+  const int nq = min(kCombineTokens, T_ - t0) * vec;
   for (int q = threadIdx.x; q < nq; q += kRowThreads) {
     const int t = t0 + q / vec, c = (q % vec) * 8;
     Vec8<T> acc;
@@ -299,7 +303,7 @@ hipError_t launch_combine(const T* y_perm, const int32_t* rmap, const float* gat
                           T* y, int T_, int k, int d, hipStream_t st) {
   if (T_ == 0) return hipSuccess;
 #define MOE_L(KC)                                                                                   \
-  combine_kernel<T, KC><<<(T_ + kRowTokens - 1) / kRowTokens, kRowThreads, 0, st>>>(y_perm, rmap, gates, \
+  combine_kernel<T, KC><<<(T_ + kCombineTokens - 1) / kCombineTokens, kRowThreads, 0, st>>>(y_perm, rmap, gates, \
                                                                                       y_shared, y, T_, k, d)
   MOE_DISPATCH_K(k, MOE_L);
 #undef MOE_L
