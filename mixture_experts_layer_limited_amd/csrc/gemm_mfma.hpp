@@ -398,12 +398,11 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
       sosb = g0 * (uint32_t)s.b_rows * 4;
     }
   };
+  // MX: a slice's scale words are fetched before its codes (the gathers of
+  // the scale lines otherwise complete last, and the wait for the slice waits
+  // for them: DeepSeek-V3 SwiGLU forward 1.92 -> 1.81 ms on one box)
   auto issue = [&](int stage) {
     const uint32_t sbase = lds0 + stage * C::STAGE_BYTES;
-    pa.issue(ra_base, ra_bytes, soa, sbase);
-    pb.issue(rb_base, rb_bytes, sob, sbase + C::A_BYTES);
-    soa += stride_a;
-    sob += stride_b;
     if constexpr (MX) {
 #if defined(__HIP_DEVICE_COMPILE__)
       const uint32_t sc = sbase + C::A_BYTES + C::B_BYTES + wave * 64 * 4;
@@ -416,6 +415,10 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
       sosa += kWordsPerSlice * (uint32_t)s.a_rows * 4;   // the next slice's group(s)
       sosb += kWordsPerSlice * (uint32_t)s.b_rows * 4;
     }
+    pa.issue(ra_base, ra_bytes, soa, sbase);
+    pb.issue(rb_base, rb_bytes, sob, sbase + C::A_BYTES);
+    soa += stride_a;
+    sob += stride_b;
   };
 
   FragPlan<LA, BM, FM> fa;
