@@ -65,11 +65,14 @@ constexpr uint32_t kOffRange = 0x80000000u;   // lane offset that is outside eve
 // MX = true: fp8 operands with e8m0 scales; a stage then also holds the
 // slice's scale words (one 32-bit word = four block scales per row), A's at
 // word q < BM of an NW*64-word region, B's at word q < BN of a second one.
-template <int BM, int BN, int WM, int WN, int STAGES, bool MX = false>
+// NLW > 0: NLW load waves issue every DMA (and wait for it) beside the WM x WN
+// compute waves, which then never wait on memory; 0: every wave does both.
+template <int BM, int BN, int WM, int WN, int STAGES, bool MX = false, int NLW = 0>
 struct TileCfg {
   static constexpr int BK = 64;
-  static constexpr int NW = WM * WN;
-  static constexpr int NTHR = 64 * NW;
+  static constexpr int NW = WM * WN;                       // compute waves
+  static constexpr int ND = NLW > 0 ? NLW : NW;            // waves that issue the DMA
+  static constexpr int NTHR = 64 * (NW + NLW);
   static constexpr int FM = BM / (32 * WM);
   static constexpr int FN = BN / (32 * WN);
   static constexpr int A_BYTES = BM * 128;                 // one operand slice in LDS
@@ -77,13 +80,14 @@ struct TileCfg {
   static constexpr int SC_WORDS = MX ? NW * 64 : 0;        // words per scale region
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + 2 * SC_WORDS * 4;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int A_DMA = BM * 8 / 64 / NW;           // DMA instructions per wave per slice
-  static constexpr int B_DMA = BN * 8 / 64 / NW;
+  static constexpr int A_DMA = BM * 8 / 64 / ND;           // DMA instructions per DMA wave per slice
+  static constexpr int B_DMA = BN * 8 / 64 / ND;
   static constexpr int SC_DMA = MX ? 2 : 0;                // one scale word per lane for A and for B
   static_assert(!MX || (SC_WORDS >= BM && SC_WORDS >= BN), "scale regions");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(FM >= 1 && FN >= 1 && BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile");
-  static_assert(A_DMA * 64 * NW == BM * 8 && B_DMA * 64 * NW == BN * 8, "DMA split");
+  static_assert(A_DMA * 64 * ND == BM * 8 && B_DMA * 64 * ND == BN * 8, "DMA split");
+  static_assert(NLW == 0 || (!MX && (STAGES - 1) * (A_DMA + B_DMA) <= 63), "load waves: bf16, counts in range");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "row-contiguous layout needs >= 16 chunks per K-row");
   static_assert(STAGES >= 2, "stages");
   static_assert(STAGE_BYTES <= 65536, "read immediates");
@@ -131,8 +135,9 @@ struct DmaPlan {
 
   // KC: rowv(r) = row of tile row r relative to the resource base, or -1
   template <class RowFn>
-  __device__ __forceinline__ void plan_kc(int64_t ld, RowFn rowv) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __device__ __forceinline__ void plan_kc(int64_t ld, RowFn rowv, int wave = -1) {
+    const int lane = threadIdx.x & 63;
+    if (wave < 0) wave = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const int p = (wave + j * NW) * 64 + lane;
@@ -157,8 +162,9 @@ struct DmaPlan {
     }
   }
   // one slice: instruction j fills chunk positions (wave + j*NW)*64 .. +63
-  __device__ __forceinline__ void issue(const void* rbase, uint32_t rbytes, uint32_t soff, uint32_t lds_byte) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __device__ __forceinline__ void issue(const void* rbase, uint32_t rbytes, uint32_t soff, uint32_t lds_byte,
+                                        int wave = -1) const {
+    wave = __builtin_amdgcn_readfirstlane(wave < 0 ? (int)(threadIdx.x >> 6) : wave);
 #pragma unroll
     for (int j = 0; j < NDMA; ++j)
       dma_b128(rbase, rbytes, off[j], soff, lds_byte + (uint32_t)((wave + j * NW) * 64 * 16));
@@ -267,12 +273,14 @@ __device__ __forceinline__ void sched_pipelined_slice() {
 // MxArgs in gemm.hpp); GemmArgs then count K, lda, ldb in 2-byte units, so a slice of
 // BK = 64 units is 128 fp8 values and the data path is the bf16 one.
 template <int BM, int BN, int WM, int WN, int STAGES, OpLayout LA, OpLayout LB, GemmMode MODE, class Epi,
-          bool MX = false, bool FP4 = false>
+          bool MX = false, bool FP4 = false, int NLW = 0>
 // (every configuration fills a CU's LDS with one workgroup, so at most two
-// waves share a SIMD: the compiler may give each the registers of two)
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_mfma_kernel(
-    GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
-  using C = TileCfg<BM, BN, WM, WN, STAGES, MX>;
+// waves share a SIMD, three with load waves: the compiler may give each the
+// registers of two, or a third of the SIMD's)
+__global__ __launch_bounds__(64 * (WM * WN + NLW)) __attribute__((amdgpu_waves_per_eu(1, NLW > 0 ? 3 : 2))) void
+gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
+  using C = TileCfg<BM, BN, WM, WN, STAGES, MX, NLW>;
+  constexpr bool WS = NLW > 0;
   static_assert(!MX || (LA == KC && LB == KC && MODE != RAGGED_K), "MXFP8: K-contiguous row-ragged products");
   // FP4: two scale words per row and slice, fetched by lanes 2 r and 2 r + 1
   static_assert(!FP4 || (MX && 2 * BM <= C::SC_WORDS && 2 * BN <= C::SC_WORDS), "fp4 scale regions");
@@ -285,7 +293,9 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
   const int G = gridDim.x;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave / WN, wn = wave % WN;       // compute waves
+  const bool is_load = WS && wave >= C::NW;
+  const int dw = WS ? wave - C::NW : wave;         // index among the DMA waves
   // each XCD walks one contiguous run of tiles (xcd_run_start); with a grid
   // of at least `total` workgroups every workgroup gets at most one tile
   const int X = G < 8 ? G : 8, xcd = b % X, wi = b / X, nx = (G - xcd + X - 1) / X;
@@ -319,8 +329,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
   };
 
   // DMA state of the load iterator: resources, per-lane offsets, slice strides
-  DmaPlan<LA, BM, C::A_DMA, C::NW> pa;
-  DmaPlan<LB, BN, C::B_DMA, C::NW> pb;
+  DmaPlan<LA, BM, C::A_DMA, C::ND> pa;
+  DmaPlan<LB, BN, C::B_DMA, C::ND> pb;
   const void* ra_base = nullptr;   // operand resources: base address and byte range
   const void* rb_base = nullptr;
   uint32_t ra_bytes = 0, rb_bytes = 0;
@@ -343,12 +353,12 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
       const int nrows = min(c.m_end - c.m0, BM);
       ra_base = A + (int64_t)c.m0 * a.lda;
       ra_bytes = (uint32_t)(nrows * a.lda * 2);
-      pa.plan_kc(a.lda, [&](int r) { return r < nrows ? r : -1; });
+      pa.plan_kc(a.lda, [&](int r) { return r < nrows ? r : -1; }, dw);
     } else {
       // K-rows k_begin .. k_end-1, columns m0 ..
       ra_base = A + (int64_t)c.k_begin * a.lda;
       ra_bytes = (uint32_t)((int64_t)(c.k_end - c.k_begin) * a.lda * 2);
-      pa.plan_mc(a.lda, c.m0);
+      pa.plan_mc(a.lda, c.m0, dw);
     }
     const int nt = c.n0;
     if (LB == KC) {
@@ -359,12 +369,12 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
         if constexpr (Epi::kPaired) g = Epi::template b_row_paired<BN, WN>(ep, nt, r);
         else g = nt * BN + r;
         return g < a.b_next ? g : -1;
-      });
+      }, dw);
     } else {
       const int b_kend = (MODE == RAGGED_K) ? c.k_end : min(c.k_end, a.b_kend);
       rb_base = B + (int64_t)c.k_begin * a.ldb;
       rb_bytes = (uint32_t)((int64_t)max(b_kend - c.k_begin, 0) * a.ldb * 2);
-      pb.plan_mc(a.ldb, nt * BN);
+      pb.plan_mc(a.ldb, nt * BN, dw);
     }
     // K-contiguous operands start at the tile's first K (a split-K part's;
     // row-contiguous ones have it in their base)
@@ -415,8 +425,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
       sosa += kWordsPerSlice * (uint32_t)s.a_rows * 4;   // the next slice's group(s)
       sosb += kWordsPerSlice * (uint32_t)s.b_rows * 4;
     }
-    pa.issue(ra_base, ra_bytes, soa, sbase);
-    pb.issue(rb_base, rb_bytes, sob, sbase + C::A_BYTES);
+    pa.issue(ra_base, ra_bytes, soa, sbase, dw);
+    pb.issue(rb_base, rb_bytes, sob, sbase + C::A_BYTES, dw);
     soa += stride_a;
     sob += stride_b;
   };
@@ -594,6 +604,86 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1,
       }
     }
   };
+
+  // bf16 MFMAs of one slice (stage at sa, sb), fragments of K-step kk + 1
+  // read while the MFMAs of step kk run
+  auto mma_slice = [&](uint32_t sa, uint32_t sb) {
+    bf16x8 af[2][FM], bfr[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[0][i] = fa.read(sa, i, 0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[0][j] = fb.read(sb, j, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[cur ^ 1][i] = fa.read(sa, i, kk + 1);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[cur ^ 1][j] = fb.read(sb, j, kk + 1);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+    }
+    sched_pipelined_slice<FM * (LA == KC ? 1 : 2) + FN * (LB == KC ? 1 : 2), FM * FN>();
+  };
+
+  if constexpr (WS) {
+    // Separate loops per role over the same tile / slice sequence, meeting at
+    // the same barriers: one per slice, and the staged epilogue's.
+    SliceIter cur;
+    settle(0, cur);
+    if (cur.r < 0) return;
+    if (is_load) {
+      SliceIter ld = cur;
+      plan_tile(ld.c);
+      auto advance = [&]() {
+        if (++ld.ks >= ld.nk) {
+          settle(ld.r + 1, ld);
+          if (ld.r >= 0) plan_tile(ld.c);
+        }
+      };
+      int issued = 0;
+#pragma unroll
+      for (int st = 0; st < STAGES - 1; ++st)
+        if (ld.r >= 0) {
+          issue(st);
+          advance();
+          ++issued;
+        }
+      int n = 0;
+      do {
+        for (int ks = 0; ks < cur.nk; ++ks, ++n) {
+          wait_slices_after<STAGES - 2, DMA_PER_SLICE>(issued - n - 1);
+          bar();
+          if (ld.r >= 0) {
+            issue(issued % STAGES);   // the stage multiplied in the previous iteration
+            advance();
+            ++issued;
+          }
+        }
+        if constexpr (Epi::kStaged) bar();   // the staged epilogue's barrier
+        settle(cur.r + 1, cur);
+      } while (cur.r >= 0);
+      return;
+    }
+    int n = 0;
+    do {
+      zero_acc();
+      for (int ks = 0; ks < cur.nk; ++ks, ++n) {
+        bar();
+        const uint32_t sa = lds0 + (n % STAGES) * C::STAGE_BYTES;
+        if (cur.c.m0 + wm * (BM / WM) < cur.c.m_end) mma_slice(sa, sa + C::A_BYTES);
+      }
+      if constexpr (Epi::kStaged) epilogue_staged(cur.c, lds0 + ((n - 1) % STAGES) * C::STAGE_BYTES);
+      else epilogue(cur.c);
+      settle(cur.r + 1, cur);
+    } while (cur.r >= 0);
+    return;
+  }
 
   SliceIter comp, ld;
   settle(0, comp);
