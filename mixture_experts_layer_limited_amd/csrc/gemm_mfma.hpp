@@ -67,7 +67,7 @@ constexpr uint32_t kOffRange = 0x80000000u;   // lane offset that is outside eve
 // word q < BM of an NW*64-word region, B's at word q < BN of a second one.
 // NLW > 0: NLW load waves issue every DMA (and wait for it) beside the WM x WN
 // compute waves, which then never wait on memory; 0: every wave does both.
-template <int BM, int BN, int WM, int WN, int STAGES, bool MX = false, int NLW = 0>
+template <int BM, int BN, int WM, int WN, int STAGES, bool MX = false, int NLW = 0, bool FP4 = false>
 struct TileCfg {
   static constexpr int BK = 64;
   static constexpr int NW = WM * WN;                       // compute waves
@@ -82,12 +82,17 @@ struct TileCfg {
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int A_DMA = BM * 8 / 64 / ND;           // DMA instructions per DMA wave per slice
   static constexpr int B_DMA = BN * 8 / 64 / ND;
-  static constexpr int SC_DMA = MX ? 2 : 0;                // one scale word per lane for A and for B
+  // scale-word DMA per DMA wave and slice: one word per lane, the A words
+  // (fp4: two per row) over SC_A instructions, the B words over SC_B
+  static constexpr int SC_A = MX ? ((FP4 ? 2 : 1) * BM + 64 * ND - 1) / (64 * ND) : 0;
+  static constexpr int SC_B = MX ? ((FP4 ? 2 : 1) * BN + 64 * ND - 1) / (64 * ND) : 0;
+  static constexpr int SC_DMA = SC_A + SC_B;
   static_assert(!MX || (SC_WORDS >= BM && SC_WORDS >= BN), "scale regions");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(FM >= 1 && FN >= 1 && BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile");
   static_assert(A_DMA * 64 * ND == BM * 8 && B_DMA * 64 * ND == BN * 8, "DMA split");
-  static_assert(NLW == 0 || (!MX && (STAGES - 1) * (A_DMA + B_DMA) <= 63), "load waves: bf16, counts in range");
+  static_assert(NLW == 0 || (STAGES - 1) * (A_DMA + B_DMA + SC_DMA) <= 63, "load waves: counts in range");
+  static_assert(!MX || (SC_A * ND * 64 <= SC_WORDS && SC_B * ND * 64 <= SC_WORDS), "scale lanes");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "row-contiguous layout needs >= 16 chunks per K-row");
   static_assert(STAGES >= 2, "stages");
   static_assert(STAGE_BYTES <= 65536, "read immediates");
@@ -279,7 +284,7 @@ template <int BM, int BN, int WM, int WN, int STAGES, OpLayout LA, OpLayout LB, 
 // registers of two, or a third of the SIMD's)
 __global__ __launch_bounds__(64 * (WM * WN + NLW)) __attribute__((amdgpu_waves_per_eu(1, NLW > 0 ? 3 : 2))) void
 gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
-  using C = TileCfg<BM, BN, WM, WN, STAGES, MX, NLW>;
+  using C = TileCfg<BM, BN, WM, WN, STAGES, MX, NLW, FP4>;
   constexpr bool WS = NLW > 0;
   static_assert(!MX || (LA == KC && LB == KC && MODE != RAGGED_K), "MXFP8: K-contiguous row-ragged products");
   // FP4: two scale words per row and slice, fetched by lanes 2 r and 2 r + 1
@@ -338,7 +343,8 @@ gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
   // MX: scale-word resources, per-lane offsets and the slice's byte offsets
   const uint8_t* rsa_base = nullptr;
   const uint8_t* rsb_base = nullptr;
-  uint32_t rsa_bytes = 0, rsb_bytes = 0, sa_off = kOffRange, sb_off = kOffRange, sosa = 0, sosb = 0;
+  uint32_t rsa_bytes = 0, rsb_bytes = 0, sosa = 0, sosb = 0;
+  uint32_t sa_off[C::SC_A > 0 ? C::SC_A : 1], sb_off[C::SC_B > 0 ? C::SC_B : 1];
   // grouped scale words per slice: one (fp8, 128 values) or two (fp4, 256)
   constexpr int kWordsPerSlice = FP4 ? 2 : 1;
   const int nb = MX ? a.K / (FP4 ? 8 : 16) : 0;     // blocks of 32 values along K (K in 2-byte units)
@@ -381,27 +387,35 @@ gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
     soa = LA == KC ? (uint32_t)(c.k_begin * 2) : 0u;
     sob = LB == KC ? (uint32_t)(c.k_begin * 2) : 0u;
     if constexpr (MX) {
-      // lane q = wave*64 + lane fetches the slice's scale word of tile row q
-      // (A) and of B row q (its weight row), or nothing (an offset outside the
-      // range); fp4: word q & 1 of row q >> 1.  In the grouped layout the
-      // words of consecutive rows are adjacent: a slice's words for a tile are
-      // a few contiguous lines.
-      const int q = wave * 64 + lane;
+      // lane q = (i ND + w) 64 + lane of instruction i of DMA wave w fetches
+      // the slice's scale word of tile row q (A) or of B row q (its weight
+      // row), or nothing (an offset outside the range); fp4: word q & 1 of row
+      // q >> 1.  In the grouped layout the words of consecutive rows are
+      // adjacent: a slice's words for a tile are a few contiguous lines.
       const int nrows = min(c.m_end - c.m0, BM);
-      const int qr = FP4 ? q >> 1 : q;
-      const uint32_t ga = FP4 ? (uint32_t)(q & 1) * (uint32_t)s.a_rows * 4 : 0u;
-      const uint32_t gb = FP4 ? (uint32_t)(q & 1) * (uint32_t)s.b_rows * 4 : 0u;
       rsa_base = s.A_s;
       rsa_bytes = (uint32_t)(s.a_rows * nb);
-      sa_off = qr < nrows ? (uint32_t)((c.m0 + qr) * 4) + ga : kOffRange;
       rsb_base = s.B_s + (MODE == RAGGED_M ? (int64_t)c.g * s.b_s_gstride : 0);
       rsb_bytes = (uint32_t)(s.b_rows * nb);
-      int g = -1;
-      if (qr < BN) {
-        if constexpr (Epi::kPaired) g = Epi::template b_row_paired<BN, WN>(ep, nt, qr);
-        else g = nt * BN + qr;
+#pragma unroll
+      for (int i = 0; i < C::SC_A; ++i) {
+        const int q = (i * C::ND + dw) * 64 + lane;
+        const int qr = FP4 ? q >> 1 : q;
+        const uint32_t ga = FP4 ? (uint32_t)(q & 1) * (uint32_t)s.a_rows * 4 : 0u;
+        sa_off[i] = qr < nrows ? (uint32_t)((c.m0 + qr) * 4) + ga : kOffRange;
       }
-      sb_off = (g >= 0 && g < a.b_next) ? (uint32_t)(g * 4) + gb : kOffRange;
+#pragma unroll
+      for (int i = 0; i < C::SC_B; ++i) {
+        const int q = (i * C::ND + dw) * 64 + lane;
+        const int qr = FP4 ? q >> 1 : q;
+        const uint32_t gb = FP4 ? (uint32_t)(q & 1) * (uint32_t)s.b_rows * 4 : 0u;
+        int g = -1;
+        if (qr < BN) {
+          if constexpr (Epi::kPaired) g = Epi::template b_row_paired<BN, WN>(ep, nt, qr);
+          else g = nt * BN + qr;
+        }
+        sb_off[i] = (g >= 0 && g < a.b_next) ? (uint32_t)(g * 4) + gb : kOffRange;
+      }
       // the tile's first slice: group (k_begin / BK) * kWordsPerSlice
       const uint32_t g0 = (uint32_t)(c.k_begin / BK) * kWordsPerSlice;
       sosa = g0 * (uint32_t)s.a_rows * 4;
@@ -415,12 +429,17 @@ gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
     const uint32_t sbase = lds0 + stage * C::STAGE_BYTES;
     if constexpr (MX) {
 #if defined(__HIP_DEVICE_COMPILE__)
-      const uint32_t sc = sbase + C::A_BYTES + C::B_BYTES + wave * 64 * 4;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(rsa_base, rsa_bytes), (MOE_LDS void*)(uintptr_t)sc, 4,
-                                               sa_off, sosa, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(rsb_base, rsb_bytes),
-                                               (MOE_LDS void*)(uintptr_t)(sc + C::SC_WORDS * 4), 4, sb_off, sosb, 0,
-                                               0);
+      const uint32_t sc = sbase + C::A_BYTES + C::B_BYTES;
+#pragma unroll
+      for (int i = 0; i < C::SC_A; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(rsa_base, rsa_bytes),
+                                                 (MOE_LDS void*)(uintptr_t)(sc + (i * C::ND + dw) * 64 * 4), 4,
+                                                 sa_off[i], sosa, 0, 0);
+#pragma unroll
+      for (int i = 0; i < C::SC_B; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(rsb_base, rsb_bytes),
+                                                 (MOE_LDS void*)(uintptr_t)(sc + (C::SC_WORDS + (i * C::ND + dw) * 64) * 4),
+                                                 4, sb_off[i], sosb, 0, 0);
 #endif
       sosa += kWordsPerSlice * (uint32_t)s.a_rows * 4;   // the next slice's group(s)
       sosb += kWordsPerSlice * (uint32_t)s.b_rows * 4;
@@ -605,6 +624,99 @@ gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
     }
   };
 
+  // microscaled MFMAs of one slice (codes at sa, sb; scale words after B's)
+  auto mx_slice = [&](uint32_t sa, uint32_t sb) {
+    if constexpr (MX && FP4) {
+      // four 64-deep steps per slice (32 bytes of a row each); lane half h
+      // takes 16-byte chunk 2 st + h of its row -- the 32 values of block h
+      // of the step -- and passes the scale of that block: byte 2 st + h of
+      // the row's two scale words
+      const int h = lane >> 5;
+      const uint32_t sc = sb + C::B_BYTES;
+      u32x2 wa[FM], wb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        wa[i] = *(const MOE_LDS u32x2*)(uintptr_t)(sc + (wm * (BM / WM) + i * 32 + (lane & 31)) * 8);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        wb[j] = *(const MOE_LDS u32x2*)(uintptr_t)(sc + C::SC_WORDS * 4 + (wn * (BN / WN) + j * 32 + (lane & 31)) * 8);
+      auto chunk = [&](uint32_t base, int row, int c) -> i32x8 {
+        const u32x4 v = *(const MOE_LDS u32x4*)(uintptr_t)(base + row * 128 + ((c ^ kc_swz(row)) * 16));
+        return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};   // e2m1 uses the low four
+      };
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        i32x8 af[FM], bfr[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = chunk(sa, wm * (BM / WM) + i * 32 + (lane & 31), 2 * st + h);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[j] = chunk(sb, wn * (BN / WN) + j * 32 + (lane & 31), 2 * st + h);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int sa_w = (int)(wa[i][st >> 1] >> (8 * h)), sb_w = (int)(wb[j][st >> 1] >> (8 * h));
+            if ((st & 1) == 0)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 4, 4, 0, sb_w,
+                                                                          0, sa_w);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 4, 4, 2, sb_w,
+                                                                          2, sa_w);
+          }
+      }
+    }
+    if constexpr (MX && !FP4) {
+      // two 64-deep steps per slice; lane half h takes 16-byte chunks
+      // 4 st + h and 4 st + 2 + h of its row and passes the scale of block h
+      const int h = lane >> 5;
+      const uint32_t sc = sb + C::B_BYTES;
+      uint32_t wa[FM], wb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        wa[i] = *(const MOE_LDS uint32_t*)(uintptr_t)(sc + (wm * (BM / WM) + i * 32 + (lane & 31)) * 4) >> (8 * h);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        wb[j] = *(const MOE_LDS uint32_t*)(uintptr_t)(sc + C::SC_WORDS * 4 +
+                                                      (wn * (BN / WN) + j * 32 + (lane & 31)) * 4) >> (8 * h);
+      auto chunk = [&](uint32_t base, int row, int c) -> u32x4 {
+        return *(const MOE_LDS u32x4*)(uintptr_t)(base + row * 128 + ((c ^ kc_swz(row)) * 16));
+      };
+      auto frag = [&](uint32_t base, int row, int st) -> i32x8 {
+        const u32x4 lo = chunk(base, row, st * 4 + h), hi = chunk(base, row, st * 4 + 2 + h);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      };
+      // step 1's fragments go to a second register set, read before step 0's
+      // MFMAs so that the LDS reads can overlap them (iglp_opt(0) below lets
+      // the scheduler interleave the two)
+      i32x8 af[2][FM], bfr[2][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[0][i] = frag(sa, wm * (BM / WM) + i * 32 + (lane & 31), 0);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[0][j] = frag(sb, wn * (BN / WN) + j * 32 + (lane & 31), 0);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (st == 0) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) af[1][i] = frag(sa, wm * (BM / WM) + i * 32 + (lane & 31), 1);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bfr[1][j] = frag(sb, wn * (BN / WN) + j * 32 + (lane & 31), 1);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            if (st == 0)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[0][j], af[0][i], acc[i][j], 0, 0, 0,
+                                                                          (int)wb[j], 0, (int)wa[i]);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[1][j], af[1][i], acc[i][j], 0, 0, 2,
+                                                                          (int)wb[j], 2, (int)wa[i]);
+          }
+      }
+      __builtin_amdgcn_iglp_opt(0);
+    }
+  };
+
   // bf16 MFMAs of one slice (stage at sa, sb), fragments of K-step kk + 1
   // read while the MFMAs of step kk run
   auto mma_slice = [&](uint32_t sa, uint32_t sb) {
@@ -676,7 +788,8 @@ gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
       for (int ks = 0; ks < cur.nk; ++ks, ++n) {
         bar();
         const uint32_t sa = lds0 + (n % STAGES) * C::STAGE_BYTES;
-        if (cur.c.m0 + wm * (BM / WM) < cur.c.m_end) mma_slice(sa, sa + C::A_BYTES);
+        if constexpr (MX) mx_slice(sa, sa + C::A_BYTES);
+        else if (cur.c.m0 + wm * (BM / WM) < cur.c.m_end) mma_slice(sa, sa + C::A_BYTES);
       }
       if constexpr (Epi::kStaged) epilogue_staged(cur.c, lds0 + ((n - 1) % STAGES) * C::STAGE_BYTES);
       else epilogue(cur.c);
@@ -737,95 +850,7 @@ gemm_mfma_kernel(GemmArgs a, MxArgs s, typename Epi::P ep, int NT, int MT) {
       }
       const uint32_t sa = lds0 + (n % STAGES) * C::STAGE_BYTES;
       const uint32_t sb = sa + C::A_BYTES;
-      if constexpr (MX && FP4) {
-        // four 64-deep steps per slice (32 bytes of a row each); lane half h
-        // takes 16-byte chunk 2 st + h of its row -- the 32 values of block h
-        // of the step -- and passes the scale of that block: byte 2 st + h of
-        // the row's two scale words
-        const int h = lane >> 5;
-        const uint32_t sc = sb + C::B_BYTES;
-        u32x2 wa[FM], wb[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          wa[i] = *(const MOE_LDS u32x2*)(uintptr_t)(sc + (wm * (BM / WM) + i * 32 + (lane & 31)) * 8);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          wb[j] = *(const MOE_LDS u32x2*)(uintptr_t)(sc + C::SC_WORDS * 4 + (wn * (BN / WN) + j * 32 + (lane & 31)) * 8);
-        auto chunk = [&](uint32_t base, int row, int c) -> i32x8 {
-          const u32x4 v = *(const MOE_LDS u32x4*)(uintptr_t)(base + row * 128 + ((c ^ kc_swz(row)) * 16));
-          return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};   // e2m1 uses the low four
-        };
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          i32x8 af[FM], bfr[FN];
-#pragma unroll
-          for (int i = 0; i < FM; ++i) af[i] = chunk(sa, wm * (BM / WM) + i * 32 + (lane & 31), 2 * st + h);
-#pragma unroll
-          for (int j = 0; j < FN; ++j) bfr[j] = chunk(sb, wn * (BN / WN) + j * 32 + (lane & 31), 2 * st + h);
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              const int sa_w = (int)(wa[i][st >> 1] >> (8 * h)), sb_w = (int)(wb[j][st >> 1] >> (8 * h));
-              if ((st & 1) == 0)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 4, 4, 0, sb_w,
-                                                                            0, sa_w);
-              else
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 4, 4, 2, sb_w,
-                                                                            2, sa_w);
-            }
-        }
-      }
-      if constexpr (MX && !FP4) {
-        // two 64-deep steps per slice; lane half h takes 16-byte chunks
-        // 4 st + h and 4 st + 2 + h of its row and passes the scale of block h
-        const int h = lane >> 5;
-        const uint32_t sc = sb + C::B_BYTES;
-        uint32_t wa[FM], wb[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          wa[i] = *(const MOE_LDS uint32_t*)(uintptr_t)(sc + (wm * (BM / WM) + i * 32 + (lane & 31)) * 4) >> (8 * h);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          wb[j] = *(const MOE_LDS uint32_t*)(uintptr_t)(sc + C::SC_WORDS * 4 +
-                                                        (wn * (BN / WN) + j * 32 + (lane & 31)) * 4) >> (8 * h);
-        auto chunk = [&](uint32_t base, int row, int c) -> u32x4 {
-          return *(const MOE_LDS u32x4*)(uintptr_t)(base + row * 128 + ((c ^ kc_swz(row)) * 16));
-        };
-        auto frag = [&](uint32_t base, int row, int st) -> i32x8 {
-          const u32x4 lo = chunk(base, row, st * 4 + h), hi = chunk(base, row, st * 4 + 2 + h);
-          return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        };
-        // step 1's fragments go to a second register set, read before step 0's
-        // MFMAs so that the LDS reads can overlap them (iglp_opt(0) below lets
-        // the scheduler interleave the two)
-        i32x8 af[2][FM], bfr[2][FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[0][i] = frag(sa, wm * (BM / WM) + i * 32 + (lane & 31), 0);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bfr[0][j] = frag(sb, wn * (BN / WN) + j * 32 + (lane & 31), 0);
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          if (st == 0) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i) af[1][i] = frag(sa, wm * (BM / WM) + i * 32 + (lane & 31), 1);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bfr[1][j] = frag(sb, wn * (BN / WN) + j * 32 + (lane & 31), 1);
-          }
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              if (st == 0)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[0][j], af[0][i], acc[i][j], 0, 0, 0,
-                                                                            (int)wb[j], 0, (int)wa[i]);
-              else
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[1][j], af[1][i], acc[i][j], 0, 0, 2,
-                                                                            (int)wb[j], 2, (int)wa[i]);
-            }
-        }
-        __builtin_amdgcn_iglp_opt(0);
-      }
+      if constexpr (MX) mx_slice(sa, sb);
       if constexpr (!MX) {
         // A wave whose rows of the tile all lie past m_end (the padding of an
         // expert's last tile) skips its reads and MFMAs, which leaves the

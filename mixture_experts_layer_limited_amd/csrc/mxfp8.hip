@@ -377,12 +377,17 @@ static void to_units(GemmArgs& a) {
 }
 
 // DMA-fed LDS ring (gemm_mfma_kernel in its microscaled form): 128x256 tiles,
-// 2x4 waves, three stages; one tile per workgroup.
+// 2x4 compute waves and two load waves, three stages; one tile per workgroup.
+// The load waves took the skewed DeepSeek-V3 MXFP8 step from 15.6 to 15.0 ms
+// (gate/up data gradient 1.93 -> 1.72 ms, down forward 1.13 -> 0.97 ms).  The
+// MXFP4 SwiGLU forward keeps every wave loading: with its fused quantisation
+// the epilogue needs more than the registers three waves per SIMD leave (it
+// spilled and ran 8.4 ms instead of 1.12).
 template <GemmMode MODE, class Epi, bool FP4>
 static hipError_t launch_mx_dma(GemmArgs a, const MxArgs& s, const typename Epi::P& ep, int n_logical,
                                 int rows_total, hipStream_t st) {
-  constexpr int BM = 128, BN = 256, WM = 2, WN = 4, STAGES = 3;
-  using C = TileCfg<BM, BN, WM, WN, STAGES, true>;
+  constexpr int BM = 128, BN = 256, WM = 2, WN = 4, STAGES = 3, NLW = (FP4 && Epi::kPaired) ? 0 : 2;
+  using C = TileCfg<BM, BN, WM, WN, STAGES, true, NLW, FP4>;
   const int bn_cols = Epi::kPaired ? BN / 2 : BN;
   const int NT = (n_logical + bn_cols - 1) / bn_cols;
   const int MT = (MODE == RAGGED_M) ? 0 : (a.M + BM - 1) / BM;
@@ -391,7 +396,7 @@ static hipError_t launch_mx_dma(GemmArgs a, const MxArgs& s, const typename Epi:
   else tiles = (int64_t)MT * NT;
   if (tiles <= 0) return hipSuccess;
   to_units<FP4>(a);
-  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, STAGES, KC, KC, MODE, Epi, true, FP4>;
+  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, STAGES, KC, KC, MODE, Epi, true, FP4, NLW>;
   static bool lds_done[kLdsAttrDevices] = {};   // per device, per instantiation
   if (hipError_t e = raise_lds_limit(lds_done, (const void*)kern, C::LDS_BYTES); e != hipSuccess) return e;
   kern<<<(unsigned)tiles, C::NTHR, C::LDS_BYTES, st>>>(a, s, ep, NT, MT);
