@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm_band.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "0d488aeec2130231670e14476688f5e44812dc2df92bb39b4d5a4078bf9ccaa2",
-                          "fetch_bytes": 880991273, "write_bytes": 15032559040},
+    "gemm_wgrad_gateup": {"src_sha": "d3e9975120ecd6f03b07aea7b763cd7214a3b22f8ca2b1727533bb1885c5a014",
+                          "fetch_bytes": 883478150, "write_bytes": 15032505760},
 }
 
 
