@@ -15,7 +15,7 @@
 //   wide:   experts of 1..192 rows, a 256-column band, 128 x 256 output tiles
 //           (each streamed slice feeds twice the outputs, so the per-slice
 //           costs -- a barrier, a DMA wait -- weigh half as much);
-//   narrow: experts of 193..320 rows, a 128-column band, 128 x 128 tiles.
+//   narrow: experts of 193..384 rows, a 128-column band, 128 x 128 tiles.
 //
 // Waits.  Vector memory operations of a wave complete in issue order, so the
 // wait for a slice allows exactly the operations issued after that slice's DMA
@@ -29,7 +29,7 @@
 // by estimated cost, and its workgroups stride through it, so the workgroups
 // of an XCD hold neighbouring bands of one expert; each unit walks its tiles
 // from its band index on, so neighbours stream different tiles at any time.
-// Experts with no rows or more than 320 rows have no units here (the caller
+// Experts with no rows or more than 384 rows have no units here (the caller
 // zero-fills the first and runs the DMA ring on the second).
 //
 // Epilogue: each compute wave writes its sub-tile as bf16, 32 x 64 at a time,
@@ -80,7 +80,7 @@ struct BandShape {
   using C = BandCfg<QBAND>;
   static constexpr int BW = WIDE ? 256 : 128;             // band width
   static constexpr int BM = QBAND ? C::SW : BW, BN = QBAND ? BW : C::SW;   // output tile
-  static constexpr int KMAX = WIDE ? 192 : 320, KS = KMAX / C::BK;
+  static constexpr int KMAX = WIDE ? 192 : 384, KS = KMAX / C::BK;
   static constexpr int WM = QBAND ? 2 : 4, WN = C::NCW / WM;   // compute waves over a tile
   static constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
   static constexpr int BAND_SLICE = C::BK * BW * 2;       // 64 rows of the band, bf16

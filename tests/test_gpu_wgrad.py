@@ -3,7 +3,7 @@
 moe_grouped_gemm_swiglu_bwd takes the expert offsets as an input, so the
 expert sizes here are picked by hand rather than by a router: empty experts,
 one row, sizes on and off the 64-row slice boundary, on both sides of 192
-rows (the band kernel's wide and narrow units), up to 320 rows (the
+rows (the band kernel's wide and narrow units), up to 384 rows (the
 stationary-band kernel) and beyond (the DMA ring kernel), with output
 shapes wide enough (N >= 512 columns) for the band kernel to run.  Every
 expert's dW13 and dW2, and dHU, are compared with the oracle's SwiGLU backward
@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-2
 
 SIZES = {
-    "mixed_sizes": [0, 1, 37, 64, 65, 192, 193, 200, 256, 300, 320, 321, 400],
+    "mixed_sizes": [0, 1, 37, 64, 65, 192, 193, 200, 256, 300, 320, 321, 384, 385, 400],
     "random_sizes_e40": [int(v) if v > 20 else 0
                          for v in np.random.default_rng(7).integers(0, 420, size=40)],
 }
