@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCES = ("gemm.hpp", "gemm_regs.hpp", "gemm_mfma.hpp", "gemm_band.hpp", "gemm.hip")
 TRAFFIC_MEASURED = {
     # profiles/gemm_wgrad_gateup_deepseek_v3_hbm_bytes.md
-    "gemm_wgrad_gateup": {"src_sha": "d3e9975120ecd6f03b07aea7b763cd7214a3b22f8ca2b1727533bb1885c5a014",
-                          "fetch_bytes": 883478150, "write_bytes": 15032505760},
+    "gemm_wgrad_gateup": {"src_sha": "8935f744abd01638b1a2386a905cfc0a480871e1ce46a6c95d1be94ad414a7d8",
+                          "fetch_bytes": 879678693, "write_bytes": 15032457952},
 }
 
 
