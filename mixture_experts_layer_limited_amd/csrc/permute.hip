@@ -237,12 +237,15 @@ constexpr int kRowThreads = 256, kRowTokens = 2;
 // KC > 0: k = KC known at compile time, so the k row loads of a chunk are all
 // issued before the sum (0: any k, one row at a time).  The fp32 sum keeps the
 // j order either way.
-// tokens per block of the forward combine (1, 2, 4, 8 tokens: DeepSeek-V3
-// 0.108, 0.109, 0.113, 0.123 ms; Qwen3 0.103, 0.106, 0.108, 0.110 ms)
-constexpr int kCombineTokens = 1;
+// tokens and threads per block of the forward combine (1, 2, 4, 8 tokens of
+// 256 threads: DeepSeek-V3 0.108, 0.109, 0.113, 0.123 ms; one token of 128,
+// 256, 448, 896 threads: 0.109, 0.109, 0.105, 0.103 ms -- 896 threads give
+// each 16-byte chunk of a d = 7168 row its own thread; Qwen3, d = 4096, 0.107,
+// 0.102, 0.101, 0.099 ms)
+constexpr int kCombineTokens = 1, kCombineThreads = 896;
 
 template <class T, int KC>
-__global__ __launch_bounds__(kRowThreads) void combine_kernel(const T* __restrict__ y_perm,
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const T* __restrict__ y_perm,
                                                               const int32_t* __restrict__ rmap,
                                                               const float* __restrict__ gates,
                                                               const T* __restrict__ y_shared, T* __restrict__ y,
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const T* __restric
   const int vec = d / 8;
   const int t0 = blockIdx.x * kCombineTokens;
   const int nq = min(kCombineTokens, T_ - t0) * vec;
-  for (int q = threadIdx.x; q < nq; q += kRowThreads) {
+  for (int q = threadIdx.x; q < nq; q += kCombineThreads) {
     const int t = t0 + q / vec, c = (q % vec) * 8;
     Vec8<T> acc;
 #pragma unroll
@@ -303,7 +306,7 @@ hipError_t launch_combine(const T* y_perm, const int32_t* rmap, const float* gat
                           T* y, int T_, int k, int d, hipStream_t st) {
   if (T_ == 0) return hipSuccess;
 #define MOE_L(KC)                                                                                   \
-  combine_kernel<T, KC><<<(T_ + kCombineTokens - 1) / kCombineTokens, kRowThreads, 0, st>>>(y_perm, rmap, gates, \
+  combine_kernel<T, KC><<<(T_ + kCombineTokens - 1) / kCombineTokens, kCombineThreads, 0, st>>>(y_perm, rmap, gates, \
                                                                                       y_shared, y, T_, k, d)
   MOE_DISPATCH_K(k, MOE_L);
 #undef MOE_L
