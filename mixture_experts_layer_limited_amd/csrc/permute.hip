@@ -241,7 +241,9 @@ constexpr int kRowThreads = 256, kRowTokens = 2;
 // 256 threads: DeepSeek-V3 0.108, 0.109, 0.113, 0.123 ms; one token of 128,
 // 256, 448, 896 threads: 0.109, 0.109, 0.105, 0.103 ms -- 896 threads give
 // each 16-byte chunk of a d = 7168 row its own thread; Qwen3, d = 4096, 0.107,
-// 0.102, 0.101, 0.099 ms)
+// 0.102, 0.101, 0.099 ms).  The unpermute-sum of the backward takes the same
+// shape (DeepSeek-V3 0.110 -> 0.103 ms, Qwen3 0.122 -> 0.114 ms against two
+// tokens of 256 threads).
 constexpr int kCombineTokens = 1, kCombineThreads = 896;
 
 template <class T, int KC>
@@ -431,15 +433,15 @@ hipError_t launch_combine_bwd(const T* dy, const T* y_perm, const int32_t* rmap,
 // dx[t] = storage(partial[t] + sum_j dx_perm[row(t,j)]), j in order; KC and
 // the work split as in combine
 template <class T, int KC>
-__global__ __launch_bounds__(kRowThreads) void unpermute_sum_kernel(const T* __restrict__ dx_perm,
+__global__ __launch_bounds__(kCombineThreads) void unpermute_sum_kernel(const T* __restrict__ dx_perm,
                                                                     const int32_t* __restrict__ rmap,
                                                                     const float* __restrict__ partial,
                                                                     T* __restrict__ dx, int T_, int k_rt, int d) {
   const int k = KC > 0 ? KC : k_rt;
   const int vec = d / 8;
-  const int t0 = blockIdx.x * kRowTokens;
-  const int nq = min(kRowTokens, T_ - t0) * vec;
-  for (int q = threadIdx.x; q < nq; q += kRowThreads) {
+  const int t0 = blockIdx.x * kCombineTokens;
+  const int nq = min(kCombineTokens, T_ - t0) * vec;
+  for (int q = threadIdx.x; q < nq; q += kCombineThreads) {
     const int t = t0 + q / vec, c = (q % vec) * 8;
     Vec8<T> acc;
     if (partial) {
@@ -477,7 +479,7 @@ hipError_t launch_unpermute_sum(const T* dx_perm, const int32_t* rmap, const flo
                                 int T_, int k, int d, hipStream_t st) {
   if (T_ == 0) return hipSuccess;
 #define MOE_L(KC)                                                                                 \
-  unpermute_sum_kernel<T, KC><<<(T_ + kRowTokens - 1) / kRowTokens, kRowThreads, 0, st>>>(dx_perm, rmap, \
+  unpermute_sum_kernel<T, KC><<<(T_ + kCombineTokens - 1) / kCombineTokens, kCombineThreads, 0, st>>>(dx_perm, rmap, \
                                                                                           partial, dx, T_, k, d)
   MOE_DISPATCH_K(k, MOE_L);
 #undef MOE_L
